@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Decode-matmul benchmark on one MI355X: packed-ternary (PQ2) weights x
+group-128 INT8 activations, the attention-QKV projection shape (K=5120,
+N=10240) at M = 1, 2, 3, 4 activation columns.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+
+A step is one pass of the per-call hot path over one batch: for each M in
+1..4, quantise the bf16 activations to INT8 (pq2_quantize_act_i8) and run the
+small-m matmul (pq2_matmul_small_m) against the prepared planes.  Weight
+preparation (pq2_prepare_planes) is one-time and outside the timing.  Every
+step reads the next of R prepared-plane copies (>= 1 GiB in total, four
+times the 256 MB Infinity Cache), so weights stream from HBM.  Steps are
+captured as HIP graphs (one per copy) and replayed; K steps are timed with
+HIP events between a synchronize on each side.
+
+value = algorithmic bytes of the timed steps / their time (GB/s), where a
+call's algorithmic bytes are what the method must move: packed weights
+(34 B / 128 weights) + bf16 activations + q + xs (quantiser) and
+weights + q + xs + y (matmul).  The per-M matmul kernel duration (HIP events
+around graph replays of back-to-back launches on the launch stream) gives the
+roofline entry.  The CPU oracle, timed on a bounded sample of the same work,
+gives cpu_baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_BYTES_PER_S = 8.0e12       # MI355X HBM3E, published peak
+PEAK_INT8_OPS_PER_S = 5.0e15        # MI355X dense INT8 MFMA, published peak
+ROTATION_BYTES = 1 << 30
+METRIC = "µs/call and achieved HBM GB/s (% of peak) for M=1..4 packed-ternary matmul"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes(n, k):
+    return n * (k // 128) * 34
+
+
+def matmul_bytes(m, n, k):
+    return weight_bytes(n, k) + m * k + m * (k // 128) * 4 + m * n * 4
+
+
+def quantize_bytes(m, k):
+    return m * k * 2 + m * k + m * (k // 128) * 4
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("small_m.hip", "pq2_device.h"):
+        with open(os.path.join(ROOT, "gemm_int8_act_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(digest):
+    """HBM bytes per launch of the small-m kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "small_m_qkv_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                vals[parts[0]] = parts[1]
+    if vals.get("kernel_source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch_avg_m1to4"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Graph:
+    """A captured HIP graph of a callable, replayed on the capture stream."""
+
+    def __init__(self, torch, fn, stream):
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            fn()  # warm (first-call attribute setup happens outside capture)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.g, stream=stream):
+            fn()
+
+    def replay(self):
+        self.g.replay()
+
+
+def time_graph(torch, graph, stream, reps):
+    """Milliseconds per replay, HIP events on the replay stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(raw, x, n, k, ms, budget_s):
+    """The CPU oracle on the same work (quantise + matmul per M), repeated up
+    to the time budget; single thread."""
+    import oracle
+    import workloads
+    bits = workloads.bf16_bits(x)
+    done_bytes = 0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for m in ms:
+            q, xs = oracle.quantize_act_i8(bits[:m])
+            oracle.matmul_raw(q, xs, raw, n, k)
+            done_bytes += quantize_bytes(m, k) + matmul_bytes(m, n, k)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": done_bytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} repetition(s) of quantise+matmul at M={list(ms)} on the full K={k} N={n} "
+                  f"shape, {dt:.1f} s single-threaded",
+        "ms_per_step": dt / reps * 1e3,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gemm_int8_act_amd as pq2
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS["qkv"]
+    n, k, ms = w.n, w.k, (1, 2, 3, 4)
+    raw_np, x_cpu = workloads.workload_inputs("qkv")
+    wb = weight_bytes(n, k)
+    copies = max(2, math.ceil(ROTATION_BYTES / wb))
+    log(f"[bench] qkv K={k} N={n} weights {wb} B, {copies} plane copies ({copies * wb / 2**30:.2f} GiB)")
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        raw = torch.from_numpy(raw_np).to(dev)
+        pool = torch.empty((copies, wb), dtype=torch.uint8, device=dev)
+        pq2.pq2_prepare_planes(raw, n, k, pool[0])
+        for c in range(1, copies):
+            pool[c].copy_(pool[0])
+        x = x_cpu.to(dev)
+        bufs = {}
+        for m in ms:
+            bufs[m] = (torch.empty((m, k), dtype=torch.int8, device=dev),
+                       torch.empty((m, k // 128), dtype=torch.float32, device=dev),
+                       torch.empty((m, n), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+
+    def step_fn(c):
+        def f():
+            for m in ms:
+                q, xs, y = bufs[m]
+                pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
+                pq2.pq2_matmul_small_m(q, xs, pool[c], y, stream=stream)
+        return f
+
+    step_graphs = [Graph(torch, step_fn(c), stream) for c in range(copies)]
+    step_bytes = sum(quantize_bytes(m, k) + matmul_bytes(m, n, k) for m in ms)
+
+    # Warmup, then exactly K timed steps.
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step_graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for i in range(args.steps):
+            step_graphs[(args.warmup + i) % copies].replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    for y in (bufs[m][2] for m in ms):
+        assert torch.isfinite(y).all(), "non-finite output"
+
+    # Per-M call timings: graphs of `copies` back-to-back launches, one per copy.
+    per_m = {}
+    reps = 20
+    for m in ms:
+        q, xs, y = bufs[m]
+
+        def mm(m=m, q=q, xs=xs, y=y):
+            for c in range(copies):
+                pq2.pq2_matmul_small_m(q, xs, pool[c], y, stream=stream)
+
+        def full(m=m, q=q, xs=xs, y=y):
+            for c in range(copies):
+                pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
+                pq2.pq2_matmul_small_m(q, xs, pool[c], y, stream=stream)
+
+        t_mm = time_graph(torch, Graph(torch, mm, stream), stream, reps) / copies * 1e3
+        t_full = time_graph(torch, Graph(torch, full, stream), stream, reps) / copies * 1e3
+        gbs = matmul_bytes(m, n, k) / (t_mm * 1e-6) / 1e9
+        per_m[str(m)] = {
+            "matmul_us": round(t_mm, 3),
+            "matmul_GBps": round(gbs, 1),
+            "matmul_pct_peak": round(100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S, 1),
+            "complete_call_us": round(t_full, 3),
+            "matmul_bytes": matmul_bytes(m, n, k),
+        }
+        log(f"[bench] M={m}: matmul {t_mm:.3f} us ({gbs:.0f} GB/s, "
+            f"{100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S:.1f}% of 8 TB/s), complete call {t_full:.3f} us")
+
+    tot_bytes = sum(v["matmul_bytes"] for v in per_m.values())
+    tot_us = sum(v["matmul_us"] for v in per_m.values())
+    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
+    digest = source_digest()
+    traffic = stored_traffic(digest)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_HBM_BYTES_PER_S / 1e9,
+        "unit": "GB/s",
+        "frac": round(achieved * 1e9 / PEAK_HBM_BYTES_PER_S, 4),
+        "traffic": traffic,
+        "kernel": "small_m_kernel (pq2_matmul_small_m), mean over one launch each at M=1..4",
+        "algorithmic_bytes_per_launch_avg": tot_bytes / len(ms),
+        "mean_launch_us": round(tot_us / len(ms), 3),
+        "kernel_source_digest": digest,
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "attention QKV projection K=5120 N=10240, M=1,2,3,4 (quantise + matmul per M)",
+            "k": k, "n": n, "ms": list(ms),
+            "weight_copies": copies, "rotation_bytes": copies * wb,
+        },
+        "us_per_call": per_m,
+        "roofline": roofline,
+    }
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(torch, pq2, workloads, dev, stream)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(raw_np, x_cpu, n, k, ms, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(torch, pq2, workloads, dev, stream):
+    """MFMA prefill at the gate (N=6144) and up (N=17408) shapes, M=256..1024."""
+    out = {}
+    for name in ("prefill_gate", "prefill_up"):
+        w = workloads.WORKLOADS[name]
+        raw_np, x_cpu = workloads.workload_inputs(name)
+        with torch.cuda.stream(stream):
+            planes = torch.empty(weight_bytes(w.n, w.k), dtype=torch.uint8, device=dev)
+            pq2.pq2_prepare_planes(torch.from_numpy(raw_np).to(dev), w.n, w.k, planes)
+            x = x_cpu.to(dev)
+        torch.cuda.synchronize()
+        for m in w.ms:
+            q = torch.empty((m, w.k), dtype=torch.int8, device=dev)
+            xs = torch.empty((m, w.k // 128), dtype=torch.float32, device=dev)
+            y = torch.empty((m, w.n), dtype=torch.float32, device=dev)
+            with torch.cuda.stream(stream):
+                pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
+
+            def f(q=q, xs=xs, y=y):
+                for _ in range(10):
+                    pq2.pq2_matmul_prefill(q, xs, planes, y, stream=stream)
+
+            t_us = time_graph(torch, Graph(torch, f, stream), stream, 5) / 10 * 1e3
+            ops = 2.0 * m * w.n * w.k
+            tops = ops / (t_us * 1e-6) / 1e12
+            out[f"{name}_m{m}"] = {"us": round(t_us, 2), "TOPS": round(tops, 1),
+                                   "pct_int8_peak": round(100 * tops * 1e12 / PEAK_INT8_OPS_PER_S, 1)}
+            log(f"[bench] {name} M={m}: {t_us:.1f} us, {tops:.0f} TOPS")
+        del planes
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+"""gemm_int8_act_amd -- packed-ternary (PQ2) x INT8-activation matmul on MI355X.
+
+A thin ctypes binding over ``libpq2.so`` (hand-written HIP for gfx950, C ABI
+in ``include/pq2.h``).  Every function here has the name of the C entry point
+it calls and only marshals arguments: torch tensors give device pointers and
+shapes, the current torch stream gives the HIP stream.  All arithmetic runs
+in the HIP kernels; there is no CPU or PyTorch fallback.  If the library is
+missing, importing the package raises ImportError; build it with
+``python gemm_int8_act_amd/build.py``.
+
+Status codes map to exceptions: EINVAL, ESHAPE and EALIGN raise ValueError;
+ELAUNCH and EDEVICE raise RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpq2.so")
+
+PQ2_OK, PQ2_EINVAL, PQ2_ESHAPE, PQ2_EALIGN, PQ2_ELAUNCH, PQ2_EDEVICE = range(6)
+PQ2_BF16, PQ2_F16, PQ2_F32 = 0, 1, 2
+PQ2_MAX_SMALL_M = 16
+PQ2_MAX_K = 65536
+
+EXPORTED = (
+    "pq2_layout_version",
+    "pq2_status_str",
+    "pq2_last_hip_error",
+    "pq2_prepare_planes",
+    "pq2_quantize_act_i8",
+    "pq2_matmul_small_m",
+    "pq2_matmul_prefill",
+    "pq2_matmul_small_m_tuned",
+)
+
+
+def _hip_runtimes_mapped():
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as fh:
+            return sorted({line.split()[-1] for line in fh if "libamdhip64" in line})
+    except OSError:
+        return []
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: the HIP library must be built "
+            "(python gemm_int8_act_amd/build.py); there is no fallback path")
+    # torch brings its own HIP runtime.  It must be loaded BEFORE libpq2.so so
+    # that the dynamic loader binds libpq2's libamdhip64 dependency to that
+    # same copy; loading libpq2 first maps the system runtime, torch then maps
+    # its own, and kernels launched through one runtime on memory and streams
+    # of the other crash the process.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped into this process ({runtimes}); "
+                          "libpq2 must share torch's runtime")
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.pq2_layout_version.argtypes = []
+    lib.pq2_layout_version.restype = i32
+    lib.pq2_status_str.argtypes = [i32]
+    lib.pq2_status_str.restype = ctypes.c_char_p
+    lib.pq2_last_hip_error.argtypes = []
+    lib.pq2_last_hip_error.restype = ctypes.c_char_p
+    lib.pq2_prepare_planes.argtypes = [p, i64, i64, i64, p, p]
+    lib.pq2_prepare_planes.restype = i32
+    lib.pq2_quantize_act_i8.argtypes = [p, i32, i64, i64, i64, p, p, p]
+    lib.pq2_quantize_act_i8.restype = i32
+    lib.pq2_matmul_small_m.argtypes = [p, p, p, i64, i64, i64, p, p]
+    lib.pq2_matmul_small_m.restype = i32
+    lib.pq2_matmul_prefill.argtypes = [p, p, p, i64, i64, i64, p, p]
+    lib.pq2_matmul_prefill.restype = i32
+    lib.pq2_matmul_small_m_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, i32, p]
+    lib.pq2_matmul_small_m_tuned.restype = i32
+    return lib
+
+
+lib = _load_library()
+
+
+class Pq2Error(Exception):
+    pass
+
+
+def pq2_status_str(status: int) -> str:
+    return lib.pq2_status_str(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status == PQ2_OK:
+        return
+    msg = f"{what}: {pq2_status_str(status)} (status {status})"
+    if status in (PQ2_EINVAL, PQ2_ESHAPE, PQ2_EALIGN):
+        raise ValueError(msg)
+    if status == PQ2_ELAUNCH:
+        msg += f" [{pq2_last_hip_error()}]"
+    raise RuntimeError(msg)
+
+
+def pq2_last_hip_error() -> str:
+    return lib.pq2_last_hip_error().decode()
+
+
+def pq2_layout_version() -> int:
+    return lib.pq2_layout_version()
+
+
+def _dev_ptr(t, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def pq2_prepare_planes(raw, n: int, k: int, planes, stream=None) -> None:
+    """raw: uint8 device tensor [n][row_stride] (row stride = raw.stride(0));
+    planes: uint8 device tensor of n*(k/128)*34 bytes."""
+    import torch
+    if raw.dtype != torch.uint8 or planes.dtype != torch.uint8 or raw.dim() != 2 or raw.stride(1) != 1:
+        raise ValueError("raw must be a 2-D uint8 tensor with unit column stride; planes uint8")
+    if planes.numel() < n * (k // 128) * 34 or not planes.is_contiguous():
+        raise ValueError("planes must be a contiguous uint8 tensor of n*(k/128)*34 bytes")
+    _check(lib.pq2_prepare_planes(_dev_ptr(raw, "raw"), raw.stride(0), n, k, _dev_ptr(planes, "planes"),
+                                  _stream(stream)), "pq2_prepare_planes")
+
+
+_DTYPES = None
+
+
+def _dtype_code(x) -> int:
+    global _DTYPES
+    import torch
+    if _DTYPES is None:
+        _DTYPES = {torch.bfloat16: PQ2_BF16, torch.float16: PQ2_F16, torch.float32: PQ2_F32}
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported activation dtype {x.dtype}")
+    return _DTYPES[x.dtype]
+
+
+def pq2_quantize_act_i8(x, q, xs, stream=None) -> None:
+    """x: [m][>=k] bf16/f16/f32 device tensor (unit column stride); q: int8
+    [m][k]; xs: float32 [m][k/128] (both contiguous)."""
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if q.dtype != torch.int8 or xs.dtype != torch.float32 or not q.is_contiguous() or not xs.is_contiguous():
+        raise ValueError("q must be contiguous int8 and xs contiguous float32")
+    m, k = q.shape
+    if x.shape[0] != m or x.shape[1] < k or xs.numel() != m * (k // 128):
+        raise ValueError("shape mismatch between x, q and xs")
+    _check(lib.pq2_quantize_act_i8(_dev_ptr(x, "x"), _dtype_code(x), x.stride(0), m, k, _dev_ptr(q, "q"),
+                                   _dev_ptr(xs, "xs"), _stream(stream)), "pq2_quantize_act_i8")
+
+
+def _matmul_args(q, xs, planes, y):
+    import torch
+    if q.dtype != torch.int8 or xs.dtype != torch.float32 or planes.dtype != torch.uint8 or y.dtype != torch.float32:
+        raise ValueError("q int8, xs float32, planes uint8, y float32 expected")
+    for name, t in (("q", q), ("xs", xs), ("planes", planes), ("y", y)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    m, k = q.shape
+    n = y.shape[1]
+    if y.shape[0] != m or xs.numel() != m * (k // 128) or planes.numel() < n * (k // 128) * 34:
+        raise ValueError("shape mismatch between q, xs, planes and y")
+    return (_dev_ptr(q, "q"), _dev_ptr(xs, "xs"), _dev_ptr(planes, "planes"), m, n, k, _dev_ptr(y, "y"))
+
+
+def pq2_matmul_small_m(q, xs, planes, y, stream=None) -> None:
+    """y[m][n] = PQ2 planes x INT8 activations, 1 <= m <= 16."""
+    _check(lib.pq2_matmul_small_m(*_matmul_args(q, xs, planes, y), _stream(stream)), "pq2_matmul_small_m")
+
+
+def pq2_matmul_small_m_tuned(q, xs, planes, y, rows_per_lane=0, max_waves=0, decode=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows_per_lane, max_waves, decode,
+                                        _stream(stream)), "pq2_matmul_small_m_tuned")
+
+
+def pq2_matmul_prefill(q, xs, planes, y, stream=None) -> None:
+    """y[m][n] on the INT8 matrix cores (any m >= 1)."""
+    _check(lib.pq2_matmul_prefill(*_matmul_args(q, xs, planes, y), _stream(stream)), "pq2_matmul_prefill")

@@ -1,0 +1,143 @@
+// api.hip -- the C ABI of libpq2 (declared in include/pq2.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, returns a status instead of aborting, and enqueues its kernel
+// on the caller's stream.  Buffers are owned by the caller.
+#include "../../include/pq2.h"
+#include "pq2_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+constexpr int64_t kMaxPrefillM = (int64_t)65535 * 128;  // grid.y limit x tile rows
+constexpr int64_t kMaxN = (int64_t)1 << 30;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Is the current device a gfx950?  Cached per device ordinal.
+int check_device() {
+    static int known[64];  // 0 unknown, 1 yes, 2 no
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PQ2_EDEVICE;
+    if (dev >= 0 && dev < 64 && known[dev]) return known[dev] == 1 ? PQ2_OK : PQ2_EDEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PQ2_EDEVICE;
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) known[dev] = ok ? 1 : 2;
+    return ok ? PQ2_OK : PQ2_EDEVICE;
+}
+
+thread_local hipError_t last_hip_error = hipSuccess;
+
+int launch_status(hipError_t e) {
+    last_hip_error = e;
+    return e == hipSuccess ? PQ2_OK : PQ2_ELAUNCH;
+}
+
+int check_k(int64_t k) {
+    if (k < kGroup || k % kGroup || k > PQ2_MAX_K) return PQ2_ESHAPE;
+    return PQ2_OK;
+}
+
+int check_matmul_args(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
+                      int64_t k, float* y, int64_t m_max) {
+    if (!q || !xs || !planes || !y) return PQ2_EINVAL;
+    if (m < 1 || m > m_max || n < 1 || n > kMaxN) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (!aligned(q, 16) || !aligned(planes, 16) || !aligned(xs, 4) || !aligned(y, 4)) return PQ2_EALIGN;
+    const size_t ybytes = (size_t)m * n * 4;
+    if (overlap(y, ybytes, q, (size_t)m * k) || overlap(y, ybytes, xs, (size_t)m * (k / kGroup) * 4) ||
+        overlap(y, ybytes, planes, (size_t)n * (k / kGroup) * 34))
+        return PQ2_EINVAL;
+    return PQ2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pq2_layout_version(void) { return 1; }
+
+const char* pq2_last_hip_error(void) { return hipGetErrorName(last_hip_error); }
+
+const char* pq2_status_str(int status) {
+    switch (status) {
+        case PQ2_OK: return "ok";
+        case PQ2_EINVAL: return "invalid argument (null pointer, dtype, or overlapping buffers)";
+        case PQ2_ESHAPE: return "unsupported shape (k % 128, m/n/k range, or row stride)";
+        case PQ2_EALIGN: return "misaligned pointer or stride";
+        case PQ2_ELAUNCH: return "kernel launch failed";
+        case PQ2_EDEVICE: return "current device is not gfx950";
+        default: return "unknown status";
+    }
+}
+
+int pq2_prepare_planes(const void* raw, int64_t raw_row_stride_bytes, int64_t n, int64_t k,
+                       void* planes, void* stream) {
+    if (!raw || !planes) return PQ2_EINVAL;
+    if (n < 1 || n > kMaxN) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (raw_row_stride_bytes < (k / kGroup) * 34) return PQ2_ESHAPE;
+    if (!aligned(planes, 16)) return PQ2_EALIGN;
+    const size_t raw_bytes = (size_t)(n - 1) * raw_row_stride_bytes + (size_t)(k / kGroup) * 34;
+    if (overlap(raw, raw_bytes, planes, (size_t)n * (k / kGroup) * 34)) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_prepare(static_cast<const uint8_t*>(raw), raw_row_stride_bytes, n, k,
+                                             static_cast<uint8_t*>(planes), (hipStream_t)stream));
+}
+
+int pq2_quantize_act_i8(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
+                        int8_t* q, float* xs, void* stream) {
+    if (!x || !q || !xs) return PQ2_EINVAL;
+    if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
+    if (m < 1 || m > ((int64_t)1 << 31)) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (x_row_stride_elems < k) return PQ2_ESHAPE;
+    const int esize = dtype == PQ2_F32 ? 4 : 2;
+    if (!aligned(x, esize) || !aligned(q, 8) || !aligned(xs, 4)) return PQ2_EALIGN;
+    const size_t xbytes = ((size_t)(m - 1) * x_row_stride_elems + k) * esize;
+    if (overlap(q, (size_t)m * k, x, xbytes) || overlap(xs, (size_t)m * (k / kGroup) * 4, x, xbytes) ||
+        overlap(q, (size_t)m * k, xs, (size_t)m * (k / kGroup) * 4))
+        return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_quantize(x, dtype, x_row_stride_elems, m, k, q, xs, (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
+                             int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
+                             int decode, void* stream) {
+    if (int rc = check_matmul_args(q, xs, planes, m, n, k, y, PQ2_MAX_SMALL_M)) return rc;
+    pq2::SmallMConfig cfg = pq2::default_small_m_config(m, n, k);
+    if (rows_per_lane) cfg.rows_per_lane = rows_per_lane;
+    if (max_waves) cfg.max_waves = max_waves;
+    if (decode) cfg.decode = decode;
+    if ((cfg.rows_per_lane != 1 && cfg.rows_per_lane != 2 && cfg.rows_per_lane != 4) || cfg.max_waves < 1 ||
+        cfg.max_waves > 8 || (cfg.decode != 1 && cfg.decode != 2))
+        return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m(q, xs, static_cast<const uint8_t*>(planes), m, n, k, y, cfg,
+                                             (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
+                       int64_t k, float* y, void* stream) {
+    return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, 0, stream);
+}
+
+int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
+                       int64_t k, float* y, void* stream) {
+    if (int rc = check_matmul_args(q, xs, planes, m, n, k, y, kMaxPrefillM)) return rc;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_prefill(q, xs, static_cast<const uint8_t*>(planes), m, n, k, y,
+                                             (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// pq2_device.h -- device-side helpers shared by the gfx950 kernels of libpq2.
+//
+// Wave64 cross-lane primitives (DPP), the byte transpose that puts INT8
+// activations into code-plane order, and the two exact 2-bit decodes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pq2 {
+
+// ---------------------------------------------------------------- DPP
+// dpp_ctrl encodings (GFX9 DPP): quad_perm [1,0,3,2] swaps neighbours,
+// [2,3,0,1] swaps pairs, row_half_mirror reverses each 8-lane half-row,
+// row_mirror reverses each 16-lane row.
+enum : int {
+    kDppXor1 = 0xB1,
+    kDppXor2 = 0x4E,
+    kDppHalfMirror = 0x141,
+    kDppMirror = 0x140,
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the
+// same value (each step pairs a with b and b with a, and FP addition is
+// commutative, so partner lanes agree bit for bit).
+__device__ __forceinline__ float sum8_f(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ int sum8_i(int v) {
+    v += dpp_i<kDppXor1>(v);
+    v += dpp_i<kDppXor2>(v);
+    v += dpp_i<kDppHalfMirror>(v);
+    return v;
+}
+
+// Max over each aligned group of 16 lanes (one DPP row); all lanes agree.
+__device__ __forceinline__ float max16_f(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    return v;
+}
+
+// ---------------------------------------------------------------- dot4
+// Signed 4 x int8 dot product accumulated into a signed int32 (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int acc) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, acc, false);
+}
+
+// ---------------------------------------------------------------- plane order
+// A code dword (4 code bytes = 16 consecutive weights 16t..16t+15 of a block)
+// splits into four planes: plane s holds weights 16t+4j+s, j = 0..3, one per
+// byte.  The matching activation dword holds q[16t+4j+s] in byte j, i.e. byte
+// s of each of the four natural-order activation dwords Q0..Q3 = a 4x4 byte
+// transpose.  __builtin_amdgcn_perm(hi, lo, sel): result byte i is byte
+// sel.i of the 8-byte value {hi:lo} (selector 0..3 = lo, 4..7 = hi).
+__device__ __forceinline__ uint4 to_plane_order(uint4 Q) {
+    const uint32_t l01 = __builtin_amdgcn_perm(Q.y, Q.x, 0x05010400u);  // Q0b0 Q1b0 Q0b1 Q1b1
+    const uint32_t h01 = __builtin_amdgcn_perm(Q.y, Q.x, 0x07030602u);  // Q0b2 Q1b2 Q0b3 Q1b3
+    const uint32_t l23 = __builtin_amdgcn_perm(Q.w, Q.z, 0x05010400u);
+    const uint32_t h23 = __builtin_amdgcn_perm(Q.w, Q.z, 0x07030602u);
+    uint4 P;
+    P.x = __builtin_amdgcn_perm(l23, l01, 0x05040100u);  // byte 0 of Q0..Q3
+    P.y = __builtin_amdgcn_perm(l23, l01, 0x07060302u);  // byte 1
+    P.z = __builtin_amdgcn_perm(h23, h01, 0x05040100u);  // byte 2
+    P.w = __builtin_amdgcn_perm(h23, h01, 0x07060302u);  // byte 3
+    return P;
+}
+
+// ---------------------------------------------------------------- decodes
+// add/XOR expansion of plane s of a code dword: each byte's 2-bit field c
+// (0..3) becomes the signed byte c-1.  c + 0x7F lies in 0x7F..0x82, so no
+// byte carries into the next, and flipping bit 7 maps 127,128,129,130 to
+// -1,0,+1,+2 as two's-complement bytes.
+template <int S>
+__device__ __forceinline__ uint32_t expand_plane(uint32_t d) {
+    return (((d >> (2 * S)) & 0x03030303u) + 0x7F7F7F7Fu) ^ 0x80808080u;
+}
+
+// Masked planes: byte values c * 4^S for S = 0,1,2 and, for S = 3, the field
+// shifted down by two (c * 16) so every byte stays below 128.
+template <int S>
+__device__ __forceinline__ uint32_t mask_plane(uint32_t d) {
+    if constexpr (S == 0) return d & 0x03030303u;
+    if constexpr (S == 1) return d & 0x0C0C0C0Cu;
+    if constexpr (S == 2) return d & 0x30303030u;
+    return (d >> 2) & 0x30303030u;
+}
+
+// 16-byte load with the non-temporal hint (streamed once, no reuse).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+}  // namespace pq2

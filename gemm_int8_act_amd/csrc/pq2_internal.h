@@ -1,0 +1,37 @@
+// pq2_internal.h -- host-side launchers shared between the libpq2 sources.
+// Arguments reaching these functions are already validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pq2 {
+
+// Discard an error another library left in this thread's HIP error slot, so
+// the hipGetLastError() that follows our launch reports our launch only.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
+// Returns a hipError_t from launching (hipSuccess on success).
+hipError_t launch_prepare(const uint8_t* raw, int64_t stride, int64_t n, int64_t k, uint8_t* planes,
+                          hipStream_t stream);
+
+hipError_t launch_quantize(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,
+                           int8_t* q, float* xs, hipStream_t stream);
+
+struct SmallMConfig {
+    int rows_per_lane;  // 1, 2 or 4
+    int max_waves;      // 1..16: waves that split k inside one workgroup
+    int decode;         // 1 = add/XOR, 2 = masked planes + sum(q) correction
+};
+
+SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k);
+
+// Returns hipErrorInvalidValue for a configuration the library has no kernel for.
+hipError_t launch_small_m(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
+                          int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
+                          hipStream_t stream);
+
+hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
+                          int64_t n, int64_t k, float* y, hipStream_t stream);
+
+}  // namespace pq2

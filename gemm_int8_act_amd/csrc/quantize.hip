@@ -1,0 +1,150 @@
+// quantize.hip -- group-128 INT8 activation quantisation and raw-block ->
+// prepared-plane preparation for gfx950.
+//
+// Quantiser (page "Baseline and the integer breakthrough", "Calculate with
+// small integers" step 1; page "Kernel experiments: recorded evidence",
+// Test 6): per group of 128 elements, scale = max|x| / 127 as one correctly
+// rounded FP32 division, each element divided (correctly rounded) by the
+// scale, or by 1 for an all-zero group, rounded half to even, clamped to
+// +-127.  The kernel uses exactly those IEEE operations (hipcc keeps FP32
+// division correctly rounded and lowers rintf to v_rndne_f32; FP32
+// subnormals are preserved), so q and xs are bit-identical to the definition.
+//
+// Geometry: 16 lanes (one DPP row) per group, 8 consecutive elements per lane
+// (one 16-byte load for 2-byte types), 16 groups per 256-thread workgroup.
+// The group max is a 4-step DPP reduction inside the row.
+#include "pq2_device.h"
+#include "pq2_internal.h"
+
+#include <hip/hip_fp16.h>
+
+namespace pq2 {
+
+template <int DT>
+__device__ __forceinline__ float elem_to_float(uint32_t bits16_or_32) {
+    if constexpr (DT == 0) return __uint_as_float(bits16_or_32 << 16);        // bf16
+    if constexpr (DT == 1) return __half2float(__ushort_as_half((unsigned short)bits16_or_32));
+    return __uint_as_float(bits16_or_32);                                        // f32
+}
+
+// DT: 0 bf16, 1 f16, 2 f32.  VEC: row bases are 16-byte aligned (2-byte types)
+// or 16-byte aligned (f32), so each lane's 8 elements load as whole vectors.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int64_t row_stride,
+                                                       int64_t k, int64_t total_groups,
+                                                       int8_t* __restrict__ q, float* __restrict__ xs) {
+    const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int l = threadIdx.x & 15;
+    if (gid >= total_groups) return;  // whole 16-lane rows leave together
+    const int64_t groups = k / 128;
+    const int64_t row = gid / groups;
+    const int64_t g = gid - row * groups;
+    const int64_t base = row * row_stride + g * 128 + l * 8;
+
+    float v[8];
+    if constexpr (DT == 2) {
+        const float* xp = static_cast<const float*>(x) + base;
+        if constexpr (VEC) {
+            const float4 a = *reinterpret_cast<const float4*>(xp);
+            const float4 b = *reinterpret_cast<const float4*>(xp + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = xp[e];
+        }
+    } else {
+        const uint16_t* xp = static_cast<const uint16_t*>(x) + base;
+        if constexpr (VEC) {
+            const uint4 w = *reinterpret_cast<const uint4*>(xp);
+            const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = elem_to_float<DT>(words[e] & 0xFFFFu);
+                v[2 * e + 1] = elem_to_float<DT>(words[e] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = elem_to_float<DT>(xp[e]);
+        }
+    }
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = max16_f(amax);
+
+    const float scale = amax / 127.0f;                 // one IEEE division
+    const float divisor = scale > 0.0f ? scale : 1.0f;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float r = rintf(v[e] / divisor);               // IEEE division, ties to even
+        r = fminf(127.0f, fmaxf(-127.0f, r));
+        packed[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+    }
+    *reinterpret_cast<uint2*>(q + row * k + g * 128 + l * 8) = make_uint2(packed[0], packed[1]);
+    if (l == 0) xs[row * groups + g] = scale;
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_q(const void* x, int64_t row_stride, int64_t m, int64_t k, int8_t* q,
+                           float* xs, hipStream_t stream) {
+    const int64_t total = m * (k / 128);
+    const int64_t blocks = (total + 15) / 16;
+    clear_stale_error();
+    hipLaunchKernelGGL((quantize_kernel<DT, VEC>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       row_stride, k, total, q, xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,
+                           int8_t* q, float* xs, hipStream_t stream) {
+    const int esize = dtype == 2 ? 4 : 2;
+    const bool vec = ((uintptr_t)x % 16 == 0) && ((row_stride * esize) % 16 == 0);
+    if (dtype == 0) return vec ? launch_q<0, true>(x, row_stride, m, k, q, xs, stream)
+                               : launch_q<0, false>(x, row_stride, m, k, q, xs, stream);
+    if (dtype == 1) return vec ? launch_q<1, true>(x, row_stride, m, k, q, xs, stream)
+                               : launch_q<1, false>(x, row_stride, m, k, q, xs, stream);
+    return vec ? launch_q<2, true>(x, row_stride, m, k, q, xs, stream)
+               : launch_q<2, false>(x, row_stride, m, k, q, xs, stream);
+}
+
+// ------------------------------------------------------------------ prepare
+// One thread per 34-byte raw block: byte loads (raw rows may sit at any
+// alignment), two 16-byte stores into the code plane, one 2-byte store into
+// the scale plane.  Values are copied unchanged (page "Baseline and the
+// integer breakthrough", "Separate the codes from their scales").
+__global__ __launch_bounds__(256) void prepare_kernel(const uint8_t* __restrict__ raw, int64_t stride,
+                                                      int64_t n, int64_t groups, int64_t total,
+                                                      uint8_t* __restrict__ planes) {
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= total) return;
+    const int64_t row = id / groups;
+    const int64_t g = id - row * groups;
+    const uint8_t* b = raw + row * stride + g * 34;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        w[i] = (uint32_t)b[2 + 4 * i] | ((uint32_t)b[3 + 4 * i] << 8) | ((uint32_t)b[4 + 4 * i] << 16) |
+               ((uint32_t)b[5 + 4 * i] << 24);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(planes + row * groups * 32 + g * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    uint16_t* scale_plane = reinterpret_cast<uint16_t*>(planes + n * groups * 32);
+    scale_plane[row * groups + g] = (uint16_t)(b[0] | (b[1] << 8));
+}
+
+hipError_t launch_prepare(const uint8_t* raw, int64_t stride, int64_t n, int64_t k, uint8_t* planes,
+                          hipStream_t stream) {
+    const int64_t groups = k / 128;
+    const int64_t total = n * groups;
+    const int64_t blocks = (total + 255) / 256;
+    clear_stale_error();
+    hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, raw, stride, n,
+                       groups, total, planes);
+    return hipGetLastError();
+}
+
+}  // namespace pq2

@@ -1,0 +1,141 @@
+/*
+ * pq2.h -- C ABI of the MI355X (gfx950) library for the packed-ternary
+ * weight ("PQ2") x group-128 INT8 activation matmul.
+ *
+ * The method (pages "Kernel experiments: recorded evidence" and "Baseline and
+ * the integer breakthrough", series "Making a ternary reasoning model fast in
+ * vLLM"):
+ *   w[n][k]  = (c[n][k] - 1) * ws[n][k/128]   c in 0..3 (2-bit code), ws fp16
+ *   xs[m][g] = max_{i in g} |x[m][i]| / 127    (FP32, one correctly rounded division)
+ *   q[m][i]  = clamp(round_half_even(x[m][i] / xs[m][g]), -127, 127)   (divide by 1 if xs == 0)
+ *   y[m][n]  = sum_g float(sum_{i in g} q[m][i] * (c[n][i] - 1)) * xs[m][g] * ws[n][g]
+ * The per-group integer dot product is exact; each output sums one FP32 term
+ * per group.
+ *
+ * Conventions for every entry point
+ *  - Data pointers are DEVICE pointers on the current HIP device; the caller
+ *    allocates and owns every buffer.  The library keeps no reference to any
+ *    argument after the call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it; nothing synchronises the host.
+ *  - Arguments are validated on the host BEFORE any HIP call.  A bad argument
+ *    returns a status and enqueues nothing.  The library never aborts.
+ *  - Values: NaN/Inf activations are unsupported (results are unspecified);
+ *    FP32 subnormals are kept (gradual underflow), as on the CPU.
+ *
+ * Layouts
+ *  - Raw PQ2 rows: row n starts at raw + n*raw_row_stride_bytes and holds
+ *    k/128 blocks of 34 bytes: bytes 0-1 the block's fp16 scale (IEEE
+ *    binary16, little-endian), bytes 2..33 the 32 code bytes.  Weight 4b+s of
+ *    the block is bits 2s..2s+1 of code byte b (lowest bits first); code c
+ *    stands for c-1 (page "Kernel experiments: recorded evidence", section A,
+ *    Diagram 1 and Tests 1-2).
+ *  - Prepared planes (layout version 1): ONE allocation of n*(k/128)*34
+ *    bytes: the code plane [n][k/4] (row*k/4 + block*32 + byte) followed by
+ *    the fp16 scale plane [n][k/128] starting at byte n*k/4 (page "Baseline
+ *    and the integer breakthrough", section "Separate the codes from their
+ *    scales"; "Kernel experiments", Test 4).  Same values, other addresses.
+ *  - Activations x: [m][k] with a row stride in elements; bf16, fp16 or fp32.
+ *  - q: int8 [m][k] contiguous (row stride k).  xs: float [m][k/128].
+ *  - y: float [m][n] contiguous (row stride n).
+ */
+#ifndef PQ2_H
+#define PQ2_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+    PQ2_OK = 0,
+    PQ2_EINVAL = 1,   /* null pointer, unknown dtype, overlapping buffers      */
+    PQ2_ESHAPE = 2,   /* k % 128 != 0, m/n/k out of range, raw stride too small */
+    PQ2_EALIGN = 3,   /* a pointer or stride breaks the alignment stated below */
+    PQ2_ELAUNCH = 4,  /* the HIP runtime reported an error for a launch        */
+    PQ2_EDEVICE = 5   /* the current device is not a gfx950 GPU                */
+};
+
+/* Activation element types for pq2_quantize_act_i8. */
+enum { PQ2_BF16 = 0, PQ2_F16 = 1, PQ2_F32 = 2 };
+
+/* Limits (inclusive). */
+#define PQ2_MAX_SMALL_M 16
+#define PQ2_MAX_K 65536
+
+/* Version of the prepared-plane layout the matmul entry points read: 1 =
+ * code plane [n][k/4] followed by the fp16 scale plane [n][k/128].  A layout
+ * switch must change what callers key compiled graphs on (page "Baseline and
+ * the integer breakthrough", "Separate the codes from their scales": the
+ * cache-key bug). */
+int pq2_layout_version(void);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* pq2_status_str(int status);
+
+/* Name of the HIP runtime error behind the last PQ2_ELAUNCH returned on the
+ * calling thread ("hipSuccess" if the last launch succeeded); static storage. */
+const char* pq2_last_hip_error(void);
+
+/* Raw PQ2 rows -> prepared planes.  One-time weight preparation, outside
+ * any timed loop (page "Kernel experiments", Tests 1 and 4).
+ *   raw     device, n rows of raw_row_stride_bytes >= (k/128)*34; any alignment.
+ *   planes  device, n*(k/128)*34 bytes, 16-byte aligned; must not overlap raw.
+ * Errors: EINVAL (null, overlap), ESHAPE (k%128, n<1, stride too small),
+ *         EALIGN (planes not 16-byte aligned), ELAUNCH, EDEVICE. */
+int pq2_prepare_planes(const void* raw, int64_t raw_row_stride_bytes, int64_t n, int64_t k,
+                       void* planes, void* stream);
+
+/* Group-128 INT8 activation quantisation, bit-exact with the definition
+ * above (page "Baseline and the integer breakthrough", "Calculate with small
+ * integers" step 1; page "Kernel experiments", Test 6 quantizer).
+ *   x       device, dtype PQ2_BF16 / PQ2_F16 / PQ2_F32, m rows of
+ *           x_row_stride_elems >= k elements; element-aligned.
+ *   q       device int8 [m][k], 8-byte aligned.   xs  device float [m][k/128], 4-byte aligned.
+ * Errors: EINVAL (null, dtype), ESHAPE (m<1, k<128, k%128, k > PQ2_MAX_K,
+ *         stride < k), EALIGN, ELAUNCH, EDEVICE. */
+int pq2_quantize_act_i8(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
+                        int8_t* q, float* xs, void* stream);
+
+/* Decode / small-batch verification matmul for 1 <= m <= 16 activation
+ * columns: y = the definition above, from prepared planes (page "Baseline
+ * and the integer breakthrough", "Calculate with small integers" steps 2-4;
+ * page "Kernel experiments", section B, Test 6 DP4A GEMV).  Each output is
+ * the FP32 sum of k/128 group terms float(dot)*xs*ws, each group's integer
+ * dot product formed exactly before it is scaled; the summation order does
+ * not depend on m (batch-invariant).
+ *   q       device int8 [m][k], 16-byte aligned.   xs  device float [m][k/128], 4-byte aligned.
+ *   planes  device prepared planes (layout version 1), 16-byte aligned.
+ *   y       device float [m][n], 4-byte aligned; fully overwritten.
+ * Errors: EINVAL (null), ESHAPE (m outside 1..16, n<1, k<128, k%128,
+ *         k > PQ2_MAX_K), EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
+                       int64_t k, float* y, void* stream);
+
+/* Prefill matmul on the INT8 matrix cores (MFMA) for any m >= 1 (tuned for
+ * m >= 128): same definition and output as pq2_matmul_small_m (page
+ * "Baseline and the integer breakthrough", "Use matrix hardware for
+ * prefill"; page "Kernel experiments", Tests 2 and 7).  Argument rules as
+ * for pq2_matmul_small_m, except that 1 <= m <= 65535*128.
+ * Errors: EINVAL, ESHAPE, EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
+                       int64_t k, float* y, void* stream);
+
+/* Tuning hook for the small-m matmul (benchmarks and tests only; same
+ * arguments and result as pq2_matmul_small_m).  rows_per_lane in {1,2,4},
+ * max_waves in 1..8 (waves that split k inside one workgroup), decode 1 =
+ * add/XOR expansion to signed bytes, 2 = masked code planes with the
+ * per-group -sum(q) correction (both give the same exact integer dot); 0 for
+ * any of them picks the library's default.  Errors as pq2_matmul_small_m,
+ * plus EINVAL for an unsupported setting. */
+int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
+                             int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
+                             int decode, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQ2_H */

@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/pq2.h declares, and rejects bad arguments on the host before any HIP
+call (every case below fails validation, so nothing is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pq2.h")
+
+import gemm_int8_act_amd as pq2  # noqa: E402
+
+OK, EINVAL, ESHAPE, EALIGN = pq2.PQ2_OK, pq2.PQ2_EINVAL, pq2.PQ2_ESHAPE, pq2.PQ2_EALIGN
+
+# Fake device addresses: never dereferenced, because validation fails first.
+A = 0x7F0000000000          # 4 KiB aligned
+B = 0x7F0100000000
+C = 0x7F0200000000
+D = 0x7F0300000000
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pq2_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_exported():
+    names = _declared_symbols()
+    assert len(names) == 8
+    lib = ctypes.CDLL(pq2.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(pq2.EXPORTED)
+
+
+def test_layout_version_and_status_strings():
+    assert pq2.pq2_layout_version() == 1
+    for s in range(6):
+        assert pq2.pq2_status_str(s)
+    assert pq2.pq2_status_str(99) == "unknown status"
+    assert pq2.pq2_last_hip_error() == "hipSuccess"
+
+
+def test_prepare_validation():
+    f = pq2.lib.pq2_prepare_planes
+    assert f(None, 34, 4, 128, B, None) == EINVAL
+    assert f(A, 34, 4, 128, None, None) == EINVAL
+    assert f(A, 34, 0, 128, B, None) == ESHAPE
+    assert f(A, 34, 4, 100, B, None) == ESHAPE
+    assert f(A, 34, 4, 0, B, None) == ESHAPE
+    assert f(A, 33, 4, 128, B, None) == ESHAPE          # row stride below 34 bytes per block
+    assert f(A, 34 * 2, 4, 384, B, None) == ESHAPE
+    assert f(A, 34, 4, 128, B + 8, None) == EALIGN     # planes not 16-byte aligned
+    assert f(A, 34, 4, 128, A + 64, None) == EINVAL    # planes overlap raw
+
+
+def test_quantize_validation():
+    f = pq2.lib.pq2_quantize_act_i8
+    assert f(None, 0, 128, 1, 128, B, C, None) == EINVAL
+    assert f(A, 3, 128, 1, 128, B, C, None) == EINVAL    # unknown dtype
+    assert f(A, 0, 128, 0, 128, B, C, None) == ESHAPE
+    assert f(A, 0, 128, 1, 96, B, C, None) == ESHAPE
+    assert f(A, 0, 100, 1, 128, B, C, None) == ESHAPE     # stride < k
+    assert f(A, 0, 1 << 17, 1, 1 << 17, B, C, None) == ESHAPE  # k beyond the limit
+    assert f(A + 1, 0, 128, 1, 128, B, C, None) == EALIGN  # bf16 not 2-byte aligned
+    assert f(A + 2, 2, 128, 1, 128, B, C, None) == EALIGN  # f32 not 4-byte aligned
+    assert f(A, 0, 128, 1, 128, B + 4, C, None) == EALIGN  # q not 8-byte aligned
+    assert f(A, 0, 128, 1, 128, B, C + 2, None) == EALIGN
+    assert f(A, 0, 128, 2, 128, A + 16, C, None) == EINVAL  # q overlaps x
+
+
+@pytest.mark.parametrize("name", ["pq2_matmul_small_m", "pq2_matmul_prefill"])
+def test_matmul_validation(name):
+    f = getattr(pq2.lib, name)
+    assert f(None, B, C, 1, 8, 128, D, None) == EINVAL
+    assert f(A, None, C, 1, 8, 128, D, None) == EINVAL
+    assert f(A, B, None, 1, 8, 128, D, None) == EINVAL
+    assert f(A, B, C, 1, 8, 128, None, None) == EINVAL
+    assert f(A, B, C, 0, 8, 128, D, None) == ESHAPE
+    assert f(A, B, C, 1, 0, 128, D, None) == ESHAPE
+    assert f(A, B, C, 1, 8, 200, D, None) == ESHAPE
+    assert f(A, B, C, 1, 8, 1 << 17, D, None) == ESHAPE
+    assert f(A + 8, B, C, 1, 8, 128, D, None) == EALIGN   # q 16-byte alignment
+    assert f(A, B + 2, C, 1, 8, 128, D, None) == EALIGN
+    assert f(A, B, C + 8, 1, 8, 128, D, None) == EALIGN   # planes 16-byte alignment
+    assert f(A, B, C, 1, 8, 128, D + 2, None) == EALIGN
+    assert f(A, B, C, 1, 8, 128, C + 16, None) == EINVAL  # y overlaps planes
+
+
+def test_small_m_column_limit_and_tuning_validation():
+    f = pq2.lib.pq2_matmul_small_m
+    assert f(A, B, C, 17, 8, 128, D, None) == ESHAPE
+    t = pq2.lib.pq2_matmul_small_m_tuned
+    assert t(A, B, C, 1, 8, 128, D, 3, 0, 0, None) == EINVAL   # rows per lane
+    assert t(A, B, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL   # waves
+    assert t(A, B, C, 1, 8, 128, D, 0, 0, 5, None) == EINVAL   # decode
+    assert t(A, B, C, 17, 8, 128, D, 1, 1, 1, None) == ESHAPE
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros((1, 128), dtype=torch.int8)
+    xs = torch.zeros((1, 1), dtype=torch.float32)
+    planes = torch.zeros(34, dtype=torch.uint8)
+    y = torch.zeros((1, 1), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        pq2.pq2_matmul_small_m(q, xs, planes, y)
+
+
+@pytest.mark.parametrize("order", ["package_first", "torch_first"])
+def test_single_hip_runtime_whatever_the_import_order(order):
+    """Regression: importing the package before torch used to map a second
+    HIP runtime (the system one) next to torch's, and kernels launched through
+    it on torch's memory crashed the process."""
+    import subprocess
+    import sys
+    first, second = ("gemm_int8_act_amd", "torch") if order == "package_first" else ("torch", "gemm_int8_act_amd")
+    code = (f"import {first}; import {second}; "
+            "maps = open('/proc/self/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"

@@ -1,0 +1,319 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: the quantised activations and scales and the prepared planes are
+bit-exact; every output y satisfies |y_gpu - y_ref| <= 1e-5 * sum_g
+|xs*ws*dot_g| + 1e-6 (the oracle returns that bound per output).  Outputs are
+NaN-poisoned before every call, so an unwritten element fails.
+
+Sizes: full element-by-element comparisons on shapes that span several
+workgroup tiles with ragged row/column/group tails; at the full workload
+sizes (the launch configuration the benchmark times) sampled outputs against
+the oracle plus exact properties that hold at any size (negated activations
+give exactly negated outputs, doubled weight scales exactly doubled ones,
+one column does not depend on the others).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@functools.lru_cache(maxsize=None)
+def _pq2():
+    import gemm_int8_act_amd as pq2
+    return pq2
+
+
+# ------------------------------------------------------------------ helpers
+def gpu_planes(raw_np, n, k):
+    pq2 = _pq2()
+    raw = torch.from_numpy(np.ascontiguousarray(raw_np)).to(DEV)
+    planes = torch.empty(n * (k // 128) * 34, dtype=torch.uint8, device=DEV)
+    pq2.pq2_prepare_planes(raw, n, k, planes)
+    return planes
+
+
+def gpu_quantize(x, k=None):
+    pq2 = _pq2()
+    m = x.shape[0]
+    k = x.shape[1] if k is None else k
+    q = torch.empty((m, k), dtype=torch.int8, device=DEV)
+    xs = torch.full((m, k // 128), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_quantize_act_i8(x, q, xs)
+    return q, xs
+
+
+def gpu_matmul(fn, q, xs, planes, n, **kw):
+    m = q.shape[0]
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    fn(q, xs, planes, y, **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def assert_within(y_gpu, y_ref, bound, what):
+    y_gpu = y_gpu.astype(np.float64)
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output (unwritten element?)"
+    excess = np.abs(y_gpu - y_ref) - bound
+    worst = np.unravel_index(np.argmax(excess), excess.shape)
+    assert excess[worst] <= 0, (f"{what}: |diff| {abs(y_gpu[worst] - y_ref[worst]):.3e} > bound "
+                                f"{bound[worst]:.3e} at {worst}")
+
+
+def quantise_both(x_cpu, k=None):
+    """Quantise on the GPU and in the oracle; require bit equality; return
+    the (device) q, xs and the oracle's numpy copies."""
+    qo, xso = oracle.quantize_act_i8(workloads.bf16_bits(x_cpu) if x_cpu.dtype == torch.bfloat16
+                                     else x_cpu.numpy(), "bf16" if x_cpu.dtype == torch.bfloat16 else "f32", k=k)
+    q, xs = gpu_quantize(x_cpu.to(DEV), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), qo), "q differs from the oracle"
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), xso.view(np.uint32)), "xs differs from the oracle"
+    return q, xs, qo, xso
+
+
+@functools.lru_cache(maxsize=None)
+def workload_case(name):
+    w = workloads.WORKLOADS[name]
+    raw, x = workloads.workload_inputs(name)
+    return w, raw, x
+
+
+# ------------------------------------------------------------------ quantiser
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_quantize_bit_exact_workloads(name):
+    w, _, x = workload_case(name)
+    announce(f"quantize {name} m={x.shape[0]} k={w.k}")
+    quantise_both(x)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32", "bf16"])
+@pytest.mark.parametrize("m,k,stride_pad", [(1, 128, 0), (3, 640, 5), (7, 5120, 8), (33, 1024, 3)])
+def test_quantize_dtypes_and_strides(dtype, m, k, stride_pad):
+    announce(f"quantize dtype={dtype} m={m} k={k} pad={stride_pad}")
+    x = workloads.make_activations(m, k + stride_pad, 70 + m, "laplace").float() * 3.0
+    tdt = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    xt = x.to(tdt)
+    if dtype == "f32":
+        bits = xt.numpy()
+    else:
+        bits = xt.view(torch.int16).numpy().view(np.uint16)
+    qo, xso = oracle.quantize_act_i8(bits, dtype, k=k)
+    # Row stride k + pad (elements): unaligned rows take the kernel's scalar path.
+    q, xs = gpu_quantize(xt.to(DEV), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), xso.view(np.uint32))
+
+
+def test_quantize_special_groups():
+    """Zero group, subnormal scale, exact ties, +-amax."""
+    announce("quantize special groups")
+    g = np.zeros((1, 128 * 4), dtype=np.float32)
+    g[0, 128:132] = [2.0 ** -130, -3 * 2.0 ** -131, 2.0 ** -126, 5 * 2.0 ** -133]
+    g[0, 256] = 127.0
+    g[0, 257:263] = [0.5, 1.5, 2.5, -2.5, 126.5, -0.5]
+    g[0, 384:512] = np.arange(-64, 64) * 0.37
+    x = torch.tensor(g).to(torch.bfloat16)
+    q, xs, qo, xso = quantise_both(x)
+    assert xso[0, 0] == 0.0 and xso[0, 2] == 1.0
+
+
+# ------------------------------------------------------------------ prepare
+@pytest.mark.parametrize("n,k,pad", [(1, 128, 0), (37, 640, 3), (256, 5120, 0), (19, 17408, 6)])
+def test_prepare_byte_exact(n, k, pad):
+    announce(f"prepare n={n} k={k} pad={pad}")
+    raw = workloads.make_raw_weights(n, k, seed=80 + n, codes="ternary+3", row_pad=pad)
+    planes = gpu_planes(raw, n, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(planes.cpu().numpy(), oracle.prepare_planes(raw, n, k))
+
+
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_prepare_byte_exact_workloads(name):
+    w, raw, _ = workload_case(name)
+    announce(f"prepare workload {name}")
+    planes = gpu_planes(raw, w.n, w.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(planes.cpu().numpy(), oracle.prepare_planes(raw, w.n, w.k))
+
+
+# ------------------------------------------------------------------ small m: full comparisons
+SMALL_SHAPES = [
+    # (m, n, k): several row tiles, ragged row tail, partial last segment of groups
+    (1, 1024, 512), (1, 1, 128), (2, 333, 640), (3, 97, 1152), (4, 1000, 5120),
+    (5, 77, 2176), (8, 130, 384), (9, 61, 1024), (16, 40, 17408), (12, 300, 3072),
+    (6, 513, 9216), (4, 64, 34816), (2, 24, 65536), (1, 4096, 16384),
+]
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
+def test_small_m_full(m, n, k):
+    announce(f"small_m full m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=90 + m + n, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 91 + k, "normal+outliers")
+    q, xs, qo, xso = quantise_both(x)
+    planes = gpu_planes(raw, n, k)
+    y = gpu_matmul(_pq2().pq2_matmul_small_m, q, xs, planes, n)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    assert_within(y, y_ref, bound, f"small_m m={m} n={n} k={k}")
+
+
+def test_small_m_tiny_workload():
+    w, raw, x = workload_case("tiny")
+    announce("small_m tiny workload")
+    q, xs, qo, xso = quantise_both(x)
+    planes = gpu_planes(raw, w.n, w.k)
+    y = gpu_matmul(_pq2().pq2_matmul_small_m, q, xs, planes, w.n)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, w.n, w.k)
+    assert_within(y, y_ref, bound, "tiny")
+
+
+def test_small_m_zero_activations():
+    announce("small_m zero activations")
+    n, k = 100, 1024
+    raw = workloads.make_raw_weights(n, k, seed=5)
+    x = torch.zeros((3, k), dtype=torch.bfloat16)
+    q, xs, _, _ = quantise_both(x)
+    y = gpu_matmul(_pq2().pq2_matmul_small_m, q, xs, gpu_planes(raw, n, k), n)
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("rows,waves", [(1, 1), (1, 8), (2, 3), (2, 8), (4, 2), (4, 8)])
+def test_small_m_tuning_variants(rows, waves):
+    """Every rows-per-lane / k-split setting is within the bound; the two
+    decodes give bitwise identical outputs (same exact int dot, same order)."""
+    pq2 = _pq2()
+    m, n, k = 4, 200, 5248
+    announce(f"small_m variants rows={rows} waves={waves}")
+    raw = workloads.make_raw_weights(n, k, seed=7, codes="ternary+3")
+    x = workloads.make_activations(m, k, 8, "laplace")
+    q, xs, qo, xso = quantise_both(x)
+    planes = gpu_planes(raw, n, k)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    outs = []
+    for dec in (1, 2):
+        y = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows_per_lane=rows,
+                       max_waves=waves, decode=dec)
+        assert_within(y, y_ref, bound, f"rows={rows} waves={waves} decode={dec}")
+        outs.append(y)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+# ------------------------------------------------------------------ small m: full workload sizes
+def _sample_indices(m, n, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([[0, 1, n // 2, n - 2, n - 1], rng.integers(0, n, count)])
+    mi = np.repeat(np.arange(m), len(rows))
+    ni = np.tile(rows, m)
+    return mi, ni
+
+
+@pytest.mark.parametrize("name", ["qkv", "up", "down"])
+def test_small_m_workloads_sampled(name):
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    planes = gpu_planes(raw, w.n, w.k)
+    ys = {}
+    for m in w.ms:
+        announce(f"small_m workload {name} m={m}")
+        q, xs, qo, xso = quantise_both(x[:m].contiguous())
+        y = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, w.n)
+        mi, ni = _sample_indices(m, w.n, 400, seed=m)
+        y_ref, bound = oracle.matmul_raw_sample(qo, xso, raw, w.n, w.k, mi, ni)
+        assert_within(y[mi, ni], y_ref, bound, f"{name} m={m}")
+        assert np.all(np.isfinite(y))
+        ys[m] = y
+    # Batch invariance: column c is bit-identical whatever the number of columns.
+    mmax = max(w.ms)
+    for m, y in ys.items():
+        assert np.array_equal(y.view(np.uint32), ys[mmax][:m].view(np.uint32)), f"batch variance at m={m}"
+
+
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_small_m_workloads_exact_properties(name):
+    """At full size: determinism, exact negation, exact scale doubling."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    m = 4
+    announce(f"small_m properties {name}")
+    planes = gpu_planes(raw, w.n, w.k)
+    q, xs = gpu_quantize(x[:m].contiguous().to(DEV))
+    y1 = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, w.n)
+    y2 = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, w.n)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+    yneg = gpu_matmul(pq2.pq2_matmul_small_m, -q, xs, planes, w.n)
+    assert np.array_equal(yneg, -y1), "negated activations must negate outputs exactly"
+    planes2 = planes.clone()
+    sc = planes2[w.n * w.k // 4:].view(torch.float16)
+    sc.mul_(2.0)
+    y2x = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes2, w.n)
+    assert np.array_equal(y2x, 2.0 * y1), "doubled weight scales must double outputs exactly"
+
+
+# ------------------------------------------------------------------ prefill
+PREFILL_SHAPES = [(1, 64, 128), (5, 200, 640), (128, 128, 1024), (130, 257, 384), (300, 96, 5120),
+                  (257, 513, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", PREFILL_SHAPES)
+def test_prefill_full(m, n, k):
+    announce(f"prefill full m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=110 + n, codes="ternary+3", row_pad=1)
+    x = workloads.make_activations(m, k, 111 + m, "normal")
+    q, xs, qo, xso = quantise_both(x)
+    y = gpu_matmul(_pq2().pq2_matmul_prefill, q, xs, gpu_planes(raw, n, k), n)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    assert_within(y, y_ref, bound, f"prefill m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("name", ["prefill_gate", "prefill_up"])
+def test_prefill_workloads_sampled(name):
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    planes = gpu_planes(raw, w.n, w.k)
+    for m in w.ms:
+        announce(f"prefill workload {name} m={m}")
+        q, xs, qo, xso = quantise_both(x[:m].contiguous())
+        y = gpu_matmul(pq2.pq2_matmul_prefill, q, xs, planes, w.n)
+        assert np.all(np.isfinite(y))
+        rng = np.random.default_rng(m)
+        mi = np.concatenate([[0, m - 1, 0, m - 1], rng.integers(0, m, 1500)])
+        ni = np.concatenate([[0, 0, w.n - 1, w.n - 1], rng.integers(0, w.n, 1500)])
+        y_ref, bound = oracle.matmul_raw_sample(qo, xso, raw, w.n, w.k, mi, ni)
+        assert_within(y[mi, ni], y_ref, bound, f"{name} m={m}")
+        # Exact property at full size: a column does not depend on the others.
+        if m == w.ms[0]:
+            y_first = gpu_matmul(pq2.pq2_matmul_prefill, q[:1].contiguous(), xs[:1].contiguous(), planes, w.n)
+            assert np.all(np.isfinite(y_first))
+            mi1 = np.zeros(64, dtype=np.int64)
+            ni1 = np.arange(0, w.n, w.n // 64)[:64]
+            y1_ref, b1 = oracle.matmul_raw_sample(qo, xso, raw, w.n, w.k, mi1, ni1)
+            assert_within(y_first[0, ni1], y1_ref, b1, f"{name} m=1")
+
+
+def test_prefill_matches_small_m():
+    """Both paths compute the same definition: agree within twice the bound."""
+    pq2 = _pq2()
+    m, n, k = 16, 300, 5120
+    announce("prefill vs small_m")
+    raw = workloads.make_raw_weights(n, k, seed=3)
+    x = workloads.make_activations(m, k, 4, "normal")
+    q, xs, qo, xso = quantise_both(x)
+    planes = gpu_planes(raw, n, k)
+    ya = gpu_matmul(pq2.pq2_matmul_prefill, q, xs, planes, n)
+    yb = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, n)
+    _, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    assert np.all(np.abs(ya.astype(np.float64) - yb) <= 2 * bound)
