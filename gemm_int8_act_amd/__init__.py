@@ -33,6 +33,9 @@ EXPORTED = (
     "pq2_matmul_small_m",
     "pq2_matmul_prefill",
     "pq2_matmul_small_m_tuned",
+    "pq2_quantize_act_i8_planes",
+    "pq2_matmul_small_m_planes",
+    "pq2_matmul_small_m_planes_tuned",
 )
 
 
@@ -78,6 +81,12 @@ def _load_library():
     lib.pq2_matmul_prefill.restype = i32
     lib.pq2_matmul_small_m_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, i32, p]
     lib.pq2_matmul_small_m_tuned.restype = i32
+    lib.pq2_quantize_act_i8_planes.argtypes = [p, i32, i64, i64, i64, p, p, p, p]
+    lib.pq2_quantize_act_i8_planes.restype = i32
+    lib.pq2_matmul_small_m_planes.argtypes = [p, p, p, p, i64, i64, i64, p, p]
+    lib.pq2_matmul_small_m_planes.restype = i32
+    lib.pq2_matmul_small_m_planes_tuned.argtypes = [p, p, p, p, i64, i64, i64, p, i32, i32, p]
+    lib.pq2_matmul_small_m_planes_tuned.restype = i32
     return lib
 
 
@@ -191,3 +200,41 @@ def pq2_matmul_small_m_tuned(q, xs, planes, y, rows_per_lane=0, max_waves=0, dec
 def pq2_matmul_prefill(q, xs, planes, y, stream=None) -> None:
     """y[m][n] on the INT8 matrix cores (any m >= 1)."""
     _check(lib.pq2_matmul_prefill(*_matmul_args(q, xs, planes, y), _stream(stream)), "pq2_matmul_prefill")
+
+
+def pq2_quantize_act_i8_planes(x, qp, xs, qsum, stream=None) -> None:
+    """As pq2_quantize_act_i8, writing q in code-plane order (qp, int8
+    [m][k]) plus the int32 group sums qsum [m][k/128]."""
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if (qp.dtype != torch.int8 or xs.dtype != torch.float32 or qsum.dtype != torch.int32
+            or not qp.is_contiguous() or not xs.is_contiguous() or not qsum.is_contiguous()):
+        raise ValueError("qp contiguous int8, xs contiguous float32, qsum contiguous int32 expected")
+    m, k = qp.shape
+    if x.shape[0] != m or x.shape[1] < k or xs.numel() != m * (k // 128) or qsum.numel() != m * (k // 128):
+        raise ValueError("shape mismatch between x, qp, xs and qsum")
+    _check(lib.pq2_quantize_act_i8_planes(_dev_ptr(x, "x"), _dtype_code(x), x.stride(0), m, k,
+                                          _dev_ptr(qp, "qp"), _dev_ptr(xs, "xs"), _dev_ptr(qsum, "qsum"),
+                                          _stream(stream)), "pq2_quantize_act_i8_planes")
+
+
+def _planes_args(qp, xs, qsum, planes, y):
+    import torch
+    if qsum.dtype != torch.int32 or not qsum.is_contiguous():
+        raise ValueError("qsum must be contiguous int32")
+    qa, xa, pa, m, n, k, ya = _matmul_args(qp, xs, planes, y)
+    if qsum.numel() != m * (k // 128):
+        raise ValueError("qsum must hold m*k/128 group sums")
+    return (qa, xa, _dev_ptr(qsum, "qsum"), pa, m, n, k, ya)
+
+
+def pq2_matmul_small_m_planes(qp, xs, qsum, planes, y, stream=None) -> None:
+    """pq2_matmul_small_m from the plane-order quantiser's outputs."""
+    _check(lib.pq2_matmul_small_m_planes(*_planes_args(qp, xs, qsum, planes, y), _stream(stream)),
+           "pq2_matmul_small_m_planes")
+
+
+def pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, y, rows_per_lane=0, max_waves=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_planes_tuned(*_planes_args(qp, xs, qsum, planes, y), rows_per_lane,
+                                               max_waves, _stream(stream)), "pq2_matmul_small_m_planes_tuned")

@@ -111,6 +111,47 @@ int pq2_quantize_act_i8(const void* x, int dtype, int64_t x_row_stride_elems, in
     return launch_status(pq2::launch_quantize(x, dtype, x_row_stride_elems, m, k, q, xs, (hipStream_t)stream));
 }
 
+int pq2_quantize_act_i8_planes(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
+                               int8_t* qp, float* xs, int32_t* qsum, void* stream) {
+    if (!x || !qp || !xs || !qsum) return PQ2_EINVAL;
+    if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
+    if (m < 1 || m > ((int64_t)1 << 31)) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (x_row_stride_elems < k) return PQ2_ESHAPE;
+    const int esize = dtype == PQ2_F32 ? 4 : 2;
+    if (!aligned(x, esize) || !aligned(qp, 16) || !aligned(xs, 4) || !aligned(qsum, 4)) return PQ2_EALIGN;
+    const size_t xbytes = ((size_t)(m - 1) * x_row_stride_elems + k) * esize;
+    const size_t qbytes = (size_t)m * k, gbytes = (size_t)m * (k / kGroup) * 4;
+    if (overlap(qp, qbytes, x, xbytes) || overlap(xs, gbytes, x, xbytes) || overlap(qsum, gbytes, x, xbytes) ||
+        overlap(qp, qbytes, xs, gbytes) || overlap(qp, qbytes, qsum, gbytes) || overlap(xs, gbytes, qsum, gbytes))
+        return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(
+        pq2::launch_quantize_planes(x, dtype, x_row_stride_elems, m, k, qp, xs, qsum, (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
+                                    int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane,
+                                    int max_waves, void* stream) {
+    if (!qsum) return PQ2_EINVAL;
+    if (int rc = check_matmul_args(qp, xs, planes, m, n, k, y, PQ2_MAX_SMALL_M)) return rc;
+    if (!aligned(qsum, 4)) return PQ2_EALIGN;
+    if (overlap(y, (size_t)m * n * 4, qsum, (size_t)m * (k / kGroup) * 4)) return PQ2_EINVAL;
+    pq2::SmallMConfig cfg = pq2::default_planes_config(m, n, k);
+    if (rows_per_lane) cfg.rows_per_lane = rows_per_lane;
+    if (max_waves) cfg.max_waves = max_waves;
+    if ((cfg.rows_per_lane != 1 && cfg.rows_per_lane != 2) || cfg.max_waves < 1 || cfg.max_waves > 8)
+        return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m_planes(qp, xs, qsum, static_cast<const uint8_t*>(planes), m, n, k, y,
+                                                    cfg, (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
+                              int64_t m, int64_t n, int64_t k, float* y, void* stream) {
+    return pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, m, n, k, y, 0, 0, stream);
+}
+
 int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
                              int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
                              int decode, void* stream) {

@@ -109,6 +109,32 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resources (gfx9 descriptor, stride 0): a load whose byte offset
+// lies at or beyond num_records returns zero instead of touching memory, so
+// padded rows, groups and columns need no branch around their loads.
+constexpr uint32_t kBufferOOB = 0x80000000u;  // an offset past any record count used here
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kAuxNonTemporal = 2;          // cache-policy bit: streamed, not reused
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+template <int AUX = 0>
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

@@ -18,6 +18,9 @@ hipError_t launch_prepare(const uint8_t* raw, int64_t stride, int64_t n, int64_t
 hipError_t launch_quantize(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,
                            int8_t* q, float* xs, hipStream_t stream);
 
+hipError_t launch_quantize_planes(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,
+                                  int8_t* qp, float* xs, int32_t* qsum, hipStream_t stream);
+
 struct SmallMConfig {
     int rows_per_lane;  // 1, 2 or 4
     int max_waves;      // 1..16: waves that split k inside one workgroup
@@ -30,6 +33,12 @@ SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k);
 hipError_t launch_small_m(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
                           int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
                           hipStream_t stream);
+
+SmallMConfig default_planes_config(int64_t m, int64_t n, int64_t k);
+
+hipError_t launch_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const uint8_t* planes,
+                                 int64_t m, int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
+                                 hipStream_t stream);
 
 hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
                           int64_t n, int64_t k, float* y, hipStream_t stream);

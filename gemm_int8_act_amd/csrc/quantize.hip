@@ -110,6 +110,111 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t row_stride, int64_t
                : launch_q<2, false>(x, row_stride, m, k, q, xs, stream);
 }
 
+// ------------------------------------------------------------------ plane order
+// The same quantiser, writing each 16-byte block of q (the activations that
+// meet one code dword, weights 16t..16t+15) as a 4x4 byte transpose:
+// qp[16t + 4s + j] = q[16t + 4j + s], so dword s of the block is the plane-s
+// partner of the code dword (page "Kernel experiments", Test 21 / Diagram 7:
+// plane-order activations), plus qsum[row][group] = the group's sum of q for
+// the -1 code offset.  8 lanes per group, 16 elements (two 16-byte loads for
+// 2-byte types) per lane, 8 groups per wave, 32 groups per 256-thread block.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256) void quantize_planes_kernel(const void* __restrict__ x, int64_t row_stride,
+                                                              int64_t k, int64_t total_groups,
+                                                              int8_t* __restrict__ qp, float* __restrict__ xs,
+                                                              int32_t* __restrict__ qsum) {
+    const int64_t gid = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int t = threadIdx.x & 7;
+    if (gid >= total_groups) return;  // whole 8-lane groups leave together
+    const int64_t groups = k / 128;
+    const int64_t row = gid / groups;
+    const int64_t g = gid - row * groups;
+    const int64_t base = row * row_stride + g * 128 + t * 16;
+
+    float v[16];
+    if constexpr (DT == 2) {
+        const float* xp = static_cast<const float*>(x) + base;
+        if constexpr (VEC) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float4 a = *reinterpret_cast<const float4*>(xp + 4 * h);
+                v[4 * h] = a.x; v[4 * h + 1] = a.y; v[4 * h + 2] = a.z; v[4 * h + 3] = a.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = xp[e];
+        }
+    } else {
+        const uint16_t* xp = static_cast<const uint16_t*>(x) + base;
+        if constexpr (VEC) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint4 w = *reinterpret_cast<const uint4*>(xp + 8 * h);
+                const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[8 * h + 2 * e] = elem_to_float<DT>(words[e] & 0xFFFFu);
+                    v[8 * h + 2 * e + 1] = elem_to_float<DT>(words[e] >> 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = elem_to_float<DT>(xp[e]);
+        }
+    }
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+    amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));  // max over the group's 8 lanes
+
+    const float scale = amax / 127.0f;                 // one IEEE division
+    const float divisor = scale > 0.0f ? scale : 1.0f;
+    uint32_t nat[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float r = rintf(v[e] / divisor);               // IEEE division, ties to even
+        r = fminf(127.0f, fmaxf(-127.0f, r));
+        nat[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+    }
+    const uint4 Q = make_uint4(nat[0], nat[1], nat[2], nat[3]);
+    int s = dot4(Q.x, 0x01010101u, 0);
+    s = dot4(Q.y, 0x01010101u, s);
+    s = dot4(Q.z, 0x01010101u, s);
+    s = dot4(Q.w, 0x01010101u, s);
+    s = sum8_i(s);
+    *reinterpret_cast<uint4*>(qp + row * k + g * 128 + t * 16) = to_plane_order(Q);
+    if (t == 0) {
+        xs[row * groups + g] = scale;
+        qsum[row * groups + g] = s;
+    }
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_qp(const void* x, int64_t row_stride, int64_t m, int64_t k, int8_t* qp,
+                            float* xs, int32_t* qsum, hipStream_t stream) {
+    const int64_t total = m * (k / 128);
+    const int64_t blocks = (total + 31) / 32;
+    clear_stale_error();
+    hipLaunchKernelGGL((quantize_planes_kernel<DT, VEC>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       row_stride, k, total, qp, xs, qsum);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_planes(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,
+                                  int8_t* qp, float* xs, int32_t* qsum, hipStream_t stream) {
+    const int esize = dtype == 2 ? 4 : 2;
+    const bool vec = ((uintptr_t)x % 16 == 0) && ((row_stride * esize) % 16 == 0);
+    if (dtype == 0) return vec ? launch_qp<0, true>(x, row_stride, m, k, qp, xs, qsum, stream)
+                               : launch_qp<0, false>(x, row_stride, m, k, qp, xs, qsum, stream);
+    if (dtype == 1) return vec ? launch_qp<1, true>(x, row_stride, m, k, qp, xs, qsum, stream)
+                               : launch_qp<1, false>(x, row_stride, m, k, qp, xs, qsum, stream);
+    return vec ? launch_qp<2, true>(x, row_stride, m, k, qp, xs, qsum, stream)
+               : launch_qp<2, false>(x, row_stride, m, k, qp, xs, qsum, stream);
+}
+
 // ------------------------------------------------------------------ prepare
 // One thread per 34-byte raw block: byte loads (raw rows may sit at any
 // alignment), two 16-byte stores into the code plane, one 2-byte store into

@@ -52,23 +52,70 @@ __global__ __launch_bounds__(512) void small_m_kernel(
     float2* slds = reinterpret_cast<float2*>(smem + (size_t)gpad * MC * 128);       // [gpad][MC] {xs, sum q}
     float* red = reinterpret_cast<float*>(smem + (size_t)gpad * MC * 136);          // [W][MC][8R]
 
-    const int nwaves = blockDim.x >> 6;
+    constexpr int RB = kRowSlots * R;  // rows per workgroup
+    const int nthreads = blockDim.x;
+    const int nwaves = nthreads >> 6;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int slot = lane >> 3;
     const int j = lane & 7;
     const int m0 = blockIdx.y * MC;
     const int mcount = min(MC, mtotal - m0);
-    const int row_base = blockIdx.x * (kRowSlots * R);
+    const int row_base = blockIdx.x * RB;
+    const int rows_here = min(RB, n - row_base);
     const int seg_begin = wave * segs_per_wave;
     const int seg_end = min(seg_begin + segs_per_wave, nseg);
-    const int k4 = k >> 2;
+    const uint32_t k4 = (uint32_t)k >> 2;
 
-    // Codes and scales of up to SEGS segments of this wave's rows.  A padded
-    // (row, group) -- past n or past the last group -- loads nothing and
-    // contributes exactly zero (zero codes, zero weight scale).
+    // Buffer resources over exactly the bytes this workgroup may read: a row
+    // past n, a group past k or a column past m reads as zero.
+    const auto code_rs = make_rsrc(codes + (size_t)row_base * k4, (uint32_t)rows_here * k4);
+    const auto scale_rs = make_rsrc(scales + (size_t)row_base * groups, (uint32_t)(rows_here * groups * 2));
+    const auto q_rs = make_rsrc(q + (size_t)m0 * k, (uint32_t)(mcount * k));
+    const auto xs_rs = make_rsrc(xs + (size_t)m0 * groups, (uint32_t)(mcount * groups * 4));
+
+    // Staging items = (group, column, quad t); 8 consecutive threads take the
+    // 8 quads of one (group, column) so its sum of q is an 8-lane reduction.
+    constexpr int QB = 4;  // staging items per thread per batch
+    const int nitems = gpad * MC * 8;
+    uint4 qv[QB];
+    uint32_t xv[QB];
+    auto stage_load = [&](int base_it) {
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+            const int it = base_it + i * nthreads;
+            const int t = it & 7;
+            const int gm = it >> 3;
+            const int m = gm % MC;
+            const int g = gm / MC;
+            const bool ok = it < nitems && m < mcount && g < groups;
+            qv[i] = buf_load16(q_rs, ok ? (uint32_t)(m * k + g * 128 + t * 16) : kBufferOOB);
+            xv[i] = buf_load4(xs_rs, ok ? (uint32_t)((m * groups + g) * 4) : kBufferOOB);
+        }
+    };
+    auto stage_store = [&](int base_it) {
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+            const int it = base_it + i * nthreads;
+            if (it < nitems) {  // uniform over each aligned group of 8 lanes
+                const int t = it & 7;
+                const int gm = it >> 3;
+                const int g = gm / MC;
+                const uint4 Q = qv[i];
+                int tsum = dot4(Q.x, 0x01010101u, 0);
+                tsum = dot4(Q.y, 0x01010101u, tsum);
+                tsum = dot4(Q.z, 0x01010101u, tsum);
+                tsum = dot4(Q.w, 0x01010101u, tsum);
+                tsum = sum8_i(tsum);
+                qlds[(size_t)gm * 8 + (t ^ (g & 7))] = to_plane_order(Q);
+                if (t == 0) slds[gm] = make_float2(__uint_as_float(xv[i]), __int_as_float(tsum));
+            }
+        }
+    };
+
+    // Codes and raw fp16 scales of up to SEGS segments of this wave's rows.
     uint4 cw[SEGS][R][2];
-    float wsf[SEGS][R];
+    uint32_t wsraw[SEGS][R];
     auto load_step = [&](int base) {
 #pragma unroll
         for (int si = 0; si < SEGS; ++si) {
@@ -76,44 +123,25 @@ __global__ __launch_bounds__(512) void small_m_kernel(
             const bool gok = (base + si < seg_end) && (g < groups);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int row = row_base + slot + kRowSlots * r;
-                if (gok && row < n) {
-                    const uint4* p = reinterpret_cast<const uint4*>(codes + (size_t)row * k4 + (size_t)g * 32);
-                    cw[si][r][0] = load_nt(p);
-                    cw[si][r][1] = load_nt(p + 1);
-                    wsf[si][r] = __half2float(__ushort_as_half(scales[(size_t)row * groups + g]));
-                } else {
-                    cw[si][r][0] = make_uint4(0u, 0u, 0u, 0u);
-                    cw[si][r][1] = make_uint4(0u, 0u, 0u, 0u);
-                    wsf[si][r] = 0.0f;
-                }
+                const uint32_t rl = (uint32_t)(slot + kRowSlots * r);
+                const uint32_t off = gok ? rl * k4 + (uint32_t)g * 32u : kBufferOOB;
+                cw[si][r][0] = buf_load16<kAuxNonTemporal>(code_rs, off);
+                cw[si][r][1] = buf_load16<kAuxNonTemporal>(code_rs, off + 16u);
+                wsraw[si][r] = buf_load2(scale_rs, gok ? (rl * groups + g) * 2u : kBufferOOB);
             }
         }
     };
 
-    // 1. Issue the wave's first step of code and scale loads before staging q
-    //    (for k up to nwaves * SEGS * 1024 that is all of its work).
+    // 1. First batch of activation loads (short L2 latency), then every code
+    //    load of this wave's first step (HBM), so both are in flight together
+    //    and staging does not wait for the codes.
+    stage_load(threadIdx.x);
     load_step(seg_begin);
-
     // 2. Stage q in plane order, plus {xs, sum q} per (group, column).
-    //    Item = (g, m, quad t); 8 consecutive threads take the 8 quads of one
-    //    (g, m), so the group sum is an 8-lane DPP reduction.
-    const int nitems = gpad * MC * 8;
-    for (int it = threadIdx.x; it < nitems; it += blockDim.x) {
-        const int t = it & 7;
-        const int gm = it >> 3;
-        const int m = gm % MC;
-        const int g = gm / MC;
-        uint4 Q = make_uint4(0u, 0u, 0u, 0u);
-        const bool ok = (m < mcount) && (g < groups);
-        if (ok) Q = *reinterpret_cast<const uint4*>(q + (size_t)(m0 + m) * k + (size_t)g * 128 + t * 16);
-        int tsum = dot4(Q.x, 0x01010101u, 0);
-        tsum = dot4(Q.y, 0x01010101u, tsum);
-        tsum = dot4(Q.z, 0x01010101u, tsum);
-        tsum = dot4(Q.w, 0x01010101u, tsum);
-        tsum = sum8_i(tsum);
-        qlds[(size_t)gm * 8 + (t ^ (g & 7))] = to_plane_order(Q);
-        if (t == 0) slds[gm] = make_float2(ok ? xs[(size_t)(m0 + m) * groups + g] : 0.0f, __int_as_float(tsum));
+    stage_store(threadIdx.x);
+    for (int b = threadIdx.x + QB * nthreads; b < nitems; b += QB * nthreads) {
+        stage_load(b);
+        stage_store(b);
     }
     __syncthreads();
 
@@ -127,64 +155,66 @@ __global__ __launch_bounds__(512) void small_m_kernel(
     for (int base = seg_begin; base < seg_end; base += SEGS) {
         if (base != seg_begin) load_step(base);
 #pragma unroll
-    for (int si = 0; si < SEGS; ++si) {
-        if (base + si < seg_end) {
-            const int g = (base + si) * kGroupLanes + j;  // g & 7 == j
-            const int gm0 = g * MC;
-            float xsv[MC];
-            int a0[MC][R], a1[MC][R], a2[MC][R];
+        for (int si = 0; si < SEGS; ++si) {
+            if (base + si < seg_end) {
+                const int g = (base + si) * kGroupLanes + j;  // g & 7 == j
+                const int gm0 = g * MC;
+                float xsv[MC];
+                int a0[MC][R], a1[MC][R], a2[MC][R];
 #pragma unroll
-            for (int m = 0; m < MC; ++m) {
-                const float2 v = slds[gm0 + m];
-                xsv[m] = v.x;
+                for (int m = 0; m < MC; ++m) {
+                    const float2 v = slds[gm0 + m];
+                    xsv[m] = v.x;
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    a0[m][r] = DEC == 2 ? -__float_as_int(v.y) : 0;
-                    a1[m][r] = 0;
-                    a2[m][r] = 0;
+                    for (int r = 0; r < R; ++r) {
+                        a0[m][r] = DEC == 2 ? -__float_as_int(v.y) : 0;
+                        a1[m][r] = 0;
+                        a2[m][r] = 0;
+                    }
                 }
-            }
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                uint4 P[MC];
+                for (int t = 0; t < 8; ++t) {
+                    uint4 P[MC];
 #pragma unroll
-                for (int m = 0; m < MC; ++m) P[m] = qlds[(size_t)(gm0 + m) * 8 + (t ^ j)];
+                    for (int m = 0; m < MC; ++m) P[m] = qlds[(size_t)(gm0 + m) * 8 + (t ^ j)];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint32_t d = word_of(cw[si][r][t >> 2], t & 3);
-                    if constexpr (DEC == 2) {
-                        const uint32_t c0 = mask_plane<0>(d), c1 = mask_plane<1>(d);
-                        const uint32_t c2 = mask_plane<2>(d), c3 = mask_plane<3>(d);
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t d = word_of(cw[si][r][t >> 2], t & 3);
+                        if constexpr (DEC == 2) {
+                            const uint32_t c0 = mask_plane<0>(d), c1 = mask_plane<1>(d);
+                            const uint32_t c2 = mask_plane<2>(d), c3 = mask_plane<3>(d);
 #pragma unroll
-                        for (int m = 0; m < MC; ++m) {
-                            a0[m][r] = dot4(P[m].x, c0, a0[m][r]);
-                            a1[m][r] = dot4(P[m].y, c1, a1[m][r]);
-                            a2[m][r] = dot4(P[m].z, c2, a2[m][r]);
-                            a2[m][r] = dot4(P[m].w, c3, a2[m][r]);
-                        }
-                    } else {
-                        const uint32_t e0 = expand_plane<0>(d), e1 = expand_plane<1>(d);
-                        const uint32_t e2 = expand_plane<2>(d), e3 = expand_plane<3>(d);
+                            for (int m = 0; m < MC; ++m) {
+                                a0[m][r] = dot4(P[m].x, c0, a0[m][r]);
+                                a1[m][r] = dot4(P[m].y, c1, a1[m][r]);
+                                a2[m][r] = dot4(P[m].z, c2, a2[m][r]);
+                                a2[m][r] = dot4(P[m].w, c3, a2[m][r]);
+                            }
+                        } else {
+                            const uint32_t e0 = expand_plane<0>(d), e1 = expand_plane<1>(d);
+                            const uint32_t e2 = expand_plane<2>(d), e3 = expand_plane<3>(d);
 #pragma unroll
-                        for (int m = 0; m < MC; ++m) {
-                            a0[m][r] = dot4(P[m].x, e0, a0[m][r]);
-                            a0[m][r] = dot4(P[m].y, e1, a0[m][r]);
-                            a0[m][r] = dot4(P[m].z, e2, a0[m][r]);
-                            a0[m][r] = dot4(P[m].w, e3, a0[m][r]);
+                            for (int m = 0; m < MC; ++m) {
+                                a0[m][r] = dot4(P[m].x, e0, a0[m][r]);
+                                a0[m][r] = dot4(P[m].y, e1, a0[m][r]);
+                                a0[m][r] = dot4(P[m].z, e2, a0[m][r]);
+                                a0[m][r] = dot4(P[m].w, e3, a0[m][r]);
+                            }
                         }
                     }
                 }
-            }
-#pragma unroll
-            for (int m = 0; m < MC; ++m)
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    // a1 = 4 * (plane-1 sum), a2 = 16 * (plane-2 + plane-3 sums): exact shifts.
-                    const int dot = DEC == 2 ? a0[m][r] + (a1[m][r] >> 2) + (a2[m][r] >> 4) : a0[m][r];
-                    acc[m][r] += ((float)dot * xsv[m]) * wsf[si][r];
+                    const float wsf = __half2float(__ushort_as_half((unsigned short)wsraw[si][r]));
+#pragma unroll
+                    for (int m = 0; m < MC; ++m) {
+                        // a1 = 4 * (plane-1 sum), a2 = 16 * (plane-2 + plane-3 sums): exact shifts.
+                        const int dot = DEC == 2 ? a0[m][r] + (a1[m][r] >> 2) + (a2[m][r] >> 4) : a0[m][r];
+                        acc[m][r] += ((float)dot * xsv[m]) * wsf;
+                    }
                 }
+            }
         }
-    }
     }
 
     // 4. Reduce over the 8 group lanes, then over waves in index order.
@@ -193,14 +223,13 @@ __global__ __launch_bounds__(512) void small_m_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[m][r] = sum8_f(acc[m][r]);
 
-    constexpr int RB = kRowSlots * R;  // rows per workgroup
     if (nwaves == 1) {
 #pragma unroll
         for (int m = 0; m < MC; ++m)
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int row = row_base + slot + kRowSlots * r;
-                if (j == (m & 7) && m < mcount && row < n) y[(size_t)(m0 + m) * n + row] = acc[m][r];
+                const int rl = slot + kRowSlots * r;
+                if (j == (m & 7) && m < mcount && rl < rows_here) y[(size_t)(m0 + m) * n + row_base + rl] = acc[m][r];
             }
         return;
     }
@@ -211,13 +240,12 @@ __global__ __launch_bounds__(512) void small_m_kernel(
             for (int r = 0; r < R; ++r) red[(wave * MC + m) * RB + slot + kRowSlots * r] = acc[m][r];
     }
     __syncthreads();
-    for (int o = threadIdx.x; o < MC * RB; o += blockDim.x) {
+    for (int o = threadIdx.x; o < MC * RB; o += nthreads) {
         const int m = o / RB;
         const int rl = o - m * RB;
-        float s = red[m * RB + rl];
-        for (int w = 1; w < nwaves; ++w) s += red[(w * MC + m) * RB + rl];
-        const int row = row_base + rl;
-        if (m < mcount && row < n) y[(size_t)(m0 + m) * n + row] = s;
+        float sum = red[m * RB + rl];
+        for (int w = 1; w < nwaves; ++w) sum += red[(w * MC + m) * RB + rl];
+        if (m < mcount && rl < rows_here) y[(size_t)(m0 + m) * n + row_base + rl] = sum;
     }
 }
 
@@ -297,9 +325,9 @@ SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k) {
     (void)n;
     (void)k;
     SmallMConfig c;
-    c.rows_per_lane = m <= 2 ? 2 : 2;
+    c.rows_per_lane = 2;
     c.max_waves = 8;
-    c.decode = m >= 3 ? 2 : 1;
+    c.decode = 2;
     return c;
 }
 
@@ -326,5 +354,6 @@ hipError_t launch_small_m(const int8_t* q, const float* xs, const uint8_t* plane
         return pick_mc<2>(q, xs, planes, m, n, k, y, mc, rows, segs, waves, nseg, chunks, stream);
     return pick_mc<1>(q, xs, planes, m, n, k, y, mc, rows, segs, waves, nseg, chunks, stream);
 }
+
 
 }  // namespace pq2

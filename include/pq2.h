@@ -134,6 +134,50 @@ int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* plane
                              int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
                              int decode, void* stream);
 
+/* Plane-order variant of pq2_quantize_act_i8 for the decode path (page
+ * "Kernel experiments: recorded evidence", Test 21 and Diagram 7: activations
+ * stored in the order of the code planes, with per-group sums that absorb the
+ * -1 code offset).  Same xs and the same q values as pq2_quantize_act_i8,
+ * stored differently: inside every 16-byte block (weights 16t..16t+15 of a
+ * row) the bytes are 4x4-transposed,
+ *     qp[m][16t + 4s + j] = q[m][16t + 4j + s],   s, j in 0..3,
+ * so dword s of the block pairs with bit plane s of code dword t.  Also
+ *     qsum[m][g] = sum_{i in group g} q[m][i]   (int32, |qsum| <= 16256).
+ *   x       as for pq2_quantize_act_i8.
+ *   qp      device int8 [m][k] (plane order), 16-byte aligned.
+ *   xs      device float [m][k/128], 4-byte aligned.
+ *   qsum    device int32 [m][k/128], 4-byte aligned.
+ * No output may overlap x or another output.
+ * Errors: EINVAL (null, dtype, overlap), ESHAPE (m<1, k<128, k%128,
+ *         k > PQ2_MAX_K, stride < k), EALIGN, ELAUNCH, EDEVICE. */
+int pq2_quantize_act_i8_planes(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
+                               int8_t* qp, float* xs, int32_t* qsum, void* stream);
+
+/* Small-m matmul from the outputs of pq2_quantize_act_i8_planes: the same
+ * definition, limits and summation order as pq2_matmul_small_m, and the
+ * same bits for the same inputs (page "Kernel experiments", Test 21: the
+ * masked-plane decode with the -sum(q) correction gives the identical
+ * integer dot).
+ *   qp      device int8 [m][k] in plane order, 16-byte aligned.
+ *   xs      device float [m][k/128], 4-byte aligned.
+ *   qsum    device int32 [m][k/128], 4-byte aligned; must equal the group
+ *           sums of the q values held in qp (otherwise y is wrong).
+ *   planes  device prepared planes (layout version 1), 16-byte aligned.
+ *   y       device float [m][n], 4-byte aligned; fully overwritten; must not
+ *           overlap any input.
+ * Errors: EINVAL (null, overlap), ESHAPE (m outside 1..16, n<1, k<128,
+ *         k%128, k > PQ2_MAX_K), EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
+                              int64_t m, int64_t n, int64_t k, float* y, void* stream);
+
+/* Tuning hook for pq2_matmul_small_m_planes (benchmarks and tests only; same
+ * arguments and result): rows_per_lane in {1,2}, max_waves in 1..8, 0 picks
+ * the default.  Errors as pq2_matmul_small_m_planes, plus EINVAL for an
+ * unsupported setting. */
+int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
+                                    int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane,
+                                    int max_waves, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

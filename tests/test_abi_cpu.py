@@ -19,6 +19,7 @@ A = 0x7F0000000000          # 4 KiB aligned
 B = 0x7F0100000000
 C = 0x7F0200000000
 D = 0x7F0300000000
+E = 0x7F0400000000
 
 
 def _declared_symbols():
@@ -28,7 +29,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 8
+    assert len(names) == 11
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -97,6 +98,35 @@ def test_small_m_column_limit_and_tuning_validation():
     assert t(A, B, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL   # waves
     assert t(A, B, C, 1, 8, 128, D, 0, 0, 5, None) == EINVAL   # decode
     assert t(A, B, C, 17, 8, 128, D, 1, 1, 1, None) == ESHAPE
+
+
+def test_quantize_planes_validation():
+    f = pq2.lib.pq2_quantize_act_i8_planes
+    assert f(None, 0, 128, 1, 128, B, C, D, None) == EINVAL
+    assert f(A, 0, 128, 1, 128, B, C, None, None) == EINVAL   # no qsum
+    assert f(A, 3, 128, 1, 128, B, C, D, None) == EINVAL      # unknown dtype
+    assert f(A, 0, 128, 0, 128, B, C, D, None) == ESHAPE
+    assert f(A, 0, 128, 1, 96, B, C, D, None) == ESHAPE
+    assert f(A, 0, 100, 1, 128, B, C, D, None) == ESHAPE      # stride < k
+    assert f(A, 0, 128, 1, 128, B + 8, C, D, None) == EALIGN  # qp not 16-byte aligned
+    assert f(A, 0, 128, 1, 128, B, C + 2, D, None) == EALIGN
+    assert f(A, 0, 128, 1, 128, B, C, D + 2, None) == EALIGN  # qsum not 4-byte aligned
+    assert f(A, 0, 128, 2, 128, B, C, C, None) == EINVAL      # qsum overlaps xs
+    assert f(A, 0, 128, 2, 128, A + 16, C, D, None) == EINVAL  # qp overlaps x
+
+
+def test_small_m_planes_validation():
+    f = pq2.lib.pq2_matmul_small_m_planes
+    assert f(None, B, E, C, 1, 8, 128, D, None) == EINVAL
+    assert f(A, B, None, C, 1, 8, 128, D, None) == EINVAL     # no qsum
+    assert f(A, B, E, C, 17, 8, 128, D, None) == ESHAPE
+    assert f(A, B, E, C, 1, 8, 200, D, None) == ESHAPE
+    assert f(A + 8, B, E, C, 1, 8, 128, D, None) == EALIGN    # qp 16-byte alignment
+    assert f(A, B, E + 2, C, 1, 8, 128, D, None) == EALIGN    # qsum 4-byte alignment
+    assert f(A, B, E, C, 1, 8, 128, E, None) == EINVAL        # y overlaps qsum
+    t = pq2.lib.pq2_matmul_small_m_planes_tuned
+    assert t(A, B, E, C, 1, 8, 128, D, 4, 0, None) == EINVAL  # rows per lane
+    assert t(A, B, E, C, 1, 8, 128, D, 0, 9, None) == EINVAL  # waves
 
 
 def test_python_binding_rejects_host_tensors():

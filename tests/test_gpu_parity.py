@@ -317,3 +317,137 @@ def test_prefill_matches_small_m():
     yb = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, n)
     _, bound = oracle.matmul_raw(qo, xso, raw, n, k)
     assert np.all(np.abs(ya.astype(np.float64) - yb) <= 2 * bound)
+
+
+# ------------------------------------------------------------------ plane-order path
+def to_plane_order(q):
+    """The layout pq2_quantize_act_i8_planes documents: inside each 16-byte
+    block of a row, qp[16t + 4s + j] = q[16t + 4j + s] (a 4x4 byte transpose)."""
+    m, k = q.shape
+    return np.ascontiguousarray(q.reshape(m, k // 16, 4, 4).transpose(0, 1, 3, 2).reshape(m, k))
+
+
+def gpu_quantize_planes(x, k=None):
+    pq2 = _pq2()
+    m = x.shape[0]
+    k = x.shape[1] if k is None else k
+    qp = torch.empty((m, k), dtype=torch.int8, device=DEV)
+    xs = torch.full((m, k // 128), float("nan"), dtype=torch.float32, device=DEV)
+    qsum = torch.full((m, k // 128), -(1 << 30), dtype=torch.int32, device=DEV)
+    pq2.pq2_quantize_act_i8_planes(x, qp, xs, qsum)
+    return qp, xs, qsum
+
+
+def quantise_planes_both(x_cpu, dtype="bf16", k=None):
+    """Plane-order quantiser vs the oracle: the same q values (moved by the
+    documented transpose), bit-equal xs, and qsum = the oracle q's group sums."""
+    bits = workloads.bf16_bits(x_cpu) if dtype == "bf16" else (
+        x_cpu.numpy() if dtype == "f32" else x_cpu.view(torch.int16).numpy().view(np.uint16))
+    qo, xso = oracle.quantize_act_i8(bits, dtype, k=k)
+    qp, xs, qsum = gpu_quantize_planes(x_cpu.to(DEV), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(qp.cpu().numpy(), to_plane_order(qo)), "qp is not the plane-ordered oracle q"
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), xso.view(np.uint32)), "xs differs from the oracle"
+    m, kk = qo.shape
+    sums = qo.astype(np.int64).reshape(m, kk // 128, 128).sum(axis=2)
+    assert np.array_equal(qsum.cpu().numpy().astype(np.int64), sums), "qsum is not the group sum of q"
+    return qp, xs, qsum, qo, xso
+
+
+def test_plane_order_helper_is_a_transpose():
+    q = np.arange(2 * 128, dtype=np.int64).reshape(2, 128) % 251 - 125
+    p = to_plane_order(q.astype(np.int8))
+    assert p[0, 4 * 1 + 2] == q[0, 4 * 2 + 1] and p[1, 16 * 3 + 4 * 3 + 0] == q[1, 16 * 3 + 0 + 3]
+    assert np.array_equal(to_plane_order(p), q.astype(np.int8))  # an involution
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_quantize_planes_workloads(name):
+    w, _, x = workload_case(name)
+    announce(f"quantize planes {name} m={x.shape[0]} k={w.k}")
+    quantise_planes_both(x)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32", "bf16"])
+@pytest.mark.parametrize("m,k,stride_pad", [(1, 128, 0), (3, 640, 5), (7, 5120, 8), (33, 1024, 3)])
+def test_quantize_planes_dtypes_and_strides(dtype, m, k, stride_pad):
+    announce(f"quantize planes dtype={dtype} m={m} k={k} pad={stride_pad}")
+    x = workloads.make_activations(m, k + stride_pad, 170 + m, "laplace").float() * 3.0
+    tdt = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    quantise_planes_both(x.to(tdt), dtype, k=k)
+
+
+def test_quantize_planes_special_groups():
+    announce("quantize planes special groups")
+    g = np.zeros((1, 128 * 4), dtype=np.float32)
+    g[0, 128:132] = [2.0 ** -130, -3 * 2.0 ** -131, 2.0 ** -126, 5 * 2.0 ** -133]
+    g[0, 256] = 127.0
+    g[0, 257:263] = [0.5, 1.5, 2.5, -2.5, 126.5, -0.5]
+    g[0, 384:512] = -127.0  # a group at the clamp: qsum = -16256
+    quantise_planes_both(torch.tensor(g).to(torch.bfloat16))
+
+
+def gpu_matmul_planes(fn, qp, xs, qsum, planes, n, **kw):
+    m = qp.shape[0]
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    fn(qp, xs, qsum, planes, y, **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
+def test_small_m_planes_full(m, n, k):
+    """Within the bound of the oracle, and the same bits as the natural-order
+    path (same exact integer dots, same summation order)."""
+    pq2 = _pq2()
+    announce(f"small_m planes full m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=90 + m + n, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 91 + k, "normal+outliers")
+    qp, xs, qsum, qo, xso = quantise_planes_both(x)
+    planes = gpu_planes(raw, n, k)
+    y = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes, qp, xs, qsum, planes, n)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    assert_within(y, y_ref, bound, f"small_m planes m={m} n={n} k={k}")
+    q, xs2 = gpu_quantize(x.to(DEV))
+    y_nat = gpu_matmul(pq2.pq2_matmul_small_m, q, xs2, planes, n)
+    assert np.array_equal(y.view(np.uint32), y_nat.view(np.uint32)), "plane-order and natural paths differ"
+
+
+@pytest.mark.parametrize("rows,waves", [(1, 1), (1, 5), (2, 3), (2, 8)])
+def test_small_m_planes_tuning_variants(rows, waves):
+    pq2 = _pq2()
+    m, n, k = 4, 200, 5248
+    announce(f"small_m planes variants rows={rows} waves={waves}")
+    raw = workloads.make_raw_weights(n, k, seed=7, codes="ternary+3")
+    x = workloads.make_activations(m, k, 8, "laplace")
+    qp, xs, qsum, qo, xso = quantise_planes_both(x)
+    planes = gpu_planes(raw, n, k)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    y = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xs, qsum, planes, n, rows_per_lane=rows,
+                          max_waves=waves)
+    assert_within(y, y_ref, bound, f"planes rows={rows} waves={waves}")
+
+
+@pytest.mark.parametrize("name", ["qkv", "up", "down"])
+def test_small_m_planes_workloads_sampled(name):
+    """Full workload sizes in the benchmark's launch configuration: sampled
+    outputs against the oracle, bitwise batch invariance, and the same bits as
+    the natural-order path everywhere."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    planes = gpu_planes(raw, w.n, w.k)
+    ys = {}
+    for m in w.ms:
+        announce(f"small_m planes workload {name} m={m}")
+        qp, xs, qsum, qo, xso = quantise_planes_both(x[:m].contiguous())
+        y = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes, qp, xs, qsum, planes, w.n)
+        mi, ni = _sample_indices(m, w.n, 400, seed=m)
+        y_ref, bound = oracle.matmul_raw_sample(qo, xso, raw, w.n, w.k, mi, ni)
+        assert_within(y[mi, ni], y_ref, bound, f"{name} m={m}")
+        q, xs2 = gpu_quantize(x[:m].contiguous().to(DEV))
+        y_nat = gpu_matmul(pq2.pq2_matmul_small_m, q, xs2, planes, w.n)
+        assert np.array_equal(y.view(np.uint32), y_nat.view(np.uint32)), f"paths differ at m={m}"
+        ys[m] = y
+    mmax = max(w.ms)
+    for m, y in ys.items():
+        assert np.array_equal(y.view(np.uint32), ys[mmax][:m].view(np.uint32)), f"batch variance at m={m}"
