@@ -4,10 +4,13 @@ group-128 INT8 activations, the attention-QKV projection shape (K=5120,
 N=10240) at M = 1, 2, 3, 4 activation columns.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+                    [--calibrate]
 
 A step is one pass of the per-call hot path over one batch: for each M in
 1..4, quantise the bf16 activations to INT8 (pq2_quantize_act_i8) and run the
-small-m matmul (pq2_matmul_small_m) against the prepared planes.  Weight
+small-m matmul (pq2_matmul_small_m) against the prepared planes.  The
+plane-order variant (pq2_quantize_act_i8_planes + pq2_matmul_small_m_planes,
+same result bits) is timed per M as well and reported beside it.  Weight
 preparation (pq2_prepare_planes) is one-time and outside the timing.  Every
 step reads the next of R prepared-plane copies (>= 1 GiB in total, four
 times the 256 MB Infinity Cache), so weights stream from HBM.  Steps are
@@ -20,7 +23,9 @@ call's algorithmic bytes are what the method must move: packed weights
 weights + q + xs + y (matmul).  The per-M matmul kernel duration (HIP events
 around graph replays of back-to-back launches on the launch stream) gives the
 roofline entry.  The CPU oracle, timed on a bounded sample of the same work,
-gives cpu_baseline.
+gives cpu_baseline.  --calibrate adds a plain elementwise copy of 64 MiB
+(float32 negate, 64 MiB read + 64 MiB written, five times) so that
+rocprofv3 FETCH_SIZE / WRITE_SIZE counts can be scaled to bytes.
 """
 from __future__ import annotations
 
@@ -153,6 +158,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--reps", type=int, default=20, help="graph replays per per-M timing")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 64 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -182,10 +190,15 @@ def main():
             pool[c].copy_(pool[0])
         x = x_cpu.to(dev)
         bufs = {}
+        pbufs = {}
         for m in ms:
             bufs[m] = (torch.empty((m, k), dtype=torch.int8, device=dev),
                        torch.empty((m, k // 128), dtype=torch.float32, device=dev),
                        torch.empty((m, n), dtype=torch.float32, device=dev))
+            pbufs[m] = (torch.empty((m, k), dtype=torch.int8, device=dev),
+                        torch.empty((m, k // 128), dtype=torch.float32, device=dev),
+                        torch.empty((m, k // 128), dtype=torch.int32, device=dev),
+                        torch.empty((m, n), dtype=torch.float32, device=dev))
     torch.cuda.synchronize()
 
     def step_fn(c):
@@ -219,7 +232,7 @@ def main():
 
     # Per-M call timings: graphs of `copies` back-to-back launches, one per copy.
     per_m = {}
-    reps = 20
+    reps = args.reps
     for m in ms:
         q, xs, y = bufs[m]
 
@@ -232,18 +245,36 @@ def main():
                 pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
                 pq2.pq2_matmul_small_m(q, xs, pool[c], y, stream=stream)
 
+        qp, pxs, qsum, py = pbufs[m]
+
+        def mm_planes(m=m, qp=qp, pxs=pxs, qsum=qsum, py=py):
+            for c in range(copies):
+                pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
+
+        def full_planes(m=m, qp=qp, pxs=pxs, qsum=qsum, py=py):
+            for c in range(copies):
+                pq2.pq2_quantize_act_i8_planes(x[:m], qp, pxs, qsum, stream=stream)
+                pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
+
         t_mm = time_graph(torch, Graph(torch, mm, stream), stream, reps) / copies * 1e3
         t_full = time_graph(torch, Graph(torch, full, stream), stream, reps) / copies * 1e3
+        t_mm_p = time_graph(torch, Graph(torch, mm_planes, stream), stream, reps) / copies * 1e3
+        t_full_p = time_graph(torch, Graph(torch, full_planes, stream), stream, reps) / copies * 1e3
+        torch.cuda.synchronize()
+        assert torch.equal(py, y), f"plane-order and natural-order outputs differ at M={m}"
         gbs = matmul_bytes(m, n, k) / (t_mm * 1e-6) / 1e9
         per_m[str(m)] = {
             "matmul_us": round(t_mm, 3),
             "matmul_GBps": round(gbs, 1),
             "matmul_pct_peak": round(100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S, 1),
             "complete_call_us": round(t_full, 3),
+            "planes_matmul_us": round(t_mm_p, 3),
+            "planes_complete_call_us": round(t_full_p, 3),
             "matmul_bytes": matmul_bytes(m, n, k),
         }
         log(f"[bench] M={m}: matmul {t_mm:.3f} us ({gbs:.0f} GB/s, "
-            f"{100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S:.1f}% of 8 TB/s), complete call {t_full:.3f} us")
+            f"{100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S:.1f}% of 8 TB/s), complete call {t_full:.3f} us; "
+            f"plane order: matmul {t_mm_p:.3f} us, complete call {t_full_p:.3f} us")
 
     tot_bytes = sum(v["matmul_bytes"] for v in per_m.values())
     tot_us = sum(v["matmul_us"] for v in per_m.values())
@@ -287,9 +318,23 @@ def main():
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(torch, pq2, workloads, dev, stream)
+    if args.calibrate:
+        calibration_copy(torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(raw_np, x_cpu, n, k, ms, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def calibration_copy(torch, dev, stream):
+    """A plain elementwise copy of known size (64 MiB read, 64 MiB written per
+    launch), the yardstick for the FETCH_SIZE / WRITE_SIZE counters."""
+    with torch.cuda.stream(stream):
+        src = torch.ones(16 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: 5 x {src.numel() * 4} bytes read and written")
 
 
 def bench_prefill(torch, pq2, workloads, dev, stream):

@@ -79,7 +79,7 @@ def _load_library():
     lib.pq2_matmul_small_m.restype = i32
     lib.pq2_matmul_prefill.argtypes = [p, p, p, i64, i64, i64, p, p]
     lib.pq2_matmul_prefill.restype = i32
-    lib.pq2_matmul_small_m_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, i32, p]
+    lib.pq2_matmul_small_m_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tuned.restype = i32
     lib.pq2_quantize_act_i8_planes.argtypes = [p, i32, i64, i64, i64, p, p, p, p]
     lib.pq2_quantize_act_i8_planes.restype = i32
@@ -192,8 +192,8 @@ def pq2_matmul_small_m(q, xs, planes, y, stream=None) -> None:
     _check(lib.pq2_matmul_small_m(*_matmul_args(q, xs, planes, y), _stream(stream)), "pq2_matmul_small_m")
 
 
-def pq2_matmul_small_m_tuned(q, xs, planes, y, rows_per_lane=0, max_waves=0, decode=0, stream=None) -> None:
-    _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows_per_lane, max_waves, decode,
+def pq2_matmul_small_m_tuned(q, xs, planes, y, rows_per_lane=0, max_waves=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows_per_lane, max_waves,
                                         _stream(stream)), "pq2_matmul_small_m_tuned")
 
 

@@ -60,6 +60,16 @@ int check_matmul_args(const int8_t* q, const float* xs, const void* planes, int6
     return PQ2_OK;
 }
 
+// Default small-m configuration with the caller's overrides (0 = default).
+int small_m_config(int64_t m, int64_t n, int64_t k, int rows_per_lane, int max_waves, pq2::SmallMConfig* cfg) {
+    *cfg = pq2::default_small_m_config(m, n, k);
+    if (rows_per_lane) cfg->rows_per_lane = rows_per_lane;
+    if (max_waves) cfg->max_waves = max_waves;
+    if ((cfg->rows_per_lane != 1 && cfg->rows_per_lane != 2) || cfg->max_waves < 1 || cfg->max_waves > 8)
+        return PQ2_EINVAL;
+    return PQ2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,11 +147,8 @@ int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int
     if (int rc = check_matmul_args(qp, xs, planes, m, n, k, y, PQ2_MAX_SMALL_M)) return rc;
     if (!aligned(qsum, 4)) return PQ2_EALIGN;
     if (overlap(y, (size_t)m * n * 4, qsum, (size_t)m * (k / kGroup) * 4)) return PQ2_EINVAL;
-    pq2::SmallMConfig cfg = pq2::default_planes_config(m, n, k);
-    if (rows_per_lane) cfg.rows_per_lane = rows_per_lane;
-    if (max_waves) cfg.max_waves = max_waves;
-    if ((cfg.rows_per_lane != 1 && cfg.rows_per_lane != 2) || cfg.max_waves < 1 || cfg.max_waves > 8)
-        return PQ2_EINVAL;
+    pq2::SmallMConfig cfg;
+    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, &cfg)) return rc;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m_planes(qp, xs, qsum, static_cast<const uint8_t*>(planes), m, n, k, y,
                                                     cfg, (hipStream_t)stream));
@@ -154,15 +161,10 @@ int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* 
 
 int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
                              int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
-                             int decode, void* stream) {
+                             void* stream) {
     if (int rc = check_matmul_args(q, xs, planes, m, n, k, y, PQ2_MAX_SMALL_M)) return rc;
-    pq2::SmallMConfig cfg = pq2::default_small_m_config(m, n, k);
-    if (rows_per_lane) cfg.rows_per_lane = rows_per_lane;
-    if (max_waves) cfg.max_waves = max_waves;
-    if (decode) cfg.decode = decode;
-    if ((cfg.rows_per_lane != 1 && cfg.rows_per_lane != 2 && cfg.rows_per_lane != 4) || cfg.max_waves < 1 ||
-        cfg.max_waves > 8 || (cfg.decode != 1 && cfg.decode != 2))
-        return PQ2_EINVAL;
+    pq2::SmallMConfig cfg;
+    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, &cfg)) return rc;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m(q, xs, static_cast<const uint8_t*>(planes), m, n, k, y, cfg,
                                              (hipStream_t)stream));
@@ -170,7 +172,7 @@ int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* plane
 
 int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream) {
-    return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, 0, stream);
+    return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, stream);
 }
 
 int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,

@@ -34,6 +34,7 @@ __device__ __forceinline__ float dpp_f(float v) {
 // same value (each step pairs a with b and b with a, and FP addition is
 // commutative, so partner lanes agree bit for bit).
 __device__ __forceinline__ float sum8_f(float v) {
+#pragma clang fp contract(off)
     v += dpp_f<kDppXor1>(v);
     v += dpp_f<kDppXor2>(v);
     v += dpp_f<kDppHalfMirror>(v);

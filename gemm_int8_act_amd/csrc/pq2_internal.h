@@ -22,20 +22,19 @@ hipError_t launch_quantize_planes(const void* x, int dtype, int64_t row_stride, 
                                   int8_t* qp, float* xs, int32_t* qsum, hipStream_t stream);
 
 struct SmallMConfig {
-    int rows_per_lane;  // 1, 2 or 4
-    int max_waves;      // 1..16: waves that split k inside one workgroup
-    int decode;         // 1 = add/XOR, 2 = masked planes + sum(q) correction
+    int rows_per_lane;  // 1 or 2
+    int max_waves;      // 1..8: waves that split k inside one workgroup
 };
 
 SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k);
 
+// Natural-order q (the kernel transposes blocks and forms the group sums).
 // Returns hipErrorInvalidValue for a configuration the library has no kernel for.
 hipError_t launch_small_m(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
                           int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
                           hipStream_t stream);
 
-SmallMConfig default_planes_config(int64_t m, int64_t n, int64_t k);
-
+// Plane-order q with its group sums (from launch_quantize_planes).
 hipError_t launch_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const uint8_t* planes,
                                  int64_t m, int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
                                  hipStream_t stream);

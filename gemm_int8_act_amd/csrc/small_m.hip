@@ -8,29 +8,41 @@
 //   dot[m][n][g] = sum_{i in group g} q[m][i] * (c[n][i] - 1)   (exact int32).
 //
 // Design (MI355X-first, not a translation of the pages' Triton/CUDA):
-//  * HBM is the bound: every code byte is read once, with 16-byte loads that
-//    a wave issues for ALL of its work before anything else (one-shot), so
-//    the whole matrix is in flight while activations are staged.
-//  * Work unit = one lane x one 128-weight group x R rows.  A wave is 8 row
-//    slots x 8 group lanes: the 8 lanes of a slot read 8 consecutive groups
-//    (256 contiguous bytes) of one row.  The lane loops over its segments of
-//    8 groups and keeps FP32 partial sums in registers, so the cross-lane
-//    reduction happens once per output (3 DPP adds), not once per group.
-//  * Activations: the workgroup stages its columns' q into LDS once, in
-//    code-plane order (each 16-byte quad byte-transposed so a code dword's
-//    plane s meets q[16t+4j+s]), XOR-swizzled so the 8 group lanes hit 8
-//    different bank groups.  Each q quad read from LDS serves R rows.
-//  * k is split over W waves of the workgroup (each takes consecutive
-//    segments); the W wave partials are summed through LDS in fixed order.
-//  * Two exact decodes (template DEC): 1 = the pages' add/XOR expansion
-//    (four signed planes, 15 ALU ops per code dword), 2 = masked planes
-//    d & (3 << 2s) paired with plane-ordered q, three integer accumulators
-//    re-weighted by shifts and the -1 offset applied once per group as
-//    -sum(q) (page "Kernel experiments", Test 21 / Diagram 7); 5 ALU ops
-//    per code dword.  Both give the identical int32 dot.
-//  * Determinism and batch invariance: per output, the sum is lane-serial
-//    over segments, a fixed DPP tree over the 8 group lanes, then waves in
-//    index order.  None of it depends on the number of columns.
+//  * HBM is the bound: every code byte is read once.  A wave is 8 row slots x
+//    8 lanes; for one segment (8 groups = 256 contiguous code bytes of a row)
+//    lane j of a slot loads bytes 16j.. and 128+16j.. , so each load
+//    instruction reads 128 contiguous bytes per row.  A wave issues the loads
+//    of all its segments (up to SEGS at a time) before anything else.
+//  * With that layout lane j holds half (h = j & 1) of groups j/2 and 4 + j/2.
+//    It forms both half-group integer dots, swaps one of them with its
+//    partner lane j ^ 1 (one DPP move) and adds: the full, exact dot of group
+//    j/2 (h = 0) or 4 + j/2 (h = 1).  Only whole-group dots are scaled, so
+//    each output sums exactly k/128 FP32 terms.
+//  * Decode: masked code planes (page "Kernel experiments", Test 21 and
+//    Diagram 7).  Code dword D gives D & 0x03.., D & 0x0C.., D & 0x30.. and
+//    (D >> 2) & 0x30..: plane s holds c << 2s (c << 4 for s = 3), so three
+//    INT32 accumulators (scaled by 1, 4, 16) recombine exactly as
+//    a0 + (a1 >> 2) + (a23 >> 4), and the code offset -1 becomes one
+//    subtraction of sum(q) per group.  5 ALU ops per 16 weights.
+//  * The activation operand must pair plane s of a code dword with
+//    q[16t + 4j + s]: each 16-byte block of q, 4x4 byte-transposed ("plane
+//    order").  Every wave copies the blocks of its own segments into a
+//    private LDS region (no workgroup barrier); input that is already in
+//    plane order (pq2_quantize_act_i8_planes) is copied as is with its group
+//    sums, natural-order input is transposed on the way and its group sums
+//    formed with dot4 against 0x01010101.  Rows of 8 blocks are padded to 9
+//    so that the 8 distinct blocks one read instruction touches fall in
+//    distinct LDS banks and every read address is one register plus an
+//    immediate.
+//  * k is split over the W waves of a workgroup (consecutive segments); the
+//    W partial sums are added through LDS in wave order.
+//  * Summation order of an output: each lane accumulates its group terms
+//    acc = fma((float)dot * xs, ws, acc) over its segments in order (no other
+//    contraction: the pragma below), a fixed DPP tree adds the 8 lanes of a
+//    slot, and the wave partials are added in wave order.  That order depends
+//    only on the k split, which the library picks from (n, k) alone: outputs
+//    are bit-identical whatever the number of columns (batch invariance),
+//    the rows per lane, or the input order (natural or plane).
 #include "pq2_device.h"
 #include "pq2_internal.h"
 
@@ -38,27 +50,46 @@
 
 namespace pq2 {
 
-constexpr int kGroupLanes = 8;   // lanes per row slot (one group each)
+constexpr int kGroupLanes = 8;   // lanes per row slot
 constexpr int kRowSlots = 8;     // row slots per wave
+constexpr int kBlockPitch = 9;   // LDS quads per group (8 + 1 pad; pad dword 0 = sum(q))
+constexpr int kSegQuads = kGroupLanes * kBlockPitch;  // LDS quads per (segment, column)
 
-template <int MC, int R, int SEGS, int DEC>
-__global__ __launch_bounds__(512) void small_m_kernel(
-    const int8_t* __restrict__ q, const float* __restrict__ xs, const uint8_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, float* __restrict__ y, int n, int k, int groups, int nseg,
-    int segs_per_wave, int mtotal) {
+// Plane-order pairing of activation dwords with code planes, per half group.
+// acc0/acc1/acc23 are the three masked-plane accumulators.
+template <int R>
+__device__ __forceinline__ void half_group_dot(const uint4 (&P)[4], const uint4 (&cw)[R], int (&acc0)[R],
+                                               int (&acc1)[R], int (&acc23)[R]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t d = word_of(cw[r], t);
+            acc0[r] = dot4(P[t].x, mask_plane<0>(d), acc0[r]);
+            acc1[r] = dot4(P[t].y, mask_plane<1>(d), acc1[r]);
+            acc23[r] = dot4(P[t].z, mask_plane<2>(d), acc23[r]);
+            acc23[r] = dot4(P[t].w, mask_plane<3>(d), acc23[r]);
+        }
+    }
+}
+
+template <int MC, int R, int SEGS, bool NATURAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 && R == 1 && MC <= 4 ? 7 : 1))) void small_m_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ xs, const int32_t* __restrict__ qsum,
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y, int n,
+    int k, int groups, int nseg, int segs_per_wave, int mtotal) {
+#pragma clang fp contract(off)
     extern __shared__ __align__(16) unsigned char smem[];
-    const int gpad = nseg * kGroupLanes;
-    uint4* qlds = reinterpret_cast<uint4*>(smem);                                   // [gpad][MC][8 quads]
-    float2* slds = reinterpret_cast<float2*>(smem + (size_t)gpad * MC * 128);       // [gpad][MC] {xs, sum q}
-    float* red = reinterpret_cast<float*>(smem + (size_t)gpad * MC * 136);          // [W][MC][8R]
-
-    constexpr int RB = kRowSlots * R;  // rows per workgroup
+    constexpr int RB = kRowSlots * R;
+    constexpr int WAVE_QUADS = SEGS * MC * kSegQuads;
     const int nthreads = blockDim.x;
     const int nwaves = nthreads >> 6;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop bounds
     const int lane = threadIdx.x & 63;
     const int slot = lane >> 3;
     const int j = lane & 7;
+    const int h = j & 1;
+    const int gsel = (j >> 1) + 4 * h;  // group (within a segment) whose full dot this lane scales
     const int m0 = blockIdx.y * MC;
     const int mcount = min(MC, mtotal - m0);
     const int row_base = blockIdx.x * RB;
@@ -67,85 +98,20 @@ __global__ __launch_bounds__(512) void small_m_kernel(
     const int seg_end = min(seg_begin + segs_per_wave, nseg);
     const uint32_t k4 = (uint32_t)k >> 2;
 
-    // Buffer resources over exactly the bytes this workgroup may read: a row
-    // past n, a group past k or a column past m reads as zero.
+    unsigned char* region = smem + (size_t)wave * WAVE_QUADS * 16;
+    float* red = reinterpret_cast<float*>(smem + (size_t)nwaves * WAVE_QUADS * 16);
+    // One base address per access kind; the (segment, column, quad) parts are immediates.
+    unsigned char* wr_ptr = region + (slot * kBlockPitch + j) * 16;          // copies quad j of group `slot`
+    const unsigned char* rd_ptr = region + ((j >> 1) * kBlockPitch + 4 * h) * 16;  // half h of group j/2
+    const unsigned char* qs_ptr = region + (gsel * kBlockPitch + 8) * 16;     // sum(q) of group gsel
+
     const auto code_rs = make_rsrc(codes + (size_t)row_base * k4, (uint32_t)rows_here * k4);
     const auto scale_rs = make_rsrc(scales + (size_t)row_base * groups, (uint32_t)(rows_here * groups * 2));
     const auto q_rs = make_rsrc(q + (size_t)m0 * k, (uint32_t)(mcount * k));
     const auto xs_rs = make_rsrc(xs + (size_t)m0 * groups, (uint32_t)(mcount * groups * 4));
+    const auto qs_rs = make_rsrc(NATURAL ? nullptr : qsum + (size_t)m0 * groups,
+                                 NATURAL ? 0u : (uint32_t)(mcount * groups * 4));
 
-    // Staging items = (group, column, quad t); 8 consecutive threads take the
-    // 8 quads of one (group, column) so its sum of q is an 8-lane reduction.
-    constexpr int QB = 4;  // staging items per thread per batch
-    const int nitems = gpad * MC * 8;
-    uint4 qv[QB];
-    uint32_t xv[QB];
-    auto stage_load = [&](int base_it) {
-#pragma unroll
-        for (int i = 0; i < QB; ++i) {
-            const int it = base_it + i * nthreads;
-            const int t = it & 7;
-            const int gm = it >> 3;
-            const int m = gm % MC;
-            const int g = gm / MC;
-            const bool ok = it < nitems && m < mcount && g < groups;
-            qv[i] = buf_load16(q_rs, ok ? (uint32_t)(m * k + g * 128 + t * 16) : kBufferOOB);
-            xv[i] = buf_load4(xs_rs, ok ? (uint32_t)((m * groups + g) * 4) : kBufferOOB);
-        }
-    };
-    auto stage_store = [&](int base_it) {
-#pragma unroll
-        for (int i = 0; i < QB; ++i) {
-            const int it = base_it + i * nthreads;
-            if (it < nitems) {  // uniform over each aligned group of 8 lanes
-                const int t = it & 7;
-                const int gm = it >> 3;
-                const int g = gm / MC;
-                const uint4 Q = qv[i];
-                int tsum = dot4(Q.x, 0x01010101u, 0);
-                tsum = dot4(Q.y, 0x01010101u, tsum);
-                tsum = dot4(Q.z, 0x01010101u, tsum);
-                tsum = dot4(Q.w, 0x01010101u, tsum);
-                tsum = sum8_i(tsum);
-                qlds[(size_t)gm * 8 + (t ^ (g & 7))] = to_plane_order(Q);
-                if (t == 0) slds[gm] = make_float2(__uint_as_float(xv[i]), __int_as_float(tsum));
-            }
-        }
-    };
-
-    // Codes and raw fp16 scales of up to SEGS segments of this wave's rows.
-    uint4 cw[SEGS][R][2];
-    uint32_t wsraw[SEGS][R];
-    auto load_step = [&](int base) {
-#pragma unroll
-        for (int si = 0; si < SEGS; ++si) {
-            const int g = (base + si) * kGroupLanes + j;
-            const bool gok = (base + si < seg_end) && (g < groups);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t rl = (uint32_t)(slot + kRowSlots * r);
-                const uint32_t off = gok ? rl * k4 + (uint32_t)g * 32u : kBufferOOB;
-                cw[si][r][0] = buf_load16<kAuxNonTemporal>(code_rs, off);
-                cw[si][r][1] = buf_load16<kAuxNonTemporal>(code_rs, off + 16u);
-                wsraw[si][r] = buf_load2(scale_rs, gok ? (rl * groups + g) * 2u : kBufferOOB);
-            }
-        }
-    };
-
-    // 1. First batch of activation loads (short L2 latency), then every code
-    //    load of this wave's first step (HBM), so both are in flight together
-    //    and staging does not wait for the codes.
-    stage_load(threadIdx.x);
-    load_step(seg_begin);
-    // 2. Stage q in plane order, plus {xs, sum q} per (group, column).
-    stage_store(threadIdx.x);
-    for (int b = threadIdx.x + QB * nthreads; b < nitems; b += QB * nthreads) {
-        stage_load(b);
-        stage_store(b);
-    }
-    __syncthreads();
-
-    // 3. Integer group dots, FP32 scaling, lane-serial accumulation.
     float acc[MC][R];
 #pragma unroll
     for (int m = 0; m < MC; ++m)
@@ -153,71 +119,131 @@ __global__ __launch_bounds__(512) void small_m_kernel(
         for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
     for (int base = seg_begin; base < seg_end; base += SEGS) {
-        if (base != seg_begin) load_step(base);
+        // 1. Activation blocks, scales and group sums of this step (small, L2-resident) ...
+        uint4 qv[SEGS][MC];
+        uint32_t xsv[SEGS][MC], tv[SEGS][MC];
+#pragma unroll
+        for (int si = 0; si < SEGS; ++si) {
+            const bool sok = base + si < seg_end;
+            const int gq = (base + si) * kGroupLanes + slot;  // group whose quad j this lane copies
+            const int gs = (base + si) * kGroupLanes + gsel;  // group this lane scales
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                const bool qok = sok && gq < groups && m < mcount;
+                const bool gok = sok && gs < groups && m < mcount;
+                qv[si][m] = buf_load16(q_rs, qok ? (uint32_t)(m * k + gq * 128 + j * 16) : kBufferOOB);
+                xsv[si][m] = buf_load4(xs_rs, gok ? (uint32_t)((m * groups + gs) * 4) : kBufferOOB);
+                if constexpr (!NATURAL)
+                    tv[si][m] = buf_load4(qs_rs, gok ? (uint32_t)((m * groups + gs) * 4) : kBufferOOB);
+            }
+        }
+        // 2. ... then every code load of the step (HBM), all in flight together:
+        //    lane j reads 16 bytes at 16j (half h of group j/2) and at 128 + 16j
+        //    (half h of group 4 + j/2) of the segment's 256 bytes of its row.
+        uint4 cw[SEGS][2][R];
+        uint32_t wsraw[SEGS][R];
+#pragma unroll
+        for (int si = 0; si < SEGS; ++si) {
+            const int g0 = (base + si) * kGroupLanes;
+            const bool sok = base + si < seg_end;
+            const bool okA = sok && g0 + (j >> 1) < groups;
+            const bool okB = sok && g0 + 4 + (j >> 1) < groups;
+            const bool okS = sok && g0 + gsel < groups;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t rl = (uint32_t)(slot + kRowSlots * r);
+                const uint32_t off = rl * k4 + (uint32_t)g0 * 32u + 16u * (uint32_t)j;
+                cw[si][0][r] = buf_load16<kAuxNonTemporal>(code_rs, okA ? off : kBufferOOB);
+                cw[si][1][r] = buf_load16<kAuxNonTemporal>(code_rs, okB ? off + 128u : kBufferOOB);
+                wsraw[si][r] = buf_load2(scale_rs, okS ? (rl * groups + g0 + gsel) * 2u : kBufferOOB);
+            }
+        }
+        // 3. Private LDS copy of the activation blocks (natural input: transposed
+        //    here, and the group sums formed).  Only this wave touches the region,
+        //    and LDS operations of one wave complete in program order.
+#pragma unroll
+        for (int si = 0; si < SEGS; ++si)
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                uint4 v = qv[si][m];
+                if constexpr (NATURAL) {
+                    int s = dot4(v.x, 0x01010101u, 0);
+                    s = dot4(v.y, 0x01010101u, s);
+                    s = dot4(v.z, 0x01010101u, s);
+                    s = dot4(v.w, 0x01010101u, s);
+                    s = sum8_i(s);  // sum(q) of group `slot`, in all 8 lanes of the slot
+                    v = to_plane_order(v);
+                    if (j == 0)
+                        *reinterpret_cast<int*>(wr_ptr + ((si * MC + m) * kSegQuads + 8) * 16) = s;
+                }
+                *reinterpret_cast<uint4*>(wr_ptr + (si * MC + m) * kSegQuads * 16) = v;
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // 4. Exact group dots, partner exchange, FP32 scaling, lane-serial accumulation.
 #pragma unroll
         for (int si = 0; si < SEGS; ++si) {
             if (base + si < seg_end) {
-                const int g = (base + si) * kGroupLanes + j;  // g & 7 == j
-                const int gm0 = g * MC;
-                float xsv[MC];
-                int a0[MC][R], a1[MC][R], a2[MC][R];
+                const unsigned char* blk = rd_ptr + si * MC * kSegQuads * 16;
+                int half[2][MC][R];
 #pragma unroll
-                for (int m = 0; m < MC; ++m) {
-                    const float2 v = slds[gm0 + m];
-                    xsv[m] = v.x;
+                for (int hg = 0; hg < 2; ++hg) {  // hg 0: group j/2, 1: group 4 + j/2
+                    int a0[MC][R], a1[MC][R], a23[MC][R];
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        a0[m][r] = DEC == 2 ? -__float_as_int(v.y) : 0;
-                        a1[m][r] = 0;
-                        a2[m][r] = 0;
-                    }
-                }
+                    for (int m = 0; m < MC; ++m)
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    uint4 P[MC];
+                        for (int r = 0; r < R; ++r) a0[m][r] = a1[m][r] = a23[m][r] = 0;
 #pragma unroll
-                    for (int m = 0; m < MC; ++m) P[m] = qlds[(size_t)(gm0 + m) * 8 + (t ^ j)];
+                    for (int t = 0; t < 4; ++t) {
+                        uint4 P[MC];
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const uint32_t d = word_of(cw[si][r][t >> 2], t & 3);
-                        if constexpr (DEC == 2) {
+                        for (int m = 0; m < MC; ++m)
+                            P[m] = *reinterpret_cast<const uint4*>(blk + (m * kSegQuads + hg * 4 * kBlockPitch + t) * 16);
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const uint32_t d = word_of(cw[si][hg][r], t);
                             const uint32_t c0 = mask_plane<0>(d), c1 = mask_plane<1>(d);
                             const uint32_t c2 = mask_plane<2>(d), c3 = mask_plane<3>(d);
 #pragma unroll
                             for (int m = 0; m < MC; ++m) {
                                 a0[m][r] = dot4(P[m].x, c0, a0[m][r]);
                                 a1[m][r] = dot4(P[m].y, c1, a1[m][r]);
-                                a2[m][r] = dot4(P[m].z, c2, a2[m][r]);
-                                a2[m][r] = dot4(P[m].w, c3, a2[m][r]);
-                            }
-                        } else {
-                            const uint32_t e0 = expand_plane<0>(d), e1 = expand_plane<1>(d);
-                            const uint32_t e2 = expand_plane<2>(d), e3 = expand_plane<3>(d);
-#pragma unroll
-                            for (int m = 0; m < MC; ++m) {
-                                a0[m][r] = dot4(P[m].x, e0, a0[m][r]);
-                                a0[m][r] = dot4(P[m].y, e1, a0[m][r]);
-                                a0[m][r] = dot4(P[m].z, e2, a0[m][r]);
-                                a0[m][r] = dot4(P[m].w, e3, a0[m][r]);
+                                a23[m][r] = dot4(P[m].z, c2, a23[m][r]);
+                                a23[m][r] = dot4(P[m].w, c3, a23[m][r]);
                             }
                         }
                     }
+#pragma unroll
+                    for (int m = 0; m < MC; ++m)
+#pragma unroll
+                        for (int r = 0; r < R; ++r) half[hg][m][r] = a0[m][r] + (a1[m][r] >> 2) + (a23[m][r] >> 4);
                 }
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float wsf = __half2float(__ushort_as_half((unsigned short)wsraw[si][r]));
+                for (int m = 0; m < MC; ++m) {
+                    int sq;
+                    if constexpr (NATURAL)
+                        sq = *reinterpret_cast<const int*>(qs_ptr + (si * MC + m) * kSegQuads * 16);
+                    else
+                        sq = (int)tv[si][m];
+                    const float xsf = __uint_as_float(xsv[si][m]);
 #pragma unroll
-                    for (int m = 0; m < MC; ++m) {
-                        // a1 = 4 * (plane-1 sum), a2 = 16 * (plane-2 + plane-3 sums): exact shifts.
-                        const int dot = DEC == 2 ? a0[m][r] + (a1[m][r] >> 2) + (a2[m][r] >> 4) : a0[m][r];
-                        acc[m][r] += ((float)dot * xsv[m]) * wsf;
+                    for (int r = 0; r < R; ++r) {
+                        // Lane h = 0 keeps group j/2 and hands its half of group 4 + j/2
+                        // to the partner; lane h = 1 the other way round.
+                        const int mine = h ? half[1][m][r] : half[0][m][r];
+                        const int give = h ? half[0][m][r] : half[1][m][r];
+                        const int dot = mine + dpp_i<kDppXor1>(give) - sq;
+                        const float wsf = __half2float(__ushort_as_half((unsigned short)wsraw[si][r]));
+                        acc[m][r] = __builtin_fmaf((float)dot * xsf, wsf, acc[m][r]);
                     }
                 }
             }
         }
     }
 
-    // 4. Reduce over the 8 group lanes, then over waves in index order.
+    // 5. Reduce over the 8 lanes of a slot (fixed DPP tree), then over waves in index order.
 #pragma unroll
     for (int m = 0; m < MC; ++m)
 #pragma unroll
@@ -252,19 +278,29 @@ __global__ __launch_bounds__(512) void small_m_kernel(
 // ------------------------------------------------------------------ host side
 namespace {
 
-constexpr size_t kLdsBudget = 80 * 1024;  // keeps two workgroups per CU
+constexpr size_t kLdsLimit = 144 * 1024;
 
-size_t lds_bytes(int mc, int gpad, int waves, int rows_per_wg) {
-    return (size_t)gpad * mc * 136 + (size_t)waves * mc * rows_per_wg * 4;
+// Private activation regions of all waves, plus one float per (wave, column,
+// row) for the cross-wave sum.
+size_t lds_bytes(int mc, int segs, int waves, int rows_per_wg) {
+    return (size_t)waves * segs * mc * kSegQuads * 16 + (size_t)waves * mc * rows_per_wg * 4;
 }
 
-template <int MC, int R, int SEGS, int DEC>
-hipError_t launch_one(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
-                      int64_t k, float* y, int waves, int nseg, int segs_per_wave, int chunks,
-                      hipStream_t stream) {
-    auto kern = small_m_kernel<MC, R, SEGS, DEC>;
-    const int groups = (int)(k / 128);
-    const size_t lds = lds_bytes(MC, nseg * kGroupLanes, waves, kRowSlots * R);
+struct Launch {
+    const int8_t* q;
+    const float* xs;
+    const int32_t* qsum;
+    const uint8_t* planes;
+    int64_t m, n, k;
+    float* y;
+    int waves, nseg, per_wave, chunks;
+    hipStream_t stream;
+};
+
+template <int MC, int R, int SEGS, bool NAT>
+hipError_t launch_one(const Launch& a) {
+    auto kern = small_m_kernel<MC, R, SEGS, NAT>;
+    const size_t lds = lds_bytes(MC, SEGS, a.waves, kRowSlots * R);
     static bool attr_set = false;  // one instantiation = one static
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -272,88 +308,89 @@ hipError_t launch_one(const int8_t* q, const float* xs, const uint8_t* planes, i
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const uint8_t* codes = planes;
-    const uint16_t* scales = reinterpret_cast<const uint16_t*>(planes + n * (k / 4));
-    const dim3 grid((unsigned)((n + kRowSlots * R - 1) / (kRowSlots * R)), (unsigned)chunks);
+    const uint16_t* scales = reinterpret_cast<const uint16_t*>(a.planes + a.n * (a.k / 4));
+    const dim3 grid((unsigned)((a.n + kRowSlots * R - 1) / (kRowSlots * R)), (unsigned)a.chunks);
     clear_stale_error();
-    hipLaunchKernelGGL(kern, grid, dim3(64 * waves), lds, stream, q, xs, codes, scales, y, (int)n,
-                       (int)k, groups, nseg, segs_per_wave, (int)m);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * a.waves), lds, a.stream, a.q, a.xs, a.qsum, a.planes, scales, a.y,
+                       (int)a.n, (int)a.k, (int)(a.k / 128), a.nseg, a.per_wave, (int)a.m);
     return hipGetLastError();
 }
 
-template <int MC, int R, int DEC>
-hipError_t pick_segs(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
-                     int64_t k, float* y, int per_wave, int waves, int nseg, int chunks,
-                     hipStream_t stream) {
-    switch (per_wave) {
-        case 1: return launch_one<MC, R, 1, DEC>(q, xs, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream);
-        case 2: return launch_one<MC, R, 2, DEC>(q, xs, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream);
-        case 3: return launch_one<MC, R, 3, DEC>(q, xs, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream);
-        default: return launch_one<MC, R, 4, DEC>(q, xs, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream);
+template <int MC, int R, bool NAT>
+hipError_t pick_segs(const Launch& a, int segs) {
+    switch (segs) {
+        case 1: return launch_one<MC, R, 1, NAT>(a);
+        case 2: return launch_one<MC, R, 2, NAT>(a);
+        case 3: return launch_one<MC, R, 3, NAT>(a);
+        default: return launch_one<MC, R, 4, NAT>(a);
     }
 }
 
-template <int MC, int DEC>
-hipError_t pick_rows(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
-                     int64_t k, float* y, int rows, int segs, int waves, int nseg, int chunks,
-                     hipStream_t stream) {
-    switch (rows) {
-        case 1: return pick_segs<MC, 1, DEC>(q, xs, planes, m, n, k, y, segs, waves, nseg, chunks, stream);
-        case 2: return pick_segs<MC, 2, DEC>(q, xs, planes, m, n, k, y, segs, waves, nseg, chunks, stream);
-        case 4: return pick_segs<MC, 4, DEC>(q, xs, planes, m, n, k, y, segs, waves, nseg, chunks, stream);
-        default: return hipErrorInvalidValue;
-    }
+template <int MC, bool NAT>
+hipError_t pick_rows(const Launch& a, int rows, int segs) {
+    return rows == 1 ? pick_segs<MC, 1, NAT>(a, segs) : pick_segs<MC, 2, NAT>(a, segs);
 }
 
-template <int DEC>
-hipError_t pick_mc(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
-                   int64_t k, float* y, int mc, int rows, int segs, int waves, int nseg, int chunks,
-                   hipStream_t stream) {
-#define PQ2_MC_CASE(C) \
-    case C: return pick_rows<C, DEC>(q, xs, planes, m, n, k, y, rows, segs, waves, nseg, chunks, stream);
+template <bool NAT>
+hipError_t pick_mc(const Launch& a, int mc, int rows, int segs) {
     switch (mc) {
-        PQ2_MC_CASE(1) PQ2_MC_CASE(2) PQ2_MC_CASE(3) PQ2_MC_CASE(4)
-        PQ2_MC_CASE(5) PQ2_MC_CASE(6) PQ2_MC_CASE(7) PQ2_MC_CASE(8)
+        case 1: return pick_rows<1, NAT>(a, rows, segs);
+        case 2: return pick_rows<2, NAT>(a, rows, segs);
+        case 3: return pick_rows<3, NAT>(a, rows, segs);
+        case 4: return pick_rows<4, NAT>(a, rows, segs);
+        case 5: return pick_rows<5, NAT>(a, rows, segs);
+        case 6: return pick_rows<6, NAT>(a, rows, segs);
+        case 7: return pick_rows<7, NAT>(a, rows, segs);
+        case 8: return pick_rows<8, NAT>(a, rows, segs);
         default: return hipErrorInvalidValue;
     }
-#undef PQ2_MC_CASE
+}
+
+hipError_t launch_any(const int8_t* q, const float* xs, const int32_t* qsum, const uint8_t* planes, int64_t m,
+                      int64_t n, int64_t k, float* y, const SmallMConfig& cfg, hipStream_t stream) {
+    const int rows = cfg.rows_per_lane;
+    if (rows != 1 && rows != 2) return hipErrorInvalidValue;
+    if (cfg.max_waves < 1 || cfg.max_waves > 8) return hipErrorInvalidValue;
+    const int groups = (int)(k / 128);
+    const int nseg = (groups + kGroupLanes - 1) / kGroupLanes;
+    const int per_wave = (nseg + cfg.max_waves - 1) / cfg.max_waves;
+    const int waves = (nseg + per_wave - 1) / per_wave;
+    int segs = per_wave < 4 ? per_wave : 4;  // loads in flight per lane: 2 * R * segs
+    int mc = (int)(m < 8 ? m : 8);
+    while (mc > 1 && lds_bytes(mc, segs, waves, kRowSlots * rows) > kLdsLimit) --mc;
+    while (segs > 1 && lds_bytes(mc, segs, waves, kRowSlots * rows) > kLdsLimit) --segs;
+    const int chunks = (int)((m + mc - 1) / mc);
+    mc = (int)((m + chunks - 1) / chunks);  // balance the column passes
+    if (mc * rows > 12 && segs > 3) segs = 3;  // keeps the widest kernels free of register spills
+    const Launch a{q, xs, qsum, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream};
+    return qsum ? pick_mc<false>(a, mc, rows, segs) : pick_mc<true>(a, mc, rows, segs);
 }
 
 }  // namespace
 
+// The k split (max_waves) must depend on (n, k) only: it fixes the summation
+// order, and outputs must not change with the number of columns.  Rows per
+// lane does not touch the order; two rows per lane halve the LDS reads of
+// the activations, which pays from five columns on (measured on the
+// K=5120 and K=17408 shapes).
 SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k) {
     (void)n;
     (void)k;
     SmallMConfig c;
-    c.rows_per_lane = 2;
+    c.rows_per_lane = m <= 4 ? 1 : 2;
     c.max_waves = 8;
-    c.decode = 2;
     return c;
 }
 
-hipError_t launch_small_m(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
-                          int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
-                          hipStream_t stream) {
-    const int rows = cfg.rows_per_lane;
-    if (rows != 1 && rows != 2 && rows != 4) return hipErrorInvalidValue;
-    if (cfg.max_waves < 1 || cfg.max_waves > 8) return hipErrorInvalidValue;
-    if (cfg.decode != 1 && cfg.decode != 2) return hipErrorInvalidValue;
-    const int groups = (int)(k / 128);
-    const int nseg = (groups + kGroupLanes - 1) / kGroupLanes;
-    // Segments per wave; a wave holds at most 4 segments' loads at a time and
-    // loops for longer k.
-    const int segs = (nseg + cfg.max_waves - 1) / cfg.max_waves;
-    const int waves = (nseg + segs - 1) / segs;
-    // Columns per pass: as many as fit the LDS budget (at most 8).
-    int mc = (int)(m < 8 ? m : 8);
-    while (mc > 1 && lds_bytes(mc, nseg * kGroupLanes, waves, kRowSlots * rows) > kLdsBudget) --mc;
-    if (lds_bytes(mc, nseg * kGroupLanes, waves, kRowSlots * rows) > 160 * 1024) return hipErrorInvalidValue;
-    const int chunks = (int)((m + mc - 1) / mc);
-    mc = (int)((m + chunks - 1) / chunks);  // balance the passes
-    if (cfg.decode == 2)
-        return pick_mc<2>(q, xs, planes, m, n, k, y, mc, rows, segs, waves, nseg, chunks, stream);
-    return pick_mc<1>(q, xs, planes, m, n, k, y, mc, rows, segs, waves, nseg, chunks, stream);
+hipError_t launch_small_m(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
+                          int64_t k, float* y, const SmallMConfig& cfg, hipStream_t stream) {
+    return launch_any(q, xs, nullptr, planes, m, n, k, y, cfg, stream);
 }
 
+hipError_t launch_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const uint8_t* planes,
+                                 int64_t m, int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
+                                 hipStream_t stream) {
+    return launch_any(qp, xs, qsum, planes, m, n, k, y, cfg, stream);
+}
 
 }  // namespace pq2

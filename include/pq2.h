@@ -124,15 +124,15 @@ int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int
                        int64_t k, float* y, void* stream);
 
 /* Tuning hook for the small-m matmul (benchmarks and tests only; same
- * arguments and result as pq2_matmul_small_m).  rows_per_lane in {1,2,4},
- * max_waves in 1..8 (waves that split k inside one workgroup), decode 1 =
- * add/XOR expansion to signed bytes, 2 = masked code planes with the
- * per-group -sum(q) correction (both give the same exact integer dot); 0 for
- * any of them picks the library's default.  Errors as pq2_matmul_small_m,
- * plus EINVAL for an unsupported setting. */
+ * arguments and result as pq2_matmul_small_m).  rows_per_lane in {1,2}
+ * (weight rows per lane), max_waves in 1..8 (waves that split k inside one
+ * workgroup); 0 for either picks the library's default.  The summation order
+ * of an output does not depend on rows_per_lane; it depends on max_waves only
+ * through the number of waves k is split over.  Errors as
+ * pq2_matmul_small_m, plus EINVAL for an unsupported setting. */
 int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
                              int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
-                             int decode, void* stream);
+                             void* stream);
 
 /* Plane-order variant of pq2_quantize_act_i8 for the decode path (page
  * "Kernel experiments: recorded evidence", Test 21 and Diagram 7: activations
@@ -171,9 +171,9 @@ int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* 
                               int64_t m, int64_t n, int64_t k, float* y, void* stream);
 
 /* Tuning hook for pq2_matmul_small_m_planes (benchmarks and tests only; same
- * arguments and result): rows_per_lane in {1,2}, max_waves in 1..8, 0 picks
- * the default.  Errors as pq2_matmul_small_m_planes, plus EINVAL for an
- * unsupported setting. */
+ * arguments and result): settings as for pq2_matmul_small_m_tuned, and the
+ * same bits as pq2_matmul_small_m_tuned with the same settings.  Errors as
+ * pq2_matmul_small_m_planes, plus EINVAL for an unsupported setting. */
 int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
                                     int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane,
                                     int max_waves, void* stream);

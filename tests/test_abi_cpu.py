@@ -94,10 +94,10 @@ def test_small_m_column_limit_and_tuning_validation():
     f = pq2.lib.pq2_matmul_small_m
     assert f(A, B, C, 17, 8, 128, D, None) == ESHAPE
     t = pq2.lib.pq2_matmul_small_m_tuned
-    assert t(A, B, C, 1, 8, 128, D, 3, 0, 0, None) == EINVAL   # rows per lane
-    assert t(A, B, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL   # waves
-    assert t(A, B, C, 1, 8, 128, D, 0, 0, 5, None) == EINVAL   # decode
-    assert t(A, B, C, 17, 8, 128, D, 1, 1, 1, None) == ESHAPE
+    assert t(A, B, C, 1, 8, 128, D, 3, 0, None) == EINVAL   # rows per lane
+    assert t(A, B, C, 1, 8, 128, D, 4, 0, None) == EINVAL
+    assert t(A, B, C, 1, 8, 128, D, 0, 9, None) == EINVAL   # waves
+    assert t(A, B, C, 17, 8, 128, D, 1, 1, None) == ESHAPE
 
 
 def test_quantize_planes_validation():
