@@ -79,13 +79,13 @@ def _load_library():
     lib.pq2_matmul_small_m.restype = i32
     lib.pq2_matmul_prefill.argtypes = [p, p, p, i64, i64, i64, p, p]
     lib.pq2_matmul_prefill.restype = i32
-    lib.pq2_matmul_small_m_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
+    lib.pq2_matmul_small_m_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, i32, p]
     lib.pq2_matmul_small_m_tuned.restype = i32
     lib.pq2_quantize_act_i8_planes.argtypes = [p, i32, i64, i64, i64, p, p, p, p]
     lib.pq2_quantize_act_i8_planes.restype = i32
     lib.pq2_matmul_small_m_planes.argtypes = [p, p, p, p, i64, i64, i64, p, p]
     lib.pq2_matmul_small_m_planes.restype = i32
-    lib.pq2_matmul_small_m_planes_tuned.argtypes = [p, p, p, p, i64, i64, i64, p, i32, i32, p]
+    lib.pq2_matmul_small_m_planes_tuned.argtypes = [p, p, p, p, i64, i64, i64, p, i32, i32, i32, p]
     lib.pq2_matmul_small_m_planes_tuned.restype = i32
     return lib
 
@@ -192,8 +192,8 @@ def pq2_matmul_small_m(q, xs, planes, y, stream=None) -> None:
     _check(lib.pq2_matmul_small_m(*_matmul_args(q, xs, planes, y), _stream(stream)), "pq2_matmul_small_m")
 
 
-def pq2_matmul_small_m_tuned(q, xs, planes, y, rows_per_lane=0, max_waves=0, stream=None) -> None:
-    _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows_per_lane, max_waves,
+def pq2_matmul_small_m_tuned(q, xs, planes, y, rows_per_lane=0, max_waves=0, engine=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows_per_lane, max_waves, engine,
                                         _stream(stream)), "pq2_matmul_small_m_tuned")
 
 
@@ -235,6 +235,7 @@ def pq2_matmul_small_m_planes(qp, xs, qsum, planes, y, stream=None) -> None:
            "pq2_matmul_small_m_planes")
 
 
-def pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, y, rows_per_lane=0, max_waves=0, stream=None) -> None:
+def pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, y, rows_per_lane=0, max_waves=0, engine=0,
+                                    stream=None) -> None:
     _check(lib.pq2_matmul_small_m_planes_tuned(*_planes_args(qp, xs, qsum, planes, y), rows_per_lane,
-                                               max_waves, _stream(stream)), "pq2_matmul_small_m_planes_tuned")
+                                               max_waves, engine, _stream(stream)), "pq2_matmul_small_m_planes_tuned")

@@ -61,11 +61,14 @@ int check_matmul_args(const int8_t* q, const float* xs, const void* planes, int6
 }
 
 // Default small-m configuration with the caller's overrides (0 = default).
-int small_m_config(int64_t m, int64_t n, int64_t k, int rows_per_lane, int max_waves, pq2::SmallMConfig* cfg) {
+int small_m_config(int64_t m, int64_t n, int64_t k, int rows_per_lane, int max_waves, int engine,
+                   pq2::SmallMConfig* cfg) {
     *cfg = pq2::default_small_m_config(m, n, k);
     if (rows_per_lane) cfg->rows_per_lane = rows_per_lane;
     if (max_waves) cfg->max_waves = max_waves;
-    if ((cfg->rows_per_lane != 1 && cfg->rows_per_lane != 2) || cfg->max_waves < 1 || cfg->max_waves > 8)
+    if (engine) cfg->engine = engine;
+    if ((cfg->rows_per_lane != 1 && cfg->rows_per_lane != 2) || cfg->max_waves < 1 || cfg->max_waves > 8 ||
+        (cfg->engine != 1 && cfg->engine != 2))
         return PQ2_EINVAL;
     return PQ2_OK;
 }
@@ -142,13 +145,13 @@ int pq2_quantize_act_i8_planes(const void* x, int dtype, int64_t x_row_stride_el
 
 int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
                                     int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane,
-                                    int max_waves, void* stream) {
+                                    int max_waves, int engine, void* stream) {
     if (!qsum) return PQ2_EINVAL;
     if (int rc = check_matmul_args(qp, xs, planes, m, n, k, y, PQ2_MAX_SMALL_M)) return rc;
     if (!aligned(qsum, 4)) return PQ2_EALIGN;
     if (overlap(y, (size_t)m * n * 4, qsum, (size_t)m * (k / kGroup) * 4)) return PQ2_EINVAL;
     pq2::SmallMConfig cfg;
-    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, &cfg)) return rc;
+    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, engine, &cfg)) return rc;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m_planes(qp, xs, qsum, static_cast<const uint8_t*>(planes), m, n, k, y,
                                                     cfg, (hipStream_t)stream));
@@ -156,15 +159,15 @@ int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int
 
 int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
                               int64_t m, int64_t n, int64_t k, float* y, void* stream) {
-    return pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, m, n, k, y, 0, 0, stream);
+    return pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, m, n, k, y, 0, 0, 0, stream);
 }
 
 int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
-                             int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
+                             int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves, int engine,
                              void* stream) {
     if (int rc = check_matmul_args(q, xs, planes, m, n, k, y, PQ2_MAX_SMALL_M)) return rc;
     pq2::SmallMConfig cfg;
-    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, &cfg)) return rc;
+    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, engine, &cfg)) return rc;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m(q, xs, static_cast<const uint8_t*>(planes), m, n, k, y, cfg,
                                              (hipStream_t)stream));
@@ -172,7 +175,7 @@ int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* plane
 
 int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream) {
-    return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, stream);
+    return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, 0, stream);
 }
 
 int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,

@@ -22,8 +22,9 @@ hipError_t launch_quantize_planes(const void* x, int dtype, int64_t row_stride, 
                                   int8_t* qp, float* xs, int32_t* qsum, hipStream_t stream);
 
 struct SmallMConfig {
-    int rows_per_lane;  // 1 or 2
+    int rows_per_lane;  // 1 or 2 (dot-product engine only)
     int max_waves;      // 1..8: waves that split k inside one workgroup
+    int engine;         // 1 = packed dot products (v_dot4), 2 = INT8 matrix cores; same bits
 };
 
 SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k);

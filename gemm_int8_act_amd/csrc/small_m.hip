@@ -35,7 +35,13 @@
 //    distinct LDS banks and every read address is one register plus an
 //    immediate.
 //  * k is split over the W waves of a workgroup (consecutive segments); the
-//    W partial sums are added through LDS in wave order.
+//    W partial sums are added through LDS in wave order.  A wave issues the
+//    code loads of up to SEGS segments at once and stages one segment's
+//    activations at a time, so the LDS footprint does not grow with SEGS.
+//  * Two engines compute the same bits: small_m_kernel (packed v_dot4, per
+//    column 4 dot instructions per code dword) and small_m_mfma_kernel (INT8
+//    matrix cores, whose work per code dword does not grow with the number
+//    of columns).  The library picks one per shape.
 //  * Summation order of an output: each lane accumulates its group terms
 //    acc = fma((float)dot * xs, ws, acc) over its segments in order (no other
 //    contraction: the pragma below), a fixed DPP tree adds the 8 lanes of a
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
 #pragma clang fp contract(off)
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int RB = kRowSlots * R;
-    constexpr int WAVE_QUADS = SEGS * MC * kSegQuads;
+    constexpr int WAVE_QUADS = MC * kSegQuads;  // one segment staged at a time
     const int nthreads = blockDim.x;
     const int nwaves = nthreads >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop bounds
@@ -158,11 +164,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
                 wsraw[si][r] = buf_load2(scale_rs, okS ? (rl * groups + g0 + gsel) * 2u : kBufferOOB);
             }
         }
-        // 3. Private LDS copy of the activation blocks (natural input: transposed
-        //    here, and the group sums formed).  Only this wave touches the region,
-        //    and LDS operations of one wave complete in program order.
+        // 3./4. Per segment: private LDS copy of its activation blocks (natural
+        //    input: transposed here and the group sums formed), then the exact
+        //    group dots, partner exchange, FP32 scaling and lane-serial
+        //    accumulation.  Only this wave touches its region, and LDS operations
+        //    of one wave complete in program order.
 #pragma unroll
-        for (int si = 0; si < SEGS; ++si)
+        for (int si = 0; si < SEGS; ++si) {
 #pragma unroll
             for (int m = 0; m < MC; ++m) {
                 uint4 v = qv[si][m];
@@ -173,20 +181,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
                     s = dot4(v.w, 0x01010101u, s);
                     s = sum8_i(s);  // sum(q) of group `slot`, in all 8 lanes of the slot
                     v = to_plane_order(v);
-                    if (j == 0)
-                        *reinterpret_cast<int*>(wr_ptr + ((si * MC + m) * kSegQuads + 8) * 16) = s;
+                    if (j == 0) *reinterpret_cast<int*>(wr_ptr + (m * kSegQuads + 8) * 16) = s;
                 }
-                *reinterpret_cast<uint4*>(wr_ptr + (si * MC + m) * kSegQuads * 16) = v;
+                *reinterpret_cast<uint4*>(wr_ptr + m * kSegQuads * 16) = v;
             }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // 4. Exact group dots, partner exchange, FP32 scaling, lane-serial accumulation.
-#pragma unroll
-        for (int si = 0; si < SEGS; ++si) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (base + si < seg_end) {
-                const unsigned char* blk = rd_ptr + si * MC * kSegQuads * 16;
+                const unsigned char* blk = rd_ptr;
                 int half[2][MC][R];
 #pragma unroll
                 for (int hg = 0; hg < 2; ++hg) {  // hg 0: group j/2, 1: group 4 + j/2
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
                 for (int m = 0; m < MC; ++m) {
                     int sq;
                     if constexpr (NATURAL)
-                        sq = *reinterpret_cast<const int*>(qs_ptr + (si * MC + m) * kSegQuads * 16);
+                        sq = *reinterpret_cast<const int*>(qs_ptr + m * kSegQuads * 16);
                     else
                         sq = (int)tv[si][m];
                     const float xsf = __uint_as_float(xsv[si][m]);
@@ -275,6 +278,212 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
     }
 }
 
+// ------------------------------------------------------------------ matrix-core variant
+// The same result, bit for bit, from the INT8 matrix cores.  Each wave still
+// owns 8 weight rows and the segments of its k split, and reads the codes
+// with whole 128-byte lines per row, but lane l takes row l & 7 and 16-byte
+// chunk l >> 3 of the 128-byte span (group (l >> 4), half (l >> 3) & 1 of the
+// span's four groups).  With that assignment one v_mfma_i32_16x16x64_i8 per
+// code dword yields every half-group dot of the span for two columns:
+//  * B (64 x 16): lane l supplies k-block l >> 4 (= the group) of column
+//    l & 15 = (half h, row); its 16 bytes are the four bit planes of one code
+//    dword, code values 0..3 (the -1 offset is again -sum(q) per group);
+//  * A (16 x 64): row i = 4 ga + 2 mm + hp holds, in k-block ga only, the
+//    plane-ordered activations of column 2 set + mm for half hp -- zero in
+//    the other k-blocks, so D[(ga, mm, hp)][(h, row)] is the dot of group ga
+//    restricted to (activation half hp, code half h), and the hp == h entries
+//    of the lanes (ga, 0, row) and (ga, 1, row) add up (one DPP rotate) to
+//    the exact group dot.
+// Terms, the lane-serial FP32 accumulation per group class and the final
+// tree ((A0 + A4) + (A1 + A5)) + ((A2 + A6) + (A3 + A7)), then waves in
+// order, are exactly those of small_m_kernel, so both give identical bits.
+template <int MC, int SEGS, bool NATURAL>
+__global__ __launch_bounds__(512) void small_m_mfma_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ xs, const int32_t* __restrict__ qsum,
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y, int n,
+    int k, int groups, int nseg, int segs_per_wave, int mtotal) {
+#pragma clang fp contract(off)
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int MP = (MC + 1) / 2;  // matrix-core passes, two columns each
+    constexpr int WAVE_QUADS = MC * kSegQuads;  // one segment staged at a time
+    const int nthreads = blockDim.x;
+    const int nwaves = nthreads >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    // Copy roles (activation blocks): group `slot` of the segment, quad j.
+    const int slot = lane >> 3;
+    const int j = lane & 7;
+    // Matrix roles: code row, k-block (group of the span) and code half.
+    const int row = lane & 7;
+    const int kb = lane >> 4;
+    const int h = (lane >> 3) & 1;
+    // A-operand row of this lane: (ga, mm, hp); it carries data only in k-block ga.
+    const int ai = lane & 15;
+    const int a_mm = (ai >> 1) & 1;
+    const int a_hp = ai & 1;
+    const bool a_lane = (ai >> 2) == kb;
+    const int m0 = blockIdx.y * MC;
+    const int mcount = min(MC, mtotal - m0);
+    const int row_base = blockIdx.x * kRowSlots;
+    const int rows_here = min(kRowSlots, n - row_base);
+    const int seg_begin = wave * segs_per_wave;
+    const int seg_end = min(seg_begin + segs_per_wave, nseg);
+    const uint32_t k4 = (uint32_t)k >> 2;
+
+    // LDS: one all-zero region shared by the workgroup, then one private
+    // region per wave, then the reduction area.  A-operand lanes outside
+    // their k-block read the zero region at the same offsets, so every A read
+    // is unconditional and addressed by one register plus immediates.
+    unsigned char* zero_region = smem;
+    unsigned char* region = smem + (size_t)(1 + wave) * WAVE_QUADS * 16;
+    float* red = reinterpret_cast<float*>(smem + (size_t)(1 + nwaves) * WAVE_QUADS * 16);
+    unsigned char* wr_ptr = region + (slot * kBlockPitch + j) * 16;
+    const unsigned char* a_base[MP];
+#pragma unroll
+    for (int p = 0; p < MP; ++p) {
+        const int am = 2 * p + a_mm;
+        a_base[p] = (a_lane && am < mcount) ? region + ((am * kSegQuads) + kb * kBlockPitch + 4 * a_hp) * 16
+                                            : zero_region;
+    }
+    const unsigned char* meta_ptr = region + (kb * kBlockPitch + 8) * 16;      // sum(q), xs of group kb
+
+    const auto code_rs = make_rsrc(codes + (size_t)row_base * k4, (uint32_t)rows_here * k4);
+    const auto scale_rs = make_rsrc(scales + (size_t)row_base * groups, (uint32_t)(rows_here * groups * 2));
+    const auto q_rs = make_rsrc(q + (size_t)m0 * k, (uint32_t)(mcount * k));
+    const auto xs_rs = make_rsrc(xs + (size_t)m0 * groups, (uint32_t)(mcount * groups * 4));
+    const auto qs_rs = make_rsrc(NATURAL ? nullptr : qsum + (size_t)m0 * groups,
+                                 NATURAL ? 0u : (uint32_t)(mcount * groups * 4));
+
+    float acc[MP][2];
+#pragma unroll
+    for (int p = 0; p < MP; ++p) acc[p][0] = acc[p][1] = 0.0f;
+
+    for (int base = seg_begin; base < seg_end; base += SEGS) {
+        // 1. Activation blocks and per-group metadata (small, L2-resident) ...
+        uint4 qv[SEGS][MC];
+        uint32_t xsv[SEGS][MC], tv[SEGS][MC];
+#pragma unroll
+        for (int si = 0; si < SEGS; ++si) {
+            const bool sok = base + si < seg_end;
+            const int gq = (base + si) * kGroupLanes + slot;
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                const bool qok = sok && gq < groups && m < mcount;
+                qv[si][m] = buf_load16(q_rs, qok ? (uint32_t)(m * k + gq * 128 + j * 16) : kBufferOOB);
+                const uint32_t moff = (qok && j == 0) ? (uint32_t)((m * groups + gq) * 4) : kBufferOOB;
+                xsv[si][m] = buf_load4(xs_rs, moff);
+                if constexpr (!NATURAL) tv[si][m] = buf_load4(qs_rs, moff);
+            }
+        }
+        // 2. ... then the code loads of the step: two spans of four groups per segment.
+        uint4 cw[SEGS][2];
+        uint32_t wsraw[SEGS][2];
+#pragma unroll
+        for (int si = 0; si < SEGS; ++si) {
+            const int g0 = (base + si) * kGroupLanes;
+            const bool sok = base + si < seg_end;
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const bool ok = sok && g0 + 4 * sp + kb < groups;
+                const uint32_t off = (uint32_t)row * k4 + (uint32_t)g0 * 32u + 128u * sp + 16u * (uint32_t)(lane >> 3);
+                cw[si][sp] = buf_load16<kAuxNonTemporal>(code_rs, ok ? off : kBufferOOB);
+                wsraw[si][sp] = buf_load2(scale_rs, ok ? ((uint32_t)row * groups + g0 + 4 * sp + kb) * 2u : kBufferOOB);
+            }
+        }
+        // The shared zero region is filled once, while the first loads are in
+        // flight; every wave runs this first iteration (each owns >= 1 segment).
+        if (base == seg_begin) {
+            for (int i = threadIdx.x; i < WAVE_QUADS; i += nthreads)
+                reinterpret_cast<uint4*>(zero_region)[i] = make_uint4(0u, 0u, 0u, 0u);
+            __syncthreads();
+        }
+        // 3./4. Per segment: private LDS copy of its activation blocks and
+        //    metadata, then the matrix-core group dots, exact recombination and
+        //    FP32 terms.
+#pragma unroll
+        for (int si = 0; si < SEGS; ++si) {
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                uint4 v = qv[si][m];
+                int s;
+                if constexpr (NATURAL) {
+                    s = dot4(v.x, 0x01010101u, 0);
+                    s = dot4(v.y, 0x01010101u, s);
+                    s = dot4(v.z, 0x01010101u, s);
+                    s = dot4(v.w, 0x01010101u, s);
+                    s = sum8_i(s);
+                    v = to_plane_order(v);
+                } else {
+                    s = (int)tv[si][m];
+                }
+                unsigned char* blk = wr_ptr + m * kSegQuads * 16;
+                *reinterpret_cast<uint4*>(blk) = v;
+                if (j == 0) *reinterpret_cast<uint2*>(blk + 8 * 16) = make_uint2((uint32_t)s, xsv[si][m]);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (base + si < seg_end) {
+#pragma unroll
+                for (int p = 0; p < MP; ++p) {
+                    // Two independent chains (the two spans), interleaved step by step.
+                    v4i D[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+                        for (int sp = 0; sp < 2; ++sp) {
+                            const uint32_t d = word_of(cw[si][sp], st);
+                            const v4i B = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
+                                              (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
+                            const uint4 v = *reinterpret_cast<const uint4*>(
+                                a_base[p] + (sp * 4 * kBlockPitch + st) * 16);
+                            const v4i A = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                            D[sp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, D[sp], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int sp = 0; sp < 2; ++sp) {
+                        // Lane (kb, h, row): column 2p + h; its own half is D[3h], the
+                        // partner lane (kb, 1 - h, row) holds the other half.
+                        const int give = h ? D[sp][1] : D[sp][2];
+                        const int mine = h ? D[sp][3] : D[sp][0];
+                        const int dotc = mine + __builtin_amdgcn_update_dpp(0, give, 0x128, 0xF, 0xF, false);
+                        const int m = 2 * p + h;
+                        if (m < MC) {
+                            const uint2 meta = *reinterpret_cast<const uint2*>(
+                                meta_ptr + (m * kSegQuads + sp * 4 * kBlockPitch) * 16);
+                            const float wsf = __half2float(__ushort_as_half((unsigned short)wsraw[si][sp]));
+                            const int dot = dotc - (int)meta.x;
+                            acc[p][sp] = __builtin_fmaf((float)dot * __uint_as_float(meta.y), wsf, acc[p][sp]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // 5. Group classes k-block, 4 + k-block add in the lane; the four k-blocks and
+    //    the waves add through LDS in the fixed order of small_m_kernel.
+#pragma unroll
+    for (int p = 0; p < MP; ++p) {
+        const int m = 2 * p + h;
+        if (m < MC) red[((wave * 4 + kb) * MC + m) * kRowSlots + row] = acc[p][0] + acc[p][1];
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < MC * kRowSlots; o += nthreads) {
+        const int m = o / kRowSlots;
+        const int r = o - m * kRowSlots;
+        float sum = 0.0f;
+        for (int w = 0; w < nwaves; ++w) {
+            const float* t = red + (size_t)w * 4 * MC * kRowSlots + m * kRowSlots + r;
+            const float tw = (t[0] + t[MC * kRowSlots]) + (t[2 * MC * kRowSlots] + t[3 * MC * kRowSlots]);
+            sum = w == 0 ? tw : sum + tw;
+        }
+        if (m < mcount && r < rows_here) y[(size_t)(m0 + m) * n + row_base + r] = sum;
+    }
+}
+
 // ------------------------------------------------------------------ host side
 namespace {
 
@@ -283,7 +492,8 @@ constexpr size_t kLdsLimit = 144 * 1024;
 // Private activation regions of all waves, plus one float per (wave, column,
 // row) for the cross-wave sum.
 size_t lds_bytes(int mc, int segs, int waves, int rows_per_wg) {
-    return (size_t)waves * segs * mc * kSegQuads * 16 + (size_t)waves * mc * rows_per_wg * 4;
+    (void)segs;  // one segment is staged at a time
+    return (size_t)waves * mc * kSegQuads * 16 + (size_t)waves * mc * rows_per_wg * 4;
 }
 
 struct Launch {
@@ -346,8 +556,74 @@ hipError_t pick_mc(const Launch& a, int mc, int rows, int segs) {
     }
 }
 
+size_t mfma_lds_bytes(int mc, int segs, int waves) {
+    (void)segs;  // one segment is staged at a time
+    return (size_t)(waves + 1) * mc * kSegQuads * 16 + (size_t)waves * 4 * mc * kRowSlots * 4;
+}
+
+template <int MC, int SEGS, bool NAT>
+hipError_t launch_mfma_one(const Launch& a) {
+    auto kern = small_m_mfma_kernel<MC, SEGS, NAT>;
+    const size_t lds = mfma_lds_bytes(MC, SEGS, a.waves);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const uint16_t* scales = reinterpret_cast<const uint16_t*>(a.planes + a.n * (a.k / 4));
+    const dim3 grid((unsigned)((a.n + kRowSlots - 1) / kRowSlots), (unsigned)a.chunks);
+    clear_stale_error();
+    hipLaunchKernelGGL(kern, grid, dim3(64 * a.waves), lds, a.stream, a.q, a.xs, a.qsum, a.planes, scales, a.y,
+                       (int)a.n, (int)a.k, (int)(a.k / 128), a.nseg, a.per_wave, (int)a.m);
+    return hipGetLastError();
+}
+
+template <int MC, bool NAT>
+hipError_t mfma_pick_segs(const Launch& a, int segs) {
+    switch (segs) {
+        case 1: return launch_mfma_one<MC, 1, NAT>(a);
+        case 2: return launch_mfma_one<MC, 2, NAT>(a);
+        case 3: return launch_mfma_one<MC, 3, NAT>(a);
+        default: return launch_mfma_one<MC, 4, NAT>(a);
+    }
+}
+
+template <bool NAT>
+hipError_t mfma_pick_mc(const Launch& a, int mc, int segs) {
+    switch (mc) {
+        case 1: return mfma_pick_segs<1, NAT>(a, segs);
+        case 2: return mfma_pick_segs<2, NAT>(a, segs);
+        case 3: return mfma_pick_segs<3, NAT>(a, segs);
+        case 4: return mfma_pick_segs<4, NAT>(a, segs);
+        case 5: return mfma_pick_segs<5, NAT>(a, segs);
+        case 6: return mfma_pick_segs<6, NAT>(a, segs);
+        case 7: return mfma_pick_segs<7, NAT>(a, segs);
+        case 8: return mfma_pick_segs<8, NAT>(a, segs);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_any(const int8_t* q, const float* xs, const int32_t* qsum, const uint8_t* planes, int64_t m,
                       int64_t n, int64_t k, float* y, const SmallMConfig& cfg, hipStream_t stream) {
+    if (cfg.engine == 2) {
+        if (cfg.max_waves < 1 || cfg.max_waves > 8) return hipErrorInvalidValue;
+        const int groups = (int)(k / 128);
+        const int nseg = (groups + kGroupLanes - 1) / kGroupLanes;
+        const int per_wave = (nseg + cfg.max_waves - 1) / cfg.max_waves;
+        const int waves = (nseg + per_wave - 1) / per_wave;
+        int segs = per_wave < 4 ? per_wave : 4;
+        int mc = (int)(m < 8 ? m : 8);
+        while (mc > 1 && mfma_lds_bytes(mc, segs, waves) > kLdsLimit) --mc;
+        while (segs > 1 && mfma_lds_bytes(mc, segs, waves) > kLdsLimit) --segs;
+        const int chunks = (int)((m + mc - 1) / mc);
+        mc = (int)((m + chunks - 1) / chunks);
+        while (mc * segs > 2 && segs > 1) --segs;  // as for the packed-dot engine below
+        const Launch a{q, xs, qsum, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream};
+        return qsum ? mfma_pick_mc<false>(a, mc, segs) : mfma_pick_mc<true>(a, mc, segs);
+    }
+    if (cfg.engine != 1) return hipErrorInvalidValue;
     const int rows = cfg.rows_per_lane;
     if (rows != 1 && rows != 2) return hipErrorInvalidValue;
     if (cfg.max_waves < 1 || cfg.max_waves > 8) return hipErrorInvalidValue;
@@ -361,7 +637,10 @@ hipError_t launch_any(const int8_t* q, const float* xs, const int32_t* qsum, con
     while (segs > 1 && lds_bytes(mc, segs, waves, kRowSlots * rows) > kLdsLimit) --segs;
     const int chunks = (int)((m + mc - 1) / mc);
     mc = (int)((m + chunks - 1) / chunks);  // balance the column passes
-    if (mc * rows > 12 && segs > 3) segs = 3;  // keeps the widest kernels free of register spills
+    // At most two (column x row) units of code loads per lane per step: more
+    // segments per step hold more registers than the residency of the whole
+    // grid allows (measured at K = 17408), and the loop covers the rest.
+    while (mc * rows * segs > 2 && segs > 1) --segs;
     const Launch a{q, xs, qsum, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream};
     return qsum ? pick_mc<false>(a, mc, rows, segs) : pick_mc<true>(a, mc, rows, segs);
 }
@@ -373,12 +652,16 @@ hipError_t launch_any(const int8_t* q, const float* xs, const int32_t* qsum, con
 // lane does not touch the order; two rows per lane halve the LDS reads of
 // the activations, which pays from five columns on (measured on the
 // K=5120 and K=17408 shapes).
+// Both engines give the same bits, so the engine is free per shape: packed
+// dots win at one or two columns, the matrix cores from five columns on and
+// from three on when K is long (measured on the K = 5120 and K = 17408
+// shapes; the matrix-core work per code dword does not grow with M).
 SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k) {
     (void)n;
-    (void)k;
     SmallMConfig c;
     c.rows_per_lane = m <= 4 ? 1 : 2;
     c.max_waves = 8;
+    c.engine = (m >= 5 || (m >= 3 && k >= 8192)) ? 2 : 1;
     return c;
 }
 

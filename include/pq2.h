@@ -125,14 +125,16 @@ int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int
 
 /* Tuning hook for the small-m matmul (benchmarks and tests only; same
  * arguments and result as pq2_matmul_small_m).  rows_per_lane in {1,2}
- * (weight rows per lane), max_waves in 1..8 (waves that split k inside one
- * workgroup); 0 for either picks the library's default.  The summation order
- * of an output does not depend on rows_per_lane; it depends on max_waves only
- * through the number of waves k is split over.  Errors as
- * pq2_matmul_small_m, plus EINVAL for an unsupported setting. */
+ * (weight rows per lane, packed-dot engine), max_waves in 1..8 (waves that
+ * split k inside one workgroup), engine 1 = packed dot products (v_dot4),
+ * 2 = INT8 matrix cores (v_mfma); 0 for any of them picks the library's
+ * default.  The summation order of an output depends on max_waves only
+ * (through the number of waves k is split over): neither rows_per_lane nor
+ * the engine changes the bits.  Errors as pq2_matmul_small_m, plus EINVAL for
+ * an unsupported setting. */
 int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
                              int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
-                             void* stream);
+                             int engine, void* stream);
 
 /* Plane-order variant of pq2_quantize_act_i8 for the decode path (page
  * "Kernel experiments: recorded evidence", Test 21 and Diagram 7: activations
@@ -176,7 +178,7 @@ int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* 
  * pq2_matmul_small_m_planes, plus EINVAL for an unsupported setting. */
 int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
                                     int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane,
-                                    int max_waves, void* stream);
+                                    int max_waves, int engine, void* stream);
 
 #ifdef __cplusplus
 }

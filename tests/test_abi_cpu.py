@@ -94,10 +94,11 @@ def test_small_m_column_limit_and_tuning_validation():
     f = pq2.lib.pq2_matmul_small_m
     assert f(A, B, C, 17, 8, 128, D, None) == ESHAPE
     t = pq2.lib.pq2_matmul_small_m_tuned
-    assert t(A, B, C, 1, 8, 128, D, 3, 0, None) == EINVAL   # rows per lane
-    assert t(A, B, C, 1, 8, 128, D, 4, 0, None) == EINVAL
-    assert t(A, B, C, 1, 8, 128, D, 0, 9, None) == EINVAL   # waves
-    assert t(A, B, C, 17, 8, 128, D, 1, 1, None) == ESHAPE
+    assert t(A, B, C, 1, 8, 128, D, 3, 0, 0, None) == EINVAL   # rows per lane
+    assert t(A, B, C, 1, 8, 128, D, 4, 0, 0, None) == EINVAL
+    assert t(A, B, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL   # waves
+    assert t(A, B, C, 1, 8, 128, D, 0, 0, 3, None) == EINVAL   # engine
+    assert t(A, B, C, 17, 8, 128, D, 1, 1, 1, None) == ESHAPE
 
 
 def test_quantize_planes_validation():
@@ -125,8 +126,9 @@ def test_small_m_planes_validation():
     assert f(A, B, E + 2, C, 1, 8, 128, D, None) == EALIGN    # qsum 4-byte alignment
     assert f(A, B, E, C, 1, 8, 128, E, None) == EINVAL        # y overlaps qsum
     t = pq2.lib.pq2_matmul_small_m_planes_tuned
-    assert t(A, B, E, C, 1, 8, 128, D, 4, 0, None) == EINVAL  # rows per lane
-    assert t(A, B, E, C, 1, 8, 128, D, 0, 9, None) == EINVAL  # waves
+    assert t(A, B, E, C, 1, 8, 128, D, 4, 0, 0, None) == EINVAL  # rows per lane
+    assert t(A, B, E, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL  # waves
+    assert t(A, B, E, C, 1, 8, 128, D, 0, 0, 7, None) == EINVAL  # engine
 
 
 def test_python_binding_rejects_host_tensors():

@@ -191,10 +191,31 @@ def test_small_m_zero_activations():
     assert np.all(y == 0.0)
 
 
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
+def test_small_m_matrix_core_engine_full(m, n, k):
+    """The matrix-core engine against the oracle, and bit-identical to the
+    packed-dot engine, on every full-comparison shape, both input orders."""
+    pq2 = _pq2()
+    announce(f"small_m matrix-core engine m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=90 + m + n, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 91 + k, "normal+outliers")
+    q, xs, qo, xso = quantise_both(x)
+    planes = gpu_planes(raw, n, k)
+    y = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, engine=2)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    assert_within(y, y_ref, bound, f"engine 2 m={m} n={n} k={k}")
+    y1 = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, engine=1)
+    assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), "engines differ"
+    qp, xsp, qsum = gpu_quantize_planes(x.to(DEV))
+    yp = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xsp, qsum, planes, n, engine=2)
+    assert np.array_equal(yp.view(np.uint32), y1.view(np.uint32)), "plane-order matrix-core path differs"
+
+
 @pytest.mark.parametrize("m", [1, 4, 11])
 def test_small_m_tuning_variants(m):
-    """Every rows-per-lane / k-split setting is within the bound; rows per
-    lane does not change the summation order, so it keeps the bits."""
+    """Every rows-per-lane / k-split / engine setting is within the bound;
+    neither rows per lane nor the engine (packed dots or matrix cores)
+    changes the summation order, so they keep the bits."""
     pq2 = _pq2()
     n, k = 200, 5248
     announce(f"small_m variants m={m}")
@@ -207,11 +228,14 @@ def test_small_m_tuning_variants(m):
     assert_within(y0, y_ref, bound, "default")
     for waves in (1, 2, 3, 5, 8):
         ys = []
-        for rows in (1, 2):
-            y = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows_per_lane=rows, max_waves=waves)
-            assert_within(y, y_ref, bound, f"rows={rows} waves={waves}")
+        for rows, engine in ((1, 1), (2, 1), (1, 2)):
+            y = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows_per_lane=rows, max_waves=waves,
+                           engine=engine)
+            assert_within(y, y_ref, bound, f"rows={rows} waves={waves} engine={engine}")
             ys.append(y)
-        assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), f"waves={waves}: rows change the bits"
+        for y in ys[1:]:
+            assert np.array_equal(ys[0].view(np.uint32), y.view(np.uint32)), \
+                f"waves={waves}: rows per lane or engine changed the bits"
 
 
 # ------------------------------------------------------------------ small m: full workload sizes
