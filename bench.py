@@ -350,21 +350,30 @@ def bench_prefill(torch, pq2, workloads, dev, stream):
         torch.cuda.synchronize()
         for m in w.ms:
             q = torch.empty((m, w.k), dtype=torch.int8, device=dev)
+            qp = torch.empty((m, w.k), dtype=torch.int8, device=dev)
             xs = torch.empty((m, w.k // 128), dtype=torch.float32, device=dev)
+            qsum = torch.empty((m, w.k // 128), dtype=torch.int32, device=dev)
             y = torch.empty((m, w.n), dtype=torch.float32, device=dev)
             with torch.cuda.stream(stream):
                 pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
+                pq2.pq2_quantize_act_i8_planes(x[:m], qp, xs, qsum, stream=stream)
 
             def f(q=q, xs=xs, y=y):
                 for _ in range(10):
                     pq2.pq2_matmul_prefill(q, xs, planes, y, stream=stream)
 
+            def fp(qp=qp, xs=xs, y=y):
+                for _ in range(10):
+                    pq2.pq2_matmul_prefill_planes(qp, xs, planes, y, stream=stream)
+
             t_us = time_graph(torch, Graph(torch, f, stream), stream, 5) / 10 * 1e3
+            tp_us = time_graph(torch, Graph(torch, fp, stream), stream, 5) / 10 * 1e3
             ops = 2.0 * m * w.n * w.k
             tops = ops / (t_us * 1e-6) / 1e12
             out[f"{name}_m{m}"] = {"us": round(t_us, 2), "TOPS": round(tops, 1),
-                                   "pct_int8_peak": round(100 * tops * 1e12 / PEAK_INT8_OPS_PER_S, 1)}
-            log(f"[bench] {name} M={m}: {t_us:.1f} us, {tops:.0f} TOPS")
+                                   "pct_int8_peak": round(100 * tops * 1e12 / PEAK_INT8_OPS_PER_S, 1),
+                                   "planes_us": round(tp_us, 2)}
+            log(f"[bench] {name} M={m}: {t_us:.1f} us, {tops:.0f} TOPS (plane-order input {tp_us:.1f} us)")
         del planes
     return out
 

@@ -36,6 +36,9 @@ EXPORTED = (
     "pq2_quantize_act_i8_planes",
     "pq2_matmul_small_m_planes",
     "pq2_matmul_small_m_planes_tuned",
+    "pq2_matmul_prefill_tuned",
+    "pq2_matmul_prefill_planes",
+    "pq2_matmul_prefill_planes_tuned",
 )
 
 
@@ -87,6 +90,12 @@ def _load_library():
     lib.pq2_matmul_small_m_planes.restype = i32
     lib.pq2_matmul_small_m_planes_tuned.argtypes = [p, p, p, p, i64, i64, i64, p, i32, i32, i32, p]
     lib.pq2_matmul_small_m_planes_tuned.restype = i32
+    lib.pq2_matmul_prefill_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, p]
+    lib.pq2_matmul_prefill_tuned.restype = i32
+    lib.pq2_matmul_prefill_planes.argtypes = [p, p, p, i64, i64, i64, p, p]
+    lib.pq2_matmul_prefill_planes.restype = i32
+    lib.pq2_matmul_prefill_planes_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, p]
+    lib.pq2_matmul_prefill_planes_tuned.restype = i32
     return lib
 
 
@@ -202,6 +211,11 @@ def pq2_matmul_prefill(q, xs, planes, y, stream=None) -> None:
     _check(lib.pq2_matmul_prefill(*_matmul_args(q, xs, planes, y), _stream(stream)), "pq2_matmul_prefill")
 
 
+def pq2_matmul_prefill_tuned(q, xs, planes, y, tile=0, stream=None) -> None:
+    _check(lib.pq2_matmul_prefill_tuned(*_matmul_args(q, xs, planes, y), tile, _stream(stream)),
+           "pq2_matmul_prefill_tuned")
+
+
 def pq2_quantize_act_i8_planes(x, qp, xs, qsum, stream=None) -> None:
     """As pq2_quantize_act_i8, writing q in code-plane order (qp, int8
     [m][k]) plus the int32 group sums qsum [m][k/128]."""
@@ -239,3 +253,14 @@ def pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, y, rows_per_lane=0, ma
                                     stream=None) -> None:
     _check(lib.pq2_matmul_small_m_planes_tuned(*_planes_args(qp, xs, qsum, planes, y), rows_per_lane,
                                                max_waves, engine, _stream(stream)), "pq2_matmul_small_m_planes_tuned")
+
+
+def pq2_matmul_prefill_planes(qp, xs, planes, y, stream=None) -> None:
+    """pq2_matmul_prefill from plane-order activations (pq2_quantize_act_i8_planes)."""
+    _check(lib.pq2_matmul_prefill_planes(*_matmul_args(qp, xs, planes, y), _stream(stream)),
+           "pq2_matmul_prefill_planes")
+
+
+def pq2_matmul_prefill_planes_tuned(qp, xs, planes, y, tile=0, stream=None) -> None:
+    _check(lib.pq2_matmul_prefill_planes_tuned(*_matmul_args(qp, xs, planes, y), tile, _stream(stream)),
+           "pq2_matmul_prefill_planes_tuned")

@@ -40,9 +40,17 @@ def _hipcc() -> str:
     return path
 
 
+# Per-source extra flags.  The prefill kernel rescales every MFMA result on
+# the vector ALU; asking the backend for the VGPR form of the MFMA keeps the
+# accumulators out of AGPRs and saves one register move per output and group.
+EXTRA_FLAGS = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

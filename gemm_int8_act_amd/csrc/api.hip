@@ -12,7 +12,7 @@
 namespace {
 
 constexpr int64_t kGroup = 128;
-constexpr int64_t kMaxPrefillM = (int64_t)65535 * 128;  // grid.y limit x tile rows
+constexpr int64_t kMaxPrefillM = (int64_t)65535 * 64;  // grid.y limit x smallest tile rows
 constexpr int64_t kMaxN = (int64_t)1 << 30;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -178,12 +178,32 @@ int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int
     return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, 0, stream);
 }
 
+int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
+                             int64_t k, float* y, int tile, void* stream) {
+    if (int rc = check_matmul_args(q, xs, planes, m, n, k, y, kMaxPrefillM)) return rc;
+    if (tile < 0 || tile > 4) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_prefill(q, xs, static_cast<const uint8_t*>(planes), m, n, k, y, tile, false,
+                                             (hipStream_t)stream));
+}
+
 int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream) {
-    if (int rc = check_matmul_args(q, xs, planes, m, n, k, y, kMaxPrefillM)) return rc;
+    return pq2_matmul_prefill_tuned(q, xs, planes, m, n, k, y, 0, stream);
+}
+
+int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const void* planes, int64_t m, int64_t n,
+                                    int64_t k, float* y, int tile, void* stream) {
+    if (int rc = check_matmul_args(qp, xs, planes, m, n, k, y, kMaxPrefillM)) return rc;
+    if (tile < 0 || tile > 4) return PQ2_EINVAL;
     if (int rc = check_device()) return rc;
-    return launch_status(pq2::launch_prefill(q, xs, static_cast<const uint8_t*>(planes), m, n, k, y,
+    return launch_status(pq2::launch_prefill(qp, xs, static_cast<const uint8_t*>(planes), m, n, k, y, tile, true,
                                              (hipStream_t)stream));
+}
+
+int pq2_matmul_prefill_planes(const int8_t* qp, const float* xs, const void* planes, int64_t m, int64_t n,
+                              int64_t k, float* y, void* stream) {
+    return pq2_matmul_prefill_planes_tuned(qp, xs, planes, m, n, k, y, 0, stream);
 }
 
 }  // extern "C"

@@ -40,7 +40,9 @@ hipError_t launch_small_m_planes(const int8_t* qp, const float* xs, const int32_
                                  int64_t m, int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
                                  hipStream_t stream);
 
+// tile: 0 = default, 1 = 128x128, 2 = 64x128, 3 = 64x64, 4 = 128x64 outputs
+// per workgroup.  plane_a: q is in plane order (pq2_quantize_act_i8_planes).
 hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
-                          int64_t n, int64_t k, float* y, hipStream_t stream);
+                          int64_t n, int64_t k, float* y, int tile, bool plane_a, hipStream_t stream);
 
 }  // namespace pq2

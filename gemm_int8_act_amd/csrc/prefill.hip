@@ -9,20 +9,28 @@
 // accumulated over groups.
 //
 // Design:
-//  * Workgroup tile BM x BN = 128 x 128 outputs, 4 waves as 2 x 2, each wave
-//    64 x 64 = 2 x 2 tiles of v_mfma_i32_32x32x32_i8.  One group (k = 128) =
-//    four MFMA k-steps of 32.
+//  * Workgroup tile BM x BN (128x128, 64x128, 128x64 or 64x64, chosen so
+//    the grid fills the chip), 4 waves as 2 x 2, each wave (BM/2) x (BN/2)
+//    made of 32 x 32 tiles of v_mfma_i32_32x32x32_i8.  One group (k = 128)
+//    = four MFMA k-steps of 32.
+//  * Activations come in natural order (transposed while staged) or already
+//    in plane order (pq2_quantize_act_i8_planes; copied as they are).
 //  * Operand order inside a k-step is free as long as A and B agree: lane l
 //    of an MFMA supplies 16 bytes of row (l % 32) of A and of column (l % 32)
-//    of B for the same 16 k positions.  We give lane half h = l / 32 in
-//    k-step kk the 16 weights of code dword t = 2kk + h, in the order the
-//    add/XOR decode produces them (plane s, byte j <-> weight 16t + 4j + s),
-//    and stage A in LDS already byte-transposed to that order.  So B needs
-//    no re-shuffle after decoding: one code dword -> one 16-byte operand.
-//  * Both tiles live in LDS with a quad-level XOR swizzle (slot t ^ (row & 7))
-//    so the 32 rows a fragment read touches spread over all banks.
-//  * After the four MFMA k-steps of a group, each lane rescales its 16 INT32
-//    results per tile: acc += float(dot) * xs[m] * ws[n].
+//    of B for the same 16 k positions.  Lane half h = l / 32 in k-step kk
+//    takes code dword t = 2kk + h, whose four bit planes are the 16 weights
+//    16t + 4j + s (plane s, byte j); A is staged byte-transposed to match.
+//  * B decode: the 2-bit field of each byte becomes c - 1 through one
+//    v_perm_b32 table lookup per plane (table bytes -1, 0, +1, +2), 11 ALU
+//    ops per code dword.
+//  * LDS is double-buffered: the global loads of group g + 1 are in flight
+//    while group g is multiplied, then written to the other buffer; one
+//    barrier per group.  Quads of a row are XOR-swizzled over 16 rows so the
+//    32-row fragment reads and the staging writes hit distinct banks.
+//  * After the four k-steps of a group each lane rescales its INT32 results:
+//    acc += (float(dot) * xs[m]) * ws[n].  That rescale (3 VALU per output
+//    and group) is the bound of the kernel: it costs more issue slots than
+//    the matrix cores need for the group's 128 multiply-adds.
 #include "pq2_device.h"
 #include "pq2_internal.h"
 
@@ -33,151 +41,236 @@ namespace pq2 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
+constexpr uint32_t kCodeLut = 0x020100FFu;  // code c -> byte c - 1 (as v_perm table)
 
+__device__ __forceinline__ uint32_t lut_plane(uint32_t fields) {
+    return __builtin_amdgcn_perm(0u, kCodeLut, fields);
+}
+
+// Quad slot of quad t of row i.  With the row parity, the key (i >> 1) & 7
+// makes the 16-byte slots of any 16 consecutive rows distinct modulo 16, so
+// 16 lanes of a fragment read (16 rows, one quad each) or of a staging write
+// (rows i, i + 1 or (row, half) pairs) touch all 64 banks once.  Of the keys
+// measured, this one showed the fewest SQ_LDS_BANK_CONFLICT cycles.
+__device__ __forceinline__ int swz(int i, int t) { return i * 8 + (t ^ ((i >> 1) & 7)); }
+
+template <int BM, int BN, bool PLANE_A>
 __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__ q,
                                                       const float* __restrict__ xs,
                                                       const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
                                                       float* __restrict__ y, int m, int n, int k,
                                                       int groups) {
-    __shared__ uint4 As[kBM * 8];  // [row m][quad slot]: plane-ordered activations
-    __shared__ uint4 Bs[kBN * 8];  // [row n][quad slot]: decoded signed weights
-    __shared__ float xsS[kBM];
-    __shared__ float wsS[kBN];
+#pragma clang fp contract(off)
+    constexpr int MT = BM / 64;          // 32-row tiles per wave
+    constexpr int NT = BN / 64;          // 32-column tiles per wave
+    constexpr int AQ = BM * 8 / 256;     // A quads staged per thread
+    constexpr int BI = BN * 2;           // B items (row, half) per group
+    __shared__ uint4 As[2][BM * 8];
+    __shared__ uint4 Bs[2][BN * 8];
+    __shared__ float xsS[2][BM];
+    __shared__ float wsS[2][BN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    const int nb = blockIdx.x * kBN;
-    const int mb = blockIdx.y * kBM;
+    const int nb = blockIdx.x * BN;
+    const int mb = blockIdx.y * BM;
     const int k4 = k >> 2;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    float acc[2][2][16];
+    // Raw buffer resources over this workgroup's rows: out-of-range rows read
+    // zero, and a group's offsets are the first group's plus a uniform step.
+    const int mrows = min(BM, m - mb);
+    const int nrows = min(BN, n - nb);
+    const auto q_rs = make_rsrc(q + (size_t)mb * k, (uint32_t)(mrows * k));
+    const auto c_rs = make_rsrc(codes + (size_t)nb * k4, (uint32_t)(nrows * k4));
+    const auto x_rs = make_rsrc(xs + (size_t)mb * groups, (uint32_t)(mrows * groups * 4));
+    const auto s_rs = make_rsrc(scales + (size_t)nb * groups, (uint32_t)(nrows * groups * 2));
+    uint32_t a_off[AQ];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int p = 0; p < AQ; ++p) {
+        const int it = tid + 256 * p;
+        a_off[p] = (uint32_t)((it >> 3) * k + (it & 7) * 16);
+    }
+    const uint32_t b_off = tid < BI ? (uint32_t)((tid >> 1) * k4 + (tid & 1) * 16) : kBufferOOB;
+    const bool s_is_x = tid < BM;
+    const bool s_is_w = tid >= 256 - BN;
+    const uint32_t s_off = s_is_x ? (uint32_t)(tid * groups * 4)
+                                  : (s_is_w ? (uint32_t)((tid - (256 - BN)) * groups * 2) : kBufferOOB);
+
+    uint4 areg[AQ];
+    uint4 breg;
+    uint32_t sreg;
+
+    auto load_stage = [&](int g) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int p = 0; p < AQ; ++p) areg[p] = buf_load16(q_rs, a_off[p] + (uint32_t)g * 128u);
+        breg = buf_load16(c_rs, b_off == kBufferOOB ? kBufferOOB : b_off + (uint32_t)g * 32u);
+        if (s_is_x)
+            sreg = buf_load4(x_rs, s_off + (uint32_t)g * 4u);
+        else
+            sreg = buf_load2(s_rs, s_off == kBufferOOB ? kBufferOOB : s_off + (uint32_t)g * 2u);
+    };
+    // LDS slots this thread writes (fixed for the whole kernel).
+    int a_slot[AQ];
+#pragma unroll
+    for (int p = 0; p < AQ; ++p) {
+        const int it = tid + 256 * p;
+        a_slot[p] = swz(it >> 3, it & 7);
+    }
+    int b_slot[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b_slot[c] = swz(tid >> 1, 4 * (tid & 1) + c);
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < AQ; ++p) As[buf][a_slot[p]] = PLANE_A ? areg[p] : to_plane_order(areg[p]);
+        if (tid < BI) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t d = word_of(breg, c);
+                Bs[buf][b_slot[c]] =
+                    make_uint4(lut_plane(d & 0x03030303u), lut_plane((d >> 2) & 0x03030303u),
+                               lut_plane((d >> 4) & 0x03030303u), lut_plane((d >> 6) & 0x03030303u));
+            }
+        }
+        if (s_is_x) xsS[buf][tid] = __uint_as_float(sreg);
+        else if (s_is_w) wsS[buf][tid - (256 - BN)] = __half2float(__ushort_as_half((unsigned short)sreg));
+    };
+    // Fragment read slots per k-step (fixed for the whole kernel).
+    int af_slot[4][MT], bf_slot[4][NT];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) af_slot[kk][mt] = swz(wm * (BM / 2) + mt * 32 + l32, 2 * kk + hi);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bf_slot[kk][nt] = swz(wn * (BN / 2) + nt * 32 + l32, 2 * kk + hi);
+    }
+
+    float acc[MT][NT][16];
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+
     for (int g = 0; g < groups; ++g) {
-        // Stage A: 128 rows x 8 quads, four quads per thread.
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int it = tid + 256 * p;
-            const int i = it >> 3;
-            const int t = it & 7;
-            const int row = mb + i;
-            uint4 Q = make_uint4(0u, 0u, 0u, 0u);
-            if (row < m) Q = *reinterpret_cast<const uint4*>(q + (size_t)row * k + (size_t)g * 128 + t * 16);
-            As[i * 8 + (t ^ (i & 7))] = to_plane_order(Q);
-        }
-        // Stage B: 128 rows x 32 code bytes; thread = (row, half), 4 code dwords each.
-        {
-            const int i = tid >> 1;
-            const int h = tid & 1;
-            const int row = nb + i;
-            uint4 C = make_uint4(0u, 0u, 0u, 0u);
-            if (row < n) C = *reinterpret_cast<const uint4*>(codes + (size_t)row * k4 + (size_t)g * 32 + h * 16);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t d = word_of(C, c);
-                const int t = 4 * h + c;
-                Bs[i * 8 + (t ^ (i & 7))] =
-                    make_uint4(expand_plane<0>(d), expand_plane<1>(d), expand_plane<2>(d), expand_plane<3>(d));
-            }
-        }
-        if (tid < kBM) {
-            const int row = mb + tid;
-            xsS[tid] = row < m ? xs[(size_t)row * groups + g] : 0.0f;
-        } else {
-            const int i = tid - kBM;
-            const int row = nb + i;
-            wsS[i] = row < n ? __half2float(__ushort_as_half(scales[(size_t)row * groups + g])) : 0.0f;
-        }
-        __syncthreads();
+        const int buf = g & 1;
+        if (g + 1 < groups) load_stage(g + 1);
 
-        v16i D[2][2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) D[a][b][r] = 0;
-
+        v16i D[MT][NT];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int t = 2 * kk + hi;
-            v4i af[2], bf[2];
+            v4i af[MT], bf[NT];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int i = wm * 64 + mt * 32 + l32;
-                const uint4 v = As[i * 8 + (t ^ (i & 7))];
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint4 v = As[buf][af_slot[kk][mt]];
                 af[mt] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
             }
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int i = wn * 64 + nt * 32 + l32;
-                const uint4 v = Bs[i * 8 + (t ^ (i & 7))];
+            for (int nt = 0; nt < NT; ++nt) {
+                const uint4 v = Bs[buf][bf_slot[kk][nt]];
                 bf[nt] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
             }
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-                    D[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[nt], D[mt][nt], 0, 0, 0);
+                for (int nt = 0; nt < NT; ++nt) {
+                    if (kk == 0)
+                        D[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[nt], v16i{}, 0, 0, 0);
+                    else
+                        D[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[nt], D[mt][nt], 0, 0, 0);
+                }
         }
 
-        // Rescale: lane holds column n = l32 of each 32x32 tile and rows
+        // Rescale: lane holds column l32 of each 32x32 tile and rows
         // 8*(r/4) + 4*hi + (r%4), r = 0..15.
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const float wsv = wsS[wn * 64 + nt * 32 + l32];
+        for (int nt = 0; nt < NT; ++nt) {
+            const float wsv = wsS[buf][wn * (BN / 2) + nt * 32 + l32];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    const float4 xv = *reinterpret_cast<const float4*>(&xsS[wm * 64 + mt * 32 + rb * 8 + hi * 4]);
+                    const float4 xv =
+                        *reinterpret_cast<const float4*>(&xsS[buf][wm * (BM / 2) + mt * 32 + rb * 8 + hi * 4]);
                     const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = rb * 4 + e;
-                        acc[mt][nt][r] += ((float)D[mt][nt][r] * xa[e]) * wsv;
+                        acc[mt][nt][r] = __builtin_fmaf((float)D[mt][nt][r] * xa[e], wsv, acc[mt][nt][r]);
                     }
                 }
             }
         }
+        if (g + 1 < groups) store_stage(buf ^ 1);
         __syncthreads();
     }
 
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int col = nb + wn * 64 + nt * 32 + l32;
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = nb + wn * (BN / 2) + nt * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = mb + wm * 64 + mt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                const int row = mb + wm * (BM / 2) + mt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
                 if (row < m && col < n) y[(size_t)row * n + col] = acc[mt][nt][r];
             }
         }
 }
 
-hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
-                          int64_t n, int64_t k, float* y, hipStream_t stream) {
-    const uint8_t* codes = planes;
+namespace {
+
+template <int BM, int BN, bool PLANE_A>
+hipError_t launch_tile(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
+                       int64_t k, float* y, hipStream_t stream) {
     const uint16_t* scales = reinterpret_cast<const uint16_t*>(planes + n * (k / 4));
-    const dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
+    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
     clear_stale_error();
-    hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, stream, q, xs, codes, scales, y, (int)m,
-                       (int)n, (int)k, (int)(k / 128));
+    hipLaunchKernelGGL((prefill_kernel<BM, BN, PLANE_A>), grid, dim3(256), 0, stream, q, xs, planes, scales, y,
+                       (int)m, (int)n, (int)k, (int)(k / 128));
     return hipGetLastError();
+}
+
+template <bool PLANE_A>
+hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
+                           int64_t k, float* y, int tile, hipStream_t stream) {
+    switch (tile) {
+        case 1: return launch_tile<128, 128, PLANE_A>(q, xs, planes, m, n, k, y, stream);
+        case 2: return launch_tile<64, 128, PLANE_A>(q, xs, planes, m, n, k, y, stream);
+        case 3: return launch_tile<64, 64, PLANE_A>(q, xs, planes, m, n, k, y, stream);
+        case 4: return launch_tile<128, 64, PLANE_A>(q, xs, planes, m, n, k, y, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+// Tile choice: 64x128 when its grid still gives every CU two workgroups
+// (512 on the 256-CU part), else 64x64 -- for either activation order (the
+// 128x64 tile, which shares each code decode among more rows, measured no
+// better).  The 128x128 tile needs more than 256 registers per lane (one
+// wave per SIMD); it stays available through the tuning entry points.
+int default_prefill_tile(int64_t m, int64_t n, bool plane_a) {
+    (void)plane_a;
+    const int64_t wgs = ((n + 127) / 128) * ((m + 63) / 64);
+    return wgs >= 512 ? 2 : 3;
+}
+
+hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
+                          int64_t n, int64_t k, float* y, int tile, bool plane_a, hipStream_t stream) {
+    if (tile == 0) tile = default_prefill_tile(m, n, plane_a);
+    return plane_a ? launch_any_tile<true>(q, xs, planes, m, n, k, y, tile, stream)
+                   : launch_any_tile<false>(q, xs, planes, m, n, k, y, tile, stream);
 }
 
 }  // namespace pq2

@@ -118,10 +118,33 @@ int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int
  * m >= 128): same definition and output as pq2_matmul_small_m (page
  * "Baseline and the integer breakthrough", "Use matrix hardware for
  * prefill"; page "Kernel experiments", Tests 2 and 7).  Argument rules as
- * for pq2_matmul_small_m, except that 1 <= m <= 65535*128.
+ * for pq2_matmul_small_m, except that 1 <= m <= 65535*64.
  * Errors: EINVAL, ESHAPE, EALIGN, ELAUNCH, EDEVICE. */
 int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream);
+
+/* Tuning hook for the prefill matmul (benchmarks and tests only; same
+ * arguments and result as pq2_matmul_prefill): tile 1 = 128x128, 2 = 64x128,
+ * 3 = 64x64, 4 = 128x64 outputs per workgroup, 0 = the library's choice.
+ * The result does not depend on the tile.  Errors as pq2_matmul_prefill,
+ * plus EINVAL for an unknown tile. */
+int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
+                             int64_t k, float* y, int tile, void* stream);
+
+/* Prefill matmul from plane-order activations (the qp output of
+ * pq2_quantize_act_i8_planes; its qsum is not needed): the same result as
+ * pq2_matmul_prefill on the natural-order q, bit for bit, without the byte
+ * transpose while staging (page "Kernel experiments", Test 21: activations
+ * prepared in the order the decoded codes need).  Argument rules as for
+ * pq2_matmul_prefill, qp 16-byte aligned.
+ * Errors: EINVAL, ESHAPE, EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_prefill_planes(const int8_t* qp, const float* xs, const void* planes, int64_t m, int64_t n,
+                              int64_t k, float* y, void* stream);
+
+/* Tuning hook for pq2_matmul_prefill_planes (tile as for
+ * pq2_matmul_prefill_tuned). */
+int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const void* planes, int64_t m, int64_t n,
+                                    int64_t k, float* y, int tile, void* stream);
 
 /* Tuning hook for the small-m matmul (benchmarks and tests only; same
  * arguments and result as pq2_matmul_small_m).  rows_per_lane in {1,2}

@@ -29,7 +29,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 14
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -72,7 +72,7 @@ def test_quantize_validation():
     assert f(A, 0, 128, 2, 128, A + 16, C, None) == EINVAL  # q overlaps x
 
 
-@pytest.mark.parametrize("name", ["pq2_matmul_small_m", "pq2_matmul_prefill"])
+@pytest.mark.parametrize("name", ["pq2_matmul_small_m", "pq2_matmul_prefill", "pq2_matmul_prefill_planes"])
 def test_matmul_validation(name):
     f = getattr(pq2.lib, name)
     assert f(None, B, C, 1, 8, 128, D, None) == EINVAL
@@ -99,6 +99,15 @@ def test_small_m_column_limit_and_tuning_validation():
     assert t(A, B, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL   # waves
     assert t(A, B, C, 1, 8, 128, D, 0, 0, 3, None) == EINVAL   # engine
     assert t(A, B, C, 17, 8, 128, D, 1, 1, 1, None) == ESHAPE
+
+
+def test_prefill_tile_validation():
+    t = pq2.lib.pq2_matmul_prefill_tuned
+    assert t(A, B, C, 1, 8, 128, D, 5, None) == EINVAL
+    assert pq2.lib.pq2_matmul_prefill_planes_tuned(A, B, C, 1, 8, 128, D, 5, None) == EINVAL
+    assert pq2.lib.pq2_matmul_prefill_planes(A + 8, B, C, 1, 8, 128, D, None) == EALIGN
+    assert t(A, B, C, 1, 8, 128, D, -1, None) == EINVAL
+    assert t(A, B, C, 0, 8, 128, D, 1, None) == ESHAPE
 
 
 def test_quantize_planes_validation():

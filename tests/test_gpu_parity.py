@@ -315,6 +315,9 @@ def test_prefill_workloads_sampled(name):
         q, xs, qo, xso = quantise_both(x[:m].contiguous())
         y = gpu_matmul(pq2.pq2_matmul_prefill, q, xs, planes, w.n)
         assert np.all(np.isfinite(y))
+        qp, xsp, _ = gpu_quantize_planes(x[:m].contiguous().to(DEV))
+        yp = gpu_matmul(pq2.pq2_matmul_prefill_planes, qp, xsp, planes, w.n)
+        assert np.array_equal(yp.view(np.uint32), y.view(np.uint32)), "plane-order prefill differs"
         rng = np.random.default_rng(m)
         mi = np.concatenate([[0, m - 1, 0, m - 1], rng.integers(0, m, 1500)])
         ni = np.concatenate([[0, 0, w.n - 1, w.n - 1], rng.integers(0, w.n, 1500)])
@@ -328,6 +331,28 @@ def test_prefill_workloads_sampled(name):
             ni1 = np.arange(0, w.n, w.n // 64)[:64]
             y1_ref, b1 = oracle.matmul_raw_sample(qo, xso, raw, w.n, w.k, mi1, ni1)
             assert_within(y_first[0, ni1], y1_ref, b1, f"{name} m=1")
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+def test_prefill_tiles(tile):
+    """Every workgroup tile, from natural- and plane-order activations, gives
+    outputs within the bound, with ragged row, column and group tails, and
+    the same bits as the default tile."""
+    pq2 = _pq2()
+    m, n, k = 200, 333, 1408
+    announce(f"prefill tile={tile}")
+    raw = workloads.make_raw_weights(n, k, seed=120 + tile, codes="ternary+3", row_pad=3)
+    x = workloads.make_activations(m, k, 121, "laplace")
+    q, xs, qo, xso = quantise_both(x)
+    planes = gpu_planes(raw, n, k)
+    y = gpu_matmul(pq2.pq2_matmul_prefill_tuned, q, xs, planes, n, tile=tile)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    assert_within(y, y_ref, bound, f"prefill tile={tile}")
+    y0 = gpu_matmul(pq2.pq2_matmul_prefill, q, xs, planes, n)
+    assert np.array_equal(y.view(np.uint32), y0.view(np.uint32)), "tile changed the bits"
+    qp, xsp, _ = gpu_quantize_planes(x.to(DEV))
+    yp = gpu_matmul(pq2.pq2_matmul_prefill_planes_tuned, qp, xsp, planes, n, tile=tile)
+    assert np.array_equal(yp.view(np.uint32), y0.view(np.uint32)), "plane-order prefill changed the bits"
 
 
 def test_prefill_matches_small_m():
