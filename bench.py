@@ -10,7 +10,8 @@ A step is one pass of the per-call hot path over one batch: for each M in
 1..4, quantise the bf16 activations to INT8 (pq2_quantize_act_i8) and run the
 small-m matmul (pq2_matmul_small_m) against the prepared planes.  The
 plane-order variant (pq2_quantize_act_i8_planes + pq2_matmul_small_m_planes,
-same result bits) is timed per M as well and reported beside it.  Weight
+same result bits) is timed per M as well and reported beside it, and so is
+the one-launch pq2_matmul_small_m_fused (same bits again).  Weight
 preparation (pq2_prepare_planes) is one-time and outside the timing.  Every
 step reads the next of R prepared-plane copies (>= 1 GiB in total, four
 times the 256 MB Infinity Cache), so weights stream from HBM.  Steps are
@@ -256,12 +257,20 @@ def main():
                 pq2.pq2_quantize_act_i8_planes(x[:m], qp, pxs, qsum, stream=stream)
                 pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
 
+        yf = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+        def fused(m=m, yf=yf):
+            for c in range(copies):
+                pq2.pq2_matmul_small_m_fused(x[:m], pool[c], yf, stream=stream)
+
         t_mm = time_graph(torch, Graph(torch, mm, stream), stream, reps) / copies * 1e3
         t_full = time_graph(torch, Graph(torch, full, stream), stream, reps) / copies * 1e3
         t_mm_p = time_graph(torch, Graph(torch, mm_planes, stream), stream, reps) / copies * 1e3
         t_full_p = time_graph(torch, Graph(torch, full_planes, stream), stream, reps) / copies * 1e3
+        t_fused = time_graph(torch, Graph(torch, fused, stream), stream, reps) / copies * 1e3
         torch.cuda.synchronize()
         assert torch.equal(py, y), f"plane-order and natural-order outputs differ at M={m}"
+        assert torch.equal(yf, y), f"fused and two-launch outputs differ at M={m}"
         gbs = matmul_bytes(m, n, k) / (t_mm * 1e-6) / 1e9
         per_m[str(m)] = {
             "matmul_us": round(t_mm, 3),
@@ -270,11 +279,13 @@ def main():
             "complete_call_us": round(t_full, 3),
             "planes_matmul_us": round(t_mm_p, 3),
             "planes_complete_call_us": round(t_full_p, 3),
+            "fused_call_us": round(t_fused, 3),
             "matmul_bytes": matmul_bytes(m, n, k),
         }
         log(f"[bench] M={m}: matmul {t_mm:.3f} us ({gbs:.0f} GB/s, "
             f"{100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S:.1f}% of 8 TB/s), complete call {t_full:.3f} us; "
-            f"plane order: matmul {t_mm_p:.3f} us, complete call {t_full_p:.3f} us")
+            f"plane order: matmul {t_mm_p:.3f} us, complete call {t_full_p:.3f} us; "
+            f"fused quantise+matmul {t_fused:.3f} us")
 
     tot_bytes = sum(v["matmul_bytes"] for v in per_m.values())
     tot_us = sum(v["matmul_us"] for v in per_m.values())

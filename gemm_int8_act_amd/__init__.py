@@ -39,6 +39,8 @@ EXPORTED = (
     "pq2_matmul_prefill_tuned",
     "pq2_matmul_prefill_planes",
     "pq2_matmul_prefill_planes_tuned",
+    "pq2_matmul_small_m_fused",
+    "pq2_matmul_small_m_fused_tuned",
 )
 
 
@@ -96,6 +98,10 @@ def _load_library():
     lib.pq2_matmul_prefill_planes.restype = i32
     lib.pq2_matmul_prefill_planes_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, p]
     lib.pq2_matmul_prefill_planes_tuned.restype = i32
+    lib.pq2_matmul_small_m_fused.argtypes = [p, i32, i64, p, i64, i64, i64, p, p]
+    lib.pq2_matmul_small_m_fused.restype = i32
+    lib.pq2_matmul_small_m_fused_tuned.argtypes = [p, i32, i64, p, i64, i64, i64, p, i32, i32, i32, p]
+    lib.pq2_matmul_small_m_fused_tuned.restype = i32
     return lib
 
 
@@ -204,6 +210,31 @@ def pq2_matmul_small_m(q, xs, planes, y, stream=None) -> None:
 def pq2_matmul_small_m_tuned(q, xs, planes, y, rows_per_lane=0, max_waves=0, engine=0, stream=None) -> None:
     _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows_per_lane, max_waves, engine,
                                         _stream(stream)), "pq2_matmul_small_m_tuned")
+
+
+def _fused_args(x, planes, y):
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if planes.dtype != torch.uint8 or y.dtype != torch.float32 or not planes.is_contiguous() or not y.is_contiguous():
+        raise ValueError("planes contiguous uint8 and y contiguous float32 expected")
+    m, k = x.shape
+    n = y.shape[1]
+    if y.shape[0] != m or planes.numel() < n * (k // 128) * 34:
+        raise ValueError("shape mismatch between x, planes and y")
+    return (_dev_ptr(x, "x"), _dtype_code(x), x.stride(0), _dev_ptr(planes, "planes"), m, n, k, _dev_ptr(y, "y"))
+
+
+def pq2_matmul_small_m_fused(x, planes, y, stream=None) -> None:
+    """Quantise x ([m][k] bf16/f16/f32, unit column stride, any row stride)
+    and multiply in one launch: the y of pq2_quantize_act_i8 followed by
+    pq2_matmul_small_m, bit for bit, 1 <= m <= 16."""
+    _check(lib.pq2_matmul_small_m_fused(*_fused_args(x, planes, y), _stream(stream)), "pq2_matmul_small_m_fused")
+
+
+def pq2_matmul_small_m_fused_tuned(x, planes, y, rows_per_lane=0, max_waves=0, engine=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_fused_tuned(*_fused_args(x, planes, y), rows_per_lane, max_waves, engine,
+                                              _stream(stream)), "pq2_matmul_small_m_fused_tuned")
 
 
 def pq2_matmul_prefill(q, xs, planes, y, stream=None) -> None:

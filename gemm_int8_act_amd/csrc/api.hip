@@ -62,8 +62,8 @@ int check_matmul_args(const int8_t* q, const float* xs, const void* planes, int6
 
 // Default small-m configuration with the caller's overrides (0 = default).
 int small_m_config(int64_t m, int64_t n, int64_t k, int rows_per_lane, int max_waves, int engine,
-                   pq2::SmallMConfig* cfg) {
-    *cfg = pq2::default_small_m_config(m, n, k);
+                   pq2::SmallMConfig* cfg, bool fused = false) {
+    *cfg = fused ? pq2::default_small_m_fused_config(m, n, k) : pq2::default_small_m_config(m, n, k);
     if (rows_per_lane) cfg->rows_per_lane = rows_per_lane;
     if (max_waves) cfg->max_waves = max_waves;
     if (engine) cfg->engine = engine;
@@ -176,6 +176,34 @@ int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* plane
 int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream) {
     return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, 0, stream);
+}
+
+int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes,
+                                   int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
+                                   int engine, void* stream) {
+    if (!x || !planes || !y) return PQ2_EINVAL;
+    if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
+    if (m < 1 || m > PQ2_MAX_SMALL_M || n < 1 || n > kMaxN) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (x_row_stride_elems < k) return PQ2_ESHAPE;
+    const int esize = dtype == PQ2_F32 ? 4 : 2;
+    const size_t xbytes = ((size_t)(m - 1) * x_row_stride_elems + k) * esize;
+    if (xbytes >= ((size_t)1 << 31)) return PQ2_ESHAPE;  // the kernel addresses x with 32-bit offsets
+    if (!aligned(x, 16) || (x_row_stride_elems * esize) % 16 || !aligned(planes, 16) || !aligned(y, 4))
+        return PQ2_EALIGN;
+    const size_t ybytes = (size_t)m * n * 4;
+    if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, planes, (size_t)n * (k / kGroup) * 34))
+        return PQ2_EINVAL;
+    pq2::SmallMConfig cfg;
+    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, engine, &cfg, true)) return rc;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m_fused(x, dtype, x_row_stride_elems, static_cast<const uint8_t*>(planes),
+                                                   m, n, k, y, cfg, (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_fused(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes, int64_t m,
+                             int64_t n, int64_t k, float* y, void* stream) {
+    return pq2_matmul_small_m_fused_tuned(x, dtype, x_row_stride_elems, planes, m, n, k, y, 0, 0, 0, stream);
 }
 
 int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,

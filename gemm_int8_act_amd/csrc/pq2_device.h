@@ -48,6 +48,14 @@ __device__ __forceinline__ int sum8_i(int v) {
     return v;
 }
 
+// Max over each aligned group of 8 lanes; all lanes of the group agree.
+__device__ __forceinline__ float max8_f(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    return v;
+}
+
 // Max over each aligned group of 16 lanes (one DPP row); all lanes agree.
 __device__ __forceinline__ float max16_f(float v) {
     v = fmaxf(v, dpp_f<kDppXor1>(v));

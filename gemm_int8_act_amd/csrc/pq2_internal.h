@@ -28,6 +28,7 @@ struct SmallMConfig {
 };
 
 SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k);
+SmallMConfig default_small_m_fused_config(int64_t m, int64_t n, int64_t k);  // same k split
 
 // Natural-order q (the kernel transposes blocks and forms the group sums).
 // Returns hipErrorInvalidValue for a configuration the library has no kernel for.
@@ -39,6 +40,12 @@ hipError_t launch_small_m(const int8_t* q, const float* xs, const uint8_t* plane
 hipError_t launch_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const uint8_t* planes,
                                  int64_t m, int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
                                  hipStream_t stream);
+
+// Unquantised activations x (dtype 0 bf16, 1 f16, 2 f32; rows x_stride
+// elements apart), quantised inside the matmul kernel with the quantiser's
+// exact results: same output bits as launch_quantize + launch_small_m.
+hipError_t launch_small_m_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* planes, int64_t m,
+                                int64_t n, int64_t k, float* y, const SmallMConfig& cfg, hipStream_t stream);
 
 // tile: 0 = default, 1 = 128x128, 2 = 64x128, 3 = 64x64, 4 = 128x64 outputs
 // per workgroup.  plane_a: q is in plane order (pq2_quantize_act_i8_planes).

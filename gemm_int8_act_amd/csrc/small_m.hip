@@ -42,6 +42,11 @@
 //    column 4 dot instructions per code dword) and small_m_mfma_kernel (INT8
 //    matrix cores, whose work per code dword does not grow with the number
 //    of columns).  The library picks one per shape.
+//  * The fused entry points start from the unquantised activations x: the
+//    lanes that stage a group's 16-byte blocks quantise them first (each
+//    workgroup quantises the k slice it reads), with results bit-identical to
+//    the quantiser kernel, so quantiser + matmul become one launch with the
+//    same output bits.
 //  * Summation order of an output: each lane accumulates its group terms
 //    acc = fma((float)dot * xs, ws, acc) over its segments in order (no other
 //    contraction: the pragma below), a fixed DPP tree adds the 8 lanes of a
@@ -61,6 +66,113 @@ constexpr int kRowSlots = 8;     // row slots per wave
 constexpr int kBlockPitch = 9;   // LDS quads per group (8 + 1 pad; pad dword 0 = sum(q))
 constexpr int kSegQuads = kGroupLanes * kBlockPitch;  // LDS quads per (segment, column)
 
+// Where a kernel's activations come from.
+enum : int {
+    kSrcPlanes = 0,   // plane-order q and group sums (pq2_quantize_act_i8_planes)
+    kSrcNatural = 1,  // natural-order q (pq2_quantize_act_i8): transposed and summed while staged
+    kSrcBf16 = 2,     // unquantised x of this element type, quantised while staged
+    kSrcF16 = 3,
+    kSrcF32 = 4,
+};
+constexpr bool src_fused(int src) { return src >= kSrcBf16; }
+constexpr int src_esize(int src) { return src == kSrcF32 ? 4 : 2; }
+constexpr int src_xloads(int src) { return src == kSrcF32 ? 4 : 2; }  // 16-byte loads per lane and group
+
+// Bytes 0 of a, b, c, d packed into one dword (byte i from the i-th argument).
+__device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+    return ab | (cd << 16);
+}
+
+// Group-128 INT8 quantisation (page "Baseline and the integer
+// breakthrough", "Calculate with small integers" step 1) of one row slot's
+// group, 16 elements per lane: lane j of the slot holds elements
+// 16j..16j+15 in v.  Returns the lane's 16 codes in plane order (dword s =
+// codes 16j + s, +4, +8, +12) and sets gsum (group sum of q, all 8 lanes)
+// and scale (max|x| / 127, correctly rounded).  The codes equal the
+// definition q = clamp(rint(RN(x / d)), +-127), d = scale or 1 for an
+// all-zero group, bit for bit:
+//  * r = 1/d from the hardware reciprocal refined by one Newton step lies
+//    within 2^-22 (relative) of 1/d, so t = RN(x * r) differs from x / d by
+//    at most 127.0001 * (2^-22 + 2^-24) and from RN(x / d) by less than
+//    4.3e-5 < 2^-14 whenever d is normal (|x / d| <= 127 * (1 + 2^-23), and
+//    half an ulp of RN(x / d) below 128 is 2^-18);
+//  * so if t lies at least 2^-14 from every half-integer, rint(t) is
+//    rint(RN(x / d)).  Adding 1.5 * 2^23 rounds t to that integer in the
+//    low mantissa bits, whose low byte is the two's-complement code, and
+//    |t| < 127.5 makes the clamp a no-op;
+//  * otherwise (a near-tie in any of the lane's 16 elements, or d
+//    subnormal) the lane repeats the definition with IEEE divisions.
+__device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum, float& scale) {
+#pragma clang fp contract(off)
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = max8_f(amax);
+    scale = amax / 127.0f;
+    const float d = scale > 0.0f ? scale : 1.0f;
+    const float r0 = __builtin_amdgcn_rcpf(d);
+    const float r = __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
+    constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+    uint32_t bits[16];
+    float worst = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float t = v[e] * r;
+        const float s = t + kRound;
+        worst = fmaxf(worst, fabsf(t - (s - kRound)));
+        bits[e] = __float_as_uint(s);
+    }
+    if (!(d >= 0x1p-126f && worst <= 0.5f - 0x1p-14f)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float qf = fminf(127.0f, fmaxf(-127.0f, rintf(v[e] / d)));
+            bits[e] = (uint32_t)(int)qf;
+        }
+    }
+    uint4 out;
+    out.x = low_bytes4(bits[0], bits[4], bits[8], bits[12]);
+    out.y = low_bytes4(bits[1], bits[5], bits[9], bits[13]);
+    out.z = low_bytes4(bits[2], bits[6], bits[10], bits[14]);
+    out.w = low_bytes4(bits[3], bits[7], bits[11], bits[15]);
+    int s = dot4(out.x, 0x01010101u, 0);
+    s = dot4(out.y, 0x01010101u, s);
+    s = dot4(out.z, 0x01010101u, s);
+    s = dot4(out.w, 0x01010101u, s);
+    gsum = sum8_i(s);
+    return out;
+}
+
+// The 16 elements of x a lane quantises, from its SRC-typed 16-byte loads.
+template <int SRC>
+__device__ __forceinline__ void x_to_float16(const uint4 (&w)[src_xloads(SRC)], float (&v)[16]) {
+    if constexpr (SRC == kSrcF32) {
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            v[4 * l + 0] = __uint_as_float(w[l].x);
+            v[4 * l + 1] = __uint_as_float(w[l].y);
+            v[4 * l + 2] = __uint_as_float(w[l].z);
+            v[4 * l + 3] = __uint_as_float(w[l].w);
+        }
+    } else {
+#pragma unroll
+        for (int l = 0; l < 2; ++l) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t d = word_of(w[l], i);
+                if constexpr (SRC == kSrcBf16) {
+                    v[8 * l + 2 * i] = __uint_as_float(d << 16);
+                    v[8 * l + 2 * i + 1] = __uint_as_float(d & 0xFFFF0000u);
+                } else {
+                    v[8 * l + 2 * i] = __half2float(__ushort_as_half((unsigned short)(d & 0xFFFFu)));
+                    v[8 * l + 2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(d >> 16)));
+                }
+            }
+        }
+    }
+}
+
 // Plane-order pairing of activation dwords with code planes, per half group.
 // acc0/acc1/acc23 are the three masked-plane accumulators.
 template <int R>
@@ -79,12 +191,15 @@ __device__ __forceinline__ void half_group_dot(const uint4 (&P)[4], const uint4 
     }
 }
 
-template <int MC, int R, int SEGS, bool NATURAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 && R == 1 && MC <= 4 ? 7 : 1))) void small_m_kernel(
+template <int MC, int R, int SEGS, int SRC>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 && R == 1 && MC <= (src_fused(SRC) ? 1 : 4) ? 7 : 1))) void small_m_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const int32_t* __restrict__ qsum,
+    const void* __restrict__ x, int64_t x_stride,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y, int n,
     int k, int groups, int nseg, int segs_per_wave, int mtotal) {
 #pragma clang fp contract(off)
+    constexpr bool FUSED = src_fused(SRC);
+    constexpr int XL = src_xloads(SRC);
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int RB = kRowSlots * R;
     constexpr int WAVE_QUADS = MC * kSegQuads;  // one segment staged at a time
@@ -113,10 +228,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
 
     const auto code_rs = make_rsrc(codes + (size_t)row_base * k4, (uint32_t)rows_here * k4);
     const auto scale_rs = make_rsrc(scales + (size_t)row_base * groups, (uint32_t)(rows_here * groups * 2));
-    const auto q_rs = make_rsrc(q + (size_t)m0 * k, (uint32_t)(mcount * k));
-    const auto xs_rs = make_rsrc(xs + (size_t)m0 * groups, (uint32_t)(mcount * groups * 4));
-    const auto qs_rs = make_rsrc(NATURAL ? nullptr : qsum + (size_t)m0 * groups,
-                                 NATURAL ? 0u : (uint32_t)(mcount * groups * 4));
+    const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
+    const auto xs_rs = make_rsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
+    const auto qs_rs = make_rsrc(SRC == kSrcPlanes ? qsum + (size_t)m0 * groups : nullptr,
+                                 SRC == kSrcPlanes ? (uint32_t)(mcount * groups * 4) : 0u);
+    const auto x_rs = make_rsrc(
+        FUSED ? static_cast<const unsigned char*>(x) + (size_t)m0 * x_stride * src_esize(SRC) : nullptr,
+        FUSED ? (uint32_t)(((int64_t)(mcount - 1) * x_stride + k) * src_esize(SRC)) : 0u);
 
     float acc[MC][R];
 #pragma unroll
@@ -127,6 +245,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
     for (int base = seg_begin; base < seg_end; base += SEGS) {
         // 1. Activation blocks, scales and group sums of this step (small, L2-resident) ...
         uint4 qv[SEGS][MC];
+        uint4 xv[SEGS][MC][FUSED ? XL : 1];
         uint32_t xsv[SEGS][MC], tv[SEGS][MC];
 #pragma unroll
         for (int si = 0; si < SEGS; ++si) {
@@ -137,9 +256,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
             for (int m = 0; m < MC; ++m) {
                 const bool qok = sok && gq < groups && m < mcount;
                 const bool gok = sok && gs < groups && m < mcount;
-                qv[si][m] = buf_load16(q_rs, qok ? (uint32_t)(m * k + gq * 128 + j * 16) : kBufferOOB);
-                xsv[si][m] = buf_load4(xs_rs, gok ? (uint32_t)((m * groups + gs) * 4) : kBufferOOB);
-                if constexpr (!NATURAL)
+                if constexpr (FUSED) {
+                    // Elements 16j..16j+15 of group gq (out-of-range groups read zero).
+                    const uint32_t off = (uint32_t)((m * x_stride + gq * 128 + j * 16) * src_esize(SRC));
+#pragma unroll
+                    for (int l = 0; l < XL; ++l) xv[si][m][l] = buf_load16(x_rs, qok ? off + 16u * l : kBufferOOB);
+                } else {
+                    qv[si][m] = buf_load16(q_rs, qok ? (uint32_t)(m * k + gq * 128 + j * 16) : kBufferOOB);
+                    xsv[si][m] = buf_load4(xs_rs, gok ? (uint32_t)((m * groups + gs) * 4) : kBufferOOB);
+                }
+                if constexpr (SRC == kSrcPlanes)
                     tv[si][m] = buf_load4(qs_rs, gok ? (uint32_t)((m * groups + gs) * 4) : kBufferOOB);
             }
         }
@@ -174,7 +300,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
 #pragma unroll
             for (int m = 0; m < MC; ++m) {
                 uint4 v = qv[si][m];
-                if constexpr (NATURAL) {
+                if constexpr (SRC == kSrcNatural) {
                     int s = dot4(v.x, 0x01010101u, 0);
                     s = dot4(v.y, 0x01010101u, s);
                     s = dot4(v.z, 0x01010101u, s);
@@ -182,6 +308,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
                     s = sum8_i(s);  // sum(q) of group `slot`, in all 8 lanes of the slot
                     v = to_plane_order(v);
                     if (j == 0) *reinterpret_cast<int*>(wr_ptr + (m * kSegQuads + 8) * 16) = s;
+                }
+                if constexpr (FUSED) {
+                    float xf[16];
+                    x_to_float16<SRC>(xv[si][m], xf);
+                    int s;
+                    float scale;
+                    v = quantize_lane16(xf, s, scale);  // group `slot`, all 8 lanes of the slot agree
+                    if (j == 0)
+                        *reinterpret_cast<uint2*>(wr_ptr + (m * kSegQuads + 8) * 16) =
+                            make_uint2((uint32_t)s, __float_as_uint(scale));
                 }
                 *reinterpret_cast<uint4*>(wr_ptr + m * kSegQuads * 16) = v;
             }
@@ -226,11 +362,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
 #pragma unroll
                 for (int m = 0; m < MC; ++m) {
                     int sq;
-                    if constexpr (NATURAL)
-                        sq = *reinterpret_cast<const int*>(qs_ptr + m * kSegQuads * 16);
-                    else
-                        sq = (int)tv[si][m];
-                    const float xsf = __uint_as_float(xsv[si][m]);
+                    float xsf;
+                    if constexpr (FUSED) {
+                        const uint2 meta = *reinterpret_cast<const uint2*>(qs_ptr + m * kSegQuads * 16);
+                        sq = (int)meta.x;
+                        xsf = __uint_as_float(meta.y);
+                    } else {
+                        sq = SRC == kSrcNatural ? *reinterpret_cast<const int*>(qs_ptr + m * kSegQuads * 16)
+                                                : (int)tv[si][m];
+                        xsf = __uint_as_float(xsv[si][m]);
+                    }
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         // Lane h = 0 keeps group j/2 and hands its half of group 4 + j/2
@@ -297,12 +438,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
 // Terms, the lane-serial FP32 accumulation per group class and the final
 // tree ((A0 + A4) + (A1 + A5)) + ((A2 + A6) + (A3 + A7)), then waves in
 // order, are exactly those of small_m_kernel, so both give identical bits.
-template <int MC, int SEGS, bool NATURAL>
+template <int MC, int SEGS, int SRC>
 __global__ __launch_bounds__(512) void small_m_mfma_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const int32_t* __restrict__ qsum,
+    const void* __restrict__ x, int64_t x_stride,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y, int n,
     int k, int groups, int nseg, int segs_per_wave, int mtotal) {
 #pragma clang fp contract(off)
+    constexpr bool FUSED = src_fused(SRC);
+    constexpr int XL = src_xloads(SRC);
     typedef int v4i __attribute__((ext_vector_type(4)));
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int MP = (MC + 1) / 2;  // matrix-core passes, two columns each
@@ -350,10 +494,13 @@ __global__ __launch_bounds__(512) void small_m_mfma_kernel(
 
     const auto code_rs = make_rsrc(codes + (size_t)row_base * k4, (uint32_t)rows_here * k4);
     const auto scale_rs = make_rsrc(scales + (size_t)row_base * groups, (uint32_t)(rows_here * groups * 2));
-    const auto q_rs = make_rsrc(q + (size_t)m0 * k, (uint32_t)(mcount * k));
-    const auto xs_rs = make_rsrc(xs + (size_t)m0 * groups, (uint32_t)(mcount * groups * 4));
-    const auto qs_rs = make_rsrc(NATURAL ? nullptr : qsum + (size_t)m0 * groups,
-                                 NATURAL ? 0u : (uint32_t)(mcount * groups * 4));
+    const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
+    const auto xs_rs = make_rsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
+    const auto qs_rs = make_rsrc(SRC == kSrcPlanes ? qsum + (size_t)m0 * groups : nullptr,
+                                 SRC == kSrcPlanes ? (uint32_t)(mcount * groups * 4) : 0u);
+    const auto x_rs = make_rsrc(
+        FUSED ? static_cast<const unsigned char*>(x) + (size_t)m0 * x_stride * src_esize(SRC) : nullptr,
+        FUSED ? (uint32_t)(((int64_t)(mcount - 1) * x_stride + k) * src_esize(SRC)) : 0u);
 
     float acc[MP][2];
 #pragma unroll
@@ -362,6 +509,7 @@ __global__ __launch_bounds__(512) void small_m_mfma_kernel(
     for (int base = seg_begin; base < seg_end; base += SEGS) {
         // 1. Activation blocks and per-group metadata (small, L2-resident) ...
         uint4 qv[SEGS][MC];
+        uint4 xv[SEGS][MC][FUSED ? XL : 1];
         uint32_t xsv[SEGS][MC], tv[SEGS][MC];
 #pragma unroll
         for (int si = 0; si < SEGS; ++si) {
@@ -370,10 +518,16 @@ __global__ __launch_bounds__(512) void small_m_mfma_kernel(
 #pragma unroll
             for (int m = 0; m < MC; ++m) {
                 const bool qok = sok && gq < groups && m < mcount;
-                qv[si][m] = buf_load16(q_rs, qok ? (uint32_t)(m * k + gq * 128 + j * 16) : kBufferOOB);
-                const uint32_t moff = (qok && j == 0) ? (uint32_t)((m * groups + gq) * 4) : kBufferOOB;
-                xsv[si][m] = buf_load4(xs_rs, moff);
-                if constexpr (!NATURAL) tv[si][m] = buf_load4(qs_rs, moff);
+                if constexpr (FUSED) {
+                    const uint32_t off = (uint32_t)((m * x_stride + gq * 128 + j * 16) * src_esize(SRC));
+#pragma unroll
+                    for (int l = 0; l < XL; ++l) xv[si][m][l] = buf_load16(x_rs, qok ? off + 16u * l : kBufferOOB);
+                } else {
+                    qv[si][m] = buf_load16(q_rs, qok ? (uint32_t)(m * k + gq * 128 + j * 16) : kBufferOOB);
+                    const uint32_t moff = (qok && j == 0) ? (uint32_t)((m * groups + gq) * 4) : kBufferOOB;
+                    xsv[si][m] = buf_load4(xs_rs, moff);
+                    if constexpr (SRC == kSrcPlanes) tv[si][m] = buf_load4(qs_rs, moff);
+                }
             }
         }
         // 2. ... then the code loads of the step: two spans of four groups per segment.
@@ -407,19 +561,28 @@ __global__ __launch_bounds__(512) void small_m_mfma_kernel(
             for (int m = 0; m < MC; ++m) {
                 uint4 v = qv[si][m];
                 int s;
-                if constexpr (NATURAL) {
+                uint32_t scale_bits;
+                if constexpr (FUSED) {
+                    float xf[16];
+                    x_to_float16<SRC>(xv[si][m], xf);
+                    float scale;
+                    v = quantize_lane16(xf, s, scale);
+                    scale_bits = __float_as_uint(scale);
+                } else if constexpr (SRC == kSrcNatural) {
                     s = dot4(v.x, 0x01010101u, 0);
                     s = dot4(v.y, 0x01010101u, s);
                     s = dot4(v.z, 0x01010101u, s);
                     s = dot4(v.w, 0x01010101u, s);
                     s = sum8_i(s);
                     v = to_plane_order(v);
+                    scale_bits = xsv[si][m];
                 } else {
                     s = (int)tv[si][m];
+                    scale_bits = xsv[si][m];
                 }
                 unsigned char* blk = wr_ptr + m * kSegQuads * 16;
                 *reinterpret_cast<uint4*>(blk) = v;
-                if (j == 0) *reinterpret_cast<uint2*>(blk + 8 * 16) = make_uint2((uint32_t)s, xsv[si][m]);
+                if (j == 0) *reinterpret_cast<uint2*>(blk + 8 * 16) = make_uint2((uint32_t)s, scale_bits);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -500,6 +663,8 @@ struct Launch {
     const int8_t* q;
     const float* xs;
     const int32_t* qsum;
+    const void* x;
+    int64_t x_stride;
     const uint8_t* planes;
     int64_t m, n, k;
     float* y;
@@ -507,9 +672,9 @@ struct Launch {
     hipStream_t stream;
 };
 
-template <int MC, int R, int SEGS, bool NAT>
+template <int MC, int R, int SEGS, int SRC>
 hipError_t launch_one(const Launch& a) {
-    auto kern = small_m_kernel<MC, R, SEGS, NAT>;
+    auto kern = small_m_kernel<MC, R, SEGS, SRC>;
     const size_t lds = lds_bytes(MC, SEGS, a.waves, kRowSlots * R);
     static bool attr_set = false;  // one instantiation = one static
     if (!attr_set) {
@@ -521,39 +686,44 @@ hipError_t launch_one(const Launch& a) {
     const uint16_t* scales = reinterpret_cast<const uint16_t*>(a.planes + a.n * (a.k / 4));
     const dim3 grid((unsigned)((a.n + kRowSlots * R - 1) / (kRowSlots * R)), (unsigned)a.chunks);
     clear_stale_error();
-    hipLaunchKernelGGL(kern, grid, dim3(64 * a.waves), lds, a.stream, a.q, a.xs, a.qsum, a.planes, scales, a.y,
-                       (int)a.n, (int)a.k, (int)(a.k / 128), a.nseg, a.per_wave, (int)a.m);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * a.waves), lds, a.stream, a.q, a.xs, a.qsum, a.x, a.x_stride, a.planes,
+                       scales, a.y, (int)a.n, (int)a.k, (int)(a.k / 128), a.nseg, a.per_wave, (int)a.m);
     return hipGetLastError();
 }
 
-template <int MC, int R, bool NAT>
+// Segments per load step: 1 or 2 (the register cap in launch_any never asks for more).
+template <int MC, int R, int SRC>
 hipError_t pick_segs(const Launch& a, int segs) {
-    switch (segs) {
-        case 1: return launch_one<MC, R, 1, NAT>(a);
-        case 2: return launch_one<MC, R, 2, NAT>(a);
-        case 3: return launch_one<MC, R, 3, NAT>(a);
-        default: return launch_one<MC, R, 4, NAT>(a);
-    }
+    return segs == 1 ? launch_one<MC, R, 1, SRC>(a) : launch_one<MC, R, 2, SRC>(a);
 }
 
-template <int MC, bool NAT>
+template <int MC, int SRC>
 hipError_t pick_rows(const Launch& a, int rows, int segs) {
-    return rows == 1 ? pick_segs<MC, 1, NAT>(a, segs) : pick_segs<MC, 2, NAT>(a, segs);
+    return rows == 1 ? pick_segs<MC, 1, SRC>(a, segs) : pick_segs<MC, 2, SRC>(a, segs);
 }
 
-template <bool NAT>
+// Fused (quantising) instantiations cover up to 4 columns per pass.
+constexpr int max_mc(int src) { return src_fused(src) ? 4 : 8; }
+
+template <int SRC>
 hipError_t pick_mc(const Launch& a, int mc, int rows, int segs) {
     switch (mc) {
-        case 1: return pick_rows<1, NAT>(a, rows, segs);
-        case 2: return pick_rows<2, NAT>(a, rows, segs);
-        case 3: return pick_rows<3, NAT>(a, rows, segs);
-        case 4: return pick_rows<4, NAT>(a, rows, segs);
-        case 5: return pick_rows<5, NAT>(a, rows, segs);
-        case 6: return pick_rows<6, NAT>(a, rows, segs);
-        case 7: return pick_rows<7, NAT>(a, rows, segs);
-        case 8: return pick_rows<8, NAT>(a, rows, segs);
-        default: return hipErrorInvalidValue;
+        case 1: return pick_rows<1, SRC>(a, rows, segs);
+        case 2: return pick_rows<2, SRC>(a, rows, segs);
+        case 3: return pick_rows<3, SRC>(a, rows, segs);
+        case 4: return pick_rows<4, SRC>(a, rows, segs);
+        default: break;
     }
+    if constexpr (max_mc(SRC) == 8) {
+        switch (mc) {
+            case 5: return pick_rows<5, SRC>(a, rows, segs);
+            case 6: return pick_rows<6, SRC>(a, rows, segs);
+            case 7: return pick_rows<7, SRC>(a, rows, segs);
+            case 8: return pick_rows<8, SRC>(a, rows, segs);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 size_t mfma_lds_bytes(int mc, int segs, int waves) {
@@ -561,9 +731,9 @@ size_t mfma_lds_bytes(int mc, int segs, int waves) {
     return (size_t)(waves + 1) * mc * kSegQuads * 16 + (size_t)waves * 4 * mc * kRowSlots * 4;
 }
 
-template <int MC, int SEGS, bool NAT>
+template <int MC, int SEGS, int SRC>
 hipError_t launch_mfma_one(const Launch& a) {
-    auto kern = small_m_mfma_kernel<MC, SEGS, NAT>;
+    auto kern = small_m_mfma_kernel<MC, SEGS, SRC>;
     const size_t lds = mfma_lds_bytes(MC, SEGS, a.waves);
     static bool attr_set = false;
     if (!attr_set) {
@@ -575,74 +745,79 @@ hipError_t launch_mfma_one(const Launch& a) {
     const uint16_t* scales = reinterpret_cast<const uint16_t*>(a.planes + a.n * (a.k / 4));
     const dim3 grid((unsigned)((a.n + kRowSlots - 1) / kRowSlots), (unsigned)a.chunks);
     clear_stale_error();
-    hipLaunchKernelGGL(kern, grid, dim3(64 * a.waves), lds, a.stream, a.q, a.xs, a.qsum, a.planes, scales, a.y,
-                       (int)a.n, (int)a.k, (int)(a.k / 128), a.nseg, a.per_wave, (int)a.m);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * a.waves), lds, a.stream, a.q, a.xs, a.qsum, a.x, a.x_stride, a.planes,
+                       scales, a.y, (int)a.n, (int)a.k, (int)(a.k / 128), a.nseg, a.per_wave, (int)a.m);
     return hipGetLastError();
 }
 
-template <int MC, bool NAT>
+template <int MC, int SRC>
 hipError_t mfma_pick_segs(const Launch& a, int segs) {
-    switch (segs) {
-        case 1: return launch_mfma_one<MC, 1, NAT>(a);
-        case 2: return launch_mfma_one<MC, 2, NAT>(a);
-        case 3: return launch_mfma_one<MC, 3, NAT>(a);
-        default: return launch_mfma_one<MC, 4, NAT>(a);
-    }
+    return segs == 1 ? launch_mfma_one<MC, 1, SRC>(a) : launch_mfma_one<MC, 2, SRC>(a);
 }
 
-template <bool NAT>
+template <int SRC>
 hipError_t mfma_pick_mc(const Launch& a, int mc, int segs) {
     switch (mc) {
-        case 1: return mfma_pick_segs<1, NAT>(a, segs);
-        case 2: return mfma_pick_segs<2, NAT>(a, segs);
-        case 3: return mfma_pick_segs<3, NAT>(a, segs);
-        case 4: return mfma_pick_segs<4, NAT>(a, segs);
-        case 5: return mfma_pick_segs<5, NAT>(a, segs);
-        case 6: return mfma_pick_segs<6, NAT>(a, segs);
-        case 7: return mfma_pick_segs<7, NAT>(a, segs);
-        case 8: return mfma_pick_segs<8, NAT>(a, segs);
-        default: return hipErrorInvalidValue;
+        case 1: return mfma_pick_segs<1, SRC>(a, segs);
+        case 2: return mfma_pick_segs<2, SRC>(a, segs);
+        case 3: return mfma_pick_segs<3, SRC>(a, segs);
+        case 4: return mfma_pick_segs<4, SRC>(a, segs);
+        default: break;
     }
+    if constexpr (max_mc(SRC) == 8) {
+        switch (mc) {
+            case 5: return mfma_pick_segs<5, SRC>(a, segs);
+            case 6: return mfma_pick_segs<6, SRC>(a, segs);
+            case 7: return mfma_pick_segs<7, SRC>(a, segs);
+            case 8: return mfma_pick_segs<8, SRC>(a, segs);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
-hipError_t launch_any(const int8_t* q, const float* xs, const int32_t* qsum, const uint8_t* planes, int64_t m,
-                      int64_t n, int64_t k, float* y, const SmallMConfig& cfg, hipStream_t stream) {
-    if (cfg.engine == 2) {
-        if (cfg.max_waves < 1 || cfg.max_waves > 8) return hipErrorInvalidValue;
-        const int groups = (int)(k / 128);
-        const int nseg = (groups + kGroupLanes - 1) / kGroupLanes;
-        const int per_wave = (nseg + cfg.max_waves - 1) / cfg.max_waves;
-        const int waves = (nseg + per_wave - 1) / per_wave;
-        int segs = per_wave < 4 ? per_wave : 4;
-        int mc = (int)(m < 8 ? m : 8);
-        while (mc > 1 && mfma_lds_bytes(mc, segs, waves) > kLdsLimit) --mc;
-        while (segs > 1 && mfma_lds_bytes(mc, segs, waves) > kLdsLimit) --segs;
-        const int chunks = (int)((m + mc - 1) / mc);
-        mc = (int)((m + chunks - 1) / chunks);
-        while (mc * segs > 2 && segs > 1) --segs;  // as for the packed-dot engine below
-        const Launch a{q, xs, qsum, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream};
-        return qsum ? mfma_pick_mc<false>(a, mc, segs) : mfma_pick_mc<true>(a, mc, segs);
-    }
-    if (cfg.engine != 1) return hipErrorInvalidValue;
-    const int rows = cfg.rows_per_lane;
-    if (rows != 1 && rows != 2) return hipErrorInvalidValue;
+template <int SRC>
+hipError_t dispatch(const Launch& a, int engine, int mc, int rows, int segs) {
+    return engine == 2 ? mfma_pick_mc<SRC>(a, mc, segs) : pick_mc<SRC>(a, mc, rows, segs);
+}
+
+hipError_t launch_any(int src, const Launch& base, const SmallMConfig& cfg) {
     if (cfg.max_waves < 1 || cfg.max_waves > 8) return hipErrorInvalidValue;
+    if (cfg.engine != 1 && cfg.engine != 2) return hipErrorInvalidValue;
+    const int rows = cfg.engine == 2 ? 1 : cfg.rows_per_lane;
+    if (rows != 1 && rows != 2) return hipErrorInvalidValue;
+    const int64_t m = base.m, k = base.k;
     const int groups = (int)(k / 128);
     const int nseg = (groups + kGroupLanes - 1) / kGroupLanes;
     const int per_wave = (nseg + cfg.max_waves - 1) / cfg.max_waves;
     const int waves = (nseg + per_wave - 1) / per_wave;
-    int segs = per_wave < 4 ? per_wave : 4;  // loads in flight per lane: 2 * R * segs
-    int mc = (int)(m < 8 ? m : 8);
-    while (mc > 1 && lds_bytes(mc, segs, waves, kRowSlots * rows) > kLdsLimit) --mc;
-    while (segs > 1 && lds_bytes(mc, segs, waves, kRowSlots * rows) > kLdsLimit) --segs;
+    auto lds = [&](int mc, int segs) {
+        return cfg.engine == 2 ? mfma_lds_bytes(mc, segs, waves) : lds_bytes(mc, segs, waves, kRowSlots * rows);
+    };
+    int segs = per_wave < 2 ? per_wave : 2;
+    const int mc_cap = max_mc(src);
+    int mc = (int)(m < mc_cap ? m : mc_cap);
+    while (mc > 1 && lds(mc, segs) > kLdsLimit) --mc;
+    while (segs > 1 && lds(mc, segs) > kLdsLimit) --segs;
     const int chunks = (int)((m + mc - 1) / mc);
     mc = (int)((m + chunks - 1) / chunks);  // balance the column passes
     // At most two (column x row) units of code loads per lane per step: more
     // segments per step hold more registers than the residency of the whole
     // grid allows (measured at K = 17408), and the loop covers the rest.
     while (mc * rows * segs > 2 && segs > 1) --segs;
-    const Launch a{q, xs, qsum, planes, m, n, k, y, waves, nseg, per_wave, chunks, stream};
-    return qsum ? pick_mc<false>(a, mc, rows, segs) : pick_mc<true>(a, mc, rows, segs);
+    Launch a = base;
+    a.waves = waves;
+    a.nseg = nseg;
+    a.per_wave = per_wave;
+    a.chunks = chunks;
+    switch (src) {
+        case kSrcPlanes: return dispatch<kSrcPlanes>(a, cfg.engine, mc, rows, segs);
+        case kSrcNatural: return dispatch<kSrcNatural>(a, cfg.engine, mc, rows, segs);
+        case kSrcBf16: return dispatch<kSrcBf16>(a, cfg.engine, mc, rows, segs);
+        case kSrcF16: return dispatch<kSrcF16>(a, cfg.engine, mc, rows, segs);
+        case kSrcF32: return dispatch<kSrcF32>(a, cfg.engine, mc, rows, segs);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -665,15 +840,35 @@ SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k) {
     return c;
 }
 
+// The fused path quantises its k slice once per workgroup, so two rows per
+// lane (half the workgroups, half the repeated quantisation) pays at every
+// measured shape, on the packed-dot engine.  The k split is the unfused
+// default, which keeps the two-launch path's bits.
+SmallMConfig default_small_m_fused_config(int64_t m, int64_t n, int64_t k) {
+    SmallMConfig c = default_small_m_config(m, n, k);
+    c.rows_per_lane = 2;
+    c.engine = 1;
+    return c;
+}
+
 hipError_t launch_small_m(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
                           int64_t k, float* y, const SmallMConfig& cfg, hipStream_t stream) {
-    return launch_any(q, xs, nullptr, planes, m, n, k, y, cfg, stream);
+    const Launch a{q, xs, nullptr, nullptr, 0, planes, m, n, k, y, 0, 0, 0, 0, stream};
+    return launch_any(kSrcNatural, a, cfg);
 }
 
 hipError_t launch_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const uint8_t* planes,
                                  int64_t m, int64_t n, int64_t k, float* y, const SmallMConfig& cfg,
                                  hipStream_t stream) {
-    return launch_any(qp, xs, qsum, planes, m, n, k, y, cfg, stream);
+    const Launch a{qp, xs, qsum, nullptr, 0, planes, m, n, k, y, 0, 0, 0, 0, stream};
+    return launch_any(kSrcPlanes, a, cfg);
+}
+
+hipError_t launch_small_m_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* planes, int64_t m,
+                                int64_t n, int64_t k, float* y, const SmallMConfig& cfg, hipStream_t stream) {
+    const Launch a{nullptr, nullptr, nullptr, x, x_stride, planes, m, n, k, y, 0, 0, 0, 0, stream};
+    const int src = dtype == 0 ? kSrcBf16 : dtype == 1 ? kSrcF16 : dtype == 2 ? kSrcF32 : -1;
+    return launch_any(src, a, cfg);
 }
 
 }  // namespace pq2

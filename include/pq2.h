@@ -203,6 +203,34 @@ int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int
                                     int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane,
                                     int max_waves, int engine, void* stream);
 
+/* Quantise + small-m matmul in one launch: y = the definition above for the
+ * activations pq2_quantize_act_i8 would produce from x, bit for bit the y of
+ * pq2_quantize_act_i8 followed by pq2_matmul_small_m (same codes, scales and
+ * summation order), without the intermediate q / xs buffers or the second
+ * launch.  Every workgroup quantises the k slice of x it reads (page
+ * "Kernel experiments", Test 12 fusion screen and Test 18: fused preparation
+ * must reproduce the standalone quantiser's codes exactly).
+ *   x       device, dtype PQ2_BF16 / PQ2_F16 / PQ2_F32, m rows of
+ *           x_row_stride_elems elements (>= k); x and the row stride in
+ *           bytes 16-byte aligned; all m rows within 2^31 - 1 bytes.
+ *   planes  device prepared planes (layout version 1), 16-byte aligned.
+ *   y       device float [m][n], 4-byte aligned; fully overwritten; must not
+ *           overlap x or planes.
+ * Errors: EINVAL (null, dtype, overlap), ESHAPE (m outside 1..16, n<1,
+ *         k<128, k%128, k > PQ2_MAX_K, stride < k, x span >= 2^31 bytes),
+ *         EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_small_m_fused(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes,
+                             int64_t m, int64_t n, int64_t k, float* y, void* stream);
+
+/* Tuning hook for pq2_matmul_small_m_fused (benchmarks and tests only):
+ * settings as for pq2_matmul_small_m_tuned, and the same bits as
+ * pq2_quantize_act_i8 + pq2_matmul_small_m_tuned with the same settings.
+ * Errors as pq2_matmul_small_m_fused, plus EINVAL for an unsupported
+ * setting. */
+int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes,
+                                   int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
+                                   int engine, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

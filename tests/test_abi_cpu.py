@@ -29,7 +29,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 16
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -138,6 +138,30 @@ def test_small_m_planes_validation():
     assert t(A, B, E, C, 1, 8, 128, D, 4, 0, 0, None) == EINVAL  # rows per lane
     assert t(A, B, E, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL  # waves
     assert t(A, B, E, C, 1, 8, 128, D, 0, 0, 7, None) == EINVAL  # engine
+
+
+def test_small_m_fused_validation():
+    f = pq2.lib.pq2_matmul_small_m_fused
+    assert f(None, 0, 128, C, 1, 8, 128, D, None) == EINVAL
+    assert f(A, 0, 128, None, 1, 8, 128, D, None) == EINVAL
+    assert f(A, 0, 128, C, 1, 8, 128, None, None) == EINVAL
+    assert f(A, 3, 128, C, 1, 8, 128, D, None) == EINVAL        # unknown dtype
+    assert f(A, 0, 128, C, 0, 8, 128, D, None) == ESHAPE
+    assert f(A, 0, 128, C, 17, 8, 128, D, None) == ESHAPE       # column limit
+    assert f(A, 0, 128, C, 1, 0, 128, D, None) == ESHAPE
+    assert f(A, 0, 200, C, 1, 8, 200, D, None) == ESHAPE        # k % 128
+    assert f(A, 0, 100, C, 1, 8, 128, D, None) == ESHAPE        # stride < k
+    assert f(A, 2, 1 << 26, C, 16, 8, 128, D, None) == ESHAPE   # x span beyond 2^31 bytes
+    assert f(A + 2, 0, 128, C, 1, 8, 128, D, None) == EALIGN    # x 16-byte alignment
+    assert f(A, 0, 132, C, 2, 8, 128, D, None) == EALIGN        # row stride 264 bytes
+    assert f(A, 0, 128, C + 8, 1, 8, 128, D, None) == EALIGN    # planes 16-byte alignment
+    assert f(A, 0, 128, C, 1, 8, 128, D + 2, None) == EALIGN
+    assert f(A, 0, 128, C, 1, 8, 128, A + 64, None) == EINVAL   # y overlaps x
+    assert f(A, 0, 128, C, 1, 8, 128, C + 16, None) == EINVAL   # y overlaps planes
+    t = pq2.lib.pq2_matmul_small_m_fused_tuned
+    assert t(A, 0, 128, C, 1, 8, 128, D, 3, 0, 0, None) == EINVAL  # rows per lane
+    assert t(A, 0, 128, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL  # waves
+    assert t(A, 0, 128, C, 1, 8, 128, D, 0, 0, 3, None) == EINVAL  # engine
 
 
 def test_python_binding_rejects_host_tensors():

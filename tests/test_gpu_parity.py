@@ -505,3 +505,143 @@ def test_small_m_planes_workloads_sampled(name):
     mmax = max(w.ms)
     for m, y in ys.items():
         assert np.array_equal(y.view(np.uint32), ys[mmax][:m].view(np.uint32)), f"batch variance at m={m}"
+
+
+# ------------------------------------------------------------------ fused quantise + matmul
+def gpu_fused(x_dev, planes, n, **kw):
+    pq2 = _pq2()
+    y = torch.full((x_dev.shape[0], n), float("nan"), dtype=torch.float32, device=DEV)
+    if kw:
+        pq2.pq2_matmul_small_m_fused_tuned(x_dev, planes, y, **kw)
+    else:
+        pq2.pq2_matmul_small_m_fused(x_dev, planes, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def same_bits(a, b):
+    return np.array_equal(np.asarray(a, dtype=np.float32).view(np.uint32), np.asarray(b, dtype=np.float32).view(np.uint32))
+
+
+FUSED_SHAPES = [(1, 1024, 512), (1, 1, 128), (2, 333, 640), (3, 97, 1152), (4, 1000, 5120), (5, 77, 2176),
+                (8, 130, 384), (16, 40, 17408), (12, 300, 3072), (2, 24, 65536)]
+
+
+@pytest.mark.parametrize("m,n,k", FUSED_SHAPES)
+def test_fused_full(m, n, k):
+    """Quantise + matmul in one launch: within the bound of the oracle (which
+    quantises with the definition), and bit-identical to the two-launch path
+    for every engine and rows-per-lane setting."""
+    pq2 = _pq2()
+    announce(f"fused full m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=90 + m + n, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 91 + k, "normal+outliers")
+    q, xs, qo, xso = quantise_both(x)
+    planes = gpu_planes(raw, n, k)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    xd = x.to(DEV)
+    for rows, engine in ((1, 1), (2, 1), (1, 2)):
+        yf = gpu_fused(xd, planes, n, rows_per_lane=rows, engine=engine)
+        assert_within(yf, y_ref, bound, f"fused rows={rows} engine={engine}")
+        yu = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows_per_lane=rows, engine=engine)
+        assert same_bits(yf, yu), f"fused rows={rows} engine={engine} differs from quantise + matmul"
+    y0 = gpu_fused(xd, planes, n)
+    assert same_bits(y0, gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, n)), "default fused path differs"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k,pad", [(1, 200, 1024, 0), (3, 150, 640, 8), (4, 64, 5120, 16), (7, 90, 2048, 24)])
+def test_fused_dtypes_and_strides(dtype, m, n, k, pad):
+    pq2 = _pq2()
+    announce(f"fused dtype={dtype} m={m} n={n} k={k} pad={pad}")
+    tdt = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    xt = (workloads.make_activations(m, k + pad, 170 + m, "laplace").float() * 3.0).to(tdt)
+    bits = xt.numpy() if dtype == "f32" else xt.view(torch.int16).numpy().view(np.uint16)
+    qo, xso = oracle.quantize_act_i8(bits, dtype, k=k)
+    raw = workloads.make_raw_weights(n, k, seed=171 + n, codes="ternary+3")
+    planes = gpu_planes(raw, n, k)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    xd = xt.to(DEV)
+    yf = gpu_fused(xd[:, :k], planes, n)  # row stride k + pad elements
+    assert_within(yf, y_ref, bound, f"fused {dtype}")
+    q, xs = gpu_quantize(xd, k)
+    assert same_bits(yf, gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, n))
+
+
+def probe_weights(k):
+    """Raw rows that read one activation each: row r has weight +1 (code 2)
+    at position r, weight 0 (code 1) elsewhere, and every scale is fp16 1.0,
+    so y[m][r] = float(q[m][r]) * xs[m][r // 128] exactly."""
+    groups = k // 128
+    raw = np.zeros((k, groups, 34), dtype=np.uint8)
+    raw[:, :, 0], raw[:, :, 1] = 0x00, 0x3C  # 1.0 = 0x3C00, little-endian
+    raw[:, :, 2:] = 0x55
+    r = np.arange(k)
+    i = r % 128
+    shift = 2 * (i % 4)
+    raw[r, r // 128, 2 + i // 4] = (0x55 & ~(3 << shift)) | (2 << shift)
+    return raw.reshape(k, groups * 34)
+
+
+def probe_activations(dtype, k):
+    """16 columns: random groups of several distributions and magnitudes, and
+    groups built to reach the exact-division fallback of the fused
+    quantiser: exact rounding ties (power-of-two scales), a zero group,
+    subnormal scales (with f32 input also a scale that makes the clamp bind),
+    repeated +-amax, and huge values."""
+    m = 16
+    cols = [workloads.make_activations(1, k, 300 + c, "normal+outliers" if c % 2 else "laplace").float()[0]
+            * (10.0 ** (c % 5 - 2)) for c in range(m)]
+    x = torch.stack(cols)
+    g = x[5].view(k // 128, 128)
+    g[0] = 0.0
+    g[1] = torch.tensor([(j - 63.5) * 0.125 for j in range(128)])          # d = 2^-3: every element a tie
+    g[1, 0] = 127 * 0.125
+    g[2] = torch.tensor([((j % 9) - 4) * 2.0 ** -131 for j in range(128)])  # subnormal scale
+    g[3] = torch.tensor([(-1.0) ** j * 3.0e30 for j in range(128)])        # all at +-amax
+    g[4] = torch.tensor([(j - 64) * 0.5 + 0.25 for j in range(128)])       # d = 0.5: ties
+    g[4, 0] = 63.5
+    if dtype == "f32":
+        g[5] = torch.tensor([(j % 7 - 3) * 2.0 ** -149 for j in range(128)], dtype=torch.float64).float()
+        g[5, 0] = 190 * 2.0 ** -149                                         # scale rounds to 2^-149: clamp
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    return x.to(tdt)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_quantiser_codes_exact(dtype):
+    """Every code and scale of the fused quantiser, read back through
+    single-weight rows: y[m][r] must equal the oracle's q * xs bit for bit
+    (fast path, near-tie fallback, subnormal scales and the clamp)."""
+    k = 2048
+    announce(f"fused quantiser probe dtype={dtype} k={k}")
+    x = probe_activations(dtype, k)
+    bits = x.numpy() if dtype == "f32" else workloads.bf16_bits(x)
+    qo, xso = oracle.quantize_act_i8(bits, dtype)
+    assert np.any(np.abs(qo) == 127)
+    raw = probe_weights(k)
+    planes = gpu_planes(raw, k, k)
+    expect = qo.astype(np.float32) * np.repeat(xso, 128, axis=1)
+    for rows, engine in ((1, 1), (1, 2)):
+        y = gpu_fused(x.to(DEV), planes, k, rows_per_lane=rows, engine=engine)
+        bad = np.argwhere(y.view(np.uint32) != expect.view(np.uint32))
+        assert bad.size == 0, f"engine={engine}: {len(bad)} codes differ, first at {tuple(bad[0])}: " \
+                              f"{y[tuple(bad[0])]!r} vs {expect[tuple(bad[0])]!r}"
+
+
+@pytest.mark.parametrize("name", ["qkv", "up", "down"])
+def test_fused_workloads(name):
+    """Full workload sizes: bit-identical to quantise + matmul at every M,
+    and sampled outputs within the oracle's bound."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    planes = gpu_planes(raw, w.n, w.k)
+    for m in w.ms:
+        announce(f"fused workload {name} m={m}")
+        xd = x[:m].contiguous().to(DEV)
+        yf = gpu_fused(xd, planes, w.n)
+        q, xs, qo, xso = quantise_both(x[:m].contiguous())
+        assert same_bits(yf, gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, w.n)), f"{name} m={m}"
+        mi, ni = _sample_indices(m, w.n, 200, seed=50 + m)
+        y_ref, bound = oracle.matmul_raw_sample(qo, xso, raw, w.n, w.k, mi, ni)
+        assert_within(yf[mi, ni], y_ref, bound, f"fused {name} m={m}")
