@@ -207,8 +207,8 @@ def pq2_matmul_small_m(q, xs, planes, y, stream=None) -> None:
     _check(lib.pq2_matmul_small_m(*_matmul_args(q, xs, planes, y), _stream(stream)), "pq2_matmul_small_m")
 
 
-def pq2_matmul_small_m_tuned(q, xs, planes, y, rows_per_lane=0, max_waves=0, engine=0, stream=None) -> None:
-    _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows_per_lane, max_waves, engine,
+def pq2_matmul_small_m_tuned(q, xs, planes, y, rows=0, max_waves=0, engine=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows, max_waves, engine,
                                         _stream(stream)), "pq2_matmul_small_m_tuned")
 
 
@@ -232,8 +232,8 @@ def pq2_matmul_small_m_fused(x, planes, y, stream=None) -> None:
     _check(lib.pq2_matmul_small_m_fused(*_fused_args(x, planes, y), _stream(stream)), "pq2_matmul_small_m_fused")
 
 
-def pq2_matmul_small_m_fused_tuned(x, planes, y, rows_per_lane=0, max_waves=0, engine=0, stream=None) -> None:
-    _check(lib.pq2_matmul_small_m_fused_tuned(*_fused_args(x, planes, y), rows_per_lane, max_waves, engine,
+def pq2_matmul_small_m_fused_tuned(x, planes, y, rows=0, max_waves=0, engine=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_fused_tuned(*_fused_args(x, planes, y), rows, max_waves, engine,
                                               _stream(stream)), "pq2_matmul_small_m_fused_tuned")
 
 
@@ -280,9 +280,9 @@ def pq2_matmul_small_m_planes(qp, xs, qsum, planes, y, stream=None) -> None:
            "pq2_matmul_small_m_planes")
 
 
-def pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, y, rows_per_lane=0, max_waves=0, engine=0,
+def pq2_matmul_small_m_planes_tuned(qp, xs, qsum, planes, y, rows=0, max_waves=0, engine=0,
                                     stream=None) -> None:
-    _check(lib.pq2_matmul_small_m_planes_tuned(*_planes_args(qp, xs, qsum, planes, y), rows_per_lane,
+    _check(lib.pq2_matmul_small_m_planes_tuned(*_planes_args(qp, xs, qsum, planes, y), rows,
                                                max_waves, engine, _stream(stream)), "pq2_matmul_small_m_planes_tuned")
 
 

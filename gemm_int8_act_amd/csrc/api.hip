@@ -61,16 +61,25 @@ int check_matmul_args(const int8_t* q, const float* xs, const void* planes, int6
 }
 
 // Default small-m configuration with the caller's overrides (0 = default).
-int small_m_config(int64_t m, int64_t n, int64_t k, int rows_per_lane, int max_waves, int engine,
-                   pq2::SmallMConfig* cfg, bool fused = false) {
-    *cfg = fused ? pq2::default_small_m_fused_config(m, n, k) : pq2::default_small_m_config(m, n, k);
-    if (rows_per_lane) cfg->rows_per_lane = rows_per_lane;
+// An explicit engine without explicit rows takes that engine's default rows.
+int small_m_config(int src, int64_t m, int64_t n, int64_t k, int rows, int max_waves, int engine,
+                   pq2::SmallMConfig* cfg) {
+    *cfg = pq2::default_small_m_config(src, m, n, k);
     if (max_waves) cfg->max_waves = max_waves;
-    if (engine) cfg->engine = engine;
-    if ((cfg->rows_per_lane != 1 && cfg->rows_per_lane != 2) || cfg->max_waves < 1 || cfg->max_waves > 8 ||
-        (cfg->engine != 1 && cfg->engine != 2))
-        return PQ2_EINVAL;
-    return PQ2_OK;
+    if (cfg->max_waves < 1 || cfg->max_waves > 8) return PQ2_EINVAL;
+    if (engine && engine != cfg->engine) {
+        cfg->engine = engine;
+        cfg->rows = pq2::default_small_m_rows(engine, src, m, n, k, cfg->max_waves);
+    } else if (max_waves && cfg->engine == 3) {
+        cfg->rows = pq2::default_small_m_rows(3, src, m, n, k, cfg->max_waves);
+    }
+    if (rows) cfg->rows = rows;
+    switch (cfg->engine) {
+        case 1: return (cfg->rows == 1 || cfg->rows == 2) ? PQ2_OK : PQ2_EINVAL;
+        case 2: return cfg->rows == 1 ? PQ2_OK : PQ2_EINVAL;
+        case 3: return pq2::wg_supported(src, m, k, cfg->max_waves, cfg->rows) ? PQ2_OK : PQ2_EINVAL;
+        default: return PQ2_EINVAL;
+    }
 }
 
 }  // namespace
@@ -144,14 +153,14 @@ int pq2_quantize_act_i8_planes(const void* x, int dtype, int64_t x_row_stride_el
 }
 
 int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
-                                    int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane,
+                                    int64_t m, int64_t n, int64_t k, float* y, int rows,
                                     int max_waves, int engine, void* stream) {
     if (!qsum) return PQ2_EINVAL;
     if (int rc = check_matmul_args(qp, xs, planes, m, n, k, y, PQ2_MAX_SMALL_M)) return rc;
     if (!aligned(qsum, 4)) return PQ2_EALIGN;
     if (overlap(y, (size_t)m * n * 4, qsum, (size_t)m * (k / kGroup) * 4)) return PQ2_EINVAL;
     pq2::SmallMConfig cfg;
-    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, engine, &cfg)) return rc;
+    if (int rc = small_m_config(pq2::kSrcPlanes, m, n, k, rows, max_waves, engine, &cfg)) return rc;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m_planes(qp, xs, qsum, static_cast<const uint8_t*>(planes), m, n, k, y,
                                                     cfg, (hipStream_t)stream));
@@ -163,11 +172,11 @@ int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* 
 }
 
 int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
-                             int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves, int engine,
+                             int64_t n, int64_t k, float* y, int rows, int max_waves, int engine,
                              void* stream) {
     if (int rc = check_matmul_args(q, xs, planes, m, n, k, y, PQ2_MAX_SMALL_M)) return rc;
     pq2::SmallMConfig cfg;
-    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, engine, &cfg)) return rc;
+    if (int rc = small_m_config(pq2::kSrcNatural, m, n, k, rows, max_waves, engine, &cfg)) return rc;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m(q, xs, static_cast<const uint8_t*>(planes), m, n, k, y, cfg,
                                              (hipStream_t)stream));
@@ -179,7 +188,7 @@ int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int
 }
 
 int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes,
-                                   int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
+                                   int64_t m, int64_t n, int64_t k, float* y, int rows, int max_waves,
                                    int engine, void* stream) {
     if (!x || !planes || !y) return PQ2_EINVAL;
     if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
@@ -195,7 +204,7 @@ int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_strid
     if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, planes, (size_t)n * (k / kGroup) * 34))
         return PQ2_EINVAL;
     pq2::SmallMConfig cfg;
-    if (int rc = small_m_config(m, n, k, rows_per_lane, max_waves, engine, &cfg, true)) return rc;
+    if (int rc = small_m_config(pq2::src_of_dtype(dtype), m, n, k, rows, max_waves, engine, &cfg)) return rc;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m_fused(x, dtype, x_row_stride_elems, static_cast<const uint8_t*>(planes),
                                                    m, n, k, y, cfg, (hipStream_t)stream));

@@ -7,6 +7,19 @@
 
 namespace pq2 {
 
+// Where a small-m kernel's activations come from.
+enum : int {
+    kSrcPlanes = 0,   // plane-order q and group sums (pq2_quantize_act_i8_planes)
+    kSrcNatural = 1,  // natural-order q (pq2_quantize_act_i8): transposed and summed while staged
+    kSrcBf16 = 2,     // unquantised x of this element type, quantised while staged
+    kSrcF16 = 3,
+    kSrcF32 = 4,
+};
+constexpr bool src_fused(int src) { return src >= kSrcBf16; }
+constexpr int src_esize(int src) { return src == kSrcF32 ? 4 : 2; }
+constexpr int src_xloads(int src) { return src == kSrcF32 ? 4 : 2; }  // 16-byte loads per lane and group
+inline int src_of_dtype(int dtype) { return dtype == 0 ? kSrcBf16 : dtype == 1 ? kSrcF16 : dtype == 2 ? kSrcF32 : -1; }
+
 // Discard an error another library left in this thread's HIP error slot, so
 // the hipGetLastError() that follows our launch reports our launch only.
 inline void clear_stale_error() { (void)hipGetLastError(); }
@@ -22,13 +35,44 @@ hipError_t launch_quantize_planes(const void* x, int dtype, int64_t row_stride, 
                                   int8_t* qp, float* xs, int32_t* qsum, hipStream_t stream);
 
 struct SmallMConfig {
-    int rows_per_lane;  // 1 or 2 (dot-product engine only)
-    int max_waves;      // 1..8: waves that split k inside one workgroup
-    int engine;         // 1 = packed dot products (v_dot4), 2 = INT8 matrix cores; same bits
+    int rows;       // engine 1: weight rows per lane (1, 2); engine 3: 8-row blocks per workgroup
+    int max_waves;  // 1..8: waves that split k inside one workgroup
+    int engine;     // 1 = packed dot products (v_dot4), 2 = INT8 matrix cores, one row block per
+                    // workgroup, 3 = INT8 matrix cores, one 8-wave workgroup staging the
+                    // activations for `rows` row blocks; same bits
 };
 
-SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k);
-SmallMConfig default_small_m_fused_config(int64_t m, int64_t n, int64_t k);  // same k split
+// Arguments of one small-m launch, any engine.  waves, nseg, per_wave and
+// chunks (k split and column passes) are filled in by the dispatcher.
+struct SmallMLaunch {
+    const int8_t* q;
+    const float* xs;
+    const int32_t* qsum;
+    const void* x;
+    int64_t x_stride;
+    const uint8_t* planes;
+    int64_t m, n, k;
+    float* y;
+    int waves, nseg, per_wave, chunks;
+    hipStream_t stream;
+};
+
+// Columns one pass of the workgroup-staged engine covers; more columns take
+// several passes over the weights.
+constexpr int kWgMaxColumns = 4;
+
+// Workgroup-staged matrix-core engine (small_m_wg.hip); src is a kSrc* value
+// and rows the row blocks (8 weight rows) per workgroup.
+bool wg_supported(int src, int64_t m, int64_t k, int max_waves, int rows);
+int wg_default_row_blocks(int src, int64_t m, int64_t n, int64_t k, int max_waves);  // 0: unsupported
+hipError_t launch_small_m_wg(int src, const SmallMLaunch& a, int max_waves, int rows);
+
+// The library's choice for activations of kind src; the k split (max_waves)
+// depends on (n, k) only, so every source and column count sums in one order.
+SmallMConfig default_small_m_config(int src, int64_t m, int64_t n, int64_t k);
+// The `rows` setting an engine uses by default at this shape (0: the engine
+// cannot run it).
+int default_small_m_rows(int engine, int src, int64_t m, int64_t n, int64_t k, int max_waves);
 
 // Natural-order q (the kernel transposes blocks and forms the group sums).
 // Returns hipErrorInvalidValue for a configuration the library has no kernel for.

@@ -54,124 +54,10 @@
 //    only on the k split, which the library picks from (n, k) alone: outputs
 //    are bit-identical whatever the number of columns (batch invariance),
 //    the rows per lane, or the input order (natural or plane).
-#include "pq2_device.h"
 #include "pq2_internal.h"
-
-#include <hip/hip_fp16.h>
+#include "small_m_common.h"
 
 namespace pq2 {
-
-constexpr int kGroupLanes = 8;   // lanes per row slot
-constexpr int kRowSlots = 8;     // row slots per wave
-constexpr int kBlockPitch = 9;   // LDS quads per group (8 + 1 pad; pad dword 0 = sum(q))
-constexpr int kSegQuads = kGroupLanes * kBlockPitch;  // LDS quads per (segment, column)
-
-// Where a kernel's activations come from.
-enum : int {
-    kSrcPlanes = 0,   // plane-order q and group sums (pq2_quantize_act_i8_planes)
-    kSrcNatural = 1,  // natural-order q (pq2_quantize_act_i8): transposed and summed while staged
-    kSrcBf16 = 2,     // unquantised x of this element type, quantised while staged
-    kSrcF16 = 3,
-    kSrcF32 = 4,
-};
-constexpr bool src_fused(int src) { return src >= kSrcBf16; }
-constexpr int src_esize(int src) { return src == kSrcF32 ? 4 : 2; }
-constexpr int src_xloads(int src) { return src == kSrcF32 ? 4 : 2; }  // 16-byte loads per lane and group
-
-// Bytes 0 of a, b, c, d packed into one dword (byte i from the i-th argument).
-__device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
-    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
-    return ab | (cd << 16);
-}
-
-// Group-128 INT8 quantisation (page "Baseline and the integer
-// breakthrough", "Calculate with small integers" step 1) of one row slot's
-// group, 16 elements per lane: lane j of the slot holds elements
-// 16j..16j+15 in v.  Returns the lane's 16 codes in plane order (dword s =
-// codes 16j + s, +4, +8, +12) and sets gsum (group sum of q, all 8 lanes)
-// and scale (max|x| / 127, correctly rounded).  The codes equal the
-// definition q = clamp(rint(RN(x / d)), +-127), d = scale or 1 for an
-// all-zero group, bit for bit:
-//  * r = 1/d from the hardware reciprocal refined by one Newton step lies
-//    within 2^-22 (relative) of 1/d, so t = RN(x * r) differs from x / d by
-//    at most 127.0001 * (2^-22 + 2^-24) and from RN(x / d) by less than
-//    4.3e-5 < 2^-14 whenever d is normal (|x / d| <= 127 * (1 + 2^-23), and
-//    half an ulp of RN(x / d) below 128 is 2^-18);
-//  * so if t lies at least 2^-14 from every half-integer, rint(t) is
-//    rint(RN(x / d)).  Adding 1.5 * 2^23 rounds t to that integer in the
-//    low mantissa bits, whose low byte is the two's-complement code, and
-//    |t| < 127.5 makes the clamp a no-op;
-//  * otherwise (a near-tie in any of the lane's 16 elements, or d
-//    subnormal) the lane repeats the definition with IEEE divisions.
-__device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum, float& scale) {
-#pragma clang fp contract(off)
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    amax = max8_f(amax);
-    scale = amax / 127.0f;
-    const float d = scale > 0.0f ? scale : 1.0f;
-    const float r0 = __builtin_amdgcn_rcpf(d);
-    const float r = __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
-    constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
-    uint32_t bits[16];
-    float worst = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const float t = v[e] * r;
-        const float s = t + kRound;
-        worst = fmaxf(worst, fabsf(t - (s - kRound)));
-        bits[e] = __float_as_uint(s);
-    }
-    if (!(d >= 0x1p-126f && worst <= 0.5f - 0x1p-14f)) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float qf = fminf(127.0f, fmaxf(-127.0f, rintf(v[e] / d)));
-            bits[e] = (uint32_t)(int)qf;
-        }
-    }
-    uint4 out;
-    out.x = low_bytes4(bits[0], bits[4], bits[8], bits[12]);
-    out.y = low_bytes4(bits[1], bits[5], bits[9], bits[13]);
-    out.z = low_bytes4(bits[2], bits[6], bits[10], bits[14]);
-    out.w = low_bytes4(bits[3], bits[7], bits[11], bits[15]);
-    int s = dot4(out.x, 0x01010101u, 0);
-    s = dot4(out.y, 0x01010101u, s);
-    s = dot4(out.z, 0x01010101u, s);
-    s = dot4(out.w, 0x01010101u, s);
-    gsum = sum8_i(s);
-    return out;
-}
-
-// The 16 elements of x a lane quantises, from its SRC-typed 16-byte loads.
-template <int SRC>
-__device__ __forceinline__ void x_to_float16(const uint4 (&w)[src_xloads(SRC)], float (&v)[16]) {
-    if constexpr (SRC == kSrcF32) {
-#pragma unroll
-        for (int l = 0; l < 4; ++l) {
-            v[4 * l + 0] = __uint_as_float(w[l].x);
-            v[4 * l + 1] = __uint_as_float(w[l].y);
-            v[4 * l + 2] = __uint_as_float(w[l].z);
-            v[4 * l + 3] = __uint_as_float(w[l].w);
-        }
-    } else {
-#pragma unroll
-        for (int l = 0; l < 2; ++l) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t d = word_of(w[l], i);
-                if constexpr (SRC == kSrcBf16) {
-                    v[8 * l + 2 * i] = __uint_as_float(d << 16);
-                    v[8 * l + 2 * i + 1] = __uint_as_float(d & 0xFFFF0000u);
-                } else {
-                    v[8 * l + 2 * i] = __half2float(__ushort_as_half((unsigned short)(d & 0xFFFFu)));
-                    v[8 * l + 2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(d >> 16)));
-                }
-            }
-        }
-    }
-}
 
 // Plane-order pairing of activation dwords with code planes, per half group.
 // acc0/acc1/acc23 are the three masked-plane accumulators.
@@ -659,18 +545,7 @@ size_t lds_bytes(int mc, int segs, int waves, int rows_per_wg) {
     return (size_t)waves * mc * kSegQuads * 16 + (size_t)waves * mc * rows_per_wg * 4;
 }
 
-struct Launch {
-    const int8_t* q;
-    const float* xs;
-    const int32_t* qsum;
-    const void* x;
-    int64_t x_stride;
-    const uint8_t* planes;
-    int64_t m, n, k;
-    float* y;
-    int waves, nseg, per_wave, chunks;
-    hipStream_t stream;
-};
+using Launch = SmallMLaunch;
 
 template <int MC, int R, int SEGS, int SRC>
 hipError_t launch_one(const Launch& a) {
@@ -783,8 +658,9 @@ hipError_t dispatch(const Launch& a, int engine, int mc, int rows, int segs) {
 
 hipError_t launch_any(int src, const Launch& base, const SmallMConfig& cfg) {
     if (cfg.max_waves < 1 || cfg.max_waves > 8) return hipErrorInvalidValue;
+    if (cfg.engine == 3) return launch_small_m_wg(src, base, cfg.max_waves, cfg.rows);
     if (cfg.engine != 1 && cfg.engine != 2) return hipErrorInvalidValue;
-    const int rows = cfg.engine == 2 ? 1 : cfg.rows_per_lane;
+    const int rows = cfg.engine == 2 ? 1 : cfg.rows;
     if (rows != 1 && rows != 2) return hipErrorInvalidValue;
     const int64_t m = base.m, k = base.k;
     const int groups = (int)(k / 128);
@@ -822,32 +698,39 @@ hipError_t launch_any(int src, const Launch& base, const SmallMConfig& cfg) {
 
 }  // namespace
 
+int default_small_m_rows(int engine, int src, int64_t m, int64_t n, int64_t k, int max_waves) {
+    switch (engine) {
+        case 1: return src_fused(src) ? 2 : (m <= 4 ? 1 : 2);
+        case 2: return 1;
+        case 3: return wg_default_row_blocks(src, m, n, k, max_waves);
+        default: return 0;
+    }
+}
+
 // The k split (max_waves) must depend on (n, k) only: it fixes the summation
 // order, and outputs must not change with the number of columns.  Rows per
 // lane does not touch the order; two rows per lane halve the LDS reads of
 // the activations, which pays from five columns on (measured on the
 // K=5120 and K=17408 shapes).
-// Both engines give the same bits, so the engine is free per shape: packed
+// Every engine gives the same bits, so the engine is free per shape: packed
 // dots win at one or two columns, the matrix cores from five columns on and
 // from three on when K is long (measured on the K = 5120 and K = 17408
 // shapes; the matrix-core work per code dword does not grow with M).
-SmallMConfig default_small_m_config(int64_t m, int64_t n, int64_t k) {
-    (void)n;
+// The fused path quantises the activations inside the matmul.  The
+// packed-dot engine repeats that per 16-row workgroup (two rows per lane),
+// which is cheapest at one column; from two to eight columns the
+// workgroup-staged engine, which quantises once per CU-sized workgroup, is
+// faster at every measured shape (K = 5120 and 17408).
+SmallMConfig default_small_m_config(int src, int64_t m, int64_t n, int64_t k) {
     SmallMConfig c;
-    c.rows_per_lane = m <= 4 ? 1 : 2;
     c.max_waves = 8;
-    c.engine = (m >= 5 || (m >= 3 && k >= 8192)) ? 2 : 1;
-    return c;
-}
-
-// The fused path quantises its k slice once per workgroup, so two rows per
-// lane (half the workgroups, half the repeated quantisation) pays at every
-// measured shape, on the packed-dot engine.  The k split is the unfused
-// default, which keeps the two-launch path's bits.
-SmallMConfig default_small_m_fused_config(int64_t m, int64_t n, int64_t k) {
-    SmallMConfig c = default_small_m_config(m, n, k);
-    c.rows_per_lane = 2;
-    c.engine = 1;
+    if (src_fused(src)) {
+        c.engine = 1;
+        if (m >= 2 && m <= 8 && default_small_m_rows(3, src, m, n, k, c.max_waves) > 0) c.engine = 3;
+    } else {
+        c.engine = (m >= 5 || (m >= 3 && k >= 8192)) ? 2 : 1;
+    }
+    c.rows = default_small_m_rows(c.engine, src, m, n, k, c.max_waves);
     return c;
 }
 
@@ -867,8 +750,7 @@ hipError_t launch_small_m_planes(const int8_t* qp, const float* xs, const int32_
 hipError_t launch_small_m_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* planes, int64_t m,
                                 int64_t n, int64_t k, float* y, const SmallMConfig& cfg, hipStream_t stream) {
     const Launch a{nullptr, nullptr, nullptr, x, x_stride, planes, m, n, k, y, 0, 0, 0, 0, stream};
-    const int src = dtype == 0 ? kSrcBf16 : dtype == 1 ? kSrcF16 : dtype == 2 ? kSrcF32 : -1;
-    return launch_any(src, a, cfg);
+    return launch_any(src_of_dtype(dtype), a, cfg);
 }
 
 }  // namespace pq2

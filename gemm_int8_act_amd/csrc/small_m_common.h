@@ -1,0 +1,114 @@
+// small_m_common.h -- pieces shared by the small-m (decode / verification)
+// kernels of libpq2: the per-wave activation staging geometry, the kinds of
+// activation source, and the exact in-kernel group-128 quantiser used by the
+// fused (quantise + matmul) entry points.
+#pragma once
+
+#include "pq2_device.h"
+#include "pq2_internal.h"
+
+#include <hip/hip_fp16.h>
+
+namespace pq2 {
+
+constexpr int kGroupLanes = 8;   // lanes per row slot
+constexpr int kRowSlots = 8;     // row slots per wave
+constexpr int kBlockPitch = 9;   // LDS quads per group (8 + 1 pad; pad dword 0 = sum(q))
+constexpr int kSegQuads = kGroupLanes * kBlockPitch;  // LDS quads per (segment, column)
+
+// Bytes 0 of a, b, c, d packed into one dword (byte i from the i-th argument).
+__device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+    return ab | (cd << 16);
+}
+
+// Group-128 INT8 quantisation (page "Baseline and the integer
+// breakthrough", "Calculate with small integers" step 1) of one row slot's
+// group, 16 elements per lane: lane j of the slot holds elements
+// 16j..16j+15 in v.  Returns the lane's 16 codes in plane order (dword s =
+// codes 16j + s, +4, +8, +12) and sets gsum (group sum of q, all 8 lanes)
+// and scale (max|x| / 127, correctly rounded).  The codes equal the
+// definition q = clamp(rint(RN(x / d)), +-127), d = scale or 1 for an
+// all-zero group, bit for bit:
+//  * r = 1/d from the hardware reciprocal refined by one Newton step lies
+//    within 2^-22 (relative) of 1/d, so t = RN(x * r) differs from x / d by
+//    at most 127.0001 * (2^-22 + 2^-24) and from RN(x / d) by less than
+//    4.3e-5 < 2^-14 whenever d is normal (|x / d| <= 127 * (1 + 2^-23), and
+//    half an ulp of RN(x / d) below 128 is 2^-18);
+//  * so if t lies at least 2^-14 from every half-integer, rint(t) is
+//    rint(RN(x / d)).  Adding 1.5 * 2^23 rounds t to that integer in the
+//    low mantissa bits, whose low byte is the two's-complement code, and
+//    |t| < 127.5 makes the clamp a no-op;
+//  * otherwise (a near-tie in any of the lane's 16 elements, or d
+//    subnormal) the lane repeats the definition with IEEE divisions.
+__device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum, float& scale) {
+#pragma clang fp contract(off)
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    amax = max8_f(amax);
+    scale = amax / 127.0f;
+    const float d = scale > 0.0f ? scale : 1.0f;
+    const float r0 = __builtin_amdgcn_rcpf(d);
+    const float r = __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
+    constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+    uint32_t bits[16];
+    float worst = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float t = v[e] * r;
+        const float s = t + kRound;
+        worst = fmaxf(worst, fabsf(t - (s - kRound)));
+        bits[e] = __float_as_uint(s);
+    }
+    if (!(d >= 0x1p-126f && worst <= 0.5f - 0x1p-14f)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float qf = fminf(127.0f, fmaxf(-127.0f, rintf(v[e] / d)));
+            bits[e] = (uint32_t)(int)qf;
+        }
+    }
+    uint4 out;
+    out.x = low_bytes4(bits[0], bits[4], bits[8], bits[12]);
+    out.y = low_bytes4(bits[1], bits[5], bits[9], bits[13]);
+    out.z = low_bytes4(bits[2], bits[6], bits[10], bits[14]);
+    out.w = low_bytes4(bits[3], bits[7], bits[11], bits[15]);
+    int s = dot4(out.x, 0x01010101u, 0);
+    s = dot4(out.y, 0x01010101u, s);
+    s = dot4(out.z, 0x01010101u, s);
+    s = dot4(out.w, 0x01010101u, s);
+    gsum = sum8_i(s);
+    return out;
+}
+
+// The 16 elements of x a lane quantises, from its SRC-typed 16-byte loads.
+template <int SRC>
+__device__ __forceinline__ void x_to_float16(const uint4 (&w)[src_xloads(SRC)], float (&v)[16]) {
+    if constexpr (SRC == kSrcF32) {
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            v[4 * l + 0] = __uint_as_float(w[l].x);
+            v[4 * l + 1] = __uint_as_float(w[l].y);
+            v[4 * l + 2] = __uint_as_float(w[l].z);
+            v[4 * l + 3] = __uint_as_float(w[l].w);
+        }
+    } else {
+#pragma unroll
+        for (int l = 0; l < 2; ++l) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t d = word_of(w[l], i);
+                if constexpr (SRC == kSrcBf16) {
+                    v[8 * l + 2 * i] = __uint_as_float(d << 16);
+                    v[8 * l + 2 * i + 1] = __uint_as_float(d & 0xFFFF0000u);
+                } else {
+                    v[8 * l + 2 * i] = __half2float(__ushort_as_half((unsigned short)(d & 0xFFFFu)));
+                    v[8 * l + 2 * i + 1] = __half2float(__ushort_as_half((unsigned short)(d >> 16)));
+                }
+            }
+        }
+    }
+}
+
+}  // namespace pq2

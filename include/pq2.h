@@ -147,16 +147,20 @@ int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const voi
                                     int64_t k, float* y, int tile, void* stream);
 
 /* Tuning hook for the small-m matmul (benchmarks and tests only; same
- * arguments and result as pq2_matmul_small_m).  rows_per_lane in {1,2}
- * (weight rows per lane, packed-dot engine), max_waves in 1..8 (waves that
- * split k inside one workgroup), engine 1 = packed dot products (v_dot4),
- * 2 = INT8 matrix cores (v_mfma); 0 for any of them picks the library's
- * default.  The summation order of an output depends on max_waves only
- * (through the number of waves k is split over): neither rows_per_lane nor
- * the engine changes the bits.  Errors as pq2_matmul_small_m, plus EINVAL for
- * an unsupported setting. */
+ * arguments and result as pq2_matmul_small_m).  engine selects one of three
+ * kernels that compute the same bits:
+ *   1 = packed dot products (v_dot4), `rows` = weight rows per lane (1, 2);
+ *   2 = INT8 matrix cores (v_mfma), one 8-row block per workgroup, `rows` = 1;
+ *   3 = INT8 matrix cores, `rows` 8-row blocks per workgroup (1, 2),
+ *       with the fewest instructions per weight.
+ * max_waves in 1..8 is the number of waves that split k inside one
+ * workgroup.  0 for any setting picks the library's default (with an
+ * explicit engine, that engine's default rows).  The summation order of an
+ * output depends on max_waves only (through the number of waves k is split
+ * over): neither rows nor the engine changes the bits.  Errors as
+ * pq2_matmul_small_m, plus EINVAL for an unsupported setting. */
 int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
-                             int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
+                             int64_t n, int64_t k, float* y, int rows, int max_waves,
                              int engine, void* stream);
 
 /* Plane-order variant of pq2_quantize_act_i8 for the decode path (page
@@ -200,7 +204,7 @@ int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* 
  * same bits as pq2_matmul_small_m_tuned with the same settings.  Errors as
  * pq2_matmul_small_m_planes, plus EINVAL for an unsupported setting. */
 int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
-                                    int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane,
+                                    int64_t m, int64_t n, int64_t k, float* y, int rows,
                                     int max_waves, int engine, void* stream);
 
 /* Quantise + small-m matmul in one launch: y = the definition above for the
@@ -228,7 +232,7 @@ int pq2_matmul_small_m_fused(const void* x, int dtype, int64_t x_row_stride_elem
  * Errors as pq2_matmul_small_m_fused, plus EINVAL for an unsupported
  * setting. */
 int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes,
-                                   int64_t m, int64_t n, int64_t k, float* y, int rows_per_lane, int max_waves,
+                                   int64_t m, int64_t n, int64_t k, float* y, int rows, int max_waves,
                                    int engine, void* stream);
 
 #ifdef __cplusplus

@@ -1,6 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every symbol that
 include/pq2.h declares, and rejects bad arguments on the host before any HIP
-call (every case below fails validation, so nothing is ever launched)."""
+call (every case below fails validation or, without a GPU, the device check,
+so nothing is ever launched)."""
 import ctypes
 import os
 import re
@@ -12,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "pq2.h")
 
 import gemm_int8_act_amd as pq2  # noqa: E402
 
-OK, EINVAL, ESHAPE, EALIGN = pq2.PQ2_OK, pq2.PQ2_EINVAL, pq2.PQ2_ESHAPE, pq2.PQ2_EALIGN
+OK, EINVAL, ESHAPE, EALIGN, EDEVICE = pq2.PQ2_OK, pq2.PQ2_EINVAL, pq2.PQ2_ESHAPE, pq2.PQ2_EALIGN, pq2.PQ2_EDEVICE
 
 # Fake device addresses: never dereferenced, because validation fails first.
 A = 0x7F0000000000          # 4 KiB aligned
@@ -20,6 +21,11 @@ B = 0x7F0100000000
 C = 0x7F0200000000
 D = 0x7F0300000000
 E = 0x7F0400000000
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0  # counts devices without initialising the runtime
 
 
 def _declared_symbols():
@@ -94,11 +100,23 @@ def test_small_m_column_limit_and_tuning_validation():
     f = pq2.lib.pq2_matmul_small_m
     assert f(A, B, C, 17, 8, 128, D, None) == ESHAPE
     t = pq2.lib.pq2_matmul_small_m_tuned
-    assert t(A, B, C, 1, 8, 128, D, 3, 0, 0, None) == EINVAL   # rows per lane
-    assert t(A, B, C, 1, 8, 128, D, 4, 0, 0, None) == EINVAL
+    assert t(A, B, C, 1, 8, 128, D, 3, 0, 1, None) == EINVAL   # rows per lane of the packed-dot engine
+    assert t(A, B, C, 1, 8, 128, D, 4, 0, 1, None) == EINVAL
+    assert t(A, B, C, 1, 8, 128, D, 2, 0, 2, None) == EINVAL   # one row block per matrix-core workgroup
+    assert t(A, B, C, 1, 8, 128, D, 100, 0, 3, None) == EINVAL  # more row blocks than a workgroup's waves run
+    assert t(A, B, C, 4, 8, 65536, D, 2, 0, 3, None) == EINVAL  # more items per wave than it holds
     assert t(A, B, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL   # waves
-    assert t(A, B, C, 1, 8, 128, D, 0, 0, 3, None) == EINVAL   # engine
+    assert t(A, B, C, 1, 8, 128, D, 0, 0, 4, None) == EINVAL   # engine
     assert t(A, B, C, 17, 8, 128, D, 1, 1, 1, None) == ESHAPE
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="the device check passes on a GPU")
+def test_small_m_valid_settings_reach_the_device_check():
+    """Every supported (rows, engine) setting passes validation: without a
+    GPU the call gets as far as the device check."""
+    t = pq2.lib.pq2_matmul_small_m_tuned
+    for rows, engine in ((0, 0), (1, 1), (2, 1), (1, 2), (1, 3), (2, 3), (0, 3)):
+        assert t(A, B, C, 4, 8, 128, D, rows, 0, engine, None) == EDEVICE, (rows, engine)
 
 
 def test_prefill_tile_validation():
@@ -135,7 +153,8 @@ def test_small_m_planes_validation():
     assert f(A, B, E + 2, C, 1, 8, 128, D, None) == EALIGN    # qsum 4-byte alignment
     assert f(A, B, E, C, 1, 8, 128, E, None) == EINVAL        # y overlaps qsum
     t = pq2.lib.pq2_matmul_small_m_planes_tuned
-    assert t(A, B, E, C, 1, 8, 128, D, 4, 0, 0, None) == EINVAL  # rows per lane
+    assert t(A, B, E, C, 1, 8, 128, D, 4, 0, 1, None) == EINVAL  # rows per lane
+    assert t(A, B, E, C, 1, 8, 128, D, 100, 0, 3, None) == EINVAL  # row blocks
     assert t(A, B, E, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL  # waves
     assert t(A, B, E, C, 1, 8, 128, D, 0, 0, 7, None) == EINVAL  # engine
 
@@ -159,9 +178,10 @@ def test_small_m_fused_validation():
     assert f(A, 0, 128, C, 1, 8, 128, A + 64, None) == EINVAL   # y overlaps x
     assert f(A, 0, 128, C, 1, 8, 128, C + 16, None) == EINVAL   # y overlaps planes
     t = pq2.lib.pq2_matmul_small_m_fused_tuned
-    assert t(A, 0, 128, C, 1, 8, 128, D, 3, 0, 0, None) == EINVAL  # rows per lane
+    assert t(A, 0, 128, C, 1, 8, 128, D, 3, 0, 1, None) == EINVAL  # rows per lane
+    assert t(A, 0, 128, C, 1, 8, 128, D, 100, 0, 3, None) == EINVAL  # row blocks
     assert t(A, 0, 128, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL  # waves
-    assert t(A, 0, 128, C, 1, 8, 128, D, 0, 0, 3, None) == EINVAL  # engine
+    assert t(A, 0, 128, C, 1, 8, 128, D, 0, 0, 4, None) == EINVAL  # engine
 
 
 def test_python_binding_rejects_host_tensors():

@@ -193,8 +193,9 @@ def test_small_m_zero_activations():
 
 @pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
 def test_small_m_matrix_core_engine_full(m, n, k):
-    """The matrix-core engine against the oracle, and bit-identical to the
-    packed-dot engine, on every full-comparison shape, both input orders."""
+    """The matrix-core engines against the oracle, and bit-identical to the
+    packed-dot engine, on every full-comparison shape, both input orders and
+    every row-block count of the row-streaming engine."""
     pq2 = _pq2()
     announce(f"small_m matrix-core engine m={m} n={n} k={k}")
     raw = workloads.make_raw_weights(n, k, seed=90 + m + n, codes="ternary+3", row_pad=2)
@@ -209,13 +210,18 @@ def test_small_m_matrix_core_engine_full(m, n, k):
     qp, xsp, qsum = gpu_quantize_planes(x.to(DEV))
     yp = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xsp, qsum, planes, n, engine=2)
     assert np.array_equal(yp.view(np.uint32), y1.view(np.uint32)), "plane-order matrix-core path differs"
+    for rows in (0, 1):  # the library's row blocks per workgroup, and one
+        y3 = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows=rows, engine=3)
+        assert np.array_equal(y3.view(np.uint32), y1.view(np.uint32)), f"workgroup-staged engine rows={rows} differs"
+        y3p = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xsp, qsum, planes, n, rows=rows, engine=3)
+        assert np.array_equal(y3p.view(np.uint32), y1.view(np.uint32)), f"plane-order engine 3 rows={rows} differs"
 
 
 @pytest.mark.parametrize("m", [1, 4, 11])
 def test_small_m_tuning_variants(m):
-    """Every rows-per-lane / k-split / engine setting is within the bound;
-    neither rows per lane nor the engine (packed dots or matrix cores)
-    changes the summation order, so they keep the bits."""
+    """Every rows / k-split / engine setting is within the bound; neither
+    rows nor the engine (packed dots, matrix cores, workgroup-staged matrix
+    cores) changes the summation order, so they keep the bits."""
     pq2 = _pq2()
     n, k = 200, 5248
     announce(f"small_m variants m={m}")
@@ -228,8 +234,8 @@ def test_small_m_tuning_variants(m):
     assert_within(y0, y_ref, bound, "default")
     for waves in (1, 2, 3, 5, 8):
         ys = []
-        for rows, engine in ((1, 1), (2, 1), (1, 2)):
-            y = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows_per_lane=rows, max_waves=waves,
+        for rows, engine in ((1, 1), (2, 1), (1, 2), (1, 3), (2, 3)):
+            y = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows=rows, max_waves=waves,
                            engine=engine)
             assert_within(y, y_ref, bound, f"rows={rows} waves={waves} engine={engine}")
             ys.append(y)
@@ -464,21 +470,21 @@ def test_small_m_planes_full(m, n, k):
     assert np.array_equal(y.view(np.uint32), y_nat.view(np.uint32)), "plane-order and natural paths differ"
 
 
-@pytest.mark.parametrize("rows,waves", [(1, 1), (1, 5), (2, 3), (2, 8)])
-def test_small_m_planes_tuning_variants(rows, waves):
+@pytest.mark.parametrize("rows,waves,engine", [(1, 1, 1), (1, 5, 1), (2, 3, 1), (2, 8, 1), (2, 3, 3), (1, 8, 3)])
+def test_small_m_planes_tuning_variants(rows, waves, engine):
     pq2 = _pq2()
     m, n, k = 4, 200, 5248
-    announce(f"small_m planes variants rows={rows} waves={waves}")
+    announce(f"small_m planes variants rows={rows} waves={waves} engine={engine}")
     raw = workloads.make_raw_weights(n, k, seed=7, codes="ternary+3")
     x = workloads.make_activations(m, k, 8, "laplace")
     qp, xs, qsum, qo, xso = quantise_planes_both(x)
     planes = gpu_planes(raw, n, k)
     y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
-    y = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xs, qsum, planes, n, rows_per_lane=rows,
-                          max_waves=waves)
-    assert_within(y, y_ref, bound, f"planes rows={rows} waves={waves}")
+    y = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xs, qsum, planes, n, rows=rows,
+                          max_waves=waves, engine=engine)
+    assert_within(y, y_ref, bound, f"planes rows={rows} waves={waves} engine={engine}")
     q, xs2 = gpu_quantize(x.to(DEV))
-    y_nat = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs2, planes, n, rows_per_lane=rows, max_waves=waves)
+    y_nat = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs2, planes, n, rows=rows, max_waves=waves, engine=engine)
     assert np.array_equal(y.view(np.uint32), y_nat.view(np.uint32)), "same settings, same bits"
 
 
@@ -540,10 +546,10 @@ def test_fused_full(m, n, k):
     planes = gpu_planes(raw, n, k)
     y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
     xd = x.to(DEV)
-    for rows, engine in ((1, 1), (2, 1), (1, 2)):
-        yf = gpu_fused(xd, planes, n, rows_per_lane=rows, engine=engine)
+    for rows, engine in ((1, 1), (2, 1), (1, 2), (0, 3), (1, 3)):
+        yf = gpu_fused(xd, planes, n, rows=rows, engine=engine)
         assert_within(yf, y_ref, bound, f"fused rows={rows} engine={engine}")
-        yu = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows_per_lane=rows, engine=engine)
+        yu = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows=rows, engine=engine)
         assert same_bits(yf, yu), f"fused rows={rows} engine={engine} differs from quantise + matmul"
     y0 = gpu_fused(xd, planes, n)
     assert same_bits(y0, gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, n)), "default fused path differs"
@@ -622,8 +628,8 @@ def test_fused_quantiser_codes_exact(dtype):
     raw = probe_weights(k)
     planes = gpu_planes(raw, k, k)
     expect = qo.astype(np.float32) * np.repeat(xso, 128, axis=1)
-    for rows, engine in ((1, 1), (1, 2)):
-        y = gpu_fused(x.to(DEV), planes, k, rows_per_lane=rows, engine=engine)
+    for rows, engine in ((1, 1), (1, 2), (1, 3), (2, 3)):
+        y = gpu_fused(x.to(DEV), planes, k, rows=rows, engine=engine)
         bad = np.argwhere(y.view(np.uint32) != expect.view(np.uint32))
         assert bad.size == 0, f"engine={engine}: {len(bad)} codes differ, first at {tuple(bad[0])}: " \
                               f"{y[tuple(bad[0])]!r} vs {expect[tuple(bad[0])]!r}"
