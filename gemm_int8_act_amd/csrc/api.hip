@@ -70,14 +70,15 @@ int small_m_config(int src, int64_t m, int64_t n, int64_t k, int rows, int max_w
     if (engine && engine != cfg->engine) {
         cfg->engine = engine;
         cfg->rows = pq2::default_small_m_rows(engine, src, m, n, k, cfg->max_waves);
-    } else if (max_waves && cfg->engine == 3) {
-        cfg->rows = pq2::default_small_m_rows(3, src, m, n, k, cfg->max_waves);
+    } else if (max_waves && cfg->engine >= 3) {
+        cfg->rows = pq2::default_small_m_rows(cfg->engine, src, m, n, k, cfg->max_waves);
     }
     if (rows) cfg->rows = rows;
     switch (cfg->engine) {
         case 1: return (cfg->rows == 1 || cfg->rows == 2) ? PQ2_OK : PQ2_EINVAL;
         case 2: return cfg->rows == 1 ? PQ2_OK : PQ2_EINVAL;
-        case 3: return pq2::wg_supported(src, m, k, cfg->max_waves, cfg->rows) ? PQ2_OK : PQ2_EINVAL;
+        case 3: return pq2::wg_supported(src, m, k, cfg->max_waves, cfg->rows, false) ? PQ2_OK : PQ2_EINVAL;
+        case 4: return pq2::wg_supported(src, m, k, cfg->max_waves, cfg->rows, true) ? PQ2_OK : PQ2_EINVAL;
         default: return PQ2_EINVAL;
     }
 }

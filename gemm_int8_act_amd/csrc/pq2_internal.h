@@ -35,11 +35,12 @@ hipError_t launch_quantize_planes(const void* x, int dtype, int64_t row_stride, 
                                   int8_t* qp, float* xs, int32_t* qsum, hipStream_t stream);
 
 struct SmallMConfig {
-    int rows;       // engine 1: weight rows per lane (1, 2); engine 3: 8-row blocks per workgroup
+    int rows;       // engine 1: weight rows per lane (1, 2); engines 3, 4: 8-row blocks per workgroup
     int max_waves;  // 1..8: waves that split k inside one workgroup
     int engine;     // 1 = packed dot products (v_dot4), 2 = INT8 matrix cores, one row block per
                     // workgroup, 3 = INT8 matrix cores, one 8-wave workgroup staging the
-                    // activations for `rows` row blocks; same bits
+                    // activations for `rows` row blocks, 4 = the same kernel with one
+                    // unit per wave; same bits
 };
 
 // Arguments of one small-m launch, any engine.  waves, nseg, per_wave and
@@ -62,10 +63,11 @@ struct SmallMLaunch {
 constexpr int kWgMaxColumns = 4;
 
 // Workgroup-staged matrix-core engine (small_m_wg.hip); src is a kSrc* value
-// and rows the row blocks (8 weight rows) per workgroup.
-bool wg_supported(int src, int64_t m, int64_t k, int max_waves, int rows);
-int wg_default_row_blocks(int src, int64_t m, int64_t n, int64_t k, int max_waves);  // 0: unsupported
-hipError_t launch_small_m_wg(int src, const SmallMLaunch& a, int max_waves, int rows);
+// and rows the row blocks (8 weight rows) per workgroup.  wave_mode false:
+// one 8-wave workgroup per CU (engine 3); true: one unit per wave (engine 4).
+bool wg_supported(int src, int64_t m, int64_t k, int max_waves, int rows, bool wave_mode);
+int wg_default_row_blocks(int src, int64_t m, int64_t n, int64_t k, int max_waves, bool wave_mode);  // 0: none
+hipError_t launch_small_m_wg(int src, const SmallMLaunch& a, int max_waves, int rows, bool wave_mode);
 
 // The library's choice for activations of kind src; the k split (max_waves)
 // depends on (n, k) only, so every source and column count sums in one order.

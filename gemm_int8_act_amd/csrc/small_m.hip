@@ -658,7 +658,7 @@ hipError_t dispatch(const Launch& a, int engine, int mc, int rows, int segs) {
 
 hipError_t launch_any(int src, const Launch& base, const SmallMConfig& cfg) {
     if (cfg.max_waves < 1 || cfg.max_waves > 8) return hipErrorInvalidValue;
-    if (cfg.engine == 3) return launch_small_m_wg(src, base, cfg.max_waves, cfg.rows);
+    if (cfg.engine == 3 || cfg.engine == 4) return launch_small_m_wg(src, base, cfg.max_waves, cfg.rows, cfg.engine == 4);
     if (cfg.engine != 1 && cfg.engine != 2) return hipErrorInvalidValue;
     const int rows = cfg.engine == 2 ? 1 : cfg.rows;
     if (rows != 1 && rows != 2) return hipErrorInvalidValue;
@@ -702,7 +702,8 @@ int default_small_m_rows(int engine, int src, int64_t m, int64_t n, int64_t k, i
     switch (engine) {
         case 1: return src_fused(src) ? 2 : (m <= 4 ? 1 : 2);
         case 2: return 1;
-        case 3: return wg_default_row_blocks(src, m, n, k, max_waves);
+        case 3: return wg_default_row_blocks(src, m, n, k, max_waves, false);
+        case 4: return wg_default_row_blocks(src, m, n, k, max_waves, true);
         default: return 0;
     }
 }

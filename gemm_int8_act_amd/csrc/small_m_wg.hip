@@ -52,10 +52,16 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kWgWaves = 8;
-constexpr int kWgThreads = 64 * kWgWaves;
-constexpr int kStageRounds = 8;   // staging quads per thread: nseg * MC * 64 <= 8 * 512
-constexpr int kMaxItems = 12;     // (row block, segment) items per wave
+// Two launch shapes share the kernel:
+//  * CU mode: one 8-wave workgroup per CU, up to 12 (row block, segment)
+//    items per wave (the activations are staged once per CU);
+//  * wave mode: one unit (row block, k slice) per wave, as many waves per
+//    workgroup as (row blocks x k slices) of the workgroup, up to 16, so
+//    that the grid has thousands of short waves and the staging is still
+//    shared by the row blocks of a workgroup.
+constexpr int kCuWaves = 8;
+constexpr int kCuItems = 12;
+constexpr int kMaxWgWaves = 16;
 
 // Zero quads read by A-operand lanes outside their k-block: the largest
 // immediate offset an A read adds is (4 * kBlockPitch + 3) quads.
@@ -75,8 +81,21 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 }  // namespace
 
-template <int MC, int SRC>
-__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2))) void small_m_wg_kernel(
+// Threads per workgroup and waves per SIMD the registers must leave room
+// for: CU mode runs one 8-wave workgroup per CU (2 waves per SIMD); wave mode
+// must keep its whole grid resident (up to 8 waves per SIMD for the common
+// one-item, few-round shapes); multi-segment units use at most 8 waves per
+// workgroup so that their code registers fit.
+constexpr int wg_threads(int max_items) { return max_items > 1 ? 64 * kCuWaves : 64 * kMaxWgWaves; }
+constexpr int wg_occupancy(int max_items, int rounds, int src) {
+    return max_items > 8 ? 2
+         : max_items > 1 ? ((src_fused(src) || rounds >= 8) ? 2 : 3)
+         : (rounds >= 8 || (src_fused(src) && rounds >= 4)) ? 4
+         : src_fused(src) ? 6 : 8;
+}
+
+template <int MC, int SRC, int MAX_ITEMS, int ROUNDS>
+__global__ __launch_bounds__(wg_threads(MAX_ITEMS)) __attribute__((amdgpu_waves_per_eu(wg_occupancy(MAX_ITEMS, ROUNDS, SRC)))) void small_m_wg_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const int32_t* __restrict__ qsum,
     const void* __restrict__ x, int64_t x_stride,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y, int n,
@@ -88,6 +107,8 @@ __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2)))
     constexpr int BLOCK_QUADS = kSegQuads;  // LDS quads of one (segment, column) block
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    const int nwaves = nthreads >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     // Matrix roles: code row, 16-byte chunk of the 128-byte span, its group (k-block) and half.
@@ -132,13 +153,13 @@ __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2)))
     //      ((s * MC + m) * 8 + slot) * 8 + j is quad j of group slot of segment
     //      s, column m; the 8 quads of a group sit in 8 consecutive lanes.
     const int stage_quads = nseg * MC * 64;
-    uint4 qv[kStageRounds];
-    uint4 xv[kStageRounds][XL];
-    uint32_t xsv[kStageRounds], tv[kStageRounds];
+    uint4 qv[ROUNDS];
+    uint4 xv[ROUNDS][XL];
+    uint32_t xsv[ROUNDS], tv[ROUNDS];
 #pragma unroll
-    for (int i = 0; i < kStageRounds; ++i) {
-        if (kWgThreads * i >= stage_quads) break;  // uniform
-        const int Q = tid + kWgThreads * i;
+    for (int i = 0; i < ROUNDS; ++i) {
+        if (nthreads * i >= stage_quads) break;  // uniform
+        const int Q = tid + nthreads * i;
         const int j = Q & 7;
         const int slot = (Q >> 3) & 7;
         const int sm = Q >> 6;
@@ -165,14 +186,14 @@ __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2)))
     // ---- 2. this wave's items (row block r, segment s) in the order they run:
     //      units u = wave, wave + 8, ..., each the segments of its k slice in
     //      order (uniform scalar bookkeeping), then their code and scale loads
-    int it_r[kMaxItems], it_s[kMaxItems], it_u[kMaxItems];
-    bool it_first[kMaxItems], it_last[kMaxItems];
+    int it_r[MAX_ITEMS], it_s[MAX_ITEMS], it_u[MAX_ITEMS];
+    bool it_first[MAX_ITEMS], it_last[MAX_ITEMS];
     {
         int u = wave;
         int sl = u % nslice;
         int s_cur = sl * per_wave;
 #pragma unroll
-        for (int i = 0; i < kMaxItems; ++i) {
+        for (int i = 0; i < MAX_ITEMS; ++i) {
             const int s_end = min(sl * per_wave + per_wave, nseg);
             it_u[i] = u;
             it_r[i] = u / nslice;
@@ -182,16 +203,16 @@ __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2)))
             if (s_cur + 1 < s_end) {
                 ++s_cur;
             } else {
-                u += kWgWaves;
+                u += nwaves;
                 sl = u % nslice;
                 s_cur = sl * per_wave;
             }
         }
     }
-    uint4 cw[kMaxItems][2];
-    uint32_t wsraw[kMaxItems][2];
+    uint4 cw[MAX_ITEMS][2];
+    uint32_t wsraw[MAX_ITEMS][2];
 #pragma unroll
-    for (int i = 0; i < kMaxItems; ++i) {
+    for (int i = 0; i < MAX_ITEMS; ++i) {
         if (it_u[i] >= units) break;  // uniform: items run in unit order
         const int g0 = it_s[i] * kGroupLanes;
         const uint32_t rl = (uint32_t)(it_r[i] * kRowSlots + row);
@@ -210,9 +231,9 @@ __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2)))
     // ---- 3. stage the activations (while the code loads are in flight)
     if (tid < kZeroQuads) reinterpret_cast<uint4*>(zero)[tid] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int i = 0; i < kStageRounds; ++i) {
-        const int Q = tid + kWgThreads * i;
-        if (kWgThreads * i >= stage_quads) break;  // uniform
+    for (int i = 0; i < ROUNDS; ++i) {
+        const int Q = tid + nthreads * i;
+        if (nthreads * i >= stage_quads) break;  // uniform
         const int j = Q & 7;
         const int slot = (Q >> 3) & 7;
         const int sm = Q >> 6;
@@ -260,7 +281,7 @@ __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const uint32_t meta_base = (uint32_t)((kb * kBlockPitch + 8) * 16);  // sum(q), xs of group kb (+4 sp)
     float acc[MP][2];
 #pragma unroll
-    for (int i = 0; i < kMaxItems; ++i) {
+    for (int i = 0; i < MAX_ITEMS; ++i) {
         if (it_u[i] >= units) break;  // uniform: items run in unit order
         const int s = it_s[i];
         v4i D[MP][2];
@@ -322,7 +343,7 @@ __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2)))
 
     // ---- 5. the k slices add in index order; one thread per (column, row)
     const int rows_pad = ((rows_here + kRowSlots - 1) / kRowSlots) * kRowSlots;
-    for (int o = tid; o < MC * rows_pad; o += kWgThreads) {
+    for (int o = tid; o < MC * rows_pad; o += nthreads) {
         const int m = o / rows_pad;
         const int rl = o - m * rows_pad;
         const int r = rl >> 3;
@@ -337,34 +358,57 @@ __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2)))
 namespace {
 
 constexpr size_t kWgLdsLimit = 150 * 1024;
+constexpr int kWaveItems = 8;  // wave mode: a unit of up to 8 segments per wave
 
-struct WgShape {
-    int nseg, per_wave, nslice;
+struct WgPlan {
+    int nseg, per_wave, nslice;  // k split: slices of per_wave segments
+    int mc, chunks;              // columns per pass, passes
+    int waves, items, rounds;    // waves per workgroup, items per wave, staging rounds
+    bool wave_mode;
+    size_t lds;
 };
 
-WgShape wg_shape(int64_t k, int max_waves) {
-    WgShape w;
-    w.nseg = (int)((k / 128 + kGroupLanes - 1) / kGroupLanes);
-    w.per_wave = (w.nseg + max_waves - 1) / max_waves;
-    w.nslice = (w.nseg + w.per_wave - 1) / w.per_wave;
-    return w;
+// Staging rounds the source's registers allow (fp32 input is twice as wide).
+int max_rounds(int src) { return src == kSrcF32 ? 4 : 8; }
+
+bool make_plan(int src, int64_t m, int64_t k, int max_waves, int rbw, bool wave_mode, WgPlan* p) {
+    if (max_waves < 1 || max_waves > 8 || rbw < 1 || src < 0) return false;
+    p->nseg = (int)((k / 128 + kGroupLanes - 1) / kGroupLanes);
+    p->per_wave = (p->nseg + max_waves - 1) / max_waves;
+    p->nslice = (p->nseg + p->per_wave - 1) / p->per_wave;
+    const int units = rbw * p->nslice;
+    p->wave_mode = wave_mode;
+    if (wave_mode) {
+        // Multi-segment units run in the 8-wave (512-thread) instantiation.
+        if (units > (p->per_wave > 1 ? kCuWaves : kMaxWgWaves) || p->per_wave > kWaveItems) return false;
+        p->waves = units;
+        p->items = p->per_wave;
+    } else {
+        p->waves = kCuWaves;
+        p->items = ((units + kCuWaves - 1) / kCuWaves) * p->per_wave;
+        if (p->items > kCuItems) return false;
+    }
+    // Columns per pass: up to four, fewer if the workgroup cannot stage the
+    // activations of all of k for more (more passes over the weights then).
+    const int64_t stage_cap = (int64_t)max_rounds(src) * p->waves * 64;
+    int cap = kWgMaxColumns;
+    auto lds_of = [&](int mc) {
+        return ((size_t)p->nseg * mc * kSegQuads + kZeroQuads) * 16 + (size_t)units * mc * kRowSlots * 4;
+    };
+    while (cap > 0 && ((int64_t)p->nseg * cap * 64 > stage_cap || lds_of(cap) > kWgLdsLimit)) --cap;
+    if (cap < 1) return false;
+    p->chunks = (int)((m + cap - 1) / cap);
+    p->mc = (int)((m + p->chunks - 1) / p->chunks);
+    const int64_t quads = (int64_t)p->nseg * p->mc * 64;
+    const int64_t rounds = (quads + p->waves * 64 - 1) / (p->waves * 64);
+    p->rounds = rounds <= 1 ? 1 : rounds <= 2 ? 2 : rounds <= 4 ? 4 : 8;
+    p->lds = lds_of(p->mc);
+    return true;
 }
 
-size_t wg_lds_bytes(int mc, const WgShape& w, int rbw) {
-    return ((size_t)w.nseg * mc * kSegQuads + kZeroQuads) * 16 + (size_t)rbw * w.nslice * mc * kRowSlots * 4;
-}
-
-// Items the busiest wave runs: units u = wave + 8 i, each per_wave segments.
-int wg_max_items(const WgShape& w, int rbw) {
-    const int units = rbw * w.nslice;
-    return ((units + kWgWaves - 1) / kWgWaves) * w.per_wave;
-}
-
-
-template <int MC, int SRC>
-hipError_t launch_wg_one(const SmallMLaunch& a, const WgShape& w, int rbw) {
-    auto kern = small_m_wg_kernel<MC, SRC>;
-    const size_t lds = wg_lds_bytes(MC, w, rbw);
+template <int MC, int SRC, int ITEMS, int ROUNDS>
+hipError_t launch_wg_one(const SmallMLaunch& a, const WgPlan& p, int rbw) {
+    auto kern = small_m_wg_kernel<MC, SRC, ITEMS, ROUNDS>;
     static bool attr_set = false;  // one instantiation = one static
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -374,76 +418,72 @@ hipError_t launch_wg_one(const SmallMLaunch& a, const WgShape& w, int rbw) {
     }
     const uint16_t* scales = reinterpret_cast<const uint16_t*>(a.planes + a.n * (a.k / 4));
     const int64_t nblk = (a.n + kRowSlots - 1) / kRowSlots;
-    const dim3 grid((unsigned)((nblk + rbw - 1) / rbw), (unsigned)a.chunks);
+    const dim3 grid((unsigned)((nblk + rbw - 1) / rbw), (unsigned)p.chunks);
     clear_stale_error();
-    hipLaunchKernelGGL(kern, grid, dim3(kWgThreads), lds, a.stream, a.q, a.xs, a.qsum, a.x, a.x_stride, a.planes,
-                       scales, a.y, (int)a.n, (int)a.k, (int)(a.k / 128), w.nseg, w.per_wave, rbw, (int)a.m);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * p.waves), p.lds, a.stream, a.q, a.xs, a.qsum, a.x, a.x_stride, a.planes,
+                       scales, a.y, (int)a.n, (int)a.k, (int)(a.k / 128), p.nseg, p.per_wave, rbw, (int)a.m);
     return hipGetLastError();
 }
 
+// Instantiations: CU mode (12 items, 8 rounds; 4 for fp32 input) and wave
+// mode (1 or 3 items, 2, 4 or 8 rounds).
+template <int MC, int SRC>
+hipError_t wg_pick_shape(const SmallMLaunch& a, const WgPlan& p, int rbw) {
+    constexpr int R8 = SRC == kSrcF32 ? 4 : 8;  // fp32 input stages at most 4 rounds
+    if (p.waves == kCuWaves && p.items > 1 && !p.wave_mode) return launch_wg_one<MC, SRC, kCuItems, R8>(a, p, rbw);
+    if (p.items == 1) {
+        switch (p.rounds) {
+            case 1: case 2: return launch_wg_one<MC, SRC, 1, 2>(a, p, rbw);
+            case 4: return launch_wg_one<MC, SRC, 1, 4>(a, p, rbw);
+            default: return launch_wg_one<MC, SRC, 1, R8>(a, p, rbw);
+        }
+    }
+    switch (p.rounds) {
+        case 1: case 2: return launch_wg_one<MC, SRC, kWaveItems, 2>(a, p, rbw);
+        case 4: return launch_wg_one<MC, SRC, kWaveItems, 4>(a, p, rbw);
+        default: return launch_wg_one<MC, SRC, kWaveItems, R8>(a, p, rbw);
+    }
+}
+
 template <int SRC>
-hipError_t wg_pick_mc(const SmallMLaunch& a, const WgShape& w, int mc, int rbw) {
-    switch (mc) {
-        case 1: return launch_wg_one<1, SRC>(a, w, rbw);
-        case 2: return launch_wg_one<2, SRC>(a, w, rbw);
-        case 3: return launch_wg_one<3, SRC>(a, w, rbw);
-        case 4: return launch_wg_one<4, SRC>(a, w, rbw);
+hipError_t wg_pick_mc(const SmallMLaunch& a, const WgPlan& p, int rbw) {
+    switch (p.mc) {
+        case 1: return wg_pick_shape<1, SRC>(a, p, rbw);
+        case 2: return wg_pick_shape<2, SRC>(a, p, rbw);
+        case 3: return wg_pick_shape<3, SRC>(a, p, rbw);
+        case 4: return wg_pick_shape<4, SRC>(a, p, rbw);
         default: return hipErrorInvalidValue;
     }
 }
 
-// Staging rounds the source's registers allow (fp32 input is twice as wide).
-int wg_stage_rounds(int src) { return src == kSrcF32 ? kStageRounds / 2 : kStageRounds; }
-
-// Columns per pass: up to four, fewer when one workgroup cannot stage the
-// activations of all of k for more (more passes over the weights then).
-int wg_pass_columns(int src, int64_t k) {
-    const int64_t nseg = (k / 128 + kGroupLanes - 1) / kGroupLanes;
-    int64_t cap = (int64_t)wg_stage_rounds(src) * kWgThreads / (nseg * 64);
-    while (cap > 0 && ((size_t)nseg * cap * kSegQuads + kZeroQuads) * 16 > kWgLdsLimit / 2) --cap;
-    return (int)(cap < kWgMaxColumns ? cap : kWgMaxColumns);
-}
-
-// Columns of each pass, balanced over the passes.
-int wg_columns(int src, int64_t m, int64_t k, int* chunks) {
-    const int cap = wg_pass_columns(src, k);
-    if (cap < 1) return 0;
-    const int64_t c = (m + cap - 1) / cap;
-    if (chunks) *chunks = (int)c;
-    return (int)((m + c - 1) / c);
-}
-
 }  // namespace
 
-bool wg_supported(int src, int64_t m, int64_t k, int max_waves, int rbw) {
-    if (max_waves < 1 || max_waves > 8 || rbw < 1) return false;
-    const WgShape w = wg_shape(k, max_waves);
-    const int mc = wg_columns(src, m, k, nullptr);
-    if (mc < 1 || wg_max_items(w, rbw) > kMaxItems) return false;
-    if ((int64_t)w.nseg * mc * 64 > (int64_t)wg_stage_rounds(src) * kWgThreads) return false;
-    return wg_lds_bytes(mc, w, rbw) <= kWgLdsLimit;
+bool wg_supported(int src, int64_t m, int64_t k, int max_waves, int rbw, bool wave_mode) {
+    WgPlan p;
+    return make_plan(src, m, k, max_waves, rbw, wave_mode, &p);
 }
 
-// Row blocks per workgroup: one workgroup per CU when that fits the item,
-// staging and LDS budgets, else the most that fits; 0 if none does.
-int wg_default_row_blocks(int src, int64_t m, int64_t n, int64_t k, int max_waves) {
+// Row blocks per workgroup.  CU mode: one workgroup per CU when that fits
+// the item, staging and LDS budgets, else the most that fits.  Wave mode:
+// the most row blocks whose units fit one workgroup (at most 16 waves).
+// 0 if no setting fits.
+int wg_default_row_blocks(int src, int64_t m, int64_t n, int64_t k, int max_waves, bool wave_mode) {
     const int64_t nblk = (n + kRowSlots - 1) / kRowSlots;
-    int rbw = (int)((nblk + 255) / 256);
-    while (rbw > 1 && !wg_supported(src, m, k, max_waves, rbw)) --rbw;
-    return wg_supported(src, m, k, max_waves, rbw) ? rbw : 0;
+    int rbw = wave_mode ? kMaxWgWaves : (int)((nblk + 255) / 256);
+    if (rbw > nblk) rbw = (int)nblk;
+    while (rbw > 1 && !wg_supported(src, m, k, max_waves, rbw, wave_mode)) --rbw;
+    return wg_supported(src, m, k, max_waves, rbw, wave_mode) ? rbw : 0;
 }
 
-hipError_t launch_small_m_wg(int src, const SmallMLaunch& base, int max_waves, int rbw) {
-    if (!wg_supported(src, base.m, base.k, max_waves, rbw)) return hipErrorInvalidValue;
-    const WgShape w = wg_shape(base.k, max_waves);
-    SmallMLaunch a = base;
-    const int mc = wg_columns(src, base.m, base.k, &a.chunks);
+hipError_t launch_small_m_wg(int src, const SmallMLaunch& base, int max_waves, int rbw, bool wave_mode) {
+    WgPlan p;
+    if (!make_plan(src, base.m, base.k, max_waves, rbw, wave_mode, &p)) return hipErrorInvalidValue;
     switch (src) {
-        case kSrcPlanes: return wg_pick_mc<kSrcPlanes>(a, w, mc, rbw);
-        case kSrcNatural: return wg_pick_mc<kSrcNatural>(a, w, mc, rbw);
-        case kSrcBf16: return wg_pick_mc<kSrcBf16>(a, w, mc, rbw);
-        case kSrcF16: return wg_pick_mc<kSrcF16>(a, w, mc, rbw);
-        case kSrcF32: return wg_pick_mc<kSrcF32>(a, w, mc, rbw);
+        case kSrcPlanes: return wg_pick_mc<kSrcPlanes>(base, p, rbw);
+        case kSrcNatural: return wg_pick_mc<kSrcNatural>(base, p, rbw);
+        case kSrcBf16: return wg_pick_mc<kSrcBf16>(base, p, rbw);
+        case kSrcF16: return wg_pick_mc<kSrcF16>(base, p, rbw);
+        case kSrcF32: return wg_pick_mc<kSrcF32>(base, p, rbw);
         default: return hipErrorInvalidValue;
     }
 }

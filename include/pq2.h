@@ -147,12 +147,17 @@ int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const voi
                                     int64_t k, float* y, int tile, void* stream);
 
 /* Tuning hook for the small-m matmul (benchmarks and tests only; same
- * arguments and result as pq2_matmul_small_m).  engine selects one of three
+ * arguments and result as pq2_matmul_small_m).  engine selects one of four
  * kernels that compute the same bits:
  *   1 = packed dot products (v_dot4), `rows` = weight rows per lane (1, 2);
  *   2 = INT8 matrix cores (v_mfma), one 8-row block per workgroup, `rows` = 1;
- *   3 = INT8 matrix cores, `rows` 8-row blocks per workgroup (1, 2),
- *       with the fewest instructions per weight.
+ *   3 = INT8 matrix cores, one 8-wave workgroup per CU that stages the
+ *       activations of its k range once in LDS for `rows` 8-row blocks;
+ *       its waves take the (row block, k slice) units in turn;
+ *   4 = the kernel of engine 3 with one unit per wave: `rows` 8-row blocks
+ *       per workgroup, one wave per (row block, k slice).
+ *   Engines 3 and 4 cover at most 4 columns per pass over the weights and
+ *   accept only the `rows` whose staging fits LDS and the wave limits.
  * max_waves in 1..8 is the number of waves that split k inside one
  * workgroup.  0 for any setting picks the library's default (with an
  * explicit engine, that engine's default rows).  The summation order of an

@@ -106,7 +106,7 @@ def test_small_m_column_limit_and_tuning_validation():
     assert t(A, B, C, 1, 8, 128, D, 100, 0, 3, None) == EINVAL  # more row blocks than a workgroup's waves run
     assert t(A, B, C, 4, 8, 65536, D, 2, 0, 3, None) == EINVAL  # more items per wave than it holds
     assert t(A, B, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL   # waves
-    assert t(A, B, C, 1, 8, 128, D, 0, 0, 4, None) == EINVAL   # engine
+    assert t(A, B, C, 1, 8, 128, D, 0, 0, 5, None) == EINVAL   # engine
     assert t(A, B, C, 17, 8, 128, D, 1, 1, 1, None) == ESHAPE
 
 
@@ -115,7 +115,7 @@ def test_small_m_valid_settings_reach_the_device_check():
     """Every supported (rows, engine) setting passes validation: without a
     GPU the call gets as far as the device check."""
     t = pq2.lib.pq2_matmul_small_m_tuned
-    for rows, engine in ((0, 0), (1, 1), (2, 1), (1, 2), (1, 3), (2, 3), (0, 3)):
+    for rows, engine in ((0, 0), (1, 1), (2, 1), (1, 2), (1, 3), (2, 3), (0, 3), (1, 4), (0, 4)):
         assert t(A, B, C, 4, 8, 128, D, rows, 0, engine, None) == EDEVICE, (rows, engine)
 
 
@@ -181,7 +181,7 @@ def test_small_m_fused_validation():
     assert t(A, 0, 128, C, 1, 8, 128, D, 3, 0, 1, None) == EINVAL  # rows per lane
     assert t(A, 0, 128, C, 1, 8, 128, D, 100, 0, 3, None) == EINVAL  # row blocks
     assert t(A, 0, 128, C, 1, 8, 128, D, 0, 9, 0, None) == EINVAL  # waves
-    assert t(A, 0, 128, C, 1, 8, 128, D, 0, 0, 4, None) == EINVAL  # engine
+    assert t(A, 0, 128, C, 1, 8, 128, D, 0, 0, 5, None) == EINVAL  # engine
 
 
 def test_python_binding_rejects_host_tensors():

@@ -210,11 +210,15 @@ def test_small_m_matrix_core_engine_full(m, n, k):
     qp, xsp, qsum = gpu_quantize_planes(x.to(DEV))
     yp = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xsp, qsum, planes, n, engine=2)
     assert np.array_equal(yp.view(np.uint32), y1.view(np.uint32)), "plane-order matrix-core path differs"
-    for rows in (0, 1):  # the library's row blocks per workgroup, and one
-        y3 = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows=rows, engine=3)
-        assert np.array_equal(y3.view(np.uint32), y1.view(np.uint32)), f"workgroup-staged engine rows={rows} differs"
-        y3p = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xsp, qsum, planes, n, rows=rows, engine=3)
-        assert np.array_equal(y3p.view(np.uint32), y1.view(np.uint32)), f"plane-order engine 3 rows={rows} differs"
+    for engine in (3, 4):
+        for rows in (0, 1):  # the library's row blocks per workgroup, and one
+            y3 = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows=rows, engine=engine)
+            assert np.array_equal(y3.view(np.uint32), y1.view(np.uint32)), \
+                f"workgroup-staged engine {engine} rows={rows} differs"
+            y3p = gpu_matmul_planes(pq2.pq2_matmul_small_m_planes_tuned, qp, xsp, qsum, planes, n, rows=rows,
+                                    engine=engine)
+            assert np.array_equal(y3p.view(np.uint32), y1.view(np.uint32)), \
+                f"plane-order engine {engine} rows={rows} differs"
 
 
 @pytest.mark.parametrize("m", [1, 4, 11])
@@ -234,7 +238,7 @@ def test_small_m_tuning_variants(m):
     assert_within(y0, y_ref, bound, "default")
     for waves in (1, 2, 3, 5, 8):
         ys = []
-        for rows, engine in ((1, 1), (2, 1), (1, 2), (1, 3), (2, 3)):
+        for rows, engine in ((1, 1), (2, 1), (1, 2), (1, 3), (2, 3), (1, 4), (2, 4)):
             y = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows=rows, max_waves=waves,
                            engine=engine)
             assert_within(y, y_ref, bound, f"rows={rows} waves={waves} engine={engine}")
@@ -470,7 +474,7 @@ def test_small_m_planes_full(m, n, k):
     assert np.array_equal(y.view(np.uint32), y_nat.view(np.uint32)), "plane-order and natural paths differ"
 
 
-@pytest.mark.parametrize("rows,waves,engine", [(1, 1, 1), (1, 5, 1), (2, 3, 1), (2, 8, 1), (2, 3, 3), (1, 8, 3)])
+@pytest.mark.parametrize("rows,waves,engine", [(1, 1, 1), (1, 5, 1), (2, 3, 1), (2, 8, 1), (2, 3, 3), (1, 8, 3), (2, 3, 4), (0, 8, 4)])
 def test_small_m_planes_tuning_variants(rows, waves, engine):
     pq2 = _pq2()
     m, n, k = 4, 200, 5248
@@ -546,7 +550,7 @@ def test_fused_full(m, n, k):
     planes = gpu_planes(raw, n, k)
     y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
     xd = x.to(DEV)
-    for rows, engine in ((1, 1), (2, 1), (1, 2), (0, 3), (1, 3)):
+    for rows, engine in ((1, 1), (2, 1), (1, 2), (0, 3), (1, 3), (0, 4), (1, 4)):
         yf = gpu_fused(xd, planes, n, rows=rows, engine=engine)
         assert_within(yf, y_ref, bound, f"fused rows={rows} engine={engine}")
         yu = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, rows=rows, engine=engine)
@@ -628,7 +632,7 @@ def test_fused_quantiser_codes_exact(dtype):
     raw = probe_weights(k)
     planes = gpu_planes(raw, k, k)
     expect = qo.astype(np.float32) * np.repeat(xso, 128, axis=1)
-    for rows, engine in ((1, 1), (1, 2), (1, 3), (2, 3)):
+    for rows, engine in ((1, 1), (1, 2), (1, 3), (2, 3), (1, 4), (3, 4)):
         y = gpu_fused(x.to(DEV), planes, k, rows=rows, engine=engine)
         bad = np.argwhere(y.view(np.uint32) != expect.view(np.uint32))
         assert bad.size == 0, f"engine={engine}: {len(bad)} codes differ, first at {tuple(bad[0])}: " \
