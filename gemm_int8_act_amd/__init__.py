@@ -37,6 +37,10 @@ EXPORTED = (
     "pq2_matmul_small_m_planes",
     "pq2_matmul_small_m_planes_tuned",
     "pq2_matmul_prefill_tuned",
+    "pq2_tiles_bytes",
+    "pq2_prepare_tiles",
+    "pq2_matmul_small_m_tiles",
+    "pq2_matmul_small_m_tiles_tuned",
     "pq2_matmul_prefill_planes",
     "pq2_matmul_prefill_planes_tuned",
     "pq2_matmul_small_m_fused",
@@ -102,6 +106,14 @@ def _load_library():
     lib.pq2_matmul_small_m_fused.restype = i32
     lib.pq2_matmul_small_m_fused_tuned.argtypes = [p, i32, i64, p, i64, i64, i64, p, i32, i32, i32, p]
     lib.pq2_matmul_small_m_fused_tuned.restype = i32
+    lib.pq2_tiles_bytes.argtypes = [i64, i64]
+    lib.pq2_tiles_bytes.restype = i64
+    lib.pq2_prepare_tiles.argtypes = [p, i64, i64, i64, p, p]
+    lib.pq2_prepare_tiles.restype = i32
+    lib.pq2_matmul_small_m_tiles.argtypes = [p, p, p, i64, i64, i64, p, p]
+    lib.pq2_matmul_small_m_tiles.restype = i32
+    lib.pq2_matmul_small_m_tiles_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
+    lib.pq2_matmul_small_m_tiles_tuned.restype = i32
     return lib
 
 
@@ -210,6 +222,51 @@ def pq2_matmul_small_m(q, xs, planes, y, stream=None) -> None:
 def pq2_matmul_small_m_tuned(q, xs, planes, y, rows=0, max_waves=0, engine=0, stream=None) -> None:
     _check(lib.pq2_matmul_small_m_tuned(*_matmul_args(q, xs, planes, y), rows, max_waves, engine,
                                         _stream(stream)), "pq2_matmul_small_m_tuned")
+
+
+def pq2_tiles_bytes(n: int, k: int) -> int:
+    """Bytes of the tile layout of an n x k weight matrix (ValueError on a bad shape)."""
+    size = lib.pq2_tiles_bytes(n, k)
+    if size < 0:
+        raise ValueError(f"pq2_tiles_bytes: unsupported shape n={n} k={k}")
+    return size
+
+
+def pq2_prepare_tiles(raw, n: int, k: int, tiles, stream=None) -> None:
+    """raw: uint8 device tensor [n][row_stride]; tiles: contiguous uint8
+    device tensor of pq2_tiles_bytes(n, k) bytes."""
+    import torch
+    if raw.dtype != torch.uint8 or tiles.dtype != torch.uint8 or raw.dim() != 2 or raw.stride(1) != 1:
+        raise ValueError("raw must be a 2-D uint8 tensor with unit column stride; tiles uint8")
+    if tiles.numel() < pq2_tiles_bytes(n, k) or not tiles.is_contiguous():
+        raise ValueError("tiles must be a contiguous uint8 tensor of pq2_tiles_bytes(n, k) bytes")
+    _check(lib.pq2_prepare_tiles(_dev_ptr(raw, "raw"), raw.stride(0), n, k, _dev_ptr(tiles, "tiles"),
+                                 _stream(stream)), "pq2_prepare_tiles")
+
+
+def _tiles_args(q, xs, tiles, y):
+    import torch
+    if q.dtype != torch.int8 or xs.dtype != torch.float32 or tiles.dtype != torch.uint8 or y.dtype != torch.float32:
+        raise ValueError("q int8, xs float32, tiles uint8, y float32 expected")
+    for name, t in (("q", q), ("xs", xs), ("tiles", tiles), ("y", y)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    m, k = q.shape
+    n = y.shape[1]
+    if y.shape[0] != m or xs.numel() != m * (k // 128) or tiles.numel() < pq2_tiles_bytes(n, k):
+        raise ValueError("shape mismatch between q, xs, tiles and y")
+    return (_dev_ptr(q, "q"), _dev_ptr(xs, "xs"), _dev_ptr(tiles, "tiles"), m, n, k, _dev_ptr(y, "y"))
+
+
+def pq2_matmul_small_m_tiles(q, xs, tiles, y, stream=None) -> None:
+    """pq2_matmul_small_m from the tile layout (same bits)."""
+    _check(lib.pq2_matmul_small_m_tiles(*_tiles_args(q, xs, tiles, y), _stream(stream)),
+           "pq2_matmul_small_m_tiles")
+
+
+def pq2_matmul_small_m_tiles_tuned(q, xs, tiles, y, max_waves=0, split=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_tiles_tuned(*_tiles_args(q, xs, tiles, y), max_waves, split, _stream(stream)),
+           "pq2_matmul_small_m_tiles_tuned")
 
 
 def _fused_args(x, planes, y):

@@ -48,14 +48,14 @@ int check_k(int64_t k) {
 }
 
 int check_matmul_args(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
-                      int64_t k, float* y, int64_t m_max) {
+                      int64_t k, float* y, int64_t m_max, bool tiles = false) {
     if (!q || !xs || !planes || !y) return PQ2_EINVAL;
     if (m < 1 || m > m_max || n < 1 || n > kMaxN) return PQ2_ESHAPE;
     if (int rc = check_k(k)) return rc;
     if (!aligned(q, 16) || !aligned(planes, 16) || !aligned(xs, 4) || !aligned(y, 4)) return PQ2_EALIGN;
     const size_t ybytes = (size_t)m * n * 4;
     if (overlap(y, ybytes, q, (size_t)m * k) || overlap(y, ybytes, xs, (size_t)m * (k / kGroup) * 4) ||
-        overlap(y, ybytes, planes, (size_t)n * (k / kGroup) * 34))
+        overlap(y, ybytes, planes, tiles ? (size_t)pq2::tiles_bytes(n, k) : (size_t)n * (k / kGroup) * 34))
         return PQ2_EINVAL;
     return PQ2_OK;
 }
@@ -115,6 +115,42 @@ int pq2_prepare_planes(const void* raw, int64_t raw_row_stride_bytes, int64_t n,
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_prepare(static_cast<const uint8_t*>(raw), raw_row_stride_bytes, n, k,
                                              static_cast<uint8_t*>(planes), (hipStream_t)stream));
+}
+
+int64_t pq2_tiles_bytes(int64_t n, int64_t k) {
+    if (n < 1 || n > kMaxN || check_k(k)) return -1;
+    return pq2::tiles_bytes(n, k);
+}
+
+int pq2_prepare_tiles(const void* raw, int64_t raw_row_stride_bytes, int64_t n, int64_t k, void* tiles,
+                      void* stream) {
+    if (!raw || !tiles) return PQ2_EINVAL;
+    if (n < 1 || n > kMaxN) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (raw_row_stride_bytes < (k / kGroup) * 34) return PQ2_ESHAPE;
+    if (!aligned(tiles, 16)) return PQ2_EALIGN;
+    const size_t raw_bytes = (size_t)(n - 1) * raw_row_stride_bytes + (size_t)(k / kGroup) * 34;
+    if (overlap(raw, raw_bytes, tiles, (size_t)pq2::tiles_bytes(n, k))) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_prepare_tiles(static_cast<const uint8_t*>(raw), raw_row_stride_bytes, n, k,
+                                                   static_cast<uint8_t*>(tiles), (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                                   int64_t k, float* y, int max_waves, int split, void* stream) {
+    if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, PQ2_MAX_SMALL_M, true)) return rc;
+    if (max_waves < 0 || max_waves > 8) return PQ2_EINVAL;
+    const int waves = max_waves ? max_waves : pq2::default_small_m_config(pq2::kSrcNatural, m, n, k).max_waves;
+    if (!split) split = pq2::tiles_default_split(k, waves);
+    if (!pq2::tiles_supported(k, waves, split)) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m_tiles(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, y, waves,
+                                                   split, (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_tiles(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                             int64_t k, float* y, void* stream) {
+    return pq2_matmul_small_m_tiles_tuned(q, xs, tiles, m, n, k, y, 0, 0, stream);
 }
 
 int pq2_quantize_act_i8(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,

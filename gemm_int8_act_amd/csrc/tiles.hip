@@ -1,0 +1,396 @@
+// tiles.hip -- tile-major weight layout for the decode GEMV, and the
+// matrix-core small-m engine that reads it.
+//
+// Why a second layout (page "Kernel experiments: recorded evidence",
+// section H, Tests 24 and 25: storing the pieces a warp loads next to each
+// other lifted copy-only code reads to the streaming limit, and the
+// tile-major integer projection kept the output bits): the INT8 matrix
+// core's operand layout on gfx950 gives each lane 16 bytes of one weight row
+// and one 16-weight k block, so with row-major codes one load instruction
+// can cover at most 64 bytes of a row.  Here every load instruction of a
+// wave reads one contiguous kilobyte.
+//
+// Layout (all sizes in bytes; T = ceil(n/16) tiles of 16 rows, G = k/128
+// groups, G2 = ceil(G/2), S8 = ceil(G/8)):
+//   code part   T x G2 blocks of 1024, block (t, b) at (t*G2 + b)*1024.
+//               Lane l = j + 16*kb (j = row within the tile, kb = 0..3)
+//               owns bytes 16*l .. 16*l+15 of the block: dword u = 0..3
+//               holds the 16 weights k0 .. k0+15 of row 16t+j, with
+//               k0 = 128*(2b + u/2) + 64*(u%2) + 16*kb, and bits 2s..2s+1
+//               of its byte v hold the code of weight k0 + 4s + v.  (The
+//               prepared planes keep weight 4v + s there: inside each dword
+//               the 2-bit fields are 4x4-transposed, so bit plane s of a
+//               dword is the natural-order activation dword s.)
+//   scale part  at T*G2*1024: T x S8 blocks of 256, block (t, sb) at
+//               T*G2*1024 + (t*S8 + sb)*256, row j at +16*j: the eight fp16
+//               scales of groups 8*sb .. 8*sb+7.
+//   Rows >= n and groups >= G are padding: code 1 (weight 0), scale 0.
+// At even G with G % 8 == 0 (every shape measured here) the size equals the
+// prepared planes', n*k/128*34 when n % 16 == 0.
+//
+// Engine (same summation order as small_m.hip, so the same bits):
+//  * A workgroup owns one 16-row tile; its waves split k into consecutive
+//    segments of 8 groups exactly as the other small-m engines do.
+//  * Per group one wave issues v_mfma_i32_16x16x64_i8 twice with B = the two
+//    code dwords' bit planes (codes 0..3, natural order) and A = the
+//    activations of up to four columns; D starts from -sum(q) of each group
+//    and column, so the accumulated D is the exact dot of the codes minus 1
+//    with no decode of the -1 offset.
+//  * The wave stages its segment's activation blocks in a private LDS region
+//    (one load per column for the whole segment, no workgroup barrier) and
+//    reads the A operand from there; the fp32 terms
+//    fma((float)dot * xs, ws, acc) are accumulated per group class over the
+//    wave's segments, the classes added as ((A0+A4)+(A1+A5))+((A2+A6)+(A3+A7)),
+//    then the waves in index order.
+#include "pq2_internal.h"
+#include "pq2_device.h"
+
+#include <hip/hip_fp16.h>
+
+namespace pq2 {
+
+namespace {
+
+constexpr int kTileRows = 16;
+constexpr int kCodeBlock = 1024;   // one (tile, group pair) code block
+constexpr int kScaleBlock = 256;   // one (tile, 8 groups) scale block
+constexpr int kTilesMaxColumns = 4;
+
+struct TileGeometry {
+    int64_t tiles, g2, s8, code_bytes, total;
+};
+
+TileGeometry geometry(int64_t n, int64_t k) {
+    TileGeometry t;
+    const int64_t groups = k / 128;
+    t.tiles = (n + kTileRows - 1) / kTileRows;
+    t.g2 = (groups + 1) / 2;
+    t.s8 = (groups + 7) / 8;
+    t.code_bytes = t.tiles * t.g2 * kCodeBlock;
+    t.total = t.code_bytes + t.tiles * t.s8 * kScaleBlock;
+    return t;
+}
+
+// out byte v, field s = in byte s, field v (4x4 transpose of 2-bit fields).
+__device__ uint32_t transpose_fields(uint32_t d) {
+    uint32_t out = 0;
+    for (int v = 0; v < 4; ++v)
+        for (int s = 0; s < 4; ++s) out |= ((d >> (8 * s + 2 * v)) & 3u) << (8 * v + 2 * s);
+    return out;
+}
+
+// One thread per 16-byte lane chunk of the code part.
+__global__ void prepare_tile_codes_kernel(const uint8_t* __restrict__ raw, int64_t stride, int64_t n, int groups,
+                                          int g2, int64_t chunks, uint4* __restrict__ out) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= chunks) return;
+    const int lane = (int)(c & 63);
+    const int64_t tb = c >> 6;
+    const int b = (int)(tb % g2);
+    const int64_t t = tb / g2;
+    const int64_t row = t * kTileRows + (lane & 15);
+    const int kb = lane >> 4;
+    uint32_t w[4];
+    for (int u = 0; u < 4; ++u) {
+        const int g = 2 * b + (u >> 1);
+        if (row < n && g < groups) {
+            const uint8_t* src = raw + row * stride + (int64_t)g * 34 + 2 + 16 * (u & 1) + 4 * kb;
+            const uint32_t d = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16) |
+                               ((uint32_t)src[3] << 24);
+            w[u] = transpose_fields(d);
+        } else {
+            w[u] = 0x55555555u;
+        }
+    }
+    out[c] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// One thread per (tile, 8-group block, row): eight fp16 scales.
+__global__ void prepare_tile_scales_kernel(const uint8_t* __restrict__ raw, int64_t stride, int64_t n, int groups,
+                                           int s8, int64_t chunks, uint4* __restrict__ out) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= chunks) return;
+    const int j = (int)(c & 15);
+    const int64_t tsb = c >> 4;
+    const int sb = (int)(tsb % s8);
+    const int64_t row = (tsb / s8) * kTileRows + j;
+    uint32_t h[8];
+    for (int e = 0; e < 8; ++e) {
+        const int g = 8 * sb + e;
+        h[e] = 0;
+        if (row < n && g < groups) {
+            const uint8_t* src = raw + row * stride + (int64_t)g * 34;
+            h[e] = (uint32_t)src[0] | ((uint32_t)src[1] << 8);
+        }
+    }
+    out[c] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+__device__ __forceinline__ void keep_order() { __builtin_amdgcn_sched_barrier(0); }
+
+// Per-wave LDS: MC staged columns of CPW groups and a spare column (each
+// padded by 64 bytes: the columns of one A read fall in distinct banks), then
+// 8 x 8 floats of xs and 8 x 8 ints of -sum(q) (group class x column).
+__host__ __device__ constexpr int tiles_col_pitch(int cpw) { return 128 * cpw + 64; }
+__host__ __device__ constexpr int tiles_region_bytes(int mc, int cpw) { return (mc + 1) * tiles_col_pitch(cpw) + 512; }
+
+__device__ __forceinline__ float half_of(const uint4& v, int c) {
+    const uint32_t w = word_of(v, c >> 1);
+    return __half2float(__ushort_as_half((unsigned short)((c & 1) ? (w >> 16) : (w & 0xFFFFu))));
+}
+
+template <int MC, int CPW>
+__global__ __launch_bounds__(1024) void small_m_tiles_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ xs, const uint8_t* __restrict__ tiles,
+    float* __restrict__ y, int n, int k, int groups, int g2, int s8, int nseg, int per_wave, int mtotal,
+    int64_t scale_off) {
+#pragma clang fp contract(off)
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int WPS = 8 / CPW;            // waves per k slice (each takes CPW group classes)
+    constexpr int CHUNKS = 8 * CPW;         // 16-byte chunks of one column's activations per segment
+    constexpr int COLS_PER_LOAD = 64 / CHUNKS;
+    constexpr int QLOADS = (MC + COLS_PER_LOAD - 1) / COLS_PER_LOAD;
+    constexpr int PITCH = tiles_col_pitch(CPW);
+    const int nwaves = blockDim.x >> 6;
+    const int nslices = nwaves / WPS;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slice = wave / WPS;
+    const int c_lo = (wave - slice * WPS) * CPW;  // first group class of this wave
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15;   // B column (row of the tile) and A row (activation column)
+    const int kb = lane >> 4;  // k block of the 64-wide MFMA step
+    const int tile = blockIdx.x;
+    const int m0 = blockIdx.y * MC;
+    const int mcount = min(MC, mtotal - m0);
+    const int seg_begin = slice * per_wave;
+    const int seg_end = min(seg_begin + per_wave, nseg);
+
+    // Private region: MC staged columns (CPW groups each) and one column that
+    // takes the stores of lanes past the last column, then per class c of the
+    // wave 8 floats xs[c][m] and 8 ints -sum(q)[c][m].
+    unsigned char* region = smem + (size_t)wave * tiles_region_bytes(MC, CPW);
+    float* red = reinterpret_cast<float*>(smem + (size_t)nwaves * tiles_region_bytes(MC, CPW));
+    float* xs_lds = reinterpret_cast<float*>(region + (MC + 1) * PITCH);
+    int* nsq_lds = reinterpret_cast<int*>(region + (MC + 1) * PITCH + 256);
+    // A row i reads column i mod mcount: rows >= mcount repeat real columns,
+    // so one read touches at most 4 x 16 distinct banks, and the D rows they
+    // produce are never used.
+    const unsigned char* a_base = region + (j % mcount) * PITCH + 16 * kb;
+    nsq_lds[lane] = 0;
+
+    const auto code_rs = make_rsrc(tiles + (size_t)tile * g2 * kCodeBlock, (uint32_t)(g2 * kCodeBlock));
+    const auto scale_rs = make_rsrc(tiles + scale_off + (size_t)tile * s8 * kScaleBlock, (uint32_t)(s8 * kScaleBlock));
+    const auto q_rs = make_rsrc(q + (size_t)m0 * k, (uint32_t)(mcount * k));
+    const auto xs_rs = make_rsrc(xs + (size_t)m0 * groups, (uint32_t)(mcount * groups * 4));
+    // Staging roles: chunk ch of column (load t) * COLS_PER_LOAD + sub.
+    const int ch = lane % CHUNKS;
+    const int sub = lane / CHUNKS;
+
+    float acc[CPW][MC];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int r = 0; r < MC; ++r) acc[c][r] = 0.0f;
+
+    for (int s = seg_begin; s < seg_end; ++s) {
+        // 1. This segment's activation chunks for the wave's classes and xs
+        //    (lane l: column l >> 3, group l & 7), then the code blocks and
+        //    weight scales, all in flight together.  Groups past the end read
+        //    zeros.
+        uint4 qv[QLOADS];
+        const uint32_t qoff = (uint32_t)(s * 1024 + 128 * c_lo + 16 * ch);
+#pragma unroll
+        for (int t = 0; t < QLOADS; ++t) {
+            const int m = t * COLS_PER_LOAD + sub;
+            qv[t] = buf_load16(q_rs, (m < mcount && (int)qoff < k) ? (uint32_t)(m * k) + qoff : kBufferOOB);
+        }
+        const int xm = lane >> 3, xc = lane & 7;
+        const uint32_t xsw = buf_load4(xs_rs, (xm < mcount && 8 * s + xc < groups)
+                                                  ? (uint32_t)((xm * groups + 8 * s + xc) * 4) : kBufferOOB);
+        const uint4 wsv = buf_load16(scale_rs, (uint32_t)((s * kTileRows + j) * 16));
+        keep_order();
+        // Code blocks last and in use order: loads complete in order, so the
+        // first group pair can start while the later blocks are in flight.
+        uint4 cw[CPW / 2];
+#pragma unroll
+        for (int b = 0; b < CPW / 2; ++b) {
+            const int blk = 4 * s + c_lo / 2 + b;
+            cw[b] = buf_load16<kAuxNonTemporal>(code_rs, blk < g2 ? (uint32_t)((blk * 64 + lane) * 16) : kBufferOOB);
+        }
+        keep_order();
+
+        // 2. Stage the activations, xs and each group's -sum(q) (dot4 against
+        //    ones over the lane's 16 bytes, then the 8 lanes of the group).
+        //    Lanes past the last column write their (zero) chunk to the spare column.
+        xs_lds[xc * 8 + xm] = __uint_as_float(xsw);
+#pragma unroll
+        for (int t = 0; t < QLOADS; ++t) {
+            const int m = t * COLS_PER_LOAD + sub;
+            const uint4 v = qv[t];
+            *reinterpret_cast<uint4*>(region + (m < MC ? m : MC) * PITCH + 16 * ch) = v;
+            int sq = dot4(v.x, 0x01010101u, 0);
+            sq = dot4(v.y, 0x01010101u, sq);
+            sq = dot4(v.z, 0x01010101u, sq);
+            sq = dot4(v.w, 0x01010101u, sq);
+            sq = sum8_i(sq);
+            if ((lane & 7) == 0 && m < MC) nsq_lds[(c_lo + (ch >> 3)) * 8 + m] = -sq;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // 3. Group dots on the matrix cores, two groups at a time: D starts
+        //    at -sum(q) of its column (the code offset), then adds the two
+        //    64-wide halves of codes 0..3 times q.
+#pragma unroll
+        for (int c0 = 0; c0 < CPW; c0 += 2) {
+            v4i D[2];
+            v4i A[2][2];
+            v4i B[2][2];
+            float4 xsg[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int c = c0 + p;  // class c_lo + c
+                const uint4 a0 = *reinterpret_cast<const uint4*>(a_base + 128 * c);
+                const uint4 a1 = *reinterpret_cast<const uint4*>(a_base + 128 * c + 64);
+                A[p][0] = v4i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
+                A[p][1] = v4i{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                const int4 nsq = *reinterpret_cast<const int4*>(nsq_lds + (c_lo + c) * 8);
+                D[p] = v4i{nsq.x, nsq.y, nsq.z, nsq.w};
+                xsg[p] = *reinterpret_cast<const float4*>(xs_lds + (c_lo + c) * 8);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t d = word_of(cw[c >> 1], 2 * (c & 1) + h);
+                    B[p][h] = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
+                                  (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) D[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[p][h], B[p][h], D[p], 0, 0, 0);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int c = c0 + p;
+                const float wsf = half_of(wsv, c_lo + c);
+                const float xv[4] = {xsg[p].x, xsg[p].y, xsg[p].z, xsg[p].w};
+#pragma unroll
+                for (int r = 0; r < MC; ++r) acc[c][r] = __builtin_fmaf((float)D[p][r] * xv[r], wsf, acc[c][r]);
+            }
+        }
+        // The next segment rewrites the region: every lane's reads of this one
+        // are done (LDS operations of one wave complete in order).
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // 4. Class sums through LDS: ((A0+A4)+(A1+A5))+((A2+A6)+(A3+A7)) per
+    //    slice, then the slices in index order.  D row 4*kb + r is column
+    //    4*kb + r, so the columns live in the lanes with kb = 0.
+    if (kb == 0) {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int r = 0; r < MC; ++r) red[((slice * 8 + c_lo + c) * MC + r) * kTileRows + j] = acc[c][r];
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < MC * kTileRows; o += blockDim.x) {
+        const int r = o / kTileRows;
+        const int jj = o - r * kTileRows;
+        float sum = 0.0f;
+        for (int w = 0; w < nslices; ++w) {
+            const float* a = red + ((size_t)w * 8 * MC + r) * kTileRows + jj;
+            constexpr int C = MC * kTileRows;  // stride between classes
+            const float t = ((a[0] + a[4 * C]) + (a[1 * C] + a[5 * C])) + ((a[2 * C] + a[6 * C]) + (a[3 * C] + a[7 * C]));
+            sum = w == 0 ? t : sum + t;
+        }
+        const int rr = tile * kTileRows + jj;
+        if (r < mcount && rr < n) y[(size_t)(m0 + r) * n + rr] = sum;
+    }
+}
+
+template <int MC, int CPW>
+hipError_t launch_tiles_one(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n, int64_t k,
+                            float* y, int slices, int nseg, int per_wave, int chunks, hipStream_t stream) {
+    const TileGeometry t = geometry(n, k);
+    const int waves = slices * (8 / CPW);
+    const size_t lds = (size_t)waves * tiles_region_bytes(MC, CPW) + (size_t)slices * 8 * MC * kTileRows * 4;
+    const dim3 grid((unsigned)t.tiles, (unsigned)chunks);
+    clear_stale_error();
+    hipLaunchKernelGGL((small_m_tiles_kernel<MC, CPW>), grid, dim3(64 * waves), lds, stream, q, xs, tiles, y, (int)n,
+                       (int)k, (int)(k / 128), (int)t.g2, (int)t.s8, nseg, per_wave, (int)m, t.code_bytes);
+    return hipGetLastError();
+}
+
+template <int CPW>
+hipError_t launch_tiles_mc(int mc, const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                           int64_t k, float* y, int slices, int nseg, int per_wave, int chunks, hipStream_t stream) {
+    switch (mc) {
+        case 1: return launch_tiles_one<1, CPW>(q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
+        case 2: return launch_tiles_one<2, CPW>(q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
+        case 3: return launch_tiles_one<3, CPW>(q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
+        case 4: return launch_tiles_one<4, CPW>(q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int64_t tiles_bytes(int64_t n, int64_t k) { return geometry(n, k).total; }
+
+hipError_t launch_prepare_tiles(const uint8_t* raw, int64_t stride, int64_t n, int64_t k, uint8_t* tiles,
+                                hipStream_t stream) {
+    const TileGeometry t = geometry(n, k);
+    const int groups = (int)(k / 128);
+    const int64_t code_chunks = t.tiles * t.g2 * 64;
+    const int64_t scale_chunks = t.tiles * t.s8 * kTileRows;
+    clear_stale_error();
+    hipLaunchKernelGGL(prepare_tile_codes_kernel, dim3((unsigned)((code_chunks + 255) / 256)), dim3(256), 0, stream,
+                       raw, stride, n, groups, (int)t.g2, code_chunks, reinterpret_cast<uint4*>(tiles));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prepare_tile_scales_kernel, dim3((unsigned)((scale_chunks + 255) / 256)), dim3(256), 0, stream,
+                       raw, stride, n, groups, (int)t.s8, scale_chunks,
+                       reinterpret_cast<uint4*>(tiles + t.code_bytes));
+    return hipGetLastError();
+}
+
+// The k split is the one every small-m engine uses for (n, k) and max_waves,
+// so the outputs are bit-identical to pq2_matmul_small_m's.  split = waves
+// per k slice (1, 2 or 4; each takes 8/split of the segment's group
+// classes), at most 16 waves per workgroup.
+static int tiles_slices(int64_t k, int max_waves, int* nseg, int* per_wave) {
+    const int groups = (int)(k / 128);
+    *nseg = (groups + 7) / 8;
+    *per_wave = (*nseg + max_waves - 1) / max_waves;
+    return (*nseg + *per_wave - 1) / *per_wave;
+}
+
+int tiles_default_split(int64_t k, int max_waves) {
+    int nseg, per_wave;
+    const int slices = tiles_slices(k, max_waves, &nseg, &per_wave);
+    return slices * 2 <= 16 ? 2 : 1;
+}
+
+bool tiles_supported(int64_t k, int max_waves, int split) {
+    if (max_waves < 1 || max_waves > 8 || (split != 1 && split != 2 && split != 4)) return false;
+    int nseg, per_wave;
+    return tiles_slices(k, max_waves, &nseg, &per_wave) * split <= 16;
+}
+
+hipError_t launch_small_m_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                int64_t k, float* y, int max_waves, int split, hipStream_t stream) {
+    if (!tiles_supported(k, max_waves, split)) return hipErrorInvalidValue;
+    int nseg, per_wave;
+    const int slices = tiles_slices(k, max_waves, &nseg, &per_wave);
+    int mc = (int)(m < kTilesMaxColumns ? m : kTilesMaxColumns);
+    const int chunks = (int)((m + mc - 1) / mc);
+    mc = (int)((m + chunks - 1) / chunks);
+    switch (split) {
+        case 1: return launch_tiles_mc<8>(mc, q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
+        case 2: return launch_tiles_mc<4>(mc, q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
+        default: return launch_tiles_mc<2>(mc, q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
+    }
+}
+
+}  // namespace pq2

@@ -240,6 +240,62 @@ int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_strid
                                    int64_t m, int64_t n, int64_t k, float* y, int rows, int max_waves,
                                    int engine, void* stream);
 
+/* ---- Tile-major weights for the decode GEMV (page "Kernel experiments:
+ * recorded evidence", section H, Tests 24 and 25: storing the bytes one
+ * warp loads next to each other, same values at other addresses).
+ *
+ * Tile layout: T = ceil(n/16) tiles of 16 rows, G = k/128 groups,
+ * G2 = ceil(G/2), S8 = ceil(G/8).  ONE allocation of pq2_tiles_bytes(n, k)
+ * = T*(G2*1024 + S8*256) bytes:
+ *  - code part: block (t, b) of 1024 bytes at (t*G2 + b)*1024; bytes
+ *    16*l .. 16*l+15 with l = j + 16*kb (j = 0..15, kb = 0..3) hold four
+ *    dwords u = 0..3, dword u = the 16 weights k0..k0+15 of row 16t+j with
+ *    k0 = 128*(2b + u/2) + 64*(u%2) + 16*kb; bits 2s..2s+1 of its byte v are
+ *    the code of weight k0 + 4s + v;
+ *  - scale part at byte T*G2*1024: block (t, sb) of 256 bytes at
+ *    T*G2*1024 + (t*S8 + sb)*256; its bytes 16*j .. 16*j+15 are the eight
+ *    fp16 scales of row 16t+j, groups 8*sb .. 8*sb+7;
+ *  - padding rows (>= n) and groups (>= G) hold code 1 (weight 0), scale 0. */
+
+/* Bytes of the tile layout for an n x k weight matrix; -1 if n < 1,
+ * n > 2^30, k < 128, k % 128 or k > PQ2_MAX_K. */
+int64_t pq2_tiles_bytes(int64_t n, int64_t k);
+
+/* Raw PQ2 rows -> tile layout.  One-time weight preparation, outside any
+ * timed loop.
+ *   raw     device, n rows of raw_row_stride_bytes >= (k/128)*34; any alignment.
+ *   tiles   device, pq2_tiles_bytes(n, k) bytes, 16-byte aligned, fully
+ *           written (padding included); must not overlap raw.
+ * Errors: EINVAL (null, overlap), ESHAPE (k%128, n<1, stride too small),
+ *         EALIGN, ELAUNCH, EDEVICE. */
+int pq2_prepare_tiles(const void* raw, int64_t raw_row_stride_bytes, int64_t n, int64_t k, void* tiles,
+                      void* stream);
+
+/* pq2_matmul_small_m from the tile layout: the same definition, limits and
+ * summation order, hence the same bits as pq2_matmul_small_m for the same
+ * weights (page "Kernel experiments", Test 25: the tile-major projection
+ * matched the row-major one bit for bit).  Each group's exact integer dot
+ * comes from the INT8 matrix cores.
+ *   q       device int8 [m][k], 16-byte aligned.   xs  device float [m][k/128], 4-byte aligned.
+ *   tiles   device tile layout of the weights, 16-byte aligned.
+ *   y       device float [m][n], 4-byte aligned; fully overwritten; must
+ *           not overlap any input.
+ * Errors: EINVAL (null, overlap), ESHAPE (m outside 1..16, n<1, k<128,
+ *         k%128, k > PQ2_MAX_K), EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_small_m_tiles(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                             int64_t k, float* y, void* stream);
+
+/* Tuning hook for pq2_matmul_small_m_tiles (benchmarks and tests only):
+ * max_waves in 1..8 fixes the k split as for pq2_matmul_small_m_tuned;
+ * split in {1, 2, 4} is the number of waves that share one k slice (each
+ * takes 8/split of its group classes), with at most 16 waves per workgroup.
+ * 0 for either picks the library's default.  The bits equal
+ * pq2_matmul_small_m_tuned's at the same max_waves, whatever the split.
+ * Errors as pq2_matmul_small_m_tiles, plus EINVAL for an unsupported
+ * setting. */
+int pq2_matmul_small_m_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                                   int64_t k, float* y, int max_waves, int split, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

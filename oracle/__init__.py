@@ -55,6 +55,10 @@ def _load():
     lib.oracle_decode_byte.restype = None
     lib.oracle_prepare_planes.argtypes = [p, i64, i64, i64, p]
     lib.oracle_prepare_planes.restype = i32
+    lib.oracle_tiles_bytes.argtypes = [i64, i64]
+    lib.oracle_tiles_bytes.restype = i64
+    lib.oracle_prepare_tiles.argtypes = [p, i64, i64, i64, p]
+    lib.oracle_prepare_tiles.restype = i32
     lib.oracle_quantize_act_i8.argtypes = [p, i32, i64, i64, i64, p, p]
     lib.oracle_quantize_act_i8.restype = i32
     lib.oracle_matmul_raw.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
@@ -93,6 +97,21 @@ def prepare_planes(raw: np.ndarray, n: int, k: int) -> np.ndarray:
     if rc:
         raise ValueError("oracle_prepare_planes: bad shape")
     return planes
+
+
+def tiles_bytes(n: int, k: int) -> int:
+    return int(_load().oracle_tiles_bytes(n, k))
+
+
+def prepare_tiles(raw: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Raw [n][row_stride] uint8 blocks -> the tile layout of the decode GEMV."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    assert raw.ndim == 2 and raw.shape[0] == n
+    out = np.empty(tiles_bytes(n, k), dtype=np.uint8)
+    rc = _load().oracle_prepare_tiles(_ptr(raw), raw.shape[1], n, k, _ptr(out))
+    if rc:
+        raise ValueError("oracle_prepare_tiles: bad shape")
+    return out
 
 
 def quantize_act_i8(x_bits: np.ndarray, dtype: str = "bf16", k: int | None = None):

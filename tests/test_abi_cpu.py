@@ -30,12 +30,12 @@ def _gpu_visible():
 
 def _declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pq2_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(pq2_\w+)\s*\(", text, re.M)))
 
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 16
+    assert len(names) == 20
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -78,7 +78,8 @@ def test_quantize_validation():
     assert f(A, 0, 128, 2, 128, A + 16, C, None) == EINVAL  # q overlaps x
 
 
-@pytest.mark.parametrize("name", ["pq2_matmul_small_m", "pq2_matmul_prefill", "pq2_matmul_prefill_planes"])
+@pytest.mark.parametrize("name", ["pq2_matmul_small_m", "pq2_matmul_prefill", "pq2_matmul_prefill_planes",
+                                  "pq2_matmul_small_m_tiles"])
 def test_matmul_validation(name):
     f = getattr(pq2.lib, name)
     assert f(None, B, C, 1, 8, 128, D, None) == EINVAL
@@ -117,6 +118,45 @@ def test_small_m_valid_settings_reach_the_device_check():
     t = pq2.lib.pq2_matmul_small_m_tuned
     for rows, engine in ((0, 0), (1, 1), (2, 1), (1, 2), (1, 3), (2, 3), (0, 3), (1, 4), (0, 4)):
         assert t(A, B, C, 4, 8, 128, D, rows, 0, engine, None) == EDEVICE, (rows, engine)
+
+
+def test_tiles_bytes():
+    """T*(G2*1024 + S8*256) with T = ceil(n/16), G2 = ceil(G/2), S8 = ceil(G/8)."""
+    f = pq2.pq2_tiles_bytes
+    assert f(10240, 5120) == 10240 * 40 * 34           # no padding: equal to the prepared planes
+    assert f(5120, 17408) == 5120 * 136 * 34
+    assert f(1, 128) == 1024 + 256                     # one tile, one (padded) group pair and scale block
+    assert f(17, 384) == 2 * (2 * 1024 + 256)
+    for n, k in ((0, 128), (1, 100), (1, 0), (1, 1 << 17), ((1 << 30) + 1, 128)):
+        assert pq2.lib.pq2_tiles_bytes(n, k) == -1, (n, k)
+
+
+def test_prepare_tiles_validation():
+    f = pq2.lib.pq2_prepare_tiles
+    assert f(None, 34, 4, 128, B, None) == EINVAL
+    assert f(A, 34, 4, 128, None, None) == EINVAL
+    assert f(A, 34, 0, 128, B, None) == ESHAPE
+    assert f(A, 34, 4, 100, B, None) == ESHAPE
+    assert f(A, 33, 4, 128, B, None) == ESHAPE          # row stride below 34 bytes per block
+    assert f(A, 34, 4, 128, B + 8, None) == EALIGN     # tiles not 16-byte aligned
+    assert f(A, 34, 4, 128, A + 64, None) == EINVAL    # tiles overlap raw
+    assert f(A, 34, 4, 128, A - 1024, None) == EINVAL  # the 1280-byte tiles end inside raw's 136 bytes
+    if not _gpu_visible():
+        assert f(A, 34, 4, 128, A + 144, None) == EDEVICE  # adjacent, no overlap: valid
+
+
+def test_small_m_tiles_validation():
+    f = pq2.lib.pq2_matmul_small_m_tiles
+    assert f(A, B, C, 17, 8, 128, D, None) == ESHAPE
+    assert f(A, B, C, 1, 8, 128, C + 1024, None) == EINVAL  # y overlaps the tiles (1280 bytes)
+    t = pq2.lib.pq2_matmul_small_m_tiles_tuned
+    assert t(A, B, C, 1, 8, 128, D, 9, 0, None) == EINVAL     # waves
+    assert t(A, B, C, 1, 8, 128, D, -1, 0, None) == EINVAL
+    assert t(A, B, C, 1, 8, 128, D, 0, 3, None) == EINVAL     # split
+    assert t(A, B, C, 1, 8, 65536, D, 8, 4, None) == EINVAL   # 8 slices x 4 waves > 16
+    if not _gpu_visible():
+        for waves, split in ((0, 0), (1, 1), (8, 2), (1, 4), (5, 0)):
+            assert t(A, B, C, 4, 8, 5120, D, waves, split, None) == EDEVICE, (waves, split)
 
 
 def test_prefill_tile_validation():

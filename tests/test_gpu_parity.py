@@ -299,6 +299,97 @@ def test_small_m_workloads_exact_properties(name):
     assert np.array_equal(y2x, 2.0 * y1), "doubled weight scales must double outputs exactly"
 
 
+# ------------------------------------------------------------------ small m: tile layout
+def gpu_tiles(raw_np, n, k):
+    pq2 = _pq2()
+    raw = torch.from_numpy(np.ascontiguousarray(raw_np)).to(DEV)
+    tiles = torch.full((pq2.pq2_tiles_bytes(n, k),), 0xA5, dtype=torch.uint8, device=DEV)  # poisoned
+    pq2.pq2_prepare_tiles(raw, n, k, tiles)
+    return tiles
+
+
+@pytest.mark.parametrize("n,k,pad", [(1, 128, 0), (37, 384, 3), (33, 640, 0), (256, 5120, 0), (19, 17408, 6)])
+def test_prepare_tiles_byte_exact(n, k, pad):
+    announce(f"prepare tiles n={n} k={k} pad={pad}")
+    raw = workloads.make_raw_weights(n, k, seed=82 + n, codes="ternary+3", row_pad=pad)
+    tiles = gpu_tiles(raw, n, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(tiles.cpu().numpy(), oracle.prepare_tiles(raw, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
+def test_small_m_tiles_full(m, n, k):
+    """The tile-layout engine against the oracle, and bit-identical to
+    pq2_matmul_small_m on the row-major planes (same k split)."""
+    pq2 = _pq2()
+    announce(f"small_m tiles m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=90 + m + n, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 91 + k, "normal+outliers")
+    q, xs, qo, xso = quantise_both(x)
+    y = gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, gpu_tiles(raw, n, k), n)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    assert_within(y, y_ref, bound, f"tiles m={m} n={n} k={k}")
+    y1 = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, gpu_planes(raw, n, k), n)
+    assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), "tile layout and planes differ"
+
+
+@pytest.mark.parametrize("m", [1, 3, 4, 6])
+def test_small_m_tiles_waves(m):
+    """Every k split gives the bits of the planes path at the same split."""
+    pq2 = _pq2()
+    n, k = 200, 5248
+    announce(f"small_m tiles waves m={m}")
+    raw = workloads.make_raw_weights(n, k, seed=7, codes="ternary+3")
+    x = workloads.make_activations(m, k, 8, "laplace")
+    q, xs, qo, xso = quantise_both(x)
+    tiles, planes = gpu_tiles(raw, n, k), gpu_planes(raw, n, k)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    for waves in (1, 2, 3, 5, 8):
+        y1 = gpu_matmul(pq2.pq2_matmul_small_m_tuned, q, xs, planes, n, max_waves=waves)
+        nseg = -(-(k // 128) // 8)
+        slices = -(-nseg // -(-nseg // waves))
+        for split in (1, 2, 4):
+            if slices * split > 16:  # more than 16 waves per workgroup: not offered
+                continue
+            y = gpu_matmul(pq2.pq2_matmul_small_m_tiles_tuned, q, xs, tiles, n, max_waves=waves, split=split)
+            assert_within(y, y_ref, bound, f"tiles waves={waves} split={split}")
+            assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), \
+                f"waves={waves} split={split}: tiles differ from planes"
+
+
+def test_small_m_tiles_zero_activations_and_tiny():
+    pq2 = _pq2()
+    announce("small_m tiles zero activations / tiny workload")
+    n, k = 100, 1024
+    raw = workloads.make_raw_weights(n, k, seed=5)
+    q, xs, _, _ = quantise_both(torch.zeros((3, k), dtype=torch.bfloat16))
+    y = gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, gpu_tiles(raw, n, k), n)
+    assert np.all(y == 0.0)
+    w, raw, x = workload_case("tiny")
+    q, xs, qo, xso = quantise_both(x)
+    y = gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, gpu_tiles(raw, w.n, w.k), w.n)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, w.n, w.k)
+    assert_within(y, y_ref, bound, "tiles tiny")
+
+
+@pytest.mark.parametrize("name", ["qkv", "up", "down"])
+def test_small_m_tiles_workloads(name):
+    """Full workload sizes: sampled outputs against the oracle, and every
+    output bit-identical to the planes path."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    tiles, planes = gpu_tiles(raw, w.n, w.k), gpu_planes(raw, w.n, w.k)
+    for m in w.ms:
+        announce(f"small_m tiles workload {name} m={m}")
+        q, xs, qo, xso = quantise_both(x[:m].contiguous())
+        y = gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, tiles, w.n)
+        mi, ni = _sample_indices(m, w.n, 400, seed=m)
+        y_ref, bound = oracle.matmul_raw_sample(qo, xso, raw, w.n, w.k, mi, ni)
+        assert_within(y[mi, ni], y_ref, bound, f"tiles {name} m={m}")
+        y1 = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, w.n)
+        assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), f"{name} m={m}: tiles differ from planes"
+
+
 # ------------------------------------------------------------------ prefill
 PREFILL_SHAPES = [(1, 64, 128), (5, 200, 640), (128, 128, 1024), (130, 257, 384), (300, 96, 5120),
                   (257, 513, 2048)]
