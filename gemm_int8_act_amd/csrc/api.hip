@@ -141,7 +141,7 @@ int pq2_matmul_small_m_tiles_tuned(const int8_t* q, const float* xs, const void*
     if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, PQ2_MAX_SMALL_M, true)) return rc;
     if (max_waves < 0 || max_waves > 8) return PQ2_EINVAL;
     const int waves = max_waves ? max_waves : pq2::default_small_m_config(pq2::kSrcNatural, m, n, k).max_waves;
-    if (!split) split = pq2::tiles_default_split(k, waves);
+    if (!split) split = pq2::tiles_default_split(m, k, waves);
     if (!pq2::tiles_supported(k, waves, split)) return PQ2_EINVAL;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m_tiles(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, y, waves,

@@ -73,7 +73,7 @@ hipError_t launch_small_m_wg(int src, const SmallMLaunch& a, int max_waves, int 
 int64_t tiles_bytes(int64_t n, int64_t k);
 hipError_t launch_prepare_tiles(const uint8_t* raw, int64_t stride, int64_t n, int64_t k, uint8_t* tiles,
                                 hipStream_t stream);
-int tiles_default_split(int64_t k, int max_waves);
+int tiles_default_split(int64_t m, int64_t k, int max_waves);
 bool tiles_supported(int64_t k, int max_waves, int split);
 hipError_t launch_small_m_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int max_waves, int split, hipStream_t stream);

@@ -10,23 +10,24 @@
 // can cover at most 64 bytes of a row.  Here every load instruction of a
 // wave reads one contiguous kilobyte.
 //
-// Layout (all sizes in bytes; T = ceil(n/16) tiles of 16 rows, G = k/128
-// groups, G2 = ceil(G/2), S8 = ceil(G/8)):
-//   code part   T x G2 blocks of 1024, block (t, b) at (t*G2 + b)*1024.
-//               Lane l = j + 16*kb (j = row within the tile, kb = 0..3)
-//               owns bytes 16*l .. 16*l+15 of the block: dword u = 0..3
-//               holds the 16 weights k0 .. k0+15 of row 16t+j, with
-//               k0 = 128*(2b + u/2) + 64*(u%2) + 16*kb, and bits 2s..2s+1
-//               of its byte v hold the code of weight k0 + 4s + v.  (The
-//               prepared planes keep weight 4v + s there: inside each dword
-//               the 2-bit fields are 4x4-transposed, so bit plane s of a
-//               dword is the natural-order activation dword s.)
-//   scale part  at T*G2*1024: T x S8 blocks of 256, block (t, sb) at
-//               T*G2*1024 + (t*S8 + sb)*256, row j at +16*j: the eight fp16
-//               scales of groups 8*sb .. 8*sb+7.
+// Layout (sizes in bytes; T = ceil(n/16) tiles of 16 rows, G = k/128
+// groups, S8 = ceil(G/8) segments of 8 groups): T x S8 segment units of
+// 4352 bytes, unit (t, sb) at (t*S8 + sb)*4352, each
+//   four code blocks b = 0..3 of 1024 (groups 8sb + 2b and 8sb + 2b + 1):
+//               lane l = j + 16*kb (j = row within the tile, kb = 0..3) owns
+//               bytes 1024*b + 16*l .. +15; its dword u = 0..3 holds the 16
+//               weights k0 .. k0+15 of row 16t+j, k0 = 128*(8sb + 2b + u/2)
+//               + 64*(u%2) + 16*kb, and bits 2s..2s+1 of its byte v hold the
+//               code of weight k0 + 4s + v.  (The prepared planes keep weight
+//               4v + s there: inside each dword the 2-bit fields are
+//               4x4-transposed, so bit plane s of a dword is the
+//               natural-order activation dword s.)
+//   then 256 bytes of scales: row j at 4096 + 16*j, the eight fp16 scales of
+//               groups 8sb .. 8sb+7, next to the codes they scale (the wave
+//               reads them from the same DRAM pages).
 //   Rows >= n and groups >= G are padding: code 1 (weight 0), scale 0.
-// At even G with G % 8 == 0 (every shape measured here) the size equals the
-// prepared planes', n*k/128*34 when n % 16 == 0.
+// When G % 8 == 0 (every shape measured here) and n % 16 == 0 the size
+// equals the prepared planes', n*k/128*34.
 //
 // Engine (same summation order as small_m.hip, so the same bits):
 //  * A workgroup owns one 16-row tile; its waves split k into consecutive
@@ -53,21 +54,18 @@ namespace {
 
 constexpr int kTileRows = 16;
 constexpr int kCodeBlock = 1024;   // one (tile, group pair) code block
-constexpr int kScaleBlock = 256;   // one (tile, 8 groups) scale block
+constexpr int kSegUnit = 4 * kCodeBlock + 256;  // one (tile, 8 groups) unit: codes then scales
 constexpr int kTilesMaxColumns = 4;
 
 struct TileGeometry {
-    int64_t tiles, g2, s8, code_bytes, total;
+    int64_t tiles, s8, total;
 };
 
 TileGeometry geometry(int64_t n, int64_t k) {
     TileGeometry t;
-    const int64_t groups = k / 128;
     t.tiles = (n + kTileRows - 1) / kTileRows;
-    t.g2 = (groups + 1) / 2;
-    t.s8 = (groups + 7) / 8;
-    t.code_bytes = t.tiles * t.g2 * kCodeBlock;
-    t.total = t.code_bytes + t.tiles * t.s8 * kScaleBlock;
+    t.s8 = (k / 128 + 7) / 8;
+    t.total = t.tiles * t.s8 * kSegUnit;
     return t;
 }
 
@@ -79,20 +77,20 @@ __device__ uint32_t transpose_fields(uint32_t d) {
     return out;
 }
 
-// One thread per 16-byte lane chunk of the code part.
+// One thread per 16-byte lane chunk of a code block: chunk c = (unit, b, lane).
 __global__ void prepare_tile_codes_kernel(const uint8_t* __restrict__ raw, int64_t stride, int64_t n, int groups,
-                                          int g2, int64_t chunks, uint4* __restrict__ out) {
+                                          int s8, int64_t chunks, uint8_t* __restrict__ out) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= chunks) return;
     const int lane = (int)(c & 63);
-    const int64_t tb = c >> 6;
-    const int b = (int)(tb % g2);
-    const int64_t t = tb / g2;
-    const int64_t row = t * kTileRows + (lane & 15);
+    const int b = (int)((c >> 6) & 3);
+    const int64_t unit = c >> 8;  // t * S8 + sb
+    const int sb = (int)(unit % s8);
+    const int64_t row = (unit / s8) * kTileRows + (lane & 15);
     const int kb = lane >> 4;
     uint32_t w[4];
     for (int u = 0; u < 4; ++u) {
-        const int g = 2 * b + (u >> 1);
+        const int g = 8 * sb + 2 * b + (u >> 1);
         if (row < n && g < groups) {
             const uint8_t* src = raw + row * stride + (int64_t)g * 34 + 2 + 16 * (u & 1) + 4 * kb;
             const uint32_t d = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16) |
@@ -102,18 +100,18 @@ __global__ void prepare_tile_codes_kernel(const uint8_t* __restrict__ raw, int64
             w[u] = 0x55555555u;
         }
     }
-    out[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(out + unit * kSegUnit + b * kCodeBlock + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// One thread per (tile, 8-group block, row): eight fp16 scales.
+// One thread per (unit, row): the eight fp16 scales after the unit's codes.
 __global__ void prepare_tile_scales_kernel(const uint8_t* __restrict__ raw, int64_t stride, int64_t n, int groups,
-                                           int s8, int64_t chunks, uint4* __restrict__ out) {
+                                           int s8, int64_t chunks, uint8_t* __restrict__ out) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= chunks) return;
     const int j = (int)(c & 15);
-    const int64_t tsb = c >> 4;
-    const int sb = (int)(tsb % s8);
-    const int64_t row = (tsb / s8) * kTileRows + j;
+    const int64_t unit = c >> 4;
+    const int sb = (int)(unit % s8);
+    const int64_t row = (unit / s8) * kTileRows + j;
     uint32_t h[8];
     for (int e = 0; e < 8; ++e) {
         const int g = 8 * sb + e;
@@ -123,7 +121,8 @@ __global__ void prepare_tile_scales_kernel(const uint8_t* __restrict__ raw, int6
             h[e] = (uint32_t)src[0] | ((uint32_t)src[1] << 8);
         }
     }
-    out[c] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    *reinterpret_cast<uint4*>(out + unit * kSegUnit + 4 * kCodeBlock + 16 * j) =
+        make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
 __device__ __forceinline__ void keep_order() { __builtin_amdgcn_sched_barrier(0); }
@@ -140,10 +139,9 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
 }
 
 template <int MC, int CPW>
-__global__ __launch_bounds__(1024) void small_m_tiles_kernel(
+__global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const uint8_t* __restrict__ tiles,
-    float* __restrict__ y, int n, int k, int groups, int g2, int s8, int nseg, int per_wave, int mtotal,
-    int64_t scale_off) {
+    float* __restrict__ y, int n, int k, int groups, int s8, int nseg, int per_wave, int mtotal) {
 #pragma clang fp contract(off)
     typedef int v4i __attribute__((ext_vector_type(4)));
     extern __shared__ __align__(16) unsigned char smem[];
@@ -179,8 +177,7 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
     const unsigned char* a_base = region + (j % mcount) * PITCH + 16 * kb;
     nsq_lds[lane] = 0;
 
-    const auto code_rs = make_rsrc(tiles + (size_t)tile * g2 * kCodeBlock, (uint32_t)(g2 * kCodeBlock));
-    const auto scale_rs = make_rsrc(tiles + scale_off + (size_t)tile * s8 * kScaleBlock, (uint32_t)(s8 * kScaleBlock));
+    const auto tile_rs = make_rsrc(tiles + (size_t)tile * s8 * kSegUnit, (uint32_t)(s8 * kSegUnit));
     const auto q_rs = make_rsrc(q + (size_t)m0 * k, (uint32_t)(mcount * k));
     const auto xs_rs = make_rsrc(xs + (size_t)m0 * groups, (uint32_t)(mcount * groups * 4));
     // Staging roles: chunk ch of column (load t) * COLS_PER_LOAD + sub.
@@ -208,16 +205,15 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
         const int xm = lane >> 3, xc = lane & 7;
         const uint32_t xsw = buf_load4(xs_rs, (xm < mcount && 8 * s + xc < groups)
                                                   ? (uint32_t)((xm * groups + 8 * s + xc) * 4) : kBufferOOB);
-        const uint4 wsv = buf_load16(scale_rs, (uint32_t)((s * kTileRows + j) * 16));
+        const uint32_t unit_off = (uint32_t)(s * kSegUnit);
+        const uint4 wsv = buf_load16(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
         keep_order();
         // Code blocks last and in use order: loads complete in order, so the
         // first group pair can start while the later blocks are in flight.
         uint4 cw[CPW / 2];
 #pragma unroll
-        for (int b = 0; b < CPW / 2; ++b) {
-            const int blk = 4 * s + c_lo / 2 + b;
-            cw[b] = buf_load16<kAuxNonTemporal>(code_rs, blk < g2 ? (uint32_t)((blk * 64 + lane) * 16) : kBufferOOB);
-        }
+        for (int b = 0; b < CPW / 2; ++b)
+            cw[b] = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + (c_lo / 2 + b) * kCodeBlock + 16 * lane);
         keep_order();
 
         // 2. Stage the activations, xs and each group's -sum(q) (dot4 against
@@ -284,9 +280,40 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
         __builtin_amdgcn_wave_barrier();
     }
 
-    // 4. Class sums through LDS: ((A0+A4)+(A1+A5))+((A2+A6)+(A3+A7)) per
-    //    slice, then the slices in index order.  D row 4*kb + r is column
-    //    4*kb + r, so the columns live in the lanes with kb = 0.
+    // 4. Class sums ((A0+A4)+(A1+A5))+((A2+A6)+(A3+A7)) per slice, then the
+    //    slices in index order.  D row 4*kb + r is column 4*kb + r, so the
+    //    columns live in the lanes with kb = 0.  A wave that holds all eight
+    //    classes adds them in registers.
+    if constexpr (CPW == 8) {
+        float part[MC];
+#pragma unroll
+        for (int r = 0; r < MC; ++r)
+            part[r] = ((acc[0][r] + acc[4][r]) + (acc[1][r] + acc[5][r])) +
+                      ((acc[2][r] + acc[6][r]) + (acc[3][r] + acc[7][r]));
+        const int row = tile * kTileRows + j;
+        if (nwaves == 1) {
+            if (kb == 0 && row < n) {
+#pragma unroll
+                for (int r = 0; r < MC; ++r)
+                    if (r < mcount) y[(size_t)(m0 + r) * n + row] = part[r];
+            }
+            return;
+        }
+        if (kb == 0) {
+#pragma unroll
+            for (int r = 0; r < MC; ++r) red[(wave * MC + r) * kTileRows + j] = part[r];
+        }
+        __syncthreads();
+        for (int o = threadIdx.x; o < MC * kTileRows; o += blockDim.x) {
+            const int r = o / kTileRows;
+            const int jj = o - r * kTileRows;
+            float sum = red[r * kTileRows + jj];
+            for (int w = 1; w < nwaves; ++w) sum += red[(w * MC + r) * kTileRows + jj];
+            const int rr = tile * kTileRows + jj;
+            if (r < mcount && rr < n) y[(size_t)(m0 + r) * n + rr] = sum;
+        }
+        return;
+    }
     if (kb == 0) {
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
@@ -318,7 +345,7 @@ hipError_t launch_tiles_one(const int8_t* q, const float* xs, const uint8_t* til
     const dim3 grid((unsigned)t.tiles, (unsigned)chunks);
     clear_stale_error();
     hipLaunchKernelGGL((small_m_tiles_kernel<MC, CPW>), grid, dim3(64 * waves), lds, stream, q, xs, tiles, y, (int)n,
-                       (int)k, (int)(k / 128), (int)t.g2, (int)t.s8, nseg, per_wave, (int)m, t.code_bytes);
+                       (int)k, (int)(k / 128), (int)t.s8, nseg, per_wave, (int)m);
     return hipGetLastError();
 }
 
@@ -342,16 +369,15 @@ hipError_t launch_prepare_tiles(const uint8_t* raw, int64_t stride, int64_t n, i
                                 hipStream_t stream) {
     const TileGeometry t = geometry(n, k);
     const int groups = (int)(k / 128);
-    const int64_t code_chunks = t.tiles * t.g2 * 64;
+    const int64_t code_chunks = t.tiles * t.s8 * 4 * 64;
     const int64_t scale_chunks = t.tiles * t.s8 * kTileRows;
     clear_stale_error();
     hipLaunchKernelGGL(prepare_tile_codes_kernel, dim3((unsigned)((code_chunks + 255) / 256)), dim3(256), 0, stream,
-                       raw, stride, n, groups, (int)t.g2, code_chunks, reinterpret_cast<uint4*>(tiles));
+                       raw, stride, n, groups, (int)t.s8, code_chunks, tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prepare_tile_scales_kernel, dim3((unsigned)((scale_chunks + 255) / 256)), dim3(256), 0, stream,
-                       raw, stride, n, groups, (int)t.s8, scale_chunks,
-                       reinterpret_cast<uint4*>(tiles + t.code_bytes));
+                       raw, stride, n, groups, (int)t.s8, scale_chunks, tiles);
     return hipGetLastError();
 }
 
@@ -366,10 +392,13 @@ static int tiles_slices(int64_t k, int max_waves, int* nseg, int* per_wave) {
     return (*nseg + *per_wave - 1) / *per_wave;
 }
 
-int tiles_default_split(int64_t k, int max_waves) {
+// Two waves per slice pay only when each slice spans several segments
+// (long k) and there are four or more columns (measured on the K = 5120 and
+// K = 17408 shapes); the split never changes the bits.
+int tiles_default_split(int64_t m, int64_t k, int max_waves) {
     int nseg, per_wave;
     const int slices = tiles_slices(k, max_waves, &nseg, &per_wave);
-    return slices * 2 <= 16 ? 2 : 1;
+    return (per_wave >= 2 && m >= 4 && slices * 2 <= 16) ? 2 : 1;
 }
 
 bool tiles_supported(int64_t k, int max_waves, int split) {

@@ -245,16 +245,16 @@ int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_strid
  * warp loads next to each other, same values at other addresses).
  *
  * Tile layout: T = ceil(n/16) tiles of 16 rows, G = k/128 groups,
- * G2 = ceil(G/2), S8 = ceil(G/8).  ONE allocation of pq2_tiles_bytes(n, k)
- * = T*(G2*1024 + S8*256) bytes:
- *  - code part: block (t, b) of 1024 bytes at (t*G2 + b)*1024; bytes
- *    16*l .. 16*l+15 with l = j + 16*kb (j = 0..15, kb = 0..3) hold four
+ * S8 = ceil(G/8) segments of 8 groups.  ONE allocation of
+ * pq2_tiles_bytes(n, k) = T*S8*4352 bytes made of segment units: unit
+ * (t, sb) at (t*S8 + sb)*4352 holds
+ *  - four code blocks b = 0..3 of 1024 bytes: bytes 1024*b + 16*l ..
+ *    1024*b + 16*l + 15 with l = j + 16*kb (j = 0..15, kb = 0..3) hold four
  *    dwords u = 0..3, dword u = the 16 weights k0..k0+15 of row 16t+j with
- *    k0 = 128*(2b + u/2) + 64*(u%2) + 16*kb; bits 2s..2s+1 of its byte v are
- *    the code of weight k0 + 4s + v;
- *  - scale part at byte T*G2*1024: block (t, sb) of 256 bytes at
- *    T*G2*1024 + (t*S8 + sb)*256; its bytes 16*j .. 16*j+15 are the eight
- *    fp16 scales of row 16t+j, groups 8*sb .. 8*sb+7;
+ *    k0 = 128*(8sb + 2b + u/2) + 64*(u%2) + 16*kb; bits 2s..2s+1 of its byte
+ *    v are the code of weight k0 + 4s + v;
+ *  - then 256 bytes of scales: bytes 4096 + 16*j .. 4096 + 16*j + 15 are the
+ *    eight fp16 scales of row 16t+j, groups 8*sb .. 8*sb+7;
  *  - padding rows (>= n) and groups (>= G) hold code 1 (weight 0), scale 0. */
 
 /* Bytes of the tile layout for an n x k weight matrix; -1 if n < 1,

@@ -116,59 +116,57 @@ int oracle_prepare_planes(const uint8_t* raw, int64_t row_stride, int64_t n, int
  * is stated with the library's pq2_prepare_tiles; the pages motivate it in
  * [KE] section H, Tests 24 and 25: the bytes one wave loads sit next to each
  * other).  Same values, other addresses.  T = ceil(n/16) tiles of 16 rows,
- * G2 = ceil(G/2), S8 = ceil(G/8):
- *  - code byte (t*G2 + b)*1024 + 16*l + 4*u + v, bits 2s..2s+1, with
+ * S8 = ceil(G/8) segments of 8 groups, one 4352-byte unit per (tile,
+ * segment) at (t*S8 + sb)*4352:
+ *  - code byte 1024*b + 16*l + 4*u + v of the unit, bits 2s..2s+1, with
  *    l = j + 16*kb, holds the code of weight k0 + 4s + v of row 16t + j,
- *    k0 = 128*(2b + u/2) + 64*(u%2) + 16*kb;
- *  - the fp16 scale of row 16t + j, group 8*sb + e sits at byte
- *    T*G2*1024 + (t*S8 + sb)*256 + 16*j + 2*e (little-endian);
+ *    k0 = 128*(8sb + 2b + u/2) + 64*(u%2) + 16*kb;
+ *  - the fp16 scale of row 16t + j, group 8*sb + e sits at unit byte
+ *    4096 + 16*j + 2*e (little-endian);
  *  - padding (rows >= n, groups >= G): code 1 (weight 0), scale 0.
  * Written as a scatter over every (row, weight) and (row, group) of the
  * padded matrix, one field at a time. */
 int64_t oracle_tiles_bytes(int64_t n, int64_t k) {
     if (k <= 0 || k % GROUP || n <= 0) return -1;
-    int64_t groups = k / GROUP, tiles = (n + 15) / 16;
-    return tiles * (((groups + 1) / 2) * 1024 + ((groups + 7) / 8) * 256);
+    return ((n + 15) / 16) * ((k / GROUP + 7) / 8) * 4352;
 }
 
 int oracle_prepare_tiles(const uint8_t* raw, int64_t row_stride, int64_t n, int64_t k, uint8_t* out) {
     if (k <= 0 || k % GROUP || n <= 0 || row_stride < (k / GROUP) * BLOCK_BYTES) return 1;
-    int64_t groups = k / GROUP, tiles = (n + 15) / 16;
-    int64_t g2 = (groups + 1) / 2, s8 = (groups + 7) / 8;
-    int64_t code_bytes = tiles * g2 * 1024;
+    int64_t groups = k / GROUP, tiles = (n + 15) / 16, s8 = (groups + 7) / 8;
     for (int64_t i = 0; i < oracle_tiles_bytes(n, k); ++i) out[i] = 0;
     for (int64_t t = 0; t < tiles; ++t) {
-        for (int64_t b = 0; b < g2; ++b) {
-            for (int l = 0; l < 64; ++l) {
-                int j = l % 16, kb = l / 16;
-                int64_t row = 16 * t + j;
-                for (int u = 0; u < 4; ++u) {
-                    int64_t g = 2 * b + u / 2;
-                    int64_t k0 = 128 * g + 64 * (u % 2) + 16 * kb;
-                    for (int v = 0; v < 4; ++v) {
-                        for (int s = 0; s < 4; ++s) {
-                            int64_t w = k0 + 4 * s + v;   /* weight index within the row */
-                            unsigned code = 1;
-                            if (row < n && g < groups) {
-                                int64_t i = w % GROUP;    /* weight index within its block */
-                                uint8_t byte = raw[row * row_stride + g * BLOCK_BYTES + 2 + i / 4];
-                                code = (byte >> (2 * (i % 4))) & 3u;
+        for (int64_t sb = 0; sb < s8; ++sb) {
+            uint8_t* unit = out + (t * s8 + sb) * 4352;
+            for (int b = 0; b < 4; ++b) {
+                for (int l = 0; l < 64; ++l) {
+                    int j = l % 16, kb = l / 16;
+                    int64_t row = 16 * t + j;
+                    for (int u = 0; u < 4; ++u) {
+                        int64_t g = 8 * sb + 2 * b + u / 2;
+                        int64_t k0 = 128 * g + 64 * (u % 2) + 16 * kb;
+                        for (int v = 0; v < 4; ++v) {
+                            for (int s = 0; s < 4; ++s) {
+                                int64_t w = k0 + 4 * s + v;   /* weight index within the row */
+                                unsigned code = 1;
+                                if (row < n && g < groups) {
+                                    int64_t i = w % GROUP;    /* weight index within its block */
+                                    uint8_t byte = raw[row * row_stride + g * BLOCK_BYTES + 2 + i / 4];
+                                    code = (byte >> (2 * (i % 4))) & 3u;
+                                }
+                                unit[1024 * b + 16 * l + 4 * u + v] |= (uint8_t)(code << (2 * s));
                             }
-                            out[(t * g2 + b) * 1024 + 16 * l + 4 * u + v] |= (uint8_t)(code << (2 * s));
                         }
                     }
                 }
             }
-        }
-        for (int64_t sb = 0; sb < s8; ++sb) {
             for (int j = 0; j < 16; ++j) {
                 int64_t row = 16 * t + j;
                 for (int e = 0; e < 8; ++e) {
                     int64_t g = 8 * sb + e;
-                    uint8_t* dst = out + code_bytes + (t * s8 + sb) * 256 + 16 * j + 2 * e;
                     if (row < n && g < groups) {
-                        dst[0] = raw[row * row_stride + g * BLOCK_BYTES + 0];
-                        dst[1] = raw[row * row_stride + g * BLOCK_BYTES + 1];
+                        unit[4096 + 16 * j + 2 * e] = raw[row * row_stride + g * BLOCK_BYTES + 0];
+                        unit[4096 + 16 * j + 2 * e + 1] = raw[row * row_stride + g * BLOCK_BYTES + 1];
                     }
                 }
             }

@@ -121,12 +121,12 @@ def test_small_m_valid_settings_reach_the_device_check():
 
 
 def test_tiles_bytes():
-    """T*(G2*1024 + S8*256) with T = ceil(n/16), G2 = ceil(G/2), S8 = ceil(G/8)."""
+    """T*S8*4352 with T = ceil(n/16), S8 = ceil(G/8)."""
     f = pq2.pq2_tiles_bytes
     assert f(10240, 5120) == 10240 * 40 * 34           # no padding: equal to the prepared planes
     assert f(5120, 17408) == 5120 * 136 * 34
-    assert f(1, 128) == 1024 + 256                     # one tile, one (padded) group pair and scale block
-    assert f(17, 384) == 2 * (2 * 1024 + 256)
+    assert f(1, 128) == 4352                           # one tile, one (padded) segment unit
+    assert f(17, 1152) == 2 * 2 * 4352
     for n, k in ((0, 128), (1, 100), (1, 0), (1, 1 << 17), ((1 << 30) + 1, 128)):
         assert pq2.lib.pq2_tiles_bytes(n, k) == -1, (n, k)
 
@@ -140,7 +140,7 @@ def test_prepare_tiles_validation():
     assert f(A, 33, 4, 128, B, None) == ESHAPE          # row stride below 34 bytes per block
     assert f(A, 34, 4, 128, B + 8, None) == EALIGN     # tiles not 16-byte aligned
     assert f(A, 34, 4, 128, A + 64, None) == EINVAL    # tiles overlap raw
-    assert f(A, 34, 4, 128, A - 1024, None) == EINVAL  # the 1280-byte tiles end inside raw's 136 bytes
+    assert f(A, 34, 4, 128, A - 4096, None) == EINVAL  # the 4352-byte tiles end inside raw's 136 bytes
     if not _gpu_visible():
         assert f(A, 34, 4, 128, A + 144, None) == EDEVICE  # adjacent, no overlap: valid
 
@@ -148,7 +148,7 @@ def test_prepare_tiles_validation():
 def test_small_m_tiles_validation():
     f = pq2.lib.pq2_matmul_small_m_tiles
     assert f(A, B, C, 17, 8, 128, D, None) == ESHAPE
-    assert f(A, B, C, 1, 8, 128, C + 1024, None) == EINVAL  # y overlaps the tiles (1280 bytes)
+    assert f(A, B, C, 1, 8, 128, C + 4096, None) == EINVAL  # y overlaps the tiles (4352 bytes)
     t = pq2.lib.pq2_matmul_small_m_tiles_tuned
     assert t(A, B, C, 1, 8, 128, D, 9, 0, None) == EINVAL     # waves
     assert t(A, B, C, 1, 8, 128, D, -1, 0, None) == EINVAL

@@ -157,19 +157,20 @@ def test_prepare_tiles_preserves_every_value(n, k, pad):
     raw = workloads.make_raw_weights(n, k, seed=21 + n, codes="ternary+3", row_pad=pad)
     tiles = oracle.prepare_tiles(raw, n, k)
     g = k // 128
-    t, g2, s8 = -(-n // 16), -(-g // 2), -(-g // 8)
-    assert tiles.size == t * (g2 * 1024 + s8 * 256)
+    t, s8 = -(-n // 16), -(-g // 8)
+    assert tiles.size == t * s8 * 4352
     blocks = raw[:, : g * 34].reshape(n, g, 34)
     # Raw codes in weight order: weight 4b + s of a block is field s of byte b.
     raw_codes = ((blocks[:, :, 2:, None] >> (2 * np.arange(4))) & 3).reshape(n, k)
-    # Tile bytes: [t][b][kb][j][u][v], field s of byte v of dword u = weight
-    # 128*(2b + u//2) + 64*(u%2) + 16*kb + 4s + v of row 16t + j.
-    code = tiles[: t * g2 * 1024].reshape(t, g2, 4, 16, 2, 2, 4)
-    fields = (code[..., None] >> (2 * np.arange(4))) & 3          # ..., v, s
-    w = fields.transpose(0, 3, 1, 4, 5, 2, 7, 6).reshape(t * 16, g2 * 256)  # [row][b, ug, uh, kb, s, v]
+    units = tiles.reshape(t, s8, 4352)
+    # Unit code bytes: [b][kb][j][u][v], field s of byte v of dword u = weight
+    # 128*(8sb + 2b + u//2) + 64*(u%2) + 16*kb + 4s + v of row 16t + j.
+    code = units[:, :, :4096].reshape(t, s8, 4, 4, 16, 2, 2, 4)   # t, sb, b, kb, j, ug, uh, v
+    fields = (code[..., None] >> (2 * np.arange(4))) & 3         # ..., v, s
+    w = fields.transpose(0, 4, 1, 2, 5, 6, 3, 8, 7).reshape(t * 16, s8 * 1024)  # [row][sb, b, ug, uh, kb, s, v]
     assert np.array_equal(w[:n, :k], raw_codes)
     assert np.all(w[n:] == 1) and np.all(w[:, k:] == 1)
-    sc = tiles[t * g2 * 1024:].reshape(t, s8, 16, 8, 2).transpose(0, 2, 1, 3, 4).reshape(t * 16, s8 * 8, 2)
+    sc = units[:, :, 4096:].reshape(t, s8, 16, 8, 2).transpose(0, 2, 1, 3, 4).reshape(t * 16, s8 * 8, 2)
     assert np.array_equal(sc[:n, :g], blocks[:, :, :2])
     assert np.all(sc[n:] == 0) and np.all(sc[:, g:] == 0)
 
