@@ -41,6 +41,8 @@ EXPORTED = (
     "pq2_prepare_tiles",
     "pq2_matmul_small_m_tiles",
     "pq2_matmul_small_m_tiles_tuned",
+    "pq2_matmul_small_m_tiles_fused",
+    "pq2_matmul_small_m_tiles_fused_tuned",
     "pq2_matmul_prefill_planes",
     "pq2_matmul_prefill_planes_tuned",
     "pq2_matmul_small_m_fused",
@@ -114,6 +116,10 @@ def _load_library():
     lib.pq2_matmul_small_m_tiles.restype = i32
     lib.pq2_matmul_small_m_tiles_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tiles_tuned.restype = i32
+    lib.pq2_matmul_small_m_tiles_fused.argtypes = [p, i32, i64, p, i64, i64, i64, p, p]
+    lib.pq2_matmul_small_m_tiles_fused.restype = i32
+    lib.pq2_matmul_small_m_tiles_fused_tuned.argtypes = [p, i32, i64, p, i64, i64, i64, p, i32, i32, p]
+    lib.pq2_matmul_small_m_tiles_fused_tuned.restype = i32
     return lib
 
 
@@ -267,6 +273,30 @@ def pq2_matmul_small_m_tiles(q, xs, tiles, y, stream=None) -> None:
 def pq2_matmul_small_m_tiles_tuned(q, xs, tiles, y, max_waves=0, split=0, stream=None) -> None:
     _check(lib.pq2_matmul_small_m_tiles_tuned(*_tiles_args(q, xs, tiles, y), max_waves, split, _stream(stream)),
            "pq2_matmul_small_m_tiles_tuned")
+
+
+def _tiles_fused_args(x, tiles, y):
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if tiles.dtype != torch.uint8 or y.dtype != torch.float32 or not tiles.is_contiguous() or not y.is_contiguous():
+        raise ValueError("tiles uint8 and y float32, both contiguous, expected")
+    m, n = y.shape
+    k = x.shape[1]
+    if x.shape[0] != m or tiles.numel() < pq2_tiles_bytes(n, k):
+        raise ValueError("shape mismatch between x, tiles and y")
+    return (_dev_ptr(x, "x"), _dtype_code(x), x.stride(0), _dev_ptr(tiles, "tiles"), m, n, k, _dev_ptr(y, "y"))
+
+
+def pq2_matmul_small_m_tiles_fused(x, tiles, y, stream=None) -> None:
+    """Quantise x (bf16/f16/f32 [m][k]) and multiply by the tile layout in one launch."""
+    _check(lib.pq2_matmul_small_m_tiles_fused(*_tiles_fused_args(x, tiles, y), _stream(stream)),
+           "pq2_matmul_small_m_tiles_fused")
+
+
+def pq2_matmul_small_m_tiles_fused_tuned(x, tiles, y, max_waves=0, split=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_tiles_fused_tuned(*_tiles_fused_args(x, tiles, y), max_waves, split,
+                                                    _stream(stream)), "pq2_matmul_small_m_tiles_fused_tuned")
 
 
 def _fused_args(x, planes, y):

@@ -153,6 +153,36 @@ int pq2_matmul_small_m_tiles(const int8_t* q, const float* xs, const void* tiles
     return pq2_matmul_small_m_tiles_tuned(q, xs, tiles, m, n, k, y, 0, 0, stream);
 }
 
+int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
+                                         int64_t m, int64_t n, int64_t k, float* y, int max_waves, int split,
+                                         void* stream) {
+    if (!x || !tiles || !y) return PQ2_EINVAL;
+    if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
+    if (m < 1 || m > PQ2_MAX_SMALL_M || n < 1 || n > kMaxN) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (x_row_stride_elems < k) return PQ2_ESHAPE;
+    const int esize = dtype == PQ2_F32 ? 4 : 2;
+    const size_t xbytes = ((size_t)(m - 1) * x_row_stride_elems + k) * esize;
+    if (xbytes >= ((size_t)1 << 31)) return PQ2_ESHAPE;  // the kernel addresses x with 32-bit offsets
+    if (!aligned(x, 16) || (x_row_stride_elems * esize) % 16 || !aligned(tiles, 16) || !aligned(y, 4))
+        return PQ2_EALIGN;
+    const size_t ybytes = (size_t)m * n * 4;
+    if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, tiles, (size_t)pq2::tiles_bytes(n, k))) return PQ2_EINVAL;
+    if (max_waves < 0 || max_waves > 8) return PQ2_EINVAL;
+    const int waves = max_waves ? max_waves : pq2::default_small_m_config(pq2::kSrcNatural, m, n, k).max_waves;
+    if (!split) split = pq2::tiles_default_split(m, k, waves);
+    if (!pq2::tiles_supported(k, waves, split)) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m_tiles_fused(x, dtype, x_row_stride_elems,
+                                                         static_cast<const uint8_t*>(tiles), m, n, k, y, waves, split,
+                                                         (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_tiles_fused(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
+                                   int64_t m, int64_t n, int64_t k, float* y, void* stream) {
+    return pq2_matmul_small_m_tiles_fused_tuned(x, dtype, x_row_stride_elems, tiles, m, n, k, y, 0, 0, stream);
+}
+
 int pq2_quantize_act_i8(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
                         int8_t* q, float* xs, void* stream) {
     if (!x || !q || !xs) return PQ2_EINVAL;

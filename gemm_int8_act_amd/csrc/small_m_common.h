@@ -27,7 +27,8 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t 
 // breakthrough", "Calculate with small integers" step 1) of one row slot's
 // group, 16 elements per lane: lane j of the slot holds elements
 // 16j..16j+15 in v.  Returns the lane's 16 codes in plane order (dword s =
-// codes 16j + s, +4, +8, +12) and sets gsum (group sum of q, all 8 lanes)
+// codes 16j + s, +4, +8, +12), or with PLANE false in natural order (dword s
+// = codes 16j + 4s .. 16j + 4s + 3), and sets gsum (group sum of q, all 8 lanes)
 // and scale (max|x| / 127, correctly rounded).  The codes equal the
 // definition q = clamp(rint(RN(x / d)), +-127), d = scale or 1 for an
 // all-zero group, bit for bit:
@@ -42,6 +43,7 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t 
 //    |t| < 127.5 makes the clamp a no-op;
 //  * otherwise (a near-tie in any of the lane's 16 elements, or d
 //    subnormal) the lane repeats the definition with IEEE divisions.
+template <bool PLANE = true>
 __device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum, float& scale) {
 #pragma clang fp contract(off)
     float amax = 0.0f;
@@ -70,10 +72,17 @@ __device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum
         }
     }
     uint4 out;
-    out.x = low_bytes4(bits[0], bits[4], bits[8], bits[12]);
-    out.y = low_bytes4(bits[1], bits[5], bits[9], bits[13]);
-    out.z = low_bytes4(bits[2], bits[6], bits[10], bits[14]);
-    out.w = low_bytes4(bits[3], bits[7], bits[11], bits[15]);
+    if constexpr (PLANE) {
+        out.x = low_bytes4(bits[0], bits[4], bits[8], bits[12]);
+        out.y = low_bytes4(bits[1], bits[5], bits[9], bits[13]);
+        out.z = low_bytes4(bits[2], bits[6], bits[10], bits[14]);
+        out.w = low_bytes4(bits[3], bits[7], bits[11], bits[15]);
+    } else {
+        out.x = low_bytes4(bits[0], bits[1], bits[2], bits[3]);
+        out.y = low_bytes4(bits[4], bits[5], bits[6], bits[7]);
+        out.z = low_bytes4(bits[8], bits[9], bits[10], bits[11]);
+        out.w = low_bytes4(bits[12], bits[13], bits[14], bits[15]);
+    }
     int s = dot4(out.x, 0x01010101u, 0);
     s = dot4(out.y, 0x01010101u, s);
     s = dot4(out.z, 0x01010101u, s);

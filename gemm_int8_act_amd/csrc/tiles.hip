@@ -44,7 +44,7 @@
 //    wave's segments, the classes added as ((A0+A4)+(A1+A5))+((A2+A6)+(A3+A7)),
 //    then the waves in index order.
 #include "pq2_internal.h"
-#include "pq2_device.h"
+#include "small_m_common.h"
 
 #include <hip/hip_fp16.h>
 
@@ -138,11 +138,17 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
     return __half2float(__ushort_as_half((unsigned short)((c & 1) ? (w >> 16) : (w & 0xFFFFu))));
 }
 
-template <int MC, int CPW>
+// SRC: kSrcNatural reads q and xs; kSrcBf16 / kSrcF16 / kSrcF32 read x and
+// quantise each staged group in the wave (the exact in-kernel quantiser, so
+// the codes and scales are those of pq2_quantize_act_i8).
+template <int MC, int CPW, int SRC>
 __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
-    const int8_t* __restrict__ q, const float* __restrict__ xs, const uint8_t* __restrict__ tiles,
-    float* __restrict__ y, int n, int k, int groups, int s8, int nseg, int per_wave, int mtotal) {
+    const int8_t* __restrict__ q, const float* __restrict__ xs, const void* __restrict__ x, int64_t x_stride,
+    const uint8_t* __restrict__ tiles, float* __restrict__ y, int n, int k, int groups, int s8, int nseg,
+    int per_wave, int mtotal) {
 #pragma clang fp contract(off)
+    constexpr bool FUSED = src_fused(SRC);
+    constexpr int XL = src_xloads(SRC);
     typedef int v4i __attribute__((ext_vector_type(4)));
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int WPS = 8 / CPW;            // waves per k slice (each takes CPW group classes)
@@ -178,8 +184,11 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     nsq_lds[lane] = 0;
 
     const auto tile_rs = make_rsrc(tiles + (size_t)tile * s8 * kSegUnit, (uint32_t)(s8 * kSegUnit));
-    const auto q_rs = make_rsrc(q + (size_t)m0 * k, (uint32_t)(mcount * k));
-    const auto xs_rs = make_rsrc(xs + (size_t)m0 * groups, (uint32_t)(mcount * groups * 4));
+    const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
+    const auto xs_rs = make_rsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
+    const auto x_rs = make_rsrc(
+        FUSED ? static_cast<const unsigned char*>(x) + (size_t)m0 * x_stride * src_esize(SRC) : nullptr,
+        FUSED ? (uint32_t)(((int64_t)(mcount - 1) * x_stride + k) * src_esize(SRC)) : 0u);
     // Staging roles: chunk ch of column (load t) * COLS_PER_LOAD + sub.
     const int ch = lane % CHUNKS;
     const int sub = lane / CHUNKS;
@@ -196,15 +205,24 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
         //    weight scales, all in flight together.  Groups past the end read
         //    zeros.
         uint4 qv[QLOADS];
-        const uint32_t qoff = (uint32_t)(s * 1024 + 128 * c_lo + 16 * ch);
+        uint4 xv[QLOADS][FUSED ? XL : 1];
+        const uint32_t qoff = (uint32_t)(s * 1024 + 128 * c_lo + 16 * ch);  // element offset in the row
 #pragma unroll
         for (int t = 0; t < QLOADS; ++t) {
             const int m = t * COLS_PER_LOAD + sub;
-            qv[t] = buf_load16(q_rs, (m < mcount && (int)qoff < k) ? (uint32_t)(m * k) + qoff : kBufferOOB);
+            const bool ok = m < mcount && (int)qoff < k;
+            if constexpr (FUSED) {
+                const uint32_t off = (uint32_t)((m * x_stride + qoff) * src_esize(SRC));
+#pragma unroll
+                for (int l = 0; l < XL; ++l) xv[t][l] = buf_load16(x_rs, ok ? off + 16u * l : kBufferOOB);
+            } else {
+                qv[t] = buf_load16(q_rs, ok ? (uint32_t)(m * k) + qoff : kBufferOOB);
+            }
         }
         const int xm = lane >> 3, xc = lane & 7;
-        const uint32_t xsw = buf_load4(xs_rs, (xm < mcount && 8 * s + xc < groups)
-                                                  ? (uint32_t)((xm * groups + 8 * s + xc) * 4) : kBufferOOB);
+        const uint32_t xsw = FUSED ? 0u
+                                   : buf_load4(xs_rs, (xm < mcount && 8 * s + xc < groups)
+                                                          ? (uint32_t)((xm * groups + 8 * s + xc) * 4) : kBufferOOB);
         const uint32_t unit_off = (uint32_t)(s * kSegUnit);
         const uint4 wsv = buf_load16(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
         keep_order();
@@ -219,17 +237,27 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
         // 2. Stage the activations, xs and each group's -sum(q) (dot4 against
         //    ones over the lane's 16 bytes, then the 8 lanes of the group).
         //    Lanes past the last column write their (zero) chunk to the spare column.
-        xs_lds[xc * 8 + xm] = __uint_as_float(xsw);
+        if constexpr (!FUSED) xs_lds[xc * 8 + xm] = __uint_as_float(xsw);
 #pragma unroll
         for (int t = 0; t < QLOADS; ++t) {
             const int m = t * COLS_PER_LOAD + sub;
-            const uint4 v = qv[t];
+            uint4 v;
+            int sq;
+            if constexpr (FUSED) {
+                float xf[16];
+                x_to_float16<SRC>(xv[t], xf);
+                float scale;
+                v = quantize_lane16<false>(xf, sq, scale);  // the 8 lanes of the group agree
+                if ((lane & 7) == 0 && m < MC) xs_lds[(c_lo + (ch >> 3)) * 8 + m] = scale;
+            } else {
+                v = qv[t];
+                sq = dot4(v.x, 0x01010101u, 0);
+                sq = dot4(v.y, 0x01010101u, sq);
+                sq = dot4(v.z, 0x01010101u, sq);
+                sq = dot4(v.w, 0x01010101u, sq);
+                sq = sum8_i(sq);
+            }
             *reinterpret_cast<uint4*>(region + (m < MC ? m : MC) * PITCH + 16 * ch) = v;
-            int sq = dot4(v.x, 0x01010101u, 0);
-            sq = dot4(v.y, 0x01010101u, sq);
-            sq = dot4(v.z, 0x01010101u, sq);
-            sq = dot4(v.w, 0x01010101u, sq);
-            sq = sum8_i(sq);
             if ((lane & 7) == 0 && m < MC) nsq_lds[(c_lo + (ch >> 3)) * 8 + m] = -sq;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -336,28 +364,47 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     }
 }
 
-template <int MC, int CPW>
-hipError_t launch_tiles_one(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n, int64_t k,
-                            float* y, int slices, int nseg, int per_wave, int chunks, hipStream_t stream) {
+struct TilesArgs {
+    const int8_t* q;
+    const float* xs;
+    const void* x;
+    int64_t x_stride;
+    const uint8_t* tiles;
+    int64_t m, n, k;
+    float* y;
+    hipStream_t stream;
+};
+
+template <int MC, int CPW, int SRC>
+hipError_t launch_tiles_one(const TilesArgs& a, int slices, int nseg, int per_wave, int chunks) {
+    const int64_t m = a.m, n = a.n, k = a.k;
     const TileGeometry t = geometry(n, k);
     const int waves = slices * (8 / CPW);
     const size_t lds = (size_t)waves * tiles_region_bytes(MC, CPW) + (size_t)slices * 8 * MC * kTileRows * 4;
     const dim3 grid((unsigned)t.tiles, (unsigned)chunks);
     clear_stale_error();
-    hipLaunchKernelGGL((small_m_tiles_kernel<MC, CPW>), grid, dim3(64 * waves), lds, stream, q, xs, tiles, y, (int)n,
-                       (int)k, (int)(k / 128), (int)t.s8, nseg, per_wave, (int)m);
+    hipLaunchKernelGGL((small_m_tiles_kernel<MC, CPW, SRC>), grid, dim3(64 * waves), lds, a.stream, a.q, a.xs, a.x,
+                       a.x_stride, a.tiles, a.y, (int)n, (int)k, (int)(k / 128), (int)t.s8, nseg, per_wave, (int)m);
     return hipGetLastError();
 }
 
-template <int CPW>
-hipError_t launch_tiles_mc(int mc, const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
-                           int64_t k, float* y, int slices, int nseg, int per_wave, int chunks, hipStream_t stream) {
+template <int CPW, int SRC>
+hipError_t launch_tiles_mc(int mc, const TilesArgs& a, int slices, int nseg, int per_wave, int chunks) {
     switch (mc) {
-        case 1: return launch_tiles_one<1, CPW>(q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
-        case 2: return launch_tiles_one<2, CPW>(q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
-        case 3: return launch_tiles_one<3, CPW>(q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
-        case 4: return launch_tiles_one<4, CPW>(q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
+        case 1: return launch_tiles_one<1, CPW, SRC>(a, slices, nseg, per_wave, chunks);
+        case 2: return launch_tiles_one<2, CPW, SRC>(a, slices, nseg, per_wave, chunks);
+        case 3: return launch_tiles_one<3, CPW, SRC>(a, slices, nseg, per_wave, chunks);
+        case 4: return launch_tiles_one<4, CPW, SRC>(a, slices, nseg, per_wave, chunks);
         default: return hipErrorInvalidValue;
+    }
+}
+
+template <int SRC>
+hipError_t launch_tiles_split(int split, int mc, const TilesArgs& a, int slices, int nseg, int per_wave, int chunks) {
+    switch (split) {
+        case 1: return launch_tiles_mc<8, SRC>(mc, a, slices, nseg, per_wave, chunks);
+        case 2: return launch_tiles_mc<4, SRC>(mc, a, slices, nseg, per_wave, chunks);
+        default: return launch_tiles_mc<2, SRC>(mc, a, slices, nseg, per_wave, chunks);
     }
 }
 
@@ -407,19 +454,32 @@ bool tiles_supported(int64_t k, int max_waves, int split) {
     return tiles_slices(k, max_waves, &nseg, &per_wave) * split <= 16;
 }
 
+static hipError_t launch_tiles_any(int src, const TilesArgs& a, int max_waves, int split) {
+    if (!tiles_supported(a.k, max_waves, split)) return hipErrorInvalidValue;
+    int nseg, per_wave;
+    const int slices = tiles_slices(a.k, max_waves, &nseg, &per_wave);
+    int mc = (int)(a.m < kTilesMaxColumns ? a.m : kTilesMaxColumns);
+    const int chunks = (int)((a.m + mc - 1) / mc);
+    mc = (int)((a.m + chunks - 1) / chunks);
+    switch (src) {
+        case kSrcNatural: return launch_tiles_split<kSrcNatural>(split, mc, a, slices, nseg, per_wave, chunks);
+        case kSrcBf16: return launch_tiles_split<kSrcBf16>(split, mc, a, slices, nseg, per_wave, chunks);
+        case kSrcF16: return launch_tiles_split<kSrcF16>(split, mc, a, slices, nseg, per_wave, chunks);
+        case kSrcF32: return launch_tiles_split<kSrcF32>(split, mc, a, slices, nseg, per_wave, chunks);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_small_m_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int max_waves, int split, hipStream_t stream) {
-    if (!tiles_supported(k, max_waves, split)) return hipErrorInvalidValue;
-    int nseg, per_wave;
-    const int slices = tiles_slices(k, max_waves, &nseg, &per_wave);
-    int mc = (int)(m < kTilesMaxColumns ? m : kTilesMaxColumns);
-    const int chunks = (int)((m + mc - 1) / mc);
-    mc = (int)((m + chunks - 1) / chunks);
-    switch (split) {
-        case 1: return launch_tiles_mc<8>(mc, q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
-        case 2: return launch_tiles_mc<4>(mc, q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
-        default: return launch_tiles_mc<2>(mc, q, xs, tiles, m, n, k, y, slices, nseg, per_wave, chunks, stream);
-    }
+    const TilesArgs a{q, xs, nullptr, 0, tiles, m, n, k, y, stream};
+    return launch_tiles_any(kSrcNatural, a, max_waves, split);
+}
+
+hipError_t launch_small_m_tiles_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* tiles, int64_t m,
+                                      int64_t n, int64_t k, float* y, int max_waves, int split, hipStream_t stream) {
+    const TilesArgs a{nullptr, nullptr, x, x_stride, tiles, m, n, k, y, stream};
+    return launch_tiles_any(src_of_dtype(dtype), a, max_waves, split);
 }
 
 }  // namespace pq2

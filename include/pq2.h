@@ -296,6 +296,34 @@ int pq2_matmul_small_m_tiles(const int8_t* q, const float* xs, const void* tiles
 int pq2_matmul_small_m_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
                                    int64_t k, float* y, int max_waves, int split, void* stream);
 
+/* Quantise + tile-layout matmul in one launch: bit for bit the y of
+ * pq2_quantize_act_i8 followed by pq2_matmul_small_m_tiles (same codes,
+ * scales and summation order).  Every wave quantises the activation groups
+ * it stages, with the exact in-kernel quantiser of
+ * pq2_matmul_small_m_fused (page "Kernel experiments", Test 12 fusion screen
+ * and Test 18: fused preparation must reproduce the standalone quantiser's
+ * codes exactly).
+ *   x       device, dtype PQ2_BF16 / PQ2_F16 / PQ2_F32, m rows of
+ *           x_row_stride_elems elements (>= k); x and the row stride in
+ *           bytes 16-byte aligned; all m rows within 2^31 - 1 bytes.
+ *   tiles   device tile layout of the weights, 16-byte aligned.
+ *   y       device float [m][n], 4-byte aligned; fully overwritten; must not
+ *           overlap x or tiles.
+ * Errors: EINVAL (null, dtype, overlap), ESHAPE (m outside 1..16, n<1,
+ *         k<128, k%128, k > PQ2_MAX_K, stride < k, x span >= 2^31 bytes),
+ *         EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_small_m_tiles_fused(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
+                                   int64_t m, int64_t n, int64_t k, float* y, void* stream);
+
+/* Tuning hook for pq2_matmul_small_m_tiles_fused (benchmarks and tests
+ * only): max_waves and split as for pq2_matmul_small_m_tiles_tuned, with
+ * the same bits as pq2_quantize_act_i8 + pq2_matmul_small_m_tiles_tuned at
+ * the same settings.  Errors as pq2_matmul_small_m_tiles_fused, plus EINVAL
+ * for an unsupported setting. */
+int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
+                                         int64_t m, int64_t n, int64_t k, float* y, int max_waves, int split,
+                                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

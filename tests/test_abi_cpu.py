@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 20
+    assert len(names) == 22
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -157,6 +157,22 @@ def test_small_m_tiles_validation():
     if not _gpu_visible():
         for waves, split in ((0, 0), (1, 1), (8, 2), (1, 4), (5, 0)):
             assert t(A, B, C, 4, 8, 5120, D, waves, split, None) == EDEVICE, (waves, split)
+
+
+def test_small_m_tiles_fused_validation():
+    f = pq2.lib.pq2_matmul_small_m_tiles_fused
+    assert f(None, 0, 128, C, 1, 8, 128, D, None) == EINVAL
+    assert f(A, 3, 128, C, 1, 8, 128, D, None) == EINVAL        # dtype
+    assert f(A, 0, 128, C, 17, 8, 128, D, None) == ESHAPE       # columns
+    assert f(A, 0, 100, C, 1, 8, 128, D, None) == ESHAPE        # stride < k
+    assert f(A + 2, 0, 128, C, 1, 8, 128, D, None) == EALIGN    # x not 16-byte aligned
+    assert f(A, 0, 129, C, 2, 8, 128, D, None) == EALIGN        # row stride not 16-byte aligned
+    assert f(A, 0, 128, C, 1, 8, 128, C + 64, None) == EINVAL   # y overlaps the tiles
+    t = pq2.lib.pq2_matmul_small_m_tiles_fused_tuned
+    assert t(A, 0, 128, C, 1, 8, 128, D, 9, 0, None) == EINVAL
+    assert t(A, 0, 128, C, 1, 8, 128, D, 0, 3, None) == EINVAL
+    if not _gpu_visible():
+        assert t(A, 2, 5120, C, 4, 8, 5120, D, 0, 0, None) == EDEVICE
 
 
 def test_prefill_tile_validation():

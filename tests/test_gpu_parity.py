@@ -746,3 +746,93 @@ def test_fused_workloads(name):
         mi, ni = _sample_indices(m, w.n, 200, seed=50 + m)
         y_ref, bound = oracle.matmul_raw_sample(qo, xso, raw, w.n, w.k, mi, ni)
         assert_within(yf[mi, ni], y_ref, bound, f"fused {name} m={m}")
+
+
+# ------------------------------------------------------------------ fused quantise + tile-layout matmul
+def gpu_tiles_fused(x_dev, tiles, n, **kw):
+    pq2 = _pq2()
+    y = torch.full((x_dev.shape[0], n), float("nan"), dtype=torch.float32, device=DEV)
+    if kw:
+        pq2.pq2_matmul_small_m_tiles_fused_tuned(x_dev, tiles, y, **kw)
+    else:
+        pq2.pq2_matmul_small_m_tiles_fused(x_dev, tiles, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _tiles_splits(k, waves=8):
+    """The (max_waves, split) settings offered for this k (at most 16 waves)."""
+    nseg = -(-(k // 128) // 8)
+    slices = -(-nseg // -(-nseg // waves))
+    return [s for s in (1, 2, 4) if slices * s <= 16]
+
+
+@pytest.mark.parametrize("m,n,k", FUSED_SHAPES)
+def test_tiles_fused_full(m, n, k):
+    """Quantise + tile matmul in one launch: within the oracle's bound and
+    bit-identical to pq2_quantize_act_i8 + pq2_matmul_small_m_tiles for
+    every split."""
+    pq2 = _pq2()
+    announce(f"tiles fused full m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=90 + m + n, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 91 + k, "normal+outliers")
+    q, xs, qo, xso = quantise_both(x)
+    tiles = gpu_tiles(raw, n, k)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    xd = x.to(DEV)
+    for split in _tiles_splits(k):
+        yf = gpu_tiles_fused(xd, tiles, n, split=split)
+        assert_within(yf, y_ref, bound, f"tiles fused split={split}")
+        yu = gpu_matmul(pq2.pq2_matmul_small_m_tiles_tuned, q, xs, tiles, n, split=split)
+        assert same_bits(yf, yu), f"tiles fused split={split} differs from quantise + matmul"
+    assert same_bits(gpu_tiles_fused(xd, tiles, n), gpu_matmul(pq2.pq2_matmul_small_m, q, xs, gpu_planes(raw, n, k), n))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k,pad", [(1, 200, 1024, 0), (3, 150, 640, 8), (4, 64, 5120, 16), (7, 90, 2048, 24)])
+def test_tiles_fused_dtypes_and_strides(dtype, m, n, k, pad):
+    pq2 = _pq2()
+    announce(f"tiles fused dtype={dtype} m={m} n={n} k={k} pad={pad}")
+    tdt = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    xt = (workloads.make_activations(m, k + pad, 170 + m, "laplace").float() * 3.0).to(tdt)
+    bits = xt.numpy() if dtype == "f32" else xt.view(torch.int16).numpy().view(np.uint16)
+    qo, xso = oracle.quantize_act_i8(bits, dtype, k=k)
+    raw = workloads.make_raw_weights(n, k, seed=171 + n, codes="ternary+3")
+    tiles = gpu_tiles(raw, n, k)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    xd = xt.to(DEV)
+    yf = gpu_tiles_fused(xd[:, :k], tiles, n)  # row stride k + pad elements
+    assert_within(yf, y_ref, bound, f"tiles fused {dtype}")
+    q, xs = gpu_quantize(xd, k)
+    assert same_bits(yf, gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, tiles, n))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tiles_fused_quantiser_codes_exact(dtype):
+    """Every code and scale of the tile engine's in-kernel quantiser, read
+    back through single-weight rows, equals the oracle's q * xs bit for bit."""
+    k = 2048
+    announce(f"tiles fused quantiser probe dtype={dtype} k={k}")
+    x = probe_activations(dtype, k)
+    bits = x.numpy() if dtype == "f32" else workloads.bf16_bits(x)
+    qo, xso = oracle.quantize_act_i8(bits, dtype)
+    tiles = gpu_tiles(probe_weights(k), k, k)
+    expect = qo.astype(np.float32) * np.repeat(xso, 128, axis=1)
+    for split in _tiles_splits(k):
+        y = gpu_tiles_fused(x.to(DEV), tiles, k, split=split)
+        bad = np.argwhere(y.view(np.uint32) != expect.view(np.uint32))
+        assert bad.size == 0, f"split={split}: {len(bad)} codes differ, first at {tuple(bad[0])}"
+
+
+@pytest.mark.parametrize("name", ["qkv", "up", "down"])
+def test_tiles_fused_workloads(name):
+    """Full workload sizes: bit-identical to quantise + tile matmul at every M."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    tiles = gpu_tiles(raw, w.n, w.k)
+    for m in w.ms:
+        announce(f"tiles fused workload {name} m={m}")
+        xd = x[:m].contiguous().to(DEV)
+        q, xs = gpu_quantize(xd)
+        assert same_bits(gpu_tiles_fused(xd, tiles, w.n), gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, tiles, w.n)), \
+            f"{name} m={m}"
