@@ -8,15 +8,16 @@ N=10240) at M = 1, 2, 3, 4 activation columns.
 
 A step is one pass of the per-call hot path over one batch: for each M in
 1..4, quantise the bf16 activations to INT8 (pq2_quantize_act_i8) and run the
-small-m matmul (pq2_matmul_small_m) against the prepared planes.  The
-plane-order variant (pq2_quantize_act_i8_planes + pq2_matmul_small_m_planes,
-same result bits) is timed per M as well and reported beside it, and so is
-the one-launch pq2_matmul_small_m_fused (same bits again).  Weight
-preparation (pq2_prepare_planes) is one-time and outside the timing.  Every
-step reads the next of R prepared-plane copies (>= 1 GiB in total, four
-times the 256 MB Infinity Cache), so weights stream from HBM.  Steps are
-captured as HIP graphs (one per copy) and replayed; K steps are timed with
-HIP events between a synchronize on each side.
+small-m matmul on the tile-layout weights (pq2_matmul_small_m_tiles, the
+fastest path over M = 1..4).  The same calls on the row-major prepared planes
+(pq2_matmul_small_m), their plane-order variant and both one-launch fused
+entry points are timed per M and reported beside it; every path gives the
+same output bits, which the run checks.  Weight preparation
+(pq2_prepare_tiles / pq2_prepare_planes) is one-time and outside the timing.
+Every step reads the next of R weight copies (>= 1 GiB in total per layout,
+four times the 256 MB Infinity Cache), so weights stream from HBM.  Steps
+are captured as HIP graphs (one per copy) and replayed; K steps are timed
+with HIP events between a synchronize on each side.
 
 value = algorithmic bytes of the timed steps / their time (GB/s), where a
 call's algorithmic bytes are what the method must move: packed weights
@@ -65,17 +66,19 @@ def quantize_bytes(m, k):
 
 
 def source_digest():
+    """Digest of the sources of the tile-layout small-m kernel."""
     h = hashlib.sha256()
-    for f in ("small_m.hip", "pq2_device.h"):
+    for f in ("tiles.hip", "small_m_common.h", "pq2_device.h"):
         with open(os.path.join(ROOT, "gemm_int8_act_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(digest):
-    """HBM bytes per launch of the small-m kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "small_m_qkv_traffic.txt")
+    """HBM bytes per launch of the tile-layout small-m kernel from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel source."""
+    path = os.path.join(ROOT, "profiles", "small_m_tiles_qkv_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -179,16 +182,21 @@ def main():
     n, k, ms = w.n, w.k, (1, 2, 3, 4)
     raw_np, x_cpu = workloads.workload_inputs("qkv")
     wb = weight_bytes(n, k)
+    tb = pq2.pq2_tiles_bytes(n, k)
     copies = max(2, math.ceil(ROTATION_BYTES / wb))
-    log(f"[bench] qkv K={k} N={n} weights {wb} B, {copies} plane copies ({copies * wb / 2**30:.2f} GiB)")
+    log(f"[bench] qkv K={k} N={n} weights {wb} B, {copies} copies per layout "
+        f"({copies * wb / 2**30:.2f} GiB planes, {copies * tb / 2**30:.2f} GiB tiles)")
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         raw = torch.from_numpy(raw_np).to(dev)
         pool = torch.empty((copies, wb), dtype=torch.uint8, device=dev)
-        pq2.pq2_prepare_planes(raw, n, k, pool[0])
+        tpool = torch.empty((copies, tb), dtype=torch.uint8, device=dev)
+        pq2.pq2_prepare_planes(raw, n, k, pool[0], stream=stream)
+        pq2.pq2_prepare_tiles(raw, n, k, tpool[0], stream=stream)
         for c in range(1, copies):
             pool[c].copy_(pool[0])
+            tpool[c].copy_(tpool[0])
         x = x_cpu.to(dev)
         bufs = {}
         pbufs = {}
@@ -207,7 +215,7 @@ def main():
             for m in ms:
                 q, xs, y = bufs[m]
                 pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
-                pq2.pq2_matmul_small_m(q, xs, pool[c], y, stream=stream)
+                pq2.pq2_matmul_small_m_tiles(q, xs, tpool[c], y, stream=stream)
         return f
 
     step_graphs = [Graph(torch, step_fn(c), stream) for c in range(copies)]
@@ -230,66 +238,80 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     for y in (bufs[m][2] for m in ms):
         assert torch.isfinite(y).all(), "non-finite output"
+    del step_graphs
 
-    # Per-M call timings: graphs of `copies` back-to-back launches, one per copy.
+    # Per-M call timings: graphs of `copies` back-to-back calls, one per copy.
     per_m = {}
     reps = args.reps
+
+    def per_call_us(body):
+        return time_graph(torch, Graph(torch, body, stream), stream, reps) / copies * 1e3
+
     for m in ms:
         q, xs, y = bufs[m]
-
-        def mm(m=m, q=q, xs=xs, y=y):
-            for c in range(copies):
-                pq2.pq2_matmul_small_m(q, xs, pool[c], y, stream=stream)
-
-        def full(m=m, q=q, xs=xs, y=y):
-            for c in range(copies):
-                pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
-                pq2.pq2_matmul_small_m(q, xs, pool[c], y, stream=stream)
-
         qp, pxs, qsum, py = pbufs[m]
+        ys = {key: torch.empty((m, n), dtype=torch.float32, device=dev)
+              for key in ("planes", "tiles_fused", "planes_fused")}
+        xm = x[:m]
 
-        def mm_planes(m=m, qp=qp, pxs=pxs, qsum=qsum, py=py):
-            for c in range(copies):
-                pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
+        def calls(kind, m=m, q=q, xs=xs, y=y, qp=qp, pxs=pxs, qsum=qsum, py=py, xm=xm):
+            def body():
+                for c in range(copies):
+                    if kind == "tiles_mm":
+                        pq2.pq2_matmul_small_m_tiles(q, xs, tpool[c], y, stream=stream)
+                    elif kind == "tiles_call":
+                        pq2.pq2_quantize_act_i8(xm, q, xs, stream=stream)
+                        pq2.pq2_matmul_small_m_tiles(q, xs, tpool[c], y, stream=stream)
+                    elif kind == "tiles_fused":
+                        pq2.pq2_matmul_small_m_tiles_fused(xm, tpool[c], ys["tiles_fused"], stream=stream)
+                    elif kind == "planes_mm":
+                        pq2.pq2_matmul_small_m(q, xs, pool[c], ys["planes"], stream=stream)
+                    elif kind == "planes_call":
+                        pq2.pq2_quantize_act_i8(xm, q, xs, stream=stream)
+                        pq2.pq2_matmul_small_m(q, xs, pool[c], ys["planes"], stream=stream)
+                    elif kind == "planes_order_mm":
+                        pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
+                    elif kind == "planes_order_call":
+                        pq2.pq2_quantize_act_i8_planes(xm, qp, pxs, qsum, stream=stream)
+                        pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
+                    elif kind == "planes_fused":
+                        pq2.pq2_matmul_small_m_fused(xm, pool[c], ys["planes_fused"], stream=stream)
+            return body
 
-        def full_planes(m=m, qp=qp, pxs=pxs, qsum=qsum, py=py):
-            for c in range(copies):
-                pq2.pq2_quantize_act_i8_planes(x[:m], qp, pxs, qsum, stream=stream)
-                pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
-
-        yf = torch.empty((m, n), dtype=torch.float32, device=dev)
-
-        def fused(m=m, yf=yf):
-            for c in range(copies):
-                pq2.pq2_matmul_small_m_fused(x[:m], pool[c], yf, stream=stream)
-
-        t_mm = time_graph(torch, Graph(torch, mm, stream), stream, reps) / copies * 1e3
-        t_full = time_graph(torch, Graph(torch, full, stream), stream, reps) / copies * 1e3
-        t_mm_p = time_graph(torch, Graph(torch, mm_planes, stream), stream, reps) / copies * 1e3
-        t_full_p = time_graph(torch, Graph(torch, full_planes, stream), stream, reps) / copies * 1e3
-        t_fused = time_graph(torch, Graph(torch, fused, stream), stream, reps) / copies * 1e3
+        t = {kind: per_call_us(calls(kind)) for kind in
+             ("tiles_mm", "tiles_call", "tiles_fused", "planes_mm", "planes_call", "planes_order_mm",
+              "planes_order_call", "planes_fused")}
         torch.cuda.synchronize()
-        assert torch.equal(py, y), f"plane-order and natural-order outputs differ at M={m}"
-        assert torch.equal(yf, y), f"fused and two-launch outputs differ at M={m}"
-        gbs = matmul_bytes(m, n, k) / (t_mm * 1e-6) / 1e9
+        for key, other in (("planes", ys["planes"]), ("plane order", py), ("tiles fused", ys["tiles_fused"]),
+                           ("planes fused", ys["planes_fused"])):
+            assert torch.equal(other.view(torch.int32), y.view(torch.int32)), \
+                f"{key} output differs from the tile-layout output at M={m}"
+        gbs = matmul_bytes(m, n, k) / (t["tiles_mm"] * 1e-6) / 1e9
+        pgbs = matmul_bytes(m, n, k) / (t["planes_mm"] * 1e-6) / 1e9
         per_m[str(m)] = {
-            "matmul_us": round(t_mm, 3),
+            "matmul_us": round(t["tiles_mm"], 3),
             "matmul_GBps": round(gbs, 1),
             "matmul_pct_peak": round(100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S, 1),
-            "complete_call_us": round(t_full, 3),
-            "planes_matmul_us": round(t_mm_p, 3),
-            "planes_complete_call_us": round(t_full_p, 3),
-            "fused_call_us": round(t_fused, 3),
+            "complete_call_us": round(t["tiles_call"], 3),
+            "fused_call_us": round(t["tiles_fused"], 3),
+            "planes_matmul_us": round(t["planes_mm"], 3),
+            "planes_matmul_GBps": round(pgbs, 1),
+            "planes_complete_call_us": round(t["planes_call"], 3),
+            "planes_fused_call_us": round(t["planes_fused"], 3),
+            "plane_order_matmul_us": round(t["planes_order_mm"], 3),
+            "plane_order_complete_call_us": round(t["planes_order_call"], 3),
             "matmul_bytes": matmul_bytes(m, n, k),
         }
-        log(f"[bench] M={m}: matmul {t_mm:.3f} us ({gbs:.0f} GB/s, "
-            f"{100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S:.1f}% of 8 TB/s), complete call {t_full:.3f} us; "
-            f"plane order: matmul {t_mm_p:.3f} us, complete call {t_full_p:.3f} us; "
-            f"fused quantise+matmul {t_fused:.3f} us")
+        log(f"[bench] M={m}: tiles matmul {t['tiles_mm']:.3f} us ({gbs:.0f} GB/s, "
+            f"{100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S:.1f}% of 8 TB/s), call {t['tiles_call']:.3f}, "
+            f"fused {t['tiles_fused']:.3f}; planes matmul {t['planes_mm']:.3f} ({pgbs:.0f} GB/s), "
+            f"call {t['planes_call']:.3f}, fused {t['planes_fused']:.3f}; plane order matmul "
+            f"{t['planes_order_mm']:.3f}, call {t['planes_order_call']:.3f}")
 
     tot_bytes = sum(v["matmul_bytes"] for v in per_m.values())
     tot_us = sum(v["matmul_us"] for v in per_m.values())
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
+    ptot_us = sum(v["planes_matmul_us"] for v in per_m.values())
     digest = source_digest()
     traffic = stored_traffic(digest)
     roofline = {
@@ -299,10 +321,12 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved * 1e9 / PEAK_HBM_BYTES_PER_S, 4),
         "traffic": traffic,
-        "kernel": "small_m_kernel (pq2_matmul_small_m), mean over one launch each at M=1..4",
+        "kernel": "small_m_tiles_kernel (pq2_matmul_small_m_tiles), mean over one launch each at M=1..4",
         "algorithmic_bytes_per_launch_avg": tot_bytes / len(ms),
         "mean_launch_us": round(tot_us / len(ms), 3),
         "kernel_source_digest": digest,
+        "planes_kernel_achieved": round(tot_bytes / (ptot_us * 1e-6) / 1e9, 1),
+        "planes_kernel_mean_launch_us": round(ptot_us / len(ms), 3),
     }
 
     result = {
@@ -319,9 +343,9 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "attention QKV projection K=5120 N=10240, M=1,2,3,4 (quantise + matmul per M)",
+            "workload": "attention QKV projection K=5120 N=10240, M=1,2,3,4 (quantise + tile-layout matmul per M)",
             "k": k, "n": n, "ms": list(ms),
-            "weight_copies": copies, "rotation_bytes": copies * wb,
+            "weight_copies": copies, "rotation_bytes": copies * tb,
         },
         "us_per_call": per_m,
         "roofline": roofline,
