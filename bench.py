@@ -373,14 +373,19 @@ def calibration_copy(torch, dev, stream):
 
 
 def bench_prefill(torch, pq2, workloads, dev, stream):
-    """MFMA prefill at the gate (N=6144) and up (N=17408) shapes, M=256..1024."""
+    """MFMA prefill at the gate (N=6144) and up (N=17408) shapes, M=256..1024:
+    from the tile layout (the decode step's weights), and from the planes with
+    natural- and plane-order activations; all give the same bits."""
     out = {}
     for name in ("prefill_gate", "prefill_up"):
         w = workloads.WORKLOADS[name]
         raw_np, x_cpu = workloads.workload_inputs(name)
         with torch.cuda.stream(stream):
             planes = torch.empty(weight_bytes(w.n, w.k), dtype=torch.uint8, device=dev)
-            pq2.pq2_prepare_planes(torch.from_numpy(raw_np).to(dev), w.n, w.k, planes)
+            tiles = torch.empty(pq2.pq2_tiles_bytes(w.n, w.k), dtype=torch.uint8, device=dev)
+            raw = torch.from_numpy(raw_np).to(dev)
+            pq2.pq2_prepare_planes(raw, w.n, w.k, planes, stream=stream)
+            pq2.pq2_prepare_tiles(raw, w.n, w.k, tiles, stream=stream)
             x = x_cpu.to(dev)
         torch.cuda.synchronize()
         for m in w.ms:
@@ -401,15 +406,25 @@ def bench_prefill(torch, pq2, workloads, dev, stream):
                 for _ in range(10):
                     pq2.pq2_matmul_prefill_planes(qp, xs, planes, y, stream=stream)
 
+            yt = torch.empty((m, w.n), dtype=torch.float32, device=dev)
+
+            def ft(q=q, xs=xs, yt=yt):
+                for _ in range(10):
+                    pq2.pq2_matmul_prefill_tiles(q, xs, tiles, yt, stream=stream)
+
             t_us = time_graph(torch, Graph(torch, f, stream), stream, 5) / 10 * 1e3
             tp_us = time_graph(torch, Graph(torch, fp, stream), stream, 5) / 10 * 1e3
+            tt_us = time_graph(torch, Graph(torch, ft, stream), stream, 5) / 10 * 1e3
+            torch.cuda.synchronize()
+            assert torch.equal(yt.view(torch.int32), y.view(torch.int32)), f"prefill from tiles differs at M={m}"
             ops = 2.0 * m * w.n * w.k
-            tops = ops / (t_us * 1e-6) / 1e12
-            out[f"{name}_m{m}"] = {"us": round(t_us, 2), "TOPS": round(tops, 1),
+            tops = ops / (tt_us * 1e-6) / 1e12
+            out[f"{name}_m{m}"] = {"us": round(tt_us, 2), "TOPS": round(tops, 1),
                                    "pct_int8_peak": round(100 * tops * 1e12 / PEAK_INT8_OPS_PER_S, 1),
-                                   "planes_us": round(tp_us, 2)}
-            log(f"[bench] {name} M={m}: {t_us:.1f} us, {tops:.0f} TOPS (plane-order input {tp_us:.1f} us)")
-        del planes
+                                   "planes_us": round(t_us, 2), "planes_plane_order_us": round(tp_us, 2)}
+            log(f"[bench] {name} M={m}: tile layout {tt_us:.1f} us, {tops:.0f} TOPS (planes {t_us:.1f} us, "
+                f"planes with plane-order input {tp_us:.1f} us)")
+        del planes, tiles
     return out
 
 

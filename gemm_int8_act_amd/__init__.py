@@ -43,6 +43,8 @@ EXPORTED = (
     "pq2_matmul_small_m_tiles_tuned",
     "pq2_matmul_small_m_tiles_fused",
     "pq2_matmul_small_m_tiles_fused_tuned",
+    "pq2_matmul_prefill_tiles",
+    "pq2_matmul_prefill_tiles_tuned",
     "pq2_matmul_prefill_planes",
     "pq2_matmul_prefill_planes_tuned",
     "pq2_matmul_small_m_fused",
@@ -116,6 +118,10 @@ def _load_library():
     lib.pq2_matmul_small_m_tiles.restype = i32
     lib.pq2_matmul_small_m_tiles_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tiles_tuned.restype = i32
+    lib.pq2_matmul_prefill_tiles.argtypes = [p, p, p, i64, i64, i64, p, p]
+    lib.pq2_matmul_prefill_tiles.restype = i32
+    lib.pq2_matmul_prefill_tiles_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, p]
+    lib.pq2_matmul_prefill_tiles_tuned.restype = i32
     lib.pq2_matmul_small_m_tiles_fused.argtypes = [p, i32, i64, p, i64, i64, i64, p, p]
     lib.pq2_matmul_small_m_tiles_fused.restype = i32
     lib.pq2_matmul_small_m_tiles_fused_tuned.argtypes = [p, i32, i64, p, i64, i64, i64, p, i32, i32, p]
@@ -273,6 +279,16 @@ def pq2_matmul_small_m_tiles(q, xs, tiles, y, stream=None) -> None:
 def pq2_matmul_small_m_tiles_tuned(q, xs, tiles, y, max_waves=0, split=0, stream=None) -> None:
     _check(lib.pq2_matmul_small_m_tiles_tuned(*_tiles_args(q, xs, tiles, y), max_waves, split, _stream(stream)),
            "pq2_matmul_small_m_tiles_tuned")
+
+
+def pq2_matmul_prefill_tiles(q, xs, tiles, y, stream=None) -> None:
+    """pq2_matmul_prefill from the tile layout (same bits)."""
+    _check(lib.pq2_matmul_prefill_tiles(*_tiles_args(q, xs, tiles, y), _stream(stream)), "pq2_matmul_prefill_tiles")
+
+
+def pq2_matmul_prefill_tiles_tuned(q, xs, tiles, y, tile=0, stream=None) -> None:
+    _check(lib.pq2_matmul_prefill_tiles_tuned(*_tiles_args(q, xs, tiles, y), tile, _stream(stream)),
+           "pq2_matmul_prefill_tiles_tuned")
 
 
 def _tiles_fused_args(x, tiles, y):

@@ -291,6 +291,20 @@ int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* plane
                                              (hipStream_t)stream));
 }
 
+int pq2_matmul_prefill_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                                   int64_t k, float* y, int tile, void* stream) {
+    if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, kMaxPrefillM, true)) return rc;
+    if (tile < 0 || tile > 4) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_prefill_tiles(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, y, tile,
+                                                   (hipStream_t)stream));
+}
+
+int pq2_matmul_prefill_tiles(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                             int64_t k, float* y, void* stream) {
+    return pq2_matmul_prefill_tiles_tuned(q, xs, tiles, m, n, k, y, 0, stream);
+}
+
 int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream) {
     return pq2_matmul_prefill_tuned(q, xs, planes, m, n, k, y, 0, stream);

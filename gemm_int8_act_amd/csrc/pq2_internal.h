@@ -77,6 +77,8 @@ int tiles_default_split(int64_t m, int64_t k, int max_waves);
 bool tiles_supported(int64_t k, int max_waves, int split);
 hipError_t launch_small_m_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int max_waves, int split, hipStream_t stream);
+hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                int64_t k, float* y, int tile, hipStream_t stream);
 hipError_t launch_small_m_tiles_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* tiles, int64_t m,
                                       int64_t n, int64_t k, float* y, int max_waves, int split, hipStream_t stream);
 

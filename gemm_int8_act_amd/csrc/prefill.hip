@@ -54,7 +54,13 @@ __device__ __forceinline__ uint32_t lut_plane(uint32_t fields) {
 // measured, this one showed the fewest SQ_LDS_BANK_CONFLICT cycles.
 __device__ __forceinline__ int swz(int i, int t) { return i * 8 + (t ^ ((i >> 1) & 7)); }
 
-template <int BM, int BN, bool PLANE_A>
+// TILES: the weights are in the tile layout of the decode GEMV (16-row
+// tiles of 4352-byte segment units: four 1 KB code blocks, then 256 bytes of
+// scales).  Its 2-bit fields are stored transposed, so the decoded planes of
+// a code dword are natural-order weights and natural-order q is staged as it
+// is (no byte transpose).  Each thread then stages 8-byte pieces: the two
+// code dwords (k-blocks kb and 4 + kb) of one row and group.
+template <int BM, int BN, bool PLANE_A, bool TILES>
 __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__ q,
                                                       const float* __restrict__ xs,
                                                       const uint8_t* __restrict__ codes,
@@ -87,7 +93,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     const int mrows = min(BM, m - mb);
     const int nrows = min(BN, n - nb);
     const auto q_rs = make_rsrc(q + (size_t)mb * k, (uint32_t)(mrows * k));
-    const auto c_rs = make_rsrc(codes + (size_t)nb * k4, (uint32_t)(nrows * k4));
+    // Tile layout: BN is a multiple of 16, so the workgroup's rows are whole
+    // tiles; their units are contiguous, (nb / 16) * S8 units from the start.
+    const int s8 = (groups + 7) / 8;
+    const int tiles_here = (nrows + 15) / 16;
+    const auto c_rs = TILES ? make_rsrc(codes + (size_t)(nb / 16) * s8 * 4352, (uint32_t)(tiles_here * s8 * 4352))
+                            : make_rsrc(codes + (size_t)nb * k4, (uint32_t)(nrows * k4));
     const auto x_rs = make_rsrc(xs + (size_t)mb * groups, (uint32_t)(mrows * groups * 4));
     const auto s_rs = make_rsrc(scales + (size_t)nb * groups, (uint32_t)(nrows * groups * 2));
     uint32_t a_off[AQ];
@@ -97,6 +108,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
         a_off[p] = (uint32_t)((it >> 3) * k + (it & 7) * 16);
     }
     const uint32_t b_off = tid < BI ? (uint32_t)((tid >> 1) * k4 + (tid & 1) * 16) : kBufferOOB;
+    // Tile layout: items it = tid + 256 p (p < BN * 4 / 256) take row it >> 2, k-block it & 3.
+    constexpr int TI = TILES ? BN * 4 / 256 : 1;
+    uint32_t tb_off[TI];
+#pragma unroll
+    for (int p = 0; p < TI; ++p) {
+        const int it = tid + 256 * p;
+        const int row = it >> 2, kbb = it & 3;
+        tb_off[p] = (uint32_t)((row >> 4) * s8 * 4352 + 16 * ((row & 15) + 16 * kbb));
+    }
     const bool s_is_x = tid < BM;
     const bool s_is_w = tid >= 256 - BN;
     const uint32_t s_off = s_is_x ? (uint32_t)(tid * groups * 4)
@@ -104,14 +124,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 
     uint4 areg[AQ];
     uint4 breg;
+    uint2 treg[TI];
     uint32_t sreg;
 
     auto load_stage = [&](int g) {
 #pragma unroll
         for (int p = 0; p < AQ; ++p) areg[p] = buf_load16(q_rs, a_off[p] + (uint32_t)g * 128u);
-        breg = buf_load16(c_rs, b_off == kBufferOOB ? kBufferOOB : b_off + (uint32_t)g * 32u);
+        if constexpr (TILES) {
+            // Unit (tile, g / 8), block (g % 8) / 2, dwords 2 (g % 2) and 2 (g % 2) + 1.
+            const uint32_t goff = (uint32_t)((g >> 3) * 4352 + ((g & 7) >> 1) * 1024 + (g & 1) * 8);
+#pragma unroll
+            for (int p = 0; p < TI; ++p) treg[p] = buf_load8(c_rs, tb_off[p] + goff);
+        } else {
+            breg = buf_load16(c_rs, b_off == kBufferOOB ? kBufferOOB : b_off + (uint32_t)g * 32u);
+        }
         if (s_is_x)
             sreg = buf_load4(x_rs, s_off + (uint32_t)g * 4u);
+        else if constexpr (TILES)
+            sreg = buf_load2(c_rs, s_is_w ? (uint32_t)((((tid - (256 - BN)) >> 4) * s8 + (g >> 3)) * 4352 + 4096 +
+                                                       16 * ((tid - (256 - BN)) & 15) + 2 * (g & 7))
+                                          : kBufferOOB);
         else
             sreg = buf_load2(s_rs, s_off == kBufferOOB ? kBufferOOB : s_off + (uint32_t)g * 2u);
     };
@@ -127,8 +159,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     for (int c = 0; c < 4; ++c) b_slot[c] = swz(tid >> 1, 4 * (tid & 1) + c);
     auto store_stage = [&](int buf) {
 #pragma unroll
-        for (int p = 0; p < AQ; ++p) As[buf][a_slot[p]] = PLANE_A ? areg[p] : to_plane_order(areg[p]);
-        if (tid < BI) {
+        for (int p = 0; p < AQ; ++p) As[buf][a_slot[p]] = (PLANE_A || TILES) ? areg[p] : to_plane_order(areg[p]);
+        if constexpr (TILES) {
+#pragma unroll
+            for (int p = 0; p < TI; ++p) {
+                const int it = tid + 256 * p;
+                const int row = it >> 2, kbb = it & 3;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t d = h ? treg[p].y : treg[p].x;  // weights 16 (4h + kb) .. +15, natural planes
+                    Bs[buf][swz(row, 4 * h + kbb)] =
+                        make_uint4(lut_plane(d & 0x03030303u), lut_plane((d >> 2) & 0x03030303u),
+                                   lut_plane((d >> 4) & 0x03030303u), lut_plane((d >> 6) & 0x03030303u));
+                }
+            }
+        } else if (tid < BI) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t d = word_of(breg, c);
@@ -230,25 +275,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 
 namespace {
 
-template <int BM, int BN, bool PLANE_A>
+template <int BM, int BN, bool PLANE_A, bool TILES>
 hipError_t launch_tile(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
                        int64_t k, float* y, hipStream_t stream) {
-    const uint16_t* scales = reinterpret_cast<const uint16_t*>(planes + n * (k / 4));
+    const uint16_t* scales = TILES ? nullptr : reinterpret_cast<const uint16_t*>(planes + n * (k / 4));
     const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
     clear_stale_error();
-    hipLaunchKernelGGL((prefill_kernel<BM, BN, PLANE_A>), grid, dim3(256), 0, stream, q, xs, planes, scales, y,
-                       (int)m, (int)n, (int)k, (int)(k / 128));
+    hipLaunchKernelGGL((prefill_kernel<BM, BN, PLANE_A, TILES>), grid, dim3(256), 0, stream, q, xs, planes, scales,
+                       y, (int)m, (int)n, (int)k, (int)(k / 128));
     return hipGetLastError();
 }
 
-template <bool PLANE_A>
+template <bool PLANE_A, bool TILES>
 hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
                            int64_t k, float* y, int tile, hipStream_t stream) {
     switch (tile) {
-        case 1: return launch_tile<128, 128, PLANE_A>(q, xs, planes, m, n, k, y, stream);
-        case 2: return launch_tile<64, 128, PLANE_A>(q, xs, planes, m, n, k, y, stream);
-        case 3: return launch_tile<64, 64, PLANE_A>(q, xs, planes, m, n, k, y, stream);
-        case 4: return launch_tile<128, 64, PLANE_A>(q, xs, planes, m, n, k, y, stream);
+        case 1: return launch_tile<128, 128, PLANE_A, TILES>(q, xs, planes, m, n, k, y, stream);
+        case 2: return launch_tile<64, 128, PLANE_A, TILES>(q, xs, planes, m, n, k, y, stream);
+        case 3: return launch_tile<64, 64, PLANE_A, TILES>(q, xs, planes, m, n, k, y, stream);
+        case 4: return launch_tile<128, 64, PLANE_A, TILES>(q, xs, planes, m, n, k, y, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -269,8 +314,14 @@ int default_prefill_tile(int64_t m, int64_t n, bool plane_a) {
 hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
                           int64_t n, int64_t k, float* y, int tile, bool plane_a, hipStream_t stream) {
     if (tile == 0) tile = default_prefill_tile(m, n, plane_a);
-    return plane_a ? launch_any_tile<true>(q, xs, planes, m, n, k, y, tile, stream)
-                   : launch_any_tile<false>(q, xs, planes, m, n, k, y, tile, stream);
+    return plane_a ? launch_any_tile<true, false>(q, xs, planes, m, n, k, y, tile, stream)
+                   : launch_any_tile<false, false>(q, xs, planes, m, n, k, y, tile, stream);
+}
+
+hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                int64_t k, float* y, int tile, hipStream_t stream) {
+    if (tile == 0) tile = default_prefill_tile(m, n, false);
+    return launch_any_tile<false, true>(q, xs, tiles, m, n, k, y, tile, stream);
 }
 
 }  // namespace pq2

@@ -324,6 +324,26 @@ int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row
                                          int64_t m, int64_t n, int64_t k, float* y, int max_waves, int split,
                                          void* stream);
 
+/* Prefill matmul from the tile layout: the definition, limits and output of
+ * pq2_matmul_prefill, and the same bits, with the weights read from the
+ * decode GEMV's tile layout, so one prepared copy serves decode and prefill
+ * (page "Kernel experiments", section H: keeping one weight layout for
+ * every reader).
+ *   q       device int8 [m][k], 16-byte aligned.   xs  device float [m][k/128], 4-byte aligned.
+ *   tiles   device tile layout of the weights, 16-byte aligned.
+ *   y       device float [m][n], 4-byte aligned; fully overwritten; must
+ *           not overlap any input.
+ * Errors: EINVAL (null, overlap), ESHAPE (m outside 1..65535*64, n<1,
+ *         k<128, k%128, k > PQ2_MAX_K), EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_prefill_tiles(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                             int64_t k, float* y, void* stream);
+
+/* Tuning hook for pq2_matmul_prefill_tiles: tile as for
+ * pq2_matmul_prefill_tuned (0 = the library's choice), same bits.  Errors as
+ * pq2_matmul_prefill_tiles, plus EINVAL for tile outside 0..4. */
+int pq2_matmul_prefill_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                                   int64_t k, float* y, int tile, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 22
+    assert len(names) == 24
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -79,7 +79,7 @@ def test_quantize_validation():
 
 
 @pytest.mark.parametrize("name", ["pq2_matmul_small_m", "pq2_matmul_prefill", "pq2_matmul_prefill_planes",
-                                  "pq2_matmul_small_m_tiles"])
+                                  "pq2_matmul_small_m_tiles", "pq2_matmul_prefill_tiles"])
 def test_matmul_validation(name):
     f = getattr(pq2.lib, name)
     assert f(None, B, C, 1, 8, 128, D, None) == EINVAL
@@ -179,6 +179,7 @@ def test_prefill_tile_validation():
     t = pq2.lib.pq2_matmul_prefill_tuned
     assert t(A, B, C, 1, 8, 128, D, 5, None) == EINVAL
     assert pq2.lib.pq2_matmul_prefill_planes_tuned(A, B, C, 1, 8, 128, D, 5, None) == EINVAL
+    assert pq2.lib.pq2_matmul_prefill_tiles_tuned(A, B, C, 1, 8, 128, D, 5, None) == EINVAL
     assert pq2.lib.pq2_matmul_prefill_planes(A + 8, B, C, 1, 8, 128, D, None) == EALIGN
     assert t(A, B, C, 1, 8, 128, D, -1, None) == EINVAL
     assert t(A, B, C, 0, 8, 128, D, 1, None) == ESHAPE

@@ -404,6 +404,8 @@ def test_prefill_full(m, n, k):
     y = gpu_matmul(_pq2().pq2_matmul_prefill, q, xs, gpu_planes(raw, n, k), n)
     y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
     assert_within(y, y_ref, bound, f"prefill m={m} n={n} k={k}")
+    yt = gpu_matmul(_pq2().pq2_matmul_prefill_tiles, q, xs, gpu_tiles(raw, n, k), n)
+    assert np.array_equal(yt.view(np.uint32), y.view(np.uint32)), "prefill from the tile layout differs"
 
 
 @pytest.mark.parametrize("name", ["prefill_gate", "prefill_up"])
@@ -411,6 +413,7 @@ def test_prefill_workloads_sampled(name):
     pq2 = _pq2()
     w, raw, x = workload_case(name)
     planes = gpu_planes(raw, w.n, w.k)
+    tiles = gpu_tiles(raw, w.n, w.k)
     for m in w.ms:
         announce(f"prefill workload {name} m={m}")
         q, xs, qo, xso = quantise_both(x[:m].contiguous())
@@ -419,6 +422,8 @@ def test_prefill_workloads_sampled(name):
         qp, xsp, _ = gpu_quantize_planes(x[:m].contiguous().to(DEV))
         yp = gpu_matmul(pq2.pq2_matmul_prefill_planes, qp, xsp, planes, w.n)
         assert np.array_equal(yp.view(np.uint32), y.view(np.uint32)), "plane-order prefill differs"
+        yt = gpu_matmul(pq2.pq2_matmul_prefill_tiles, q, xs, tiles, w.n)
+        assert np.array_equal(yt.view(np.uint32), y.view(np.uint32)), "prefill from the tile layout differs"
         rng = np.random.default_rng(m)
         mi = np.concatenate([[0, m - 1, 0, m - 1], rng.integers(0, m, 1500)])
         ni = np.concatenate([[0, 0, w.n - 1, w.n - 1], rng.integers(0, w.n, 1500)])
@@ -454,6 +459,8 @@ def test_prefill_tiles(tile):
     qp, xsp, _ = gpu_quantize_planes(x.to(DEV))
     yp = gpu_matmul(pq2.pq2_matmul_prefill_planes_tuned, qp, xsp, planes, n, tile=tile)
     assert np.array_equal(yp.view(np.uint32), y0.view(np.uint32)), "plane-order prefill changed the bits"
+    yt = gpu_matmul(pq2.pq2_matmul_prefill_tiles_tuned, q, xs, gpu_tiles(raw, n, k), n, tile=tile)
+    assert np.array_equal(yt.view(np.uint32), y0.view(np.uint32)), "prefill from the tile layout changed the bits"
 
 
 def test_prefill_matches_small_m():
