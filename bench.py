@@ -16,8 +16,10 @@ same output bits, which the run checks.  Weight preparation
 (pq2_prepare_tiles / pq2_prepare_planes) is one-time and outside the timing.
 Every step reads the next of R weight copies (>= 1 GiB in total per layout,
 four times the 256 MB Infinity Cache), so weights stream from HBM.  Steps
-are captured as HIP graphs (one per copy) and replayed; K steps are timed
-with HIP events between a synchronize on each side.
+are captured as HIP graphs (one graph of R consecutive steps, as a decode
+loop runs its calls inside one larger graph, and one of the remainder) and
+replayed; exactly K steps are timed with HIP events between a synchronize
+on each side.
 
 value = algorithmic bytes of the timed steps / their time (GB/s), where a
 call's algorithmic bytes are what the method must move: packed weights
@@ -218,27 +220,43 @@ def main():
                 pq2.pq2_matmul_small_m_tiles(q, xs, tpool[c], y, stream=stream)
         return f
 
-    step_graphs = [Graph(torch, step_fn(c), stream) for c in range(copies)]
+    # One graph holds `copies` consecutive steps (step i reads copy i), as a
+    # decode loop runs its calls inside one larger graph; a second graph of
+    # the first r steps makes the count exact.
+    def steps_fn(count):
+        def f():
+            for c in range(count):
+                step_fn(c)()
+        return f
+
+    def run_steps(count, graphs):
+        full, rest = divmod(count, copies)
+        for _ in range(full):
+            graphs[copies].replay()
+        if rest:
+            graphs[rest].replay()
+
     step_bytes = sum(quantize_bytes(m, k) + matmul_bytes(m, n, k) for m in ms)
+    graphs = {copies: Graph(torch, steps_fn(copies), stream)}
+    for count in {args.warmup % copies, args.steps % copies} - {0}:
+        graphs[count] = Graph(torch, steps_fn(count), stream)
 
     # Warmup, then exactly K timed steps.
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step_graphs[i % copies].replay()
+        run_steps(args.warmup, graphs)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         start.record(stream)
-        for i in range(args.steps):
-            step_graphs[(args.warmup + i) % copies].replay()
+        run_steps(args.steps, graphs)
         end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     for y in (bufs[m][2] for m in ms):
         assert torch.isfinite(y).all(), "non-finite output"
-    del step_graphs
+    del graphs
 
     # Per-M call timings: graphs of `copies` back-to-back calls, one per copy.
     per_m = {}
