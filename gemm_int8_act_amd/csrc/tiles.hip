@@ -127,6 +127,15 @@ __global__ void prepare_tile_scales_kernel(const uint8_t* __restrict__ raw, int6
 
 __device__ __forceinline__ void keep_order() { __builtin_amdgcn_sched_barrier(0); }
 
+// j mod mcount for j < 16 and mcount = 1..4 (mcount is uniform), without
+// the generic integer division.
+__device__ __forceinline__ int small_mod(int j, int mcount) {
+    if (mcount == 4) return j & 3;
+    if (mcount == 3) return j - 3 * ((j * 11) >> 5);  // (j * 11) >> 5 == j / 3 for j < 16
+    if (mcount == 2) return j & 1;
+    return 0;
+}
+
 // Per-wave LDS: MC staged columns of CPW groups and a spare column (each
 // padded by 64 bytes: the columns of one A read fall in distinct banks), then
 // 8 x 8 floats of xs and 8 x 8 ints of -sum(q) (group class x column).
@@ -170,19 +179,6 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     const int seg_begin = slice * per_wave;
     const int seg_end = min(seg_begin + per_wave, nseg);
 
-    // Private region: MC staged columns (CPW groups each) and one column that
-    // takes the stores of lanes past the last column, then per class c of the
-    // wave 8 floats xs[c][m] and 8 ints -sum(q)[c][m].
-    unsigned char* region = smem + (size_t)wave * tiles_region_bytes(MC, CPW);
-    float* red = reinterpret_cast<float*>(smem + (size_t)nwaves * tiles_region_bytes(MC, CPW));
-    float* xs_lds = reinterpret_cast<float*>(region + (MC + 1) * PITCH);
-    int* nsq_lds = reinterpret_cast<int*>(region + (MC + 1) * PITCH + 256);
-    // A row i reads column i mod mcount: rows >= mcount repeat real columns,
-    // so one read touches at most 4 x 16 distinct banks, and the D rows they
-    // produce are never used.
-    const unsigned char* a_base = region + (j % mcount) * PITCH + 16 * kb;
-    nsq_lds[lane] = 0;
-
     const auto tile_rs = make_rsrc(tiles + (size_t)tile * s8 * kSegUnit, (uint32_t)(s8 * kSegUnit));
     const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
     const auto xs_rs = make_rsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
@@ -192,20 +188,19 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     // Staging roles: chunk ch of column (load t) * COLS_PER_LOAD + sub.
     const int ch = lane % CHUNKS;
     const int sub = lane / CHUNKS;
+    const int xm = lane >> 3, xc = lane & 7;
 
-    float acc[CPW][MC];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c)
-#pragma unroll
-        for (int r = 0; r < MC; ++r) acc[c][r] = 0.0f;
-
-    for (int s = seg_begin; s < seg_end; ++s) {
-        // 1. This segment's activation chunks for the wave's classes and xs
-        //    (lane l: column l >> 3, group l & 7), then the code blocks and
-        //    weight scales, all in flight together.  Groups past the end read
-        //    zeros.
-        uint4 qv[QLOADS];
-        uint4 xv[QLOADS][FUSED ? XL : 1];
+    // 1. One segment's loads: the activation chunks of the wave's classes
+    //    and xs (lane l: column l >> 3, group l & 7), then the weight scales,
+    //    then the code blocks in use order (loads complete in order, so the
+    //    first group pair can start while the later blocks are in flight).
+    //    Groups past the end read zeros.
+    uint4 qv[QLOADS];
+    uint4 xv[QLOADS][FUSED ? XL : 1];
+    uint32_t xsw;
+    uint4 wsv;
+    uint4 cw[CPW / 2];
+    auto issue = [&](int s) {
         const uint32_t qoff = (uint32_t)(s * 1024 + 128 * c_lo + 16 * ch);  // element offset in the row
 #pragma unroll
         for (int t = 0; t < QLOADS; ++t) {
@@ -219,20 +214,41 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
                 qv[t] = buf_load16(q_rs, ok ? (uint32_t)(m * k) + qoff : kBufferOOB);
             }
         }
-        const int xm = lane >> 3, xc = lane & 7;
-        const uint32_t xsw = FUSED ? 0u
-                                   : buf_load4(xs_rs, (xm < mcount && 8 * s + xc < groups)
-                                                          ? (uint32_t)((xm * groups + 8 * s + xc) * 4) : kBufferOOB);
+        xsw = FUSED ? 0u
+                    : buf_load4(xs_rs, (xm < mcount && 8 * s + xc < groups) ? (uint32_t)((xm * groups + 8 * s + xc) * 4)
+                                                                            : kBufferOOB);
         const uint32_t unit_off = (uint32_t)(s * kSegUnit);
-        const uint4 wsv = buf_load16(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
+        wsv = buf_load16(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
         keep_order();
-        // Code blocks last and in use order: loads complete in order, so the
-        // first group pair can start while the later blocks are in flight.
-        uint4 cw[CPW / 2];
 #pragma unroll
         for (int b = 0; b < CPW / 2; ++b)
             cw[b] = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + (c_lo / 2 + b) * kCodeBlock + 16 * lane);
         keep_order();
+    };
+    // Private region: MC staged columns (CPW groups each) and one column that
+    // takes the stores of lanes past the last column, then per class c of the
+    // wave 8 floats xs[c][m] and 8 ints -sum(q)[c][m].
+    unsigned char* region = smem + (size_t)wave * tiles_region_bytes(MC, CPW);
+    float* red = reinterpret_cast<float*>(smem + (size_t)nwaves * tiles_region_bytes(MC, CPW));
+    float* xs_lds = reinterpret_cast<float*>(region + (MC + 1) * PITCH);
+    int* nsq_lds = reinterpret_cast<int*>(region + (MC + 1) * PITCH + 256);
+    // A row i reads column i mod mcount: rows >= mcount repeat real columns,
+    // so one read touches at most 4 x 16 distinct banks, and the D rows they
+    // produce are never used.
+    const unsigned char* a_base = region + small_mod(j, mcount) * PITCH + 16 * kb;
+    nsq_lds[lane] = 0;
+
+    float acc[CPW][MC];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int r = 0; r < MC; ++r) acc[c][r] = 0.0f;
+
+    // Every wave has at least one segment (slice * per_wave < nseg), so the
+    // loop has no zero-trip test and the kernel arguments load in one go.
+    int s = seg_begin;
+    do {
+        issue(s);
 
         // 2. Stage the activations, xs and each group's -sum(q) (dot4 against
         //    ones over the lane's 16 bytes, then the 8 lanes of the group).
@@ -306,7 +322,7 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
         // The next segment rewrites the region: every lane's reads of this one
         // are done (LDS operations of one wave complete in order).
         __builtin_amdgcn_wave_barrier();
-    }
+    } while (++s < seg_end);
 
     // 4. Class sums ((A0+A4)+(A1+A5))+((A2+A6)+(A3+A7)) per slice, then the
     //    slices in index order.  D row 4*kb + r is column 4*kb + r, so the
@@ -332,13 +348,20 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
             for (int r = 0; r < MC; ++r) red[(wave * MC + r) * kTileRows + j] = part[r];
         }
         __syncthreads();
-        for (int o = threadIdx.x; o < MC * kTileRows; o += blockDim.x) {
-            const int r = o / kTileRows;
-            const int jj = o - r * kTileRows;
-            float sum = red[r * kTileRows + jj];
-            for (int w = 1; w < nwaves; ++w) sum += red[(w * MC + r) * kTileRows + jj];
-            const int rr = tile * kTileRows + jj;
-            if (r < mcount && rr < n) y[(size_t)(m0 + r) * n + rr] = sum;
+        // Wave 0 adds the slices in index order.  All reads go out before the
+        // first add; slots past the last slice re-read the last one and are
+        // not added.
+        if (wave == 0 && lane < MC * kTileRows) {
+            const int r = lane >> 4;
+            float v[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) v[w] = red[(min(w, nwaves - 1) * MC + r) * kTileRows + j];
+            float sum = v[0];
+#pragma unroll
+            for (int w = 1; w < 8; ++w)
+                if (w < nwaves) sum += v[w];
+            const int row = tile * kTileRows + j;
+            if (r < mcount && row < n) y[(size_t)(m0 + r) * n + row] = sum;
         }
         return;
     }
@@ -349,18 +372,21 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
             for (int r = 0; r < MC; ++r) red[((slice * 8 + c_lo + c) * MC + r) * kTileRows + j] = acc[c][r];
     }
     __syncthreads();
-    for (int o = threadIdx.x; o < MC * kTileRows; o += blockDim.x) {
-        const int r = o / kTileRows;
-        const int jj = o - r * kTileRows;
-        float sum = 0.0f;
-        for (int w = 0; w < nslices; ++w) {
-            const float* a = red + ((size_t)w * 8 * MC + r) * kTileRows + jj;
-            constexpr int C = MC * kTileRows;  // stride between classes
-            const float t = ((a[0] + a[4 * C]) + (a[1 * C] + a[5 * C])) + ((a[2 * C] + a[6 * C]) + (a[3 * C] + a[7 * C]));
-            sum = w == 0 ? t : sum + t;
+    if (wave == 0 && lane < MC * kTileRows) {
+        const int r = lane >> 4;
+        constexpr int C = MC * kTileRows;  // stride between classes
+        float t[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const float* a = red + ((size_t)min(w, nslices - 1) * 8 * MC + r) * kTileRows + j;
+            t[w] = ((a[0] + a[4 * C]) + (a[1 * C] + a[5 * C])) + ((a[2 * C] + a[6 * C]) + (a[3 * C] + a[7 * C]));
         }
-        const int rr = tile * kTileRows + jj;
-        if (r < mcount && rr < n) y[(size_t)(m0 + r) * n + rr] = sum;
+        float sum = t[0];
+#pragma unroll
+        for (int w = 1; w < 8; ++w)
+            if (w < nslices) sum += t[w];
+        const int row = tile * kTileRows + j;
+        if (r < mcount && row < n) y[(size_t)(m0 + r) * n + row] = sum;
     }
 }
 
