@@ -150,6 +150,42 @@ __device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t
     return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 
+// Scalar buffer loads (uniform offset, results in SGPRs): the same range
+// check, dword by dword, without a slot in the vector memory queue.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+extern "C" __device__ float pq2_sbuf_load_f32(i32x4_t rsrc, int off, int aux) __asm("llvm.amdgcn.s.buffer.load.f32");
+extern "C" __device__ f32x2_t pq2_sbuf_load_f32x2(i32x4_t rsrc, int off, int aux) __asm("llvm.amdgcn.s.buffer.load.v2f32");
+extern "C" __device__ f32x4_t pq2_sbuf_load_f32x4(i32x4_t rsrc, int off, int aux) __asm("llvm.amdgcn.s.buffer.load.v4f32");
+extern "C" __device__ f32x8_t pq2_sbuf_load_f32x8(i32x4_t rsrc, int off, int aux) __asm("llvm.amdgcn.s.buffer.load.v8f32");
+
+__device__ __forceinline__ i32x4_t make_srsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)bytes, kBufferFlags};
+}
+
+// N = 1, 2, 4 or 8 consecutive floats at byte offset off (a multiple of 4).
+template <int N>
+__device__ __forceinline__ void sbuf_load_f32(i32x4_t r, int off, float* out) {
+    if constexpr (N == 8) {
+        const f32x8_t v = pq2_sbuf_load_f32x8(r, off, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = v[i];
+    } else if constexpr (N == 4) {
+        const f32x4_t v = pq2_sbuf_load_f32x4(r, off, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = v[i];
+    } else if constexpr (N == 2) {
+        const f32x2_t v = pq2_sbuf_load_f32x2(r, off, 0);
+        out[0] = v[0];
+        out[1] = v[1];
+    } else {
+        out[0] = pq2_sbuf_load_f32(r, off, 0);
+    }
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

@@ -181,23 +181,21 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
 
     const auto tile_rs = make_rsrc(tiles + (size_t)tile * s8 * kSegUnit, (uint32_t)(s8 * kSegUnit));
     const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
-    const auto xs_rs = make_rsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
+    const i32x4_t xs_srs = make_srsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
     const auto x_rs = make_rsrc(
         FUSED ? static_cast<const unsigned char*>(x) + (size_t)m0 * x_stride * src_esize(SRC) : nullptr,
         FUSED ? (uint32_t)(((int64_t)(mcount - 1) * x_stride + k) * src_esize(SRC)) : 0u);
     // Staging roles: chunk ch of column (load t) * COLS_PER_LOAD + sub.
     const int ch = lane % CHUNKS;
     const int sub = lane / CHUNKS;
-    const int xm = lane >> 3, xc = lane & 7;
 
-    // 1. One segment's loads: the activation chunks of the wave's classes
-    //    and xs (lane l: column l >> 3, group l & 7), then the weight scales,
-    //    then the code blocks in use order (loads complete in order, so the
-    //    first group pair can start while the later blocks are in flight).
-    //    Groups past the end read zeros.
+    // 1. One segment's loads: the activation chunks of the wave's classes,
+    //    then the weight scales, then the code blocks in use order (loads
+    //    complete in order, so the first group pair can start while the later
+    //    blocks are in flight), then xs.  Groups past the end read zeros.
     uint4 qv[QLOADS];
     uint4 xv[QLOADS][FUSED ? XL : 1];
-    uint32_t xsw;
+    float xss[FUSED ? 1 : MC][CPW];  // xs of the wave's groups, scalar loads (uniform)
     uint4 wsv;
     uint4 cw[CPW / 2];
     auto issue = [&](int s) {
@@ -214,9 +212,6 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
                 qv[t] = buf_load16(q_rs, ok ? (uint32_t)(m * k) + qoff : kBufferOOB);
             }
         }
-        xsw = FUSED ? 0u
-                    : buf_load4(xs_rs, (xm < mcount && 8 * s + xc < groups) ? (uint32_t)((xm * groups + 8 * s + xc) * 4)
-                                                                            : kBufferOOB);
         const uint32_t unit_off = (uint32_t)(s * kSegUnit);
         wsv = buf_load16(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
         keep_order();
@@ -224,6 +219,24 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
         for (int b = 0; b < CPW / 2; ++b)
             cw[b] = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + (c_lo / 2 + b) * kCodeBlock + 16 * lane);
         keep_order();
+        if constexpr (!FUSED) {
+            // xs of the wave's groups: uniform offsets, so the scalar unit
+            // fetches them, outside the vector memory queue.  Columns past
+            // the last re-read it (their D rows are never used).  A segment
+            // that runs past the last group reads dword by dword, so the
+            // missing groups read zero and the others their values.
+            const int g0 = 8 * s + c_lo;
+#pragma unroll
+            for (int r = 0; r < MC; ++r) {
+                const int off = (min(r, mcount - 1) * groups + g0) * 4;
+                if (g0 + CPW <= groups) {
+                    sbuf_load_f32<CPW>(xs_srs, off, xss[r]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CPW; ++c) sbuf_load_f32<1>(xs_srs, off + 4 * c, &xss[r][c]);
+                }
+            }
+        }
     };
     // Private region: MC staged columns (CPW groups each) and one column that
     // takes the stores of lanes past the last column, then per class c of the
@@ -253,7 +266,6 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
         // 2. Stage the activations, xs and each group's -sum(q) (dot4 against
         //    ones over the lane's 16 bytes, then the 8 lanes of the group).
         //    Lanes past the last column write their (zero) chunk to the spare column.
-        if constexpr (!FUSED) xs_lds[xc * 8 + xm] = __uint_as_float(xsw);
 #pragma unroll
         for (int t = 0; t < QLOADS; ++t) {
             const int m = t * COLS_PER_LOAD + sub;
@@ -298,7 +310,7 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
                 A[p][1] = v4i{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
                 const int4 nsq = *reinterpret_cast<const int4*>(nsq_lds + (c_lo + c) * 8);
                 D[p] = v4i{nsq.x, nsq.y, nsq.z, nsq.w};
-                xsg[p] = *reinterpret_cast<const float4*>(xs_lds + (c_lo + c) * 8);
+                if constexpr (FUSED) xsg[p] = *reinterpret_cast<const float4*>(xs_lds + (c_lo + c) * 8);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const uint32_t d = word_of(cw[c >> 1], 2 * (c & 1) + h);
@@ -314,7 +326,13 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
             for (int p = 0; p < 2; ++p) {
                 const int c = c0 + p;
                 const float wsf = half_of(wsv, c_lo + c);
-                const float xv[4] = {xsg[p].x, xsg[p].y, xsg[p].z, xsg[p].w};
+                float xv[4];
+                if constexpr (FUSED) {
+                    xv[0] = xsg[p].x; xv[1] = xsg[p].y; xv[2] = xsg[p].z; xv[3] = xsg[p].w;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < MC; ++r) xv[r] = xss[r][c];
+                }
 #pragma unroll
                 for (int r = 0; r < MC; ++r) acc[c][r] = __builtin_fmaf((float)D[p][r] * xv[r], wsf, acc[c][r]);
             }
