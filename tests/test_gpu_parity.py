@@ -390,6 +390,35 @@ def test_small_m_tiles_workloads(name):
         assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), f"{name} m={m}: tiles differ from planes"
 
 
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_small_m_repeatable(name):
+    """48 back-to-back launches of each decode path, every one with its own
+    output buffer, give the same bits as the first (an intermittent hazard
+    or race would show up as a differing launch)."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    tiles, planes = gpu_tiles(raw, w.n, w.k), gpu_planes(raw, w.n, w.k)
+    reps = 48
+    for m in w.ms:
+        announce(f"repeatable {name} m={m}")
+        q, xs, _, _ = quantise_both(x[:m].contiguous())
+        xd = x[:m].contiguous().to(DEV)
+        calls = {
+            "tiles": lambda out: pq2.pq2_matmul_small_m_tiles(q, xs, tiles, out),
+            "tiles fused": lambda out: pq2.pq2_matmul_small_m_tiles_fused(xd, tiles, out),
+            "planes": lambda out: pq2.pq2_matmul_small_m(q, xs, planes, out),
+        }
+        for what, call in calls.items():
+            ys = torch.full((reps, m, w.n), float("nan"), dtype=torch.float32, device=DEV)
+            for i in range(reps):
+                call(ys[i])
+            torch.cuda.synchronize()
+            bits = ys.view(torch.int32)
+            same = (bits == bits[0:1]).all(dim=(1, 2)).cpu().numpy()
+            assert same.all(), f"{name} m={m} {what}: launches {np.nonzero(~same)[0].tolist()} differ from the first"
+            assert torch.isfinite(ys[0]).all(), f"{name} m={m} {what}: unwritten outputs"
+
+
 # ------------------------------------------------------------------ prefill
 PREFILL_SHAPES = [(1, 64, 128), (5, 200, 640), (128, 128, 1024), (130, 257, 384), (300, 96, 5120),
                   (257, 513, 2048)]
