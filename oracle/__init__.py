@@ -65,6 +65,12 @@ def _load():
     lib.oracle_matmul_raw.restype = i32
     lib.oracle_matmul_raw_sample.argtypes = [p, p, p, i64, i64, i64, i64, p, p, i64, p, p]
     lib.oracle_matmul_raw_sample.restype = i32
+    lib.oracle_quantize_act_i8_g.argtypes = [p, i32, i64, i64, i64, i64, p, p]
+    lib.oracle_quantize_act_i8_g.restype = i32
+    lib.oracle_matmul_raw_g.argtypes = [p, p, p, i64, i64, i64, i64, i64, p, p]
+    lib.oracle_matmul_raw_g.restype = i32
+    lib.oracle_matmul_raw_sample_g.argtypes = [p, p, p, i64, i64, i64, i64, i64, p, p, i64, p, p]
+    lib.oracle_matmul_raw_sample_g.restype = i32
     _lib = lib
     return lib
 
@@ -165,4 +171,60 @@ def matmul_raw_sample(q, xs, raw, n: int, k: int, mi, ni):
                                           _ptr(mi), _ptr(ni), count, _ptr(y), _ptr(bound))
     if rc:
         raise ValueError("oracle_matmul_raw_sample: bad shape or index")
+    return y, bound
+
+
+# ---------------------------------------------------------------- smaller activation groups
+# Page "Kernel experiments: recorded evidence", section C (Diagram 3, Tests 8
+# and 9): weight blocks stay 128 weights with one fp16 scale; activations get
+# one scale per `agroup` = 128, 64 or 32 elements.
+AGROUPS = (128, 64, 32)
+
+
+def quantize_act_i8_g(x_bits: np.ndarray, agroup: int, dtype: str = "bf16", k: int | None = None):
+    """Quantisation in activation groups of ``agroup`` elements.  Returns
+    (q int8 [m][k], xs float32 [m][k/agroup])."""
+    code = DTYPE_CODES[dtype]
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.float32 if code == 2 else np.uint16)
+    m, width = x_bits.shape
+    k = width if k is None else k
+    q = np.empty((m, k), dtype=np.int8)
+    xs = np.empty((m, k // agroup if agroup else 0), dtype=np.float32)
+    rc = _load().oracle_quantize_act_i8_g(_ptr(x_bits), code, width, m, k, agroup, _ptr(q), _ptr(xs))
+    if rc:
+        raise ValueError("oracle_quantize_act_i8_g: bad shape or group")
+    return q, xs
+
+
+def matmul_raw_g(q: np.ndarray, xs: np.ndarray, raw: np.ndarray, n: int, k: int, agroup: int):
+    """y[m][n] (float64) and bound[m][n] with activation groups of ``agroup``."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    m = q.shape[0]
+    assert q.shape == (m, k) and xs.shape == (m, k // agroup) and raw.shape[0] == n
+    y = np.empty((m, n), dtype=np.float64)
+    bound = np.empty((m, n), dtype=np.float64)
+    rc = _load().oracle_matmul_raw_g(_ptr(q), _ptr(xs), _ptr(raw), raw.shape[1], m, n, k, agroup, _ptr(y),
+                                     _ptr(bound))
+    if rc:
+        raise ValueError("oracle_matmul_raw_g: bad shape or group")
+    return y, bound
+
+
+def matmul_raw_sample_g(q, xs, raw, n: int, k: int, agroup: int, mi, ni):
+    """Selected outputs y[mi[c]][ni[c]] and bounds with activation groups of ``agroup``."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    m = q.shape[0]
+    count = mi.shape[0]
+    y = np.empty(count, dtype=np.float64)
+    bound = np.empty(count, dtype=np.float64)
+    rc = _load().oracle_matmul_raw_sample_g(_ptr(q), _ptr(xs), _ptr(raw), raw.shape[1], m, n, k, agroup,
+                                            _ptr(mi), _ptr(ni), count, _ptr(y), _ptr(bound))
+    if rc:
+        raise ValueError("oracle_matmul_raw_sample_g: bad shape, group or index")
     return y, bound

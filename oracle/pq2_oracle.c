@@ -248,3 +248,90 @@ int oracle_matmul_raw_sample(const int8_t* q, const float* xs, const uint8_t* ra
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Smaller activation groups ([KE] section C, Diagram 3, Tests 8 and 9): the
+ * weights keep their 128-weight blocks and one fp16 scale per block, while
+ * each activation row is quantised in groups of `agroup` = 128, 64 or 32
+ * elements, every group with its own scale max|x|/127 (the same steps as
+ * above, on the smaller group).  A weight block then spans 128/agroup
+ * activation groups; the integer dot of each activation group against the
+ * block's codes is scaled by that group's xs and the block's ws, and all
+ * these terms are summed.  agroup = 128 is the group-128 definition above.
+ */
+static int valid_agroup(int64_t agroup) { return agroup == 128 || agroup == 64 || agroup == 32; }
+
+/* q is [m][k] int8; xs is [m][k/agroup] float. */
+int oracle_quantize_act_i8_g(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,
+                             int64_t agroup, int8_t* q, float* xs) {
+    if (k <= 0 || k % GROUP || m <= 0 || row_stride < k || !valid_agroup(agroup)) return 1;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F16 && dtype != ORACLE_F32) return 1;
+    int64_t ngroups = k / agroup;
+    for (int64_t row = 0; row < m; ++row) {
+        for (int64_t a = 0; a < ngroups; ++a) {
+            int64_t base = row * row_stride + a * agroup;
+            float amax = 0.0f;
+            for (int64_t i = 0; i < agroup; ++i) {
+                float v = fabsf(load_activation(x, dtype, base + i));
+                if (v > amax) amax = v;
+            }
+            float scale = amax / 127.0f;               /* one IEEE FP32 division */
+            float divisor = scale > 0.0f ? scale : 1.0f;
+            for (int64_t i = 0; i < agroup; ++i) {
+                float v = load_activation(x, dtype, base + i);
+                float r = nearbyintf(v / divisor);     /* ties to even (FE_TONEAREST) */
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                q[row * k + a * agroup + i] = (int8_t)r;
+            }
+            xs[row * ngroups + a] = scale;
+        }
+    }
+    return 0;
+}
+
+/* One output with activation groups of `agroup`, plus its acceptance bound
+ * (the same form as the group-128 bound, over every scaled term). */
+static void one_output_g(const int8_t* q, const float* xs, const uint8_t* raw, int64_t row_stride,
+                         int64_t k, int64_t agroup, int64_t mi, int64_t ni, double* y, double* bound) {
+    int64_t blocks = k / GROUP, per_block = GROUP / agroup, ngroups = k / agroup;
+    double acc = 0.0, mag = 0.0;
+    for (int64_t g = 0; g < blocks; ++g) {
+        const uint8_t* block = raw + ni * row_stride + g * BLOCK_BYTES;
+        double ws = half_bits_to_double((uint16_t)(block[0] | (block[1] << 8)));
+        for (int64_t s = 0; s < per_block; ++s) {
+            int64_t a = g * per_block + s;             /* activation group */
+            int32_t dot = 0;                           /* exact integer dot over that group */
+            for (int64_t i = 0; i < agroup; ++i)
+                dot += (int32_t)q[mi * k + a * agroup + i] * oracle_decode_weight(block + 2, (int)(s * agroup + i));
+            /* |dot| < 2^15, xs has 24 significant bits, ws 11: exact in double. */
+            double term = (double)dot * (double)xs[mi * ngroups + a] * ws;
+            acc += term;
+            mag += fabs(term);
+        }
+    }
+    *y = acc;
+    *bound = 1e-5 * mag + 1e-6;
+}
+
+int oracle_matmul_raw_g(const int8_t* q, const float* xs, const uint8_t* raw, int64_t row_stride,
+                        int64_t m, int64_t n, int64_t k, int64_t agroup, double* y, double* bound) {
+    if (k <= 0 || k % GROUP || m <= 0 || n <= 0 || row_stride < (k / GROUP) * BLOCK_BYTES || !valid_agroup(agroup))
+        return 1;
+    for (int64_t mi = 0; mi < m; ++mi)
+        for (int64_t ni = 0; ni < n; ++ni)
+            one_output_g(q, xs, raw, row_stride, k, agroup, mi, ni, &y[mi * n + ni], &bound[mi * n + ni]);
+    return 0;
+}
+
+int oracle_matmul_raw_sample_g(const int8_t* q, const float* xs, const uint8_t* raw, int64_t row_stride,
+                               int64_t m, int64_t n, int64_t k, int64_t agroup, const int64_t* mi,
+                               const int64_t* ni, int64_t count, double* y, double* bound) {
+    if (k <= 0 || k % GROUP || m <= 0 || n <= 0 || row_stride < (k / GROUP) * BLOCK_BYTES || !valid_agroup(agroup))
+        return 1;
+    for (int64_t c = 0; c < count; ++c) {
+        if (mi[c] < 0 || mi[c] >= m || ni[c] < 0 || ni[c] >= n) return 1;
+        one_output_g(q, xs, raw, row_stride, k, agroup, mi[c], ni[c], &y[c], &bound[c]);
+    }
+    return 0;
+}

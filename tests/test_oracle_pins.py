@@ -403,3 +403,120 @@ def test_quantised_projection_error_sanity():
     ref = x.double().numpy() @ dense.T
     rel = np.sqrt(((y - ref) ** 2).sum() / (ref ** 2).sum())
     assert rel < 0.03
+
+
+# ---------------------------------------------------------------- smaller activation groups
+# Page "Kernel experiments: recorded evidence", section C (Diagram 3, Tests 8
+# and 9): the same weights, activations quantised per 64 or 32 elements.
+@pytest.mark.parametrize("agroup", [64, 32])
+def test_agroup_closed_forms(agroup):
+    """Each activation group gets its own power-of-two scale: group a holds
+    127 * 2^e_a, so xs = 2^e_a exactly and q = round_half_even(x / 2^e_a),
+    with the values placed so that a shifted group index would read another
+    group's scale."""
+    k = 256
+    per = k // agroup
+    exps = [(-3 + 2 * a) % 7 - 3 for a in range(per)]
+    x = np.zeros((1, k))
+    picks = [1.5, 2.5, -2.5, 0.5, 3.25, -7.0, 126.5, 17.75]
+    for a in range(per):
+        x[0, a * agroup] = 127.0 * 2.0 ** exps[a]
+        for j, v in enumerate(picks[: agroup // 8]):
+            x[0, a * agroup + 1 + 3 * j] = v * 2.0 ** exps[a]
+    q, xs = oracle.quantize_act_i8_g(_bf16(x), agroup)
+    assert xs.shape == (1, per)
+    for a in range(per):
+        assert xs[0, a] == np.float32(2.0 ** exps[a])
+        for i in range(agroup):
+            val = Fraction(float(x[0, a * agroup + i])) / Fraction(2) ** exps[a]
+            assert q[0, a * agroup + i] == round(val), (a, i)
+
+
+@pytest.mark.parametrize("agroup", [64, 32])
+def test_agroup_exact_rational(agroup):
+    """Every activation group against exact rational quantisation."""
+    x = workloads.make_activations(2, 512, 40 + agroup, "normal+outliers")
+    q, xs = oracle.quantize_act_i8_g(workloads.bf16_bits(x), agroup)
+    xf = x.float().numpy()
+    for m in range(2):
+        for a in range(512 // agroup):
+            eq, es = _exact_quantise(xf[m, a * agroup:(a + 1) * agroup])
+            assert xs[m, a].view(np.uint32) == np.float32(es).view(np.uint32)
+            assert np.array_equal(q[m, a * agroup:(a + 1) * agroup].astype(np.int64), eq)
+
+
+def test_agroup_128_is_the_group_128_definition_and_equal_amax_groups_agree():
+    x = workloads.make_activations(3, 640, 12, "laplace")
+    bits = workloads.bf16_bits(x)
+    q, xs = oracle.quantize_act_i8(bits)
+    q1, xs1 = oracle.quantize_act_i8_g(bits, 128)
+    assert np.array_equal(q, q1) and np.array_equal(xs.view(np.uint32), xs1.view(np.uint32))
+    # When every 32-group of a 128-group holds the same amax, the smaller
+    # groups reproduce the group-128 codes and repeat its scale.
+    xv = x.float().numpy().copy()
+    for g in range(640 // 32):
+        xv[:, g * 32] = 9.0  # above every other |x| of this Laplace(0, 0.5) draw
+    bits = _bf16(xv)
+    q, xs = oracle.quantize_act_i8(bits)
+    for agroup in (64, 32):
+        qa, xsa = oracle.quantize_act_i8_g(bits, agroup)
+        assert np.array_equal(qa, q)
+        assert np.array_equal(xsa, np.repeat(xs, 128 // agroup, axis=1))
+
+
+@pytest.mark.parametrize("agroup,m,n,k", [(64, 1, 2, 128), (64, 2, 3, 256), (32, 2, 2, 256), (32, 1, 3, 384)])
+def test_agroup_matmul_exact_rational_brute_force(agroup, m, n, k):
+    raw = workloads.make_raw_weights(n, k, seed=300 + k + n + agroup, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 301 + m, "laplace")
+    q, xs = oracle.quantize_act_i8_g(workloads.bf16_bits(x), agroup)
+    y, bound = oracle.matmul_raw_g(q, xs, raw, n, k, agroup)
+    for mi in range(m):
+        for ni in range(n):
+            exact = Fraction(0)
+            for kk in range(k):
+                blk = raw[ni, (kk // 128) * 34:(kk // 128) * 34 + 34]
+                ws = Fraction(float(blk[:2].copy().view(np.float16)[0]))
+                w = _digit_decode(int(blk[2 + (kk % 128) // 4]))[kk % 4]
+                exact += Fraction(int(q[mi, kk])) * Fraction(float(xs[mi, kk // agroup])) * w * ws
+            err = abs(Fraction(y[mi, ni]) - exact)
+            assert err <= abs(exact) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 30), (mi, ni)
+    assert np.all(bound >= 1e-6)
+
+
+@pytest.mark.parametrize("agroup", [128, 64, 32])
+def test_agroup_matmul_dense_identity_and_sample(agroup):
+    m, n, k = 2, 24, 1024
+    raw = workloads.make_raw_weights(n, k, seed=23, codes="ternary+3")
+    x = workloads.make_activations(m, k, 24, "normal+outliers")
+    q, xs = oracle.quantize_act_i8_g(workloads.bf16_bits(x), agroup)
+    y, bound = oracle.matmul_raw_g(q, xs, raw, n, k, agroup)
+    dense, _ = _dense_weights(raw, n, k)
+    act = q.astype(np.float64) * np.repeat(xs.astype(np.float64), agroup, axis=1)
+    np.testing.assert_allclose(y, act @ dense.T, rtol=1e-12, atol=1e-12)
+    if agroup == 128:
+        y0, b0 = oracle.matmul_raw(q, xs, raw, n, k)
+        assert np.array_equal(y, y0) and np.array_equal(bound, b0)
+    mi = np.array([0, 1, 1, 0]); ni = np.array([0, 5, 23, 17])
+    ys, bs = oracle.matmul_raw_sample_g(q, xs, raw, n, k, agroup, mi, ni)
+    assert np.array_equal(ys, y[mi, ni]) and np.array_equal(bs, bound[mi, ni])
+
+
+def test_agroup_smaller_groups_reduce_error():
+    """Smaller activation groups quantise more finely: the dequantised
+    activations' relative RMS error falls from 128 to 64 to 32 on data with
+    outliers (the direction Test 8 reports; a sanity property, not parity)."""
+    x = workloads.make_activations(4, 2048, 77, "normal+outliers")
+    xf = x.float().numpy().astype(np.float64)
+    errs = []
+    for agroup in (128, 64, 32):
+        q, xs = oracle.quantize_act_i8_g(workloads.bf16_bits(x), agroup)
+        deq = q.astype(np.float64) * np.repeat(xs.astype(np.float64), agroup, axis=1)
+        errs.append(np.sqrt(((deq - xf) ** 2).sum() / (xf ** 2).sum()))
+    assert errs[0] > errs[1] > errs[2], errs
+
+
+def test_agroup_rejects_bad_groups():
+    x = np.zeros((1, 256), dtype=np.float32)
+    for bad in (0, 16, 96, 256):
+        with pytest.raises(ValueError):
+            oracle.quantize_act_i8_g(x, bad, "f32")
