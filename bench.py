@@ -326,6 +326,39 @@ def main():
             f"call {t['planes_call']:.3f}, fused {t['planes_fused']:.3f}; plane order matmul "
             f"{t['planes_order_mm']:.3f}, call {t['planes_order_call']:.3f}")
 
+    # Smaller activation groups (page "Kernel experiments", section C, Tests
+    # 8 and 9): the tile matmul and the complete call with 64- and 32-element
+    # activation groups, beside the group-128 figures above.
+    agroups = {}
+    for ag in (64, 32):
+        agroups[str(ag)] = {}
+        for m in ms:
+            xm = x[:m]
+            qg = torch.empty((m, k), dtype=torch.int8, device=dev)
+            xsg = torch.empty((m, k // ag), dtype=torch.float32, device=dev)
+            yg = torch.empty((m, n), dtype=torch.float32, device=dev)
+            with torch.cuda.stream(stream):
+                pq2.pq2_quantize_act_i8_g(xm, qg, xsg, ag, stream=stream)
+
+            def g_calls(call, m=m, xm=xm, qg=qg, xsg=xsg, yg=yg, ag=ag):
+                def body():
+                    for c in range(copies):
+                        if call:
+                            pq2.pq2_quantize_act_i8_g(xm, qg, xsg, ag, stream=stream)
+                        pq2.pq2_matmul_small_m_tiles_g(qg, xsg, tpool[c], yg, ag, stream=stream)
+                return body
+
+            mm_us, call_us = per_call_us(g_calls(False)), per_call_us(g_calls(True))
+            torch.cuda.synchronize()
+            assert torch.isfinite(yg).all(), "non-finite output"
+            agroups[str(ag)][str(m)] = {
+                "matmul_us": round(mm_us, 3),
+                "complete_call_us": round(call_us, 3),
+                "matmul_vs_group128": round(mm_us / per_m[str(m)]["matmul_us"], 3),
+            }
+        log(f"[bench] activation groups of {ag}: matmul us " +
+            ", ".join(f"M={m} {v['matmul_us']:.3f}" for m, v in agroups[str(ag)].items()))
+
     tot_bytes = sum(v["matmul_bytes"] for v in per_m.values())
     tot_us = sum(v["matmul_us"] for v in per_m.values())
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
@@ -366,6 +399,7 @@ def main():
             "weight_copies": copies, "rotation_bytes": copies * tb,
         },
         "us_per_call": per_m,
+        "activation_groups_us_per_call": agroups,
         "roofline": roofline,
     }
 

@@ -49,6 +49,8 @@ EXPORTED = (
     "pq2_matmul_prefill_planes_tuned",
     "pq2_matmul_small_m_fused",
     "pq2_matmul_small_m_fused_tuned",
+    "pq2_quantize_act_i8_g",
+    "pq2_matmul_small_m_tiles_g",
 )
 
 
@@ -116,6 +118,10 @@ def _load_library():
     lib.pq2_prepare_tiles.restype = i32
     lib.pq2_matmul_small_m_tiles.argtypes = [p, p, p, i64, i64, i64, p, p]
     lib.pq2_matmul_small_m_tiles.restype = i32
+    lib.pq2_quantize_act_i8_g.argtypes = [p, i32, i64, i64, i64, i64, p, p, p]
+    lib.pq2_quantize_act_i8_g.restype = i32
+    lib.pq2_matmul_small_m_tiles_g.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
+    lib.pq2_matmul_small_m_tiles_g.restype = i32
     lib.pq2_matmul_small_m_tiles_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tiles_tuned.restype = i32
     lib.pq2_matmul_prefill_tiles.argtypes = [p, p, p, i64, i64, i64, p, p]
@@ -279,6 +285,43 @@ def pq2_matmul_small_m_tiles(q, xs, tiles, y, stream=None) -> None:
 def pq2_matmul_small_m_tiles_tuned(q, xs, tiles, y, max_waves=0, split=0, stream=None) -> None:
     _check(lib.pq2_matmul_small_m_tiles_tuned(*_tiles_args(q, xs, tiles, y), max_waves, split, _stream(stream)),
            "pq2_matmul_small_m_tiles_tuned")
+
+
+def pq2_quantize_act_i8_g(x, q, xs, agroup: int, stream=None) -> None:
+    """Quantisation in activation groups of agroup = 128, 64 or 32 elements:
+    x [m][>=k] bf16/f16/f32 (unit column stride), q int8 [m][k], xs float32
+    [m][k/agroup] (both contiguous)."""
+    import torch
+    if agroup not in (128, 64, 32):
+        raise ValueError("agroup must be 128, 64 or 32")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if q.dtype != torch.int8 or xs.dtype != torch.float32 or not q.is_contiguous() or not xs.is_contiguous():
+        raise ValueError("q must be contiguous int8 and xs contiguous float32")
+    m, k = q.shape
+    if x.shape[0] != m or x.shape[1] < k or xs.numel() != m * (k // agroup):
+        raise ValueError("shape mismatch between x, q and xs")
+    _check(lib.pq2_quantize_act_i8_g(_dev_ptr(x, "x"), _dtype_code(x), x.stride(0), m, k, agroup, _dev_ptr(q, "q"),
+                                     _dev_ptr(xs, "xs"), _stream(stream)), "pq2_quantize_act_i8_g")
+
+
+def pq2_matmul_small_m_tiles_g(q, xs, tiles, y, agroup: int, stream=None) -> None:
+    """Tile-layout decode matmul with activation groups of agroup elements
+    (q, xs from pq2_quantize_act_i8_g with the same agroup)."""
+    import torch
+    if agroup not in (128, 64, 32):
+        raise ValueError("agroup must be 128, 64 or 32")
+    if q.dtype != torch.int8 or xs.dtype != torch.float32 or tiles.dtype != torch.uint8 or y.dtype != torch.float32:
+        raise ValueError("q int8, xs float32, tiles uint8, y float32 expected")
+    for name, t in (("q", q), ("xs", xs), ("tiles", tiles), ("y", y)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    m, k = q.shape
+    n = y.shape[1]
+    if y.shape[0] != m or xs.numel() != m * (k // agroup) or tiles.numel() < pq2_tiles_bytes(n, k):
+        raise ValueError("shape mismatch between q, xs, tiles and y")
+    _check(lib.pq2_matmul_small_m_tiles_g(_dev_ptr(q, "q"), _dev_ptr(xs, "xs"), _dev_ptr(tiles, "tiles"), m, n, k,
+                                          agroup, _dev_ptr(y, "y"), _stream(stream)), "pq2_matmul_small_m_tiles_g")
 
 
 def pq2_matmul_prefill_tiles(q, xs, tiles, y, stream=None) -> None:

@@ -200,6 +200,37 @@ int pq2_quantize_act_i8(const void* x, int dtype, int64_t x_row_stride_elems, in
     return launch_status(pq2::launch_quantize(x, dtype, x_row_stride_elems, m, k, q, xs, (hipStream_t)stream));
 }
 
+int pq2_quantize_act_i8_g(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
+                          int64_t agroup, int8_t* q, float* xs, void* stream) {
+    if (!x || !q || !xs) return PQ2_EINVAL;
+    if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
+    if (agroup != 128 && agroup != 64 && agroup != 32) return PQ2_EINVAL;
+    if (m < 1 || m > ((int64_t)1 << 31)) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (x_row_stride_elems < k) return PQ2_ESHAPE;
+    const int esize = dtype == PQ2_F32 ? 4 : 2;
+    if (!aligned(x, esize) || !aligned(q, 8) || !aligned(xs, 4)) return PQ2_EALIGN;
+    const size_t xbytes = ((size_t)(m - 1) * x_row_stride_elems + k) * esize;
+    const size_t sbytes = (size_t)m * (k / agroup) * 4;
+    if (overlap(q, (size_t)m * k, x, xbytes) || overlap(xs, sbytes, x, xbytes) || overlap(q, (size_t)m * k, xs, sbytes))
+        return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(
+        pq2::launch_quantize_g(x, dtype, x_row_stride_elems, m, k, (int)agroup, q, xs, (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_tiles_g(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n, int64_t k,
+                               int64_t agroup, float* y, void* stream) {
+    if (agroup != 128 && agroup != 64 && agroup != 32) return PQ2_EINVAL;
+    if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, PQ2_MAX_SMALL_M, true)) return rc;
+    if (overlap(y, (size_t)m * n * 4, xs, (size_t)m * (k / agroup) * 4)) return PQ2_EINVAL;
+    const int waves = pq2::default_small_m_config(pq2::kSrcNatural, m, n, k).max_waves;
+    const int split = pq2::tiles_default_split(m, k, waves);
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m_tiles_g(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, (int)agroup,
+                                                     y, waves, split, (hipStream_t)stream));
+}
+
 int pq2_quantize_act_i8_planes(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
                                int8_t* qp, float* xs, int32_t* qsum, void* stream) {
     if (!x || !qp || !xs || !qsum) return PQ2_EINVAL;

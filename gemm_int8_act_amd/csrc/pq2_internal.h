@@ -31,6 +31,9 @@ hipError_t launch_prepare(const uint8_t* raw, int64_t stride, int64_t n, int64_t
 hipError_t launch_quantize(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,
                            int8_t* q, float* xs, hipStream_t stream);
 
+// Activation groups of agroup = 128, 64 or 32 elements (q [m][k], xs [m][k/agroup]).
+hipError_t launch_quantize_g(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k, int agroup,
+                             int8_t* q, float* xs, hipStream_t stream);
 hipError_t launch_quantize_planes(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,
                                   int8_t* qp, float* xs, int32_t* qsum, hipStream_t stream);
 
@@ -81,6 +84,10 @@ hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t*
                                 int64_t k, float* y, int tile, hipStream_t stream);
 hipError_t launch_small_m_tiles_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* tiles, int64_t m,
                                       int64_t n, int64_t k, float* y, int max_waves, int split, hipStream_t stream);
+// Tile engine with activation groups of agroup = 128, 64 or 32 (natural-order
+// q from launch_quantize_g, xs [m][k/agroup]).
+hipError_t launch_small_m_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                  int64_t k, int agroup, float* y, int max_waves, int split, hipStream_t stream);
 
 // The library's choice for activations of kind src; the k split (max_waves)
 // depends on (n, k) only, so every source and column count sums in one order.

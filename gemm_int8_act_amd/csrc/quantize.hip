@@ -27,19 +27,34 @@ __device__ __forceinline__ float elem_to_float(uint32_t bits16_or_32) {
     return __uint_as_float(bits16_or_32);                                        // f32
 }
 
+// Max over each aligned group of LPG = 16, 8 or 4 lanes; all lanes agree.
+template <int LPG>
+__device__ __forceinline__ float max_lanes_f(float v) {
+    if constexpr (LPG == 16) return max16_f(v);
+    if constexpr (LPG == 8) return max8_f(v);
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    return fmaxf(v, dpp_f<kDppXor2>(v));
+}
+
 // DT: 0 bf16, 1 f16, 2 f32.  VEC: row bases are 16-byte aligned (2-byte types)
 // or 16-byte aligned (f32), so each lane's 8 elements load as whole vectors.
-template <int DT, bool VEC>
+// LPG lanes per activation group of 8 * LPG elements: 16 for the group-128
+// quantiser; 8 and 4 for activation groups of 64 and 32 (page "Kernel
+// experiments: recorded evidence", section C, Tests 8 and 9), the same
+// steps on the smaller group.
+template <int DT, bool VEC, int LPG = 16>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x, int64_t row_stride,
                                                        int64_t k, int64_t total_groups,
                                                        int8_t* __restrict__ q, float* __restrict__ xs) {
-    const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int l = threadIdx.x & 15;
-    if (gid >= total_groups) return;  // whole 16-lane rows leave together
-    const int64_t groups = k / 128;
+    constexpr int AG = 8 * LPG;     // elements per activation group
+    constexpr int GPB = 256 / LPG;  // groups per workgroup
+    const int64_t gid = (int64_t)blockIdx.x * GPB + (threadIdx.x / LPG);
+    const int l = threadIdx.x % LPG;
+    if (gid >= total_groups) return;  // whole LPG-lane groups leave together
+    const int64_t groups = k / AG;
     const int64_t row = gid / groups;
     const int64_t g = gid - row * groups;
-    const int64_t base = row * row_stride + g * 128 + l * 8;
+    const int64_t base = row * row_stride + g * AG + l * 8;
 
     float v[8];
     if constexpr (DT == 2) {
@@ -72,7 +87,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    amax = max16_f(amax);
+    amax = max_lanes_f<LPG>(amax);
 
     const float scale = amax / 127.0f;                 // one IEEE division
     const float divisor = scale > 0.0f ? scale : 1.0f;
@@ -83,19 +98,41 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         r = fminf(127.0f, fmaxf(-127.0f, r));
         packed[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
     }
-    *reinterpret_cast<uint2*>(q + row * k + g * 128 + l * 8) = make_uint2(packed[0], packed[1]);
+    *reinterpret_cast<uint2*>(q + row * k + g * AG + l * 8) = make_uint2(packed[0], packed[1]);
     if (l == 0) xs[row * groups + g] = scale;
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int LPG = 16>
 static hipError_t launch_q(const void* x, int64_t row_stride, int64_t m, int64_t k, int8_t* q,
                            float* xs, hipStream_t stream) {
-    const int64_t total = m * (k / 128);
-    const int64_t blocks = (total + 15) / 16;
+    constexpr int GPB = 256 / LPG;
+    const int64_t total = m * (k / (8 * LPG));
+    const int64_t blocks = (total + GPB - 1) / GPB;
     clear_stale_error();
-    hipLaunchKernelGGL((quantize_kernel<DT, VEC>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
+    hipLaunchKernelGGL((quantize_kernel<DT, VEC, LPG>), dim3((unsigned)blocks), dim3(256), 0, stream, x,
                        row_stride, k, total, q, xs);
     return hipGetLastError();
+}
+
+template <int LPG>
+static hipError_t launch_q_lpg(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k, int8_t* q,
+                               float* xs, hipStream_t stream) {
+    const int esize = dtype == 2 ? 4 : 2;
+    const bool vec = ((uintptr_t)x % 16 == 0) && ((row_stride * esize) % 16 == 0);
+    if (dtype == 0) return vec ? launch_q<0, true, LPG>(x, row_stride, m, k, q, xs, stream)
+                               : launch_q<0, false, LPG>(x, row_stride, m, k, q, xs, stream);
+    if (dtype == 1) return vec ? launch_q<1, true, LPG>(x, row_stride, m, k, q, xs, stream)
+                               : launch_q<1, false, LPG>(x, row_stride, m, k, q, xs, stream);
+    return vec ? launch_q<2, true, LPG>(x, row_stride, m, k, q, xs, stream)
+               : launch_q<2, false, LPG>(x, row_stride, m, k, q, xs, stream);
+}
+
+hipError_t launch_quantize_g(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k, int agroup,
+                             int8_t* q, float* xs, hipStream_t stream) {
+    if (agroup == 128) return launch_q_lpg<16>(x, dtype, row_stride, m, k, q, xs, stream);
+    if (agroup == 64) return launch_q_lpg<8>(x, dtype, row_stride, m, k, q, xs, stream);
+    if (agroup == 32) return launch_q_lpg<4>(x, dtype, row_stride, m, k, q, xs, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_quantize(const void* x, int dtype, int64_t row_stride, int64_t m, int64_t k,

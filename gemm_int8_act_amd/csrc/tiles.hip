@@ -140,7 +140,12 @@ __device__ __forceinline__ int small_mod(int j, int mcount) {
 // padded by 64 bytes: the columns of one A read fall in distinct banks), then
 // 8 x 8 floats of xs and 8 x 8 ints of -sum(q) (group class x column).
 __host__ __device__ constexpr int tiles_col_pitch(int cpw) { return 128 * cpw + 64; }
-__host__ __device__ constexpr int tiles_region_bytes(int mc, int cpw) { return (mc + 1) * tiles_col_pitch(cpw) + 512; }
+// With activation groups of ag < 128 elements the xs and -sum(q) tables hold
+// 128/ag entries per class, and ag = 32 adds a zero block that the lanes
+// outside a 32-element group read as their A operand.
+__host__ __device__ constexpr int tiles_region_bytes(int mc, int cpw, int ag = 128) {
+    return (mc + 1) * tiles_col_pitch(cpw) + 512 * (128 / ag) + (ag == 32 ? 128 * cpw : 0);
+}
 
 __device__ __forceinline__ float half_of(const uint4& v, int c) {
     const uint32_t w = word_of(v, c >> 1);
@@ -150,7 +155,13 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
 // SRC: kSrcNatural reads q and xs; kSrcBf16 / kSrcF16 / kSrcF32 read x and
 // quantise each staged group in the wave (the exact in-kernel quantiser, so
 // the codes and scales are those of pq2_quantize_act_i8).
-template <int MC, int CPW, int SRC>
+//
+// AG: activation group size (128; 64 or 32 for the smaller activation groups
+// of page "Kernel experiments: recorded evidence", section C, Tests 8 and 9:
+// natural-order q only).  Each activation group has its own D chain seeded
+// with its own -sum(q) and its own fp32 term fma((float)dot * xs_a, ws, acc),
+// added in k order within the weight group.
+template <int MC, int CPW, int SRC, int AG = 128>
 __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const void* __restrict__ x, int64_t x_stride,
     const uint8_t* __restrict__ tiles, float* __restrict__ y, int n, int k, int groups, int s8, int nseg,
@@ -165,6 +176,12 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     constexpr int COLS_PER_LOAD = 64 / CHUNKS;
     constexpr int QLOADS = (MC + COLS_PER_LOAD - 1) / COLS_PER_LOAD;
     constexpr int PITCH = tiles_col_pitch(CPW);
+    constexpr int S = 128 / AG;             // activation groups per weight group
+    constexpr int LPS = AG / 16;            // staging lanes per activation group
+    constexpr int XSV = CPW * S * MC;       // xs values of one segment (AG < 128)
+    constexpr int XSL = (XSV + 63) / 64;    // their loads per lane
+    static_assert(AG == 128 || AG == 64 || AG == 32, "activation group");
+    static_assert(AG == 128 || !src_fused(SRC), "smaller activation groups read natural-order q");
     const int nwaves = blockDim.x >> 6;
     const int nslices = nwaves / WPS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -182,6 +199,8 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     const auto tile_rs = make_rsrc(tiles + (size_t)tile * s8 * kSegUnit, (uint32_t)(s8 * kSegUnit));
     const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
     const i32x4_t xs_srs = make_srsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
+    const auto xsa_rs = make_rsrc(AG == 128 ? nullptr : xs + (size_t)m0 * groups * S,
+                                  AG == 128 ? 0u : (uint32_t)(mcount * groups * S * 4));
     const auto x_rs = make_rsrc(
         FUSED ? static_cast<const unsigned char*>(x) + (size_t)m0 * x_stride * src_esize(SRC) : nullptr,
         FUSED ? (uint32_t)(((int64_t)(mcount - 1) * x_stride + k) * src_esize(SRC)) : 0u);
@@ -195,7 +214,8 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     //    blocks are in flight), then xs.  Groups past the end read zeros.
     uint4 qv[QLOADS];
     uint4 xv[QLOADS][FUSED ? XL : 1];
-    float xss[FUSED ? 1 : MC][CPW];  // xs of the wave's groups, scalar loads (uniform)
+    float xss[FUSED || AG < 128 ? 1 : MC][CPW];  // xs of the wave's groups, scalar loads (uniform)
+    uint32_t xsa[AG < 128 ? XSL : 1];              // xs of activation groups (AG < 128), vector loads
     uint4 wsv;
     uint4 cw[CPW / 2];
     auto issue = [&](int s) {
@@ -219,7 +239,18 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
         for (int b = 0; b < CPW / 2; ++b)
             cw[b] = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + (c_lo / 2 + b) * kCodeBlock + 16 * lane);
         keep_order();
-        if constexpr (!FUSED) {
+        if constexpr (AG < 128) {
+            // Value i of the segment: column i / (CPW*S), activation group
+            // (8s + c_lo)*S + i % (CPW*S).
+#pragma unroll
+            for (int t = 0; t < XSL; ++t) {
+                const int i = t * 64 + lane;
+                const int col = i / (CPW * S);
+                const int a = (8 * s + c_lo) * S + i % (CPW * S);
+                const bool ok = i < XSV && col < mcount && a < groups * S;
+                xsa[t] = buf_load4(xsa_rs, ok ? (uint32_t)((col * groups * S + a) * 4) : kBufferOOB);
+            }
+        } else if constexpr (!FUSED) {
             // xs of the wave's groups: uniform offsets, so the scalar unit
             // fetches them, outside the vector memory queue.  Columns past
             // the last re-read it (their D rows are never used).  A segment
@@ -241,15 +272,24 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     // Private region: MC staged columns (CPW groups each) and one column that
     // takes the stores of lanes past the last column, then per class c of the
     // wave 8 floats xs[c][m] and 8 ints -sum(q)[c][m].
-    unsigned char* region = smem + (size_t)wave * tiles_region_bytes(MC, CPW);
-    float* red = reinterpret_cast<float*>(smem + (size_t)nwaves * tiles_region_bytes(MC, CPW));
+    unsigned char* region = smem + (size_t)wave * tiles_region_bytes(MC, CPW, AG);
+    float* red = reinterpret_cast<float*>(smem + (size_t)nwaves * tiles_region_bytes(MC, CPW, AG));
     float* xs_lds = reinterpret_cast<float*>(region + (MC + 1) * PITCH);
-    int* nsq_lds = reinterpret_cast<int*>(region + (MC + 1) * PITCH + 256);
+    int* nsq_lds = reinterpret_cast<int*>(region + (MC + 1) * PITCH + 256 * S);
+    const unsigned char* zero_lds = region + (MC + 1) * PITCH + 512 * S;  // AG == 32 only
     // A row i reads column i mod mcount: rows >= mcount repeat real columns,
     // so one read touches at most 4 x 16 distinct banks, and the D rows they
     // produce are never used.
     const unsigned char* a_base = region + small_mod(j, mcount) * PITCH + 16 * kb;
-    nsq_lds[lane] = 0;
+#pragma unroll
+    for (int i = 0; i < S; ++i) nsq_lds[lane + 64 * i] = 0;
+    if constexpr (AG == 32) {
+        if (lane < 8 * CPW) *reinterpret_cast<uint4*>(const_cast<unsigned char*>(zero_lds) + 16 * lane) = make_uint4(0, 0, 0, 0);
+    }
+    // With 32-element activation groups lanes kb = 2s, 2s + 1 hold group s of
+    // each 64-wide half; the others read zeros for that group's product.
+    const unsigned char* a_grp[2] = {AG == 32 && (kb >> 1) != 0 ? zero_lds : a_base,
+                                     AG == 32 && (kb >> 1) != 1 ? zero_lds : a_base};
 
     float acc[CPW][MC];
 #pragma unroll
@@ -283,10 +323,23 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
                 sq = dot4(v.y, 0x01010101u, sq);
                 sq = dot4(v.z, 0x01010101u, sq);
                 sq = dot4(v.w, 0x01010101u, sq);
-                sq = sum8_i(sq);
+                if constexpr (AG == 128) {
+                    sq = sum8_i(sq);
+                } else {
+                    sq += dpp_i<kDppXor1>(sq);
+                    if constexpr (AG == 64) sq += dpp_i<kDppXor2>(sq);
+                }
             }
             *reinterpret_cast<uint4*>(region + (m < MC ? m : MC) * PITCH + 16 * ch) = v;
-            if ((lane & 7) == 0 && m < MC) nsq_lds[(c_lo + (ch >> 3)) * 8 + m] = -sq;
+            if ((lane & (LPS - 1)) == 0 && m < MC)
+                nsq_lds[((c_lo + (ch >> 3)) * S + (ch & 7) / LPS) * 8 + m] = -sq;
+        }
+        if constexpr (AG < 128) {
+#pragma unroll
+            for (int t = 0; t < XSL; ++t) {
+                const int i = t * 64 + lane;
+                if (i < XSV) xs_lds[(c_lo * S + i % (CPW * S)) * 8 + i / (CPW * S)] = __uint_as_float(xsa[t]);
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -297,6 +350,44 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
         //    64-wide halves of codes 0..3 times q.
 #pragma unroll
         for (int c0 = 0; c0 < CPW; c0 += 2) {
+          if constexpr (AG < 128) {
+            // One chain per activation group, seeded with its -sum(q); its
+            // term uses its own xs.  The groups' terms are added in k order.
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int c = c0 + p;
+                v4i Bh[2], Dt[S];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t d = word_of(cw[c >> 1], 2 * (c & 1) + h);
+                    Bh[h] = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
+                                (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
+                }
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    const int4 nsq = *reinterpret_cast<const int4*>(nsq_lds + ((c_lo + c) * S + t) * 8);
+                    Dt[t] = v4i{nsq.x, nsq.y, nsq.z, nsq.w};
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int u = 0; u < S / 2; ++u) {  // activation group t = h * S/2 + u of this weight group
+                        const uint4 a = *reinterpret_cast<const uint4*>((S == 2 ? a_base : a_grp[u]) + 128 * c + 64 * h);
+                        const int t = h * (S / 2) + u;
+                        Dt[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w},
+                                                                      Bh[h], Dt[t], 0, 0, 0);
+                    }
+                }
+                const float wsf = half_of(wsv, c_lo + c);
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    const float4 xg = *reinterpret_cast<const float4*>(xs_lds + ((c_lo + c) * S + t) * 8);
+                    const float xv[4] = {xg.x, xg.y, xg.z, xg.w};
+#pragma unroll
+                    for (int r = 0; r < MC; ++r) acc[c][r] = __builtin_fmaf((float)Dt[t][r] * xv[r], wsf, acc[c][r]);
+                }
+            }
+          } else {
             v4i D[2];
             v4i A[2][2];
             v4i B[2][2];
@@ -336,6 +427,7 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
 #pragma unroll
                 for (int r = 0; r < MC; ++r) acc[c][r] = __builtin_fmaf((float)D[p][r] * xv[r], wsf, acc[c][r]);
             }
+          }
         }
         // The next segment rewrites the region: every lane's reads of this one
         // are done (LDS operations of one wave complete in order).
@@ -419,36 +511,36 @@ struct TilesArgs {
     hipStream_t stream;
 };
 
-template <int MC, int CPW, int SRC>
+template <int MC, int CPW, int SRC, int AG>
 hipError_t launch_tiles_one(const TilesArgs& a, int slices, int nseg, int per_wave, int chunks) {
     const int64_t m = a.m, n = a.n, k = a.k;
     const TileGeometry t = geometry(n, k);
     const int waves = slices * (8 / CPW);
-    const size_t lds = (size_t)waves * tiles_region_bytes(MC, CPW) + (size_t)slices * 8 * MC * kTileRows * 4;
+    const size_t lds = (size_t)waves * tiles_region_bytes(MC, CPW, AG) + (size_t)slices * 8 * MC * kTileRows * 4;
     const dim3 grid((unsigned)t.tiles, (unsigned)chunks);
     clear_stale_error();
-    hipLaunchKernelGGL((small_m_tiles_kernel<MC, CPW, SRC>), grid, dim3(64 * waves), lds, a.stream, a.q, a.xs, a.x,
+    hipLaunchKernelGGL((small_m_tiles_kernel<MC, CPW, SRC, AG>), grid, dim3(64 * waves), lds, a.stream, a.q, a.xs, a.x,
                        a.x_stride, a.tiles, a.y, (int)n, (int)k, (int)(k / 128), (int)t.s8, nseg, per_wave, (int)m);
     return hipGetLastError();
 }
 
-template <int CPW, int SRC>
+template <int CPW, int SRC, int AG>
 hipError_t launch_tiles_mc(int mc, const TilesArgs& a, int slices, int nseg, int per_wave, int chunks) {
     switch (mc) {
-        case 1: return launch_tiles_one<1, CPW, SRC>(a, slices, nseg, per_wave, chunks);
-        case 2: return launch_tiles_one<2, CPW, SRC>(a, slices, nseg, per_wave, chunks);
-        case 3: return launch_tiles_one<3, CPW, SRC>(a, slices, nseg, per_wave, chunks);
-        case 4: return launch_tiles_one<4, CPW, SRC>(a, slices, nseg, per_wave, chunks);
+        case 1: return launch_tiles_one<1, CPW, SRC, AG>(a, slices, nseg, per_wave, chunks);
+        case 2: return launch_tiles_one<2, CPW, SRC, AG>(a, slices, nseg, per_wave, chunks);
+        case 3: return launch_tiles_one<3, CPW, SRC, AG>(a, slices, nseg, per_wave, chunks);
+        case 4: return launch_tiles_one<4, CPW, SRC, AG>(a, slices, nseg, per_wave, chunks);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int SRC>
+template <int SRC, int AG = 128>
 hipError_t launch_tiles_split(int split, int mc, const TilesArgs& a, int slices, int nseg, int per_wave, int chunks) {
     switch (split) {
-        case 1: return launch_tiles_mc<8, SRC>(mc, a, slices, nseg, per_wave, chunks);
-        case 2: return launch_tiles_mc<4, SRC>(mc, a, slices, nseg, per_wave, chunks);
-        default: return launch_tiles_mc<2, SRC>(mc, a, slices, nseg, per_wave, chunks);
+        case 1: return launch_tiles_mc<8, SRC, AG>(mc, a, slices, nseg, per_wave, chunks);
+        case 2: return launch_tiles_mc<4, SRC, AG>(mc, a, slices, nseg, per_wave, chunks);
+        default: return launch_tiles_mc<2, SRC, AG>(mc, a, slices, nseg, per_wave, chunks);
     }
 }
 
@@ -498,13 +590,15 @@ bool tiles_supported(int64_t k, int max_waves, int split) {
     return tiles_slices(k, max_waves, &nseg, &per_wave) * split <= 16;
 }
 
-static hipError_t launch_tiles_any(int src, const TilesArgs& a, int max_waves, int split) {
+static hipError_t launch_tiles_any(int src, const TilesArgs& a, int max_waves, int split, int agroup = 128) {
     if (!tiles_supported(a.k, max_waves, split)) return hipErrorInvalidValue;
     int nseg, per_wave;
     const int slices = tiles_slices(a.k, max_waves, &nseg, &per_wave);
     int mc = (int)(a.m < kTilesMaxColumns ? a.m : kTilesMaxColumns);
     const int chunks = (int)((a.m + mc - 1) / mc);
     mc = (int)((a.m + chunks - 1) / chunks);
+    if (agroup == 64) return launch_tiles_split<kSrcNatural, 64>(split, mc, a, slices, nseg, per_wave, chunks);
+    if (agroup == 32) return launch_tiles_split<kSrcNatural, 32>(split, mc, a, slices, nseg, per_wave, chunks);
     switch (src) {
         case kSrcNatural: return launch_tiles_split<kSrcNatural>(split, mc, a, slices, nseg, per_wave, chunks);
         case kSrcBf16: return launch_tiles_split<kSrcBf16>(split, mc, a, slices, nseg, per_wave, chunks);
@@ -524,6 +618,13 @@ hipError_t launch_small_m_tiles_fused(const void* x, int dtype, int64_t x_stride
                                       int64_t n, int64_t k, float* y, int max_waves, int split, hipStream_t stream) {
     const TilesArgs a{nullptr, nullptr, x, x_stride, tiles, m, n, k, y, stream};
     return launch_tiles_any(src_of_dtype(dtype), a, max_waves, split);
+}
+
+hipError_t launch_small_m_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                  int64_t k, int agroup, float* y, int max_waves, int split, hipStream_t stream) {
+    if (agroup != 128 && agroup != 64 && agroup != 32) return hipErrorInvalidValue;
+    const TilesArgs a{q, xs, nullptr, 0, tiles, m, n, k, y, stream};
+    return launch_tiles_any(kSrcNatural, a, max_waves, split, agroup);
 }
 
 }  // namespace pq2

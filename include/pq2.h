@@ -324,6 +324,32 @@ int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row
                                          int64_t m, int64_t n, int64_t k, float* y, int max_waves, int split,
                                          void* stream);
 
+/* Smaller activation groups (page "Kernel experiments", section C,
+ * Diagram 3, Tests 8 and 9): the weights keep their 128-weight blocks and
+ * fp16 scales; activations are quantised in groups of agroup = 128, 64 or 32
+ * elements, each with its own scale max|x|/127 (the same steps as
+ * pq2_quantize_act_i8 on the smaller group; agroup = 128 is that function).
+ *   x, q    as pq2_quantize_act_i8.   xs  device float [m][k/agroup], 4-byte aligned.
+ * Errors: EINVAL (null, dtype, agroup not 128/64/32, overlap), otherwise as
+ *         pq2_quantize_act_i8. */
+int pq2_quantize_act_i8_g(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
+                          int64_t agroup, int8_t* q, float* xs, void* stream);
+
+/* Tile-layout decode matmul with activation groups of agroup elements:
+ *   y[m][n] = sum over weight blocks g of ws[n][g] * sum over the activation
+ *             groups a inside block g of float(dot_a) * xs[m][a],
+ * dot_a the exact integer dot of group a's q with the block's codes minus 1.
+ * Each activation group has its own integer product (no rounding inside it);
+ * the fp32 terms are added in k order within a weight block, then as
+ * pq2_matmul_small_m_tiles adds its group terms (so agroup = 128 gives the
+ * same bits as pq2_matmul_small_m_tiles).  q and xs come from
+ * pq2_quantize_act_i8_g with the same agroup.
+ *   q       device int8 [m][k], 16-byte aligned.  xs  device float [m][k/agroup].
+ *   tiles, y, limits and errors as pq2_matmul_small_m_tiles, plus EINVAL for
+ *   agroup not 128/64/32. */
+int pq2_matmul_small_m_tiles_g(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n, int64_t k,
+                               int64_t agroup, float* y, void* stream);
+
 /* Prefill matmul from the tile layout: the definition, limits and output of
  * pq2_matmul_prefill, and the same bits, with the weights read from the
  * decode GEMV's tile layout, so one prepared copy serves decode and prefill

@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 24
+    assert len(names) == 26
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -173,6 +173,28 @@ def test_small_m_tiles_fused_validation():
     assert t(A, 0, 128, C, 1, 8, 128, D, 0, 3, None) == EINVAL
     if not _gpu_visible():
         assert t(A, 2, 5120, C, 4, 8, 5120, D, 0, 0, None) == EDEVICE
+
+
+def test_activation_group_validation():
+    f = pq2.lib.pq2_quantize_act_i8_g
+    for bad in (0, 16, 96, 256):
+        assert f(A, 0, 128, 1, 128, bad, B, C, None) == EINVAL, bad
+    assert f(None, 0, 128, 1, 128, 64, B, C, None) == EINVAL
+    assert f(A, 3, 128, 1, 128, 64, B, C, None) == EINVAL        # dtype
+    assert f(A, 0, 128, 1, 96, 32, B, C, None) == ESHAPE         # k % 128
+    assert f(A, 0, 100, 1, 128, 64, B, C, None) == ESHAPE        # stride < k
+    assert f(A, 0, 128, 1, 128, 32, B + 4, C, None) == EALIGN    # q not 8-byte aligned
+    assert f(A, 0, 256, 1, 256, 32, B, B + 128, None) == EINVAL  # xs (8 floats) overlaps q
+    g = pq2.lib.pq2_matmul_small_m_tiles_g
+    for bad in (0, 16, 96, 256):
+        assert g(A, B, C, 1, 8, 128, bad, D, None) == EINVAL, bad
+    assert g(A, B, C, 17, 8, 128, 64, D, None) == ESHAPE         # columns
+    assert g(A + 8, B, C, 1, 8, 128, 64, D, None) == EALIGN      # q not 16-byte aligned
+    assert g(A, B, C, 1, 8, 256, 32, B + 16, None) == EINVAL     # y overlaps xs (8 floats)
+    if not _gpu_visible():
+        for agroup in (128, 64, 32):
+            assert f(A, 0, 5120, 4, 5120, agroup, B, C, None) == EDEVICE
+            assert g(A, B, C, 4, 8, 5120, agroup, D, None) == EDEVICE
 
 
 def test_prefill_tile_validation():

@@ -872,3 +872,95 @@ def test_tiles_fused_workloads(name):
         q, xs = gpu_quantize(xd)
         assert same_bits(gpu_tiles_fused(xd, tiles, w.n), gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, tiles, w.n)), \
             f"{name} m={m}"
+
+
+# ------------------------------------------------------------------ smaller activation groups
+# Page "Kernel experiments: recorded evidence", section C (Tests 8 and 9).
+def quantise_g_both(x_cpu, agroup, dtype="bf16", k=None):
+    """Activation-group quantiser on the GPU and in the oracle, bit-equal."""
+    pq2 = _pq2()
+    bits = workloads.bf16_bits(x_cpu) if dtype == "bf16" else (
+        x_cpu.numpy() if dtype == "f32" else x_cpu.view(torch.int16).numpy().view(np.uint16))
+    qo, xso = oracle.quantize_act_i8_g(bits, agroup, dtype, k=k)
+    m = x_cpu.shape[0]
+    k = x_cpu.shape[1] if k is None else k
+    q = torch.empty((m, k), dtype=torch.int8, device=DEV)
+    xs = torch.full((m, k // agroup), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_quantize_act_i8_g(x_cpu.to(DEV), q, xs, agroup)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), qo), f"agroup {agroup}: q differs from the oracle"
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), xso.view(np.uint32)), f"agroup {agroup}: xs differs"
+    return q, xs, qo, xso
+
+
+@pytest.mark.parametrize("agroup", [64, 32])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_quantize_g_bit_exact(agroup, dtype):
+    announce(f"quantize agroup={agroup} {dtype}")
+    x = workloads.make_activations(5, 1152, 60 + agroup, "normal+outliers")
+    x[1, :64] = 0                                    # zero groups
+    x[2, 128:256] = torch.linspace(-3, 3, 128)       # exact ties at power-of-two scales
+    x[3, 256:288] = 1e-38                            # tiny group (subnormal scale)
+    xc = {"bf16": x, "f16": x.float().to(torch.float16), "f32": x.float()}[dtype]
+    quantise_g_both(xc, agroup, dtype)
+    if agroup == 64:  # a padded row stride takes the unaligned path
+        wide = torch.zeros((5, 1160), dtype=xc.dtype)
+        wide[:, :1152] = xc
+        quantise_g_both(wide, agroup, dtype, k=1152)
+
+
+G_SHAPES = [(1, 1024, 512), (2, 333, 640), (3, 97, 1152), (4, 1000, 5120), (5, 77, 2176), (9, 61, 1024),
+            (16, 40, 17408)]
+
+
+@pytest.mark.parametrize("agroup", [64, 32])
+@pytest.mark.parametrize("m,n,k", G_SHAPES)
+def test_small_m_tiles_g_full(agroup, m, n, k):
+    pq2 = _pq2()
+    announce(f"tiles agroup={agroup} m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=70 + m + n, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 71 + k, "normal+outliers")
+    q, xs, qo, xso = quantise_g_both(x, agroup)
+    tiles = gpu_tiles(raw, n, k)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_small_m_tiles_g(q, xs, tiles, y, agroup)
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_raw_g(qo, xso, raw, n, k, agroup)
+    assert_within(y.cpu().numpy(), y_ref, bound, f"tiles agroup={agroup} m={m} n={n} k={k}")
+
+
+def test_small_m_tiles_g_128_is_the_tile_matmul():
+    pq2 = _pq2()
+    m, n, k = 4, 300, 3072
+    raw = workloads.make_raw_weights(n, k, seed=73, codes="ternary+3")
+    x = workloads.make_activations(m, k, 74, "laplace")
+    q, xs, _, _ = quantise_g_both(x, 128)
+    tiles = gpu_tiles(raw, n, k)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_small_m_tiles_g(q, xs, tiles, y, 128)
+    y0 = gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, tiles, n)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_small_m_tiles_g_workloads(name):
+    """Full workload sizes, sampled outputs against the oracle, and 16
+    repeated launches with identical bits."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    tiles = gpu_tiles(raw, w.n, w.k)
+    for agroup in (64, 32):
+        for m in w.ms:
+            announce(f"tiles agroup={agroup} workload {name} m={m}")
+            q, xs, qo, xso = quantise_g_both(x[:m].contiguous(), agroup)
+            ys = torch.full((16, m, w.n), float("nan"), dtype=torch.float32, device=DEV)
+            for i in range(16):
+                pq2.pq2_matmul_small_m_tiles_g(q, xs, tiles, ys[i], agroup)
+            torch.cuda.synchronize()
+            bits = ys.view(torch.int32)
+            assert bool((bits == bits[0:1]).all()), f"{name} m={m} agroup={agroup}: launches differ"
+            y = ys[0].cpu().numpy()
+            mi, ni = _sample_indices(m, w.n, 300, seed=m + agroup)
+            y_ref, bound = oracle.matmul_raw_sample_g(qo, xso, raw, w.n, w.k, agroup, mi, ni)
+            assert_within(y[mi, ni], y_ref, bound, f"tiles agroup={agroup} {name} m={m}")
