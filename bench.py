@@ -216,8 +216,7 @@ def main():
         def f():
             for m in ms:
                 q, xs, y = bufs[m]
-                pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
-                pq2.pq2_matmul_small_m_tiles(q, xs, tpool[c], y, stream=stream)
+                pq2.pq2_gemv_tiles(x[:m], tpool[c], y, q, xs, stream=stream)
         return f
 
     # One graph holds `copies` consecutive steps (step i reads copy i), as a
@@ -280,6 +279,8 @@ def main():
                     elif kind == "tiles_call":
                         pq2.pq2_quantize_act_i8(xm, q, xs, stream=stream)
                         pq2.pq2_matmul_small_m_tiles(q, xs, tpool[c], y, stream=stream)
+                    elif kind == "gemv":
+                        pq2.pq2_gemv_tiles(xm, tpool[c], y, q, xs, stream=stream)
                     elif kind == "tiles_fused":
                         pq2.pq2_matmul_small_m_tiles_fused(xm, tpool[c], ys["tiles_fused"], stream=stream)
                     elif kind == "planes_mm":
@@ -297,7 +298,7 @@ def main():
             return body
 
         t = {kind: per_call_us(calls(kind)) for kind in
-             ("tiles_mm", "tiles_call", "tiles_fused", "planes_mm", "planes_call", "planes_order_mm",
+             ("tiles_mm", "tiles_call", "gemv", "tiles_fused", "planes_mm", "planes_call", "planes_order_mm",
               "planes_order_call", "planes_fused")}
         torch.cuda.synchronize()
         for key, other in (("planes", ys["planes"]), ("plane order", py), ("tiles fused", ys["tiles_fused"]),
@@ -311,6 +312,7 @@ def main():
             "matmul_GBps": round(gbs, 1),
             "matmul_pct_peak": round(100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S, 1),
             "complete_call_us": round(t["tiles_call"], 3),
+            "gemv_call_us": round(t["gemv"], 3),
             "fused_call_us": round(t["tiles_fused"], 3),
             "planes_matmul_us": round(t["planes_mm"], 3),
             "planes_matmul_GBps": round(pgbs, 1),
@@ -322,6 +324,7 @@ def main():
         }
         log(f"[bench] M={m}: tiles matmul {t['tiles_mm']:.3f} us ({gbs:.0f} GB/s, "
             f"{100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S:.1f}% of 8 TB/s), call {t['tiles_call']:.3f}, "
+            f"gemv {t['gemv']:.3f}, "
             f"fused {t['tiles_fused']:.3f}; planes matmul {t['planes_mm']:.3f} ({pgbs:.0f} GB/s), "
             f"call {t['planes_call']:.3f}, fused {t['planes_fused']:.3f}; plane order matmul "
             f"{t['planes_order_mm']:.3f}, call {t['planes_order_call']:.3f}")
@@ -394,7 +397,8 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "attention QKV projection K=5120 N=10240, M=1,2,3,4 (quantise + tile-layout matmul per M)",
+            "workload": "attention QKV projection K=5120 N=10240, M=1,2,3,4 (x -> y per M with pq2_gemv_tiles: "
+                        "fused quantise + tile matmul at M=1, quantiser + tile matmul at M=2..4)",
             "k": k, "n": n, "ms": list(ms),
             "weight_copies": copies, "rotation_bytes": copies * tb,
         },

@@ -51,6 +51,7 @@ EXPORTED = (
     "pq2_matmul_small_m_fused_tuned",
     "pq2_quantize_act_i8_g",
     "pq2_matmul_small_m_tiles_g",
+    "pq2_gemv_tiles",
 )
 
 
@@ -118,6 +119,8 @@ def _load_library():
     lib.pq2_prepare_tiles.restype = i32
     lib.pq2_matmul_small_m_tiles.argtypes = [p, p, p, i64, i64, i64, p, p]
     lib.pq2_matmul_small_m_tiles.restype = i32
+    lib.pq2_gemv_tiles.argtypes = [p, i32, i64, p, i64, i64, i64, p, p, p, p]
+    lib.pq2_gemv_tiles.restype = i32
     lib.pq2_quantize_act_i8_g.argtypes = [p, i32, i64, i64, i64, i64, p, p, p]
     lib.pq2_quantize_act_i8_g.restype = i32
     lib.pq2_matmul_small_m_tiles_g.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
@@ -285,6 +288,30 @@ def pq2_matmul_small_m_tiles(q, xs, tiles, y, stream=None) -> None:
 def pq2_matmul_small_m_tiles_tuned(q, xs, tiles, y, max_waves=0, split=0, stream=None) -> None:
     _check(lib.pq2_matmul_small_m_tiles_tuned(*_tiles_args(q, xs, tiles, y), max_waves, split, _stream(stream)),
            "pq2_matmul_small_m_tiles_tuned")
+
+
+def pq2_gemv_tiles(x, tiles, y, q_work=None, xs_work=None, stream=None) -> None:
+    """y = W x from activations: one fused launch at m = 1 (k <= 8192), else
+    the quantiser into q_work (int8 [m][k]) / xs_work (float32 [m][k/128])
+    and the tile matmul; the same bits either way."""
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if tiles.dtype != torch.uint8 or y.dtype != torch.float32 or not tiles.is_contiguous() or not y.is_contiguous():
+        raise ValueError("tiles contiguous uint8 and y contiguous float32 expected")
+    m, n = y.shape
+    k = x.shape[1] if q_work is None else q_work.shape[1]
+    if x.shape[0] != m or x.shape[1] < k or tiles.numel() < pq2_tiles_bytes(n, k):
+        raise ValueError("shape mismatch between x, tiles and y")
+    qp = xp = None
+    if q_work is not None or xs_work is not None:
+        if q_work is None or xs_work is None or q_work.dtype != torch.int8 or xs_work.dtype != torch.float32 or \
+                not q_work.is_contiguous() or not xs_work.is_contiguous() or q_work.shape != (m, k) or \
+                xs_work.numel() != m * (k // 128):
+            raise ValueError("q_work int8 [m][k] and xs_work float32 [m][k/128], contiguous, expected")
+        qp, xp = _dev_ptr(q_work, "q_work"), _dev_ptr(xs_work, "xs_work")
+    _check(lib.pq2_gemv_tiles(_dev_ptr(x, "x"), _dtype_code(x), x.stride(0), _dev_ptr(tiles, "tiles"), m, n, k,
+                              _dev_ptr(y, "y"), qp, xp, _stream(stream)), "pq2_gemv_tiles")
 
 
 def pq2_quantize_act_i8_g(x, q, xs, agroup: int, stream=None) -> None:

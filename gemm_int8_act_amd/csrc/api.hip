@@ -200,6 +200,30 @@ int pq2_quantize_act_i8(const void* x, int dtype, int64_t x_row_stride_elems, in
     return launch_status(pq2::launch_quantize(x, dtype, x_row_stride_elems, m, k, q, xs, (hipStream_t)stream));
 }
 
+int pq2_gemv_tiles(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m, int64_t n,
+                   int64_t k, float* y, int8_t* q_work, float* xs_work, void* stream) {
+    // One column whose waves each hold a single segment (k <= 1024 * 8 at the
+    // default k split): the single launch wins; otherwise the quantiser
+    // launch plus the tile matmul.  Both give the same bits.
+    if (m == 1 && k <= 8192)
+        return pq2_matmul_small_m_tiles_fused(x, dtype, x_row_stride_elems, tiles, m, n, k, y, stream);
+    if (!x || !q_work || !xs_work) return PQ2_EINVAL;
+    if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
+    if (int rc = check_matmul_args(q_work, xs_work, tiles, m, n, k, y, PQ2_MAX_SMALL_M, true)) return rc;
+    if (x_row_stride_elems < k) return PQ2_ESHAPE;
+    const int esize = dtype == PQ2_F32 ? 4 : 2;
+    if (!aligned(x, esize)) return PQ2_EALIGN;
+    const size_t xbytes = ((size_t)(m - 1) * x_row_stride_elems + k) * esize;
+    const size_t qbytes = (size_t)m * k, sbytes = (size_t)m * (k / kGroup) * 4, ybytes = (size_t)m * n * 4;
+    if (overlap(q_work, qbytes, x, xbytes) || overlap(xs_work, sbytes, x, xbytes) ||
+        overlap(q_work, qbytes, xs_work, sbytes) || overlap(y, ybytes, x, xbytes) ||
+        overlap(q_work, qbytes, tiles, (size_t)pq2::tiles_bytes(n, k)) ||
+        overlap(xs_work, sbytes, tiles, (size_t)pq2::tiles_bytes(n, k)))
+        return PQ2_EINVAL;
+    if (int rc = pq2_quantize_act_i8(x, dtype, x_row_stride_elems, m, k, q_work, xs_work, stream)) return rc;
+    return pq2_matmul_small_m_tiles(q_work, xs_work, tiles, m, n, k, y, stream);
+}
+
 int pq2_quantize_act_i8_g(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,
                           int64_t agroup, int8_t* q, float* xs, void* stream) {
     if (!x || !q || !xs) return PQ2_EINVAL;

@@ -874,6 +874,31 @@ def test_tiles_fused_workloads(name):
             f"{name} m={m}"
 
 
+@pytest.mark.parametrize("name", ["qkv", "up", "down"])
+def test_gemv_tiles_same_bits(name):
+    """pq2_gemv_tiles (fused at one column and k <= 8192, two launches
+    otherwise) gives the bits of quantise + tile matmul at every M."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    tiles = gpu_tiles(raw, w.n, w.k)
+    for m in w.ms:
+        announce(f"gemv tiles {name} m={m}")
+        q, xs, _, _ = quantise_both(x[:m].contiguous())
+        y0 = gpu_matmul(pq2.pq2_matmul_small_m_tiles, q, xs, tiles, w.n)
+        xd = x[:m].contiguous().to(DEV)
+        y = torch.full((m, w.n), float("nan"), dtype=torch.float32, device=DEV)
+        qw = torch.empty((m, w.k), dtype=torch.int8, device=DEV)
+        xw = torch.empty((m, w.k // 128), dtype=torch.float32, device=DEV)
+        pq2.pq2_gemv_tiles(xd, tiles, y, qw, xw)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32)), f"{name} m={m}"
+        if m == 1 and w.k <= 8192:  # the fused path needs no scratch
+            y.fill_(float("nan"))
+            pq2.pq2_gemv_tiles(xd, tiles, y)
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32)), f"{name} m=1 no scratch"
+
+
 # ------------------------------------------------------------------ smaller activation groups
 # Page "Kernel experiments: recorded evidence", section C (Tests 8 and 9).
 def quantise_g_both(x_cpu, agroup, dtype="bf16", k=None):
