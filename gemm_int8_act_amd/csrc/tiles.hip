@@ -55,7 +55,7 @@ namespace {
 constexpr int kTileRows = 16;
 constexpr int kCodeBlock = 1024;   // one (tile, group pair) code block
 constexpr int kSegUnit = 4 * kCodeBlock + 256;  // one (tile, 8 groups) unit: codes then scales
-constexpr int kTilesMaxColumns = 4;
+constexpr int kTilesMaxColumns = 8;
 
 struct TileGeometry {
     int64_t tiles, s8, total;
@@ -127,24 +127,31 @@ __global__ void prepare_tile_scales_kernel(const uint8_t* __restrict__ raw, int6
 
 __device__ __forceinline__ void keep_order() { __builtin_amdgcn_sched_barrier(0); }
 
-// j mod mcount for j < 16 and mcount = 1..4 (mcount is uniform), without
+// j mod mcount for j < 16 and mcount = 1..8 (mcount is uniform), without
 // the generic integer division.
 __device__ __forceinline__ int small_mod(int j, int mcount) {
-    if (mcount == 4) return j & 3;
+    if (mcount == 4 || mcount == 8) return j & (mcount - 1);
     if (mcount == 3) return j - 3 * ((j * 11) >> 5);  // (j * 11) >> 5 == j / 3 for j < 16
     if (mcount == 2) return j & 1;
+    if (mcount > 4) return j >= 2 * mcount ? j - 2 * mcount : (j >= mcount ? j - mcount : j);
     return 0;
 }
 
-// Per-wave LDS: MC staged columns of CPW groups and a spare column (each
-// padded by 64 bytes: the columns of one A read fall in distinct banks), then
-// 8 x 8 floats of xs and 8 x 8 ints of -sum(q) (group class x column).
-__host__ __device__ constexpr int tiles_col_pitch(int cpw) { return 128 * cpw + 64; }
+// Per-wave LDS: the staged columns of CPW groups (each padded by 64 bytes:
+// the columns of one A read fall in distinct banks), then 8 x 8 floats of xs
+// and 8 x 8 ints of -sum(q) (group class x column, up to eight columns).
 // With activation groups of ag < 128 elements the xs and -sum(q) tables hold
 // 128/ag entries per class, and ag = 32 adds a zero block that the lanes
 // outside a 32-element group read as their A operand.
+__host__ __device__ constexpr int tiles_col_pitch(int cpw) { return 128 * cpw + 64; }
+// Staged columns: MC, plus a spare column that takes the stores of lanes
+// past the last column when a staging load spans more columns than remain
+// (8 / CPW columns per load).
+__host__ __device__ constexpr int tiles_cols_staged(int mc, int cpw) {
+    return mc + (((mc + 8 / cpw - 1) / (8 / cpw)) * (8 / cpw) > mc ? 1 : 0);
+}
 __host__ __device__ constexpr int tiles_region_bytes(int mc, int cpw, int ag = 128) {
-    return (mc + 1) * tiles_col_pitch(cpw) + 512 * (128 / ag) + (ag == 32 ? 128 * cpw : 0);
+    return tiles_cols_staged(mc, cpw) * tiles_col_pitch(cpw) + 512 * (128 / ag) + (ag == 32 ? 128 * cpw : 0);
 }
 
 __device__ __forceinline__ float half_of(const uint4& v, int c) {
@@ -155,6 +162,11 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
 // SRC: kSrcNatural reads q and xs; kSrcBf16 / kSrcF16 / kSrcF32 read x and
 // quantise each staged group in the wave (the exact in-kernel quantiser, so
 // the codes and scales are those of pq2_quantize_act_i8).
+//
+// MC: columns per pass, 1..4 or 8.  A row i holds column i mod mcount, so D
+// row 4*kb + r is column 4*kb + r: with MC = 8 the lanes kb = 0 and 1 both
+// hold outputs (columns 0..3 and 4..7), one decode of each code word feeding
+// eight columns.
 //
 // AG: activation group size (128; 64 or 32 for the smaller activation groups
 // of page "Kernel experiments: recorded evidence", section C, Tests 8 and 9:
@@ -182,6 +194,10 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     constexpr int XSL = (XSV + 63) / 64;    // their loads per lane
     static_assert(AG == 128 || AG == 64 || AG == 32, "activation group");
     static_assert(AG == 128 || !src_fused(SRC), "smaller activation groups read natural-order q");
+    static_assert(MC <= 4 || (MC == 8 && AG == 128), "eight-column passes take 128-element activation groups");
+    constexpr int R = MC < 4 ? MC : 4;      // outputs per lane and class (D rows 4*kb + r)
+    constexpr int KBU = MC > 4 ? 2 : 1;     // lane groups kb holding outputs
+    constexpr bool XS_VEC = !src_fused(SRC) && (AG < 128 || MC > 4);  // xs through LDS from vector loads
     const int nwaves = blockDim.x >> 6;
     const int nslices = nwaves / WPS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -199,8 +215,8 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     const auto tile_rs = make_rsrc(tiles + (size_t)tile * s8 * kSegUnit, (uint32_t)(s8 * kSegUnit));
     const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
     const i32x4_t xs_srs = make_srsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
-    const auto xsa_rs = make_rsrc(AG == 128 ? nullptr : xs + (size_t)m0 * groups * S,
-                                  AG == 128 ? 0u : (uint32_t)(mcount * groups * S * 4));
+    const auto xsa_rs = make_rsrc(XS_VEC ? xs + (size_t)m0 * groups * S : nullptr,
+                                  XS_VEC ? (uint32_t)(mcount * groups * S * 4) : 0u);
     const auto x_rs = make_rsrc(
         FUSED ? static_cast<const unsigned char*>(x) + (size_t)m0 * x_stride * src_esize(SRC) : nullptr,
         FUSED ? (uint32_t)(((int64_t)(mcount - 1) * x_stride + k) * src_esize(SRC)) : 0u);
@@ -214,8 +230,8 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     //    blocks are in flight), then xs.  Groups past the end read zeros.
     uint4 qv[QLOADS];
     uint4 xv[QLOADS][FUSED ? XL : 1];
-    float xss[FUSED || AG < 128 ? 1 : MC][CPW];  // xs of the wave's groups, scalar loads (uniform)
-    uint32_t xsa[AG < 128 ? XSL : 1];              // xs of activation groups (AG < 128), vector loads
+    float xss[FUSED || XS_VEC ? 1 : MC][CPW];  // xs of the wave's groups, scalar loads (uniform)
+    uint32_t xsa[XS_VEC ? XSL : 1];              // xs through LDS (AG < 128 or MC > 4), vector loads
     uint4 wsv;
     uint4 cw[CPW / 2];
     auto issue = [&](int s) {
@@ -239,7 +255,7 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
         for (int b = 0; b < CPW / 2; ++b)
             cw[b] = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + (c_lo / 2 + b) * kCodeBlock + 16 * lane);
         keep_order();
-        if constexpr (AG < 128) {
+        if constexpr (XS_VEC) {
             // Value i of the segment: column i / (CPW*S), activation group
             // (8s + c_lo)*S + i % (CPW*S).
 #pragma unroll
@@ -269,14 +285,14 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
             }
         }
     };
-    // Private region: MC staged columns (CPW groups each) and one column that
-    // takes the stores of lanes past the last column, then per class c of the
-    // wave 8 floats xs[c][m] and 8 ints -sum(q)[c][m].
+    // Private region: the staged columns (CPW groups each), then per class c
+    // of the wave 8 floats xs[c][m] and 8 ints -sum(q)[c][m].
     unsigned char* region = smem + (size_t)wave * tiles_region_bytes(MC, CPW, AG);
     float* red = reinterpret_cast<float*>(smem + (size_t)nwaves * tiles_region_bytes(MC, CPW, AG));
-    float* xs_lds = reinterpret_cast<float*>(region + (MC + 1) * PITCH);
-    int* nsq_lds = reinterpret_cast<int*>(region + (MC + 1) * PITCH + 256 * S);
-    const unsigned char* zero_lds = region + (MC + 1) * PITCH + 512 * S;  // AG == 32 only
+    constexpr int NCOLS = tiles_cols_staged(MC, CPW);
+    float* xs_lds = reinterpret_cast<float*>(region + NCOLS * PITCH);
+    int* nsq_lds = reinterpret_cast<int*>(region + NCOLS * PITCH + 256 * S);
+    const unsigned char* zero_lds = region + NCOLS * PITCH + 512 * S;  // AG == 32 only
     // A row i reads column i mod mcount: rows >= mcount repeat real columns,
     // so one read touches at most 4 x 16 distinct banks, and the D rows they
     // produce are never used.
@@ -291,11 +307,12 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     const unsigned char* a_grp[2] = {AG == 32 && (kb >> 1) != 0 ? zero_lds : a_base,
                                      AG == 32 && (kb >> 1) != 1 ? zero_lds : a_base};
 
-    float acc[CPW][MC];
+    float acc[CPW][R];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
-        for (int r = 0; r < MC; ++r) acc[c][r] = 0.0f;
+        for (int r = 0; r < R; ++r) acc[c][r] = 0.0f;
+    const int col4 = MC > 4 ? 4 * (kb & 1) : 0;  // first column of this lane's D rows
 
     // Every wave has at least one segment (slice * per_wave < nseg), so the
     // loop has no zero-trip test and the kernel arguments load in one go.
@@ -334,7 +351,7 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
             if ((lane & (LPS - 1)) == 0 && m < MC)
                 nsq_lds[((c_lo + (ch >> 3)) * S + (ch & 7) / LPS) * 8 + m] = -sq;
         }
-        if constexpr (AG < 128) {
+        if constexpr (XS_VEC) {
 #pragma unroll
             for (int t = 0; t < XSL; ++t) {
                 const int i = t * 64 + lane;
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
                     const float4 xg = *reinterpret_cast<const float4*>(xs_lds + ((c_lo + c) * S + t) * 8);
                     const float xv[4] = {xg.x, xg.y, xg.z, xg.w};
 #pragma unroll
-                    for (int r = 0; r < MC; ++r) acc[c][r] = __builtin_fmaf((float)Dt[t][r] * xv[r], wsf, acc[c][r]);
+                    for (int r = 0; r < R; ++r) acc[c][r] = __builtin_fmaf((float)Dt[t][r] * xv[r], wsf, acc[c][r]);
                 }
             }
           } else {
@@ -399,9 +416,9 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
                 const uint4 a1 = *reinterpret_cast<const uint4*>(a_base + 128 * c + 64);
                 A[p][0] = v4i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
                 A[p][1] = v4i{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                const int4 nsq = *reinterpret_cast<const int4*>(nsq_lds + (c_lo + c) * 8);
+                const int4 nsq = *reinterpret_cast<const int4*>(nsq_lds + (c_lo + c) * 8 + col4);
                 D[p] = v4i{nsq.x, nsq.y, nsq.z, nsq.w};
-                if constexpr (FUSED) xsg[p] = *reinterpret_cast<const float4*>(xs_lds + (c_lo + c) * 8);
+                if constexpr (FUSED || XS_VEC) xsg[p] = *reinterpret_cast<const float4*>(xs_lds + (c_lo + c) * 8 + col4);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const uint32_t d = word_of(cw[c >> 1], 2 * (c & 1) + h);
@@ -418,14 +435,14 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
                 const int c = c0 + p;
                 const float wsf = half_of(wsv, c_lo + c);
                 float xv[4];
-                if constexpr (FUSED) {
+                if constexpr (FUSED || XS_VEC) {
                     xv[0] = xsg[p].x; xv[1] = xsg[p].y; xv[2] = xsg[p].z; xv[3] = xsg[p].w;
                 } else {
 #pragma unroll
-                    for (int r = 0; r < MC; ++r) xv[r] = xss[r][c];
+                    for (int r = 0; r < R; ++r) xv[r] = xss[r][c];
                 }
 #pragma unroll
-                for (int r = 0; r < MC; ++r) acc[c][r] = __builtin_fmaf((float)D[p][r] * xv[r], wsf, acc[c][r]);
+                for (int r = 0; r < R; ++r) acc[c][r] = __builtin_fmaf((float)D[p][r] * xv[r], wsf, acc[c][r]);
             }
           }
         }
@@ -439,64 +456,71 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     //    columns live in the lanes with kb = 0.  A wave that holds all eight
     //    classes adds them in registers.
     if constexpr (CPW == 8) {
-        float part[MC];
+        float part[R];
 #pragma unroll
-        for (int r = 0; r < MC; ++r)
+        for (int r = 0; r < R; ++r)
             part[r] = ((acc[0][r] + acc[4][r]) + (acc[1][r] + acc[5][r])) +
                       ((acc[2][r] + acc[6][r]) + (acc[3][r] + acc[7][r]));
         const int row = tile * kTileRows + j;
         if (nwaves == 1) {
-            if (kb == 0 && row < n) {
+            if (kb < KBU && row < n) {
 #pragma unroll
-                for (int r = 0; r < MC; ++r)
-                    if (r < mcount) y[(size_t)(m0 + r) * n + row] = part[r];
+                for (int r = 0; r < R; ++r)
+                    if (col4 + r < mcount) y[(size_t)(m0 + col4 + r) * n + row] = part[r];
             }
             return;
         }
-        if (kb == 0) {
+        if (kb < KBU) {
 #pragma unroll
-            for (int r = 0; r < MC; ++r) red[(wave * MC + r) * kTileRows + j] = part[r];
+            for (int r = 0; r < R; ++r) red[(wave * MC + col4 + r) * kTileRows + j] = part[r];
         }
         __syncthreads();
         // Wave 0 adds the slices in index order.  All reads go out before the
         // first add; slots past the last slice re-read the last one and are
         // not added.
-        if (wave == 0 && lane < MC * kTileRows) {
-            const int r = lane >> 4;
-            float v[8];
 #pragma unroll
-            for (int w = 0; w < 8; ++w) v[w] = red[(min(w, nwaves - 1) * MC + r) * kTileRows + j];
-            float sum = v[0];
+        for (int o0 = 0; o0 < MC * kTileRows; o0 += 64) {
+            const int o = o0 + lane;
+            if (wave == 0 && o < MC * kTileRows) {
+                const int col = o >> 4;
+                float v[8];
 #pragma unroll
-            for (int w = 1; w < 8; ++w)
-                if (w < nwaves) sum += v[w];
-            const int row = tile * kTileRows + j;
-            if (r < mcount && row < n) y[(size_t)(m0 + r) * n + row] = sum;
+                for (int w = 0; w < 8; ++w) v[w] = red[(min(w, nwaves - 1) * MC + col) * kTileRows + j];
+                float sum = v[0];
+#pragma unroll
+                for (int w = 1; w < 8; ++w)
+                    if (w < nwaves) sum += v[w];
+                if (col < mcount && row < n) y[(size_t)(m0 + col) * n + row] = sum;
+            }
         }
         return;
     }
-    if (kb == 0) {
+    if (kb < KBU) {
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
-            for (int r = 0; r < MC; ++r) red[((slice * 8 + c_lo + c) * MC + r) * kTileRows + j] = acc[c][r];
+            for (int r = 0; r < R; ++r) red[((slice * 8 + c_lo + c) * MC + col4 + r) * kTileRows + j] = acc[c][r];
     }
     __syncthreads();
-    if (wave == 0 && lane < MC * kTileRows) {
-        const int r = lane >> 4;
-        constexpr int C = MC * kTileRows;  // stride between classes
-        float t[8];
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            const float* a = red + ((size_t)min(w, nslices - 1) * 8 * MC + r) * kTileRows + j;
-            t[w] = ((a[0] + a[4 * C]) + (a[1 * C] + a[5 * C])) + ((a[2 * C] + a[6 * C]) + (a[3 * C] + a[7 * C]));
+    for (int o0 = 0; o0 < MC * kTileRows; o0 += 64) {
+        const int o = o0 + lane;
+        if (wave == 0 && o < MC * kTileRows) {
+            const int col = o >> 4;
+            constexpr int C = MC * kTileRows;  // stride between classes
+            float t[8];
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const float* a = red + ((size_t)min(w, nslices - 1) * 8 * MC + col) * kTileRows + j;
+                t[w] = ((a[0] + a[4 * C]) + (a[1 * C] + a[5 * C])) + ((a[2 * C] + a[6 * C]) + (a[3 * C] + a[7 * C]));
+            }
+            float sum = t[0];
+#pragma unroll
+            for (int w = 1; w < 8; ++w)
+                if (w < nslices) sum += t[w];
+            const int row = tile * kTileRows + j;
+            if (col < mcount && row < n) y[(size_t)(m0 + col) * n + row] = sum;
         }
-        float sum = t[0];
-#pragma unroll
-        for (int w = 1; w < 8; ++w)
-            if (w < nslices) sum += t[w];
-        const int row = tile * kTileRows + j;
-        if (r < mcount && row < n) y[(size_t)(m0 + r) * n + row] = sum;
     }
 }
 
@@ -516,7 +540,8 @@ hipError_t launch_tiles_one(const TilesArgs& a, int slices, int nseg, int per_wa
     const int64_t m = a.m, n = a.n, k = a.k;
     const TileGeometry t = geometry(n, k);
     const int waves = slices * (8 / CPW);
-    const size_t lds = (size_t)waves * tiles_region_bytes(MC, CPW, AG) + (size_t)slices * 8 * MC * kTileRows * 4;
+    const size_t lds = (size_t)waves * tiles_region_bytes(MC, CPW, AG) +
+                       (size_t)(CPW == 8 ? waves : slices * 8) * MC * kTileRows * 4;
     const dim3 grid((unsigned)t.tiles, (unsigned)chunks);
     clear_stale_error();
     hipLaunchKernelGGL((small_m_tiles_kernel<MC, CPW, SRC, AG>), grid, dim3(64 * waves), lds, a.stream, a.q, a.xs, a.x,
@@ -531,6 +556,9 @@ hipError_t launch_tiles_mc(int mc, const TilesArgs& a, int slices, int nseg, int
         case 2: return launch_tiles_one<2, CPW, SRC, AG>(a, slices, nseg, per_wave, chunks);
         case 3: return launch_tiles_one<3, CPW, SRC, AG>(a, slices, nseg, per_wave, chunks);
         case 4: return launch_tiles_one<4, CPW, SRC, AG>(a, slices, nseg, per_wave, chunks);
+        case 8:
+            if constexpr (AG == 128) return launch_tiles_one<8, CPW, SRC, AG>(a, slices, nseg, per_wave, chunks);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
@@ -575,13 +603,13 @@ static int tiles_slices(int64_t k, int max_waves, int* nseg, int* per_wave) {
     return (*nseg + *per_wave - 1) / *per_wave;
 }
 
-// Two waves per slice pay only when each slice spans several segments
-// (long k) and there are four or more columns (measured on the K = 5120 and
-// K = 17408 shapes); the split never changes the bits.
+// One wave per slice: with the activation scales through the scalar unit
+// and eight-column passes, splitting a slice over two waves no longer pays
+// at any measured shape (K = 17408: 9.71 against 9.87 us at four columns,
+// 16.6 against 21.0 us at sixteen); the split never changes the bits.
 int tiles_default_split(int64_t m, int64_t k, int max_waves) {
-    int nseg, per_wave;
-    const int slices = tiles_slices(k, max_waves, &nseg, &per_wave);
-    return (per_wave >= 2 && m >= 4 && slices * 2 <= 16) ? 2 : 1;
+    (void)m, (void)k, (void)max_waves;
+    return 1;
 }
 
 bool tiles_supported(int64_t k, int max_waves, int split) {
@@ -594,9 +622,18 @@ static hipError_t launch_tiles_any(int src, const TilesArgs& a, int max_waves, i
     if (!tiles_supported(a.k, max_waves, split)) return hipErrorInvalidValue;
     int nseg, per_wave;
     const int slices = tiles_slices(a.k, max_waves, &nseg, &per_wave);
-    int mc = (int)(a.m < kTilesMaxColumns ? a.m : kTilesMaxColumns);
-    const int chunks = (int)((a.m + mc - 1) / mc);
+    // Up to four columns: one pass of exactly M.  More: passes of at most
+    // four, or, when every wave holds several segments (long k) and the
+    // activation groups are 128, passes of eight, the last one partial.
+    // (Eight-column passes halve the weight reads; at short k with many
+    // tiles they measured no faster: up, M = 8: 12.3 against 12.1 us.)
+    int mc = (int)(a.m < 4 ? a.m : 4);
+    int chunks = (int)((a.m + mc - 1) / mc);
     mc = (int)((a.m + chunks - 1) / chunks);
+    if (a.m > 4 && agroup == 128 && per_wave >= 2) {
+        mc = kTilesMaxColumns;
+        chunks = (int)((a.m + kTilesMaxColumns - 1) / kTilesMaxColumns);
+    }
     if (agroup == 64) return launch_tiles_split<kSrcNatural, 64>(split, mc, a, slices, nseg, per_wave, chunks);
     if (agroup == 32) return launch_tiles_split<kSrcNatural, 32>(split, mc, a, slices, nseg, per_wave, chunks);
     switch (src) {
