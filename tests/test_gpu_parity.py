@@ -155,7 +155,7 @@ SMALL_SHAPES = [
     # (m, n, k): several row tiles, ragged row tail, partial last segment of groups
     (1, 1024, 512), (1, 1, 128), (2, 333, 640), (3, 97, 1152), (4, 1000, 5120),
     (5, 77, 2176), (8, 130, 384), (9, 61, 1024), (16, 40, 17408), (12, 300, 3072),
-    (6, 513, 9216), (4, 64, 34816), (2, 24, 65536), (1, 4096, 16384),
+    (6, 513, 9216), (4, 64, 34816), (2, 24, 65536), (1, 4096, 16384), (11, 70, 9216),
 ]
 
 
@@ -333,7 +333,7 @@ def test_small_m_tiles_full(m, n, k):
     assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), "tile layout and planes differ"
 
 
-@pytest.mark.parametrize("m", [1, 3, 4, 6])
+@pytest.mark.parametrize("m", [1, 3, 4, 6, 13])
 def test_small_m_tiles_waves(m):
     """Every k split gives the bits of the planes path at the same split."""
     pq2 = _pq2()
