@@ -471,15 +471,32 @@ def bench_prefill(torch, pq2, workloads, dev, stream):
             t_us = time_graph(torch, Graph(torch, f, stream), stream, 5) / 10 * 1e3
             tp_us = time_graph(torch, Graph(torch, fp, stream), stream, 5) / 10 * 1e3
             tt_us = time_graph(torch, Graph(torch, ft, stream), stream, 5) / 10 * 1e3
+            # Smaller activation groups (one scale per 64 or 32 activations),
+            # same weights: the tile-layout prefill with per-group rescales.
+            ag_us = {}
+            for agroup in (64, 32):
+                qg = torch.empty((m, w.k), dtype=torch.int8, device=dev)
+                xsg = torch.empty((m, w.k // agroup), dtype=torch.float32, device=dev)
+                yg = torch.empty((m, w.n), dtype=torch.float32, device=dev)
+                with torch.cuda.stream(stream):
+                    pq2.pq2_quantize_act_i8_g(x[:m], qg, xsg, agroup, stream=stream)
+
+                def fg(qg=qg, xsg=xsg, yg=yg, agroup=agroup):
+                    for _ in range(10):
+                        pq2.pq2_matmul_prefill_tiles_g(qg, xsg, tiles, yg, agroup, stream=stream)
+
+                ag_us[agroup] = time_graph(torch, Graph(torch, fg, stream), stream, 5) / 10 * 1e3
             torch.cuda.synchronize()
             assert torch.equal(yt.view(torch.int32), y.view(torch.int32)), f"prefill from tiles differs at M={m}"
             ops = 2.0 * m * w.n * w.k
             tops = ops / (tt_us * 1e-6) / 1e12
             out[f"{name}_m{m}"] = {"us": round(tt_us, 2), "TOPS": round(tops, 1),
                                    "pct_int8_peak": round(100 * tops * 1e12 / PEAK_INT8_OPS_PER_S, 1),
-                                   "planes_us": round(t_us, 2), "planes_plane_order_us": round(tp_us, 2)}
+                                   "planes_us": round(t_us, 2), "planes_plane_order_us": round(tp_us, 2),
+                                   "agroup64_us": round(ag_us[64], 2), "agroup32_us": round(ag_us[32], 2)}
             log(f"[bench] {name} M={m}: tile layout {tt_us:.1f} us, {tops:.0f} TOPS (planes {t_us:.1f} us, "
-                f"planes with plane-order input {tp_us:.1f} us)")
+                f"planes with plane-order input {tp_us:.1f} us; activation groups 64 / 32: "
+                f"{ag_us[64]:.1f} / {ag_us[32]:.1f} us)")
         del planes, tiles
     return out
 

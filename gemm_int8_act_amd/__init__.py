@@ -52,6 +52,7 @@ EXPORTED = (
     "pq2_quantize_act_i8_g",
     "pq2_matmul_small_m_tiles_g",
     "pq2_gemv_tiles",
+    "pq2_matmul_prefill_tiles_g",
 )
 
 
@@ -125,6 +126,8 @@ def _load_library():
     lib.pq2_quantize_act_i8_g.restype = i32
     lib.pq2_matmul_small_m_tiles_g.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
     lib.pq2_matmul_small_m_tiles_g.restype = i32
+    lib.pq2_matmul_prefill_tiles_g.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
+    lib.pq2_matmul_prefill_tiles_g.restype = i32
     lib.pq2_matmul_small_m_tiles_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tiles_tuned.restype = i32
     lib.pq2_matmul_prefill_tiles.argtypes = [p, p, p, i64, i64, i64, p, p]
@@ -332,9 +335,7 @@ def pq2_quantize_act_i8_g(x, q, xs, agroup: int, stream=None) -> None:
                                      _dev_ptr(xs, "xs"), _stream(stream)), "pq2_quantize_act_i8_g")
 
 
-def pq2_matmul_small_m_tiles_g(q, xs, tiles, y, agroup: int, stream=None) -> None:
-    """Tile-layout decode matmul with activation groups of agroup elements
-    (q, xs from pq2_quantize_act_i8_g with the same agroup)."""
+def _tiles_g_args(q, xs, tiles, y, agroup):
     import torch
     if agroup not in (128, 64, 32):
         raise ValueError("agroup must be 128, 64 or 32")
@@ -347,8 +348,21 @@ def pq2_matmul_small_m_tiles_g(q, xs, tiles, y, agroup: int, stream=None) -> Non
     n = y.shape[1]
     if y.shape[0] != m or xs.numel() != m * (k // agroup) or tiles.numel() < pq2_tiles_bytes(n, k):
         raise ValueError("shape mismatch between q, xs, tiles and y")
-    _check(lib.pq2_matmul_small_m_tiles_g(_dev_ptr(q, "q"), _dev_ptr(xs, "xs"), _dev_ptr(tiles, "tiles"), m, n, k,
-                                          agroup, _dev_ptr(y, "y"), _stream(stream)), "pq2_matmul_small_m_tiles_g")
+    return (_dev_ptr(q, "q"), _dev_ptr(xs, "xs"), _dev_ptr(tiles, "tiles"), m, n, k, agroup, _dev_ptr(y, "y"))
+
+
+def pq2_matmul_small_m_tiles_g(q, xs, tiles, y, agroup: int, stream=None) -> None:
+    """Tile-layout decode matmul with activation groups of agroup elements
+    (q, xs from pq2_quantize_act_i8_g with the same agroup)."""
+    _check(lib.pq2_matmul_small_m_tiles_g(*_tiles_g_args(q, xs, tiles, y, agroup), _stream(stream)),
+           "pq2_matmul_small_m_tiles_g")
+
+
+def pq2_matmul_prefill_tiles_g(q, xs, tiles, y, agroup: int, stream=None) -> None:
+    """Tile-layout prefill matmul with activation groups of agroup elements
+    (q, xs from pq2_quantize_act_i8_g with the same agroup)."""
+    _check(lib.pq2_matmul_prefill_tiles_g(*_tiles_g_args(q, xs, tiles, y, agroup), _stream(stream)),
+           "pq2_matmul_prefill_tiles_g")
 
 
 def pq2_matmul_prefill_tiles(q, xs, tiles, y, stream=None) -> None:

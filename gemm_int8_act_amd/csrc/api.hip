@@ -360,6 +360,16 @@ int pq2_matmul_prefill_tiles(const int8_t* q, const float* xs, const void* tiles
     return pq2_matmul_prefill_tiles_tuned(q, xs, tiles, m, n, k, y, 0, stream);
 }
 
+int pq2_matmul_prefill_tiles_g(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n, int64_t k,
+                               int64_t agroup, float* y, void* stream) {
+    if (agroup != 128 && agroup != 64 && agroup != 32) return PQ2_EINVAL;
+    if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, kMaxPrefillM, true)) return rc;
+    if (overlap(y, (size_t)m * n * 4, xs, (size_t)m * (k / agroup) * 4)) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_prefill_tiles_g(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, y, 0,
+                                                     (int)agroup, (hipStream_t)stream));
+}
+
 int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream) {
     return pq2_matmul_prefill_tuned(q, xs, planes, m, n, k, y, 0, stream);

@@ -82,6 +82,10 @@ hipError_t launch_small_m_tiles(const int8_t* q, const float* xs, const uint8_t*
                                 int64_t k, float* y, int max_waves, int split, hipStream_t stream);
 hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int tile, hipStream_t stream);
+// Tile-layout prefill with activation groups of agroup = 128, 64 or 32
+// (natural-order q, xs [m][k/agroup]); tile 0 picks the default.
+hipError_t launch_prefill_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                  int64_t k, float* y, int tile, int agroup, hipStream_t stream);
 hipError_t launch_small_m_tiles_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* tiles, int64_t m,
                                       int64_t n, int64_t k, float* y, int max_waves, int split, hipStream_t stream);
 // Tile engine with activation groups of agroup = 128, 64 or 32 (natural-order

@@ -60,7 +60,13 @@ __device__ __forceinline__ int swz(int i, int t) { return i * 8 + (t ^ ((i >> 1)
 // a code dword are natural-order weights and natural-order q is staged as it
 // is (no byte transpose).  Each thread then stages 8-byte pieces: the two
 // code dwords (k-blocks kb and 4 + kb) of one row and group.
-template <int BM, int BN, bool PLANE_A, bool TILES>
+//
+// AG: activation group size.  128, or (tile layout only, where k-step kk
+// covers natural positions 32kk .. 32kk + 31 of the group) 64 or 32 for the
+// smaller activation groups of page "Kernel experiments: recorded evidence",
+// section C, Tests 8 and 9: each activation group's k-steps form their own
+// INT32 chain, rescaled by its own xs into acc, in k order.
+template <int BM, int BN, bool PLANE_A, bool TILES, int AG = 128>
 __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__ q,
                                                       const float* __restrict__ xs,
                                                       const uint8_t* __restrict__ codes,
@@ -72,9 +78,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     constexpr int NT = BN / 64;          // 32-column tiles per wave
     constexpr int AQ = BM * 8 / 256;     // A quads staged per thread
     constexpr int BI = BN * 2;           // B items (row, half) per group
+    constexpr int S = 128 / AG;          // activation groups per weight group
+    constexpr int KS = 4 / S;            // k-steps per activation group
+    static_assert(AG == 128 || (TILES && (AG == 64 || AG == 32)), "smaller activation groups: tile layout only");
     __shared__ uint4 As[2][BM * 8];
     __shared__ uint4 Bs[2][BN * 8];
-    __shared__ float xsS[2][BM];
+    __shared__ float xsS[2][S][BM];
     __shared__ float wsS[2][BN];
 
     const int tid = threadIdx.x;
@@ -99,7 +108,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     const int tiles_here = (nrows + 15) / 16;
     const auto c_rs = TILES ? make_rsrc(codes + (size_t)(nb / 16) * s8 * 4352, (uint32_t)(tiles_here * s8 * 4352))
                             : make_rsrc(codes + (size_t)nb * k4, (uint32_t)(nrows * k4));
-    const auto x_rs = make_rsrc(xs + (size_t)mb * groups, (uint32_t)(mrows * groups * 4));
+    const auto x_rs = make_rsrc(xs + (size_t)mb * groups * S, (uint32_t)(mrows * groups * S * 4));
     const auto s_rs = make_rsrc(scales + (size_t)nb * groups, (uint32_t)(nrows * groups * 2));
     uint32_t a_off[AQ];
 #pragma unroll
@@ -119,13 +128,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     }
     const bool s_is_x = tid < BM;
     const bool s_is_w = tid >= 256 - BN;
-    const uint32_t s_off = s_is_x ? (uint32_t)(tid * groups * 4)
+    const uint32_t s_off = s_is_x ? (uint32_t)(tid * groups * S * 4)
                                   : (s_is_w ? (uint32_t)((tid - (256 - BN)) * groups * 2) : kBufferOOB);
 
     uint4 areg[AQ];
     uint4 breg;
     uint2 treg[TI];
     uint32_t sreg;
+    uint32_t xreg[S];
 
     auto load_stage = [&](int g) {
 #pragma unroll
@@ -138,9 +148,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
         } else {
             breg = buf_load16(c_rs, b_off == kBufferOOB ? kBufferOOB : b_off + (uint32_t)g * 32u);
         }
-        if (s_is_x)
-            sreg = buf_load4(x_rs, s_off + (uint32_t)g * 4u);
-        else if constexpr (TILES)
+        if (s_is_x) {
+#pragma unroll
+            for (int t = 0; t < S; ++t) xreg[t] = buf_load4(x_rs, s_off + (uint32_t)(g * S + t) * 4u);
+        } else if constexpr (TILES)
             sreg = buf_load2(c_rs, s_is_w ? (uint32_t)((((tid - (256 - BN)) >> 4) * s8 + (g >> 3)) * 4352 + 4096 +
                                                        16 * ((tid - (256 - BN)) & 15) + 2 * (g & 7))
                                           : kBufferOOB);
@@ -182,8 +193,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
                                lut_plane((d >> 4) & 0x03030303u), lut_plane((d >> 6) & 0x03030303u));
             }
         }
-        if (s_is_x) xsS[buf][tid] = __uint_as_float(sreg);
-        else if (s_is_w) wsS[buf][tid - (256 - BN)] = __half2float(__ushort_as_half((unsigned short)sreg));
+        if (s_is_x) {
+#pragma unroll
+            for (int t = 0; t < S; ++t) xsS[buf][t][tid] = __uint_as_float(xreg[t]);
+        } else if (s_is_w) wsS[buf][tid - (256 - BN)] = __half2float(__ushort_as_half((unsigned short)sreg));
     };
     // Fragment read slots per k-step (fixed for the whole kernel).
     int af_slot[4][MT], bf_slot[4][NT];
@@ -211,9 +224,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
         const int buf = g & 1;
         if (g + 1 < groups) load_stage(g + 1);
 
+        // Activation group t of this weight group: k-steps KS*t .. KS*t + KS - 1.
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
         v16i D[MT][NT];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int u = 0; u < KS; ++u) {
+            const int kk = KS * t + u;
             v4i af[MT], bf[NT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -229,7 +246,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    if (kk == 0)
+                    if (u == 0)
                         D[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[nt], v16i{}, 0, 0, 0);
                     else
                         D[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[nt], D[mt][nt], 0, 0, 0);
@@ -246,7 +263,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
                     const float4 xv =
-                        *reinterpret_cast<const float4*>(&xsS[buf][wm * (BM / 2) + mt * 32 + rb * 8 + hi * 4]);
+                        *reinterpret_cast<const float4*>(&xsS[buf][t][wm * (BM / 2) + mt * 32 + rb * 8 + hi * 4]);
                     const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -255,6 +272,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
                     }
                 }
             }
+        }
+        // One activation group's chain at a time: the empty statement takes
+        // the sums as operands and orders memory, so this group's rescale
+        // finishes before the next group's fragments are read.  Without it the
+        // compiler starts every group's products first and holds S sets of D.
+        if constexpr (S > 1) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(acc[mt][nt][r]) : : "memory");
+        }
         }
         if (g + 1 < groups) store_stage(buf ^ 1);
         __syncthreads();
@@ -275,25 +305,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 
 namespace {
 
-template <int BM, int BN, bool PLANE_A, bool TILES>
+template <int BM, int BN, bool PLANE_A, bool TILES, int AG = 128>
 hipError_t launch_tile(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
                        int64_t k, float* y, hipStream_t stream) {
     const uint16_t* scales = TILES ? nullptr : reinterpret_cast<const uint16_t*>(planes + n * (k / 4));
     const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
     clear_stale_error();
-    hipLaunchKernelGGL((prefill_kernel<BM, BN, PLANE_A, TILES>), grid, dim3(256), 0, stream, q, xs, planes, scales,
+    hipLaunchKernelGGL((prefill_kernel<BM, BN, PLANE_A, TILES, AG>), grid, dim3(256), 0, stream, q, xs, planes, scales,
                        y, (int)m, (int)n, (int)k, (int)(k / 128));
     return hipGetLastError();
 }
 
-template <bool PLANE_A, bool TILES>
+template <bool PLANE_A, bool TILES, int AG = 128>
 hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
                            int64_t k, float* y, int tile, hipStream_t stream) {
     switch (tile) {
-        case 1: return launch_tile<128, 128, PLANE_A, TILES>(q, xs, planes, m, n, k, y, stream);
-        case 2: return launch_tile<64, 128, PLANE_A, TILES>(q, xs, planes, m, n, k, y, stream);
-        case 3: return launch_tile<64, 64, PLANE_A, TILES>(q, xs, planes, m, n, k, y, stream);
-        case 4: return launch_tile<128, 64, PLANE_A, TILES>(q, xs, planes, m, n, k, y, stream);
+        case 1: return launch_tile<128, 128, PLANE_A, TILES, AG>(q, xs, planes, m, n, k, y, stream);
+        case 2: return launch_tile<64, 128, PLANE_A, TILES, AG>(q, xs, planes, m, n, k, y, stream);
+        case 3: return launch_tile<64, 64, PLANE_A, TILES, AG>(q, xs, planes, m, n, k, y, stream);
+        case 4: return launch_tile<128, 64, PLANE_A, TILES, AG>(q, xs, planes, m, n, k, y, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -322,6 +352,17 @@ hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t*
                                 int64_t k, float* y, int tile, hipStream_t stream) {
     if (tile == 0) tile = default_prefill_tile(m, n, false);
     return launch_any_tile<false, true>(q, xs, tiles, m, n, k, y, tile, stream);
+}
+
+hipError_t launch_prefill_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                  int64_t k, float* y, int tile, int agroup, hipStream_t stream) {
+    if (tile == 0) tile = default_prefill_tile(m, n, false);
+    switch (agroup) {
+        case 128: return launch_any_tile<false, true>(q, xs, tiles, m, n, k, y, tile, stream);
+        case 64: return launch_any_tile<false, true, 64>(q, xs, tiles, m, n, k, y, tile, stream);
+        case 32: return launch_any_tile<false, true, 32>(q, xs, tiles, m, n, k, y, tile, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace pq2

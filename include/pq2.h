@@ -387,6 +387,19 @@ int pq2_matmul_prefill_tiles(const int8_t* q, const float* xs, const void* tiles
 int pq2_matmul_prefill_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
                                    int64_t k, float* y, int tile, void* stream);
 
+/* Tile-layout prefill matmul with activation groups of agroup elements
+ * (page "Kernel experiments", section C, Tests 8 and 9, which timed them at
+ * prefill sizes): the y of pq2_matmul_small_m_tiles_g's definition for any m.
+ * Each activation group's integer product is rescaled by its own xs into the
+ * fp32 sum, in k order per output; agroup = 128 gives the bits of
+ * pq2_matmul_prefill_tiles.  q and xs come from pq2_quantize_act_i8_g with
+ * the same agroup.
+ *   q       device int8 [m][k], 16-byte aligned.  xs  device float [m][k/agroup].
+ *   tiles, y, limits and errors as pq2_matmul_prefill_tiles, plus EINVAL for
+ *   agroup not 128/64/32. */
+int pq2_matmul_prefill_tiles_g(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n, int64_t k,
+                               int64_t agroup, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

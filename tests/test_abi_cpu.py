@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 27
+    assert len(names) == 28
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -213,10 +213,18 @@ def test_activation_group_validation():
     assert g(A, B, C, 17, 8, 128, 64, D, None) == ESHAPE         # columns
     assert g(A + 8, B, C, 1, 8, 128, 64, D, None) == EALIGN      # q not 16-byte aligned
     assert g(A, B, C, 1, 8, 256, 32, B + 16, None) == EINVAL     # y overlaps xs (8 floats)
+    h = pq2.lib.pq2_matmul_prefill_tiles_g
+    for bad in (0, 16, 96, 256):
+        assert h(A, B, C, 64, 8, 128, bad, D, None) == EINVAL, bad
+    assert h(A, B, C, 0, 8, 128, 64, D, None) == ESHAPE          # no rows
+    assert h(A, B, C, 64, 8, 96, 64, D, None) == ESHAPE          # k % 128
+    assert h(A + 8, B, C, 64, 8, 128, 64, D, None) == EALIGN     # q not 16-byte aligned
+    assert h(A, B, C, 1, 8, 256, 32, B + 16, None) == EINVAL     # y overlaps xs (8 floats)
     if not _gpu_visible():
         for agroup in (128, 64, 32):
             assert f(A, 0, 5120, 4, 5120, agroup, B, C, None) == EDEVICE
             assert g(A, B, C, 4, 8, 5120, agroup, D, None) == EDEVICE
+            assert h(A, B, C, 256, 8, 5120, agroup, D, None) == EDEVICE
 
 
 def test_prefill_tile_validation():

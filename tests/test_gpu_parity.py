@@ -989,3 +989,58 @@ def test_small_m_tiles_g_workloads(name):
             mi, ni = _sample_indices(m, w.n, 300, seed=m + agroup)
             y_ref, bound = oracle.matmul_raw_sample_g(qo, xso, raw, w.n, w.k, agroup, mi, ni)
             assert_within(y[mi, ni], y_ref, bound, f"tiles agroup={agroup} {name} m={m}")
+
+
+@pytest.mark.parametrize("agroup", [64, 32])
+@pytest.mark.parametrize("m,n,k", PREFILL_SHAPES)
+def test_prefill_tiles_g_full(agroup, m, n, k):
+    """Tile-layout prefill with smaller activation groups against the oracle,
+    element by element, with ragged row, column and group tails."""
+    pq2 = _pq2()
+    announce(f"prefill agroup={agroup} m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=130 + n, codes="ternary+3", row_pad=1)
+    x = workloads.make_activations(m, k, 131 + m, "normal+outliers")
+    q, xs, qo, xso = quantise_g_both(x, agroup)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_prefill_tiles_g(q, xs, gpu_tiles(raw, n, k), y, agroup)
+    torch.cuda.synchronize()
+    y_ref, bound = oracle.matmul_raw_g(qo, xso, raw, n, k, agroup)
+    assert_within(y.cpu().numpy(), y_ref, bound, f"prefill agroup={agroup} m={m} n={n} k={k}")
+
+
+def test_prefill_tiles_g_128_is_the_tile_prefill():
+    pq2 = _pq2()
+    m, n, k = 200, 333, 1408
+    raw = workloads.make_raw_weights(n, k, seed=132, codes="ternary+3")
+    x = workloads.make_activations(m, k, 133, "laplace")
+    q, xs, _, _ = quantise_g_both(x, 128)
+    tiles = gpu_tiles(raw, n, k)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_prefill_tiles_g(q, xs, tiles, y, 128)
+    y0 = gpu_matmul(pq2.pq2_matmul_prefill_tiles, q, xs, tiles, n)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["prefill_gate", "prefill_up"])
+def test_prefill_tiles_g_workloads(name):
+    """Full prefill sizes: sampled outputs against the oracle, and two
+    launches with identical bits."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    tiles = gpu_tiles(raw, w.n, w.k)
+    for agroup in (64, 32):
+        for m in w.ms:
+            announce(f"prefill agroup={agroup} workload {name} m={m}")
+            q, xs, qo, xso = quantise_g_both(x[:m].contiguous(), agroup)
+            ys = torch.full((2, m, w.n), float("nan"), dtype=torch.float32, device=DEV)
+            for i in range(2):
+                pq2.pq2_matmul_prefill_tiles_g(q, xs, tiles, ys[i], agroup)
+            torch.cuda.synchronize()
+            assert torch.equal(ys[0].view(torch.int32), ys[1].view(torch.int32)), f"{name} m={m}: launches differ"
+            y = ys[0].cpu().numpy()
+            rng = np.random.default_rng(m + agroup)
+            mi = np.concatenate([[0, m - 1, 0, m - 1], rng.integers(0, m, 1000)])
+            ni = np.concatenate([[0, 0, w.n - 1, w.n - 1], rng.integers(0, w.n, 1000)])
+            y_ref, bound = oracle.matmul_raw_sample_g(qo, xso, raw, w.n, w.k, agroup, mi, ni)
+            assert_within(y[mi, ni], y_ref, bound, f"prefill agroup={agroup} {name} m={m}")
