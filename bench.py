@@ -194,11 +194,14 @@ def main():
         raw = torch.from_numpy(raw_np).to(dev)
         pool = torch.empty((copies, wb), dtype=torch.uint8, device=dev)
         tpool = torch.empty((copies, tb), dtype=torch.uint8, device=dev)
+        rpool = torch.empty((copies,) + tuple(raw.shape), dtype=torch.uint8, device=dev)  # raw rows, read in place
         pq2.pq2_prepare_planes(raw, n, k, pool[0], stream=stream)
         pq2.pq2_prepare_tiles(raw, n, k, tpool[0], stream=stream)
-        for c in range(1, copies):
-            pool[c].copy_(pool[0])
-            tpool[c].copy_(tpool[0])
+        for c in range(copies):
+            if c:
+                pool[c].copy_(pool[0])
+                tpool[c].copy_(tpool[0])
+            rpool[c].copy_(raw)
         x = x_cpu.to(dev)
         bufs = {}
         pbufs = {}
@@ -268,7 +271,7 @@ def main():
         q, xs, y = bufs[m]
         qp, pxs, qsum, py = pbufs[m]
         ys = {key: torch.empty((m, n), dtype=torch.float32, device=dev)
-              for key in ("planes", "tiles_fused", "planes_fused")}
+              for key in ("planes", "tiles_fused", "planes_fused", "raw")}
         xm = x[:m]
 
         def calls(kind, m=m, q=q, xs=xs, y=y, qp=qp, pxs=pxs, qsum=qsum, py=py, xm=xm):
@@ -295,14 +298,16 @@ def main():
                         pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
                     elif kind == "planes_fused":
                         pq2.pq2_matmul_small_m_fused(xm, pool[c], ys["planes_fused"], stream=stream)
+                    elif kind == "raw_mm":
+                        pq2.pq2_matmul_small_m_raw(q, xs, rpool[c], ys["raw"], stream=stream)
             return body
 
         t = {kind: per_call_us(calls(kind)) for kind in
              ("tiles_mm", "tiles_call", "gemv", "tiles_fused", "planes_mm", "planes_call", "planes_order_mm",
-              "planes_order_call", "planes_fused")}
+              "planes_order_call", "planes_fused", "raw_mm")}
         torch.cuda.synchronize()
         for key, other in (("planes", ys["planes"]), ("plane order", py), ("tiles fused", ys["tiles_fused"]),
-                           ("planes fused", ys["planes_fused"])):
+                           ("planes fused", ys["planes_fused"]), ("raw reader", ys["raw"])):
             assert torch.equal(other.view(torch.int32), y.view(torch.int32)), \
                 f"{key} output differs from the tile-layout output at M={m}"
         gbs = matmul_bytes(m, n, k) / (t["tiles_mm"] * 1e-6) / 1e9
@@ -320,6 +325,7 @@ def main():
             "planes_fused_call_us": round(t["planes_fused"], 3),
             "plane_order_matmul_us": round(t["planes_order_mm"], 3),
             "plane_order_complete_call_us": round(t["planes_order_call"], 3),
+            "raw_matmul_us": round(t["raw_mm"], 3),
             "matmul_bytes": matmul_bytes(m, n, k),
         }
         log(f"[bench] M={m}: tiles matmul {t['tiles_mm']:.3f} us ({gbs:.0f} GB/s, "
@@ -327,7 +333,7 @@ def main():
             f"gemv {t['gemv']:.3f}, "
             f"fused {t['tiles_fused']:.3f}; planes matmul {t['planes_mm']:.3f} ({pgbs:.0f} GB/s), "
             f"call {t['planes_call']:.3f}, fused {t['planes_fused']:.3f}; plane order matmul "
-            f"{t['planes_order_mm']:.3f}, call {t['planes_order_call']:.3f}")
+            f"{t['planes_order_mm']:.3f}, call {t['planes_order_call']:.3f}; raw reader matmul {t['raw_mm']:.3f}")
 
     # Smaller activation groups (page "Kernel experiments", section C, Tests
     # 8 and 9): the tile matmul and the complete call with 64- and 32-element

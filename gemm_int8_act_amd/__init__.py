@@ -53,6 +53,7 @@ EXPORTED = (
     "pq2_matmul_small_m_tiles_g",
     "pq2_gemv_tiles",
     "pq2_matmul_prefill_tiles_g",
+    "pq2_matmul_small_m_raw",
 )
 
 
@@ -128,6 +129,8 @@ def _load_library():
     lib.pq2_matmul_small_m_tiles_g.restype = i32
     lib.pq2_matmul_prefill_tiles_g.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
     lib.pq2_matmul_prefill_tiles_g.restype = i32
+    lib.pq2_matmul_small_m_raw.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
+    lib.pq2_matmul_small_m_raw.restype = i32
     lib.pq2_matmul_small_m_tiles_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tiles_tuned.restype = i32
     lib.pq2_matmul_prefill_tiles.argtypes = [p, p, p, i64, i64, i64, p, p]
@@ -356,6 +359,26 @@ def pq2_matmul_small_m_tiles_g(q, xs, tiles, y, agroup: int, stream=None) -> Non
     (q, xs from pq2_quantize_act_i8_g with the same agroup)."""
     _check(lib.pq2_matmul_small_m_tiles_g(*_tiles_g_args(q, xs, tiles, y, agroup), _stream(stream)),
            "pq2_matmul_small_m_tiles_g")
+
+
+def pq2_matmul_small_m_raw(q, xs, raw, y, stream=None) -> None:
+    """pq2_matmul_small_m reading the raw block layout in place: raw uint8
+    [n][stride] (stride >= k/128*34 bytes, even; row padding is not read),
+    same bits as pq2_matmul_small_m on the prepared planes."""
+    import torch
+    if q.dtype != torch.int8 or xs.dtype != torch.float32 or raw.dtype != torch.uint8 or y.dtype != torch.float32:
+        raise ValueError("q int8, xs float32, raw uint8, y float32 expected")
+    for name, t in (("q", q), ("xs", xs), ("y", y)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if raw.dim() != 2 or raw.stride(1) != 1:
+        raise ValueError("raw must be [n][stride] bytes with unit column stride")
+    m, k = q.shape
+    n = y.shape[1]
+    if y.shape[0] != m or xs.numel() != m * (k // 128) or raw.shape[0] != n or raw.shape[1] < k // 128 * 34:
+        raise ValueError("shape mismatch between q, xs, raw and y")
+    _check(lib.pq2_matmul_small_m_raw(_dev_ptr(q, "q"), _dev_ptr(xs, "xs"), _dev_ptr(raw, "raw"), raw.stride(0), m, n,
+                                      k, _dev_ptr(y, "y"), _stream(stream)), "pq2_matmul_small_m_raw")
 
 
 def pq2_matmul_prefill_tiles_g(q, xs, tiles, y, agroup: int, stream=None) -> None:

@@ -14,6 +14,9 @@ namespace {
 constexpr int64_t kGroup = 128;
 constexpr int64_t kMaxPrefillM = (int64_t)65535 * 64;  // grid.y limit x smallest tile rows
 constexpr int64_t kMaxN = (int64_t)1 << 30;
+// Raw rows read in place: a workgroup's 16 rows stay below 2^31 bytes, the
+// range of the kernels' 32-bit buffer offsets.
+constexpr int64_t kMaxRawStride = (int64_t)1 << 26;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -307,6 +310,26 @@ int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* plane
 int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream) {
     return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, 0, stream);
+}
+
+int pq2_matmul_small_m_raw(const int8_t* q, const float* xs, const void* raw, int64_t raw_row_stride_bytes, int64_t m,
+                           int64_t n, int64_t k, float* y, void* stream) {
+    if (!q || !xs || !raw || !y) return PQ2_EINVAL;
+    if (m < 1 || m > PQ2_MAX_SMALL_M || n < 1 || n > kMaxN) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    const int64_t row_bytes = k / kGroup * 34;
+    if (raw_row_stride_bytes < row_bytes || (raw_row_stride_bytes & 1) || raw_row_stride_bytes > kMaxRawStride)
+        return PQ2_ESHAPE;
+    if (!aligned(q, 16) || !aligned(xs, 4) || !aligned(raw, 2) || !aligned(y, 4)) return PQ2_EALIGN;
+    const size_t ybytes = (size_t)m * n * 4;
+    if (overlap(y, ybytes, q, (size_t)m * k) || overlap(y, ybytes, xs, (size_t)m * (k / kGroup) * 4) ||
+        overlap(y, ybytes, raw, (size_t)(n - 1) * raw_row_stride_bytes + row_bytes))
+        return PQ2_EINVAL;
+    const pq2::SmallMConfig cfg = pq2::default_small_m_config(pq2::kSrcNatural, m, n, k);
+    const int rows = pq2::default_small_m_rows(1, pq2::kSrcNatural, m, n, k, cfg.max_waves);
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m_raw(q, xs, static_cast<const uint8_t*>(raw), raw_row_stride_bytes, m, n,
+                                                 k, y, cfg.max_waves, rows, (hipStream_t)stream));
 }
 
 int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes,

@@ -59,6 +59,7 @@ struct SmallMLaunch {
     float* y;
     int waves, nseg, per_wave, chunks;
     hipStream_t stream;
+    int64_t raw_stride = 0;  // nonzero: `planes` is the raw block layout with this row stride in bytes
 };
 
 // Columns one pass of the workgroup-staged engine covers; more columns take
@@ -82,6 +83,11 @@ hipError_t launch_small_m_tiles(const int8_t* q, const float* xs, const uint8_t*
                                 int64_t k, float* y, int max_waves, int split, hipStream_t stream);
 hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int tile, hipStream_t stream);
+// Packed-dot small-m matmul straight from the raw block layout (34 bytes per
+// 128 weights: fp16 scale, then 32 code bytes; rows raw_stride bytes apart),
+// natural-order q; max_waves fixes the k split as for launch_small_m.
+hipError_t launch_small_m_raw(const int8_t* q, const float* xs, const uint8_t* raw, int64_t raw_stride, int64_t m,
+                              int64_t n, int64_t k, float* y, int max_waves, int rows, hipStream_t stream);
 // Tile-layout prefill with activation groups of agroup = 128, 64 or 32
 // (natural-order q, xs [m][k/agroup]); tile 0 picks the default.
 hipError_t launch_prefill_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,

@@ -77,12 +77,28 @@ __device__ __forceinline__ void half_group_dot(const uint4 (&P)[4], const uint4 
     }
 }
 
-template <int MC, int R, int SEGS, int SRC>
+// 16 code bytes of the raw block layout at byte offset off (2-byte aligned:
+// blocks are 34 bytes).  An offset of 2 mod 4 reads the dwords from two bytes
+// before it plus the ushort at off + 14 and shifts them into place, so no
+// read reaches past the block's last byte.
+__device__ __forceinline__ uint4 raw_codes16(__amdgpu_buffer_rsrc_t r, bool ok, uint32_t off) {
+    const uint32_t sh = (off & 2u) * 8u;  // 0 or 16 bits
+    const uint4 a = buf_load16<kAuxNonTemporal>(r, ok ? off & ~3u : kBufferOOB);
+    const uint32_t e = buf_load2(r, ok ? off + 14u : kBufferOOB);
+    return make_uint4(__builtin_amdgcn_alignbit(a.y, a.x, sh), __builtin_amdgcn_alignbit(a.z, a.y, sh),
+                      __builtin_amdgcn_alignbit(a.w, a.z, sh), __builtin_amdgcn_alignbit(e, a.w, sh));
+}
+
+// RAW: `codes` is the raw block layout (page "Kernel experiments", section
+// A, Tests 4 and 24: each 128-weight block is its fp16 scale then 32 code
+// bytes, rows raw_stride bytes apart), read without a preparation pass; each
+// lane takes the same 16 code bytes and scale as from the planes.
+template <int MC, int R, int SEGS, int SRC, bool RAW = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 && R == 1 && MC <= (src_fused(SRC) ? 1 : 4) ? 7 : 1))) void small_m_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const int32_t* __restrict__ qsum,
     const void* __restrict__ x, int64_t x_stride,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y, int n,
-    int k, int groups, int nseg, int segs_per_wave, int mtotal) {
+    int k, int groups, int nseg, int segs_per_wave, int mtotal, int raw_stride) {
 #pragma clang fp contract(off)
     constexpr bool FUSED = src_fused(SRC);
     constexpr int XL = src_xloads(SRC);
@@ -112,8 +128,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
     const unsigned char* rd_ptr = region + ((j >> 1) * kBlockPitch + 4 * h) * 16;  // half h of group j/2
     const unsigned char* qs_ptr = region + (gsel * kBlockPitch + 8) * 16;     // sum(q) of group gsel
 
-    const auto code_rs = make_rsrc(codes + (size_t)row_base * k4, (uint32_t)rows_here * k4);
-    const auto scale_rs = make_rsrc(scales + (size_t)row_base * groups, (uint32_t)(rows_here * groups * 2));
+    // Raw rows: the resource starts at the 4-byte boundary at or below this
+    // workgroup's first row (rows are 2-byte aligned), and adj re-adds the
+    // difference, so an offset's low bits are its address's.
+    const uint8_t* raw_rows = codes + (size_t)row_base * raw_stride;
+    const uint32_t adj = RAW ? (uint32_t)(reinterpret_cast<uintptr_t>(raw_rows) & 3u) : 0u;
+    const auto code_rs = RAW ? make_rsrc(raw_rows - adj, (uint32_t)rows_here * (uint32_t)raw_stride + adj)
+                             : make_rsrc(codes + (size_t)row_base * k4, (uint32_t)rows_here * k4);
+    const auto scale_rs = make_rsrc(RAW ? nullptr : scales + (size_t)row_base * groups,
+                                    RAW ? 0u : (uint32_t)(rows_here * groups * 2));
     const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
     const auto xs_rs = make_rsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
     const auto qs_rs = make_rsrc(SRC == kSrcPlanes ? qsum + (size_t)m0 * groups : nullptr,
@@ -170,10 +193,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SEGS == 1 &
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const uint32_t rl = (uint32_t)(slot + kRowSlots * r);
-                const uint32_t off = rl * k4 + (uint32_t)g0 * 32u + 16u * (uint32_t)j;
-                cw[si][0][r] = buf_load16<kAuxNonTemporal>(code_rs, okA ? off : kBufferOOB);
-                cw[si][1][r] = buf_load16<kAuxNonTemporal>(code_rs, okB ? off + 128u : kBufferOOB);
-                wsraw[si][r] = buf_load2(scale_rs, okS ? (rl * groups + g0 + gsel) * 2u : kBufferOOB);
+                if constexpr (RAW) {
+                    // Block g of row rl starts at rl * raw_stride + 34 g.
+                    const uint32_t row_off = adj + rl * (uint32_t)raw_stride;
+                    const uint32_t off = row_off + (uint32_t)(g0 + (j >> 1)) * 34u + 2u + 16u * (uint32_t)h;
+                    cw[si][0][r] = raw_codes16(code_rs, okA, off);
+                    cw[si][1][r] = raw_codes16(code_rs, okB, off + 4u * 34u);
+                    wsraw[si][r] = buf_load2(code_rs, okS ? row_off + (uint32_t)(g0 + gsel) * 34u : kBufferOOB);
+                } else {
+                    const uint32_t off = rl * k4 + (uint32_t)g0 * 32u + 16u * (uint32_t)j;
+                    cw[si][0][r] = buf_load16<kAuxNonTemporal>(code_rs, okA ? off : kBufferOOB);
+                    cw[si][1][r] = buf_load16<kAuxNonTemporal>(code_rs, okB ? off + 128u : kBufferOOB);
+                    wsraw[si][r] = buf_load2(scale_rs, okS ? (rl * groups + g0 + gsel) * 2u : kBufferOOB);
+                }
             }
         }
         // 3./4. Per segment: private LDS copy of its activation blocks (natural
@@ -547,9 +579,9 @@ size_t lds_bytes(int mc, int segs, int waves, int rows_per_wg) {
 
 using Launch = SmallMLaunch;
 
-template <int MC, int R, int SEGS, int SRC>
+template <int MC, int R, int SEGS, int SRC, bool RAW = false>
 hipError_t launch_one(const Launch& a) {
-    auto kern = small_m_kernel<MC, R, SEGS, SRC>;
+    auto kern = small_m_kernel<MC, R, SEGS, SRC, RAW>;
     const size_t lds = lds_bytes(MC, SEGS, a.waves, kRowSlots * R);
     static bool attr_set = false;  // one instantiation = one static
     if (!attr_set) {
@@ -558,43 +590,44 @@ hipError_t launch_one(const Launch& a) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const uint16_t* scales = reinterpret_cast<const uint16_t*>(a.planes + a.n * (a.k / 4));
+    const uint16_t* scales = RAW ? nullptr : reinterpret_cast<const uint16_t*>(a.planes + a.n * (a.k / 4));
     const dim3 grid((unsigned)((a.n + kRowSlots * R - 1) / (kRowSlots * R)), (unsigned)a.chunks);
     clear_stale_error();
     hipLaunchKernelGGL(kern, grid, dim3(64 * a.waves), lds, a.stream, a.q, a.xs, a.qsum, a.x, a.x_stride, a.planes,
-                       scales, a.y, (int)a.n, (int)a.k, (int)(a.k / 128), a.nseg, a.per_wave, (int)a.m);
+                       scales, a.y, (int)a.n, (int)a.k, (int)(a.k / 128), a.nseg, a.per_wave, (int)a.m,
+                       (int)a.raw_stride);
     return hipGetLastError();
 }
 
 // Segments per load step: 1 or 2 (the register cap in launch_any never asks for more).
-template <int MC, int R, int SRC>
+template <int MC, int R, int SRC, bool RAW = false>
 hipError_t pick_segs(const Launch& a, int segs) {
-    return segs == 1 ? launch_one<MC, R, 1, SRC>(a) : launch_one<MC, R, 2, SRC>(a);
+    return segs == 1 ? launch_one<MC, R, 1, SRC, RAW>(a) : launch_one<MC, R, 2, SRC, RAW>(a);
 }
 
-template <int MC, int SRC>
+template <int MC, int SRC, bool RAW = false>
 hipError_t pick_rows(const Launch& a, int rows, int segs) {
-    return rows == 1 ? pick_segs<MC, 1, SRC>(a, segs) : pick_segs<MC, 2, SRC>(a, segs);
+    return rows == 1 ? pick_segs<MC, 1, SRC, RAW>(a, segs) : pick_segs<MC, 2, SRC, RAW>(a, segs);
 }
 
 // Fused (quantising) instantiations cover up to 4 columns per pass.
 constexpr int max_mc(int src) { return src_fused(src) ? 4 : 8; }
 
-template <int SRC>
+template <int SRC, bool RAW = false>
 hipError_t pick_mc(const Launch& a, int mc, int rows, int segs) {
     switch (mc) {
-        case 1: return pick_rows<1, SRC>(a, rows, segs);
-        case 2: return pick_rows<2, SRC>(a, rows, segs);
-        case 3: return pick_rows<3, SRC>(a, rows, segs);
-        case 4: return pick_rows<4, SRC>(a, rows, segs);
+        case 1: return pick_rows<1, SRC, RAW>(a, rows, segs);
+        case 2: return pick_rows<2, SRC, RAW>(a, rows, segs);
+        case 3: return pick_rows<3, SRC, RAW>(a, rows, segs);
+        case 4: return pick_rows<4, SRC, RAW>(a, rows, segs);
         default: break;
     }
     if constexpr (max_mc(SRC) == 8) {
         switch (mc) {
-            case 5: return pick_rows<5, SRC>(a, rows, segs);
-            case 6: return pick_rows<6, SRC>(a, rows, segs);
-            case 7: return pick_rows<7, SRC>(a, rows, segs);
-            case 8: return pick_rows<8, SRC>(a, rows, segs);
+            case 5: return pick_rows<5, SRC, RAW>(a, rows, segs);
+            case 6: return pick_rows<6, SRC, RAW>(a, rows, segs);
+            case 7: return pick_rows<7, SRC, RAW>(a, rows, segs);
+            case 8: return pick_rows<8, SRC, RAW>(a, rows, segs);
             default: break;
         }
     }
@@ -686,6 +719,10 @@ hipError_t launch_any(int src, const Launch& base, const SmallMConfig& cfg) {
     a.nseg = nseg;
     a.per_wave = per_wave;
     a.chunks = chunks;
+    if (a.raw_stride != 0) {  // raw block layout: packed-dot engine, natural-order q
+        if (src != kSrcNatural || cfg.engine != 1) return hipErrorInvalidValue;
+        return pick_mc<kSrcNatural, true>(a, mc, rows, segs);
+    }
     switch (src) {
         case kSrcPlanes: return dispatch<kSrcPlanes>(a, cfg.engine, mc, rows, segs);
         case kSrcNatural: return dispatch<kSrcNatural>(a, cfg.engine, mc, rows, segs);
@@ -746,6 +783,17 @@ hipError_t launch_small_m_planes(const int8_t* qp, const float* xs, const int32_
                                  hipStream_t stream) {
     const Launch a{qp, xs, qsum, nullptr, 0, planes, m, n, k, y, 0, 0, 0, 0, stream};
     return launch_any(kSrcPlanes, a, cfg);
+}
+
+hipError_t launch_small_m_raw(const int8_t* q, const float* xs, const uint8_t* raw, int64_t raw_stride, int64_t m,
+                              int64_t n, int64_t k, float* y, int max_waves, int rows, hipStream_t stream) {
+    Launch a{q, xs, nullptr, nullptr, 0, raw, m, n, k, y, 0, 0, 0, 0, stream};
+    a.raw_stride = raw_stride;
+    SmallMConfig cfg;
+    cfg.engine = 1;
+    cfg.max_waves = max_waves;
+    cfg.rows = rows;
+    return launch_any(kSrcNatural, a, cfg);
 }
 
 hipError_t launch_small_m_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* planes, int64_t m,

@@ -146,6 +146,22 @@ int pq2_matmul_prefill_planes(const int8_t* qp, const float* xs, const void* pla
 int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const void* planes, int64_t m, int64_t n,
                                     int64_t k, float* y, int tile, void* stream);
 
+/* pq2_matmul_small_m straight from the raw block layout, with no
+ * preparation pass (page "Kernel experiments", section A, Tests 4 and 24:
+ * the interleaved 34-byte blocks, fp16 scale then 32 code bytes, read in
+ * place): the same definition, limits and summation order as
+ * pq2_matmul_small_m, hence the same bits, from the packed-dot engine.
+ *   q       device int8 [m][k], 16-byte aligned.   xs  device float [m][k/128], 4-byte aligned.
+ *   raw     device, n rows of raw_row_stride_bytes >= k/128*34 bytes (even,
+ *           at most 2^26); 2-byte aligned.  Row padding is never read.
+ *   y       device float [m][n], 4-byte aligned; fully overwritten; must
+ *           not overlap any input.
+ * Errors: EINVAL (null, overlap), ESHAPE (m outside 1..16, n<1, k<128,
+ *         k%128, k > PQ2_MAX_K, stride too small, odd or too large),
+ *         EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_small_m_raw(const int8_t* q, const float* xs, const void* raw, int64_t raw_row_stride_bytes, int64_t m,
+                           int64_t n, int64_t k, float* y, void* stream);
+
 /* Tuning hook for the small-m matmul (benchmarks and tests only; same
  * arguments and result as pq2_matmul_small_m).  engine selects one of four
  * kernels that compute the same bits:

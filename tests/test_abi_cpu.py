@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 28
+    assert len(names) == 29
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -317,3 +317,18 @@ def test_single_hip_runtime_whatever_the_import_order(order):
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_raw_reader_validation():
+    r = pq2.lib.pq2_matmul_small_m_raw
+    assert r(None, B, C, 34, 1, 8, 128, D, None) == EINVAL
+    assert r(A, B, C, 33, 1, 8, 128, D, None) == ESHAPE           # stride below one block
+    assert r(A, B, C, 35, 1, 8, 128, D, None) == ESHAPE           # odd stride
+    assert r(A, B, C, 1 << 27, 1, 8, 128, D, None) == ESHAPE      # stride too large
+    assert r(A, B, C, 34, 17, 8, 128, D, None) == ESHAPE          # columns
+    assert r(A, B, C, 34, 1, 8, 96, D, None) == ESHAPE            # k % 128
+    assert r(A, B, C + 1, 34, 1, 8, 128, D, None) == EALIGN       # raw not 2-byte aligned
+    assert r(A + 8, B, C, 34, 1, 8, 128, D, None) == EALIGN       # q not 16-byte aligned
+    assert r(A, B, C, 34, 1, 8, 128, C + 16, None) == EINVAL      # y overlaps raw
+    if not _gpu_visible():
+        assert r(A, B, C + 2, 170, 4, 8, 640, D, None) == EDEVICE

@@ -1044,3 +1044,61 @@ def test_prefill_tiles_g_workloads(name):
             ni = np.concatenate([[0, 0, w.n - 1, w.n - 1], rng.integers(0, w.n, 1000)])
             y_ref, bound = oracle.matmul_raw_sample_g(qo, xso, raw, w.n, w.k, agroup, mi, ni)
             assert_within(y[mi, ni], y_ref, bound, f"prefill agroup={agroup} {name} m={m}")
+
+
+def gpu_raw(raw_np, shift=0):
+    """The raw rows on the device as [n][stride] bytes, starting `shift`
+    bytes past a 256-byte boundary."""
+    n, stride = raw_np.shape
+    buf = torch.full((n * stride + shift,), 0xEE, dtype=torch.uint8, device=DEV)
+    raw = buf[shift:].view(n, stride)
+    raw.copy_(torch.from_numpy(np.ascontiguousarray(raw_np)))
+    return raw
+
+
+# (m, n, k, row padding, pointer shift): strides of 0 and 2 mod 4, padded
+# rows (pad bytes 0xEE, never read), a raw pointer 2 bytes off a 4-byte
+# boundary, one and two rows per lane, several column passes.
+RAW_SHAPES = [(1, 1024, 512, 0, 0), (2, 333, 640, 0, 0), (3, 97, 1152, 6, 0), (4, 1000, 5120, 0, 2),
+              (5, 77, 2176, 2, 0), (9, 61, 1024, 0, 2), (16, 40, 17408, 4, 2), (1, 1, 128, 0, 0),
+              (12, 300, 3072, 10, 0), (2, 24, 65536, 0, 2)]
+
+
+@pytest.mark.parametrize("m,n,k,pad,shift", RAW_SHAPES)
+def test_small_m_raw_full(m, n, k, pad, shift):
+    """The raw-layout reader against the oracle, element by element, and
+    bit-identical to pq2_matmul_small_m on the prepared planes."""
+    pq2 = _pq2()
+    announce(f"small_m raw m={m} n={n} k={k} pad={pad} shift={shift}")
+    raw_np = workloads.make_raw_weights(n, k, seed=140 + m + n, codes="ternary+3", row_pad=pad)
+    x = workloads.make_activations(m, k, 141 + k, "normal+outliers")
+    q, xs, qo, xso = quantise_both(x)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_small_m_raw(q, xs, gpu_raw(raw_np, shift), y)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw_np, n, k)
+    assert_within(y, y_ref, bound, f"raw m={m} n={n} k={k}")
+    y1 = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, gpu_planes(raw_np, n, k), n)
+    assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), "raw reader and planes differ"
+
+
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_small_m_raw_workloads(name):
+    """Full workload sizes: bit-identical to the planes path, sampled outputs
+    against the oracle."""
+    pq2 = _pq2()
+    w, raw_np, x = workload_case(name)
+    raw = gpu_raw(raw_np)
+    planes = gpu_planes(raw_np, w.n, w.k)
+    for m in w.ms:
+        announce(f"raw workload {name} m={m}")
+        q, xs, qo, xso = quantise_both(x[:m].contiguous())
+        y = torch.full((m, w.n), float("nan"), dtype=torch.float32, device=DEV)
+        pq2.pq2_matmul_small_m_raw(q, xs, raw, y)
+        y1 = gpu_matmul(pq2.pq2_matmul_small_m, q, xs, planes, w.n)
+        y = y.cpu().numpy()
+        assert np.array_equal(y.view(np.uint32), y1.view(np.uint32)), f"{name} m={m}: raw reader and planes differ"
+        mi, ni = _sample_indices(m, w.n, 300, seed=m + 7)
+        y_ref, bound = oracle.matmul_raw_sample(qo, xso, raw_np, w.n, w.k, mi, ni)
+        assert_within(y[mi, ni], y_ref, bound, f"raw {name} m={m}")
