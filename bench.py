@@ -368,6 +368,25 @@ def main():
         log(f"[bench] activation groups of {ag}: matmul us " +
             ", ".join(f"M={m} {v['matmul_us']:.3f}" for m, v in agroups[str(ag)].items()))
 
+    # Read ceiling: each layout's decode-engine weight loads with no
+    # arithmetic (pq2_read_probe), over the same rotating copies.
+    probe = {}
+    for name, layout, wpool in (("tiles", pq2.LAYOUT_TILES, tpool), ("planes", pq2.LAYOUT_PLANES, pool)):
+        pout = torch.empty((pq2.pq2_read_probe_words(layout, n, k),), dtype=torch.int32, device=dev)
+
+        def probe_calls(layout=layout, wpool=wpool, pout=pout):
+            def body():
+                for c in range(copies):
+                    pq2.pq2_read_probe(wpool[c], layout, n, k, pout, stream=stream)
+            return body
+
+        p_us = per_call_us(probe_calls())
+        probe[name] = {"us": round(p_us, 3), "weight_GBps": round(wb / (p_us * 1e-6) / 1e9, 1)}
+    torch.cuda.synchronize()
+    log(f"[bench] read probe (weights only, no arithmetic): tiles {probe['tiles']['us']:.3f} us "
+        f"({probe['tiles']['weight_GBps']:.0f} GB/s), planes {probe['planes']['us']:.3f} us "
+        f"({probe['planes']['weight_GBps']:.0f} GB/s)")
+
     tot_bytes = sum(v["matmul_bytes"] for v in per_m.values())
     tot_us = sum(v["matmul_us"] for v in per_m.values())
     achieved = tot_bytes / (tot_us * 1e-6) / 1e9
@@ -410,6 +429,7 @@ def main():
         },
         "us_per_call": per_m,
         "activation_groups_us_per_call": agroups,
+        "read_probe_us_per_call": probe,
         "roofline": roofline,
     }
 

@@ -54,6 +54,8 @@ EXPORTED = (
     "pq2_gemv_tiles",
     "pq2_matmul_prefill_tiles_g",
     "pq2_matmul_small_m_raw",
+    "pq2_read_probe",
+    "pq2_read_probe_words",
 )
 
 
@@ -131,6 +133,10 @@ def _load_library():
     lib.pq2_matmul_prefill_tiles_g.restype = i32
     lib.pq2_matmul_small_m_raw.argtypes = [p, p, p, i64, i64, i64, i64, p, p]
     lib.pq2_matmul_small_m_raw.restype = i32
+    lib.pq2_read_probe.argtypes = [p, i32, i64, i64, p, p]
+    lib.pq2_read_probe.restype = i32
+    lib.pq2_read_probe_words.argtypes = [i32, i64, i64]
+    lib.pq2_read_probe_words.restype = i64
     lib.pq2_matmul_small_m_tiles_tuned.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tiles_tuned.restype = i32
     lib.pq2_matmul_prefill_tiles.argtypes = [p, p, p, i64, i64, i64, p, p]
@@ -379,6 +385,34 @@ def pq2_matmul_small_m_raw(q, xs, raw, y, stream=None) -> None:
         raise ValueError("shape mismatch between q, xs, raw and y")
     _check(lib.pq2_matmul_small_m_raw(_dev_ptr(q, "q"), _dev_ptr(xs, "xs"), _dev_ptr(raw, "raw"), raw.stride(0), m, n,
                                       k, _dev_ptr(y, "y"), _stream(stream)), "pq2_matmul_small_m_raw")
+
+
+LAYOUT_PLANES = 0
+LAYOUT_TILES = 1
+
+
+def pq2_read_probe_words(layout: int, n: int, k: int) -> int:
+    """Words pq2_read_probe writes (one per wave of its grid)."""
+    return int(lib.pq2_read_probe_words(layout, n, k))
+
+
+def pq2_read_probe(weights, layout: int, n: int, k: int, out, stream=None) -> None:
+    """Read-only probe: the decode engine's weight loads for this layout with
+    no arithmetic; out uint32-sized int32 [pq2_read_probe_words(...)] gets
+    each wave's XOR fold."""
+    import torch
+    if weights.dtype != torch.uint8 or out.dtype != torch.int32:
+        raise ValueError("weights uint8 and out int32 expected")
+    if not weights.is_contiguous() or not out.is_contiguous():
+        raise ValueError("weights and out must be contiguous")
+    words = pq2_read_probe_words(layout, n, k)
+    if words == 0:
+        raise ValueError("bad layout or shape")
+    need = pq2_tiles_bytes(n, k) if layout == LAYOUT_TILES else n * (k // 128) * 34
+    if weights.numel() < need or out.numel() < words:
+        raise ValueError("weights or out too small")
+    _check(lib.pq2_read_probe(_dev_ptr(weights, "weights"), layout, n, k, _dev_ptr(out, "out"), _stream(stream)),
+           "pq2_read_probe")
 
 
 def pq2_matmul_prefill_tiles_g(q, xs, tiles, y, agroup: int, stream=None) -> None:

@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpq2.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "quantize.hip", "small_m.hip", "small_m_wg.hip", "tiles.hip", "prefill.hip"]
+SOURCES = ["api.hip", "quantize.hip", "small_m.hip", "small_m_wg.hip", "tiles.hip", "prefill.hip", "probe.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

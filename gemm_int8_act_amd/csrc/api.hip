@@ -312,6 +312,24 @@ int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int
     return pq2_matmul_small_m_tuned(q, xs, planes, m, n, k, y, 0, 0, 0, stream);
 }
 
+int64_t pq2_read_probe_words(int layout, int64_t n, int64_t k) {
+    if ((layout != PQ2_LAYOUT_PLANES && layout != PQ2_LAYOUT_TILES) || n < 1 || n > kMaxN || check_k(k)) return 0;
+    return pq2::read_probe_words(layout, n, k);
+}
+
+int pq2_read_probe(const void* weights, int layout, int64_t n, int64_t k, uint32_t* out, void* stream) {
+    if (!weights || !out) return PQ2_EINVAL;
+    if (layout != PQ2_LAYOUT_PLANES && layout != PQ2_LAYOUT_TILES) return PQ2_EINVAL;
+    if (n < 1 || n > kMaxN) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if (!aligned(weights, 16) || !aligned(out, 4)) return PQ2_EALIGN;
+    const size_t wbytes = layout == PQ2_LAYOUT_TILES ? (size_t)pq2::tiles_bytes(n, k) : (size_t)n * (k / kGroup) * 34;
+    if (overlap(out, (size_t)pq2::read_probe_words(layout, n, k) * 4, weights, wbytes)) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(
+        pq2::launch_read_probe(static_cast<const uint8_t*>(weights), layout, n, k, out, (hipStream_t)stream));
+}
+
 int pq2_matmul_small_m_raw(const int8_t* q, const float* xs, const void* raw, int64_t raw_row_stride_bytes, int64_t m,
                            int64_t n, int64_t k, float* y, void* stream) {
     if (!q || !xs || !raw || !y) return PQ2_EINVAL;

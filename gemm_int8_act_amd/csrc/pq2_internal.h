@@ -83,6 +83,12 @@ hipError_t launch_small_m_tiles(const int8_t* q, const float* xs, const uint8_t*
                                 int64_t k, float* y, int max_waves, int split, hipStream_t stream);
 hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int tile, hipStream_t stream);
+// Read-only probes of the weight layouts (layout 0 = planes, 1 = tiles): the
+// decode engines' weight loads without arithmetic; out gets
+// read_probe_words(layout, n, k) XOR folds.
+int64_t read_probe_words(int layout, int64_t n, int64_t k);
+hipError_t launch_read_probe(const uint8_t* weights, int layout, int64_t n, int64_t k, uint32_t* out,
+                             hipStream_t stream);
 // Packed-dot small-m matmul straight from the raw block layout (34 bytes per
 // 128 weights: fp16 scale, then 32 code bytes; rows raw_stride bytes apart),
 // natural-order q; max_waves fixes the k split as for launch_small_m.

@@ -1,0 +1,138 @@
+// probe.hip -- read-only probes of the weight layouts: the decode engines'
+// weight loads with no arithmetic, the ceiling their matmuls are measured
+// against.
+//
+// Page "Kernel experiments: recorded evidence", section H, Test 24 timed
+// copy-free read patterns of the weight layouts (row-major segments against
+// tile-major) to separate what the access pattern allows from what the
+// kernel's work costs.  These probes issue exactly the weight loads of the
+// gfx950 decode engines: the same grid, waves, k split (segments of 8
+// groups, at most 8 waves), instruction widths and cache policy, one segment
+// at a time.  Each wave folds what it reads with XOR (so no load is dead)
+// and writes one word.  Every byte of the layout is read once, so the XOR of
+// all output words is the XOR of the layout's dwords (code dwords and tile
+// units; the planes' fp16 scales each zero-extended), which the tests check.
+#include "pq2_device.h"
+#include "pq2_internal.h"
+
+namespace pq2 {
+
+namespace {
+
+// Tile layout (pq2_prepare_tiles): per 16-row tile and 8-group segment one
+// 4352-byte unit, four 1 KB code blocks (one 16-byte MFMA operand per lane)
+// then the 16 rows' 8 fp16 scales.
+constexpr int kProbeTileRows = 16;
+constexpr int kProbeCodeBlock = 1024;
+constexpr int kProbeUnit = 4 * kProbeCodeBlock + 256;
+// Planes: a wave is 8 row slots of 8 lanes, as in the packed-dot engine.
+constexpr int kProbeRowSlots = 8;
+constexpr int kProbeMaxWaves = 8;
+
+__device__ __forceinline__ uint32_t fold4(const uint4& v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+__device__ __forceinline__ uint32_t wave_xor(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v ^= (uint32_t)__shfl_xor((int)v, d);
+    return v;
+}
+
+// Grid: one workgroup per 16-row tile, one wave per k slice.  Per segment a
+// wave reads the unit's 256 scale bytes (16 bytes per lane; lanes 16..63
+// repeat lanes 0..15 as in the matmul and are not folded) and its four code
+// blocks (16 bytes per lane each, streamed).
+__global__ __launch_bounds__(512) void read_probe_tiles_kernel(const uint8_t* __restrict__ tiles, int s8,
+                                                               int per_wave, uint32_t* __restrict__ out) {
+    const int nwaves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int tile = blockIdx.x;
+    const auto rs = make_rsrc(tiles + (size_t)tile * s8 * kProbeUnit, (uint32_t)(s8 * kProbeUnit));
+    const int seg_end = min((wave + 1) * per_wave, s8);
+    uint32_t f = 0;
+    for (int s = wave * per_wave; s < seg_end; ++s) {
+        const uint32_t unit = (uint32_t)(s * kProbeUnit);
+        const uint4 ws = buf_load16(rs, unit + 4 * kProbeCodeBlock + 16 * (lane & 15));
+        uint4 cw[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) cw[b] = buf_load16<kAuxNonTemporal>(rs, unit + b * kProbeCodeBlock + 16 * lane);
+        f ^= fold4(cw[0]) ^ fold4(cw[1]) ^ fold4(cw[2]) ^ fold4(cw[3]) ^ (lane < 16 ? fold4(ws) : 0u);
+    }
+    f = wave_xor(f);
+    if (lane == 0) out[(size_t)tile * nwaves + wave] = f;
+}
+
+// Grid: one workgroup per 8 rows, one wave per k slice.  Per segment lane j
+// of row slot r reads code bytes 16j and 128 + 16j of the row's 256 (the
+// halves of groups j/2 and 4 + j/2; groups past the end are not read) and
+// the fp16 scale of one of the segment's 8 groups.
+__global__ __launch_bounds__(512) void read_probe_planes_kernel(const uint8_t* __restrict__ codes,
+                                                                const uint16_t* __restrict__ scales, int n, int k,
+                                                                int groups, int per_wave, int nseg,
+                                                                uint32_t* __restrict__ out) {
+    const int nwaves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int slot = lane >> 3;
+    const int j = lane & 7;
+    const int gsel = (j >> 1) + 4 * (j & 1);
+    const int row_base = blockIdx.x * kProbeRowSlots;
+    const int rows_here = min(kProbeRowSlots, n - row_base);
+    const uint32_t k4 = (uint32_t)k >> 2;
+    const auto code_rs = make_rsrc(codes + (size_t)row_base * k4, (uint32_t)rows_here * k4);
+    const auto scale_rs = make_rsrc(scales + (size_t)row_base * groups, (uint32_t)(rows_here * groups * 2));
+    const int seg_end = min((wave + 1) * per_wave, nseg);
+    uint32_t f = 0;
+    for (int s = wave * per_wave; s < seg_end; ++s) {
+        const int g0 = s * 8;
+        const bool okA = g0 + (j >> 1) < groups;
+        const bool okB = g0 + 4 + (j >> 1) < groups;
+        const bool okS = g0 + gsel < groups;
+        const uint32_t off = (uint32_t)slot * k4 + (uint32_t)g0 * 32u + 16u * (uint32_t)j;
+        const uint4 a = buf_load16<kAuxNonTemporal>(code_rs, okA ? off : kBufferOOB);
+        const uint4 b = buf_load16<kAuxNonTemporal>(code_rs, okB ? off + 128u : kBufferOOB);
+        const uint32_t w = buf_load2(scale_rs, okS ? ((uint32_t)slot * groups + g0 + gsel) * 2u : kBufferOOB);
+        f ^= fold4(a) ^ fold4(b) ^ w;
+    }
+    f = wave_xor(f);
+    if (lane == 0) out[(size_t)blockIdx.x * nwaves + wave] = f;
+}
+
+struct ProbeGrid {
+    int64_t blocks;
+    int waves, per_wave, nseg;
+};
+
+// The engines' k split: segments of 8 groups over at most 8 waves.
+ProbeGrid probe_grid(int layout, int64_t n, int64_t k) {
+    ProbeGrid g;
+    g.nseg = (int)((k / 128 + 7) / 8);
+    g.per_wave = (g.nseg + kProbeMaxWaves - 1) / kProbeMaxWaves;
+    g.waves = (g.nseg + g.per_wave - 1) / g.per_wave;
+    g.blocks = layout == 1 ? (n + kProbeTileRows - 1) / kProbeTileRows : (n + kProbeRowSlots - 1) / kProbeRowSlots;
+    return g;
+}
+
+}  // namespace
+
+int64_t read_probe_words(int layout, int64_t n, int64_t k) {
+    const ProbeGrid g = probe_grid(layout, n, k);
+    return g.blocks * g.waves;
+}
+
+hipError_t launch_read_probe(const uint8_t* weights, int layout, int64_t n, int64_t k, uint32_t* out,
+                             hipStream_t stream) {
+    const ProbeGrid g = probe_grid(layout, n, k);
+    clear_stale_error();
+    if (layout == 1) {
+        hipLaunchKernelGGL(read_probe_tiles_kernel, dim3((unsigned)g.blocks), dim3(64 * g.waves), 0, stream, weights,
+                           g.nseg, g.per_wave, out);
+    } else {
+        const uint16_t* scales = reinterpret_cast<const uint16_t*>(weights + n * (k / 4));
+        hipLaunchKernelGGL(read_probe_planes_kernel, dim3((unsigned)g.blocks), dim3(64 * g.waves), 0, stream, weights,
+                           scales, (int)n, (int)k, (int)(k / 128), g.per_wave, g.nseg, out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pq2

@@ -60,6 +60,8 @@ enum {
 
 /* Activation element types for pq2_quantize_act_i8. */
 enum { PQ2_BF16 = 0, PQ2_F16 = 1, PQ2_F32 = 2 };
+/* Weight layouts, for the read probe. */
+enum { PQ2_LAYOUT_PLANES = 0, PQ2_LAYOUT_TILES = 1 };
 
 /* Limits (inclusive). */
 #define PQ2_MAX_SMALL_M 16
@@ -161,6 +163,27 @@ int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const voi
  *         EALIGN, ELAUNCH, EDEVICE. */
 int pq2_matmul_small_m_raw(const int8_t* q, const float* xs, const void* raw, int64_t raw_row_stride_bytes, int64_t m,
                            int64_t n, int64_t k, float* y, void* stream);
+
+/* Read-only probe of a prepared weight layout (page "Kernel experiments",
+ * section H, Test 24: copy-free read patterns of the layouts, the ceiling
+ * the matmuls are measured against).  It issues exactly the weight loads of
+ * the decode engine that reads the layout (planes: the packed-dot engine;
+ * tiles: the tile-layout engine): same grid, waves, k split, load widths and
+ * cache policy, one segment at a time, and no arithmetic but an XOR fold of
+ * what each wave read.  Every byte is read once, so the XOR of the output
+ * words equals the XOR of the layout's dwords (for the planes: the code
+ * plane's dwords and the fp16 scales, each zero-extended).
+ *   weights  device planes (layout PQ2_LAYOUT_PLANES) or tile layout
+ *            (PQ2_LAYOUT_TILES) of an n x k matrix, 16-byte aligned.
+ *   out      device uint32 [pq2_read_probe_words(layout, n, k)], 4-byte
+ *            aligned, fully overwritten; must not overlap the weights.
+ * Errors: EINVAL (null, layout, overlap), ESHAPE (n < 1, k < 128, k % 128,
+ *         k > PQ2_MAX_K), EALIGN, ELAUNCH, EDEVICE. */
+int pq2_read_probe(const void* weights, int layout, int64_t n, int64_t k, uint32_t* out, void* stream);
+
+/* Number of uint32 words pq2_read_probe writes for this layout and shape
+ * (one per wave of its grid); 0 for an invalid layout or shape.  Host only. */
+int64_t pq2_read_probe_words(int layout, int64_t n, int64_t k);
 
 /* Tuning hook for the small-m matmul (benchmarks and tests only; same
  * arguments and result as pq2_matmul_small_m).  engine selects one of four

@@ -35,7 +35,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 29
+    assert len(names) == 31
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -332,3 +332,25 @@ def test_raw_reader_validation():
     assert r(A, B, C, 34, 1, 8, 128, C + 16, None) == EINVAL      # y overlaps raw
     if not _gpu_visible():
         assert r(A, B, C + 2, 170, 4, 8, 640, D, None) == EDEVICE
+
+
+def test_read_probe_validation_and_grid():
+    w = pq2.pq2_read_probe_words
+    # One word per wave: the decode engines' grids and k split (segments of
+    # 8 groups over at most 8 waves).
+    assert w(pq2.LAYOUT_TILES, 10240, 5120) == 640 * 5
+    assert w(pq2.LAYOUT_PLANES, 10240, 5120) == 1280 * 5
+    assert w(pq2.LAYOUT_TILES, 5120, 17408) == 320 * 6       # 17 segments: 6 waves of 3
+    assert w(pq2.LAYOUT_PLANES, 33, 640) == 5                # ragged rows, one partial segment
+    assert w(pq2.LAYOUT_TILES, 17, 8192) == 2 * 8
+    assert w(2, 8, 128) == 0 and w(0, 0, 128) == 0 and w(0, 8, 96) == 0
+    r = pq2.lib.pq2_read_probe
+    assert r(None, 0, 8, 128, D, None) == EINVAL
+    assert r(A, 2, 8, 128, D, None) == EINVAL                # layout
+    assert r(A, 0, 0, 128, D, None) == ESHAPE
+    assert r(A, 1, 8, 96, D, None) == ESHAPE
+    assert r(A + 4, 0, 8, 128, D, None) == EALIGN            # weights not 16-byte aligned
+    assert r(A, 0, 8, 128, D + 2, None) == EALIGN            # out not 4-byte aligned
+    assert r(A, 0, 8, 128, A + 16, None) == EINVAL           # out overlaps the weights
+    if not _gpu_visible():
+        assert r(A, 1, 10240, 5120, D, None) == EDEVICE

@@ -1102,3 +1102,32 @@ def test_small_m_raw_workloads(name):
         mi, ni = _sample_indices(m, w.n, 300, seed=m + 7)
         y_ref, bound = oracle.matmul_raw_sample(qo, xso, raw_np, w.n, w.k, mi, ni)
         assert_within(y[mi, ni], y_ref, bound, f"raw {name} m={m}")
+
+
+def _xor_dwords(buf_u8):
+    return int(np.bitwise_xor.reduce(np.ascontiguousarray(buf_u8).view(np.uint32)))
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (33, 640), (1000, 5120), (37, 17408), (300, 1152)])
+def test_read_probe_reads_every_byte_once(n, k):
+    """The read probe's XOR folds equal the XOR of every dword of the layout
+    (planes: code dwords and zero-extended scales), computed on the host
+    from the oracle's own preparation of the same weights."""
+    pq2 = _pq2()
+    announce(f"read probe n={n} k={k}")
+    raw_np = workloads.make_raw_weights(n, k, seed=150 + n, codes="ternary+3", row_pad=2)
+    planes_ref = oracle.prepare_planes(raw_np, n, k)
+    tiles_ref = oracle.prepare_tiles(raw_np, n, k)
+    codes_bytes = n * (k // 4)
+    want = {
+        pq2.LAYOUT_PLANES: _xor_dwords(planes_ref[:codes_bytes])
+        ^ int(np.bitwise_xor.reduce(planes_ref[codes_bytes:].view(np.uint16).astype(np.uint32))),
+        pq2.LAYOUT_TILES: _xor_dwords(tiles_ref),
+    }
+    for layout, weights in ((pq2.LAYOUT_PLANES, gpu_planes(raw_np, n, k)), (pq2.LAYOUT_TILES, gpu_tiles(raw_np, n, k))):
+        words = pq2.pq2_read_probe_words(layout, n, k)
+        out = torch.full((words,), -1, dtype=torch.int32, device=DEV)
+        pq2.pq2_read_probe(weights, layout, n, k, out)
+        torch.cuda.synchronize()
+        got = int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)))
+        assert got == want[layout], f"layout {layout}: probe fold {got:#x}, layout xor {want[layout]:#x}"
