@@ -65,7 +65,8 @@ __device__ __forceinline__ int swz(int i, int t) { return i * 8 + (t ^ ((i >> 1)
 // covers natural positions 32kk .. 32kk + 31 of the group) 64 or 32 for the
 // smaller activation groups of page "Kernel experiments: recorded evidence",
 // section C, Tests 8 and 9: each activation group's k-steps form their own
-// INT32 chain, rescaled by its own xs into acc, in k order.
+// INT32 chain; a weight group's terms float(dot) * xs are summed in k order,
+// then scaled by its ws into acc.
 template <int BM, int BN, bool PLANE_A, bool TILES, int AG = 128>
 __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__ q,
                                                       const float* __restrict__ xs,
@@ -225,6 +226,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
         if (g + 1 < groups) load_stage(g + 1);
 
         // Activation group t of this weight group: k-steps KS*t .. KS*t + KS - 1.
+        // With S > 1 the group's terms float(dot_t) * xs_t are summed first
+        // (gs), then scaled by ws once: 2S + 1 VALU per output, not 3S.
+        float gs[S > 1 ? MT : 1][S > 1 ? NT : 1][16];
 #pragma unroll
         for (int t = 0; t < S; ++t) {
         v16i D[MT][NT];
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
         // 8*(r/4) + 4*hi + (r%4), r = 0..15.
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const float wsv = wsS[buf][wn * (BN / 2) + nt * 32 + l32];
+            const float wsv = S == 1 ? wsS[buf][wn * (BN / 2) + nt * 32 + l32] : 0.0f;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -268,23 +272,40 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = rb * 4 + e;
-                        acc[mt][nt][r] = __builtin_fmaf((float)D[mt][nt][r] * xa[e], wsv, acc[mt][nt][r]);
+                        if constexpr (S == 1) {
+                            acc[mt][nt][r] = __builtin_fmaf((float)D[mt][nt][r] * xa[e], wsv, acc[mt][nt][r]);
+                        } else if (t == 0) {
+                            gs[mt][nt][r] = (float)D[mt][nt][r] * xa[e];
+                        } else {
+                            gs[mt][nt][r] = __builtin_fmaf((float)D[mt][nt][r], xa[e], gs[mt][nt][r]);
+                        }
                     }
                 }
             }
         }
         // One activation group's chain at a time: the empty statement takes
-        // the sums as operands and orders memory, so this group's rescale
-        // finishes before the next group's fragments are read.  Without it the
-        // compiler starts every group's products first and holds S sets of D.
+        // the partial sums as operands and orders memory, so this group's
+        // terms are added before the next group's fragments are read.  Without
+        // it the compiler starts every group's products first and holds S sets
+        // of D.
         if constexpr (S > 1) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(acc[mt][nt][r]) : : "memory");
+                    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(gs[mt][nt][r]) : : "memory");
         }
+        }
+        if constexpr (S > 1) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float wsv = wsS[buf][wn * (BN / 2) + nt * 32 + l32];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[mt][nt][r] = __builtin_fmaf(gs[mt][nt][r], wsv, acc[mt][nt][r]);
+            }
         }
         if (g + 1 < groups) store_stage(buf ^ 1);
         __syncthreads();

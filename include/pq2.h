@@ -429,8 +429,9 @@ int pq2_matmul_prefill_tiles_tuned(const int8_t* q, const float* xs, const void*
 /* Tile-layout prefill matmul with activation groups of agroup elements
  * (page "Kernel experiments", section C, Tests 8 and 9, which timed them at
  * prefill sizes): the y of pq2_matmul_small_m_tiles_g's definition for any m.
- * Each activation group's integer product is rescaled by its own xs into the
- * fp32 sum, in k order per output; agroup = 128 gives the bits of
+ * Each activation group's integer product is exact; a weight block's terms
+ * float(dot_a) * xs[m][a] are summed in k order, then scaled by ws[n][g] into
+ * the output's fp32 sum, block after block; agroup = 128 gives the bits of
  * pq2_matmul_prefill_tiles.  q and xs come from pq2_quantize_act_i8_g with
  * the same agroup.
  *   q       device int8 [m][k], 16-byte aligned.  xs  device float [m][k/agroup].
