@@ -171,8 +171,8 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
 // AG: activation group size (128; 64 or 32 for the smaller activation groups
 // of page "Kernel experiments: recorded evidence", section C, Tests 8 and 9:
 // natural-order q only).  Each activation group has its own D chain seeded
-// with its own -sum(q) and its own fp32 term fma((float)dot * xs_a, ws, acc),
-// added in k order within the weight group.
+// with its own -sum(q); the weight group's terms (float)dot * xs_a are summed
+// in k order, then scaled by ws into the class accumulator, fma(sum, ws, acc).
 template <int MC, int CPW, int SRC, int AG = 128>
 __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const void* __restrict__ x, int64_t x_stride,
@@ -395,14 +395,20 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
                                                                       Bh[h], Dt[t], 0, 0, 0);
                     }
                 }
+                // The weight group's terms float(dot_t) * xs_t in k order, then
+                // one scale by ws into the class accumulator.
                 const float wsf = half_of(wsv, c_lo + c);
+                float gsum[R];
 #pragma unroll
                 for (int t = 0; t < S; ++t) {
                     const float4 xg = *reinterpret_cast<const float4*>(xs_lds + ((c_lo + c) * S + t) * 8);
                     const float xv[4] = {xg.x, xg.y, xg.z, xg.w};
 #pragma unroll
-                    for (int r = 0; r < R; ++r) acc[c][r] = __builtin_fmaf((float)Dt[t][r] * xv[r], wsf, acc[c][r]);
+                    for (int r = 0; r < R; ++r)
+                        gsum[r] = t == 0 ? (float)Dt[t][r] * xv[r] : __builtin_fmaf((float)Dt[t][r], xv[r], gsum[r]);
                 }
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[c][r] = __builtin_fmaf(gsum[r], wsf, acc[c][r]);
             }
           } else {
             v4i D[2];

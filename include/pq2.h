@@ -396,7 +396,8 @@ int pq2_quantize_act_i8_g(const void* x, int dtype, int64_t x_row_stride_elems, 
  *             groups a inside block g of float(dot_a) * xs[m][a],
  * dot_a the exact integer dot of group a's q with the block's codes minus 1.
  * Each activation group has its own integer product (no rounding inside it);
- * the fp32 terms are added in k order within a weight block, then as
+ * a weight block's terms float(dot_a) * xs[m][a] are summed in k order and
+ * scaled by ws[n][g], and these block terms are added as
  * pq2_matmul_small_m_tiles adds its group terms (so agroup = 128 gives the
  * same bits as pq2_matmul_small_m_tiles).  q and xs come from
  * pq2_quantize_act_i8_g with the same agroup.
