@@ -406,6 +406,10 @@ def main():
         "kernel_source_digest": digest,
         "planes_kernel_achieved": round(tot_bytes / (ptot_us * 1e-6) / 1e9, 1),
         "planes_kernel_mean_launch_us": round(ptot_us / len(ms), 3),
+        # The same layout's weight loads alone (pq2_read_probe): the mean
+        # launch as a multiple of that read time.
+        "read_probe_us": probe["tiles"]["us"],
+        "mean_launch_vs_read_probe": round((tot_us / len(ms)) / probe["tiles"]["us"], 3),
     }
 
     result = {
