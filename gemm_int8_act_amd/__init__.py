@@ -303,7 +303,7 @@ def pq2_matmul_small_m_tiles_tuned(q, xs, tiles, y, max_waves=0, split=0, stream
 
 
 def pq2_gemv_tiles(x, tiles, y, q_work=None, xs_work=None, stream=None) -> None:
-    """y = W x from activations: one fused launch at m = 1 (k <= 8192), else
+    """y = W x from activations: one fused launch at m <= 2 (k <= 8192), else
     the quantiser into q_work (int8 [m][k]) / xs_work (float32 [m][k/128])
     and the tile matmul; the same bits either way."""
     import torch

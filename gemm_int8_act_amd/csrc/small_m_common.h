@@ -52,24 +52,19 @@ __device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum
     amax = max8_f(amax);
     scale = amax / 127.0f;
     const float d = scale > 0.0f ? scale : 1.0f;
-    const float r0 = __builtin_amdgcn_rcpf(d);
-    const float r = __builtin_fmaf(__builtin_fmaf(-d, r0, 1.0f), r0, r0);
-    constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+    // The IEEE quotient v / d without a division per element.  v / d of two
+    // fp32 values is either an fp32 value or at least 2^-49 (relative) away
+    // from every fp32 rounding midpoint (its numerator and denominator have
+    // 24-bit significands, a midpoint 25 bits), while the double product
+    // v * fl64(1 / d) is within 2^-52 of it; so rounding that product to fp32
+    // gives exactly the IEEE quotient, ties and subnormal scales included.
+    const double r = 1.0 / (double)d;
+    constexpr float kRound = 12582912.0f;  // 1.5 * 2^23: t + kRound rounds t half to even
     uint32_t bits[16];
-    float worst = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const float t = v[e] * r;
-        const float s = t + kRound;
-        worst = fmaxf(worst, fabsf(t - (s - kRound)));
-        bits[e] = __float_as_uint(s);
-    }
-    if (!(d >= 0x1p-126f && worst <= 0.5f - 0x1p-14f)) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float qf = fminf(127.0f, fmaxf(-127.0f, rintf(v[e] / d)));
-            bits[e] = (uint32_t)(int)qf;
-        }
+        const float t = fminf(127.0f, fmaxf(-127.0f, (float)((double)v[e] * r)));
+        bits[e] = __float_as_uint(t + kRound);  // low byte: the two's-complement code
     }
     uint4 out;
     if constexpr (PLANE) {

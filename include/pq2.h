@@ -367,14 +367,14 @@ int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row
  * experiments", Tests 3-5: the integer GEMV is called with the activations
  * and the weights and returns the outputs, quantising inside): the
  * library's fastest of pq2_matmul_small_m_tiles_fused (one launch; taken at
- * m = 1 with k <= 8192, where every wave holds one k segment) and
+ * m <= 2 with k <= 8192, where every wave holds one k segment) and
  * pq2_quantize_act_i8 into the caller's q_work / xs_work followed by
  * pq2_matmul_small_m_tiles.  Both give the same bits.
  *   x       as pq2_matmul_small_m_tiles_fused (on the fused path) or
  *           pq2_quantize_act_i8 (otherwise).
  *   q_work  device int8 [m][k], 16-byte aligned; xs_work device float
  *           [m][k/128], 4-byte aligned: scratch owned by the caller, written
- *           on the two-launch path (may be NULL when m = 1 and k <= 8192).
+ *           on the two-launch path (may be NULL when m <= 2 and k <= 8192).
  *   tiles, y as pq2_matmul_small_m_tiles; nothing may overlap.
  * Errors: those of the path taken, checked before anything is enqueued. */
 int pq2_gemv_tiles(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m, int64_t n,

@@ -177,20 +177,20 @@ def test_small_m_tiles_fused_validation():
 
 def test_gemv_tiles_validation():
     f = pq2.lib.pq2_gemv_tiles
-    # m = 1, k <= 8192: the fused path's checks; no scratch needed.
+    # m <= 2, k <= 8192: the fused path's checks; no scratch needed.
     assert f(None, 0, 128, C, 1, 8, 128, D, None, None, None) == EINVAL
     assert f(A, 3, 128, C, 1, 8, 128, D, None, None, None) == EINVAL         # dtype
     assert f(A + 2, 0, 128, C, 1, 8, 128, D, None, None, None) == EALIGN     # x not 16-byte aligned
     # Otherwise the two-launch path: scratch required, everything checked first.
-    assert f(A, 0, 128, C, 2, 8, 128, D, None, E, None) == EINVAL            # no q scratch
-    assert f(A, 0, 128, C, 2, 8, 128, D, B, None, None) == EINVAL            # no xs scratch
+    assert f(A, 0, 128, C, 3, 8, 128, D, None, E, None) == EINVAL            # no q scratch
+    assert f(A, 0, 128, C, 3, 8, 128, D, B, None, None) == EINVAL            # no xs scratch
     assert f(A, 0, 128, C, 17, 8, 128, D, B, E, None) == ESHAPE              # columns
-    assert f(A, 0, 100, C, 2, 8, 128, D, B, E, None) == ESHAPE               # stride < k
-    assert f(A, 0, 128, C, 2, 8, 128, D, B + 8, E, None) == EALIGN           # q scratch not 16-byte aligned
-    assert f(A + 1, 0, 128, C, 2, 8, 128, D, B, E, None) == EALIGN           # bf16 x not 2-byte aligned
-    assert f(A, 0, 128, C, 2, 8, 128, D, A + 64, E, None) == EINVAL          # q scratch overlaps x
-    assert f(A, 0, 128, C, 2, 8, 128, A + 128, B, E, None) == EINVAL         # y overlaps x
-    assert f(A, 0, 128, C, 2, 8, 128, D, B, C + 64, None) == EINVAL          # xs scratch overlaps the tiles
+    assert f(A, 0, 100, C, 3, 8, 128, D, B, E, None) == ESHAPE               # stride < k
+    assert f(A, 0, 128, C, 3, 8, 128, D, B + 8, E, None) == EALIGN           # q scratch not 16-byte aligned
+    assert f(A + 1, 0, 128, C, 3, 8, 128, D, B, E, None) == EALIGN           # bf16 x not 2-byte aligned
+    assert f(A, 0, 128, C, 3, 8, 128, D, A + 64, E, None) == EINVAL          # q scratch overlaps x
+    assert f(A, 0, 128, C, 3, 8, 128, A + 128, B, E, None) == EINVAL         # y overlaps x
+    assert f(A, 0, 128, C, 3, 8, 128, D, B, C + 64, None) == EINVAL          # xs scratch overlaps the tiles
     assert f(A, 0, 16384, C, 1, 8, 16384, D, None, None, None) == EINVAL     # long k takes the two-launch path
     if not _gpu_visible():
         assert f(A, 0, 5120, C, 1, 8, 5120, D, None, None, None) == EDEVICE
