@@ -91,10 +91,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 
     const float scale = amax / 127.0f;                 // one IEEE division
     const float divisor = scale > 0.0f ? scale : 1.0f;
+    // v / divisor as the IEEE quotient without a division per element: the
+    // double product v * fl64(1 / divisor), rounded to fp32, is that quotient
+    // (two fp32 values' quotient is an fp32 value or at least 2^-49 relative
+    // from every fp32 rounding midpoint; the product is within 2^-52 of it).
+    const double inv = 1.0 / (double)divisor;
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        float r = rintf(v[e] / divisor);               // IEEE division, ties to even
+        float r = rintf((float)((double)v[e] * inv));  // ties to even
         r = fminf(127.0f, fmaxf(-127.0f, r));
         packed[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
     }
