@@ -56,6 +56,13 @@ EXPORTED = (
     "pq2_matmul_small_m_raw",
     "pq2_read_probe",
     "pq2_read_probe_words",
+    "pq2_matmul_small_m_tiles_splitk",
+    "pq2_matmul_small_m_tiles_splitk_tuned",
+    "pq2_tiles_splitk_partial_floats",
+    "pq2_tiles_splitk_counter_words",
+    "pq2_stream_probe",
+    "pq2_stream_probe_words",
+    "pq2_empty_probe",
 )
 
 
@@ -147,6 +154,20 @@ def _load_library():
     lib.pq2_matmul_small_m_tiles_fused.restype = i32
     lib.pq2_matmul_small_m_tiles_fused_tuned.argtypes = [p, i32, i64, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tiles_fused_tuned.restype = i32
+    lib.pq2_matmul_small_m_tiles_splitk.argtypes = [p, p, p, i64, i64, i64, p, p, p, p]
+    lib.pq2_matmul_small_m_tiles_splitk.restype = i32
+    lib.pq2_matmul_small_m_tiles_splitk_tuned.argtypes = [p, p, p, i64, i64, i64, p, p, p, i32, p]
+    lib.pq2_matmul_small_m_tiles_splitk_tuned.restype = i32
+    lib.pq2_tiles_splitk_partial_floats.argtypes = [i64, i64, i64]
+    lib.pq2_tiles_splitk_partial_floats.restype = i64
+    lib.pq2_tiles_splitk_counter_words.argtypes = [i64]
+    lib.pq2_tiles_splitk_counter_words.restype = i64
+    lib.pq2_stream_probe.argtypes = [p, i64, i64, i32, ctypes.c_uint32, p, p]
+    lib.pq2_stream_probe.restype = i32
+    lib.pq2_stream_probe_words.argtypes = [i64]
+    lib.pq2_stream_probe_words.restype = i64
+    lib.pq2_empty_probe.argtypes = [i64, i32, p]
+    lib.pq2_empty_probe.restype = i32
     return lib
 
 
@@ -324,6 +345,71 @@ def pq2_gemv_tiles(x, tiles, y, q_work=None, xs_work=None, stream=None) -> None:
         qp, xp = _dev_ptr(q_work, "q_work"), _dev_ptr(xs_work, "xs_work")
     _check(lib.pq2_gemv_tiles(_dev_ptr(x, "x"), _dtype_code(x), x.stride(0), _dev_ptr(tiles, "tiles"), m, n, k,
                               _dev_ptr(y, "y"), qp, xp, _stream(stream)), "pq2_gemv_tiles")
+
+
+def pq2_tiles_splitk_partial_floats(m: int, n: int, k: int) -> int:
+    """Floats of partial sums pq2_matmul_small_m_tiles_splitk needs."""
+    v = int(lib.pq2_tiles_splitk_partial_floats(m, n, k))
+    if v < 0:
+        raise ValueError(f"invalid shape m={m} n={n} k={k}")
+    return v
+
+
+def pq2_tiles_splitk_counter_words(n: int) -> int:
+    """Counter words pq2_matmul_small_m_tiles_splitk needs (zero before the
+    first call; every call leaves them zero)."""
+    v = int(lib.pq2_tiles_splitk_counter_words(n))
+    if v < 0:
+        raise ValueError(f"invalid n={n}")
+    return v
+
+
+def _splitk_args(q, xs, tiles, y, partials, counters):
+    import torch
+    args = _tiles_args(q, xs, tiles, y)
+    m, n, k = args[3], args[4], args[5]
+    if partials.dtype != torch.float32 or not partials.is_contiguous() or \
+            partials.numel() < pq2_tiles_splitk_partial_floats(m, n, k):
+        raise ValueError("partials: contiguous float32 of pq2_tiles_splitk_partial_floats(m, n, k) expected")
+    if counters.dtype != torch.int32 or not counters.is_contiguous() or \
+            counters.numel() < pq2_tiles_splitk_counter_words(n):
+        raise ValueError("counters: contiguous int32 of pq2_tiles_splitk_counter_words(n) (all zero) expected")
+    return args + (_dev_ptr(partials, "partials"), _dev_ptr(counters, "counters"))
+
+
+def pq2_matmul_small_m_tiles_splitk(q, xs, tiles, y, partials, counters, stream=None) -> None:
+    """Split-k tile matmul: partials float32 scratch, counters int32 words
+    that are zero before the first call (each call leaves them zero)."""
+    _check(lib.pq2_matmul_small_m_tiles_splitk(*_splitk_args(q, xs, tiles, y, partials, counters), _stream(stream)),
+           "pq2_matmul_small_m_tiles_splitk")
+
+
+def pq2_matmul_small_m_tiles_splitk_tuned(q, xs, tiles, y, partials, counters, waves=0, stream=None) -> None:
+    _check(lib.pq2_matmul_small_m_tiles_splitk_tuned(*_splitk_args(q, xs, tiles, y, partials, counters), waves,
+                                                     _stream(stream)), "pq2_matmul_small_m_tiles_splitk_tuned")
+
+
+def pq2_stream_probe_words(workgroups: int) -> int:
+    """Words pq2_stream_probe writes (4 per workgroup)."""
+    return int(lib.pq2_stream_probe_words(workgroups))
+
+
+def pq2_stream_probe(buf, nbytes: int, workgroups: int, out, store_all: bool = False, sentinel: int = 0,
+                     stream=None) -> None:
+    """Linear streaming read of the first nbytes of buf (any contiguous
+    device tensor); out int32 [pq2_stream_probe_words(workgroups)]."""
+    import torch
+    if not buf.is_contiguous() or not out.is_contiguous() or out.dtype != torch.int32:
+        raise ValueError("buf contiguous and out contiguous int32 expected")
+    if buf.numel() * buf.element_size() < nbytes or out.numel() < pq2_stream_probe_words(workgroups):
+        raise ValueError("buf or out too small")
+    _check(lib.pq2_stream_probe(_dev_ptr(buf, "buf"), nbytes, workgroups, 1 if store_all else 0,
+                                sentinel & 0xFFFFFFFF, _dev_ptr(out, "out"), _stream(stream)), "pq2_stream_probe")
+
+
+def pq2_empty_probe(workgroups: int = 1, waves: int = 1, stream=None) -> None:
+    """An empty kernel (the launch floor of back-to-back launches)."""
+    _check(lib.pq2_empty_probe(workgroups, waves, _stream(stream)), "pq2_empty_probe")
 
 
 def pq2_quantize_act_i8_g(x, q, xs, agroup: int, stream=None) -> None:

@@ -4,6 +4,8 @@
 // HIP runtime, returns a status instead of aborting, and enqueues its kernel
 // on the caller's stream.  Buffers are owned by the caller.
 #include "../../include/pq2.h"
+#include "../../include/pq2_measure.h"
+#include "../../include/pq2_tuning.h"
 #include "pq2_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -208,9 +210,17 @@ int pq2_gemv_tiles(const void* x, int dtype, int64_t x_row_stride_elems, const v
     // One or two columns whose waves each hold a single segment (k <= 1024 * 8
     // at the default k split): the single launch wins (K = 5120: 5.3 against
     // 6.9 us at one column, 6.5 against 7.3 at two); otherwise the quantiser
-    // launch plus the tile matmul.  Both give the same bits.
-    if (m <= 2 && k <= 8192)
-        return pq2_matmul_small_m_tiles_fused(x, dtype, x_row_stride_elems, tiles, m, n, k, y, stream);
+    // launch plus the tile matmul.  Both give the same bits.  x that the
+    // fused kernel cannot read (not 16-byte aligned rows, or a span of 2^31
+    // bytes or more) takes the two-launch path when scratch is given.
+    if (m <= 2 && k <= 8192) {
+        const int esize = dtype == PQ2_F32 ? 4 : 2;
+        const bool fused_ok = x && aligned(x, 16) && (x_row_stride_elems * esize) % 16 == 0 && m >= 1 &&
+                              x_row_stride_elems >= k &&
+                              ((size_t)(m - 1) * x_row_stride_elems + k) * esize < ((size_t)1 << 31);
+        if (fused_ok || !q_work || !xs_work)
+            return pq2_matmul_small_m_tiles_fused(x, dtype, x_row_stride_elems, tiles, m, n, k, y, stream);
+    }
     if (!x || !q_work || !xs_work) return PQ2_EINVAL;
     if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
     if (int rc = check_matmul_args(q_work, xs_work, tiles, m, n, k, y, PQ2_MAX_SMALL_M, true)) return rc;
@@ -226,6 +236,68 @@ int pq2_gemv_tiles(const void* x, int dtype, int64_t x_row_stride_elems, const v
         return PQ2_EINVAL;
     if (int rc = pq2_quantize_act_i8(x, dtype, x_row_stride_elems, m, k, q_work, xs_work, stream)) return rc;
     return pq2_matmul_small_m_tiles(q_work, xs_work, tiles, m, n, k, y, stream);
+}
+
+int64_t pq2_tiles_splitk_partial_floats(int64_t m, int64_t n, int64_t k) {
+    if (m < 1 || m > PQ2_MAX_SMALL_M || n < 1 || n > kMaxN || check_k(k)) return -1;
+    return pq2::splitk_plan(m, n, k, pq2::kSplitKDefaultWaves).partial_floats;
+}
+
+int64_t pq2_tiles_splitk_counter_words(int64_t n) {
+    if (n < 1 || n > kMaxN) return -1;
+    return (int64_t)pq2::kSplitKMaxChunks * ((n + 15) / 16);
+}
+
+int pq2_matmul_small_m_tiles_splitk_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                                          int64_t k, float* y, float* partials, uint32_t* counters, int waves,
+                                          void* stream) {
+    if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, PQ2_MAX_SMALL_M, true)) return rc;
+    if (!partials || !counters) return PQ2_EINVAL;
+    if (waves < 0 || waves > 16) return PQ2_EINVAL;
+    if (!aligned(partials, 4) || !aligned(counters, 4)) return PQ2_EALIGN;
+    const size_t pbytes = (size_t)pq2_tiles_splitk_partial_floats(m, n, k) * 4;
+    const size_t cbytes = (size_t)pq2_tiles_splitk_counter_words(n) * 4;
+    const size_t tbytes = (size_t)pq2::tiles_bytes(n, k);
+    const void* bufs[5] = {partials, counters, y, q, xs};
+    const size_t lens[5] = {pbytes, cbytes, (size_t)m * n * 4, (size_t)m * k, (size_t)m * (k / kGroup) * 4};
+    for (int i = 0; i < 2; ++i) {
+        if (overlap(bufs[i], lens[i], tiles, tbytes)) return PQ2_EINVAL;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(bufs[i], lens[i], bufs[j], lens[j])) return PQ2_EINVAL;
+    }
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m_tiles_splitk(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, y,
+                                                          partials, counters,
+                                                          waves ? waves : pq2::kSplitKDefaultWaves,
+                                                          (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_tiles_splitk(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                                    int64_t k, float* y, float* partials, uint32_t* counters, void* stream) {
+    return pq2_matmul_small_m_tiles_splitk_tuned(q, xs, tiles, m, n, k, y, partials, counters, 0, stream);
+}
+
+int64_t pq2_stream_probe_words(int64_t workgroups) {
+    if (workgroups < 1 || workgroups > 65536) return 0;
+    return pq2::stream_probe_words(workgroups);
+}
+
+int pq2_stream_probe(const void* buf, int64_t bytes, int64_t workgroups, int store_all, uint32_t sentinel,
+                     uint32_t* out, void* stream) {
+    if (!buf || !out) return PQ2_EINVAL;
+    if (bytes < 16 || bytes % 16 || bytes >= ((int64_t)1 << 31) || workgroups < 1 || workgroups > 65536)
+        return PQ2_ESHAPE;
+    if (!aligned(buf, 16) || !aligned(out, 4)) return PQ2_EALIGN;
+    if (overlap(out, (size_t)pq2::stream_probe_words(workgroups) * 4, buf, (size_t)bytes)) return PQ2_EINVAL;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_stream_probe(static_cast<const uint8_t*>(buf), bytes, workgroups,
+                                                  store_all ? 1 : 0, sentinel, out, (hipStream_t)stream));
+}
+
+int pq2_empty_probe(int64_t workgroups, int waves, void* stream) {
+    if (workgroups < 1 || workgroups > ((int64_t)1 << 20) || waves < 1 || waves > 16) return PQ2_ESHAPE;
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_empty_probe(workgroups, waves, (hipStream_t)stream));
 }
 
 int pq2_quantize_act_i8_g(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,

@@ -81,6 +81,21 @@ int tiles_default_split(int64_t m, int64_t k, int max_waves);
 bool tiles_supported(int64_t k, int max_waves, int split);
 hipError_t launch_small_m_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int max_waves, int split, hipStream_t stream);
+// Split-k tile engine: one segment per wave, the k slices of a tile spread
+// over several workgroups; partial sums [nseg][m][n] fp32 and one counter per
+// (column pass, tile) (kSplitKMaxChunks x tiles words, zero before the call
+// and left zero by it).  `waves` (1..16) bounds the waves per workgroup.
+constexpr int kSplitKMaxChunks = 4;    // column passes for m <= 16 (passes of m <= 4, or of eight)
+constexpr int kSplitKDefaultWaves = 6;
+struct SplitKPlan {
+    int nseg, ks, waves, mc, chunks;
+    int64_t tiles, partial_floats, counters;
+};
+SplitKPlan splitk_plan(int64_t m, int64_t n, int64_t k, int waves);
+bool splitk_default(int64_t k);
+hipError_t launch_small_m_tiles_splitk(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                       int64_t k, float* y, float* partials, uint32_t* counters, int waves,
+                                       hipStream_t stream);
 hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int tile, hipStream_t stream);
 // Read-only probes of the weight layouts (layout 0 = planes, 1 = tiles): the
@@ -89,6 +104,12 @@ hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t*
 int64_t read_probe_words(int layout, int64_t n, int64_t k);
 hipError_t launch_read_probe(const uint8_t* weights, int layout, int64_t n, int64_t k, uint32_t* out,
                              hipStream_t stream);
+// Linear stream read of a buffer (workgroups x 4 waves, grid-stride over 1 KB
+// wave chunks) and an empty kernel: the read ceiling and launch floor.
+int64_t stream_probe_words(int64_t workgroups);
+hipError_t launch_stream_probe(const uint8_t* buf, int64_t bytes, int64_t workgroups, int store_all,
+                               uint32_t sentinel, uint32_t* out, hipStream_t stream);
+hipError_t launch_empty_probe(int64_t workgroups, int waves, hipStream_t stream);
 // Packed-dot small-m matmul straight from the raw block layout (34 bytes per
 // 128 weights: fp16 scale, then 32 code bytes; rows raw_stride bytes apart),
 // natural-order q; max_waves fixes the k split as for launch_small_m.

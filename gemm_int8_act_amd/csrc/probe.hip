@@ -52,7 +52,7 @@ __global__ __launch_bounds__(512) void read_probe_tiles_kernel(const uint8_t* __
     uint32_t f = 0;
     for (int s = wave * per_wave; s < seg_end; ++s) {
         const uint32_t unit = (uint32_t)(s * kProbeUnit);
-        const uint4 ws = buf_load16(rs, unit + 4 * kProbeCodeBlock + 16 * (lane & 15));
+        const uint4 ws = buf_load16<kAuxNonTemporal>(rs, unit + 4 * kProbeCodeBlock + 16 * (lane & 15));
         uint4 cw[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) cw[b] = buf_load16<kAuxNonTemporal>(rs, unit + b * kProbeCodeBlock + 16 * lane);
@@ -98,6 +98,35 @@ __global__ __launch_bounds__(512) void read_probe_planes_kernel(const uint8_t* _
     if (lane == 0) out[(size_t)blockIdx.x * nwaves + wave] = f;
 }
 
+// Linear stream read of `bytes` bytes (a multiple of 16), shaped like no
+// decode engine: grid-stride over 1 KB wave chunks.  Iteration i, workgroup
+// w, wave v reads chunk (i * G + w) * W + v, one 16-byte non-temporal load
+// per lane; chunks past the end read zero (buffer range check).  Each wave
+// folds what it read with XOR.  store_all = 1 writes every wave's fold (the
+// XOR of all words is the XOR of the buffer's dwords); store_all = 0 writes
+// a wave's fold only if it equals `sentinel`, so a timed run is a pure read
+// (any output store adds the latency of one store to the end of a launch).
+__global__ __launch_bounds__(256) void stream_probe_kernel(const uint8_t* __restrict__ buf, uint32_t bytes, int iters,
+                                                           int store_all, uint32_t sentinel,
+                                                           uint32_t* __restrict__ out) {
+    const int nwaves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const auto rs = make_rsrc(buf, bytes);
+    const uint32_t wave_id = (uint32_t)blockIdx.x * nwaves + wave;
+    const uint32_t stride = gridDim.x * (uint32_t)nwaves * 1024u;
+    uint32_t f = 0;
+    uint32_t off = wave_id * 1024u + 16u * lane;
+    for (int i = 0; i < iters; ++i, off += stride) f ^= fold4(buf_load16<kAuxNonTemporal>(rs, off < bytes ? off : kBufferOOB));
+    f = wave_xor(f);
+    if (lane == 0 && (store_all || f == sentinel)) out[wave_id] = f;
+}
+
+// An empty kernel: the launch floor of a graph of back-to-back launches.
+__global__ void empty_probe_kernel(uint32_t* out, int never) {
+    if (never == 1 && threadIdx.x == 0) out[blockIdx.x] = 0;
+}
+
 struct ProbeGrid {
     int64_t blocks;
     int waves, per_wave, nseg;
@@ -114,6 +143,26 @@ ProbeGrid probe_grid(int layout, int64_t n, int64_t k) {
 }
 
 }  // namespace
+
+constexpr int kStreamWaves = 4;
+
+int64_t stream_probe_words(int64_t workgroups) { return workgroups * kStreamWaves; }
+
+hipError_t launch_stream_probe(const uint8_t* buf, int64_t bytes, int64_t workgroups, int store_all,
+                               uint32_t sentinel, uint32_t* out, hipStream_t stream) {
+    const int64_t per_iter = workgroups * kStreamWaves * 1024;
+    const int iters = (int)((bytes + per_iter - 1) / per_iter);
+    clear_stale_error();
+    hipLaunchKernelGGL(stream_probe_kernel, dim3((unsigned)workgroups), dim3(64 * kStreamWaves), 0, stream, buf,
+                       (uint32_t)bytes, iters, store_all, sentinel, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_empty_probe(int64_t workgroups, int waves, hipStream_t stream) {
+    clear_stale_error();
+    hipLaunchKernelGGL(empty_probe_kernel, dim3((unsigned)workgroups), dim3(64 * waves), 0, stream, nullptr, 0);
+    return hipGetLastError();
+}
 
 int64_t read_probe_words(int layout, int64_t n, int64_t k) {
     const ProbeGrid g = probe_grid(layout, n, k);

@@ -127,6 +127,15 @@ __global__ void prepare_tile_scales_kernel(const uint8_t* __restrict__ raw, int6
 
 __device__ __forceinline__ void keep_order() { __builtin_amdgcn_sched_barrier(0); }
 
+// s_waitcnt vmcnt(0) (GFX9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15): this
+// wave's vector memory operations, stores included, have completed.  The
+// signal fences keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void wait_stores_complete() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // j mod mcount for j < 16 and mcount = 1..8 (mcount is uniform), without
 // the generic integer division.
 __device__ __forceinline__ int small_mod(int j, int mcount) {
@@ -173,11 +182,20 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
 // natural-order q only).  Each activation group has its own D chain seeded
 // with its own -sum(q); the weight group's terms (float)dot * xs_a are summed
 // in k order, then scaled by ws into the class accumulator, fma(sum, ws, acc).
-template <int MC, int CPW, int SRC, int AG = 128>
-__global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
+//
+// SPLIT: the k slices of a tile are spread over `ks` workgroups (grid.x =
+// tiles * ks, workgroup p taking slices p * nwaves .. p * nwaves + nwaves - 1,
+// one segment each).  Each wave stores its slice's class sum to
+// partials[slice][column][row]; the workgroup that arrives last at the
+// tile's counter (a device-scope atomic behind a release fence) adds the
+// slices in index order, writes y and puts the counter back to zero.  No
+// workgroup waits for another.  The sum is the one the single-workgroup
+// kernel forms for the same slices (slice sums added in index order).
+template <int MC, int CPW, int SRC, int AG = 128, bool SPLIT = false>
+__global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_m_tiles_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const void* __restrict__ x, int64_t x_stride,
     const uint8_t* __restrict__ tiles, float* __restrict__ y, int n, int k, int groups, int s8, int nseg,
-    int per_wave, int mtotal) {
+    int per_wave, int mtotal, float* __restrict__ partials, uint32_t* __restrict__ counters, int ks) {
 #pragma clang fp contract(off)
     constexpr bool FUSED = src_fused(SRC);
     constexpr int XL = src_xloads(SRC);
@@ -198,15 +216,16 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
     constexpr int R = MC < 4 ? MC : 4;      // outputs per lane and class (D rows 4*kb + r)
     constexpr int KBU = MC > 4 ? 2 : 1;     // lane groups kb holding outputs
     constexpr bool XS_VEC = !src_fused(SRC) && (AG < 128 || MC > 4);  // xs through LDS from vector loads
+    static_assert(!SPLIT || (CPW == 8 && !src_fused(SRC) && AG == 128), "split k: natural q, one wave per slice");
     const int nwaves = blockDim.x >> 6;
-    const int nslices = nwaves / WPS;
+    const int nslices = SPLIT ? (nseg + per_wave - 1) / per_wave : nwaves / WPS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slice = wave / WPS;
-    const int c_lo = (wave - slice * WPS) * CPW;  // first group class of this wave
+    const int tile = SPLIT ? (int)blockIdx.x / ks : (int)blockIdx.x;
+    const int slice = SPLIT ? ((int)blockIdx.x - tile * ks) * nwaves + wave : wave / WPS;
+    const int c_lo = (wave % WPS) * CPW;  // first group class of this wave
     const int lane = threadIdx.x & 63;
     const int j = lane & 15;   // B column (row of the tile) and A row (activation column)
     const int kb = lane >> 4;  // k block of the 64-wide MFMA step
-    const int tile = blockIdx.x;
     const int m0 = blockIdx.y * MC;
     const int mcount = min(MC, mtotal - m0);
     const int seg_begin = slice * per_wave;
@@ -249,7 +268,7 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
             }
         }
         const uint32_t unit_off = (uint32_t)(s * kSegUnit);
-        wsv = buf_load16(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
+        wsv = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
         keep_order();
 #pragma unroll
         for (int b = 0; b < CPW / 2; ++b)
@@ -316,8 +335,10 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
 
     // Every wave has at least one segment (slice * per_wave < nseg), so the
     // loop has no zero-trip test and the kernel arguments load in one go.
+    // (With SPLIT the last workgroup of a tile may hold waves past the last
+    // slice; they skip the loop and store nothing.)
     int s = seg_begin;
-    do {
+    if (!SPLIT || seg_begin < seg_end) do {
         issue(s);
 
         // 2. Stage the activations, xs and each group's -sum(q) (dot4 against
@@ -468,6 +489,58 @@ __global__ __launch_bounds__(CPW == 8 ? 512 : 1024) void small_m_tiles_kernel(
             part[r] = ((acc[0][r] + acc[4][r]) + (acc[1][r] + acc[5][r])) +
                       ((acc[2][r] + acc[6][r]) + (acc[3][r] + acc[7][r]));
         const int row = tile * kTileRows + j;
+        if constexpr (SPLIT) {
+            const size_t plane = (size_t)mtotal * n;  // one slice's [column][row] sums
+            // Partial sums, tickets and their reads are device-scope atomics
+            // (relaxed: write-through stores and loads that bypass the
+            // per-XCD caches), so no cache write-back or invalidation is
+            // needed.  Order: every wave waits for its stores to complete
+            // before the barrier, thread 0 takes the ticket after it, and the
+            // last workgroup reads the sums after its ticket returns.
+            if (seg_begin < seg_end && kb < KBU && row < n) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (col4 + r < mcount)
+                        __hip_atomic_store(partials + (size_t)slice * plane + (size_t)(m0 + col4 + r) * n + row, part[r],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            wait_stores_complete();
+            __syncthreads();
+            int* last = reinterpret_cast<int*>(red);
+            if (threadIdx.x == 0) {
+                const int ntiles = (int)gridDim.x / ks;
+                uint32_t* ctr = counters + (size_t)blockIdx.y * ntiles + tile;
+                const uint32_t before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int is_last = before == (uint32_t)(ks - 1);
+                if (is_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *last = is_last;
+            }
+            __syncthreads();
+            if (*last == 0) return;
+            // The slices in index order (loads in batches of eight, slots past
+            // the last slice re-read it and are not added).
+#pragma unroll
+            for (int o0 = 0; o0 < MC * kTileRows; o0 += 64) {
+                const int o = o0 + lane;
+                const int col = o >> 4;
+                if (wave == 0 && o < MC * kTileRows && col < mcount && row < n) {
+                    const float* p = partials + (size_t)(m0 + col) * n + row;
+                    float sum = 0.0f;
+                    for (int b = 0; b < nslices; b += 8) {
+                        float v[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            v[i] = __hip_atomic_load(p + (size_t)min(b + i, nslices - 1) * plane, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (b + i < nslices) sum = b + i == 0 ? v[i] : sum + v[i];
+                    }
+                    y[(size_t)(m0 + col) * n + row] = sum;
+                }
+            }
+            return;
+        }
         if (nwaves == 1) {
             if (kb < KBU && row < n) {
 #pragma unroll
@@ -551,7 +624,22 @@ hipError_t launch_tiles_one(const TilesArgs& a, int slices, int nseg, int per_wa
     const dim3 grid((unsigned)t.tiles, (unsigned)chunks);
     clear_stale_error();
     hipLaunchKernelGGL((small_m_tiles_kernel<MC, CPW, SRC, AG>), grid, dim3(64 * waves), lds, a.stream, a.q, a.xs, a.x,
-                       a.x_stride, a.tiles, a.y, (int)n, (int)k, (int)(k / 128), (int)t.s8, nseg, per_wave, (int)m);
+                       a.x_stride, a.tiles, a.y, (int)n, (int)k, (int)(k / 128), (int)t.s8, nseg, per_wave, (int)m,
+                       nullptr, nullptr, 1);
+    return hipGetLastError();
+}
+
+// Split k: `ks` workgroups of `waves` waves per tile, one segment per wave.
+template <int MC>
+hipError_t launch_tiles_splitk_one(const TilesArgs& a, float* partials, uint32_t* counters, int ks, int waves,
+                                   int nseg, int chunks) {
+    const TileGeometry t = geometry(a.n, a.k);
+    const size_t lds = (size_t)waves * tiles_region_bytes(MC, 8) + (size_t)waves * MC * kTileRows * 4;
+    const dim3 grid((unsigned)(t.tiles * ks), (unsigned)chunks);
+    clear_stale_error();
+    hipLaunchKernelGGL((small_m_tiles_kernel<MC, 8, kSrcNatural, 128, true>), grid, dim3(64 * waves), lds, a.stream,
+                       a.q, a.xs, nullptr, (int64_t)0, a.tiles, a.y, (int)a.n, (int)a.k, (int)(a.k / 128), (int)t.s8,
+                       nseg, 1, (int)a.m, partials, counters, ks);
     return hipGetLastError();
 }
 
@@ -647,6 +735,43 @@ static hipError_t launch_tiles_any(int src, const TilesArgs& a, int max_waves, i
         case kSrcBf16: return launch_tiles_split<kSrcBf16>(split, mc, a, slices, nseg, per_wave, chunks);
         case kSrcF16: return launch_tiles_split<kSrcF16>(split, mc, a, slices, nseg, per_wave, chunks);
         case kSrcF32: return launch_tiles_split<kSrcF32>(split, mc, a, slices, nseg, per_wave, chunks);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Split-k geometry: one segment per wave, `waves` (1..16) waves per
+// workgroup, ks = ceil(nseg / waves) workgroups per tile, then the waves
+// evened out over the ks workgroups.  Column passes: one of m at m <= 4,
+// else passes of eight (the last one partial).
+SplitKPlan splitk_plan(int64_t m, int64_t n, int64_t k, int waves) {
+    SplitKPlan p;
+    const TileGeometry t = geometry(n, k);
+    p.nseg = (int)t.s8;
+    p.ks = (p.nseg + waves - 1) / waves;
+    p.waves = (p.nseg + p.ks - 1) / p.ks;
+    p.mc = m <= 4 ? (int)m : kTilesMaxColumns;
+    p.chunks = (int)((m + p.mc - 1) / p.mc);
+    p.tiles = t.tiles;
+    p.partial_floats = (int64_t)p.nseg * m * n;
+    p.counters = (int64_t)kSplitKMaxChunks * t.tiles;
+    return p;
+}
+
+// The library's choice: split k when a single workgroup per tile would give
+// each wave several segments (k > 8192 at eight waves per tile).
+bool splitk_default(int64_t k) { return (k / 128 + 7) / 8 > 8; }
+
+hipError_t launch_small_m_tiles_splitk(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
+                                       int64_t k, float* y, float* partials, uint32_t* counters, int waves,
+                                       hipStream_t stream) {
+    const SplitKPlan p = splitk_plan(m, n, k, waves);
+    const TilesArgs a{q, xs, nullptr, 0, tiles, m, n, k, y, stream};
+    switch (p.mc) {
+        case 1: return launch_tiles_splitk_one<1>(a, partials, counters, p.ks, p.waves, p.nseg, p.chunks);
+        case 2: return launch_tiles_splitk_one<2>(a, partials, counters, p.ks, p.waves, p.nseg, p.chunks);
+        case 3: return launch_tiles_splitk_one<3>(a, partials, counters, p.ks, p.waves, p.nseg, p.chunks);
+        case 4: return launch_tiles_splitk_one<4>(a, partials, counters, p.ks, p.waves, p.nseg, p.chunks);
+        case 8: return launch_tiles_splitk_one<8>(a, partials, counters, p.ks, p.waves, p.nseg, p.chunks);
         default: return hipErrorInvalidValue;
     }
 }

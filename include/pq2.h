@@ -125,14 +125,6 @@ int pq2_matmul_small_m(const int8_t* q, const float* xs, const void* planes, int
 int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                        int64_t k, float* y, void* stream);
 
-/* Tuning hook for the prefill matmul (benchmarks and tests only; same
- * arguments and result as pq2_matmul_prefill): tile 1 = 128x128, 2 = 64x128,
- * 3 = 64x64, 4 = 128x64 outputs per workgroup, 0 = the library's choice.
- * The result does not depend on the tile.  Errors as pq2_matmul_prefill,
- * plus EINVAL for an unknown tile. */
-int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
-                             int64_t k, float* y, int tile, void* stream);
-
 /* Prefill matmul from plane-order activations (the qp output of
  * pq2_quantize_act_i8_planes; its qsum is not needed): the same result as
  * pq2_matmul_prefill on the natural-order q, bit for bit, without the byte
@@ -142,11 +134,6 @@ int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* plane
  * Errors: EINVAL, ESHAPE, EALIGN, ELAUNCH, EDEVICE. */
 int pq2_matmul_prefill_planes(const int8_t* qp, const float* xs, const void* planes, int64_t m, int64_t n,
                               int64_t k, float* y, void* stream);
-
-/* Tuning hook for pq2_matmul_prefill_planes (tile as for
- * pq2_matmul_prefill_tuned). */
-int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const void* planes, int64_t m, int64_t n,
-                                    int64_t k, float* y, int tile, void* stream);
 
 /* pq2_matmul_small_m straight from the raw block layout, with no
  * preparation pass (page "Kernel experiments", section A, Tests 4 and 24:
@@ -163,49 +150,6 @@ int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const voi
  *         EALIGN, ELAUNCH, EDEVICE. */
 int pq2_matmul_small_m_raw(const int8_t* q, const float* xs, const void* raw, int64_t raw_row_stride_bytes, int64_t m,
                            int64_t n, int64_t k, float* y, void* stream);
-
-/* Read-only probe of a prepared weight layout (page "Kernel experiments",
- * section H, Test 24: copy-free read patterns of the layouts, the ceiling
- * the matmuls are measured against).  It issues exactly the weight loads of
- * the decode engine that reads the layout (planes: the packed-dot engine;
- * tiles: the tile-layout engine): same grid, waves, k split, load widths and
- * cache policy, one segment at a time, and no arithmetic but an XOR fold of
- * what each wave read.  Every byte is read once, so the XOR of the output
- * words equals the XOR of the layout's dwords (for the planes: the code
- * plane's dwords and the fp16 scales, each zero-extended).
- *   weights  device planes (layout PQ2_LAYOUT_PLANES) or tile layout
- *            (PQ2_LAYOUT_TILES) of an n x k matrix, 16-byte aligned.
- *   out      device uint32 [pq2_read_probe_words(layout, n, k)], 4-byte
- *            aligned, fully overwritten; must not overlap the weights.
- * Errors: EINVAL (null, layout, overlap), ESHAPE (n < 1, k < 128, k % 128,
- *         k > PQ2_MAX_K), EALIGN, ELAUNCH, EDEVICE. */
-int pq2_read_probe(const void* weights, int layout, int64_t n, int64_t k, uint32_t* out, void* stream);
-
-/* Number of uint32 words pq2_read_probe writes for this layout and shape
- * (one per wave of its grid); 0 for an invalid layout or shape.  Host only. */
-int64_t pq2_read_probe_words(int layout, int64_t n, int64_t k);
-
-/* Tuning hook for the small-m matmul (benchmarks and tests only; same
- * arguments and result as pq2_matmul_small_m).  engine selects one of four
- * kernels that compute the same bits:
- *   1 = packed dot products (v_dot4), `rows` = weight rows per lane (1, 2);
- *   2 = INT8 matrix cores (v_mfma), one 8-row block per workgroup, `rows` = 1;
- *   3 = INT8 matrix cores, one 8-wave workgroup per CU that stages the
- *       activations of its k range once in LDS for `rows` 8-row blocks;
- *       its waves take the (row block, k slice) units in turn;
- *   4 = the kernel of engine 3 with one unit per wave: `rows` 8-row blocks
- *       per workgroup, one wave per (row block, k slice).
- *   Engines 3 and 4 cover at most 4 columns per pass over the weights and
- *   accept only the `rows` whose staging fits LDS and the wave limits.
- * max_waves in 1..8 is the number of waves that split k inside one
- * workgroup.  0 for any setting picks the library's default (with an
- * explicit engine, that engine's default rows).  The summation order of an
- * output depends on max_waves only (through the number of waves k is split
- * over): neither rows nor the engine changes the bits.  Errors as
- * pq2_matmul_small_m, plus EINVAL for an unsupported setting. */
-int pq2_matmul_small_m_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m,
-                             int64_t n, int64_t k, float* y, int rows, int max_waves,
-                             int engine, void* stream);
 
 /* Plane-order variant of pq2_quantize_act_i8 for the decode path (page
  * "Kernel experiments: recorded evidence", Test 21 and Diagram 7: activations
@@ -243,14 +187,6 @@ int pq2_quantize_act_i8_planes(const void* x, int dtype, int64_t x_row_stride_el
 int pq2_matmul_small_m_planes(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
                               int64_t m, int64_t n, int64_t k, float* y, void* stream);
 
-/* Tuning hook for pq2_matmul_small_m_planes (benchmarks and tests only; same
- * arguments and result): settings as for pq2_matmul_small_m_tuned, and the
- * same bits as pq2_matmul_small_m_tuned with the same settings.  Errors as
- * pq2_matmul_small_m_planes, plus EINVAL for an unsupported setting. */
-int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int32_t* qsum, const void* planes,
-                                    int64_t m, int64_t n, int64_t k, float* y, int rows,
-                                    int max_waves, int engine, void* stream);
-
 /* Quantise + small-m matmul in one launch: y = the definition above for the
  * activations pq2_quantize_act_i8 would produce from x, bit for bit the y of
  * pq2_quantize_act_i8 followed by pq2_matmul_small_m (same codes, scales and
@@ -269,15 +205,6 @@ int pq2_matmul_small_m_planes_tuned(const int8_t* qp, const float* xs, const int
  *         EALIGN, ELAUNCH, EDEVICE. */
 int pq2_matmul_small_m_fused(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes,
                              int64_t m, int64_t n, int64_t k, float* y, void* stream);
-
-/* Tuning hook for pq2_matmul_small_m_fused (benchmarks and tests only):
- * settings as for pq2_matmul_small_m_tuned, and the same bits as
- * pq2_quantize_act_i8 + pq2_matmul_small_m_tuned with the same settings.
- * Errors as pq2_matmul_small_m_fused, plus EINVAL for an unsupported
- * setting. */
-int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* planes,
-                                   int64_t m, int64_t n, int64_t k, float* y, int rows, int max_waves,
-                                   int engine, void* stream);
 
 /* ---- Tile-major weights for the decode GEMV (page "Kernel experiments:
  * recorded evidence", section H, Tests 24 and 25: storing the bytes one
@@ -324,17 +251,6 @@ int pq2_prepare_tiles(const void* raw, int64_t raw_row_stride_bytes, int64_t n, 
 int pq2_matmul_small_m_tiles(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
                              int64_t k, float* y, void* stream);
 
-/* Tuning hook for pq2_matmul_small_m_tiles (benchmarks and tests only):
- * max_waves in 1..8 fixes the k split as for pq2_matmul_small_m_tuned;
- * split in {1, 2, 4} is the number of waves that share one k slice (each
- * takes 8/split of its group classes), with at most 16 waves per workgroup.
- * 0 for either picks the library's default.  The bits equal
- * pq2_matmul_small_m_tuned's at the same max_waves, whatever the split.
- * Errors as pq2_matmul_small_m_tiles, plus EINVAL for an unsupported
- * setting. */
-int pq2_matmul_small_m_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
-                                   int64_t k, float* y, int max_waves, int split, void* stream);
-
 /* Quantise + tile-layout matmul in one launch: bit for bit the y of
  * pq2_quantize_act_i8 followed by pq2_matmul_small_m_tiles (same codes,
  * scales and summation order).  Every wave quantises the activation groups
@@ -354,15 +270,6 @@ int pq2_matmul_small_m_tiles_tuned(const int8_t* q, const float* xs, const void*
 int pq2_matmul_small_m_tiles_fused(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
                                    int64_t m, int64_t n, int64_t k, float* y, void* stream);
 
-/* Tuning hook for pq2_matmul_small_m_tiles_fused (benchmarks and tests
- * only): max_waves and split as for pq2_matmul_small_m_tiles_tuned, with
- * the same bits as pq2_quantize_act_i8 + pq2_matmul_small_m_tiles_tuned at
- * the same settings.  Errors as pq2_matmul_small_m_tiles_fused, plus EINVAL
- * for an unsupported setting. */
-int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
-                                         int64_t m, int64_t n, int64_t k, float* y, int max_waves, int split,
-                                         void* stream);
-
 /* Decode GEMV from activations, y = W x for 1 <= m <= 16 (page "Kernel
  * experiments", Tests 3-5: the integer GEMV is called with the activations
  * and the weights and returns the outputs, quantising inside): the
@@ -379,6 +286,42 @@ int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row
  * Errors: those of the path taken, checked before anything is enqueued. */
 int pq2_gemv_tiles(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m, int64_t n,
                    int64_t k, float* y, int8_t* q_work, float* xs_work, void* stream);
+
+/* ---- Split k over workgroups (page "Kernel experiments: recorded
+ * evidence", Test 30: split-K with a fixed-order combine in the last block,
+ * which resets its counter; page "KERNEL_REPORT: PTQ1_0 small-batch
+ * decoding", "Facts": a column's result must not depend on how many columns
+ * share the call).
+ *
+ * The same definition as pq2_matmul_small_m_tiles with k cut into slices of
+ * one 1024-element segment (8 groups); the slices of a 16-row tile run in
+ * several workgroups, each slice's sum of its group terms goes to
+ * `partials`, and the workgroup that arrives last at the tile's counter adds
+ * the slices in index order, writes y and sets the counter back to zero.
+ * No workgroup waits for another.  The summation order depends on k only
+ * (not on m: batch-invariant); for k <= 8192 it is the order of
+ * pq2_matmul_small_m_tiles, so the bits are the same.  On MI355X it is
+ * slower than the single-workgroup kernel at every measured shape (the
+ * device-scope store, ticket and reload add about 1.8 us per call), so no
+ * default path takes it.
+ *   q, xs, tiles, y, limits: as pq2_matmul_small_m_tiles.
+ *   partials  device float [pq2_tiles_splitk_partial_floats(m, n, k)], 4-byte
+ *             aligned, scratch (contents on entry do not matter).
+ *   counters  device uint32 [pq2_tiles_splitk_counter_words(n)], 4-byte
+ *             aligned: ALL ZERO before the first call; every call leaves
+ *             them zero.  Calls that share partials or counters must not
+ *             run at the same time.
+ * Errors: EINVAL (null, overlap), ESHAPE, EALIGN, ELAUNCH, EDEVICE. */
+int pq2_matmul_small_m_tiles_splitk(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
+                                    int64_t k, float* y, float* partials, uint32_t* counters, void* stream);
+
+/* Floats of partial sums pq2_matmul_small_m_tiles_splitk needs:
+ * ceil(k/1024) * m * n; -1 for an invalid shape.  Host only. */
+int64_t pq2_tiles_splitk_partial_floats(int64_t m, int64_t n, int64_t k);
+
+/* Counter words pq2_matmul_small_m_tiles_splitk needs: 4 * ceil(n/16); -1 for
+ * an invalid n.  Host only. */
+int64_t pq2_tiles_splitk_counter_words(int64_t n);
 
 /* Smaller activation groups (page "Kernel experiments", section C,
  * Diagram 3, Tests 8 and 9): the weights keep their 128-weight blocks and
@@ -420,12 +363,6 @@ int pq2_matmul_small_m_tiles_g(const int8_t* q, const float* xs, const void* til
  *         k<128, k%128, k > PQ2_MAX_K), EALIGN, ELAUNCH, EDEVICE. */
 int pq2_matmul_prefill_tiles(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
                              int64_t k, float* y, void* stream);
-
-/* Tuning hook for pq2_matmul_prefill_tiles: tile as for
- * pq2_matmul_prefill_tuned (0 = the library's choice), same bits.  Errors as
- * pq2_matmul_prefill_tiles, plus EINVAL for tile outside 0..4. */
-int pq2_matmul_prefill_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
-                                   int64_t k, float* y, int tile, void* stream);
 
 /* Tile-layout prefill matmul with activation groups of agroup elements
  * (page "Kernel experiments", section C, Tests 8 and 9, which timed them at

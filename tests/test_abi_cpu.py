@@ -1,7 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every symbol that
-include/pq2.h declares, and rejects bad arguments on the host before any HIP
-call (every case below fails validation or, without a GPU, the device check,
-so nothing is ever launched)."""
+include/*.h declares (pq2.h, pq2_measure.h, pq2_tuning.h), and rejects bad
+arguments on the host before any HIP call (every case below fails validation
+or, without a GPU, the device check, so nothing is ever launched)."""
 import ctypes
 import os
 import re
@@ -9,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pq2.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pq2.h", "pq2_measure.h", "pq2_tuning.h")]
 
 import gemm_int8_act_amd as pq2  # noqa: E402
 
@@ -29,13 +29,16 @@ def _gpu_visible():
 
 
 def _declared_symbols():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(pq2_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        names |= set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(pq2_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 31
+    assert len(names) == 38
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -354,3 +357,54 @@ def test_read_probe_validation_and_grid():
     assert r(A, 0, 8, 128, A + 16, None) == EINVAL           # out overlaps the weights
     if not _gpu_visible():
         assert r(A, 1, 10240, 5120, D, None) == EDEVICE
+
+
+def test_splitk_validation_and_sizes():
+    pf, cw = pq2.pq2_tiles_splitk_partial_floats, pq2.pq2_tiles_splitk_counter_words
+    assert pf(1, 5120, 17408) == 17 * 5120          # one slice per 1024-element segment
+    assert pf(4, 10240, 5120) == 5 * 4 * 10240
+    assert pf(3, 33, 640) == 1 * 3 * 33               # one partial segment
+    assert cw(5120) == 4 * 320 and cw(33) == 4 * 3
+    assert pq2.lib.pq2_tiles_splitk_partial_floats(0, 8, 128) == -1
+    assert pq2.lib.pq2_tiles_splitk_partial_floats(17, 8, 128) == -1
+    assert pq2.lib.pq2_tiles_splitk_counter_words(0) == -1
+    f = pq2.lib.pq2_matmul_small_m_tiles_splitk
+    # q, xs, tiles, m, n, k, y, partials, counters, stream
+    assert f(A, B, C, 1, 8, 128, D, None, E, None) == EINVAL            # no partials
+    assert f(A, B, C, 1, 8, 128, D, E, None, None) == EINVAL            # no counters
+    assert f(A, B, C, 17, 8, 128, D, E, E + 4096, None) == ESHAPE       # columns
+    assert f(A, B, C, 1, 8, 96, D, E, E + 4096, None) == ESHAPE         # k % 128
+    assert f(A, B, C, 1, 8, 128, D, E + 2, E + 4096, None) == EALIGN    # partials not 4-byte aligned
+    assert f(A, B, C, 1, 8, 128, D, E, E + 4098, None) == EALIGN        # counters not 4-byte aligned
+    assert f(A, B, C, 1, 8, 128, D, E, E + 16, None) == EINVAL          # counters overlap partials
+    assert f(A, B, C, 1, 8, 128, D, D + 16, E, None) == EINVAL          # partials overlap y
+    assert f(A, B, C, 1, 8, 128, D, C + 64, E, None) == EINVAL          # partials overlap the tiles
+    t = pq2.lib.pq2_matmul_small_m_tiles_splitk_tuned
+    assert t(A, B, C, 1, 8, 128, D, E, E + 4096, 17, None) == EINVAL    # more than 16 waves
+    assert t(A, B, C, 1, 8, 128, D, E, E + 4096, -1, None) == EINVAL
+    if not _gpu_visible():
+        assert f(A, B, C, 4, 5120, 17408, D, E, E + (1 << 24), None) == EDEVICE
+        assert t(A, B, C, 4, 5120, 17408, D, E, E + (1 << 24), 3, None) == EDEVICE
+
+
+def test_stream_and_empty_probe_validation():
+    w = pq2.pq2_stream_probe_words
+    assert w(2048) == 8192 and w(1) == 4 and w(0) == 0 and w(65537) == 0
+    s = pq2.lib.pq2_stream_probe
+    # buf, bytes, workgroups, store_all, sentinel, out, stream
+    assert s(None, 1024, 8, 1, 0, D, None) == EINVAL
+    assert s(A, 1024, 8, 1, 0, None, None) == EINVAL
+    assert s(A, 1000, 8, 1, 0, D, None) == ESHAPE            # not a multiple of 16
+    assert s(A, 0, 8, 1, 0, D, None) == ESHAPE
+    assert s(A, 1 << 31, 8, 1, 0, D, None) == ESHAPE          # 32-bit offsets
+    assert s(A, 1024, 0, 1, 0, D, None) == ESHAPE
+    assert s(A, 1024, 65537, 1, 0, D, None) == ESHAPE
+    assert s(A + 8, 1024, 8, 1, 0, D, None) == EALIGN
+    assert s(A, 1024, 8, 1, 0, D + 2, None) == EALIGN
+    assert s(A, 1024, 8, 1, 0, A + 512, None) == EINVAL       # out overlaps buf
+    e = pq2.lib.pq2_empty_probe
+    assert e(0, 1, None) == ESHAPE and e(1, 0, None) == ESHAPE and e(1, 17, None) == ESHAPE
+    assert e((1 << 20) + 1, 1, None) == ESHAPE
+    if not _gpu_visible():
+        assert s(A, 1024, 8, 1, 0, D, None) == EDEVICE
+        assert e(256, 4, None) == EDEVICE

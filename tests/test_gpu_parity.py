@@ -876,8 +876,9 @@ def test_tiles_fused_workloads(name):
 
 @pytest.mark.parametrize("name", ["qkv", "up", "down"])
 def test_gemv_tiles_same_bits(name):
-    """pq2_gemv_tiles (fused at one column and k <= 8192, two launches
-    otherwise) gives the bits of quantise + tile matmul at every M."""
+    """pq2_gemv_tiles (fused at one or two columns and k <= 8192, two
+    launches otherwise or when the rows are not 16-byte aligned) gives the
+    bits of quantise + tile matmul at every M."""
     pq2 = _pq2()
     w, raw, x = workload_case(name)
     tiles = gpu_tiles(raw, w.n, w.k)
@@ -892,11 +893,21 @@ def test_gemv_tiles_same_bits(name):
         pq2.pq2_gemv_tiles(xd, tiles, y, qw, xw)
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32)), f"{name} m={m}"
-        if m == 1 and w.k <= 8192:  # the fused path needs no scratch
+        if m <= 2 and w.k <= 8192:  # the fused path needs no scratch
             y.fill_(float("nan"))
             pq2.pq2_gemv_tiles(xd, tiles, y)
             torch.cuda.synchronize()
-            assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32)), f"{name} m=1 no scratch"
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32)), f"{name} m={m} no scratch"
+        if m == 2 and w.k <= 8192:
+            # Rows 8 bf16 elements + 2 apart: the fused kernel cannot read them
+            # (16-byte rows), so the call takes the two-launch path.
+            xp = torch.zeros((m, w.k + 10), dtype=x.dtype, device=DEV)
+            xp[:, 2:2 + w.k] = xd
+            xv = xp[:, 2:2 + w.k]
+            y.fill_(float("nan"))
+            pq2.pq2_gemv_tiles(xv, tiles, y, qw, xw)
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32)), f"{name} m=2 unaligned rows"
 
 
 # ------------------------------------------------------------------ smaller activation groups
