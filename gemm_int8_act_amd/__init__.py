@@ -63,6 +63,7 @@ EXPORTED = (
     "pq2_stream_probe",
     "pq2_stream_probe_words",
     "pq2_empty_probe",
+    "pq2_gemv_tiles_static",
 )
 
 
@@ -168,6 +169,8 @@ def _load_library():
     lib.pq2_stream_probe_words.restype = i64
     lib.pq2_empty_probe.argtypes = [i64, i32, p]
     lib.pq2_empty_probe.restype = i32
+    lib.pq2_gemv_tiles_static.argtypes = [p, i32, i64, p, i64, i64, i64, p, p]
+    lib.pq2_gemv_tiles_static.restype = i32
     return lib
 
 
@@ -410,6 +413,22 @@ def pq2_stream_probe(buf, nbytes: int, workgroups: int, out, store_all: bool = F
 def pq2_empty_probe(workgroups: int = 1, waves: int = 1, stream=None) -> None:
     """An empty kernel (the launch floor of back-to-back launches)."""
     _check(lib.pq2_empty_probe(workgroups, waves, _stream(stream)), "pq2_empty_probe")
+
+
+def pq2_gemv_tiles_static(x, tiles, y, k=None, stream=None) -> None:
+    """pq2_gemv_tiles with the library's own static scratch (no allocation);
+    k defaults to x.shape[1]."""
+    import torch
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if tiles.dtype != torch.uint8 or y.dtype != torch.float32 or not tiles.is_contiguous() or not y.is_contiguous():
+        raise ValueError("tiles contiguous uint8 and y contiguous float32 expected")
+    m, n = y.shape
+    k = x.shape[1] if k is None else k
+    if x.shape[0] != m or x.shape[1] < k or tiles.numel() < pq2_tiles_bytes(n, k):
+        raise ValueError("shape mismatch between x, tiles and y")
+    _check(lib.pq2_gemv_tiles_static(_dev_ptr(x, "x"), _dtype_code(x), x.stride(0), _dev_ptr(tiles, "tiles"), m, n,
+                                     k, _dev_ptr(y, "y"), _stream(stream)), "pq2_gemv_tiles_static")
 
 
 def pq2_quantize_act_i8_g(x, q, xs, agroup: int, stream=None) -> None:

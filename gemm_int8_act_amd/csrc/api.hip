@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr int64_t kGroup = 128;
@@ -86,6 +88,40 @@ int small_m_config(int src, int64_t m, int64_t n, int64_t k, int rows, int max_w
         case 4: return pq2::wg_supported(src, m, k, cfg->max_waves, cfg->rows, true) ? PQ2_OK : PQ2_EINVAL;
         default: return PQ2_EINVAL;
     }
+}
+
+// Scratch of pq2_gemv_tiles_static: the quantised activations q
+// [PQ2_MAX_SMALL_M][PQ2_MAX_K] int8, then their scales xs
+// [PQ2_MAX_SMALL_M][PQ2_MAX_K / 128] float, the largest shape any small-m
+// entry point accepts (1 MiB + 32 KiB per GPU, held until the process ends).
+constexpr size_t kStaticQBytes = (size_t)PQ2_MAX_SMALL_M * PQ2_MAX_K;
+constexpr size_t kStaticXsBytes = (size_t)PQ2_MAX_SMALL_M * (PQ2_MAX_K / 128) * 4;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticQBytes + kStaticXsBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each GPU holds its own copy of the array).  In host code the
+// array's name is not a device address; only this pointer is passed on.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PQ2_EDEVICE;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return launch_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return PQ2_OK;
 }
 
 }  // namespace
@@ -298,6 +334,19 @@ int pq2_empty_probe(int64_t workgroups, int waves, void* stream) {
     if (workgroups < 1 || workgroups > ((int64_t)1 << 20) || waves < 1 || waves > 16) return PQ2_ESHAPE;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_empty_probe(workgroups, waves, (hipStream_t)stream));
+}
+
+int pq2_gemv_tiles_static(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m,
+                          int64_t n, int64_t k, float* y, void* stream) {
+    if (m < 1 || m > PQ2_MAX_SMALL_M || n < 1 || n > kMaxN) return PQ2_ESHAPE;
+    if (int rc = check_k(k)) return rc;
+    if ((size_t)m * k > kStaticQBytes || (size_t)m * (k / kGroup) * 4 > kStaticXsBytes) return PQ2_ESHAPE;
+    if (int rc = check_device()) return rc;
+    void* base = nullptr;
+    if (int rc = scratch_address(&base)) return rc;
+    int8_t* q_work = static_cast<int8_t*>(base);
+    float* xs_work = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + kStaticQBytes);
+    return pq2_gemv_tiles(x, dtype, x_row_stride_elems, tiles, m, n, k, y, q_work, xs_work, stream);
 }
 
 int pq2_quantize_act_i8_g(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,

@@ -287,6 +287,21 @@ int pq2_matmul_small_m_tiles_fused(const void* x, int dtype, int64_t x_row_strid
 int pq2_gemv_tiles(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m, int64_t n,
                    int64_t k, float* y, int8_t* q_work, float* xs_work, void* stream);
 
+/* pq2_gemv_tiles for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without q_work / xs_work, the same bits, and no allocation of
+ * any kind.  Its scratch (quantised activations and their scales) is one
+ * library-owned device array of 1 MiB + 32 KiB per GPU, sized for
+ * m <= PQ2_MAX_SMALL_M and k <= PQ2_MAX_K and held until the process ends;
+ * its address is looked up on the first call on each device (make that
+ * first call outside graph capture).  Every call on a GPU shares that GPU's
+ * array, so calls that overlap on one GPU (other streams, other threads)
+ * race and must be ordered by the caller.
+ * Errors: those of pq2_gemv_tiles; ESHAPE for a shape beyond the scratch
+ * (m > 16 or k > 65536). */
+int pq2_gemv_tiles_static(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m,
+                          int64_t n, int64_t k, float* y, void* stream);
+
 /* ---- Split k over workgroups (page "Kernel experiments: recorded
  * evidence", Test 30: split-K with a fixed-order combine in the last block,
  * which resets its counter; page "KERNEL_REPORT: PTQ1_0 small-batch

@@ -38,7 +38,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 38
+    assert len(names) == 39
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -408,3 +408,15 @@ def test_stream_and_empty_probe_validation():
     if not _gpu_visible():
         assert s(A, 1024, 8, 1, 0, D, None) == EDEVICE
         assert e(256, 4, None) == EDEVICE
+
+
+def test_gemv_static_validation():
+    f = pq2.lib.pq2_gemv_tiles_static
+    # x, dtype, stride, tiles, m, n, k, y, stream
+    assert f(A, 0, 128, C, 0, 8, 128, D, None) == ESHAPE
+    assert f(A, 0, 128, C, 17, 8, 128, D, None) == ESHAPE      # beyond the static scratch (16 columns)
+    assert f(A, 0, 1 << 17, C, 1, 8, 1 << 17, D, None) == ESHAPE  # k beyond 65536
+    assert f(A, 0, 96, C, 1, 8, 96, D, None) == ESHAPE
+    assert f(A, 0, 128, C, 1, 0, 128, D, None) == ESHAPE
+    if not _gpu_visible():
+        assert f(A, 0, 5120, C, 4, 8, 5120, D, None) == EDEVICE
