@@ -1,35 +1,46 @@
 #!/usr/bin/env python3
 """Decode-matmul benchmark on one MI355X: packed-ternary (PQ2) weights x
-group-128 INT8 activations, the attention-QKV projection shape (K=5120,
-N=10240) at M = 1, 2, 3, 4 activation columns.
+group-128 INT8 activations at M = 1..4 activation columns.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
-                    [--calibrate]
+                    [--variants] [--calibrate] [--configs up,qkv,down]
 
-A step is one pass of the per-call hot path over one batch: for each M in
-1..4, quantise the bf16 activations to INT8 (pq2_quantize_act_i8) and run the
-small-m matmul on the tile-layout weights (pq2_matmul_small_m_tiles, the
-fastest path over M = 1..4).  The same calls on the row-major prepared planes
-(pq2_matmul_small_m), their plane-order variant and both one-launch fused
-entry points are timed per M and reported beside it; every path gives the
-same output bits, which the run checks.  Weight preparation
-(pq2_prepare_tiles / pq2_prepare_planes) is one-time and outside the timing.
-Every step reads the next of R weight copies (>= 1 GiB in total per layout,
-four times the 256 MB Infinity Cache), so weights stream from HBM.  Steps
-are captured as HIP graphs (one graph of R consecutive steps, as a decode
-loop runs its calls inside one larger graph, and one of the remainder) and
-replayed; exactly K steps are timed with HIP events between a synchronize
-on each side.
+The headline workload is the FFN up projection (K=5120, N=17408), the
+largest single-GPU decode shape of the measurement plan.  A step is one
+complete call y = W x for each of M = 1, 2, 3, 4 (pq2_gemv_tiles: one fused
+quantise + tile matmul launch at M = 1, the quantiser and the tile matmul at
+M = 2, 3, 4 at this shape), every call on its own copy of the tile-layout
+weights: the
+copies (a multiple of 4, >= 1 GiB in total, four times the 256 MB Infinity
+Cache) are read in turn, so no call re-reads bytes another call of the last
+GiB has read, and every call streams its weights from HBM.  Steps are
+captured as HIP graphs (one graph reading every copy once, and one of the
+remainder) and replayed; exactly K steps are timed with HIP events between a
+synchronize on each side.  Weight preparation is one-time and untimed.
 
-value = algorithmic bytes of the timed steps / their time (GB/s), where a
-call's algorithmic bytes are what the method must move: packed weights
-(34 B / 128 weights) + bf16 activations + q + xs (quantiser) and
-weights + q + xs + y (matmul).  The per-M matmul kernel duration (HIP events
-around graph replays of back-to-back launches on the launch stream) gives the
-roofline entry.  The CPU oracle, timed on a bounded sample of the same work,
-gives cpu_baseline.  --calibrate adds a plain elementwise copy of 64 MiB
-(float32 negate, 64 MiB read + 64 MiB written, five times) so that
-rocprofv3 FETCH_SIZE / WRITE_SIZE counts can be scaled to bytes.
+value = algorithmic bytes of the timed calls / their time (GB/s), where a
+call's algorithmic bytes are what the method must move for the matmul:
+packed weights (34 B / 128 weights) + q + xs + y.  Beside the headline, the
+attention QKV (K=5120, N=10240) and FFN down (K=17408, N=5120) shapes are
+timed the same way per call, and for each shape and M the tile matmul alone
+(the roofline kernel), over the same rotating copies:
+
+  * roofline per config: algorithmic bytes per launch / mean launch time of
+    small_m_tiles_kernel (HIP events around graphs of back-to-back launches
+    on the launch stream), against 8 TB/s; traffic from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary when its kernel digest matches;
+  * ceilings: a linear stream read of the same bytes (pq2_stream_probe,
+    shaped like no engine), the same with one store per wave, the decode
+    engine's own weight loads (pq2_read_probe), the empty-kernel launch floor
+    (pq2_empty_probe), and a fit t = t0 + B / BW of the stream read over
+    4..192 MB.
+
+The CPU oracle, timed on a bounded sample of the same work on one thread and
+on every core of the affinity mask (rows split between threads, bitwise the
+same result), gives cpu_baseline.  --calibrate adds a plain copy kernel of
+64 MiB (the yardstick for FETCH_SIZE / WRITE_SIZE); --variants times the
+other decode paths (planes, plane order, fused, raw reader, activation
+groups) at the QKV shape.
 """
 from __future__ import annotations
 
@@ -49,6 +60,10 @@ PEAK_HBM_BYTES_PER_S = 8.0e12       # MI355X HBM3E, published peak
 PEAK_INT8_OPS_PER_S = 5.0e15        # MI355X dense INT8 MFMA, published peak
 ROTATION_BYTES = 1 << 30
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for M=1..4 packed-ternary matmul"
+HEADLINE = "up"
+DECODE_MS = (1, 2, 3, 4)
+STREAM_WORKGROUPS = 2048
+STREAM_FIT_MB = (4, 8, 16, 24, 48, 96, 192)
 
 
 def log(*a):
@@ -63,10 +78,6 @@ def matmul_bytes(m, n, k):
     return weight_bytes(n, k) + m * k + m * (k // 128) * 4 + m * n * 4
 
 
-def quantize_bytes(m, k):
-    return m * k * 2 + m * k + m * (k // 128) * 4
-
-
 def source_digest():
     """Digest of the sources of the tile-layout small-m kernel."""
     h = hashlib.sha256()
@@ -76,11 +87,10 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(digest):
-    """HBM bytes per launch of the tile-layout small-m kernel from the
-    committed rocprofv3 counter summary, if it was taken on the current
-    kernel source."""
-    path = os.path.join(ROOT, "profiles", "small_m_tiles_qkv_traffic.txt")
+def stored_summary(name, digest):
+    """Key/value lines of a committed profile summary (profiles/<name>), or
+    None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -89,12 +99,7 @@ def stored_traffic(digest):
             parts = line.split()
             if len(parts) == 2 and not line.startswith("#"):
                 vals[parts[0]] = parts[1]
-    if vals.get("kernel_source_digest") != digest:
-        return None
-    try:
-        return float(vals["hbm_bytes_per_launch_avg_m1to4"])
-    except (KeyError, ValueError):
-        return None
+    return vals if vals.get("kernel_source_digest") == digest else None
 
 
 class Graph:
@@ -112,47 +117,271 @@ class Graph:
         self.g.replay()
 
 
-def time_graph(torch, graph, stream, reps):
-    """Milliseconds per replay, HIP events on the replay stream."""
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+def time_graph(torch, graph, stream, reps, repeats=5):
+    """Milliseconds per replay (median of `repeats` runs of `reps` replays),
+    HIP events on the replay stream."""
+    out = []
     with torch.cuda.stream(stream):
         graph.replay()
         torch.cuda.synchronize()
+        for _ in range(repeats):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            end.record(stream)
+            end.synchronize()
+            out.append(start.elapsed_time(end) / reps)
+    out.sort()
+    return out[len(out) // 2]
+
+
+def per_call_us(torch, stream, body, calls, reps):
+    """µs per call of a graph of `calls` back-to-back calls."""
+    return time_graph(torch, Graph(torch, body, stream), stream, reps) / calls * 1e3
+
+
+class Config:
+    """One decode shape on the device: rotating tile-layout copies, the
+    activations, per-M scratch and outputs."""
+
+    def __init__(self, torch, pq2, workloads, name, dev, stream, ms=DECODE_MS):
+        w = workloads.WORKLOADS[name]
+        self.name, self.n, self.k, self.ms = name, w.n, w.k, ms
+        self.raw_np, x_cpu = workloads.workload_inputs(name)
+        self.x_cpu = x_cpu[: max(ms)].contiguous()
+        self.wb = weight_bytes(self.n, self.k)
+        self.tb = pq2.pq2_tiles_bytes(self.n, self.k)
+        per = len(ms)
+        self.copies = per * max(1, math.ceil(ROTATION_BYTES / self.tb / per))
+        with torch.cuda.stream(stream):
+            raw = torch.from_numpy(self.raw_np).to(dev)
+            self.tpool = torch.empty((self.copies, self.tb), dtype=torch.uint8, device=dev)
+            pq2.pq2_prepare_tiles(raw, self.n, self.k, self.tpool[0], stream=stream)
+            for c in range(1, self.copies):
+                self.tpool[c].copy_(self.tpool[0])
+            self.x = self.x_cpu.to(dev)
+            self.q = {m: torch.empty((m, self.k), dtype=torch.int8, device=dev) for m in ms}
+            self.xs = {m: torch.empty((m, self.k // 128), dtype=torch.float32, device=dev) for m in ms}
+            self.y = {m: torch.empty((m, self.n), dtype=torch.float32, device=dev) for m in ms}
+            self.ymm = {m: torch.empty((m, self.n), dtype=torch.float32, device=dev) for m in ms}
+            for m in ms:
+                pq2.pq2_quantize_act_i8(self.x[:m], self.q[m], self.xs[m], stream=stream)
+        torch.cuda.synchronize()
+        log(f"[bench] {name} K={self.k} N={self.n}: weights {self.wb} B, {self.copies} tile copies "
+            f"({self.copies * self.tb / 2**30:.2f} GiB)")
+
+    def gemv(self, pq2, m, c, stream):
+        pq2.pq2_gemv_tiles(self.x[:m], self.tpool[c], self.y[m], self.q[m], self.xs[m], stream=stream)
+
+    def matmul(self, pq2, m, c, stream):
+        pq2.pq2_matmul_small_m_tiles(self.q[m], self.xs[m], self.tpool[c], self.ymm[m], stream=stream)
+
+
+def measure_config(torch, pq2, cfg, stream, reps, digest):
+    """Per-M tile matmul and complete call, and the read ceilings, over the
+    config's rotating copies."""
+    n, k, copies = cfg.n, cfg.k, cfg.copies
+    per_m = {}
+    for m in cfg.ms:
+        mm_us = per_call_us(torch, stream, lambda m=m: [cfg.matmul(pq2, m, c, stream) for c in range(copies)],
+                            copies, reps)
+        call_us = per_call_us(torch, stream, lambda m=m: [cfg.gemv(pq2, m, c, stream) for c in range(copies)],
+                              copies, reps)
+        torch.cuda.synchronize()
+        assert torch.equal(cfg.y[m].view(torch.int32), cfg.ymm[m].view(torch.int32)), \
+            f"{cfg.name} M={m}: complete call and tile matmul differ"
+        b = matmul_bytes(m, n, k)
+        per_m[str(m)] = {
+            "matmul_us": round(mm_us, 3),
+            "matmul_GBps": round(b / (mm_us * 1e-6) / 1e9, 1),
+            "matmul_pct_peak": round(100 * b / (mm_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 1),
+            "gemv_call_us": round(call_us, 3),
+            "gemv_call_GBps": round(b / (call_us * 1e-6) / 1e9, 1),
+            "matmul_bytes": b,
+        }
+        log(f"[bench] {cfg.name} M={m}: tile matmul {mm_us:.3f} us ({per_m[str(m)]['matmul_GBps']:.0f} GB/s, "
+            f"{per_m[str(m)]['matmul_pct_peak']:.1f}% of 8 TB/s), complete call {call_us:.3f} us")
+
+    # Ceilings at the same bytes, over the same copies.
+    words = pq2.pq2_stream_probe_words(STREAM_WORKGROUPS)
+    sout = torch.empty((words,), dtype=torch.int32, device=cfg.x.device)
+    pout = torch.empty((pq2.pq2_read_probe_words(pq2.LAYOUT_TILES, n, k),), dtype=torch.int32, device=cfg.x.device)
+    stream_us = per_call_us(torch, stream, lambda: [pq2.pq2_stream_probe(
+        cfg.tpool[c], cfg.tb, STREAM_WORKGROUPS, sout, False, 0x7FFFFFFF, stream=stream) for c in range(copies)],
+        copies, reps)
+    stream_store_us = per_call_us(torch, stream, lambda: [pq2.pq2_stream_probe(
+        cfg.tpool[c], cfg.tb, STREAM_WORKGROUPS, sout, True, stream=stream) for c in range(copies)], copies, reps)
+    engine_read_us = per_call_us(torch, stream, lambda: [pq2.pq2_read_probe(
+        cfg.tpool[c], pq2.LAYOUT_TILES, n, k, pout, stream=stream) for c in range(copies)], copies, reps)
+    torch.cuda.synchronize()
+    ceilings = {
+        "stream_read_us": round(stream_us, 3),
+        "stream_read_GBps": round(cfg.tb / (stream_us * 1e-6) / 1e9, 1),
+        "stream_read_plus_store_us": round(stream_store_us, 3),
+        "engine_read_probe_us": round(engine_read_us, 3),
+        "bytes": cfg.tb,
+    }
+    log(f"[bench] {cfg.name} ceilings: stream read {stream_us:.3f} us ({ceilings['stream_read_GBps']:.0f} GB/s), "
+        f"+ one store per wave {stream_store_us:.3f} us, engine read probe {engine_read_us:.3f} us")
+
+    tot_b = sum(v["matmul_bytes"] for v in per_m.values())
+    tot_us = sum(v["matmul_us"] for v in per_m.values())
+    achieved = tot_b / (tot_us * 1e-6) / 1e9
+    mean_us = tot_us / len(per_m)
+    traffic = stored_summary(f"small_m_tiles_{cfg.name}_traffic.txt", digest)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_HBM_BYTES_PER_S / 1e9,
+        "unit": "GB/s",
+        "frac": round(achieved * 1e9 / PEAK_HBM_BYTES_PER_S, 4),
+        "traffic": float(traffic["hbm_bytes_per_launch_avg_m1to4"]) if traffic else None,
+        "kernel": f"small_m_tiles_kernel (pq2_matmul_small_m_tiles), {cfg.name} K={k} N={n}, "
+                  f"mean over one launch each at M={','.join(map(str, cfg.ms))}",
+        "algorithmic_bytes_per_launch_avg": tot_b / len(per_m),
+        "mean_launch_us": round(mean_us, 3),
+        "kernel_source_digest": digest,
+        "stream_read_us": ceilings["stream_read_us"],
+        "mean_launch_vs_stream_read": round(mean_us / stream_us, 3),
+        "stream_read_frac": round(cfg.tb / (stream_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4),
+    }
+    return per_m, ceilings, roofline
+
+
+def headline_step(torch, pq2, cfg, stream, steps, warmup):
+    """Exactly `steps` complete steps (M = 1..4, each call on its own copy)."""
+    per = len(cfg.ms)
+    steps_per_graph = cfg.copies // per
+
+    def steps_fn(count):
+        def f():
+            for s in range(count):
+                for i, m in enumerate(cfg.ms):
+                    cfg.gemv(pq2, m, (s * per + i) % cfg.copies, stream)
+        return f
+
+    graphs = {steps_per_graph: Graph(torch, steps_fn(steps_per_graph), stream)}
+    for count in {warmup % steps_per_graph, steps % steps_per_graph} - {0}:
+        graphs[count] = Graph(torch, steps_fn(count), stream)
+
+    def run(count):
+        full, rest = divmod(count, steps_per_graph)
+        for _ in range(full):
+            graphs[steps_per_graph].replay()
+        if rest:
+            graphs[rest].replay()
+
+    with torch.cuda.stream(stream):
+        run(warmup)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
         start.record(stream)
-        for _ in range(reps):
-            graph.replay()
+        run(steps)
         end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / reps
+    torch.cuda.synchronize()
+    for m in cfg.ms:
+        assert torch.isfinite(cfg.y[m]).all(), "non-finite output"
+    return start.elapsed_time(end) / steps
+
+
+def launch_floor_and_stream_fit(torch, pq2, dev, stream, reps):
+    """Empty-kernel graph floor and the stream read over 4..192 MB, fitted as
+    t = t0 + B / BW (least squares)."""
+    floor = {}
+    for wg, waves in ((1, 1), (1088, 5)):
+        floor[f"{wg}x{waves}"] = round(per_call_us(
+            torch, stream, lambda wg=wg, waves=waves: [pq2.pq2_empty_probe(wg, waves, stream=stream)
+                                                       for _ in range(200)], 200, reps), 3)
+    buf = torch.empty((3 << 29,), dtype=torch.uint8, device=dev)  # 1.5 GiB
+    buf.fill_(0x5A)
+    out = torch.empty((pq2.pq2_stream_probe_words(STREAM_WORKGROUPS),), dtype=torch.int32, device=dev)
+    pts = []
+    for mb in STREAM_FIT_MB:
+        nb = mb << 20
+        copies = buf.numel() // nb
+        us = per_call_us(torch, stream, lambda nb=nb, copies=copies: [pq2.pq2_stream_probe(
+            buf[c * nb:(c + 1) * nb], nb, STREAM_WORKGROUPS, out, False, 0x7FFFFFFF, stream=stream)
+            for c in range(copies)], copies, reps)
+        pts.append((nb, us))
+    torch.cuda.synchronize()
+    del buf
+    nbar = sum(b for b, _ in pts) / len(pts)
+    tbar = sum(t for _, t in pts) / len(pts)
+    slope = sum((b - nbar) * (t - tbar) for b, t in pts) / sum((b - nbar) ** 2 for b, _ in pts)
+    t0 = tbar - slope * nbar
+    fit = {"t0_us": round(t0, 3), "bw_GBps": round(1e-3 / slope, 1),
+           "points": [{"MiB": b >> 20, "us": round(t, 3), "GBps": round(b / (t * 1e-6) / 1e9, 1)} for b, t in pts]}
+    log(f"[bench] launch floor (empty kernel, graph): {floor}; stream read fit t = {t0:.3f} us + B / "
+        f"{fit['bw_GBps']:.0f} GB/s over {', '.join(str(b >> 20) for b, _ in pts)} MiB")
+    return floor, fit
 
 
 def cpu_baseline(raw, x, n, k, ms, budget_s):
-    """The CPU oracle on the same work (quantise + matmul per M), repeated up
-    to the time budget; single thread."""
+    """The CPU oracle on the same work (quantise + matmul per M) for a bounded
+    time, on one thread and on T threads that split the weight rows; the two
+    results must be bitwise equal."""
+    import concurrent.futures
+
+    import numpy as np
+
     import oracle
     import workloads
     bits = workloads.bf16_bits(x)
-    done_bytes = 0
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        for m in ms:
-            q, xs = oracle.quantize_act_i8(bits[:m])
-            oracle.matmul_raw(q, xs, raw, n, k)
-            done_bytes += quantize_bytes(m, k) + matmul_bytes(m, n, k)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+    qs = {m: oracle.quantize_act_i8(bits[:m]) for m in ms}
+    # Every core of the affinity mask, but no more threads than the box's CPU
+    # share (OMP_NUM_THREADS, 16 where unset).
+    cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS") or 16))
+
+    def matmul_rows(m, r0, r1):
+        q, xs = qs[m]
+        return oracle.matmul_raw(q, xs, raw[r0:r1], r1 - r0, k)[0]
+
+    def run(threads, pool):
+        done_bytes, reps, results = 0, 0, {}
+        t0 = time.perf_counter()
+        while True:
+            for m in ms:
+                oracle.quantize_act_i8(bits[:m])
+                if threads == 1:
+                    results[m] = matmul_rows(m, 0, n)
+                else:
+                    cuts = [n * i // threads for i in range(threads + 1)]
+                    parts = list(pool.map(lambda i, m=m: matmul_rows(m, cuts[i], cuts[i + 1]), range(threads)))
+                    results[m] = np.concatenate(parts, axis=1)
+                done_bytes += matmul_bytes(m, n, k)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        return done_bytes / (time.perf_counter() - t0) / 1e9, reps, time.perf_counter() - t0, results
+
+    single, reps1, dt1, r1 = run(1, None)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=cores) as pool:
+        multi, repsT, dtT, rT = run(cores, pool)
+    for m in ms:
+        assert np.array_equal(r1[m].view(np.uint64), rT[m].view(np.uint64)), "threaded oracle differs"
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
-        "value": done_bytes / dt / 1e9,
+        "value": round(multi, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{reps} repetition(s) of quantise+matmul at M={list(ms)} on the full K={k} N={n} "
-                  f"shape, {dt:.1f} s single-threaded",
-        "ms_per_step": dt / reps * 1e3,
+        "sample": f"{repsT} repetition(s) of quantise+matmul at M={list(ms)} on the full K={k} N={n} shape "
+                  f"in {dtT:.1f} s on {cores} threads (weight rows split, bitwise equal to one thread)",
+        "single_thread": {"value": round(single, 4), "cores": 1,
+                          "sample": f"{reps1} repetition(s) in {dt1:.1f} s"},
+        "cpu_model": model,
     }
 
 
@@ -163,8 +392,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
-    ap.add_argument("--reps", type=int, default=20, help="graph replays per per-M timing")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work per thread count")
+    ap.add_argument("--reps", type=int, default=20, help="graph replays per timing")
+    ap.add_argument("--configs", default="up,qkv,down", help="decode shapes to measure (headline first)")
+    ap.add_argument("--variants", action="store_true", help="also time the other decode paths at the QKV shape")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -180,238 +411,40 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = workloads.WORKLOADS["qkv"]
-    n, k, ms = w.n, w.k, (1, 2, 3, 4)
-    raw_np, x_cpu = workloads.workload_inputs("qkv")
-    wb = weight_bytes(n, k)
-    tb = pq2.pq2_tiles_bytes(n, k)
-    copies = max(2, math.ceil(ROTATION_BYTES / wb))
-    log(f"[bench] qkv K={k} N={n} weights {wb} B, {copies} copies per layout "
-        f"({copies * wb / 2**30:.2f} GiB planes, {copies * tb / 2**30:.2f} GiB tiles)")
-
     stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        raw = torch.from_numpy(raw_np).to(dev)
-        pool = torch.empty((copies, wb), dtype=torch.uint8, device=dev)
-        tpool = torch.empty((copies, tb), dtype=torch.uint8, device=dev)
-        rpool = torch.empty((copies,) + tuple(raw.shape), dtype=torch.uint8, device=dev)  # raw rows, read in place
-        pq2.pq2_prepare_planes(raw, n, k, pool[0], stream=stream)
-        pq2.pq2_prepare_tiles(raw, n, k, tpool[0], stream=stream)
-        for c in range(copies):
-            if c:
-                pool[c].copy_(pool[0])
-                tpool[c].copy_(tpool[0])
-            rpool[c].copy_(raw)
-        x = x_cpu.to(dev)
-        bufs = {}
-        pbufs = {}
-        for m in ms:
-            bufs[m] = (torch.empty((m, k), dtype=torch.int8, device=dev),
-                       torch.empty((m, k // 128), dtype=torch.float32, device=dev),
-                       torch.empty((m, n), dtype=torch.float32, device=dev))
-            pbufs[m] = (torch.empty((m, k), dtype=torch.int8, device=dev),
-                        torch.empty((m, k // 128), dtype=torch.float32, device=dev),
-                        torch.empty((m, k // 128), dtype=torch.int32, device=dev),
-                        torch.empty((m, n), dtype=torch.float32, device=dev))
-    torch.cuda.synchronize()
-
-    def step_fn(c):
-        def f():
-            for m in ms:
-                q, xs, y = bufs[m]
-                pq2.pq2_gemv_tiles(x[:m], tpool[c], y, q, xs, stream=stream)
-        return f
-
-    # One graph holds `copies` consecutive steps (step i reads copy i), as a
-    # decode loop runs its calls inside one larger graph; a second graph of
-    # the first r steps makes the count exact.
-    def steps_fn(count):
-        def f():
-            for c in range(count):
-                step_fn(c)()
-        return f
-
-    def run_steps(count, graphs):
-        full, rest = divmod(count, copies)
-        for _ in range(full):
-            graphs[copies].replay()
-        if rest:
-            graphs[rest].replay()
-
-    step_bytes = sum(quantize_bytes(m, k) + matmul_bytes(m, n, k) for m in ms)
-    graphs = {copies: Graph(torch, steps_fn(copies), stream)}
-    for count in {args.warmup % copies, args.steps % copies} - {0}:
-        graphs[count] = Graph(torch, steps_fn(count), stream)
-
-    # Warmup, then exactly K timed steps.
-    with torch.cuda.stream(stream):
-        run_steps(args.warmup, graphs)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        run_steps(args.steps, graphs)
-        end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    for y in (bufs[m][2] for m in ms):
-        assert torch.isfinite(y).all(), "non-finite output"
-    del graphs
-
-    # Per-M call timings: graphs of `copies` back-to-back calls, one per copy.
-    per_m = {}
-    reps = args.reps
-
-    def per_call_us(body):
-        return time_graph(torch, Graph(torch, body, stream), stream, reps) / copies * 1e3
-
-    for m in ms:
-        q, xs, y = bufs[m]
-        qp, pxs, qsum, py = pbufs[m]
-        ys = {key: torch.empty((m, n), dtype=torch.float32, device=dev)
-              for key in ("planes", "tiles_fused", "planes_fused", "raw")}
-        xm = x[:m]
-
-        def calls(kind, m=m, q=q, xs=xs, y=y, qp=qp, pxs=pxs, qsum=qsum, py=py, xm=xm):
-            def body():
-                for c in range(copies):
-                    if kind == "tiles_mm":
-                        pq2.pq2_matmul_small_m_tiles(q, xs, tpool[c], y, stream=stream)
-                    elif kind == "tiles_call":
-                        pq2.pq2_quantize_act_i8(xm, q, xs, stream=stream)
-                        pq2.pq2_matmul_small_m_tiles(q, xs, tpool[c], y, stream=stream)
-                    elif kind == "gemv":
-                        pq2.pq2_gemv_tiles(xm, tpool[c], y, q, xs, stream=stream)
-                    elif kind == "tiles_fused":
-                        pq2.pq2_matmul_small_m_tiles_fused(xm, tpool[c], ys["tiles_fused"], stream=stream)
-                    elif kind == "planes_mm":
-                        pq2.pq2_matmul_small_m(q, xs, pool[c], ys["planes"], stream=stream)
-                    elif kind == "planes_call":
-                        pq2.pq2_quantize_act_i8(xm, q, xs, stream=stream)
-                        pq2.pq2_matmul_small_m(q, xs, pool[c], ys["planes"], stream=stream)
-                    elif kind == "planes_order_mm":
-                        pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
-                    elif kind == "planes_order_call":
-                        pq2.pq2_quantize_act_i8_planes(xm, qp, pxs, qsum, stream=stream)
-                        pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c], py, stream=stream)
-                    elif kind == "planes_fused":
-                        pq2.pq2_matmul_small_m_fused(xm, pool[c], ys["planes_fused"], stream=stream)
-                    elif kind == "raw_mm":
-                        pq2.pq2_matmul_small_m_raw(q, xs, rpool[c], ys["raw"], stream=stream)
-            return body
-
-        t = {kind: per_call_us(calls(kind)) for kind in
-             ("tiles_mm", "tiles_call", "gemv", "tiles_fused", "planes_mm", "planes_call", "planes_order_mm",
-              "planes_order_call", "planes_fused", "raw_mm")}
-        torch.cuda.synchronize()
-        for key, other in (("planes", ys["planes"]), ("plane order", py), ("tiles fused", ys["tiles_fused"]),
-                           ("planes fused", ys["planes_fused"]), ("raw reader", ys["raw"])):
-            assert torch.equal(other.view(torch.int32), y.view(torch.int32)), \
-                f"{key} output differs from the tile-layout output at M={m}"
-        gbs = matmul_bytes(m, n, k) / (t["tiles_mm"] * 1e-6) / 1e9
-        pgbs = matmul_bytes(m, n, k) / (t["planes_mm"] * 1e-6) / 1e9
-        per_m[str(m)] = {
-            "matmul_us": round(t["tiles_mm"], 3),
-            "matmul_GBps": round(gbs, 1),
-            "matmul_pct_peak": round(100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S, 1),
-            "complete_call_us": round(t["tiles_call"], 3),
-            "gemv_call_us": round(t["gemv"], 3),
-            "fused_call_us": round(t["tiles_fused"], 3),
-            "planes_matmul_us": round(t["planes_mm"], 3),
-            "planes_matmul_GBps": round(pgbs, 1),
-            "planes_complete_call_us": round(t["planes_call"], 3),
-            "planes_fused_call_us": round(t["planes_fused"], 3),
-            "plane_order_matmul_us": round(t["planes_order_mm"], 3),
-            "plane_order_complete_call_us": round(t["planes_order_call"], 3),
-            "raw_matmul_us": round(t["raw_mm"], 3),
-            "matmul_bytes": matmul_bytes(m, n, k),
-        }
-        log(f"[bench] M={m}: tiles matmul {t['tiles_mm']:.3f} us ({gbs:.0f} GB/s, "
-            f"{100 * gbs * 1e9 / PEAK_HBM_BYTES_PER_S:.1f}% of 8 TB/s), call {t['tiles_call']:.3f}, "
-            f"gemv {t['gemv']:.3f}, "
-            f"fused {t['tiles_fused']:.3f}; planes matmul {t['planes_mm']:.3f} ({pgbs:.0f} GB/s), "
-            f"call {t['planes_call']:.3f}, fused {t['planes_fused']:.3f}; plane order matmul "
-            f"{t['planes_order_mm']:.3f}, call {t['planes_order_call']:.3f}; raw reader matmul {t['raw_mm']:.3f}")
-
-    # Smaller activation groups (page "Kernel experiments", section C, Tests
-    # 8 and 9): the tile matmul and the complete call with 64- and 32-element
-    # activation groups, beside the group-128 figures above.
-    agroups = {}
-    for ag in (64, 32):
-        agroups[str(ag)] = {}
-        for m in ms:
-            xm = x[:m]
-            qg = torch.empty((m, k), dtype=torch.int8, device=dev)
-            xsg = torch.empty((m, k // ag), dtype=torch.float32, device=dev)
-            yg = torch.empty((m, n), dtype=torch.float32, device=dev)
-            with torch.cuda.stream(stream):
-                pq2.pq2_quantize_act_i8_g(xm, qg, xsg, ag, stream=stream)
-
-            def g_calls(call, m=m, xm=xm, qg=qg, xsg=xsg, yg=yg, ag=ag):
-                def body():
-                    for c in range(copies):
-                        if call:
-                            pq2.pq2_quantize_act_i8_g(xm, qg, xsg, ag, stream=stream)
-                        pq2.pq2_matmul_small_m_tiles_g(qg, xsg, tpool[c], yg, ag, stream=stream)
-                return body
-
-            mm_us, call_us = per_call_us(g_calls(False)), per_call_us(g_calls(True))
-            torch.cuda.synchronize()
-            assert torch.isfinite(yg).all(), "non-finite output"
-            agroups[str(ag)][str(m)] = {
-                "matmul_us": round(mm_us, 3),
-                "complete_call_us": round(call_us, 3),
-                "matmul_vs_group128": round(mm_us / per_m[str(m)]["matmul_us"], 3),
-            }
-        log(f"[bench] activation groups of {ag}: matmul us " +
-            ", ".join(f"M={m} {v['matmul_us']:.3f}" for m, v in agroups[str(ag)].items()))
-
-    # Read ceiling: each layout's decode-engine weight loads with no
-    # arithmetic (pq2_read_probe), over the same rotating copies.
-    probe = {}
-    for name, layout, wpool in (("tiles", pq2.LAYOUT_TILES, tpool), ("planes", pq2.LAYOUT_PLANES, pool)):
-        pout = torch.empty((pq2.pq2_read_probe_words(layout, n, k),), dtype=torch.int32, device=dev)
-
-        def probe_calls(layout=layout, wpool=wpool, pout=pout):
-            def body():
-                for c in range(copies):
-                    pq2.pq2_read_probe(wpool[c], layout, n, k, pout, stream=stream)
-            return body
-
-        p_us = per_call_us(probe_calls())
-        probe[name] = {"us": round(p_us, 3), "weight_GBps": round(wb / (p_us * 1e-6) / 1e9, 1)}
-    torch.cuda.synchronize()
-    log(f"[bench] read probe (weights only, no arithmetic): tiles {probe['tiles']['us']:.3f} us "
-        f"({probe['tiles']['weight_GBps']:.0f} GB/s), planes {probe['planes']['us']:.3f} us "
-        f"({probe['planes']['weight_GBps']:.0f} GB/s)")
-
-    tot_bytes = sum(v["matmul_bytes"] for v in per_m.values())
-    tot_us = sum(v["matmul_us"] for v in per_m.values())
-    achieved = tot_bytes / (tot_us * 1e-6) / 1e9
-    ptot_us = sum(v["planes_matmul_us"] for v in per_m.values())
     digest = source_digest()
-    traffic = stored_traffic(digest)
-    roofline = {
-        "bound": "hbm",
-        "achieved": round(achieved, 1),
-        "peak": PEAK_HBM_BYTES_PER_S / 1e9,
-        "unit": "GB/s",
-        "frac": round(achieved * 1e9 / PEAK_HBM_BYTES_PER_S, 4),
-        "traffic": traffic,
-        "kernel": "small_m_tiles_kernel (pq2_matmul_small_m_tiles), mean over one launch each at M=1..4",
-        "algorithmic_bytes_per_launch_avg": tot_bytes / len(ms),
-        "mean_launch_us": round(tot_us / len(ms), 3),
-        "kernel_source_digest": digest,
-        "planes_kernel_achieved": round(tot_bytes / (ptot_us * 1e-6) / 1e9, 1),
-        "planes_kernel_mean_launch_us": round(ptot_us / len(ms), 3),
-        # The same layout's weight loads alone (pq2_read_probe): the mean
-        # launch as a multiple of that read time.
-        "read_probe_us": probe["tiles"]["us"],
-        "mean_launch_vs_read_probe": round((tot_us / len(ms)) / probe["tiles"]["us"], 3),
-    }
+    names = [c for c in args.configs.split(",") if c]
+    if HEADLINE not in names:
+        names.insert(0, HEADLINE)
 
+    results, rooflines, ceilings = {}, {}, {}
+    ms_per_step = value = None
+    head = None
+    for name in names:
+        cfg = Config(torch, pq2, workloads, name, dev, stream)
+        if name == HEADLINE:
+            ms_per_step = headline_step(torch, pq2, cfg, stream, args.steps, args.warmup)
+            step_bytes = sum(matmul_bytes(m, cfg.n, cfg.k) for m in cfg.ms)
+            value = step_bytes / (ms_per_step * 1e-3) / 1e9
+            head = cfg
+            log(f"[bench] headline {name}: {ms_per_step * 1e3:.3f} us per step of M={list(cfg.ms)}, "
+                f"{value:.0f} GB/s")
+        per_m, ceil, roof = measure_config(torch, pq2, cfg, stream, args.reps, digest)
+        results[name] = {"k": cfg.k, "n": cfg.n, "weight_copies": cfg.copies,
+                         "rotation_bytes": cfg.copies * cfg.tb, "us_per_call": per_m}
+        ceilings[name], rooflines[name] = ceil, roof
+        if args.variants and name == "qkv":
+            results[name]["variants"] = bench_variants(torch, pq2, workloads, cfg, dev, stream, args.reps)
+        if name != HEADLINE:
+            del cfg
+            torch.cuda.empty_cache()
+
+    floor, fit = launch_floor_and_stream_fit(torch, pq2, dev, stream, args.reps)
+    roofline = dict(rooflines[HEADLINE])
+    roofline["per_config"] = {k: v for k, v in rooflines.items() if k != HEADLINE}
+
+    # pq2_gemv_tiles' choice (the C library's rule, restated for the label).
+    fused_ms = [m for m in head.ms if m <= 2 and head.k <= 8192 and m * -(-head.n // 16) <= 1600]
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -426,24 +459,88 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "attention QKV projection K=5120 N=10240, M=1,2,3,4 (x -> y per M with pq2_gemv_tiles: "
-                        "fused quantise + tile matmul at M=1, quantiser + tile matmul at M=2..4)",
-            "k": k, "n": n, "ms": list(ms),
-            "weight_copies": copies, "rotation_bytes": copies * tb,
+            "workload": f"FFN up projection K={head.k} N={head.n}, M=1,2,3,4: x -> y per M with pq2_gemv_tiles "
+                        f"(one fused quantise + tile matmul launch at M={','.join(map(str, fused_ms))}, quantiser "
+                        f"launch + tile matmul at M={','.join(map(str, [m for m in head.ms if m not in fused_ms]))}), "
+                        "each call on its own weight copy",
+            "k": head.k, "n": head.n, "ms": list(head.ms),
+            "weight_copies": head.copies, "rotation_bytes": head.copies * head.tb,
         },
-        "us_per_call": per_m,
-        "activation_groups_us_per_call": agroups,
-        "read_probe_us_per_call": probe,
+        "decode": results,
+        "ceilings": ceilings,
+        "launch_floor_us": floor,
+        "stream_read_fit": fit,
         "roofline": roofline,
     }
-
+    del head
+    torch.cuda.empty_cache()
     if not args.no_prefill:
         result["prefill"] = bench_prefill(torch, pq2, workloads, dev, stream)
     if args.calibrate:
         calibration_copy(torch, dev, stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(raw_np, x_cpu, n, k, ms, args.cpu_budget)
+        w = workloads.WORKLOADS[HEADLINE]
+        raw_np, x_cpu = workloads.workload_inputs(HEADLINE)
+        result["cpu_baseline"] = cpu_baseline(raw_np, x_cpu, w.n, w.k, DECODE_MS, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def bench_variants(torch, pq2, workloads, cfg, dev, stream, reps):
+    """The other decode paths at one shape, same rotating weights (planes,
+    plane-order activations, the fused launches, the raw-block reader,
+    activation groups of 64 and 32); every path's output bits are checked
+    against the tile matmul's (groups 64 and 32: finite only)."""
+    n, k, copies = cfg.n, cfg.k, cfg.copies
+    wb = weight_bytes(n, k)
+    with torch.cuda.stream(stream):
+        raw = torch.from_numpy(cfg.raw_np).to(dev)
+        pool = torch.empty((copies, wb), dtype=torch.uint8, device=dev)
+        pq2.pq2_prepare_planes(raw, n, k, pool[0], stream=stream)
+        for c in range(1, copies):
+            pool[c].copy_(pool[0])
+    torch.cuda.synchronize()
+    out = {}
+    for m in cfg.ms:
+        xm, q, xs, y = cfg.x[:m], cfg.q[m], cfg.xs[m], cfg.ymm[m]
+        qp = torch.empty_like(q)
+        pxs = torch.empty_like(xs)
+        qsum = torch.empty((m, k // 128), dtype=torch.int32, device=dev)
+        ys = {key: torch.empty((m, n), dtype=torch.float32, device=dev)
+              for key in ("planes", "plane_order", "tiles_fused", "planes_fused", "raw")}
+        with torch.cuda.stream(stream):
+            pq2.pq2_quantize_act_i8_planes(xm, qp, pxs, qsum, stream=stream)
+        bodies = {
+            "planes_matmul_us": lambda: [pq2.pq2_matmul_small_m(q, xs, pool[c], ys["planes"], stream=stream)
+                                         for c in range(copies)],
+            "plane_order_matmul_us": lambda: [pq2.pq2_matmul_small_m_planes(qp, pxs, qsum, pool[c],
+                                                                           ys["plane_order"], stream=stream)
+                                              for c in range(copies)],
+            "tiles_fused_call_us": lambda: [pq2.pq2_matmul_small_m_tiles_fused(xm, cfg.tpool[c], ys["tiles_fused"],
+                                                                              stream=stream) for c in range(copies)],
+            "planes_fused_call_us": lambda: [pq2.pq2_matmul_small_m_fused(xm, pool[c], ys["planes_fused"],
+                                                                         stream=stream) for c in range(copies)],
+            "raw_matmul_us": lambda: [pq2.pq2_matmul_small_m_raw(q, xs, raw, ys["raw"], stream=stream)
+                                      for c in range(copies)],
+        }
+        t = {key: round(per_call_us(torch, stream, body, copies, reps), 3) for key, body in bodies.items()}
+        torch.cuda.synchronize()
+        for key, yv in ys.items():
+            assert torch.equal(yv.view(torch.int32), y.view(torch.int32)), f"{key} differs at M={m}"
+        for ag in (64, 32):
+            qg = torch.empty((m, k), dtype=torch.int8, device=dev)
+            xsg = torch.empty((m, k // ag), dtype=torch.float32, device=dev)
+            yg = torch.empty((m, n), dtype=torch.float32, device=dev)
+            with torch.cuda.stream(stream):
+                pq2.pq2_quantize_act_i8_g(xm, qg, xsg, ag, stream=stream)
+            t[f"agroup{ag}_matmul_us"] = round(per_call_us(torch, stream, lambda qg=qg, xsg=xsg, yg=yg, ag=ag: [
+                pq2.pq2_matmul_small_m_tiles_g(qg, xsg, cfg.tpool[c], yg, ag, stream=stream)
+                for c in range(copies)], copies, reps), 3)
+            torch.cuda.synchronize()
+            assert torch.isfinite(yg).all()
+        out[str(m)] = t
+        log(f"[bench] variants {cfg.name} M={m}: {t}")
+    del pool
+    return out
 
 
 def calibration_copy(torch, dev, stream):
@@ -459,75 +556,42 @@ def calibration_copy(torch, dev, stream):
 
 
 def bench_prefill(torch, pq2, workloads, dev, stream):
-    """MFMA prefill at the gate (N=6144) and up (N=17408) shapes, M=256..1024:
-    from the tile layout (the decode step's weights), and from the planes with
-    natural- and plane-order activations; all give the same bits."""
+    """MFMA prefill at the gate (N=6144) and up (N=17408) shapes, M=256..1024,
+    from the tile layout, over weight copies that together exceed the 256 MB
+    Infinity Cache (each launch reads the next copy)."""
     out = {}
     for name in ("prefill_gate", "prefill_up"):
         w = workloads.WORKLOADS[name]
         raw_np, x_cpu = workloads.workload_inputs(name)
+        tb = pq2.pq2_tiles_bytes(w.n, w.k)
+        copies = max(2, math.ceil((320 << 20) / tb))
         with torch.cuda.stream(stream):
-            planes = torch.empty(weight_bytes(w.n, w.k), dtype=torch.uint8, device=dev)
-            tiles = torch.empty(pq2.pq2_tiles_bytes(w.n, w.k), dtype=torch.uint8, device=dev)
-            raw = torch.from_numpy(raw_np).to(dev)
-            pq2.pq2_prepare_planes(raw, w.n, w.k, planes, stream=stream)
-            pq2.pq2_prepare_tiles(raw, w.n, w.k, tiles, stream=stream)
+            tiles = torch.empty((copies, tb), dtype=torch.uint8, device=dev)
+            pq2.pq2_prepare_tiles(torch.from_numpy(raw_np).to(dev), w.n, w.k, tiles[0], stream=stream)
+            for c in range(1, copies):
+                tiles[c].copy_(tiles[0])
             x = x_cpu.to(dev)
         torch.cuda.synchronize()
         for m in w.ms:
             q = torch.empty((m, w.k), dtype=torch.int8, device=dev)
-            qp = torch.empty((m, w.k), dtype=torch.int8, device=dev)
             xs = torch.empty((m, w.k // 128), dtype=torch.float32, device=dev)
-            qsum = torch.empty((m, w.k // 128), dtype=torch.int32, device=dev)
             y = torch.empty((m, w.n), dtype=torch.float32, device=dev)
             with torch.cuda.stream(stream):
                 pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
-                pq2.pq2_quantize_act_i8_planes(x[:m], qp, xs, qsum, stream=stream)
-
-            def f(q=q, xs=xs, y=y):
-                for _ in range(10):
-                    pq2.pq2_matmul_prefill(q, xs, planes, y, stream=stream)
-
-            def fp(qp=qp, xs=xs, y=y):
-                for _ in range(10):
-                    pq2.pq2_matmul_prefill_planes(qp, xs, planes, y, stream=stream)
-
-            yt = torch.empty((m, w.n), dtype=torch.float32, device=dev)
-
-            def ft(q=q, xs=xs, yt=yt):
-                for _ in range(10):
-                    pq2.pq2_matmul_prefill_tiles(q, xs, tiles, yt, stream=stream)
-
-            t_us = time_graph(torch, Graph(torch, f, stream), stream, 5) / 10 * 1e3
-            tp_us = time_graph(torch, Graph(torch, fp, stream), stream, 5) / 10 * 1e3
-            tt_us = time_graph(torch, Graph(torch, ft, stream), stream, 5) / 10 * 1e3
-            # Smaller activation groups (one scale per 64 or 32 activations),
-            # same weights: the tile-layout prefill with per-group rescales.
-            ag_us = {}
-            for agroup in (64, 32):
-                qg = torch.empty((m, w.k), dtype=torch.int8, device=dev)
-                xsg = torch.empty((m, w.k // agroup), dtype=torch.float32, device=dev)
-                yg = torch.empty((m, w.n), dtype=torch.float32, device=dev)
-                with torch.cuda.stream(stream):
-                    pq2.pq2_quantize_act_i8_g(x[:m], qg, xsg, agroup, stream=stream)
-
-                def fg(qg=qg, xsg=xsg, yg=yg, agroup=agroup):
-                    for _ in range(10):
-                        pq2.pq2_matmul_prefill_tiles_g(qg, xsg, tiles, yg, agroup, stream=stream)
-
-                ag_us[agroup] = time_graph(torch, Graph(torch, fg, stream), stream, 5) / 10 * 1e3
+            us = per_call_us(torch, stream, lambda q=q, xs=xs, y=y: [
+                pq2.pq2_matmul_prefill_tiles(q, xs, tiles[c], y, stream=stream) for c in range(copies)],
+                copies, 5)
             torch.cuda.synchronize()
-            assert torch.equal(yt.view(torch.int32), y.view(torch.int32)), f"prefill from tiles differs at M={m}"
+            assert torch.isfinite(y).all()
             ops = 2.0 * m * w.n * w.k
-            tops = ops / (tt_us * 1e-6) / 1e12
-            out[f"{name}_m{m}"] = {"us": round(tt_us, 2), "TOPS": round(tops, 1),
+            tops = ops / (us * 1e-6) / 1e12
+            out[f"{name}_m{m}"] = {"us": round(us, 2), "TOPS": round(tops, 1),
                                    "pct_int8_peak": round(100 * tops * 1e12 / PEAK_INT8_OPS_PER_S, 1),
-                                   "planes_us": round(t_us, 2), "planes_plane_order_us": round(tp_us, 2),
-                                   "agroup64_us": round(ag_us[64], 2), "agroup32_us": round(ag_us[32], 2)}
-            log(f"[bench] {name} M={m}: tile layout {tt_us:.1f} us, {tops:.0f} TOPS (planes {t_us:.1f} us, "
-                f"planes with plane-order input {tp_us:.1f} us; activation groups 64 / 32: "
-                f"{ag_us[64]:.1f} / {ag_us[32]:.1f} us)")
-        del planes, tiles
+                                   "weight_copies": copies}
+            log(f"[bench] {name} M={m}: tile-layout prefill {us:.1f} us, {tops:.0f} TOPS "
+                f"({out[f'{name}_m{m}']['pct_int8_peak']:.1f}% of 5 POP/s)")
+        del tiles
+        torch.cuda.empty_cache()
     return out
 
 

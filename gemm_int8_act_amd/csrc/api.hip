@@ -180,8 +180,8 @@ int pq2_prepare_tiles(const void* raw, int64_t raw_row_stride_bytes, int64_t n, 
 int pq2_matmul_small_m_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
                                    int64_t k, float* y, int max_waves, int split, void* stream) {
     if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, PQ2_MAX_SMALL_M, true)) return rc;
-    if (max_waves < 0 || max_waves > 8) return PQ2_EINVAL;
-    const int waves = max_waves ? max_waves : pq2::default_small_m_config(pq2::kSrcNatural, m, n, k).max_waves;
+    if (max_waves < 0 || max_waves > 16) return PQ2_EINVAL;
+    const int waves = max_waves ? max_waves : pq2::kTilesDefaultWaves;
     if (!split) split = pq2::tiles_default_split(m, k, waves);
     if (!pq2::tiles_supported(k, waves, split)) return PQ2_EINVAL;
     if (int rc = check_device()) return rc;
@@ -209,8 +209,8 @@ int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row
         return PQ2_EALIGN;
     const size_t ybytes = (size_t)m * n * 4;
     if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, tiles, (size_t)pq2::tiles_bytes(n, k))) return PQ2_EINVAL;
-    if (max_waves < 0 || max_waves > 8) return PQ2_EINVAL;
-    const int waves = max_waves ? max_waves : pq2::default_small_m_config(pq2::kSrcNatural, m, n, k).max_waves;
+    if (max_waves < 0 || max_waves > 16) return PQ2_EINVAL;
+    const int waves = max_waves ? max_waves : pq2::kTilesDefaultWaves;
     if (!split) split = pq2::tiles_default_split(m, k, waves);
     if (!pq2::tiles_supported(k, waves, split)) return PQ2_EINVAL;
     if (int rc = check_device()) return rc;
@@ -243,13 +243,15 @@ int pq2_quantize_act_i8(const void* x, int dtype, int64_t x_row_stride_elems, in
 
 int pq2_gemv_tiles(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m, int64_t n,
                    int64_t k, float* y, int8_t* q_work, float* xs_work, void* stream) {
-    // One or two columns whose waves each hold a single segment (k <= 1024 * 8
-    // at the default k split): the single launch wins (K = 5120: 5.3 against
-    // 6.9 us at one column, 6.5 against 7.3 at two); otherwise the quantiser
-    // launch plus the tile matmul.  Both give the same bits.  x that the
+    // The single launch repeats the quantisation in every 16-row tile; the
+    // two-launch path pays a second launch (about 2 us in a graph).  The
+    // fused launch wins while m * tiles is small and every wave holds one
+    // segment (K = 5120: qkv 5.2 against 6.8 us at one column and 6.3
+    // against 6.8 at two; up 6.9 against 8.3 at one column, but 9.2 against
+    // 8.5 at two, m * tiles = 2176).  Both give the same bits.  x that the
     // fused kernel cannot read (not 16-byte aligned rows, or a span of 2^31
     // bytes or more) takes the two-launch path when scratch is given.
-    if (m <= 2 && k <= 8192) {
+    if (m <= 2 && k <= 8192 && m * ((n + 15) / 16) <= 1600) {
         const int esize = dtype == PQ2_F32 ? 4 : 2;
         const bool fused_ok = x && aligned(x, 16) && (x_row_stride_elems * esize) % 16 == 0 && m >= 1 &&
                               x_row_stride_elems >= k &&
@@ -373,7 +375,7 @@ int pq2_matmul_small_m_tiles_g(const int8_t* q, const float* xs, const void* til
     if (agroup != 128 && agroup != 64 && agroup != 32) return PQ2_EINVAL;
     if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, PQ2_MAX_SMALL_M, true)) return rc;
     if (overlap(y, (size_t)m * n * 4, xs, (size_t)m * (k / agroup) * 4)) return PQ2_EINVAL;
-    const int waves = pq2::default_small_m_config(pq2::kSrcNatural, m, n, k).max_waves;
+    const int waves = pq2::kTilesDefaultWaves;
     const int split = pq2::tiles_default_split(m, k, waves);
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m_tiles_g(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, (int)agroup,

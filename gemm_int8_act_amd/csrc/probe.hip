@@ -27,7 +27,8 @@ constexpr int kProbeCodeBlock = 1024;
 constexpr int kProbeUnit = 4 * kProbeCodeBlock + 256;
 // Planes: a wave is 8 row slots of 8 lanes, as in the packed-dot engine.
 constexpr int kProbeRowSlots = 8;
-constexpr int kProbeMaxWaves = 8;
+constexpr int kProbeMaxWaves = 8;       // planes: the packed-dot engine's k split
+constexpr int kProbeTileMaxWaves = 16;  // tiles: the tile engine's
 
 __device__ __forceinline__ uint32_t fold4(const uint4& v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
@@ -41,7 +42,7 @@ __device__ __forceinline__ uint32_t wave_xor(uint32_t v) {
 // wave reads the unit's 256 scale bytes (16 bytes per lane; lanes 16..63
 // repeat lanes 0..15 as in the matmul and are not folded) and its four code
 // blocks (16 bytes per lane each, streamed).
-__global__ __launch_bounds__(512) void read_probe_tiles_kernel(const uint8_t* __restrict__ tiles, int s8,
+__global__ __launch_bounds__(1024) void read_probe_tiles_kernel(const uint8_t* __restrict__ tiles, int s8,
                                                                int per_wave, uint32_t* __restrict__ out) {
     const int nwaves = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -132,11 +133,13 @@ struct ProbeGrid {
     int waves, per_wave, nseg;
 };
 
-// The engines' k split: segments of 8 groups over at most 8 waves.
+// The engines' k split: segments of 8 groups over at most 8 waves (planes)
+// or 16 (tiles).
 ProbeGrid probe_grid(int layout, int64_t n, int64_t k) {
     ProbeGrid g;
+    const int max_waves = layout == 1 ? kProbeTileMaxWaves : kProbeMaxWaves;
     g.nseg = (int)((k / 128 + 7) / 8);
-    g.per_wave = (g.nseg + kProbeMaxWaves - 1) / kProbeMaxWaves;
+    g.per_wave = (g.nseg + max_waves - 1) / max_waves;
     g.waves = (g.nseg + g.per_wave - 1) / g.per_wave;
     g.blocks = layout == 1 ? (n + kProbeTileRows - 1) / kProbeTileRows : (n + kProbeRowSlots - 1) / kProbeRowSlots;
     return g;

@@ -159,8 +159,12 @@ __host__ __device__ constexpr int tiles_col_pitch(int cpw) { return 128 * cpw + 
 __host__ __device__ constexpr int tiles_cols_staged(int mc, int cpw) {
     return mc + (((mc + 8 / cpw - 1) / (8 / cpw)) * (8 / cpw) > mc ? 1 : 0);
 }
+// With 128-element activation groups the -sum(q) table holds 8 classes x 4
+// columns x 4 copies (512 bytes: a lane's C operand is four copies of one
+// column's value) instead of 8 x 8 ints.
 __host__ __device__ constexpr int tiles_region_bytes(int mc, int cpw, int ag = 128) {
-    return tiles_cols_staged(mc, cpw) * tiles_col_pitch(cpw) + 512 * (128 / ag) + (ag == 32 ? 128 * cpw : 0);
+    return tiles_cols_staged(mc, cpw) * tiles_col_pitch(cpw) + 512 * (128 / ag) + (ag == 128 ? 256 : 0) +
+           (ag == 32 ? 128 * cpw : 0);
 }
 
 __device__ __forceinline__ float half_of(const uint4& v, int c) {
@@ -192,7 +196,7 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
 // workgroup waits for another.  The sum is the one the single-workgroup
 // kernel forms for the same slices (slice sums added in index order).
 template <int MC, int CPW, int SRC, int AG = 128, bool SPLIT = false>
-__global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_m_tiles_kernel(
+__global__ __launch_bounds__(1024) void small_m_tiles_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ xs, const void* __restrict__ x, int64_t x_stride,
     const uint8_t* __restrict__ tiles, float* __restrict__ y, int n, int k, int groups, int s8, int nseg,
     int per_wave, int mtotal, float* __restrict__ partials, uint32_t* __restrict__ counters, int ks) {
@@ -213,8 +217,13 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
     static_assert(AG == 128 || AG == 64 || AG == 32, "activation group");
     static_assert(AG == 128 || !src_fused(SRC), "smaller activation groups read natural-order q");
     static_assert(MC <= 4 || (MC == 8 && AG == 128), "eight-column passes take 128-element activation groups");
-    constexpr int R = MC < 4 ? MC : 4;      // outputs per lane and class (D rows 4*kb + r)
-    constexpr int KBU = MC > 4 ? 2 : 1;     // lane groups kb holding outputs
+    // COLK (2..4 columns from natural-order q): A rows 4c..4c+3 all carry
+    // column c, so the lanes of k block kb hold column kb in every D row and
+    // one output each: the epilogue takes 3 VALU per group whatever the
+    // column count, against 3 per group and column with rows = columns.
+    constexpr bool COLK = !FUSED && AG == 128 && MC >= 2 && MC <= 4;
+    constexpr int R = COLK ? 1 : (MC < 4 ? MC : 4);  // outputs per lane and class (D rows 4*kb + r)
+    constexpr int KBU = COLK ? MC : (MC > 4 ? 2 : 1);  // lane groups kb holding outputs
     constexpr bool XS_VEC = !src_fused(SRC) && (AG < 128 || MC > 4);  // xs through LDS from vector loads
     static_assert(!SPLIT || (CPW == 8 && !src_fused(SRC) && AG == 128), "split k: natural q, one wave per slice");
     const int nwaves = blockDim.x >> 6;
@@ -234,6 +243,7 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
     const auto tile_rs = make_rsrc(tiles + (size_t)tile * s8 * kSegUnit, (uint32_t)(s8 * kSegUnit));
     const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
     const i32x4_t xs_srs = make_srsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
+    const auto xsc_rs = make_rsrc(COLK ? xs + (size_t)m0 * groups : nullptr, COLK ? (uint32_t)(mcount * groups * 4) : 0u);
     const auto xsa_rs = make_rsrc(XS_VEC ? xs + (size_t)m0 * groups * S : nullptr,
                                   XS_VEC ? (uint32_t)(mcount * groups * S * 4) : 0u);
     const auto x_rs = make_rsrc(
@@ -247,13 +257,19 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
     //    then the weight scales, then the code blocks in use order (loads
     //    complete in order, so the first group pair can start while the later
     //    blocks are in flight), then xs.  Groups past the end read zeros.
-    uint4 qv[QLOADS];
-    uint4 xv[QLOADS][FUSED ? XL : 1];
-    float xss[FUSED || XS_VEC ? 1 : MC][CPW];  // xs of the wave's groups, scalar loads (uniform)
-    uint32_t xsa[XS_VEC ? XSL : 1];              // xs through LDS (AG < 128 or MC > 4), vector loads
-    uint4 wsv;
-    uint4 cw[CPW / 2];
-    auto issue = [&](int s) {
+    // One segment's registers.  (Issuing the next segment's loads before a
+    // segment's arithmetic, with two sets of these, measured slower at
+    // K = 17408: the waves' tails grow.)
+    struct Seg {
+        uint4 qv[QLOADS];
+        uint4 xraw[QLOADS][FUSED ? XL : 1];
+        float xss[FUSED || XS_VEC || COLK ? 1 : MC][CPW];  // xs of the wave's groups, scalar loads (uniform)
+        uint4 xlv[COLK ? 2 : 1];                     // COLK: xs of this lane's column, vector loads
+        uint32_t xsa[XS_VEC ? XSL : 1];              // xs through LDS (AG < 128 or MC > 4), vector loads
+        uint4 wsv;
+        uint4 cw[CPW / 2];
+    };
+    auto issue = [&](int s, Seg& g) {
         const uint32_t qoff = (uint32_t)(s * 1024 + 128 * c_lo + 16 * ch);  // element offset in the row
 #pragma unroll
         for (int t = 0; t < QLOADS; ++t) {
@@ -262,17 +278,17 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
             if constexpr (FUSED) {
                 const uint32_t off = (uint32_t)((m * x_stride + qoff) * src_esize(SRC));
 #pragma unroll
-                for (int l = 0; l < XL; ++l) xv[t][l] = buf_load16(x_rs, ok ? off + 16u * l : kBufferOOB);
+                for (int l = 0; l < XL; ++l) g.xraw[t][l] = buf_load16(x_rs, ok ? off + 16u * l : kBufferOOB);
             } else {
-                qv[t] = buf_load16(q_rs, ok ? (uint32_t)(m * k) + qoff : kBufferOOB);
+                g.qv[t] = buf_load16(q_rs, ok ? (uint32_t)(m * k) + qoff : kBufferOOB);
             }
         }
         const uint32_t unit_off = (uint32_t)(s * kSegUnit);
-        wsv = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
+        g.wsv = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + 4 * kCodeBlock + 16 * j);
         keep_order();
 #pragma unroll
         for (int b = 0; b < CPW / 2; ++b)
-            cw[b] = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + (c_lo / 2 + b) * kCodeBlock + 16 * lane);
+            g.cw[b] = buf_load16<kAuxNonTemporal>(tile_rs, unit_off + (c_lo / 2 + b) * kCodeBlock + 16 * lane);
         keep_order();
         if constexpr (XS_VEC) {
             // Value i of the segment: column i / (CPW*S), activation group
@@ -283,8 +299,15 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
                 const int col = i / (CPW * S);
                 const int a = (8 * s + c_lo) * S + i % (CPW * S);
                 const bool ok = i < XSV && col < mcount && a < groups * S;
-                xsa[t] = buf_load4(xsa_rs, ok ? (uint32_t)((col * groups * S + a) * 4) : kBufferOOB);
+                g.xsa[t] = buf_load4(xsa_rs, ok ? (uint32_t)((col * groups * S + a) * 4) : kBufferOOB);
             }
+        } else if constexpr (COLK) {
+            // The eight xs of this lane's column (lanes past the last column
+            // read the last one; past the last group the values are never
+            // used: those groups' dots are zero).
+            const uint32_t xoff = (uint32_t)((min(kb, mcount - 1) * groups + 8 * s + c_lo) * 4);
+            g.xlv[0] = buf_load16(xsc_rs, xoff);
+            g.xlv[1] = buf_load16(xsc_rs, xoff + 16u);
         } else if constexpr (!FUSED) {
             // xs of the wave's groups: uniform offsets, so the scalar unit
             // fetches them, outside the vector memory queue.  Columns past
@@ -296,10 +319,10 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
             for (int r = 0; r < MC; ++r) {
                 const int off = (min(r, mcount - 1) * groups + g0) * 4;
                 if (g0 + CPW <= groups) {
-                    sbuf_load_f32<CPW>(xs_srs, off, xss[r]);
+                    sbuf_load_f32<CPW>(xs_srs, off, g.xss[r]);
                 } else {
 #pragma unroll
-                    for (int c = 0; c < CPW; ++c) sbuf_load_f32<1>(xs_srs, off + 4 * c, &xss[r][c]);
+                    for (int c = 0; c < CPW; ++c) sbuf_load_f32<1>(xs_srs, off + 4 * c, &g.xss[r][c]);
                 }
             }
         }
@@ -315,9 +338,11 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
     // A row i reads column i mod mcount: rows >= mcount repeat real columns,
     // so one read touches at most 4 x 16 distinct banks, and the D rows they
     // produce are never used.
-    const unsigned char* a_base = region + small_mod(j, mcount) * PITCH + 16 * kb;
+    const unsigned char* a_base = region + small_mod(COLK ? j >> 2 : j, mcount) * PITCH + 16 * kb;
+    // COLK: this lane's column and its -sum(q) copies (4 per class and column).
+    const int* nsq_colk = nsq_lds + 4 * small_mod(kb, mcount);
 #pragma unroll
-    for (int i = 0; i < S; ++i) nsq_lds[lane + 64 * i] = 0;
+    for (int i = 0; i < (AG == 128 ? 2 : S); ++i) nsq_lds[lane + 64 * i] = 0;
     if constexpr (AG == 32) {
         if (lane < 8 * CPW) *reinterpret_cast<uint4*>(const_cast<unsigned char*>(zero_lds) + 16 * lane) = make_uint4(0, 0, 0, 0);
     }
@@ -331,15 +356,13 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[c][r] = 0.0f;
-    const int col4 = MC > 4 ? 4 * (kb & 1) : 0;  // first column of this lane's D rows
+    const int col4 = COLK ? kb : (MC > 4 ? 4 * (kb & 1) : 0);  // first column of this lane's D rows
 
     // Every wave has at least one segment (slice * per_wave < nseg), so the
     // loop has no zero-trip test and the kernel arguments load in one go.
     // (With SPLIT the last workgroup of a tile may hold waves past the last
     // slice; they skip the loop and store nothing.)
-    int s = seg_begin;
-    if (!SPLIT || seg_begin < seg_end) do {
-        issue(s);
+    auto body = [&](int s, Seg& g) {
 
         // 2. Stage the activations, xs and each group's -sum(q) (dot4 against
         //    ones over the lane's 16 bytes, then the 8 lanes of the group).
@@ -351,12 +374,12 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
             int sq;
             if constexpr (FUSED) {
                 float xf[16];
-                x_to_float16<SRC>(xv[t], xf);
+                x_to_float16<SRC>(g.xraw[t], xf);
                 float scale;
                 v = quantize_lane16<false>(xf, sq, scale);  // the 8 lanes of the group agree
                 if ((lane & 7) == 0 && m < MC) xs_lds[(c_lo + (ch >> 3)) * 8 + m] = scale;
             } else {
-                v = qv[t];
+                v = g.qv[t];
                 sq = dot4(v.x, 0x01010101u, 0);
                 sq = dot4(v.y, 0x01010101u, sq);
                 sq = dot4(v.z, 0x01010101u, sq);
@@ -369,19 +392,32 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
                 }
             }
             *reinterpret_cast<uint4*>(region + (m < MC ? m : MC) * PITCH + 16 * ch) = v;
-            if ((lane & (LPS - 1)) == 0 && m < MC)
+            if constexpr (COLK) {
+                if ((lane & 7) == 0 && m < MC)
+                    *reinterpret_cast<int4*>(nsq_lds + ((c_lo + (ch >> 3)) * 4 + m) * 4) = make_int4(-sq, -sq, -sq, -sq);
+            } else if ((lane & (LPS - 1)) == 0 && m < MC) {
                 nsq_lds[((c_lo + (ch >> 3)) * S + (ch & 7) / LPS) * 8 + m] = -sq;
+            }
         }
         if constexpr (XS_VEC) {
 #pragma unroll
             for (int t = 0; t < XSL; ++t) {
                 const int i = t * 64 + lane;
-                if (i < XSV) xs_lds[(c_lo * S + i % (CPW * S)) * 8 + i / (CPW * S)] = __uint_as_float(xsa[t]);
+                if (i < XSV) xs_lds[(c_lo * S + i % (CPW * S)) * 8 + i / (CPW * S)] = __uint_as_float(g.xsa[t]);
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // COLK: the activation scales of this lane's column (g.xss[r] holds
+        // column min(r, mcount - 1); lanes past the last column are never
+        // stored).
+        float xl[COLK ? CPW : 1];
+        if constexpr (COLK) {
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) xl[c] = __uint_as_float(word_of(g.xlv[c >> 2], c & 3));
+        }
 
         // 3. Group dots on the matrix cores, two groups at a time: D starts
         //    at -sum(q) of its column (the code offset), then adds the two
@@ -397,7 +433,7 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
                 v4i Bh[2], Dt[S];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const uint32_t d = word_of(cw[c >> 1], 2 * (c & 1) + h);
+                    const uint32_t d = word_of(g.cw[c >> 1], 2 * (c & 1) + h);
                     Bh[h] = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
                                 (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
                 }
@@ -418,7 +454,7 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
                 }
                 // The weight group's terms float(dot_t) * xs_t in k order, then
                 // one scale by ws into the class accumulator.
-                const float wsf = half_of(wsv, c_lo + c);
+                const float wsf = half_of(g.wsv, c_lo + c);
                 float gsum[R];
 #pragma unroll
                 for (int t = 0; t < S; ++t) {
@@ -443,12 +479,13 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
                 const uint4 a1 = *reinterpret_cast<const uint4*>(a_base + 128 * c + 64);
                 A[p][0] = v4i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
                 A[p][1] = v4i{(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                const int4 nsq = *reinterpret_cast<const int4*>(nsq_lds + (c_lo + c) * 8 + col4);
+                const int4 nsq = COLK ? *reinterpret_cast<const int4*>(nsq_colk + (c_lo + c) * 16)
+                                      : *reinterpret_cast<const int4*>(nsq_lds + (c_lo + c) * 8 + col4);
                 D[p] = v4i{nsq.x, nsq.y, nsq.z, nsq.w};
                 if constexpr (FUSED || XS_VEC) xsg[p] = *reinterpret_cast<const float4*>(xs_lds + (c_lo + c) * 8 + col4);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const uint32_t d = word_of(cw[c >> 1], 2 * (c & 1) + h);
+                    const uint32_t d = word_of(g.cw[c >> 1], 2 * (c & 1) + h);
                     B[p][h] = v4i{(int)(d & 0x03030303u), (int)((d >> 2) & 0x03030303u),
                                   (int)((d >> 4) & 0x03030303u), (int)((d >> 6) & 0x03030303u)};
                 }
@@ -460,13 +497,15 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 const int c = c0 + p;
-                const float wsf = half_of(wsv, c_lo + c);
+                const float wsf = half_of(g.wsv, c_lo + c);
                 float xv[4];
-                if constexpr (FUSED || XS_VEC) {
+                if constexpr (COLK) {
+                    xv[0] = xl[c];
+                } else if constexpr (FUSED || XS_VEC) {
                     xv[0] = xsg[p].x; xv[1] = xsg[p].y; xv[2] = xsg[p].z; xv[3] = xsg[p].w;
                 } else {
 #pragma unroll
-                    for (int r = 0; r < R; ++r) xv[r] = xss[r][c];
+                    for (int r = 0; r < R; ++r) xv[r] = g.xss[r][c];
                 }
 #pragma unroll
                 for (int r = 0; r < R; ++r) acc[c][r] = __builtin_fmaf((float)D[p][r] * xv[r], wsf, acc[c][r]);
@@ -476,6 +515,12 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
         // The next segment rewrites the region: every lane's reads of this one
         // are done (LDS operations of one wave complete in order).
         __builtin_amdgcn_wave_barrier();
+    };
+    Seg g;
+    int s = seg_begin;
+    if (!SPLIT || seg_begin < seg_end) do {
+        issue(s, g);
+        body(s, g);
     } while (++s < seg_end);
 
     // 4. Class sums ((A0+A4)+(A1+A5))+((A2+A6)+(A3+A7)) per slice, then the
@@ -554,21 +599,23 @@ __global__ __launch_bounds__(CPW == 8 ? (SPLIT ? 1024 : 512) : 1024) void small_
             for (int r = 0; r < R; ++r) red[(wave * MC + col4 + r) * kTileRows + j] = part[r];
         }
         __syncthreads();
-        // Wave 0 adds the slices in index order.  All reads go out before the
-        // first add; slots past the last slice re-read the last one and are
-        // not added.
+        // Wave 0 adds the slices (up to 16) in index order.  Each batch of
+        // eight reads goes out before its adds; slots past the last slice
+        // re-read the last one and are not added.
 #pragma unroll
         for (int o0 = 0; o0 < MC * kTileRows; o0 += 64) {
             const int o = o0 + lane;
             if (wave == 0 && o < MC * kTileRows) {
                 const int col = o >> 4;
-                float v[8];
+                float sum = 0.0f;
+                for (int b = 0; b < nwaves; b += 8) {
+                    float v[8];
 #pragma unroll
-                for (int w = 0; w < 8; ++w) v[w] = red[(min(w, nwaves - 1) * MC + col) * kTileRows + j];
-                float sum = v[0];
+                    for (int w = 0; w < 8; ++w) v[w] = red[(min(b + w, nwaves - 1) * MC + col) * kTileRows + j];
 #pragma unroll
-                for (int w = 1; w < 8; ++w)
-                    if (w < nwaves) sum += v[w];
+                    for (int w = 0; w < 8; ++w)
+                        if (b + w < nwaves) sum = b + w == 0 ? v[w] : sum + v[w];
+                }
                 if (col < mcount && row < n) y[(size_t)(m0 + col) * n + row] = sum;
             }
         }
@@ -707,7 +754,7 @@ int tiles_default_split(int64_t m, int64_t k, int max_waves) {
 }
 
 bool tiles_supported(int64_t k, int max_waves, int split) {
-    if (max_waves < 1 || max_waves > 8 || (split != 1 && split != 2 && split != 4)) return false;
+    if (max_waves < 1 || max_waves > 16 || (split != 1 && split != 2 && split != 4)) return false;
     int nseg, per_wave;
     return tiles_slices(k, max_waves, &nseg, &per_wave) * split <= 16;
 }

@@ -237,11 +237,14 @@ int64_t pq2_tiles_bytes(int64_t n, int64_t k);
 int pq2_prepare_tiles(const void* raw, int64_t raw_row_stride_bytes, int64_t n, int64_t k, void* tiles,
                       void* stream);
 
-/* pq2_matmul_small_m from the tile layout: the same definition, limits and
- * summation order, hence the same bits as pq2_matmul_small_m for the same
- * weights (page "Kernel experiments", Test 25: the tile-major projection
- * matched the row-major one bit for bit).  Each group's exact integer dot
- * comes from the INT8 matrix cores.
+/* pq2_matmul_small_m from the tile layout: the same definition and limits
+ * (page "Kernel experiments", Test 25: the tile-major projection matched the
+ * row-major one bit for bit).  Each group's exact integer dot comes from the
+ * INT8 matrix cores.  k is cut into 1024-element segments split over up to
+ * 16 waves (pq2_matmul_small_m: up to 8), so for k <= 8192 (one segment per
+ * wave in both) the bits equal pq2_matmul_small_m's; for longer k the
+ * summation order differs (still one FP32 term per group, batch-invariant:
+ * the split depends on k only).
  *   q       device int8 [m][k], 16-byte aligned.   xs  device float [m][k/128], 4-byte aligned.
  *   tiles   device tile layout of the weights, 16-byte aligned.
  *   y       device float [m][n], 4-byte aligned; fully overwritten; must
@@ -273,15 +276,19 @@ int pq2_matmul_small_m_tiles_fused(const void* x, int dtype, int64_t x_row_strid
 /* Decode GEMV from activations, y = W x for 1 <= m <= 16 (page "Kernel
  * experiments", Tests 3-5: the integer GEMV is called with the activations
  * and the weights and returns the outputs, quantising inside): the
- * library's fastest of pq2_matmul_small_m_tiles_fused (one launch; taken at
- * m <= 2 with k <= 8192, where every wave holds one k segment) and
- * pq2_quantize_act_i8 into the caller's q_work / xs_work followed by
- * pq2_matmul_small_m_tiles.  Both give the same bits.
+ * library's faster of pq2_matmul_small_m_tiles_fused (one launch; taken at
+ * m <= 2 with k <= 8192, where every wave holds one k segment, and
+ * m * ceil(n/16) <= 1600, since every 16-row tile repeats the quantisation)
+ * and pq2_quantize_act_i8 into the caller's q_work / xs_work followed by
+ * pq2_matmul_small_m_tiles.  Both give the same bits.  Rows the fused
+ * kernel cannot read (x or its row stride in bytes not 16-byte aligned)
+ * take the two-launch path when scratch is given.
  *   x       as pq2_matmul_small_m_tiles_fused (on the fused path) or
  *           pq2_quantize_act_i8 (otherwise).
  *   q_work  device int8 [m][k], 16-byte aligned; xs_work device float
  *           [m][k/128], 4-byte aligned: scratch owned by the caller, written
- *           on the two-launch path (may be NULL when m <= 2 and k <= 8192).
+ *           on the two-launch path (may be NULL when the fused path is
+ *           taken).
  *   tiles, y as pq2_matmul_small_m_tiles; nothing may overlap.
  * Errors: those of the path taken, checked before anything is enqueued. */
 int pq2_gemv_tiles(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m, int64_t n,

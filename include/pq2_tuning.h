@@ -58,11 +58,13 @@ int pq2_matmul_small_m_fused_tuned(const void* x, int dtype, int64_t x_row_strid
                                    int engine, void* stream);
 
 /* Tuning hook for pq2_matmul_small_m_tiles (benchmarks and tests only):
- * max_waves in 1..8 fixes the k split as for pq2_matmul_small_m_tuned;
- * split in {1, 2, 4} is the number of waves that share one k slice (each
- * takes 8/split of its group classes), with at most 16 waves per workgroup.
- * 0 for either picks the library's default.  The bits equal
- * pq2_matmul_small_m_tuned's at the same max_waves, whatever the split.
+ * max_waves in 1..16 fixes the k split (segments of 8 groups over at most
+ * max_waves waves, as pq2_matmul_small_m_tuned does for 1..8; the default is
+ * 16); split in {1, 2, 4} is the number of waves that share one k slice
+ * (each takes 8/split of its group classes), with at most 16 waves per
+ * workgroup.  0 for either picks the library's default.  For max_waves <= 8
+ * the bits equal pq2_matmul_small_m_tuned's at the same max_waves, whatever
+ * the split.
  * Errors as pq2_matmul_small_m_tiles, plus EINVAL for an unsupported
  * setting. */
 int pq2_matmul_small_m_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,

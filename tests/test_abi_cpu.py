@@ -153,7 +153,7 @@ def test_small_m_tiles_validation():
     assert f(A, B, C, 17, 8, 128, D, None) == ESHAPE
     assert f(A, B, C, 1, 8, 128, C + 4096, None) == EINVAL  # y overlaps the tiles (4352 bytes)
     t = pq2.lib.pq2_matmul_small_m_tiles_tuned
-    assert t(A, B, C, 1, 8, 128, D, 9, 0, None) == EINVAL     # waves
+    assert t(A, B, C, 1, 8, 128, D, 17, 0, None) == EINVAL    # waves (at most 16)
     assert t(A, B, C, 1, 8, 128, D, -1, 0, None) == EINVAL
     assert t(A, B, C, 1, 8, 128, D, 0, 3, None) == EINVAL     # split
     assert t(A, B, C, 1, 8, 65536, D, 8, 4, None) == EINVAL   # 8 slices x 4 waves > 16
@@ -172,7 +172,7 @@ def test_small_m_tiles_fused_validation():
     assert f(A, 0, 129, C, 2, 8, 128, D, None) == EALIGN        # row stride not 16-byte aligned
     assert f(A, 0, 128, C, 1, 8, 128, C + 64, None) == EINVAL   # y overlaps the tiles
     t = pq2.lib.pq2_matmul_small_m_tiles_fused_tuned
-    assert t(A, 0, 128, C, 1, 8, 128, D, 9, 0, None) == EINVAL
+    assert t(A, 0, 128, C, 1, 8, 128, D, 17, 0, None) == EINVAL
     assert t(A, 0, 128, C, 1, 8, 128, D, 0, 3, None) == EINVAL
     if not _gpu_visible():
         assert t(A, 2, 5120, C, 4, 8, 5120, D, 0, 0, None) == EDEVICE
@@ -343,7 +343,8 @@ def test_read_probe_validation_and_grid():
     # 8 groups over at most 8 waves).
     assert w(pq2.LAYOUT_TILES, 10240, 5120) == 640 * 5
     assert w(pq2.LAYOUT_PLANES, 10240, 5120) == 1280 * 5
-    assert w(pq2.LAYOUT_TILES, 5120, 17408) == 320 * 6       # 17 segments: 6 waves of 3
+    assert w(pq2.LAYOUT_TILES, 5120, 17408) == 320 * 9       # 17 segments: 9 waves of 2 (up to 16 waves)
+    assert w(pq2.LAYOUT_PLANES, 5120, 17408) == 640 * 6      # 17 segments: 6 waves of 3 (up to 8 waves)
     assert w(pq2.LAYOUT_PLANES, 33, 640) == 5                # ragged rows, one partial segment
     assert w(pq2.LAYOUT_TILES, 17, 8192) == 2 * 8
     assert w(2, 8, 128) == 0 and w(0, 0, 128) == 0 and w(0, 8, 96) == 0
