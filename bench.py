@@ -102,6 +102,21 @@ def stored_summary(name, digest):
     return vals if vals.get("kernel_source_digest") == digest else None
 
 
+def stored_trace(digest):
+    """Indented key/value lines of the committed kernel-trace summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "small_m_tiles_kernel_trace.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if line.startswith("    ") and len(parts) == 2:
+                vals[parts[0]] = parts[1]
+    return vals if vals.get("kernel_source_digest") == digest else None
+
+
 class Graph:
     """A captured HIP graph of a callable, replayed on the capture stream."""
 
@@ -231,6 +246,9 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
     achieved = tot_b / (tot_us * 1e-6) / 1e9
     mean_us = tot_us / len(per_m)
     traffic = stored_summary(f"small_m_tiles_{cfg.name}_traffic.txt", digest)
+    trace = stored_trace(digest)
+    traced_us = float(trace[f"traced_mean_launch_us_{cfg.name}"]) if trace and \
+        f"traced_mean_launch_us_{cfg.name}" in trace else None
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
@@ -245,6 +263,11 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
         "kernel_source_digest": digest,
         "stream_read_us": ceilings["stream_read_us"],
         "mean_launch_vs_stream_read": round(mean_us / stream_us, 3),
+        # The same kernel's mean duration per dispatch under rocprofv3
+        # --kernel-trace (committed summary, same kernel source), and the
+        # fraction of 8 TB/s it implies.
+        "traced_mean_launch_us": traced_us,
+        "traced_frac": round(tot_b / len(per_m) / (traced_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4) if traced_us else None,
         "stream_read_frac": round(cfg.tb / (stream_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4),
     }
     return per_m, ceilings, roofline
@@ -318,6 +341,32 @@ def launch_floor_and_stream_fit(torch, pq2, dev, stream, reps):
     log(f"[bench] launch floor (empty kernel, graph): {floor}; stream read fit t = {t0:.3f} us + B / "
         f"{fit['bw_GBps']:.0f} GB/s over {', '.join(str(b >> 20) for b, _ in pts)} MiB")
     return floor, fit
+
+
+def stream_sweep(torch, pq2, dev, stream, reps):
+    """The stream read probe over 4..192 MiB and 256..8192 workgroups (four
+    waves each), graphs of back-to-back launches over a rotating 1.5 GiB
+    buffer, plus the empty-kernel floor: µs per launch."""
+    buf = torch.empty((3 << 29,), dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    out = torch.empty((pq2.pq2_stream_probe_words(8192),), dtype=torch.int32, device=dev)
+    table = []
+    for mb in STREAM_FIT_MB:
+        nb = mb << 20
+        copies = buf.numel() // nb
+        row = {"MiB": mb}
+        for wg in (256, 512, 1024, 2048, 4096, 8192):
+            us = per_call_us(torch, stream, lambda nb=nb, copies=copies, wg=wg: [pq2.pq2_stream_probe(
+                buf[c * nb:(c + 1) * nb], nb, wg, out, False, 0x7FFFFFFF, stream=stream) for c in range(copies)],
+                copies, reps)
+            row[str(wg)] = round(us, 3)
+        table.append(row)
+        log(f"[bench] stream sweep {row}")
+    floor = {f"{wg}x{w}": round(per_call_us(torch, stream, lambda wg=wg, w=w: [
+        pq2.pq2_empty_probe(wg, w, stream=stream) for _ in range(200)], 200, reps), 3)
+        for wg, w in ((1, 1), (256, 1), (1088, 5), (2048, 4), (8192, 4))}
+    log(f"[bench] empty-kernel floor {floor}")
+    return {"stream_read_us": table, "launch_floor_us": floor}
 
 
 def cpu_baseline(raw, x, n, k, ms, budget_s):
@@ -396,6 +445,11 @@ def main():
     ap.add_argument("--reps", type=int, default=20, help="graph replays per timing")
     ap.add_argument("--configs", default="up,qkv,down", help="decode shapes to measure (headline first)")
     ap.add_argument("--variants", action="store_true", help="also time the other decode paths at the QKV shape")
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="only sweep the stream read probe over sizes and grid widths and print the table")
+    ap.add_argument("--only", default=None,
+                    help="profiling runs: measure this one decode shape (per-call timings and ceilings; "
+                         "no headline step, prefill, floor or CPU baseline) and print its JSON")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -413,6 +467,16 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream()
     digest = source_digest()
+    if args.stream_sweep:
+        print(json.dumps(stream_sweep(torch, pq2, dev, stream, args.reps)), flush=True)
+        return
+    if args.only:
+        cfg = Config(torch, pq2, workloads, args.only, dev, stream)
+        per_m, ceil, roof = measure_config(torch, pq2, cfg, stream, args.reps, digest)
+        if args.calibrate:
+            calibration_copy(torch, dev, stream)
+        print(json.dumps({"only": args.only, "us_per_call": per_m, "ceilings": ceil, "roofline": roof}), flush=True)
+        return
     names = [c for c in args.configs.split(",") if c]
     if HEADLINE not in names:
         names.insert(0, HEADLINE)

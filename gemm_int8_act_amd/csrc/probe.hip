@@ -105,8 +105,9 @@ __global__ __launch_bounds__(512) void read_probe_planes_kernel(const uint8_t* _
 // per lane; chunks past the end read zero (buffer range check).  Each wave
 // folds what it read with XOR.  store_all = 1 writes every wave's fold (the
 // XOR of all words is the XOR of the buffer's dwords); store_all = 0 writes
-// a wave's fold only if it equals `sentinel`, so a timed run is a pure read
-// (any output store adds the latency of one store to the end of a launch).
+// only from a lane whose own fold equals `sentinel` (practically never), so
+// a timed run is a pure read (any output store adds the latency of one store
+// to the end of a launch).
 __global__ __launch_bounds__(256) void stream_probe_kernel(const uint8_t* __restrict__ buf, uint32_t bytes, int iters,
                                                            int store_all, uint32_t sentinel,
                                                            uint32_t* __restrict__ out) {
@@ -119,8 +120,12 @@ __global__ __launch_bounds__(256) void stream_probe_kernel(const uint8_t* __rest
     uint32_t f = 0;
     uint32_t off = wave_id * 1024u + 16u * lane;
     for (int i = 0; i < iters; ++i, off += stride) f ^= fold4(buf_load16<kAuxNonTemporal>(rs, off < bytes ? off : kBufferOOB));
-    f = wave_xor(f);
-    if (lane == 0 && (store_all || f == sentinel)) out[wave_id] = f;
+    if (store_all) {
+        f = wave_xor(f);
+        if (lane == 0) out[wave_id] = f;
+    } else if (f == sentinel) {
+        out[wave_id] = f;  // the timed mode: a lane's own fold, practically never equal
+    }
 }
 
 // An empty kernel: the launch floor of a graph of back-to-back launches.

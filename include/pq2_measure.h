@@ -48,12 +48,13 @@ int64_t pq2_read_probe_words(int layout, int64_t n, int64_t k);
  * non-temporal load per lane, and fold what they read with XOR.  Reads past
  * the end return zero.
  *   buf        device, bytes >= 16, a multiple of 16 and < 2^31; 16-byte aligned.
- *   workgroups 1..65536 (2048 is the fastest measured for 8-200 MB).
+ *   workgroups 1..65536 (512-4096 are the fastest measured for 8-200 MB).
  *   store_all  nonzero: every wave writes its fold to out[wave], and the XOR
  *              of all pq2_stream_probe_words(workgroups) words equals the XOR
- *              of the buffer's dwords.  Zero: a wave writes its fold only if
- *              it equals `sentinel` (a timed run is then a pure read; any
- *              output store adds the latency of one store to the launch).
+ *              of the buffer's dwords.  Zero: a lane writes its own fold to
+ *              out[wave] only if it equals `sentinel` (practically never: a
+ *              timed run is then a pure read; any output store adds the
+ *              latency of one store to the launch).
  *   out        device uint32 [pq2_stream_probe_words(workgroups)], 4-byte
  *              aligned; must not overlap buf.
  * Errors: EINVAL (null, overlap), ESHAPE (bytes, workgroups), EALIGN,
