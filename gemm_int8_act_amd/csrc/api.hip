@@ -505,7 +505,7 @@ int pq2_matmul_small_m_fused(const void* x, int dtype, int64_t x_row_stride_elem
 int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
                              int64_t k, float* y, int tile, void* stream) {
     if (int rc = check_matmul_args(q, xs, planes, m, n, k, y, kMaxPrefillM)) return rc;
-    if (tile < 0 || tile > 4) return PQ2_EINVAL;
+    if (tile < 0 || tile > 5) return PQ2_EINVAL;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_prefill(q, xs, static_cast<const uint8_t*>(planes), m, n, k, y, tile, false,
                                              (hipStream_t)stream));
@@ -514,7 +514,7 @@ int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* plane
 int pq2_matmul_prefill_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
                                    int64_t k, float* y, int tile, void* stream) {
     if (int rc = check_matmul_args(q, xs, tiles, m, n, k, y, kMaxPrefillM, true)) return rc;
-    if (tile < 0 || tile > 4) return PQ2_EINVAL;
+    if (tile < 0 || tile > 5) return PQ2_EINVAL;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_prefill_tiles(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, y, tile,
                                                    (hipStream_t)stream));
@@ -543,7 +543,7 @@ int pq2_matmul_prefill(const int8_t* q, const float* xs, const void* planes, int
 int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const void* planes, int64_t m, int64_t n,
                                     int64_t k, float* y, int tile, void* stream) {
     if (int rc = check_matmul_args(qp, xs, planes, m, n, k, y, kMaxPrefillM)) return rc;
-    if (tile < 0 || tile > 4) return PQ2_EINVAL;
+    if (tile < 0 || tile > 5) return PQ2_EINVAL;
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_prefill(qp, xs, static_cast<const uint8_t*>(planes), m, n, k, y, tile, true,
                                              (hipStream_t)stream));

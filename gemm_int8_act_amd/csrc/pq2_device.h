@@ -136,6 +136,14 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same with a uniform byte offset in the instruction's scalar operand
+// (no per-lane add for an offset shared by the wave).
+template <int AUX = 0>
+__device__ __forceinline__ uint4 buf_load16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, AUX);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
@@ -143,6 +151,11 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ uint2 buf_load8s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0);
     return make_uint2(v.x, v.y);
 }
 

@@ -10,8 +10,9 @@
 //
 // Design:
 //  * Workgroup tile BM x BN (128x128, 64x128, 128x64 or 64x64, chosen so
-//    the grid fills the chip), 4 waves as 2 x 2, each wave (BM/2) x (BN/2)
-//    made of 32 x 32 tiles of v_mfma_i32_32x32x32_i8.  One group (k = 128)
+//    the grid fills the chip), WM x 2 waves (WM = 2, or 4 for the 128x128
+//    tile on eight waves), each wave (BM/WM) x (BN/2) made of 32 x 32 tiles
+//    of v_mfma_i32_32x32x32_i8.  One group (k = 128)
 //    = four MFMA k-steps of 32.
 //  * Activations come in natural order (transposed while staged) or already
 //    in plane order (pq2_quantize_act_i8_planes; copied as they are).
@@ -67,18 +68,21 @@ __device__ __forceinline__ int swz(int i, int t) { return i * 8 + (t ^ ((i >> 1)
 // section C, Tests 8 and 9: each activation group's k-steps form their own
 // INT32 chain; a weight group's terms float(dot) * xs are summed in k order,
 // then scaled by its ws into acc.
-template <int BM, int BN, bool PLANE_A, bool TILES, int AG = 128>
-__global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__ q,
+template <int BM, int BN, bool PLANE_A, bool TILES, int AG = 128, int WM = 2>
+__global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restrict__ q,
                                                       const float* __restrict__ xs,
                                                       const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
                                                       float* __restrict__ y, int m, int n, int k,
                                                       int groups) {
 #pragma clang fp contract(off)
-    constexpr int MT = BM / 64;          // 32-row tiles per wave
+    constexpr int NTH = WM * 128;        // threads: WM x 2 waves
+    constexpr int MT = BM / (32 * WM);   // 32-row tiles per wave
     constexpr int NT = BN / 64;          // 32-column tiles per wave
-    constexpr int AQ = BM * 8 / 256;     // A quads staged per thread
+    constexpr int AQ = BM * 8 / NTH;     // A quads staged per thread
     constexpr int BI = BN * 2;           // B items (row, half) per group
+    static_assert(MT >= 1 && AQ >= 1 && BI <= NTH && BM + BN <= NTH, "tile / wave split");
+    static_assert(!TILES || BN * 4 >= NTH, "tile layout: every thread stages a B item");
     constexpr int S = 128 / AG;          // activation groups per weight group
     constexpr int KS = 4 / S;            // k-steps per activation group
     static_assert(AG == 128 || (TILES && (AG == 64 || AG == 32)), "smaller activation groups: tile layout only");
@@ -114,23 +118,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     uint32_t a_off[AQ];
 #pragma unroll
     for (int p = 0; p < AQ; ++p) {
-        const int it = tid + 256 * p;
+        const int it = tid + NTH * p;
         a_off[p] = (uint32_t)((it >> 3) * k + (it & 7) * 16);
     }
     const uint32_t b_off = tid < BI ? (uint32_t)((tid >> 1) * k4 + (tid & 1) * 16) : kBufferOOB;
-    // Tile layout: items it = tid + 256 p (p < BN * 4 / 256) take row it >> 2, k-block it & 3.
-    constexpr int TI = TILES ? BN * 4 / 256 : 1;
+    // Tile layout: items it = tid + NTH p (p < BN * 4 / NTH) take row it >> 2, k-block it & 3.
+    constexpr int TI = TILES ? BN * 4 / NTH : 1;
     uint32_t tb_off[TI];
 #pragma unroll
     for (int p = 0; p < TI; ++p) {
-        const int it = tid + 256 * p;
+        const int it = tid + NTH * p;
         const int row = it >> 2, kbb = it & 3;
         tb_off[p] = (uint32_t)((row >> 4) * s8 * 4352 + 16 * ((row & 15) + 16 * kbb));
     }
     const bool s_is_x = tid < BM;
-    const bool s_is_w = tid >= 256 - BN;
+    const bool s_is_w = tid >= NTH - BN;
     const uint32_t s_off = s_is_x ? (uint32_t)(tid * groups * S * 4)
-                                  : (s_is_w ? (uint32_t)((tid - (256 - BN)) * groups * 2) : kBufferOOB);
+                                  : (s_is_w ? (uint32_t)((tid - (NTH - BN)) * groups * 2) : kBufferOOB);
 
     uint4 areg[AQ];
     uint4 breg;
@@ -140,21 +144,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 
     auto load_stage = [&](int g) {
 #pragma unroll
-        for (int p = 0; p < AQ; ++p) areg[p] = buf_load16(q_rs, a_off[p] + (uint32_t)g * 128u);
+        for (int p = 0; p < AQ; ++p) areg[p] = buf_load16s(q_rs, a_off[p], (uint32_t)g * 128u);
         if constexpr (TILES) {
             // Unit (tile, g / 8), block (g % 8) / 2, dwords 2 (g % 2) and 2 (g % 2) + 1.
             const uint32_t goff = (uint32_t)((g >> 3) * 4352 + ((g & 7) >> 1) * 1024 + (g & 1) * 8);
 #pragma unroll
-            for (int p = 0; p < TI; ++p) treg[p] = buf_load8(c_rs, tb_off[p] + goff);
+            for (int p = 0; p < TI; ++p) treg[p] = buf_load8s(c_rs, tb_off[p], goff);
         } else {
-            breg = buf_load16(c_rs, b_off == kBufferOOB ? kBufferOOB : b_off + (uint32_t)g * 32u);
+            breg = buf_load16s(c_rs, b_off, (uint32_t)g * 32u);
         }
         if (s_is_x) {
 #pragma unroll
             for (int t = 0; t < S; ++t) xreg[t] = buf_load4(x_rs, s_off + (uint32_t)(g * S + t) * 4u);
         } else if constexpr (TILES)
-            sreg = buf_load2(c_rs, s_is_w ? (uint32_t)((((tid - (256 - BN)) >> 4) * s8 + (g >> 3)) * 4352 + 4096 +
-                                                       16 * ((tid - (256 - BN)) & 15) + 2 * (g & 7))
+            sreg = buf_load2(c_rs, s_is_w ? (uint32_t)((((tid - (NTH - BN)) >> 4) * s8 + (g >> 3)) * 4352 + 4096 +
+                                                       16 * ((tid - (NTH - BN)) & 15) + 2 * (g & 7))
                                           : kBufferOOB);
         else
             sreg = buf_load2(s_rs, s_off == kBufferOOB ? kBufferOOB : s_off + (uint32_t)g * 2u);
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
     int a_slot[AQ];
 #pragma unroll
     for (int p = 0; p < AQ; ++p) {
-        const int it = tid + 256 * p;
+        const int it = tid + NTH * p;
         a_slot[p] = swz(it >> 3, it & 7);
     }
     int b_slot[4];
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
         if constexpr (TILES) {
 #pragma unroll
             for (int p = 0; p < TI; ++p) {
-                const int it = tid + 256 * p;
+                const int it = tid + NTH * p;
                 const int row = it >> 2, kbb = it & 3;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -197,14 +201,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
         if (s_is_x) {
 #pragma unroll
             for (int t = 0; t < S; ++t) xsS[buf][t][tid] = __uint_as_float(xreg[t]);
-        } else if (s_is_w) wsS[buf][tid - (256 - BN)] = __half2float(__ushort_as_half((unsigned short)sreg));
+        } else if (s_is_w) wsS[buf][tid - (NTH - BN)] = __half2float(__ushort_as_half((unsigned short)sreg));
     };
     // Fragment read slots per k-step (fixed for the whole kernel).
     int af_slot[4][MT], bf_slot[4][NT];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) af_slot[kk][mt] = swz(wm * (BM / 2) + mt * 32 + l32, 2 * kk + hi);
+        for (int mt = 0; mt < MT; ++mt) af_slot[kk][mt] = swz(wm * (BM / WM) + mt * 32 + l32, 2 * kk + hi);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) bf_slot[kk][nt] = swz(wn * (BN / 2) + nt * 32 + l32, 2 * kk + hi);
     }
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
                     const float4 xv =
-                        *reinterpret_cast<const float4*>(&xsS[buf][t][wm * (BM / 2) + mt * 32 + rb * 8 + hi * 4]);
+                        *reinterpret_cast<const float4*>(&xsS[buf][t][wm * (BM / WM) + mt * 32 + rb * 8 + hi * 4]);
                     const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
             const int col = nb + wn * (BN / 2) + nt * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = mb + wm * (BM / 2) + mt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                const int row = mb + wm * (BM / WM) + mt * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
                 if (row < m && col < n) y[(size_t)row * n + col] = acc[mt][nt][r];
             }
         }
@@ -326,14 +330,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const int8_t* __restrict__
 
 namespace {
 
-template <int BM, int BN, bool PLANE_A, bool TILES, int AG = 128>
+template <int BM, int BN, bool PLANE_A, bool TILES, int AG = 128, int WM = 2>
 hipError_t launch_tile(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m, int64_t n,
                        int64_t k, float* y, hipStream_t stream) {
     const uint16_t* scales = TILES ? nullptr : reinterpret_cast<const uint16_t*>(planes + n * (k / 4));
     const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
     clear_stale_error();
-    hipLaunchKernelGGL((prefill_kernel<BM, BN, PLANE_A, TILES, AG>), grid, dim3(256), 0, stream, q, xs, planes, scales,
-                       y, (int)m, (int)n, (int)k, (int)(k / 128));
+    hipLaunchKernelGGL((prefill_kernel<BM, BN, PLANE_A, TILES, AG, WM>), grid, dim3(WM * 128), 0, stream, q, xs, planes,
+                       scales, y, (int)m, (int)n, (int)k, (int)(k / 128));
     return hipGetLastError();
 }
 
@@ -345,6 +349,7 @@ hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* plan
         case 2: return launch_tile<64, 128, PLANE_A, TILES, AG>(q, xs, planes, m, n, k, y, stream);
         case 3: return launch_tile<64, 64, PLANE_A, TILES, AG>(q, xs, planes, m, n, k, y, stream);
         case 4: return launch_tile<128, 64, PLANE_A, TILES, AG>(q, xs, planes, m, n, k, y, stream);
+        case 5: return launch_tile<128, 128, PLANE_A, TILES, AG, 4>(q, xs, planes, m, n, k, y, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -354,12 +359,16 @@ hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* plan
 // Tile choice: 64x128 when its grid still gives every CU two workgroups
 // (512 on the 256-CU part), else 64x64 -- for either activation order (the
 // 128x64 tile, which shares each code decode among more rows, measured no
-// better).  The 128x128 tile needs more than 256 registers per lane (one
-// wave per SIMD); it stays available through the tuning entry points.
+// better).  From 2048 64x128 workgroups on (FFN up at M = 1024) the
+// 128x128 tile on eight waves, which decodes each code dword once for 128
+// rows, is 3% faster (164.3 against 169.9 us); it loses at smaller grids
+// (up M = 512: 105.9 against 96.6 us).  The 128x128 tile on four waves
+// needs more than 256 registers per lane (one wave per SIMD); it stays
+// available through the tuning entry points.
 int default_prefill_tile(int64_t m, int64_t n, bool plane_a) {
     (void)plane_a;
     const int64_t wgs = ((n + 127) / 128) * ((m + 63) / 64);
-    return wgs >= 512 ? 2 : 3;
+    return wgs >= 2048 ? 5 : wgs >= 512 ? 2 : 3;
 }
 
 hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,

@@ -81,7 +81,8 @@ int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row
 
 /* Tuning hook for the prefill matmul (benchmarks and tests only; same
  * arguments and result as pq2_matmul_prefill): tile 1 = 128x128, 2 = 64x128,
- * 3 = 64x64, 4 = 128x64 outputs per workgroup, 0 = the library's choice.
+ * 3 = 64x64, 4 = 128x64 outputs per workgroup of four waves, 5 = 128x128 on
+ * eight waves, 0 = the library's choice.
  * The result does not depend on the tile.  Errors as pq2_matmul_prefill,
  * plus EINVAL for an unknown tile. */
 int pq2_matmul_prefill_tuned(const int8_t* q, const float* xs, const void* planes, int64_t m, int64_t n,
@@ -94,7 +95,7 @@ int pq2_matmul_prefill_planes_tuned(const int8_t* qp, const float* xs, const voi
 
 /* Tuning hook for pq2_matmul_prefill_tiles: tile as for
  * pq2_matmul_prefill_tuned (0 = the library's choice), same bits.  Errors as
- * pq2_matmul_prefill_tiles, plus EINVAL for tile outside 0..4. */
+ * pq2_matmul_prefill_tiles, plus EINVAL for tile outside 0..5. */
 int pq2_matmul_prefill_tiles_tuned(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n,
                                    int64_t k, float* y, int tile, void* stream);
 

@@ -232,9 +232,9 @@ def test_activation_group_validation():
 
 def test_prefill_tile_validation():
     t = pq2.lib.pq2_matmul_prefill_tuned
-    assert t(A, B, C, 1, 8, 128, D, 5, None) == EINVAL
-    assert pq2.lib.pq2_matmul_prefill_planes_tuned(A, B, C, 1, 8, 128, D, 5, None) == EINVAL
-    assert pq2.lib.pq2_matmul_prefill_tiles_tuned(A, B, C, 1, 8, 128, D, 5, None) == EINVAL
+    assert t(A, B, C, 1, 8, 128, D, 6, None) == EINVAL
+    assert pq2.lib.pq2_matmul_prefill_planes_tuned(A, B, C, 1, 8, 128, D, 6, None) == EINVAL
+    assert pq2.lib.pq2_matmul_prefill_tiles_tuned(A, B, C, 1, 8, 128, D, 6, None) == EINVAL
     assert pq2.lib.pq2_matmul_prefill_planes(A + 8, B, C, 1, 8, 128, D, None) == EALIGN
     assert t(A, B, C, 1, 8, 128, D, -1, None) == EINVAL
     assert t(A, B, C, 0, 8, 128, D, 1, None) == ESHAPE

@@ -481,7 +481,7 @@ def test_prefill_workloads_sampled(name):
             assert_within(y_first[0, ni1], y1_ref, b1, f"{name} m=1")
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
 def test_prefill_tiles(tile):
     """Every workgroup tile, from natural- and plane-order activations, gives
     outputs within the bound, with ragged row, column and group tails, and
