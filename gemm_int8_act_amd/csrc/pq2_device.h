@@ -92,15 +92,6 @@ __device__ __forceinline__ uint4 to_plane_order(uint4 Q) {
 }
 
 // ---------------------------------------------------------------- decodes
-// add/XOR expansion of plane s of a code dword: each byte's 2-bit field c
-// (0..3) becomes the signed byte c-1.  c + 0x7F lies in 0x7F..0x82, so no
-// byte carries into the next, and flipping bit 7 maps 127,128,129,130 to
-// -1,0,+1,+2 as two's-complement bytes.
-template <int S>
-__device__ __forceinline__ uint32_t expand_plane(uint32_t d) {
-    return (((d >> (2 * S)) & 0x03030303u) + 0x7F7F7F7Fu) ^ 0x80808080u;
-}
-
 // Masked planes: byte values c * 4^S for S = 0,1,2 and, for S = 3, the field
 // shifted down by two (c * 16) so every byte stays below 128.
 template <int S>
@@ -111,17 +102,11 @@ __device__ __forceinline__ uint32_t mask_plane(uint32_t d) {
     return (d >> 2) & 0x30303030u;
 }
 
-// 16-byte load with the non-temporal hint (streamed once, no reuse).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_nt(const uint4* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // ---------------------------------------------------------------- buffer loads
 // Raw buffer resources (gfx9 descriptor, stride 0): a load whose byte offset
 // lies at or beyond num_records returns zero instead of touching memory, so
 // padded rows, groups and columns need no branch around their loads.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr uint32_t kBufferOOB = 0x80000000u;  // an offset past any record count used here
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kAuxNonTemporal = 2;          // cache-policy bit: streamed, not reused

@@ -4,11 +4,12 @@
 // Quantiser (page "Baseline and the integer breakthrough", "Calculate with
 // small integers" step 1; page "Kernel experiments: recorded evidence",
 // Test 6): per group of 128 elements, scale = max|x| / 127 as one correctly
-// rounded FP32 division, each element divided (correctly rounded) by the
-// scale, or by 1 for an all-zero group, rounded half to even, clamped to
-// +-127.  The kernel uses exactly those IEEE operations (hipcc keeps FP32
-// division correctly rounded and lowers rintf to v_rndne_f32; FP32
-// subnormals are preserved), so q and xs are bit-identical to the definition.
+// rounded FP32 division, each element divided by the scale (or by 1 for an
+// all-zero group) with the FP32 quotient correctly rounded, rounded half to
+// even, clamped to +-127.  The scale is that one IEEE division; each
+// element's quotient is the double product x * fl64(1 / divisor) rounded to
+// FP32, which equals the IEEE quotient (the argument is beside the code), so
+// q and xs are bit-identical to the definition, subnormal scales included.
 //
 // Geometry: 16 lanes (one DPP row) per group, 8 consecutive elements per lane
 // (one 16-byte load for 2-byte types), 16 groups per 256-thread workgroup.

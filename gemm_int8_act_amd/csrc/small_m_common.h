@@ -32,17 +32,14 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t 
 // and scale (max|x| / 127, correctly rounded).  The codes equal the
 // definition q = clamp(rint(RN(x / d)), +-127), d = scale or 1 for an
 // all-zero group, bit for bit:
-//  * r = 1/d from the hardware reciprocal refined by one Newton step lies
-//    within 2^-22 (relative) of 1/d, so t = RN(x * r) differs from x / d by
-//    at most 127.0001 * (2^-22 + 2^-24) and from RN(x / d) by less than
-//    4.3e-5 < 2^-14 whenever d is normal (|x / d| <= 127 * (1 + 2^-23), and
-//    half an ulp of RN(x / d) below 128 is 2^-18);
-//  * so if t lies at least 2^-14 from every half-integer, rint(t) is
-//    rint(RN(x / d)).  Adding 1.5 * 2^23 rounds t to that integer in the
-//    low mantissa bits, whose low byte is the two's-complement code, and
-//    |t| < 127.5 makes the clamp a no-op;
-//  * otherwise (a near-tie in any of the lane's 16 elements, or d
-//    subnormal) the lane repeats the definition with IEEE divisions.
+//  * RN(x / d) is computed as the double product x * fl64(1 / d) rounded to
+//    fp32.  The quotient of two fp32 values is either an fp32 value or at
+//    least 2^-49 (relative) away from every fp32 rounding midpoint (24-bit
+//    significands, 25-bit midpoints), and the product is within 2^-52 of
+//    the quotient, so both round to the same fp32 value, for subnormal d too;
+//  * the clamp to +-127 comes before the rounding: adding 1.5 * 2^23 rounds
+//    the clamped value half to even in the low mantissa bits, whose low byte
+//    is the two's-complement code.
 template <bool PLANE = true>
 __device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum, float& scale) {
 #pragma clang fp contract(off)

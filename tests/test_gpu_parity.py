@@ -735,10 +735,10 @@ def probe_weights(k):
 
 def probe_activations(dtype, k):
     """16 columns: random groups of several distributions and magnitudes, and
-    groups built to reach the exact-division fallback of the fused
-    quantiser: exact rounding ties (power-of-two scales), a zero group,
-    subnormal scales (with f32 input also a scale that makes the clamp bind),
-    repeated +-amax, and huge values."""
+    groups built for the edge cases of the quantiser's quotient: exact
+    rounding ties (power-of-two scales), a zero group, subnormal scales (with
+    f32 input also a scale that makes the clamp bind), repeated +-amax, and
+    huge values."""
     m = 16
     cols = [workloads.make_activations(1, k, 300 + c, "normal+outliers" if c % 2 else "laplace").float()[0]
             * (10.0 ** (c % 5 - 2)) for c in range(m)]
@@ -762,7 +762,8 @@ def probe_activations(dtype, k):
 def test_fused_quantiser_codes_exact(dtype):
     """Every code and scale of the fused quantiser, read back through
     single-weight rows: y[m][r] must equal the oracle's q * xs bit for bit
-    (fast path, near-tie fallback, subnormal scales and the clamp)."""
+    (exact ties and near-ties of the quotient, subnormal scales and the
+    clamp)."""
     k = 2048
     announce(f"fused quantiser probe dtype={dtype} k={k}")
     x = probe_activations(dtype, k)
