@@ -62,6 +62,7 @@ ROTATION_BYTES = 1 << 30
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for M=1..4 packed-ternary matmul"
 HEADLINE = "up"
 DECODE_MS = (1, 2, 3, 4)
+SPLITK_MIN_K = 8192      # split k is timed beside the tile matmul above this k (down)
 STREAM_WORKGROUPS = 2048
 STREAM_FIT_MB = (4, 8, 16, 24, 48, 96, 192)
 
@@ -216,8 +217,24 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
             "gemv_call_GBps": round(b / (call_us * 1e-6) / 1e9, 1),
             "matmul_bytes": b,
         }
+        if k > SPLITK_MIN_K:
+            # Cross-workgroup split k (one 1024-element segment per wave, the
+            # last workgroup of a tile adds the slices in index order): a
+            # different summation order, so compared within a relative 1e-4.
+            dev = cfg.x.device
+            part = torch.empty((pq2.pq2_tiles_splitk_partial_floats(m, n, k),), dtype=torch.float32, device=dev)
+            ctr = torch.zeros((pq2.pq2_tiles_splitk_counter_words(n),), dtype=torch.int32, device=dev)
+            ysk = torch.empty((m, n), dtype=torch.float32, device=dev)
+            sk_us = per_call_us(torch, stream, lambda m=m: [pq2.pq2_matmul_small_m_tiles_splitk(
+                cfg.q[m], cfg.xs[m], cfg.tpool[c], ysk, part, ctr, stream=stream) for c in range(copies)],
+                copies, reps)
+            torch.cuda.synchronize()
+            assert torch.allclose(ysk, cfg.ymm[m], rtol=1e-4, atol=1e-6), f"{cfg.name} M={m}: split k differs"
+            assert int(ctr.abs().sum()) == 0, "split-k counters not reset"
+            per_m[str(m)]["splitk_matmul_us"] = round(sk_us, 3)
         log(f"[bench] {cfg.name} M={m}: tile matmul {mm_us:.3f} us ({per_m[str(m)]['matmul_GBps']:.0f} GB/s, "
-            f"{per_m[str(m)]['matmul_pct_peak']:.1f}% of 8 TB/s), complete call {call_us:.3f} us")
+            f"{per_m[str(m)]['matmul_pct_peak']:.1f}% of 8 TB/s), complete call {call_us:.3f} us"
+            + (f", split-k matmul {per_m[str(m)]['splitk_matmul_us']:.3f} us" if k > SPLITK_MIN_K else ""))
 
     # Ceilings at the same bytes, over the same copies.
     words = pq2.pq2_stream_probe_words(STREAM_WORKGROUPS)
