@@ -37,6 +37,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 namespace pq2 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -225,8 +227,11 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     store_stage(0);
     __syncthreads();
 
-    for (int g = 0; g < groups; ++g) {
-        const int buf = g & 1;
+    // One group: its products and rescale from LDS buffer BUF (a constant, so
+    // every LDS address is a register plus an immediate), while group g + 1
+    // is loaded and then staged into the other buffer.
+    auto group_step = [&](int g, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         if (g + 1 < groups) load_stage(g + 1);
 
         // Activation group t of this weight group: k-steps KS*t .. KS*t + KS - 1.
@@ -313,6 +318,10 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
         }
         if (g + 1 < groups) store_stage(buf ^ 1);
         __syncthreads();
+    };
+    for (int g = 0; g < groups; g += 2) {
+        group_step(g, std::integral_constant<int, 0>{});
+        if (g + 1 < groups) group_step(g + 1, std::integral_constant<int, 1>{});
     }
 
 #pragma unroll
