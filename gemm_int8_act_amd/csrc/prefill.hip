@@ -98,8 +98,10 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     const int wave = tid >> 6;
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    const int nb = blockIdx.x * BN;
-    const int mb = blockIdx.y * BM;
+    const int bx = blockIdx.x;
+    const int by = blockIdx.y;
+    const int nb = bx * BN;
+    const int mb = by * BM;
     const int k4 = k >> 2;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
@@ -138,32 +140,46 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     const uint32_t s_off = s_is_x ? (uint32_t)(tid * groups * S * 4)
                                   : (s_is_w ? (uint32_t)((tid - (NTH - BN)) * groups * 2) : kBufferOOB);
 
-    uint4 areg[AQ];
-    uint4 breg;
-    uint2 treg[TI];
-    uint32_t sreg;
-    uint32_t xreg[S];
+    // Global loads are issued PD groups ahead of their products: PD = 2 with
+    // two register sets (group g's loads land in set g % 2), or PD = 1 with
+    // one where two sets would not fit the registers of four waves per SIMD
+    // (the 128 x 128 tile on eight waves).
+    constexpr int PD = WM == 4 ? 1 : 2;
+    uint4 areg[PD][AQ];
+    uint4 breg[PD];
+    uint2 treg[PD][TI];
+    uint32_t sreg[PD];
+    uint32_t xreg[PD][S];
 
-    auto load_stage = [&](int g) {
+    // Every thread issues the same loads whatever its role and whatever g
+    // (threads without a scale role, and groups past the last, read past the
+    // buffer's range, which returns zero): no branch around a load, so the
+    // compiler's wait for one register set counts only that set's loads.
+    auto load_stage = [&](int g, auto setc) {
+        constexpr int st = decltype(setc)::value;
 #pragma unroll
-        for (int p = 0; p < AQ; ++p) areg[p] = buf_load16s(q_rs, a_off[p], (uint32_t)g * 128u);
+        for (int p = 0; p < AQ; ++p) areg[st][p] = buf_load16s(q_rs, a_off[p], (uint32_t)g * 128u);
         if constexpr (TILES) {
             // Unit (tile, g / 8), block (g % 8) / 2, dwords 2 (g % 2) and 2 (g % 2) + 1.
             const uint32_t goff = (uint32_t)((g >> 3) * 4352 + ((g & 7) >> 1) * 1024 + (g & 1) * 8);
 #pragma unroll
-            for (int p = 0; p < TI; ++p) treg[p] = buf_load8s(c_rs, tb_off[p], goff);
+            for (int p = 0; p < TI; ++p) treg[st][p] = buf_load8s(c_rs, tb_off[p], goff);
         } else {
-            breg = buf_load16s(c_rs, b_off, (uint32_t)g * 32u);
+            breg[st] = buf_load16s(c_rs, b_off, (uint32_t)g * 32u);
         }
-        if (s_is_x) {
 #pragma unroll
-            for (int t = 0; t < S; ++t) xreg[t] = buf_load4(x_rs, s_off + (uint32_t)(g * S + t) * 4u);
-        } else if constexpr (TILES)
-            sreg = buf_load2(c_rs, s_is_w ? (uint32_t)((((tid - (NTH - BN)) >> 4) * s8 + (g >> 3)) * 4352 + 4096 +
-                                                       16 * ((tid - (NTH - BN)) & 15) + 2 * (g & 7))
-                                          : kBufferOOB);
+        for (int t = 0; t < S; ++t)
+            xreg[st][t] = buf_load4(x_rs, s_is_x && g < groups ? s_off + (uint32_t)(g * S + t) * 4u : kBufferOOB);
+        if constexpr (TILES)
+            // The dword holding the scales of groups g & ~1 and g | 1 (a
+            // 16-bit load would be zero-extended right after it is issued,
+            // which waits for it); store_stage takes half g % 2 = the set.
+            sreg[st] = buf_load4(c_rs, s_is_w && g < groups
+                                           ? (uint32_t)((((tid - (NTH - BN)) >> 4) * s8 + (g >> 3)) * 4352 + 4096 +
+                                                        16 * ((tid - (NTH - BN)) & 15) + 4 * ((g & 7) >> 1))
+                                           : kBufferOOB);
         else
-            sreg = buf_load2(s_rs, s_off == kBufferOOB ? kBufferOOB : s_off + (uint32_t)g * 2u);
+            sreg[st] = buf_load2(s_rs, s_is_w && g < groups ? s_off + (uint32_t)g * 2u : kBufferOOB);
     };
     // LDS slots this thread writes (fixed for the whole kernel).
     int a_slot[AQ];
@@ -175,9 +191,11 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     int b_slot[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) b_slot[c] = swz(tid >> 1, 4 * (tid & 1) + c);
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](auto bufc, auto setc) {
+        constexpr int buf = decltype(bufc)::value;  // LDS buffer = parity of the group
+        constexpr int st = decltype(setc)::value;   // register set
 #pragma unroll
-        for (int p = 0; p < AQ; ++p) As[buf][a_slot[p]] = (PLANE_A || TILES) ? areg[p] : to_plane_order(areg[p]);
+        for (int p = 0; p < AQ; ++p) As[buf][a_slot[p]] = (PLANE_A || TILES) ? areg[st][p] : to_plane_order(areg[st][p]);
         if constexpr (TILES) {
 #pragma unroll
             for (int p = 0; p < TI; ++p) {
@@ -185,7 +203,7 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
                 const int row = it >> 2, kbb = it & 3;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const uint32_t d = h ? treg[p].y : treg[p].x;  // weights 16 (4h + kb) .. +15, natural planes
+                    const uint32_t d = h ? treg[st][p].y : treg[st][p].x;  // weights 16 (4h + kb) .. +15, natural planes
                     Bs[buf][swz(row, 4 * h + kbb)] =
                         make_uint4(lut_plane(d & 0x03030303u), lut_plane((d >> 2) & 0x03030303u),
                                    lut_plane((d >> 4) & 0x03030303u), lut_plane((d >> 6) & 0x03030303u));
@@ -194,7 +212,7 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
         } else if (tid < BI) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint32_t d = word_of(breg, c);
+                const uint32_t d = word_of(breg[st], c);
                 Bs[buf][b_slot[c]] =
                     make_uint4(lut_plane(d & 0x03030303u), lut_plane((d >> 2) & 0x03030303u),
                                lut_plane((d >> 4) & 0x03030303u), lut_plane((d >> 6) & 0x03030303u));
@@ -202,8 +220,11 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
         }
         if (s_is_x) {
 #pragma unroll
-            for (int t = 0; t < S; ++t) xsS[buf][t][tid] = __uint_as_float(xreg[t]);
-        } else if (s_is_w) wsS[buf][tid - (NTH - BN)] = __half2float(__ushort_as_half((unsigned short)sreg));
+            for (int t = 0; t < S; ++t) xsS[buf][t][tid] = __uint_as_float(xreg[st][t]);
+        } else if (s_is_w) {
+            const uint32_t h = TILES ? (buf ? sreg[st] >> 16 : sreg[st] & 0xFFFFu) : sreg[st];
+            wsS[buf][tid - (NTH - BN)] = __half2float(__ushort_as_half((unsigned short)h));
+        }
     };
     // Fragment read slots per k-step (fixed for the whole kernel).
     int af_slot[4][MT], bf_slot[4][NT];
@@ -223,16 +244,23 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    load_stage(0);
-    store_stage(0);
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    load_stage(0, C0{});
+    if constexpr (PD == 2) load_stage(1, C1{});
+    store_stage(C0{}, C0{});
     __syncthreads();
 
     // One group: its products and rescale from LDS buffer BUF (a constant, so
-    // every LDS address is a register plus an immediate), while group g + 1
-    // is loaded and then staged into the other buffer.
+    // every LDS address is a register plus an immediate), while group g + PD
+    // is loaded and group g + 1 (loaded PD - 1 groups earlier) is staged into
+    // the other buffer.
     auto group_step = [&](int g, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        if (g + 1 < groups) load_stage(g + 1);
+        if constexpr (PD == 2)
+            load_stage(g + 2, bufc);
+        else
+            load_stage(g + 1, C0{});
 
         // Activation group t of this weight group: k-steps KS*t .. KS*t + KS - 1.
         // With S > 1 the group's terms float(dot_t) * xs_t are summed first
@@ -316,12 +344,13 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
                     for (int r = 0; r < 16; ++r) acc[mt][nt][r] = __builtin_fmaf(gs[mt][nt][r], wsv, acc[mt][nt][r]);
             }
         }
-        if (g + 1 < groups) store_stage(buf ^ 1);
+        if (g + 1 < groups)
+            store_stage(std::integral_constant<int, buf ^ 1>{}, std::integral_constant<int, PD == 2 ? (buf ^ 1) : 0>{});
         __syncthreads();
     };
     for (int g = 0; g < groups; g += 2) {
-        group_step(g, std::integral_constant<int, 0>{});
-        if (g + 1 < groups) group_step(g + 1, std::integral_constant<int, 1>{});
+        group_step(g, C0{});
+        if (g + 1 < groups) group_step(g + 1, C1{});
     }
 
 #pragma unroll
