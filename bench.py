@@ -466,7 +466,8 @@ def main():
                     help="only sweep the stream read probe over sizes and grid widths and print the table")
     ap.add_argument("--only", default=None,
                     help="profiling runs: measure this one decode shape (per-call timings and ceilings; "
-                         "no headline step, prefill, floor or CPU baseline) and print its JSON")
+                         "no headline step, prefill, floor or CPU baseline), or 'prefill' for the prefill "
+                         "timings only, and print its JSON")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -486,6 +487,10 @@ def main():
     digest = source_digest()
     if args.stream_sweep:
         print(json.dumps(stream_sweep(torch, pq2, dev, stream, args.reps)), flush=True)
+        return
+    if args.only == "prefill":
+        print(json.dumps({"only": "prefill", "prefill": bench_prefill(torch, pq2, workloads, dev, stream, args.reps)}),
+              flush=True)
         return
     if args.only:
         cfg = Config(torch, pq2, workloads, args.only, dev, stream)
@@ -556,7 +561,7 @@ def main():
     del head
     torch.cuda.empty_cache()
     if not args.no_prefill:
-        result["prefill"] = bench_prefill(torch, pq2, workloads, dev, stream)
+        result["prefill"] = bench_prefill(torch, pq2, workloads, dev, stream, 5)
     if args.calibrate:
         calibration_copy(torch, dev, stream)
     if not args.no_cpu_baseline:
@@ -636,7 +641,7 @@ def calibration_copy(torch, dev, stream):
     log(f"[bench] calibration copy: 5 x {src.numel() * 4} bytes read and written")
 
 
-def bench_prefill(torch, pq2, workloads, dev, stream):
+def bench_prefill(torch, pq2, workloads, dev, stream, reps=5):
     """MFMA prefill at the gate (N=6144) and up (N=17408) shapes, M=256..1024,
     from the tile layout, over weight copies that together exceed the 256 MB
     Infinity Cache (each launch reads the next copy)."""
@@ -661,7 +666,7 @@ def bench_prefill(torch, pq2, workloads, dev, stream):
                 pq2.pq2_quantize_act_i8(x[:m], q, xs, stream=stream)
             us = per_call_us(torch, stream, lambda q=q, xs=xs, y=y: [
                 pq2.pq2_matmul_prefill_tiles(q, xs, tiles[c], y, stream=stream) for c in range(copies)],
-                copies, 5)
+                copies, reps)
             torch.cuda.synchronize()
             assert torch.isfinite(y).all()
             ops = 2.0 * m * w.n * w.k
