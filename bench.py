@@ -62,6 +62,7 @@ ROTATION_BYTES = 1 << 30
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for M=1..4 packed-ternary matmul"
 HEADLINE = "up"
 DECODE_MS = (1, 2, 3, 4)
+WARMUP_MS = 25.0         # replays before each timing
 SPLITK_MIN_K = 8192      # split k is timed beside the tile matmul above this k (down)
 STREAM_WORKGROUPS = 2048
 STREAM_FIT_MB = (4, 8, 16, 24, 48, 96, 192)
@@ -138,7 +139,17 @@ def time_graph(torch, graph, stream, reps, repeats=5):
     HIP events on the replay stream."""
     out = []
     with torch.cuda.stream(stream):
+        # Warm-up of at least WARMUP_MS of replays: the clocks settle after a
+        # spell of host-side work (a shorter warm-up left the first shape of
+        # a series 5% slow).
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
         graph.replay()
+        end.record(stream)
+        end.synchronize()
+        for _ in range(max(0, math.ceil(WARMUP_MS / max(start.elapsed_time(end), 1e-3)) - 1)):
+            graph.replay()
         torch.cuda.synchronize()
         for _ in range(repeats):
             start = torch.cuda.Event(enable_timing=True)
