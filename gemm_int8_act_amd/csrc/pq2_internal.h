@@ -97,7 +97,6 @@ struct SplitKPlan {
     int64_t tiles, partial_floats, counters;
 };
 SplitKPlan splitk_plan(int64_t m, int64_t n, int64_t k, int waves);
-bool splitk_default(int64_t k);
 hipError_t launch_small_m_tiles_splitk(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                        int64_t k, float* y, float* partials, uint32_t* counters, int waves,
                                        hipStream_t stream);

@@ -7,8 +7,8 @@
 // tile-major) to separate what the access pattern allows from what the
 // kernel's work costs.  These probes issue exactly the weight loads of the
 // gfx950 decode engines: the same grid, waves, k split (segments of 8
-// groups, at most 8 waves), instruction widths and cache policy, one segment
-// at a time.  Each wave folds what it reads with XOR (so no load is dead)
+// groups over at most 16 waves for the tile layout, 8 for the planes),
+// instruction widths and cache policy, one segment at a time.  Each wave folds what it reads with XOR (so no load is dead)
 // and writes one word.  Every byte of the layout is read once, so the XOR of
 // all output words is the XOR of the layout's dwords (code dwords and tile
 // units; the planes' fp16 scales each zero-extended), which the tests check.

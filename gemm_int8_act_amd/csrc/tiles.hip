@@ -29,9 +29,11 @@
 // When G % 8 == 0 (every shape measured here) and n % 16 == 0 the size
 // equals the prepared planes', n*k/128*34.
 //
-// Engine (same summation order as small_m.hip, so the same bits):
+// Engine (the summation order of small_m.hip):
 //  * A workgroup owns one 16-row tile; its waves split k into consecutive
-//    segments of 8 groups exactly as the other small-m engines do.
+//    segments of 8 groups over at most 16 waves (by default), which is the
+//    other small-m engines' split wherever k <= 8192, so the bits are theirs
+//    there.
 //  * Per group one wave issues v_mfma_i32_16x16x64_i8 twice with B = the two
 //    code dwords' bit planes (codes 0..3, natural order) and A = the
 //    activations of up to four columns; D starts from -sum(q) of each group
@@ -190,8 +192,9 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
 // SPLIT: the k slices of a tile are spread over `ks` workgroups (grid.x =
 // tiles * ks, workgroup p taking slices p * nwaves .. p * nwaves + nwaves - 1,
 // one segment each).  Each wave stores its slice's class sum to
-// partials[slice][column][row]; the workgroup that arrives last at the
-// tile's counter (a device-scope atomic behind a release fence) adds the
+// partials[slice][column][row] (write-through device-scope stores, waited
+// for before the workgroup's barrier); the workgroup that draws the last
+// ticket from the tile's counter (a device-scope vector atomic) adds the
 // slices in index order, writes y and puts the counter back to zero.  No
 // workgroup waits for another.  The sum is the one the single-workgroup
 // kernel forms for the same slices (slice sums added in index order).
@@ -803,10 +806,6 @@ SplitKPlan splitk_plan(int64_t m, int64_t n, int64_t k, int waves) {
     p.counters = (int64_t)kSplitKMaxChunks * t.tiles;
     return p;
 }
-
-// The library's choice: split k when a single workgroup per tile would give
-// each wave several segments (k > 8192 at eight waves per tile).
-bool splitk_default(int64_t k) { return (k / 128 + 7) / 8 > 8; }
 
 hipError_t launch_small_m_tiles_splitk(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                        int64_t k, float* y, float* partials, uint32_t* counters, int waves,

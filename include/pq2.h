@@ -324,8 +324,8 @@ int pq2_gemv_tiles_static(const void* x, int dtype, int64_t x_row_stride_elems, 
  * (not on m: batch-invariant); for k <= 8192 it is the order of
  * pq2_matmul_small_m_tiles, so the bits are the same.  On MI355X it is
  * slower than the single-workgroup kernel at every measured shape (the
- * device-scope store, ticket and reload add about 1.8 us per call), so no
- * default path takes it.
+ * device-scope stores, ticket and reloads add about 1.4 us per call at
+ * k = 17408), so no default path takes it.
  *   q, xs, tiles, y, limits: as pq2_matmul_small_m_tiles.
  *   partials  device float [pq2_tiles_splitk_partial_floats(m, n, k)], 4-byte
  *             aligned, scratch (contents on entry do not matter).
