@@ -61,8 +61,12 @@ __device__ __forceinline__ int swz(int i, int t) { return i * 8 + (t ^ ((i >> 1)
 // tiles of 4352-byte segment units: four 1 KB code blocks, then 256 bytes of
 // scales).  Its 2-bit fields are stored transposed, so the decoded planes of
 // a code dword are natural-order weights and natural-order q is staged as it
-// is (no byte transpose).  Each thread then stages 8-byte pieces: the two
-// code dwords (k-blocks kb and 4 + kb) of one row and group.
+// is (no byte transpose).  A code block holds the 16 bytes of (row, k-block
+// kb) for a pair of groups side by side: the code dwords of k-blocks kb and
+// 4 + kb of the even group, then those of the odd group.  Each thread loads
+// such 16-byte items once per group pair and stages half of each per group.
+// The scale block of a unit holds 16 bytes per row: the fp16 scales of its 8
+// groups.
 //
 // AG: activation group size.  128, or (tile layout only, where k-step kk
 // covers natural positions 32kk .. 32kk + 31 of the group) 64 or 32 for the
@@ -88,10 +92,25 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     constexpr int S = 128 / AG;          // activation groups per weight group
     constexpr int KS = 4 / S;            // k-steps per activation group
     static_assert(AG == 128 || (TILES && (AG == 64 || AG == 32)), "smaller activation groups: tile layout only");
+    // Scale blocks (tile layout, 128-element activation groups): xs and ws of
+    // 8 groups are loaded at once, every lane of the load carrying one (row,
+    // group) of xs or one (row, group pair) dword of ws, and staged once per
+    // 8 groups.  Otherwise each group's scales are loaded and staged with it.
+    constexpr bool SBLK = TILES && S == 1;
+    constexpr int XB = SBLK ? BM * 8 / NTH : 1;   // xs items per thread per block
+    constexpr int WB = SBLK ? BN * 4 / NTH : 1;   // ws dwords per thread per block
+    static_assert(!SBLK || (XB * NTH == BM * 8 && WB * NTH == BN * 4), "scale block split");
+    // The group loop is unrolled so that every register set, LDS buffer and
+    // scale slot index is a constant: by 8 with scale blocks, else by 4 (the
+    // code items come per group pair) or 2.
+    constexpr int UNR = SBLK ? 8 : TILES ? 4 : 2;
+
     __shared__ uint4 As[2][BM * 8];
     __shared__ uint4 Bs[2][BN * 8];
-    __shared__ float xsS[2][S][BM];
-    __shared__ float wsS[2][BN];
+    __shared__ float xsS[SBLK ? 1 : 2][S][SBLK ? 1 : BM];
+    __shared__ float wsS[SBLK ? 1 : 2][SBLK ? 1 : BN];
+    __shared__ float xsB[SBLK ? 8 : 1][SBLK ? BM : 1];       // [group % 8][row]
+    __shared__ uint32_t wsB[SBLK ? 4 : 1][SBLK ? BN : 1];    // [(group % 8) / 2][row]: fp16 pair
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -135,51 +154,88 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
         const int row = it >> 2, kbb = it & 3;
         tb_off[p] = (uint32_t)((row >> 4) * s8 * 4352 + 16 * ((row & 15) + 16 * kbb));
     }
+    // Per-group scales: thread tid < BM loads xs of row tid, the last BN threads ws.
     const bool s_is_x = tid < BM;
     const bool s_is_w = tid >= NTH - BN;
     const uint32_t s_off = s_is_x ? (uint32_t)(tid * groups * S * 4)
                                   : (s_is_w ? (uint32_t)((tid - (NTH - BN)) * groups * 2) : kBufferOOB);
+    // Scale blocks: xs item it = tid + NTH p is (row it >> 3, group it & 7 of
+    // the block), ws item (row it >> 2, dword it & 3 of the row's 16 bytes).
+    uint32_t xb_off[XB], wb_off[WB];
+    int xb_g[XB];
+#pragma unroll
+    for (int p = 0; p < XB; ++p) {
+        const int it = tid + NTH * p;
+        xb_g[p] = it & 7;
+        xb_off[p] = (uint32_t)(((it >> 3) * groups + (it & 7)) * 4);
+    }
+#pragma unroll
+    for (int p = 0; p < WB; ++p) {
+        const int it = tid + NTH * p;
+        const int row = it >> 2;
+        wb_off[p] = (uint32_t)((row >> 4) * s8 * 4352 + 4096 + 16 * (row & 15) + 4 * (it & 3));
+    }
 
     // Global loads are issued PD groups ahead of their products: PD = 2 with
     // two register sets (group g's loads land in set g % 2), or PD = 1 with
     // one where two sets would not fit the registers of four waves per SIMD
-    // (the 128 x 128 tile on eight waves).
+    // (the 128 x 128 tile on eight waves).  Code items of the tile layout
+    // come per group pair (loaded with the even group) into set (g / 2) % 2
+    // when two pairs can be live at once (PD = 2), else into one set.
     constexpr int PD = WM == 4 ? 1 : 2;
+    constexpr int TPS = PD == 2 ? 2 : 1;
     uint4 areg[PD][AQ];
     uint4 breg[PD];
-    uint2 treg[PD][TI];
-    uint32_t sreg[PD];
-    uint32_t xreg[PD][S];
+    uint4 treg[TPS][TI];
+    uint32_t sreg[SBLK ? 1 : PD];
+    uint32_t xreg[SBLK ? 1 : PD][S];
+    uint32_t xbreg[XB], wbreg[WB];
 
     // Every thread issues the same loads whatever its role and whatever g
     // (threads without a scale role, and groups past the last, read past the
     // buffer's range, which returns zero): no branch around a load, so the
     // compiler's wait for one register set counts only that set's loads.
-    auto load_stage = [&](int g, auto setc) {
-        constexpr int st = decltype(setc)::value;
+    // JC: g modulo the unroll (a constant); loads of group g land in set
+    // g % PD.
+    auto load_stage = [&](int g, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int st = j % PD;
 #pragma unroll
         for (int p = 0; p < AQ; ++p) areg[st][p] = buf_load16s(q_rs, a_off[p], (uint32_t)g * 128u);
         if constexpr (TILES) {
-            // Unit (tile, g / 8), block (g % 8) / 2, dwords 2 (g % 2) and 2 (g % 2) + 1.
-            const uint32_t goff = (uint32_t)((g >> 3) * 4352 + ((g & 7) >> 1) * 1024 + (g & 1) * 8);
+            if constexpr (j % 2 == 0) {
+                // Unit (tile, g / 8), block (g % 8) / 2: both groups of the pair.
+                const uint32_t goff = (uint32_t)((g >> 3) * 4352 + ((g & 7) >> 1) * 1024);
 #pragma unroll
-            for (int p = 0; p < TI; ++p) treg[st][p] = buf_load8s(c_rs, tb_off[p], goff);
+                for (int p = 0; p < TI; ++p) treg[(j / 2) % TPS][p] = buf_load16s(c_rs, tb_off[p], goff);
+            }
         } else {
             breg[st] = buf_load16s(c_rs, b_off, (uint32_t)g * 32u);
         }
+        if constexpr (SBLK) {
+            if constexpr (j % 8 == 0) {
+                // Groups g .. g + 7: xs of the workgroup's rows and the unit's scale block.
 #pragma unroll
-        for (int t = 0; t < S; ++t)
-            xreg[st][t] = buf_load4(x_rs, s_is_x && g < groups ? s_off + (uint32_t)(g * S + t) * 4u : kBufferOOB);
-        if constexpr (TILES)
-            // The dword holding the scales of groups g & ~1 and g | 1 (a
-            // 16-bit load would be zero-extended right after it is issued,
-            // which waits for it); store_stage takes half g % 2 = the set.
-            sreg[st] = buf_load4(c_rs, s_is_w && g < groups
-                                           ? (uint32_t)((((tid - (NTH - BN)) >> 4) * s8 + (g >> 3)) * 4352 + 4096 +
-                                                        16 * ((tid - (NTH - BN)) & 15) + 4 * ((g & 7) >> 1))
-                                           : kBufferOOB);
-        else
-            sreg[st] = buf_load2(s_rs, s_is_w && g < groups ? s_off + (uint32_t)g * 2u : kBufferOOB);
+                for (int p = 0; p < XB; ++p)
+                    xbreg[p] = buf_load4(x_rs, g + xb_g[p] < groups ? xb_off[p] + (uint32_t)g * 4u : kBufferOOB);
+#pragma unroll
+                for (int p = 0; p < WB; ++p) wbreg[p] = buf_load4(c_rs, wb_off[p] + (uint32_t)(g >> 3) * 4352u);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < S; ++t)
+                xreg[st][t] = buf_load4(x_rs, s_is_x && g < groups ? s_off + (uint32_t)(g * S + t) * 4u : kBufferOOB);
+            if constexpr (TILES)
+                // The dword holding the scales of groups g & ~1 and g | 1 (a
+                // 16-bit load would be zero-extended right after it is issued,
+                // which waits for it); store_stage takes half g % 2.
+                sreg[st] = buf_load4(c_rs, s_is_w && g < groups
+                                               ? (uint32_t)((((tid - (NTH - BN)) >> 4) * s8 + (g >> 3)) * 4352 + 4096 +
+                                                            16 * ((tid - (NTH - BN)) & 15) + 4 * ((g & 7) >> 1))
+                                               : kBufferOOB);
+            else
+                sreg[st] = buf_load2(s_rs, s_is_w && g < groups ? s_off + (uint32_t)g * 2u : kBufferOOB);
+        }
     };
     // LDS slots this thread writes (fixed for the whole kernel).
     int a_slot[AQ];
@@ -191,9 +247,11 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     int b_slot[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) b_slot[c] = swz(tid >> 1, 4 * (tid & 1) + c);
-    auto store_stage = [&](auto bufc, auto setc) {
-        constexpr int buf = decltype(bufc)::value;  // LDS buffer = parity of the group
-        constexpr int st = decltype(setc)::value;   // register set
+    // Stage group h (JC = h modulo the unroll) into LDS buffer h % 2.
+    auto store_stage = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int buf = j % 2;   // LDS buffer = parity of the group
+        constexpr int st = j % PD;   // register set
 #pragma unroll
         for (int p = 0; p < AQ; ++p) As[buf][a_slot[p]] = (PLANE_A || TILES) ? areg[st][p] : to_plane_order(areg[st][p]);
         if constexpr (TILES) {
@@ -201,9 +259,11 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
             for (int p = 0; p < TI; ++p) {
                 const int it = tid + NTH * p;
                 const int row = it >> 2, kbb = it & 3;
+                const uint4 v = treg[(j / 2) % TPS][p];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const uint32_t d = h ? treg[st][p].y : treg[st][p].x;  // weights 16 (4h + kb) .. +15, natural planes
+                    // Weights 16 (4h + kb) .. +15 of this group, natural planes.
+                    const uint32_t d = buf ? (h ? v.w : v.z) : (h ? v.y : v.x);
                     Bs[buf][swz(row, 4 * h + kbb)] =
                         make_uint4(lut_plane(d & 0x03030303u), lut_plane((d >> 2) & 0x03030303u),
                                    lut_plane((d >> 4) & 0x03030303u), lut_plane((d >> 6) & 0x03030303u));
@@ -218,7 +278,20 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
                                lut_plane((d >> 4) & 0x03030303u), lut_plane((d >> 6) & 0x03030303u));
             }
         }
-        if (s_is_x) {
+        if constexpr (SBLK) {
+            if constexpr (j % 8 == 0) {
+#pragma unroll
+                for (int p = 0; p < XB; ++p) {
+                    const int it = tid + NTH * p;
+                    xsB[it & 7][it >> 3] = __uint_as_float(xbreg[p]);
+                }
+#pragma unroll
+                for (int p = 0; p < WB; ++p) {
+                    const int it = tid + NTH * p;
+                    wsB[it & 3][it >> 2] = wbreg[p];
+                }
+            }
+        } else if (s_is_x) {
 #pragma unroll
             for (int t = 0; t < S; ++t) xsS[buf][t][tid] = __uint_as_float(xreg[st][t]);
         } else if (s_is_w) {
@@ -248,19 +321,17 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     using C1 = std::integral_constant<int, 1>;
     load_stage(0, C0{});
     if constexpr (PD == 2) load_stage(1, C1{});
-    store_stage(C0{}, C0{});
+    store_stage(C0{});
     __syncthreads();
 
-    // One group: its products and rescale from LDS buffer BUF (a constant, so
-    // every LDS address is a register plus an immediate), while group g + PD
-    // is loaded and group g + 1 (loaded PD - 1 groups earlier) is staged into
-    // the other buffer.
-    auto group_step = [&](int g, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        if constexpr (PD == 2)
-            load_stage(g + 2, bufc);
-        else
-            load_stage(g + 1, C0{});
+    // One group g (JC = g modulo the unroll): its products and rescale from
+    // LDS buffer g % 2 (a constant, so every LDS address is a register plus an
+    // immediate), while group g + PD is loaded and group g + 1 (loaded PD - 1
+    // groups earlier) is staged into the other buffer.
+    auto group_step = [&](int g, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int buf = j % 2;
+        load_stage(g + PD, std::integral_constant<int, (j + PD) % UNR>{});
 
         // Activation group t of this weight group: k-steps KS*t .. KS*t + KS - 1.
         // With S > 1 the group's terms float(dot_t) * xs_t are summed first
@@ -298,13 +369,24 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
         // 8*(r/4) + 4*hi + (r%4), r = 0..15.
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const float wsv = S == 1 ? wsS[buf][wn * (BN / 2) + nt * 32 + l32] : 0.0f;
+            const int col = wn * (BN / 2) + nt * 32 + l32;
+            float wsv = 0.0f;
+            if constexpr (SBLK) {
+                const uint32_t wp = wsB[(j % 8) >> 1][col];
+                wsv = __half2float(__ushort_as_half((unsigned short)(j % 2 ? wp >> 16 : wp & 0xFFFFu)));
+            } else if constexpr (S == 1) {
+                wsv = wsS[buf][col];
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    const float4 xv =
-                        *reinterpret_cast<const float4*>(&xsS[buf][t][wm * (BM / WM) + mt * 32 + rb * 8 + hi * 4]);
+                    const int row = wm * (BM / WM) + mt * 32 + rb * 8 + hi * 4;
+                    float4 xv;
+                    if constexpr (SBLK)
+                        xv = *reinterpret_cast<const float4*>(&xsB[j % 8][row]);
+                    else
+                        xv = *reinterpret_cast<const float4*>(&xsS[buf][t][row]);
                     const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -344,13 +426,27 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
                     for (int r = 0; r < 16; ++r) acc[mt][nt][r] = __builtin_fmaf(gs[mt][nt][r], wsv, acc[mt][nt][r]);
             }
         }
-        if (g + 1 < groups)
-            store_stage(std::integral_constant<int, buf ^ 1>{}, std::integral_constant<int, PD == 2 ? (buf ^ 1) : 0>{});
+        if (g + 1 < groups) {
+            // The scale block has one LDS copy: before group g + 1 opens a new
+            // block, every wave must be done with this group's rescale.
+            if constexpr (SBLK && (j + 1) % 8 == 0) __syncthreads();
+            store_stage(std::integral_constant<int, (j + 1) % UNR>{});
+        }
         __syncthreads();
     };
-    for (int g = 0; g < groups; g += 2) {
+    for (int g = 0; g < groups; g += UNR) {
         group_step(g, C0{});
         if (g + 1 < groups) group_step(g + 1, C1{});
+        if constexpr (UNR >= 4) {
+            if (g + 2 < groups) group_step(g + 2, std::integral_constant<int, 2>{});
+            if (g + 3 < groups) group_step(g + 3, std::integral_constant<int, 3>{});
+        }
+        if constexpr (UNR >= 8) {
+            if (g + 4 < groups) group_step(g + 4, std::integral_constant<int, 4>{});
+            if (g + 5 < groups) group_step(g + 5, std::integral_constant<int, 5>{});
+            if (g + 6 < groups) group_step(g + 6, std::integral_constant<int, 6>{});
+            if (g + 7 < groups) group_step(g + 7, std::integral_constant<int, 7>{});
+        }
     }
 
 #pragma unroll
