@@ -490,37 +490,49 @@ hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* plan
 
 }  // namespace
 
-// Tile choice: 64x128 when its grid still gives every CU two workgroups
-// (512 on the 256-CU part), else 64x64 -- for either activation order (the
-// 128x64 tile, which shares each code decode among more rows, measured no
-// better).  From 2048 64x128 workgroups on (FFN up at M = 1024) the
-// 128x128 tile on eight waves, which decodes each code dword once for 128
-// rows, is 3% faster (164.3 against 169.9 us); it loses at smaller grids
-// (up M = 512: 105.9 against 96.6 us).  The 128x128 tile on four waves
+// Tile choice.  A tile's workgroups run in rounds of as many as the chip
+// holds at once (256 CUs; per CU four 64x64, three 64x128 or two 128x128
+// workgroups on eight waves), and a round takes nearly the time of a full one
+// however few workgroups are left in it, since each workgroup is one chain
+// over all k groups.  Below 512 workgroups of 64x128 the 64x64 tile, whose
+// grid fills more of the chip.  From there, for the tile layout, the 64x128
+// tile or the 128x128 tile on eight waves, whichever needs less time counted
+// in whole rounds: at k = 5120 a full round of 128x128 workgroups took 1.19
+// times one of 64x128 (63 against 52.9 us), so 128x128 wins where its grid
+// fills its last round better (m = 1024, n = 16384: 2 rounds against 2.67,
+// 126.3 against 138.7 us) and loses at FFN up (m = 1024, n = 17408: 2.12
+// rounds against 2.83, 156.8 against 151.5 us).  The other weight layouts keep
+// 128x128 from 2048 workgroups of 64x128 on.  The 128x128 tile on four waves
 // needs more than 256 registers per lane (one wave per SIMD); it stays
 // available through the tuning entry points.
-int default_prefill_tile(int64_t m, int64_t n, bool plane_a) {
-    (void)plane_a;
-    const int64_t wgs = ((n + 127) / 128) * ((m + 63) / 64);
-    return wgs >= 2048 ? 5 : wgs >= 512 ? 2 : 3;
+constexpr int64_t kPrefillCUs = 256;
+
+int default_prefill_tile(int64_t m, int64_t n, bool tile_layout) {
+    const int64_t wgs2 = ((n + 127) / 128) * ((m + 63) / 64);
+    if (wgs2 < 512) return 3;
+    if (!tile_layout) return wgs2 >= 2048 ? 5 : 2;
+    const int64_t wgs5 = ((n + 127) / 128) * ((m + 127) / 128);
+    const int64_t rounds2 = (wgs2 + 3 * kPrefillCUs - 1) / (3 * kPrefillCUs);
+    const int64_t rounds5 = (wgs5 + 2 * kPrefillCUs - 1) / (2 * kPrefillCUs);
+    return rounds5 * 119 < rounds2 * 100 ? 5 : 2;
 }
 
 hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,
                           int64_t n, int64_t k, float* y, int tile, bool plane_a, hipStream_t stream) {
-    if (tile == 0) tile = default_prefill_tile(m, n, plane_a);
+    if (tile == 0) tile = default_prefill_tile(m, n, false);
     return plane_a ? launch_any_tile<true, false>(q, xs, planes, m, n, k, y, tile, stream)
                    : launch_any_tile<false, false>(q, xs, planes, m, n, k, y, tile, stream);
 }
 
 hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                 int64_t k, float* y, int tile, hipStream_t stream) {
-    if (tile == 0) tile = default_prefill_tile(m, n, false);
+    if (tile == 0) tile = default_prefill_tile(m, n, true);
     return launch_any_tile<false, true>(q, xs, tiles, m, n, k, y, tile, stream);
 }
 
 hipError_t launch_prefill_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                   int64_t k, float* y, int tile, int agroup, hipStream_t stream) {
-    if (tile == 0) tile = default_prefill_tile(m, n, false);
+    if (tile == 0) tile = default_prefill_tile(m, n, true);
     switch (agroup) {
         case 128: return launch_any_tile<false, true>(q, xs, tiles, m, n, k, y, tile, stream);
         case 64: return launch_any_tile<false, true, 64>(q, xs, tiles, m, n, k, y, tile, stream);
