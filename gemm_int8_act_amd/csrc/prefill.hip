@@ -24,14 +24,19 @@
 //  * B decode: the 2-bit field of each byte becomes c - 1 through one
 //    v_perm_b32 table lookup per plane (table bytes -1, 0, +1, +2), 11 ALU
 //    ops per code dword.
-//  * LDS is double-buffered: the global loads of group g + 1 are in flight
-//    while group g is multiplied, then written to the other buffer; one
-//    barrier per group.  Quads of a row are XOR-swizzled over 16 rows so the
-//    32-row fragment reads and the staging writes hit distinct banks.
+//  * LDS is double-buffered: the global loads of later groups are in flight
+//    while group g is multiplied, then the next group is written to the
+//    other buffer; one barrier per group.  Quads of a row are XOR-swizzled
+//    over 16 rows so the 32-row fragment reads and the staging writes hit
+//    distinct banks.
+//  * Global loads cost by instruction rather than by byte here, so every
+//    lane of every load carries data: 16-byte activation loads, one 16-byte
+//    code load per group pair (tile layout), and the scales of 8 groups per
+//    load (tile layout).
 //  * After the four k-steps of a group each lane rescales its INT32 results:
 //    acc += (float(dot) * xs[m]) * ws[n].  That rescale (3 VALU per output
-//    and group) is the bound of the kernel: it costs more issue slots than
-//    the matrix cores need for the group's 128 multiply-adds.
+//    and group) makes the VALU the busiest unit: it costs more issue slots
+//    than the matrix cores need for the group's 128 multiply-adds.
 #include "pq2_device.h"
 #include "pq2_internal.h"
 
