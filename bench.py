@@ -479,6 +479,8 @@ def main():
                     help="profiling runs: measure this one decode shape (per-call timings and ceilings; "
                          "no headline step, prefill, floor or CPU baseline), or 'prefill' for the prefill "
                          "timings only, and print its JSON")
+    ap.add_argument("--prefill-agroups", action="store_true",
+                    help="with --only prefill: also time activation groups of 64 and 32")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 64 MiB copy kernel (counter calibration)")
     args = ap.parse_args()
@@ -500,8 +502,8 @@ def main():
         print(json.dumps(stream_sweep(torch, pq2, dev, stream, args.reps)), flush=True)
         return
     if args.only == "prefill":
-        print(json.dumps({"only": "prefill", "prefill": bench_prefill(torch, pq2, workloads, dev, stream, args.reps)}),
-              flush=True)
+        print(json.dumps({"only": "prefill", "prefill": bench_prefill(torch, pq2, workloads, dev, stream, args.reps,
+                                                                       args.prefill_agroups)}), flush=True)
         return
     if args.only:
         cfg = Config(torch, pq2, workloads, args.only, dev, stream)
@@ -652,10 +654,11 @@ def calibration_copy(torch, dev, stream):
     log(f"[bench] calibration copy: 5 x {src.numel() * 4} bytes read and written")
 
 
-def bench_prefill(torch, pq2, workloads, dev, stream, reps=5):
+def bench_prefill(torch, pq2, workloads, dev, stream, reps=5, agroups=False):
     """MFMA prefill at the gate (N=6144) and up (N=17408) shapes, M=256..1024,
     from the tile layout, over weight copies that together exceed the 256 MB
-    Infinity Cache (each launch reads the next copy)."""
+    Infinity Cache (each launch reads the next copy).  With agroups, also
+    with activation groups of 64 and 32 (pq2_matmul_prefill_tiles_g)."""
     out = {}
     for name in ("prefill_gate", "prefill_up"):
         w = workloads.WORKLOADS[name]
@@ -687,6 +690,18 @@ def bench_prefill(torch, pq2, workloads, dev, stream, reps=5):
                                    "weight_copies": copies}
             log(f"[bench] {name} M={m}: tile-layout prefill {us:.1f} us, {tops:.0f} TOPS "
                 f"({out[f'{name}_m{m}']['pct_int8_peak']:.1f}% of 5 POP/s)")
+            for ag in ((64, 32) if agroups else ()):
+                qg = torch.empty((m, w.k), dtype=torch.int8, device=dev)
+                xsg = torch.empty((m, w.k // ag), dtype=torch.float32, device=dev)
+                with torch.cuda.stream(stream):
+                    pq2.pq2_quantize_act_i8_g(x[:m], qg, xsg, ag, stream=stream)
+                usg = per_call_us(torch, stream, lambda qg=qg, xsg=xsg, y=y, ag=ag: [
+                    pq2.pq2_matmul_prefill_tiles_g(qg, xsg, tiles[c], y, ag, stream=stream) for c in range(copies)],
+                    copies, reps)
+                torch.cuda.synchronize()
+                assert torch.isfinite(y).all()
+                out[f"{name}_m{m}"][f"agroup{ag}_us"] = round(usg, 2)
+                log(f"[bench] {name} M={m}: activation groups of {ag}: {usg:.1f} us ({100 * (usg / us - 1):+.0f}%)")
         del tiles
         torch.cuda.empty_cache()
     return out

@@ -102,13 +102,17 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     // group) of xs or one (row, group pair) dword of ws, and staged once per
     // 8 groups.  Otherwise each group's scales are loaded and staged with it.
     constexpr bool SBLK = TILES && S == 1;
+    // Code items per group pair (tile layout, 128-element activation groups;
+    // with smaller groups the second register set would cost a wave per
+    // SIMD at 64x128): one 16-byte load per (row, k-block) for both groups.
+    // Otherwise one 8-byte load per (row, k-block) and group.
+    constexpr bool BPAIR = SBLK;
     constexpr int XB = SBLK ? BM * 8 / NTH : 1;   // xs items per thread per block
     constexpr int WB = SBLK ? BN * 4 / NTH : 1;   // ws dwords per thread per block
     static_assert(!SBLK || (XB * NTH == BM * 8 && WB * NTH == BN * 4), "scale block split");
     // The group loop is unrolled so that every register set, LDS buffer and
-    // scale slot index is a constant: by 8 with scale blocks, else by 4 (the
-    // code items come per group pair) or 2.
-    constexpr int UNR = SBLK ? 8 : TILES ? 4 : 2;
+    // scale slot index is a constant: by 8 with scale blocks, else by 2.
+    constexpr int UNR = SBLK ? 8 : 2;
 
     __shared__ uint4 As[2][BM * 8];
     __shared__ uint4 Bs[2][BN * 8];
@@ -164,6 +168,17 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     const bool s_is_w = tid >= NTH - BN;
     const uint32_t s_off = s_is_x ? (uint32_t)(tid * groups * S * 4)
                                   : (s_is_w ? (uint32_t)((tid - (NTH - BN)) * groups * 2) : kBufferOOB);
+    // Smaller activation groups (S > 1): a group's xs are BM x S floats, one
+    // per thread (item it = tid + NTH p is row it / S, activation group
+    // it % S), so the loads carry a value in every lane instead of S loads per
+    // thread with most lanes out of range.
+    constexpr int XG = !SBLK && S > 1 ? (BM * S + NTH - 1) / NTH : 1;
+    uint32_t xg_off[XG];
+#pragma unroll
+    for (int p = 0; p < XG; ++p) {
+        const int it = tid + NTH * p;
+        xg_off[p] = it < BM * S ? (uint32_t)(((it / S) * groups * S + it % S) * 4) : kBufferOOB;
+    }
     // Scale blocks: xs item it = tid + NTH p is (row it >> 3, group it & 7 of
     // the block), ws item (row it >> 2, dword it & 3 of the row's 16 bytes).
     uint32_t xb_off[XB], wb_off[WB];
@@ -184,16 +199,17 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     // Global loads are issued PD groups ahead of their products: PD = 2 with
     // two register sets (group g's loads land in set g % 2), or PD = 1 with
     // one where two sets would not fit the registers of four waves per SIMD
-    // (the 128 x 128 tile on eight waves).  Code items of the tile layout
-    // come per group pair (loaded with the even group) into set (g / 2) % 2
-    // when two pairs can be live at once (PD = 2), else into one set.
+    // (the 128 x 128 tile on eight waves).  Code item pairs are loaded with
+    // the even group into set (g / 2) % 2 when two pairs can be live at once
+    // (PD = 2), else into one set.
     constexpr int PD = WM == 4 ? 1 : 2;
     constexpr int TPS = PD == 2 ? 2 : 1;
     uint4 areg[PD][AQ];
     uint4 breg[PD];
-    uint4 treg[TPS][TI];
+    uint4 treg[BPAIR ? TPS : 1][BPAIR ? TI : 1];
+    uint2 treg8[TILES && !BPAIR ? PD : 1][TILES && !BPAIR ? TI : 1];
     uint32_t sreg[SBLK ? 1 : PD];
-    uint32_t xreg[SBLK ? 1 : PD][S];
+    uint32_t xreg[SBLK ? 1 : PD][S > 1 ? XG : 1];
     uint32_t xbreg[XB], wbreg[WB];
 
     // Every thread issues the same loads whatever its role and whatever g
@@ -207,13 +223,18 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
         constexpr int st = j % PD;
 #pragma unroll
         for (int p = 0; p < AQ; ++p) areg[st][p] = buf_load16s(q_rs, a_off[p], (uint32_t)g * 128u);
-        if constexpr (TILES) {
+        if constexpr (BPAIR) {
             if constexpr (j % 2 == 0) {
                 // Unit (tile, g / 8), block (g % 8) / 2: both groups of the pair.
                 const uint32_t goff = (uint32_t)((g >> 3) * 4352 + ((g & 7) >> 1) * 1024);
 #pragma unroll
                 for (int p = 0; p < TI; ++p) treg[(j / 2) % TPS][p] = buf_load16s(c_rs, tb_off[p], goff);
             }
+        } else if constexpr (TILES) {
+            // Unit (tile, g / 8), block (g % 8) / 2, this group's half of the item.
+            const uint32_t goff = (uint32_t)((g >> 3) * 4352 + ((g & 7) >> 1) * 1024 + (g & 1) * 8);
+#pragma unroll
+            for (int p = 0; p < TI; ++p) treg8[st][p] = buf_load8s(c_rs, tb_off[p], goff);
         } else {
             breg[st] = buf_load16s(c_rs, b_off, (uint32_t)g * 32u);
         }
@@ -227,9 +248,13 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
                 for (int p = 0; p < WB; ++p) wbreg[p] = buf_load4(c_rs, wb_off[p] + (uint32_t)(g >> 3) * 4352u);
             }
         } else {
+            if constexpr (S > 1) {
 #pragma unroll
-            for (int t = 0; t < S; ++t)
-                xreg[st][t] = buf_load4(x_rs, s_is_x && g < groups ? s_off + (uint32_t)(g * S + t) * 4u : kBufferOOB);
+                for (int p = 0; p < XG; ++p)
+                    xreg[st][p] = buf_load4(x_rs, g < groups ? xg_off[p] + (uint32_t)(g * S) * 4u : kBufferOOB);
+            } else {
+                xreg[st][0] = buf_load4(x_rs, s_is_x && g < groups ? s_off + (uint32_t)g * 4u : kBufferOOB);
+            }
             if constexpr (TILES)
                 // The dword holding the scales of groups g & ~1 and g | 1 (a
                 // 16-bit load would be zero-extended right after it is issued,
@@ -264,11 +289,16 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
             for (int p = 0; p < TI; ++p) {
                 const int it = tid + NTH * p;
                 const int row = it >> 2, kbb = it & 3;
-                const uint4 v = treg[(j / 2) % TPS][p];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     // Weights 16 (4h + kb) .. +15 of this group, natural planes.
-                    const uint32_t d = buf ? (h ? v.w : v.z) : (h ? v.y : v.x);
+                    uint32_t d;
+                    if constexpr (BPAIR) {
+                        const uint4 v = treg[(j / 2) % TPS][p];
+                        d = buf ? (h ? v.w : v.z) : (h ? v.y : v.x);
+                    } else {
+                        d = h ? treg8[st][p].y : treg8[st][p].x;
+                    }
                     Bs[buf][swz(row, 4 * h + kbb)] =
                         make_uint4(lut_plane(d & 0x03030303u), lut_plane((d >> 2) & 0x03030303u),
                                    lut_plane((d >> 4) & 0x03030303u), lut_plane((d >> 6) & 0x03030303u));
@@ -296,12 +326,20 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
                     wsB[it & 3][it >> 2] = wbreg[p];
                 }
             }
-        } else if (s_is_x) {
+        } else {
+            if constexpr (S > 1) {
 #pragma unroll
-            for (int t = 0; t < S; ++t) xsS[buf][t][tid] = __uint_as_float(xreg[st][t]);
-        } else if (s_is_w) {
-            const uint32_t h = TILES ? (buf ? sreg[st] >> 16 : sreg[st] & 0xFFFFu) : sreg[st];
-            wsS[buf][tid - (NTH - BN)] = __half2float(__ushort_as_half((unsigned short)h));
+                for (int p = 0; p < XG; ++p) {
+                    const int it = tid + NTH * p;
+                    if (it < BM * S) xsS[buf][it % S][it / S] = __uint_as_float(xreg[st][p]);
+                }
+            } else if (s_is_x) {
+                xsS[buf][0][tid] = __uint_as_float(xreg[st][0]);
+            }
+            if (s_is_w) {
+                const uint32_t h = TILES ? (buf ? sreg[st] >> 16 : sreg[st] & 0xFFFFu) : sreg[st];
+                wsS[buf][tid - (NTH - BN)] = __half2float(__ushort_as_half((unsigned short)h));
+            }
         }
     };
     // Fragment read slots per k-step (fixed for the whole kernel).
@@ -507,14 +545,17 @@ hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* plan
 // fills its last round better (m = 1024, n = 16384: 2 rounds against 2.67,
 // 126.3 against 138.7 us) and loses at FFN up (m = 1024, n = 17408: 2.12
 // rounds against 2.83, 156.8 against 151.5 us).  The other weight layouts keep
-// 128x128 from 2048 workgroups of 64x128 on.  The 128x128 tile on four waves
+// 128x128 from 2048 workgroups of 64x128 on.  Activation groups of 64 or 32
+// stay on 64x128: there the 128x128 tile on eight waves needs 146-148
+// registers, one workgroup per CU.  The 128x128 tile on four waves
 // needs more than 256 registers per lane (one wave per SIMD); it stays
 // available through the tuning entry points.
 constexpr int64_t kPrefillCUs = 256;
 
-int default_prefill_tile(int64_t m, int64_t n, bool tile_layout) {
+int default_prefill_tile(int64_t m, int64_t n, bool tile_layout, int agroup = 128) {
     const int64_t wgs2 = ((n + 127) / 128) * ((m + 63) / 64);
     if (wgs2 < 512) return 3;
+    if (agroup != 128) return 2;
     if (!tile_layout) return wgs2 >= 2048 ? 5 : 2;
     const int64_t wgs5 = ((n + 127) / 128) * ((m + 127) / 128);
     const int64_t rounds2 = (wgs2 + 3 * kPrefillCUs - 1) / (3 * kPrefillCUs);
@@ -537,7 +578,7 @@ hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t*
 
 hipError_t launch_prefill_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,
                                   int64_t k, float* y, int tile, int agroup, hipStream_t stream) {
-    if (tile == 0) tile = default_prefill_tile(m, n, true);
+    if (tile == 0) tile = default_prefill_tile(m, n, true, agroup);
     switch (agroup) {
         case 128: return launch_any_tile<false, true>(q, xs, tiles, m, n, k, y, tile, stream);
         case 64: return launch_any_tile<false, true, 64>(q, xs, tiles, m, n, k, y, tile, stream);
