@@ -510,7 +510,10 @@ def main():
         per_m, ceil, roof = measure_config(torch, pq2, cfg, stream, args.reps, digest)
         if args.calibrate:
             calibration_copy(torch, dev, stream)
-        print(json.dumps({"only": args.only, "us_per_call": per_m, "ceilings": ceil, "roofline": roof}), flush=True)
+        line = {"only": args.only, "us_per_call": per_m, "ceilings": ceil, "roofline": roof}
+        if args.variants and args.only == "qkv":
+            line["variants"] = bench_variants(torch, pq2, workloads, cfg, dev, stream, args.reps)
+        print(json.dumps(line), flush=True)
         return
     names = [c for c in args.configs.split(",") if c]
     if HEADLINE not in names:
@@ -634,8 +637,17 @@ def bench_variants(torch, pq2, workloads, cfg, dev, stream, reps):
             t[f"agroup{ag}_matmul_us"] = round(per_call_us(torch, stream, lambda qg=qg, xsg=xsg, yg=yg, ag=ag: [
                 pq2.pq2_matmul_small_m_tiles_g(qg, xsg, cfg.tpool[c], yg, ag, stream=stream)
                 for c in range(copies)], copies, reps), 3)
+            t[f"agroup{ag}_two_launch_call_us"] = round(per_call_us(torch, stream, lambda qg=qg, xsg=xsg, yg=yg, ag=ag: [
+                (pq2.pq2_quantize_act_i8_g(xm, qg, xsg, ag, stream=stream),
+                 pq2.pq2_matmul_small_m_tiles_g(qg, xsg, cfg.tpool[c], yg, ag, stream=stream))
+                for c in range(copies)], copies, reps), 3)
+            yf = torch.empty((m, n), dtype=torch.float32, device=dev)
+            t[f"agroup{ag}_fused_call_us"] = round(per_call_us(torch, stream, lambda yf=yf, ag=ag: [
+                pq2.pq2_matmul_small_m_tiles_fused_g(xm, cfg.tpool[c], yf, ag, stream=stream)
+                for c in range(copies)], copies, reps), 3)
             torch.cuda.synchronize()
             assert torch.isfinite(yg).all()
+            assert torch.equal(yf.view(torch.int32), yg.view(torch.int32)), f"fused agroup {ag} differs at M={m}"
         out[str(m)] = t
         log(f"[bench] variants {cfg.name} M={m}: {t}")
     del pool

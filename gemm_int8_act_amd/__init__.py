@@ -43,6 +43,7 @@ EXPORTED = (
     "pq2_matmul_small_m_tiles_tuned",
     "pq2_matmul_small_m_tiles_fused",
     "pq2_matmul_small_m_tiles_fused_tuned",
+    "pq2_matmul_small_m_tiles_fused_g",
     "pq2_matmul_prefill_tiles",
     "pq2_matmul_prefill_tiles_tuned",
     "pq2_matmul_prefill_planes",
@@ -155,6 +156,8 @@ def _load_library():
     lib.pq2_matmul_small_m_tiles_fused.restype = i32
     lib.pq2_matmul_small_m_tiles_fused_tuned.argtypes = [p, i32, i64, p, i64, i64, i64, p, i32, i32, p]
     lib.pq2_matmul_small_m_tiles_fused_tuned.restype = i32
+    lib.pq2_matmul_small_m_tiles_fused_g.argtypes = [p, i32, i64, p, i64, i64, i64, i64, p, p]
+    lib.pq2_matmul_small_m_tiles_fused_g.restype = i32
     lib.pq2_matmul_small_m_tiles_splitk.argtypes = [p, p, p, i64, i64, i64, p, p, p, p]
     lib.pq2_matmul_small_m_tiles_splitk.restype = i32
     lib.pq2_matmul_small_m_tiles_splitk_tuned.argtypes = [p, p, p, i64, i64, i64, p, p, p, i32, p]
@@ -554,6 +557,15 @@ def pq2_matmul_small_m_tiles_fused(x, tiles, y, stream=None) -> None:
     """Quantise x (bf16/f16/f32 [m][k]) and multiply by the tile layout in one launch."""
     _check(lib.pq2_matmul_small_m_tiles_fused(*_tiles_fused_args(x, tiles, y), _stream(stream)),
            "pq2_matmul_small_m_tiles_fused")
+
+
+def pq2_matmul_small_m_tiles_fused_g(x, tiles, y, agroup: int, stream=None) -> None:
+    """pq2_matmul_small_m_tiles_fused with activation groups of agroup = 128,
+    64 or 32 elements (the bits of pq2_quantize_act_i8_g followed by
+    pq2_matmul_small_m_tiles_g)."""
+    xp, dt, stride, tp, m, n, k, yp = _tiles_fused_args(x, tiles, y)
+    _check(lib.pq2_matmul_small_m_tiles_fused_g(xp, dt, stride, tp, m, n, k, agroup, yp, _stream(stream)),
+           "pq2_matmul_small_m_tiles_fused_g")
 
 
 def pq2_matmul_small_m_tiles_fused_tuned(x, tiles, y, max_waves=0, split=0, stream=None) -> None:

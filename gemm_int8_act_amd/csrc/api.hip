@@ -194,9 +194,9 @@ int pq2_matmul_small_m_tiles(const int8_t* q, const float* xs, const void* tiles
     return pq2_matmul_small_m_tiles_tuned(q, xs, tiles, m, n, k, y, 0, 0, stream);
 }
 
-int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
-                                         int64_t m, int64_t n, int64_t k, float* y, int max_waves, int split,
-                                         void* stream) {
+// Arguments of the fused tile matmul: x is read in place with 16-byte loads.
+static int check_tiles_fused_args(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles, int64_t m,
+                                  int64_t n, int64_t k, const float* y) {
     if (!x || !tiles || !y) return PQ2_EINVAL;
     if (dtype != PQ2_BF16 && dtype != PQ2_F16 && dtype != PQ2_F32) return PQ2_EINVAL;
     if (m < 1 || m > PQ2_MAX_SMALL_M || n < 1 || n > kMaxN) return PQ2_ESHAPE;
@@ -209,6 +209,13 @@ int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row
         return PQ2_EALIGN;
     const size_t ybytes = (size_t)m * n * 4;
     if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, tiles, (size_t)pq2::tiles_bytes(n, k))) return PQ2_EINVAL;
+    return PQ2_OK;
+}
+
+int pq2_matmul_small_m_tiles_fused_tuned(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
+                                         int64_t m, int64_t n, int64_t k, float* y, int max_waves, int split,
+                                         void* stream) {
+    if (int rc = check_tiles_fused_args(x, dtype, x_row_stride_elems, tiles, m, n, k, y)) return rc;
     if (max_waves < 0 || max_waves > 16) return PQ2_EINVAL;
     const int waves = max_waves ? max_waves : pq2::kTilesDefaultWaves;
     if (!split) split = pq2::tiles_default_split(m, k, waves);
@@ -380,6 +387,18 @@ int pq2_matmul_small_m_tiles_g(const int8_t* q, const float* xs, const void* til
     if (int rc = check_device()) return rc;
     return launch_status(pq2::launch_small_m_tiles_g(q, xs, static_cast<const uint8_t*>(tiles), m, n, k, (int)agroup,
                                                      y, waves, split, (hipStream_t)stream));
+}
+
+int pq2_matmul_small_m_tiles_fused_g(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
+                                     int64_t m, int64_t n, int64_t k, int64_t agroup, float* y, void* stream) {
+    if (agroup != 128 && agroup != 64 && agroup != 32) return PQ2_EINVAL;
+    if (int rc = check_tiles_fused_args(x, dtype, x_row_stride_elems, tiles, m, n, k, y)) return rc;
+    const int waves = pq2::kTilesDefaultWaves;
+    const int split = pq2::tiles_default_split(m, k, waves);
+    if (int rc = check_device()) return rc;
+    return launch_status(pq2::launch_small_m_tiles_fused_g(x, dtype, x_row_stride_elems,
+                                                           static_cast<const uint8_t*>(tiles), m, n, k, (int)agroup,
+                                                           y, waves, split, (hipStream_t)stream));
 }
 
 int pq2_quantize_act_i8_planes(const void* x, int dtype, int64_t x_row_stride_elems, int64_t m, int64_t k,

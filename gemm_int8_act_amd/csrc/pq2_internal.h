@@ -125,6 +125,11 @@ hipError_t launch_prefill_tiles_g(const int8_t* q, const float* xs, const uint8_
                                   int64_t k, float* y, int tile, int agroup, hipStream_t stream);
 hipError_t launch_small_m_tiles_fused(const void* x, int dtype, int64_t x_stride, const uint8_t* tiles, int64_t m,
                                       int64_t n, int64_t k, float* y, int max_waves, int split, hipStream_t stream);
+// The fused tile matmul (x quantised while staged) with activation groups of
+// agroup = 128, 64 or 32; split must be 1 below 128.
+hipError_t launch_small_m_tiles_fused_g(const void* x, int dtype, int64_t x_stride, const uint8_t* tiles, int64_t m,
+                                        int64_t n, int64_t k, int agroup, float* y, int max_waves, int split,
+                                        hipStream_t stream);
 // Tile engine with activation groups of agroup = 128, 64 or 32 (natural-order
 // q from launch_quantize_g, xs [m][k/agroup]).
 hipError_t launch_small_m_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,

@@ -23,13 +23,15 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t 
     return ab | (cd << 16);
 }
 
-// Group-128 INT8 quantisation (page "Baseline and the integer
-// breakthrough", "Calculate with small integers" step 1) of one row slot's
-// group, 16 elements per lane: lane j of the slot holds elements
-// 16j..16j+15 in v.  Returns the lane's 16 codes in plane order (dword s =
-// codes 16j + s, +4, +8, +12), or with PLANE false in natural order (dword s
-// = codes 16j + 4s .. 16j + 4s + 3), and sets gsum (group sum of q, all 8 lanes)
-// and scale (max|x| / 127, correctly rounded).  The codes equal the
+// INT8 quantisation (page "Baseline and the integer breakthrough",
+// "Calculate with small integers" step 1) of one activation group of 16 * GL
+// elements held 16 per lane by GL aligned lanes (GL = 8: a 128-element group;
+// 4 and 2: the 64- and 32-element groups of page "Kernel experiments: recorded
+// evidence", section C): lane j of the group holds elements 16j..16j+15 in v.
+// Returns the lane's 16 codes in plane order (dword s = codes 16j + s, +4,
+// +8, +12), or with PLANE false in natural order (dword s = codes 16j + 4s ..
+// 16j + 4s + 3), and sets gsum (group sum of q, all GL lanes) and scale
+// (max|x| / 127, correctly rounded).  The codes equal the
 // definition q = clamp(rint(RN(x / d)), +-127), d = scale or 1 for an
 // all-zero group, bit for bit:
 //  * RN(x / d) is computed as the double product x * fl64(1 / d) rounded to
@@ -40,13 +42,19 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t 
 //  * the clamp to +-127 comes before the rounding: adding 1.5 * 2^23 rounds
 //    the clamped value half to even in the low mantissa bits, whose low byte
 //    is the two's-complement code.
-template <bool PLANE = true>
+template <bool PLANE = true, int GL = 8>
 __device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum, float& scale) {
 #pragma clang fp contract(off)
+    static_assert(GL == 8 || GL == 4 || GL == 2, "lanes per activation group");
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    amax = max8_f(amax);
+    if constexpr (GL == 8) {
+        amax = max8_f(amax);
+    } else {
+        amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+        if constexpr (GL == 4) amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+    }
     scale = amax / 127.0f;
     const float d = scale > 0.0f ? scale : 1.0f;
     // The IEEE quotient v / d without a division per element.  v / d of two
@@ -79,7 +87,13 @@ __device__ __forceinline__ uint4 quantize_lane16(const float (&v)[16], int& gsum
     s = dot4(out.y, 0x01010101u, s);
     s = dot4(out.z, 0x01010101u, s);
     s = dot4(out.w, 0x01010101u, s);
-    gsum = sum8_i(s);
+    if constexpr (GL == 8) {
+        gsum = sum8_i(s);
+    } else {
+        s += dpp_i<kDppXor1>(s);
+        if constexpr (GL == 4) s += dpp_i<kDppXor2>(s);
+        gsum = s;
+    }
     return out;
 }
 

@@ -184,8 +184,7 @@ __device__ __forceinline__ float half_of(const uint4& v, int c) {
 // eight columns.
 //
 // AG: activation group size (128; 64 or 32 for the smaller activation groups
-// of page "Kernel experiments: recorded evidence", section C, Tests 8 and 9:
-// natural-order q only).  Each activation group has its own D chain seeded
+// of page "Kernel experiments: recorded evidence", section C, Tests 8 and 9).  Each activation group has its own D chain seeded
 // with its own -sum(q); the weight group's terms (float)dot * xs_a are summed
 // in k order, then scaled by ws into the class accumulator, fma(sum, ws, acc).
 //
@@ -218,7 +217,6 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
     constexpr int XSV = CPW * S * MC;       // xs values of one segment (AG < 128)
     constexpr int XSL = (XSV + 63) / 64;    // their loads per lane
     static_assert(AG == 128 || AG == 64 || AG == 32, "activation group");
-    static_assert(AG == 128 || !src_fused(SRC), "smaller activation groups read natural-order q");
     static_assert(MC <= 4 || (MC == 8 && AG == 128), "eight-column passes take 128-element activation groups");
     // COLK (2..4 columns from natural-order q): A rows 4c..4c+3 all carry
     // column c, so the lanes of k block kb hold column kb in every D row and
@@ -379,8 +377,8 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
                 float xf[16];
                 x_to_float16<SRC>(g.xraw[t], xf);
                 float scale;
-                v = quantize_lane16<false>(xf, sq, scale);  // the 8 lanes of the group agree
-                if ((lane & 7) == 0 && m < MC) xs_lds[(c_lo + (ch >> 3)) * 8 + m] = scale;
+                v = quantize_lane16<false, LPS>(xf, sq, scale);  // the LPS lanes of the group agree
+                if ((lane & (LPS - 1)) == 0 && m < MC) xs_lds[((c_lo + (ch >> 3)) * S + (ch & 7) / LPS) * 8 + m] = scale;
             } else {
                 v = g.qv[t];
                 sq = dot4(v.x, 0x01010101u, 0);
@@ -762,6 +760,21 @@ bool tiles_supported(int64_t k, int max_waves, int split) {
     return tiles_slices(k, max_waves, &nseg, &per_wave) * split <= 16;
 }
 
+// Activation groups of 64 or 32: any split from natural-order q; from x (the
+// fused sources) one wave per k slice.
+template <int SRC>
+hipError_t launch_tiles_g(int agroup, int split, int mc, const TilesArgs& a, int slices, int nseg, int per_wave,
+                          int chunks) {
+    if constexpr (SRC == kSrcNatural) {
+        return agroup == 64 ? launch_tiles_split<SRC, 64>(split, mc, a, slices, nseg, per_wave, chunks)
+                            : launch_tiles_split<SRC, 32>(split, mc, a, slices, nseg, per_wave, chunks);
+    } else {
+        if (split != 1) return hipErrorInvalidValue;
+        return agroup == 64 ? launch_tiles_mc<8, SRC, 64>(mc, a, slices, nseg, per_wave, chunks)
+                            : launch_tiles_mc<8, SRC, 32>(mc, a, slices, nseg, per_wave, chunks);
+    }
+}
+
 static hipError_t launch_tiles_any(int src, const TilesArgs& a, int max_waves, int split, int agroup = 128) {
     if (!tiles_supported(a.k, max_waves, split)) return hipErrorInvalidValue;
     int nseg, per_wave;
@@ -778,8 +791,15 @@ static hipError_t launch_tiles_any(int src, const TilesArgs& a, int max_waves, i
         mc = kTilesMaxColumns;
         chunks = (int)((a.m + kTilesMaxColumns - 1) / kTilesMaxColumns);
     }
-    if (agroup == 64) return launch_tiles_split<kSrcNatural, 64>(split, mc, a, slices, nseg, per_wave, chunks);
-    if (agroup == 32) return launch_tiles_split<kSrcNatural, 32>(split, mc, a, slices, nseg, per_wave, chunks);
+    if (agroup != 128) {
+        switch (src) {
+            case kSrcNatural: return launch_tiles_g<kSrcNatural>(agroup, split, mc, a, slices, nseg, per_wave, chunks);
+            case kSrcBf16: return launch_tiles_g<kSrcBf16>(agroup, split, mc, a, slices, nseg, per_wave, chunks);
+            case kSrcF16: return launch_tiles_g<kSrcF16>(agroup, split, mc, a, slices, nseg, per_wave, chunks);
+            case kSrcF32: return launch_tiles_g<kSrcF32>(agroup, split, mc, a, slices, nseg, per_wave, chunks);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (src) {
         case kSrcNatural: return launch_tiles_split<kSrcNatural>(split, mc, a, slices, nseg, per_wave, chunks);
         case kSrcBf16: return launch_tiles_split<kSrcBf16>(split, mc, a, slices, nseg, per_wave, chunks);
@@ -832,6 +852,14 @@ hipError_t launch_small_m_tiles_fused(const void* x, int dtype, int64_t x_stride
                                       int64_t n, int64_t k, float* y, int max_waves, int split, hipStream_t stream) {
     const TilesArgs a{nullptr, nullptr, x, x_stride, tiles, m, n, k, y, stream};
     return launch_tiles_any(src_of_dtype(dtype), a, max_waves, split);
+}
+
+hipError_t launch_small_m_tiles_fused_g(const void* x, int dtype, int64_t x_stride, const uint8_t* tiles, int64_t m,
+                                        int64_t n, int64_t k, int agroup, float* y, int max_waves, int split,
+                                        hipStream_t stream) {
+    if (agroup != 128 && agroup != 64 && agroup != 32) return hipErrorInvalidValue;
+    const TilesArgs a{nullptr, nullptr, x, x_stride, tiles, m, n, k, y, stream};
+    return launch_tiles_any(src_of_dtype(dtype), a, max_waves, split, agroup);
 }
 
 hipError_t launch_small_m_tiles_g(const int8_t* q, const float* xs, const uint8_t* tiles, int64_t m, int64_t n,

@@ -372,6 +372,19 @@ int pq2_quantize_act_i8_g(const void* x, int dtype, int64_t x_row_stride_elems, 
 int pq2_matmul_small_m_tiles_g(const int8_t* q, const float* xs, const void* tiles, int64_t m, int64_t n, int64_t k,
                                int64_t agroup, float* y, void* stream);
 
+/* pq2_quantize_act_i8_g + pq2_matmul_small_m_tiles_g in one launch (page
+ * "Kernel experiments", section C, activation groups of 64 or 32, with the
+ * fusion of Tests 12 and 18): every workgroup quantises the activation
+ * groups it reads while staging them, with the definition of
+ * pq2_quantize_act_i8_g, so y has the same bits as the two calls with the
+ * same agroup.
+ *   x       device bf16 / fp16 / fp32 [m][x_row_stride_elems], read in place;
+ *           16-byte aligned rows (x and x_row_stride_elems * element size).
+ *   tiles, y, limits and errors as pq2_matmul_small_m_tiles_fused, plus
+ *   EINVAL for agroup not 128/64/32. */
+int pq2_matmul_small_m_tiles_fused_g(const void* x, int dtype, int64_t x_row_stride_elems, const void* tiles,
+                                     int64_t m, int64_t n, int64_t k, int64_t agroup, float* y, void* stream);
+
 /* Prefill matmul from the tile layout: the definition, limits and output of
  * pq2_matmul_prefill, and the same bits, with the weights read from the
  * decode GEMV's tile layout, so one prepared copy serves decode and prefill

@@ -38,7 +38,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 39
+    assert len(names) == 40
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -223,11 +223,23 @@ def test_activation_group_validation():
     assert h(A, B, C, 64, 8, 96, 64, D, None) == ESHAPE          # k % 128
     assert h(A + 8, B, C, 64, 8, 128, 64, D, None) == EALIGN     # q not 16-byte aligned
     assert h(A, B, C, 1, 8, 256, 32, B + 16, None) == EINVAL     # y overlaps xs (8 floats)
+    u = pq2.lib.pq2_matmul_small_m_tiles_fused_g  # (x, dtype, stride, tiles, m, n, k, agroup, y)
+    for bad in (0, 16, 96, 256):
+        assert u(A, 0, 128, C, 1, 8, 128, bad, D, None) == EINVAL, bad
+    assert u(None, 0, 128, C, 1, 8, 128, 64, D, None) == EINVAL
+    assert u(A, 3, 128, C, 1, 8, 128, 64, D, None) == EINVAL        # dtype
+    assert u(A, 0, 128, C, 17, 8, 128, 64, D, None) == ESHAPE       # columns
+    assert u(A, 0, 128, C, 1, 8, 96, 32, D, None) == ESHAPE         # k % 128
+    assert u(A, 0, 100, C, 1, 8, 128, 64, D, None) == ESHAPE        # stride < k
+    assert u(A + 8, 0, 128, C, 1, 8, 128, 64, D, None) == EALIGN    # x not 16-byte aligned
+    assert u(A, 0, 132, C, 2, 8, 128, 64, D, None) == EALIGN        # rows 264 bytes apart
+    assert u(A, 0, 128, C, 1, 8, 128, 32, A + 16, None) == EINVAL   # y overlaps x
     if not _gpu_visible():
         for agroup in (128, 64, 32):
             assert f(A, 0, 5120, 4, 5120, agroup, B, C, None) == EDEVICE
             assert g(A, B, C, 4, 8, 5120, agroup, D, None) == EDEVICE
             assert h(A, B, C, 256, 8, 5120, agroup, D, None) == EDEVICE
+            assert u(A, 0, 5120, C, 4, 8, 5120, agroup, D, None) == EDEVICE
 
 
 def test_prefill_tile_validation():

@@ -996,6 +996,69 @@ def test_small_m_tiles_g_128_is_the_tile_matmul():
     assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32))
 
 
+FUSED_G_SHAPES = [(1, 1024, 512), (2, 333, 640), (3, 97, 1152), (4, 1000, 5120), (5, 77, 2176), (16, 40, 17408)]
+
+
+@pytest.mark.parametrize("agroup", [64, 32])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("m,n,k", FUSED_G_SHAPES)
+def test_tiles_fused_g_same_bits(agroup, dtype, m, n, k):
+    """Quantise + tile matmul in one launch with activation groups of 64 or
+    32: the bits of pq2_quantize_act_i8_g followed by
+    pq2_matmul_small_m_tiles_g (the quantiser is checked against the oracle
+    here, the matmul against the oracle's bound in test_small_m_tiles_g_full),
+    with a zero group, ragged rows and column passes past four."""
+    pq2 = _pq2()
+    announce(f"tiles fused agroup={agroup} {dtype} m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=80 + m + n, codes="ternary+3", row_pad=2)
+    x = workloads.make_activations(m, k, 81 + k, "normal+outliers")
+    x[0, :agroup] = 0
+    xc = {"bf16": x, "f16": x.float().to(torch.float16), "f32": x.float()}[dtype]
+    q, xs, _, _ = quantise_g_both(xc, agroup, dtype)
+    tiles = gpu_tiles(raw, n, k)
+    y0 = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_small_m_tiles_g(q, xs, tiles, y0, agroup)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_small_m_tiles_fused_g(xc.to(DEV), tiles, y, agroup)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.cpu().numpy().view(np.uint32)), \
+        f"fused agroup={agroup} {dtype} m={m} n={n} k={k}"
+
+
+def test_tiles_fused_g_128_is_the_fused_matmul():
+    pq2 = _pq2()
+    m, n, k = 3, 300, 3072
+    raw = workloads.make_raw_weights(n, k, seed=83, codes="ternary+3")
+    xd = workloads.make_activations(m, k, 84, "laplace").to(DEV)
+    tiles = gpu_tiles(raw, n, k)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_small_m_tiles_fused_g(xd, tiles, y, 128)
+    y0 = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    pq2.pq2_matmul_small_m_tiles_fused(xd, tiles, y0)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y0.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["qkv", "up"])
+def test_tiles_fused_g_workloads(name):
+    """Full workload sizes, every M: the fused call with activation groups of
+    64 and 32 has the bits of the two calls."""
+    pq2 = _pq2()
+    w, raw, x = workload_case(name)
+    tiles = gpu_tiles(raw, w.n, w.k)
+    for agroup in (64, 32):
+        for m in w.ms:
+            announce(f"tiles fused agroup={agroup} workload {name} m={m}")
+            xm = x[:m].contiguous()
+            q, xs, _, _ = quantise_g_both(xm, agroup)
+            y0 = torch.full((m, w.n), float("nan"), dtype=torch.float32, device=DEV)
+            pq2.pq2_matmul_small_m_tiles_g(q, xs, tiles, y0, agroup)
+            y = torch.full((m, w.n), float("nan"), dtype=torch.float32, device=DEV)
+            pq2.pq2_matmul_small_m_tiles_fused_g(xm.to(DEV), tiles, y, agroup)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int32), y0.view(torch.int32)), f"{name} m={m} agroup={agroup}"
+
+
 @pytest.mark.parametrize("name", ["qkv", "down"])
 def test_small_m_tiles_g_workloads(name):
     """Full workload sizes, sampled outputs against the oracle, and 16
