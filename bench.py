@@ -598,8 +598,12 @@ def bench_variants(torch, pq2, workloads, cfg, dev, stream, reps):
         raw = torch.from_numpy(cfg.raw_np).to(dev)
         pool = torch.empty((copies, wb), dtype=torch.uint8, device=dev)
         pq2.pq2_prepare_planes(raw, n, k, pool[0], stream=stream)
-        for c in range(1, copies):
-            pool[c].copy_(pool[0])
+        # The raw-block reader rotates its own copies of the raw rows too.
+        rpool = torch.empty((copies, raw.numel()), dtype=torch.uint8, device=dev)
+        for c in range(copies):
+            if c:
+                pool[c].copy_(pool[0])
+            rpool[c].copy_(raw.view(-1))
     torch.cuda.synchronize()
     out = {}
     for m in cfg.ms:
@@ -621,8 +625,8 @@ def bench_variants(torch, pq2, workloads, cfg, dev, stream, reps):
                                                                               stream=stream) for c in range(copies)],
             "planes_fused_call_us": lambda: [pq2.pq2_matmul_small_m_fused(xm, pool[c], ys["planes_fused"],
                                                                          stream=stream) for c in range(copies)],
-            "raw_matmul_us": lambda: [pq2.pq2_matmul_small_m_raw(q, xs, raw, ys["raw"], stream=stream)
-                                      for c in range(copies)],
+            "raw_matmul_us": lambda: [pq2.pq2_matmul_small_m_raw(q, xs, rpool[c].view(n, -1), ys["raw"],
+                                                                 stream=stream) for c in range(copies)],
         }
         t = {key: round(per_call_us(torch, stream, body, copies, reps), 3) for key, body in bodies.items()}
         torch.cuda.synchronize()
@@ -650,7 +654,7 @@ def bench_variants(torch, pq2, workloads, cfg, dev, stream, reps):
             assert torch.equal(yf.view(torch.int32), yg.view(torch.int32)), f"fused agroup {ag} differs at M={m}"
         out[str(m)] = t
         log(f"[bench] variants {cfg.name} M={m}: {t}")
-    del pool
+    del pool, rpool
     return out
 
 
