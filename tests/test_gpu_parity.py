@@ -434,7 +434,7 @@ def test_small_m_repeatable(name):
 
 # ------------------------------------------------------------------ prefill
 PREFILL_SHAPES = [(1, 64, 128), (5, 200, 640), (128, 128, 1024), (130, 257, 384), (300, 96, 5120),
-                  (257, 513, 2048)]
+                  (257, 513, 2048), (70, 80, 9088)]
 
 
 @pytest.mark.parametrize("m,n,k", PREFILL_SHAPES)
