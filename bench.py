@@ -394,7 +394,54 @@ def stream_sweep(torch, pq2, dev, stream, reps):
         pq2.pq2_empty_probe(wg, w, stream=stream) for _ in range(200)], 200, reps), 3)
         for wg, w in ((1, 1), (256, 1), (1088, 5), (2048, 4), (8192, 4))}
     log(f"[bench] empty-kernel floor {floor}")
-    return {"stream_read_us": table, "launch_floor_us": floor}
+    shape = stream_shape_sweep(torch, pq2, buf, stream, reps)
+    del buf
+    return {"stream_read_us": table, "launch_floor_us": floor, "stream_shape_us": shape}
+
+
+# Shapes of the configurable stream read: the decode weight sizes (QKV, FFN
+# up/down) and a large read; waves per SIMD (256 CUs x 4 SIMDs: workgroups of
+# four waves, or 256 workgroups of one or two below one wave per SIMD); loads
+# in flight per lane.
+STREAM_SHAPE_BYTES = (13926400, 23674880, 192 << 20)
+STREAM_SHAPE_WAVES_PER_SIMD = (0.25, 0.5, 1, 2, 4, 8)
+STREAM_SHAPE_LOADS = (1, 2, 4, 8, 16)
+STREAM_POLICIES = ("buffer", "buffer_nt", "lds", "lds_nt")
+
+
+def stream_shape_sweep(torch, pq2, buf, stream, reps):
+    """pq2_stream_probe_cfg over bytes x load instruction and cache policy x
+    waves per SIMD x loads in flight per lane, then
+    the workgroup size (1..16 waves) at 2 and 4 waves per SIMD: µs per launch
+    in graphs of back-to-back launches over the rotating buffer."""
+    out = torch.empty((1 << 16,), dtype=torch.int32, device=buf.device)
+
+    def timed(nb, wg, waves, loads, policy):
+        copies = buf.numel() // nb
+        return round(per_call_us(torch, stream, lambda: [pq2.pq2_stream_probe_cfg(
+            buf[c * nb:(c + 1) * nb], nb, wg, waves, loads, policy, out, False, 0x7FFFFFFF, stream=stream)
+            for c in range(copies)], copies, reps), 3)
+
+    grid = []
+    for nb in STREAM_SHAPE_BYTES:
+        for policy, pname in enumerate(STREAM_POLICIES):
+            for loads in STREAM_SHAPE_LOADS:
+                row = {"bytes": nb, "policy": pname, "loads_per_lane": loads}
+                for ws in STREAM_SHAPE_WAVES_PER_SIMD:
+                    waves = min(4, int(ws * 4))  # below one wave per SIMD: 256 smaller workgroups
+                    row[str(ws)] = timed(nb, int(ws * 1024) // waves, waves, loads, policy)
+                grid.append(row)
+                log(f"[bench] stream shape {row}")
+    wg_size = []
+    for ws in (2, 4):
+        for loads in (1, 4):
+            row = {"bytes": 23674880, "policy": "buffer_nt", "waves_per_simd": ws, "loads_per_lane": loads}
+            for waves in (1, 2, 4, 8, 16):
+                if waves * loads <= 64:
+                    row[str(waves)] = timed(23674880, ws * 1024 // waves, waves, loads, 1)
+            wg_size.append(row)
+            log(f"[bench] stream workgroup size {row}")
+    return {"grid": grid, "workgroup_size": wg_size}
 
 
 def cpu_baseline(raw, x, n, k, ms, budget_s):

@@ -63,6 +63,7 @@ EXPORTED = (
     "pq2_tiles_splitk_counter_words",
     "pq2_stream_probe",
     "pq2_stream_probe_words",
+    "pq2_stream_probe_cfg",
     "pq2_empty_probe",
     "pq2_gemv_tiles_static",
 )
@@ -169,6 +170,8 @@ def _load_library():
     lib.pq2_stream_probe.argtypes = [p, i64, i64, i32, ctypes.c_uint32, p, p]
     lib.pq2_stream_probe.restype = i32
     lib.pq2_stream_probe_words.argtypes = [i64]
+    lib.pq2_stream_probe_cfg.argtypes = [p, i64, i64, i32, i32, i32, i32, ctypes.c_uint32, p, p]
+    lib.pq2_stream_probe_cfg.restype = i32
     lib.pq2_stream_probe_words.restype = i64
     lib.pq2_empty_probe.argtypes = [i64, i32, p]
     lib.pq2_empty_probe.restype = i32
@@ -413,6 +416,20 @@ def pq2_stream_probe(buf, nbytes: int, workgroups: int, out, store_all: bool = F
                                 sentinel & 0xFFFFFFFF, _dev_ptr(out, "out"), _stream(stream)), "pq2_stream_probe")
 
 
+def pq2_stream_probe_cfg(buf, nbytes: int, workgroups: int, waves: int, loads_per_lane: int, policy: int, out,
+                         store_all: bool = False, sentinel: int = 0, stream=None) -> None:
+    """The stream read with its grid, loads in flight per lane and load
+    instruction (STREAM_*) as parameters; out int32 [workgroups * waves]."""
+    import torch
+    if not buf.is_contiguous() or not out.is_contiguous() or out.dtype != torch.int32:
+        raise ValueError("buf contiguous and out contiguous int32 expected")
+    if buf.numel() * buf.element_size() < nbytes or out.numel() < workgroups * waves:
+        raise ValueError("buf or out too small")
+    _check(lib.pq2_stream_probe_cfg(_dev_ptr(buf, "buf"), nbytes, workgroups, waves, loads_per_lane, policy,
+                                    1 if store_all else 0, sentinel & 0xFFFFFFFF, _dev_ptr(out, "out"),
+                                    _stream(stream)), "pq2_stream_probe_cfg")
+
+
 def pq2_empty_probe(workgroups: int = 1, waves: int = 1, stream=None) -> None:
     """An empty kernel (the launch floor of back-to-back launches)."""
     _check(lib.pq2_empty_probe(workgroups, waves, _stream(stream)), "pq2_empty_probe")
@@ -497,6 +514,7 @@ def pq2_matmul_small_m_raw(q, xs, raw, y, stream=None) -> None:
 
 LAYOUT_PLANES = 0
 LAYOUT_TILES = 1
+STREAM_BUFFER, STREAM_BUFFER_NT, STREAM_LDS, STREAM_LDS_NT = 0, 1, 2, 3
 
 
 def pq2_read_probe_words(layout: int, n: int, k: int) -> int:

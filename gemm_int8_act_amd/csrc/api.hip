@@ -324,19 +324,28 @@ int pq2_matmul_small_m_tiles_splitk(const int8_t* q, const float* xs, const void
 
 int64_t pq2_stream_probe_words(int64_t workgroups) {
     if (workgroups < 1 || workgroups > 65536) return 0;
-    return pq2::stream_probe_words(workgroups);
+    return workgroups * 4;
 }
 
 int pq2_stream_probe(const void* buf, int64_t bytes, int64_t workgroups, int store_all, uint32_t sentinel,
                      uint32_t* out, void* stream) {
-    if (!buf || !out) return PQ2_EINVAL;
-    if (bytes < 16 || bytes % 16 || bytes >= ((int64_t)1 << 31) || workgroups < 1 || workgroups > 65536)
+    return pq2_stream_probe_cfg(buf, bytes, workgroups, 4, 1, PQ2_STREAM_BUFFER_NT, store_all, sentinel, out,
+                                stream);
+}
+
+int pq2_stream_probe_cfg(const void* buf, int64_t bytes, int64_t workgroups, int waves, int loads_per_lane,
+                         int policy, int store_all, uint32_t sentinel, uint32_t* out, void* stream) {
+    if (!buf || !out || policy < PQ2_STREAM_BUFFER || policy > PQ2_STREAM_LDS_NT) return PQ2_EINVAL;
+    const int u = loads_per_lane;
+    if (bytes < 16 || bytes % 16 || bytes >= ((int64_t)1 << 31) || workgroups < 1 || workgroups > 65536 ||
+        waves < 1 || waves > 16 || (u != 1 && u != 2 && u != 4 && u != 8 && u != 16) || waves * u > 64 ||
+        workgroups * waves * u * 1024 > ((int64_t)1 << 30) || (policy >= PQ2_STREAM_LDS && bytes % 1024))
         return PQ2_ESHAPE;
     if (!aligned(buf, 16) || !aligned(out, 4)) return PQ2_EALIGN;
-    if (overlap(out, (size_t)pq2::stream_probe_words(workgroups) * 4, buf, (size_t)bytes)) return PQ2_EINVAL;
+    if (overlap(out, (size_t)(workgroups * waves) * 4, buf, (size_t)bytes)) return PQ2_EINVAL;
     if (int rc = check_device()) return rc;
-    return launch_status(pq2::launch_stream_probe(static_cast<const uint8_t*>(buf), bytes, workgroups,
-                                                  store_all ? 1 : 0, sentinel, out, (hipStream_t)stream));
+    return launch_status(pq2::launch_stream_probe(static_cast<const uint8_t*>(buf), bytes, workgroups, waves, u,
+                                                  policy, store_all ? 1 : 0, sentinel, out, (hipStream_t)stream));
 }
 
 int pq2_empty_probe(int64_t workgroups, int waves, void* stream) {

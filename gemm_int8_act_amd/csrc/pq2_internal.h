@@ -108,11 +108,12 @@ hipError_t launch_prefill_tiles(const int8_t* q, const float* xs, const uint8_t*
 int64_t read_probe_words(int layout, int64_t n, int64_t k);
 hipError_t launch_read_probe(const uint8_t* weights, int layout, int64_t n, int64_t k, uint32_t* out,
                              hipStream_t stream);
-// Linear stream read of a buffer (workgroups x 4 waves, grid-stride over 1 KB
-// wave chunks) and an empty kernel: the read ceiling and launch floor.
-int64_t stream_probe_words(int64_t workgroups);
-hipError_t launch_stream_probe(const uint8_t* buf, int64_t bytes, int64_t workgroups, int store_all,
-                               uint32_t sentinel, uint32_t* out, hipStream_t stream);
+// Linear stream read of a buffer (workgroups x waves, grid-stride over
+// chunks of `loads` KB per wave, `loads` 16-byte loads per lane in flight;
+// policy 0..3 as in pq2_measure.h).  Writes workgroups x waves words.
+hipError_t launch_stream_probe(const uint8_t* buf, int64_t bytes, int64_t workgroups, int waves, int loads,
+                               int policy, int store_all, uint32_t sentinel, uint32_t* out, hipStream_t stream);
+// An empty kernel of workgroups x waves: the launch floor.
 hipError_t launch_empty_probe(int64_t workgroups, int waves, hipStream_t stream);
 // Packed-dot small-m matmul straight from the raw block layout (34 bytes per
 // 128 weights: fp16 scale, then 32 code bytes; rows raw_stride bytes apart),

@@ -99,27 +99,73 @@ __global__ __launch_bounds__(512) void read_probe_planes_kernel(const uint8_t* _
     if (lane == 0) out[(size_t)blockIdx.x * nwaves + wave] = f;
 }
 
-// Linear stream read of `bytes` bytes (a multiple of 16), shaped like no
-// decode engine: grid-stride over 1 KB wave chunks.  Iteration i, workgroup
-// w, wave v reads chunk (i * G + w) * W + v, one 16-byte non-temporal load
-// per lane; chunks past the end read zero (buffer range check).  Each wave
-// folds what it read with XOR.  store_all = 1 writes every wave's fold (the
-// XOR of all words is the XOR of the buffer's dwords); store_all = 0 writes
-// only from a lane whose own fold equals `sentinel` (practically never), so
-// a timed run is a pure read (any output store adds the latency of one store
-// to the end of a launch).
-__global__ __launch_bounds__(256) void stream_probe_kernel(const uint8_t* __restrict__ buf, uint32_t bytes, int iters,
-                                                           int store_all, uint32_t sentinel,
-                                                           uint32_t* __restrict__ out) {
+// Linear stream read of `bytes` bytes, shaped like no decode engine:
+// grid-stride over wave chunks of U KB.  Iteration i, workgroup w, wave v
+// reads the U consecutive 1 KB blocks starting at block ((i * G + w) * W + v)
+// * U, one 16-byte load per lane per block, all U loads issued before any is
+// used, so a lane has U loads in flight.  POLICY picks the load:
+//   0, 1  buffer_load_dwordx4 into registers (1: non-temporal); bytes past
+//         the end read zero (buffer range check);
+//   2, 3  global_load_lds_dwordx4 into a per-wave LDS slot of U KB (3:
+//         non-temporal), then, once the loads have landed, each lane reads
+//         16 bytes back (bytes is a multiple of 1 KB, so a block is wholly
+//         in or out of range: a wave-uniform branch).
+// Each wave folds what it read with XOR.  store_all = 1 writes every wave's
+// fold (the XOR of all words is the XOR of the buffer's dwords); store_all =
+// 0 writes only from a lane whose own fold equals `sentinel` (practically
+// never), so a timed run is a pure read (any output store adds the latency of
+// one store to the end of a launch).
+template <int U, int POLICY>
+__global__ __launch_bounds__(1024) void stream_probe_kernel(const uint8_t* __restrict__ buf, uint32_t bytes, int iters,
+                                                            int store_all, uint32_t sentinel,
+                                                            uint32_t* __restrict__ out) {
+    constexpr int kAux = (POLICY & 1) ? kAuxNonTemporal : 0;
     const int nwaves = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const auto rs = make_rsrc(buf, bytes);
     const uint32_t wave_id = (uint32_t)blockIdx.x * nwaves + wave;
-    const uint32_t stride = gridDim.x * (uint32_t)nwaves * 1024u;
+    const uint32_t stride = gridDim.x * (uint32_t)nwaves * (uint32_t)(U * 1024);
+    uint32_t base = wave_id * (uint32_t)(U * 1024);  // wave-uniform start of this iteration's chunk
     uint32_t f = 0;
-    uint32_t off = wave_id * 1024u + 16u * lane;
-    for (int i = 0; i < iters; ++i, off += stride) f ^= fold4(buf_load16<kAuxNonTemporal>(rs, off < bytes ? off : kBufferOOB));
+    if constexpr (POLICY < 2) {
+        const auto rs = make_rsrc(buf, bytes);
+        for (int i = 0; i < iters; ++i, base += stride) {
+            uint4 r[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t off = base + u * 1024u + 16u * lane;
+                r[u] = buf_load16<kAux>(rs, off < bytes ? off : kBufferOOB);
+            }
+            // Keep the scheduler from starting the fold (and its waits)
+            // before the last load has issued: U loads in flight.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) f ^= fold4(r[u]);
+        }
+    } else {
+        extern __shared__ uint4 stream_slots[];  // U KB per wave
+        uint4* slot = stream_slots + (size_t)wave * U * 64;
+#pragma nounroll
+        for (int i = 0; i < iters; ++i, base += stride) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (base + u * 1024u < bytes)
+                    __builtin_amdgcn_global_load_lds(
+                        (const void __attribute__((address_space(1)))*)(buf + base + u * 1024u + 16u * lane),
+                        (void __attribute__((address_space(3)))*)(slot + u * 64), 16, 0, kAux);
+            // The compiler does not order these LDS reads after the loads
+            // that fill the slot: wait for every vector-memory load of the
+            // wave (vmcnt 0; expcnt and lgkmcnt left at their maxima).
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            // Every slot is read (LDS, always in range); a block past the
+            // end holds stale bytes and is dropped from the fold.
+            uint4 r[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) r[u] = slot[u * 64 + lane];
+#pragma unroll
+            for (int u = 0; u < U; ++u) f ^= base + u * 1024u < bytes ? fold4(r[u]) : 0u;
+        }
+    }
     if (store_all) {
         f = wave_xor(f);
         if (lane == 0) out[wave_id] = f;
@@ -152,17 +198,28 @@ ProbeGrid probe_grid(int layout, int64_t n, int64_t k) {
 
 }  // namespace
 
-constexpr int kStreamWaves = 4;
-
-int64_t stream_probe_words(int64_t workgroups) { return workgroups * kStreamWaves; }
-
-hipError_t launch_stream_probe(const uint8_t* buf, int64_t bytes, int64_t workgroups, int store_all,
-                               uint32_t sentinel, uint32_t* out, hipStream_t stream) {
-    const int64_t per_iter = workgroups * kStreamWaves * 1024;
+hipError_t launch_stream_probe(const uint8_t* buf, int64_t bytes, int64_t workgroups, int waves, int loads,
+                               int policy, int store_all, uint32_t sentinel, uint32_t* out, hipStream_t stream) {
+    const int64_t per_iter = workgroups * waves * loads * 1024;
     const int iters = (int)((bytes + per_iter - 1) / per_iter);
+    const size_t lds = policy >= 2 ? (size_t)waves * loads * 1024 : 0;
+    decltype(&stream_probe_kernel<1, 0>) fn = nullptr;
+#define PQ2_STREAM_CASE(u)                                                                                 \
+    if (loads == u)                                                                                        \
+        fn = policy == 0   ? stream_probe_kernel<u, 0>                                                     \
+             : policy == 1 ? stream_probe_kernel<u, 1>                                                     \
+             : policy == 2 ? stream_probe_kernel<u, 2>                                                     \
+                           : stream_probe_kernel<u, 3>;
+    PQ2_STREAM_CASE(1)
+    PQ2_STREAM_CASE(2)
+    PQ2_STREAM_CASE(4)
+    PQ2_STREAM_CASE(8)
+    PQ2_STREAM_CASE(16)
+#undef PQ2_STREAM_CASE
+    if (!fn) return hipErrorInvalidValue;
     clear_stale_error();
-    hipLaunchKernelGGL(stream_probe_kernel, dim3((unsigned)workgroups), dim3(64 * kStreamWaves), 0, stream, buf,
-                       (uint32_t)bytes, iters, store_all, sentinel, out);
+    hipLaunchKernelGGL(fn, dim3((unsigned)workgroups), dim3(64 * waves), lds, stream, buf, (uint32_t)bytes, iters,
+                       store_all, sentinel, out);
     return hipGetLastError();
 }
 

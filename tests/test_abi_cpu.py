@@ -38,7 +38,7 @@ def _declared_symbols():
 
 def test_header_symbols_exported():
     names = _declared_symbols()
-    assert len(names) == 40
+    assert len(names) == 41
     lib = ctypes.CDLL(pq2.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -415,12 +415,35 @@ def test_stream_and_empty_probe_validation():
     assert s(A + 8, 1024, 8, 1, 0, D, None) == EALIGN
     assert s(A, 1024, 8, 1, 0, D + 2, None) == EALIGN
     assert s(A, 1024, 8, 1, 0, A + 512, None) == EINVAL       # out overlaps buf
+    c = pq2.lib.pq2_stream_probe_cfg
+    # buf, bytes, workgroups, waves, loads per lane, policy, store_all, sentinel, out, stream
+    assert c(None, 4096, 8, 4, 2, 1, 1, 0, D, None) == EINVAL
+    assert c(A, 4096, 8, 4, 2, 1, 1, 0, None, None) == EINVAL
+    assert c(A, 4096, 8, 4, 2, -1, 1, 0, D, None) == EINVAL       # policy
+    assert c(A, 4096, 8, 4, 2, 4, 1, 0, D, None) == EINVAL
+    assert c(A, 4096, 8, 0, 2, 1, 1, 0, D, None) == ESHAPE        # waves
+    assert c(A, 4096, 8, 17, 2, 1, 1, 0, D, None) == ESHAPE
+    for u in (0, 3, 5, 32):                                        # loads per lane: 1, 2, 4, 8 or 16
+        assert c(A, 4096, 8, 1, u, 1, 1, 0, D, None) == ESHAPE
+    assert c(A, 4096, 8, 8, 16, 1, 1, 0, D, None) == ESHAPE       # more than 64 KB per workgroup and chunk
+    assert c(A, 4096, 65536, 16, 2, 1, 1, 0, D, None) == ESHAPE   # an iteration spans more than 1 GiB
+    assert c(A, 1040, 8, 4, 2, 2, 1, 0, D, None) == ESHAPE        # LDS loads: whole 1 KB blocks
+    assert c(A, 1040, 8, 4, 2, 3, 1, 0, D, None) == ESHAPE
+    assert c(A, 1000, 8, 4, 2, 0, 1, 0, D, None) == ESHAPE
+    assert c(A + 8, 4096, 8, 4, 2, 1, 1, 0, D, None) == EALIGN
+    assert c(A, 4096, 8, 4, 2, 1, 1, 0, A + 1024, None) == EINVAL  # out overlaps buf
     e = pq2.lib.pq2_empty_probe
     assert e(0, 1, None) == ESHAPE and e(1, 0, None) == ESHAPE and e(1, 17, None) == ESHAPE
     assert e((1 << 20) + 1, 1, None) == ESHAPE
     if not _gpu_visible():
         assert s(A, 1024, 8, 1, 0, D, None) == EDEVICE
         assert e(256, 4, None) == EDEVICE
+        assert c(A, 4096, 8, 4, 2, 3, 1, 0, D, None) == EDEVICE
+        assert c(A, 1040, 8, 4, 2, 1, 1, 0, D, None) == EDEVICE   # buffer loads: any multiple of 16
+    text = open(os.path.join(ROOT, "include", "pq2_measure.h")).read()
+    for name, value in (("BUFFER", pq2.STREAM_BUFFER), ("BUFFER_NT", pq2.STREAM_BUFFER_NT),
+                        ("LDS", pq2.STREAM_LDS), ("LDS_NT", pq2.STREAM_LDS_NT)):
+        assert re.search(rf"PQ2_STREAM_{name} = {value}\b", text), name
 
 
 def test_gemv_static_validation():

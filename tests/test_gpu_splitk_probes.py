@@ -186,3 +186,33 @@ def test_stream_probe_reads_every_byte_once(nbytes, workgroups):
     torch.cuda.synchronize()
     words = out.cpu().numpy().view(np.uint32)
     assert np.all((words == 7) | (words == 0x7FFFFFFF))
+
+
+# Configurable stream probe: every load instruction and cache policy, loads
+# in flight per lane 1..16, 1..16 waves, ragged tails (a last iteration that
+# covers part of the grid; a partial 1 KB block for the buffer loads).
+STREAM_CFG_CASES = [(1024, 1, 1, 1), (5120, 3, 2, 4), ((1 << 20) + 3072, 7, 3, 16), (23674880, 1024, 4, 4),
+                    (13926400, 256, 16, 4), (5 << 20, 1, 1, 8), (3 << 20, 2048, 8, 2), (9216, 1, 4, 16)]
+
+
+@pytest.mark.parametrize("policy", [0, 1, 2, 3])
+@pytest.mark.parametrize("nbytes,workgroups,waves,loads", STREAM_CFG_CASES)
+def test_stream_probe_cfg_reads_every_byte_once(policy, nbytes, workgroups, waves, loads):
+    pq2 = _pq2()
+    if policy < 2 and nbytes % 1024 == 0:
+        nbytes -= 48  # buffer loads take any multiple of 16: a partial last block
+    announce(f"stream probe cfg policy={policy} bytes={nbytes} workgroups={workgroups} waves={waves} loads={loads}")
+    rng = np.random.default_rng(nbytes + policy)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(DEV)
+    out = torch.full((workgroups * waves,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    pq2.pq2_stream_probe_cfg(buf, nbytes, workgroups, waves, loads, policy, out, store_all=True)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host), "stream probe did not read each byte exactly once"
+    out.fill_(7)
+    pq2.pq2_stream_probe_cfg(buf, nbytes, workgroups, waves, loads, policy, out, store_all=False,
+                             sentinel=0x7FFFFFFF)
+    torch.cuda.synchronize()
+    words = out.cpu().numpy().view(np.uint32)
+    assert np.all((words == 7) | (words == 0x7FFFFFFF))
