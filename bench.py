@@ -30,7 +30,9 @@ timed the same way per call, and for each shape and M the tile matmul alone
     on the launch stream), against 8 TB/s; traffic from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary when its kernel digest matches;
   * ceilings: a linear stream read of the same bytes (pq2_stream_probe,
-    shaped like no engine), the same with one store per wave, the decode
+    shaped like no engine), its best over the shapes the stream sweep found
+    best at these sizes (pq2_stream_probe_cfg), the same with one store per
+    wave, the decode
     engine's own weight loads (pq2_read_probe), the empty-kernel launch floor
     (pq2_empty_probe), and a fit t = t0 + B / BW of the stream read over
     4..192 MB.
@@ -258,16 +260,31 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
         cfg.tpool[c], cfg.tb, STREAM_WORKGROUPS, sout, True, stream=stream) for c in range(copies)], copies, reps)
     engine_read_us = per_call_us(torch, stream, lambda: [pq2.pq2_read_probe(
         cfg.tpool[c], pq2.LAYOUT_TILES, n, k, pout, stream=stream) for c in range(copies)], copies, reps)
+    # The best read of the same bytes over the shapes the stream sweep found
+    # best at these sizes (about 8 loads in flight per SIMD, non-temporal).
+    best_us, best_shape = None, None
+    cout = torch.empty((1 << 13,), dtype=torch.int32, device=cfg.x.device)
+    for policy, ws, loads in BEST_STREAM_SHAPES:
+        waves = 4
+        us = per_call_us(torch, stream, lambda policy=policy, ws=ws, loads=loads: [pq2.pq2_stream_probe_cfg(
+            cfg.tpool[c], cfg.tb, ws * 256, waves, loads, policy, cout, False, 0x7FFFFFFF, stream=stream)
+            for c in range(copies)], copies, reps)
+        if best_us is None or us < best_us:
+            best_us, best_shape = us, f"{STREAM_POLICIES[policy]}, {ws} waves per SIMD, {loads} loads per lane"
     torch.cuda.synchronize()
     ceilings = {
         "stream_read_us": round(stream_us, 3),
         "stream_read_GBps": round(cfg.tb / (stream_us * 1e-6) / 1e9, 1),
+        "stream_read_best_us": round(best_us, 3),
+        "stream_read_best_frac": round(cfg.tb / (best_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4),
+        "stream_read_best_shape": best_shape,
         "stream_read_plus_store_us": round(stream_store_us, 3),
         "engine_read_probe_us": round(engine_read_us, 3),
         "bytes": cfg.tb,
     }
     log(f"[bench] {cfg.name} ceilings: stream read {stream_us:.3f} us ({ceilings['stream_read_GBps']:.0f} GB/s), "
-        f"+ one store per wave {stream_store_us:.3f} us, engine read probe {engine_read_us:.3f} us")
+        f"best shape {best_us:.3f} us ({best_shape}), + one store per wave {stream_store_us:.3f} us, "
+        f"engine read probe {engine_read_us:.3f} us")
 
     tot_b = sum(v["matmul_bytes"] for v in per_m.values())
     tot_us = sum(v["matmul_us"] for v in per_m.values())
@@ -291,6 +308,8 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
         "kernel_source_digest": digest,
         "stream_read_us": ceilings["stream_read_us"],
         "mean_launch_vs_stream_read": round(mean_us / stream_us, 3),
+        "stream_read_best_us": ceilings["stream_read_best_us"],
+        "mean_launch_vs_best_stream_read": round(mean_us / best_us, 3),
         # The same kernel's mean duration per dispatch under rocprofv3
         # --kernel-trace (committed summary, same kernel source), and the
         # fraction of 8 TB/s it implies.
@@ -407,6 +426,9 @@ STREAM_SHAPE_BYTES = (13926400, 23674880, 192 << 20)
 STREAM_SHAPE_WAVES_PER_SIMD = (0.25, 0.5, 1, 2, 4, 8)
 STREAM_SHAPE_LOADS = (1, 2, 4, 8, 16)
 STREAM_POLICIES = ("buffer", "buffer_nt", "lds", "lds_nt")
+# (policy, waves per SIMD in workgroups of four, loads per lane): the best
+# shapes of the sweep at the decode weight sizes.
+BEST_STREAM_SHAPES = ((1, 8, 1), (1, 4, 2), (1, 2, 4), (3, 8, 1))
 
 
 def stream_shape_sweep(torch, pq2, buf, stream, reps):
