@@ -178,8 +178,12 @@ class Config:
     def __init__(self, torch, pq2, workloads, name, dev, stream, ms=DECODE_MS):
         w = workloads.WORKLOADS[name]
         self.name, self.n, self.k, self.ms = name, w.n, w.k, ms
+        # The shape's other column counts (FFN up M = 8, FFN down M = 16):
+        # timed per call beside M = 1..4, outside the roofline's mean.
+        self.extra_ms = tuple(m for m in w.ms if m not in ms)
+        all_ms = tuple(ms) + self.extra_ms
         self.raw_np, x_cpu = workloads.workload_inputs(name)
-        self.x_cpu = x_cpu[: max(ms)].contiguous()
+        self.x_cpu = x_cpu[: max(all_ms)].contiguous()
         self.wb = weight_bytes(self.n, self.k)
         self.tb = pq2.pq2_tiles_bytes(self.n, self.k)
         per = len(ms)
@@ -191,11 +195,11 @@ class Config:
             for c in range(1, self.copies):
                 self.tpool[c].copy_(self.tpool[0])
             self.x = self.x_cpu.to(dev)
-            self.q = {m: torch.empty((m, self.k), dtype=torch.int8, device=dev) for m in ms}
-            self.xs = {m: torch.empty((m, self.k // 128), dtype=torch.float32, device=dev) for m in ms}
-            self.y = {m: torch.empty((m, self.n), dtype=torch.float32, device=dev) for m in ms}
-            self.ymm = {m: torch.empty((m, self.n), dtype=torch.float32, device=dev) for m in ms}
-            for m in ms:
+            self.q = {m: torch.empty((m, self.k), dtype=torch.int8, device=dev) for m in all_ms}
+            self.xs = {m: torch.empty((m, self.k // 128), dtype=torch.float32, device=dev) for m in all_ms}
+            self.y = {m: torch.empty((m, self.n), dtype=torch.float32, device=dev) for m in all_ms}
+            self.ymm = {m: torch.empty((m, self.n), dtype=torch.float32, device=dev) for m in all_ms}
+            for m in all_ms:
                 pq2.pq2_quantize_act_i8(self.x[:m], self.q[m], self.xs[m], stream=stream)
         torch.cuda.synchronize()
         log(f"[bench] {name} K={self.k} N={self.n}: weights {self.wb} B, {self.copies} tile copies "
@@ -213,7 +217,7 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
     config's rotating copies."""
     n, k, copies = cfg.n, cfg.k, cfg.copies
     per_m = {}
-    for m in cfg.ms:
+    for m in cfg.ms + cfg.extra_ms:
         mm_us = per_call_us(torch, stream, lambda m=m: [cfg.matmul(pq2, m, c, stream) for c in range(copies)],
                             copies, reps)
         call_us = per_call_us(torch, stream, lambda m=m: [cfg.gemv(pq2, m, c, stream) for c in range(copies)],
@@ -286,10 +290,10 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
         f"best shape {best_us:.3f} us ({best_shape}), + one store per wave {stream_store_us:.3f} us, "
         f"engine read probe {engine_read_us:.3f} us")
 
-    tot_b = sum(v["matmul_bytes"] for v in per_m.values())
-    tot_us = sum(v["matmul_us"] for v in per_m.values())
+    tot_b = sum(per_m[str(m)]["matmul_bytes"] for m in cfg.ms)
+    tot_us = sum(per_m[str(m)]["matmul_us"] for m in cfg.ms)
     achieved = tot_b / (tot_us * 1e-6) / 1e9
-    mean_us = tot_us / len(per_m)
+    mean_us = tot_us / len(cfg.ms)
     traffic = stored_summary(f"small_m_tiles_{cfg.name}_traffic.txt", digest)
     trace = stored_trace(digest)
     traced_us = float(trace[f"traced_mean_launch_us_{cfg.name}"]) if trace and \
@@ -303,7 +307,7 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
         "traffic": float(traffic["hbm_bytes_per_launch_avg_m1to4"]) if traffic else None,
         "kernel": f"small_m_tiles_kernel (pq2_matmul_small_m_tiles), {cfg.name} K={k} N={n}, "
                   f"mean over one launch each at M={','.join(map(str, cfg.ms))}",
-        "algorithmic_bytes_per_launch_avg": tot_b / len(per_m),
+        "algorithmic_bytes_per_launch_avg": tot_b / len(cfg.ms),
         "mean_launch_us": round(mean_us, 3),
         "kernel_source_digest": digest,
         "stream_read_us": ceilings["stream_read_us"],
@@ -314,7 +318,7 @@ def measure_config(torch, pq2, cfg, stream, reps, digest):
         # --kernel-trace (committed summary, same kernel source), and the
         # fraction of 8 TB/s it implies.
         "traced_mean_launch_us": traced_us,
-        "traced_frac": round(tot_b / len(per_m) / (traced_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4) if traced_us else None,
+        "traced_frac": round(tot_b / len(cfg.ms) / (traced_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4) if traced_us else None,
         "stream_read_frac": round(cfg.tb / (stream_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4),
     }
     return per_m, ceilings, roofline
