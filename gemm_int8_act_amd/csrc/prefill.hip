@@ -33,6 +33,11 @@
 //    lane of every load carries data: 16-byte activation loads, one 16-byte
 //    code load per group pair (tile layout), and the scales of 8 groups per
 //    load (tile layout).
+//  * The 128x128 tile on eight waves (tile layout) loads its activations
+//    straight into LDS (buffer_load_dwordx4 ... lds), each lane fetching the
+//    quad that the swizzle puts in its slot: no registers and no staging
+//    writes for A, which keeps the tile at four waves per SIMD, two
+//    workgroups per CU.
 //  * After the four k-steps of a group each lane rescales its INT32 results:
 //    acc += (float(dot) * xs[m]) * ws[n].  That rescale (3 VALU per output
 //    and group) makes the VALU the busiest unit: it costs more issue slots
@@ -50,6 +55,32 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t kCodeLut = 0x020100FFu;  // code c -> byte c - 1 (as v_perm table)
+
+// 16 bytes per lane straight into LDS, lane l's at lds_addr + 16 l
+// (buffer_load_dwordx4 ... lds; offsets past the buffer's range read zero, as
+// for buf_load16).  Issued from inline assembly so that the compiler's
+// wait-count pass does not see the LDS write: given the builtin, it took the
+// write as aliasing every later LDS read and waited for the load before the
+// next fragment read.  The caller waits (wait_vm) before other waves read.
+// A load the pass does not count only makes its own vmcnt waits longer:
+// loads complete in issue order.
+__device__ __forceinline__ void buf_load16_lds(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (GFX9 encoding; expcnt and lgkmcnt left at their
+// maxima): all but this wave's N most recent vector-memory instructions have
+// completed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 __device__ __forceinline__ uint32_t lut_plane(uint32_t fields) {
     return __builtin_amdgcn_perm(0u, kCodeLut, fields);
@@ -79,8 +110,15 @@ __device__ __forceinline__ int swz(int i, int t) { return i * 8 + (t ^ ((i >> 1)
 // section C, Tests 8 and 9: each activation group's k-steps form their own
 // INT32 chain; a weight group's terms float(dot) * xs are summed in k order,
 // then scaled by its ws into acc.
+//
+// LDA (the 128 x 128 tile on eight waves, tile layout, 128-element groups):
+// A goes straight from memory into LDS, one group ahead, into the buffer the
+// previous group used, so it takes no registers and no staging writes, and
+// the code and scale loads go two groups ahead; the kernel is held to four
+// waves per SIMD (128 registers, a 12-byte spill) so that two workgroups
+// share a CU.
 template <int BM, int BN, bool PLANE_A, bool TILES, int AG = 128, int WM = 2>
-__global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restrict__ q,
+__global__ __launch_bounds__(WM * 128, (WM == 4 && TILES && AG == 128) ? 4 : 1) void prefill_kernel(const int8_t* __restrict__ q,
                                                       const float* __restrict__ xs,
                                                       const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
@@ -107,6 +145,7 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     // SIMD at 64x128): one 16-byte load per (row, k-block) for both groups.
     // Otherwise one 8-byte load per (row, k-block) and group.
     constexpr bool BPAIR = SBLK;
+    constexpr bool LDA = SBLK && WM == 4;
     constexpr int XB = SBLK ? BM * 8 / NTH : 1;   // xs items per thread per block
     constexpr int WB = SBLK ? BN * 4 / NTH : 1;   // ws dwords per thread per block
     static_assert(!SBLK || (XB * NTH == BM * 8 && WB * NTH == BN * 4), "scale block split");
@@ -139,6 +178,8 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     const int mrows = min(BM, m - mb);
     const int nrows = min(BN, n - nb);
     const auto q_rs = make_rsrc(q + (size_t)mb * k, (uint32_t)(mrows * k));
+    i32x4_t q_srs{};
+    if constexpr (LDA) q_srs = make_srsrc(q + (size_t)mb * k, (uint32_t)(mrows * k));
     // Tile layout: BN is a multiple of 16, so the workgroup's rows are whole
     // tiles; their units are contiguous, (nb / 16) * S8 units from the start.
     const int s8 = (groups + 7) / 8;
@@ -152,6 +193,21 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     for (int p = 0; p < AQ; ++p) {
         const int it = tid + NTH * p;
         a_off[p] = (uint32_t)((it >> 3) * k + (it & 7) * 16);
+    }
+    // LDA: slot it = tid + NTH p of an A buffer (row it >> 3, position it & 7)
+    // holds quad (it & 7) ^ ((row >> 1) & 7) of the row (the swizzle of the
+    // staging writes); wave w's p-th load fills slots (w + NTH/64 p) * 64 ..
+    // + 63, lane l the l-th of them.
+    uint32_t al_off[LDA ? AQ : 1];
+    int wave_u = 0;
+    if constexpr (LDA) {
+#pragma unroll
+        for (int p = 0; p < AQ; ++p) {
+            const int it = tid + NTH * p;
+            const int row = it >> 3;
+            al_off[p] = (uint32_t)(row * k + 16 * ((it & 7) ^ ((row >> 1) & 7)));
+        }
+        wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
     }
     const uint32_t b_off = tid < BI ? (uint32_t)((tid >> 1) * k4 + (tid & 1) * 16) : kBufferOOB;
     // Tile layout: items it = tid + NTH p (p < BN * 4 / NTH) take row it >> 2, k-block it & 3.
@@ -199,10 +255,11 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     // Global loads are issued PD groups ahead of their products: PD = 2 with
     // two register sets (group g's loads land in set g % 2), or PD = 1 with
     // one where two sets would not fit the registers of four waves per SIMD
-    // (the 128 x 128 tile on eight waves).  Code item pairs are loaded with
+    // (the 128 x 128 tile on eight waves with A through registers; with A
+    // straight into LDS, one group ahead, the other loads go two ahead).  Code item pairs are loaded with
     // the even group into set (g / 2) % 2 when two pairs can be live at once
     // (PD = 2), else into one set.
-    constexpr int PD = WM == 4 ? 1 : 2;
+    constexpr int PD = WM == 4 && !LDA ? 1 : 2;
     constexpr int TPS = PD == 2 ? 2 : 1;
     uint4 areg[PD][AQ];
     uint4 breg[PD];
@@ -221,8 +278,10 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     auto load_stage = [&](int g, auto jc) {
         constexpr int j = decltype(jc)::value;
         constexpr int st = j % PD;
+        if constexpr (!LDA) {
 #pragma unroll
-        for (int p = 0; p < AQ; ++p) areg[st][p] = buf_load16s(q_rs, a_off[p], (uint32_t)g * 128u);
+            for (int p = 0; p < AQ; ++p) areg[st][p] = buf_load16s(q_rs, a_off[p], (uint32_t)g * 128u);
+        }
         if constexpr (BPAIR) {
             if constexpr (j % 2 == 0) {
                 // Unit (tile, g / 8), block (g % 8) / 2: both groups of the pair.
@@ -267,6 +326,22 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
                 sreg[st] = buf_load2(s_rs, s_is_w && g < groups ? s_off + (uint32_t)g * 2u : kBufferOOB);
         }
     };
+    // LDA: group g's A into LDS buffer JC % 2 (all waves are past their
+    // reads of it: the previous group's barrier).
+    auto load_a = [&](int g, auto jc) {
+        constexpr int buf = decltype(jc)::value % 2;
+#pragma unroll
+        for (int p = 0; p < AQ; ++p)
+            buf_load16_lds(q_srs, al_off[p], __builtin_amdgcn_readfirstlane((uint32_t)g * 128u),
+                           __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+                               (__attribute__((address_space(3))) uint4*)(&As[buf][(wave_u + (NTH / 64) * p) * 64]))));
+    };
+    // Vector-memory instructions load_stage issues under LDA for group JC
+    // (modulo the unroll): code items on even groups, the scale block every 8.
+    auto rest_loads = [](auto jc) constexpr {
+        constexpr int j = decltype(jc)::value;
+        return (j % 2 == 0 ? TI : 0) + (j % 8 == 0 ? XB + WB : 0);
+    };
     // LDS slots this thread writes (fixed for the whole kernel).
     int a_slot[AQ];
 #pragma unroll
@@ -282,8 +357,11 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
         constexpr int j = decltype(jc)::value;
         constexpr int buf = j % 2;   // LDS buffer = parity of the group
         constexpr int st = j % PD;   // register set
+        if constexpr (!LDA) {
 #pragma unroll
-        for (int p = 0; p < AQ; ++p) As[buf][a_slot[p]] = (PLANE_A || TILES) ? areg[st][p] : to_plane_order(areg[st][p]);
+            for (int p = 0; p < AQ; ++p)
+                As[buf][a_slot[p]] = (PLANE_A || TILES) ? areg[st][p] : to_plane_order(areg[st][p]);
+        }
         if constexpr (TILES) {
 #pragma unroll
             for (int p = 0; p < TI; ++p) {
@@ -362,9 +440,11 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
 
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
+    if constexpr (LDA) load_a(0, C0{});
     load_stage(0, C0{});
     if constexpr (PD == 2) load_stage(1, C1{});
     store_stage(C0{});
+    if constexpr (LDA) wait_vm<rest_loads(C0{}) + (PD == 2 ? rest_loads(C1{}) : 0)>();
     __syncthreads();
 
     // One group g (JC = g modulo the unroll): its products and rescale from
@@ -374,6 +454,14 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
     auto group_step = [&](int g, auto jc) {
         constexpr int j = decltype(jc)::value;
         constexpr int buf = j % 2;
+        if constexpr (LDA) {
+            // Unconditional: past the last group the offsets are out of range
+            // and the buffer is not read again.  (Under a branch the compiler
+            // waited on the previous group's loads before the first fragment
+            // read.)
+            load_a(g + 1, std::integral_constant<int, (j + 1) % UNR>{});
+            __builtin_amdgcn_sched_barrier(0);
+        }
         load_stage(g + PD, std::integral_constant<int, (j + PD) % UNR>{});
 
         // Activation group t of this weight group: k-steps KS*t .. KS*t + KS - 1.
@@ -475,6 +563,9 @@ __global__ __launch_bounds__(WM * 128) void prefill_kernel(const int8_t* __restr
             if constexpr (SBLK && (j + 1) % 8 == 0) __syncthreads();
             store_stage(std::integral_constant<int, (j + 1) % UNR>{});
         }
+        // LDA: group g + 1's A is in LDS once every vector-memory instruction
+        // but the ones issued after it (group g + PD's loads) has completed.
+        if constexpr (LDA) wait_vm<rest_loads(std::integral_constant<int, (j + PD) % UNR>{})>();
         __syncthreads();
     };
     for (int g = 0; g < groups; g += UNR) {
@@ -535,22 +626,36 @@ hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* plan
 
 // Tile choice.  A tile's workgroups run in rounds of as many as the chip
 // holds at once (256 CUs; per CU four 64x64, three 64x128 or two 128x128
-// workgroups on eight waves), and a round takes nearly the time of a full one
-// however few workgroups are left in it, since each workgroup is one chain
-// over all k groups.  Below 512 workgroups of 64x128 the 64x64 tile, whose
-// grid fills more of the chip.  From there, for the tile layout, the 64x128
-// tile or the 128x128 tile on eight waves, whichever needs less time counted
-// in whole rounds: at k = 5120 a full round of 128x128 workgroups took 1.19
-// times one of 64x128 (63 against 52.9 us), so 128x128 wins where its grid
-// fills its last round better (m = 1024, n = 16384: 2 rounds against 2.67,
-// 126.3 against 138.7 us) and loses at FFN up (m = 1024, n = 17408: 2.12
-// rounds against 2.83, 156.8 against 151.5 us).  The other weight layouts keep
+// workgroups on eight waves), each workgroup one chain over all k groups.
+// Below 512 workgroups of 64x128 the 64x64 tile, whose grid fills more of
+// the chip.  From there, for the tile layout with 128-element groups, the
+// 64x128 tile or the 128x128 tile on eight waves (A straight into LDS), by a
+// cost counted in rounds (round_cost): a full round of 128x128 workgroups
+// takes about 1.1 times one of 64x128 at k = 5120, and a partial round
+// costs more the fewer full rounds run before it, since the workgroups of
+// the first rounds start together and finish together.  Measured on one
+// box (µs, 64x128 against 128x128): FFN up m = 256 / 512 / 1024 / 2048,
+// 52.3 / 88.1 / 156.4 / 303.2 against 54.6 / 89.4 / 145.1 / 266.8; gate
+// (n = 6144) m = 1024 / 2048, 57.8 / 110.7 against 56.1 / 97.4; n = 16384,
+// m = 512 / 1024, 78.0 / 144.9 against 64.7 / 124.1; n = 8192, m = 1024,
+// 77.3 against 65.5.  The rule picks the faster tile at each of these but
+// FFN up m = 512 (1.5% apart).  The other weight layouts keep
 // 128x128 from 2048 workgroups of 64x128 on.  Activation groups of 64 or 32
 // stay on 64x128: there the 128x128 tile on eight waves needs 146-148
-// registers, one workgroup per CU.  The 128x128 tile on four waves
-// needs more than 256 registers per lane (one wave per SIMD); it stays
-// available through the tuning entry points.
+// registers, one workgroup per CU.  The 128x128 tile on four waves needs
+// more than 256 registers per lane (one wave per SIMD); it stays available
+// through the tuning entry points.
 constexpr int64_t kPrefillCUs = 256;
+
+// Time of `rounds` rounds of workgroups in units of one full round.
+double round_cost(double rounds) {
+    const double full = (double)(int64_t)rounds;
+    const double part = rounds - full;
+    if (part == 0.0) return full;
+    if (full == 0.0) return 0.6 + 0.4 * part;
+    if (full == 1.0) return full + 0.35 + 0.45 * part;
+    return full + 0.05 + 0.65 * part;
+}
 
 int default_prefill_tile(int64_t m, int64_t n, bool tile_layout, int agroup = 128) {
     const int64_t wgs2 = ((n + 127) / 128) * ((m + 63) / 64);
@@ -558,9 +663,9 @@ int default_prefill_tile(int64_t m, int64_t n, bool tile_layout, int agroup = 12
     if (agroup != 128) return 2;
     if (!tile_layout) return wgs2 >= 2048 ? 5 : 2;
     const int64_t wgs5 = ((n + 127) / 128) * ((m + 127) / 128);
-    const int64_t rounds2 = (wgs2 + 3 * kPrefillCUs - 1) / (3 * kPrefillCUs);
-    const int64_t rounds5 = (wgs5 + 2 * kPrefillCUs - 1) / (2 * kPrefillCUs);
-    return rounds5 * 119 < rounds2 * 100 ? 5 : 2;
+    const double t2 = round_cost((double)wgs2 / (3 * kPrefillCUs));
+    const double t5 = 1.1 * round_cost((double)wgs5 / (2 * kPrefillCUs));
+    return t5 < t2 ? 5 : 2;
 }
 
 hipError_t launch_prefill(const int8_t* q, const float* xs, const uint8_t* planes, int64_t m,

@@ -505,6 +505,29 @@ def test_prefill_tiles(tile):
     assert np.array_equal(yt.view(np.uint32), y0.view(np.uint32)), "prefill from the tile layout changed the bits"
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 200, 128), (127, 130, 1152), (129, 384, 1152), (256, 128, 5120),
+                                   (300, 272, 2176)])
+def test_prefill_tiles_lds_direct_edges(m, n, k):
+    """The 128x128 tile on eight waves from the tile layout, whose
+    activations go straight into LDS one group ahead: rows past m inside a
+    workgroup tile, a single group, group counts that are not a multiple of
+    8, several row tiles.  Within the bound, and the bits of the 64x128 tile
+    (same summation order)."""
+    pq2 = _pq2()
+    announce(f"prefill lds-direct m={m} n={n} k={k}")
+    raw = workloads.make_raw_weights(n, k, seed=130 + m, codes="ternary+3", row_pad=1)
+    x = workloads.make_activations(m, k, 131 + n, "normal+outliers")
+    q, xs, qo, xso = quantise_both(x)
+    tiles = gpu_tiles(raw, n, k)
+    y5 = gpu_matmul(pq2.pq2_matmul_prefill_tiles_tuned, q, xs, tiles, n, tile=5)
+    y_ref, bound = oracle.matmul_raw(qo, xso, raw, n, k)
+    assert_within(y5, y_ref, bound, f"prefill lds-direct m={m} n={n} k={k}")
+    y2 = gpu_matmul(pq2.pq2_matmul_prefill_tiles_tuned, q, xs, tiles, n, tile=2)
+    assert np.array_equal(y5.view(np.uint32), y2.view(np.uint32)), "128x128 tile changed the bits"
+    y5b = gpu_matmul(pq2.pq2_matmul_prefill_tiles_tuned, q, xs, tiles, n, tile=5)
+    assert np.array_equal(y5b.view(np.uint32), y5.view(np.uint32)), "repeat call differs"
+
+
 def test_prefill_matches_small_m():
     """Both paths compute the same definition: agree within twice the bound."""
     pq2 = _pq2()
