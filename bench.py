@@ -555,7 +555,7 @@ def main():
     ap.add_argument("--prefill-agroups", action="store_true",
                     help="with --only prefill: also time activation groups of 64 and 32")
     ap.add_argument("--calibrate", action="store_true",
-                    help="also run a plain 64 MiB copy kernel (counter calibration)")
+                    help="also run a plain 64 MiB copy kernel (counter calibration; with --only)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -575,8 +575,11 @@ def main():
         print(json.dumps(stream_sweep(torch, pq2, dev, stream, args.reps)), flush=True)
         return
     if args.only == "prefill":
-        print(json.dumps({"only": "prefill", "prefill": bench_prefill(torch, pq2, workloads, dev, stream, args.reps,
-                                                                       args.prefill_agroups)}), flush=True)
+        line = {"only": "prefill", "prefill": bench_prefill(torch, pq2, workloads, dev, stream, args.reps,
+                                                             args.prefill_agroups)}
+        if args.calibrate:
+            calibration_copy(torch, dev, stream)
+        print(json.dumps(line), flush=True)
         return
     if args.only:
         cfg = Config(torch, pq2, workloads, args.only, dev, stream)
