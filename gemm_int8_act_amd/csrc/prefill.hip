@@ -256,9 +256,9 @@ __global__ __launch_bounds__(WM * 128, (WM == 4 && TILES && AG == 128) ? 4 : 1) 
     // two register sets (group g's loads land in set g % 2), or PD = 1 with
     // one where two sets would not fit the registers of four waves per SIMD
     // (the 128 x 128 tile on eight waves with A through registers; with A
-    // straight into LDS, one group ahead, the other loads go two ahead).  Code item pairs are loaded with
-    // the even group into set (g / 2) % 2 when two pairs can be live at once
-    // (PD = 2), else into one set.
+    // straight into LDS, one group ahead, its other loads go two ahead).
+    // Code item pairs are loaded with the even group into set (g / 2) % 2
+    // when two pairs can be live at once (PD = 2), else into one set.
     constexpr int PD = WM == 4 && !LDA ? 1 : 2;
     constexpr int TPS = PD == 2 ? 2 : 1;
     uint4 areg[PD][AQ];
@@ -648,7 +648,7 @@ hipError_t launch_any_tile(const int8_t* q, const float* xs, const uint8_t* plan
 constexpr int64_t kPrefillCUs = 256;
 
 // Time of `rounds` rounds of workgroups in units of one full round.
-double round_cost(double rounds) {
+static double round_cost(double rounds) {
     const double full = (double)(int64_t)rounds;
     const double part = rounds - full;
     if (part == 0.0) return full;
@@ -657,7 +657,7 @@ double round_cost(double rounds) {
     return full + 0.05 + 0.65 * part;
 }
 
-int default_prefill_tile(int64_t m, int64_t n, bool tile_layout, int agroup = 128) {
+static int default_prefill_tile(int64_t m, int64_t n, bool tile_layout, int agroup = 128) {
     const int64_t wgs2 = ((n + 127) / 128) * ((m + 63) / 64);
     if (wgs2 < 512) return 3;
     if (agroup != 128) return 2;
