@@ -60,6 +60,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_BYTES_PER_S = 8.0e12       # MI355X HBM3E, published peak
 PEAK_INT8_OPS_PER_S = 5.0e15        # MI355X dense INT8 MFMA, published peak
+VALU_LANE_OPS_PER_S = 16 * 1024 * 2.4e9   # fp32 VALU: 16 lanes per SIMD per clock, 1024 SIMDs, 2.4 GHz
 ROTATION_BYTES = 1 << 30
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for M=1..4 packed-ternary matmul"
 HEADLINE = "up"
@@ -777,11 +778,17 @@ def bench_prefill(torch, pq2, workloads, dev, stream, reps=5, agroups=False):
             assert torch.isfinite(y).all()
             ops = 2.0 * m * w.n * w.k
             tops = ops / (us * 1e-6) / 1e12
+            # The rescale's own bound: 3 VALU per (m, n, group), issued at 16
+            # lanes per SIMD per clock (a wave64 instruction over 4 cycles).
+            rescale_us = 3.0 * m * w.n * (w.k // 128) / VALU_LANE_OPS_PER_S * 1e6
             out[f"{name}_m{m}"] = {"us": round(us, 2), "TOPS": round(tops, 1),
                                    "pct_int8_peak": round(100 * tops * 1e12 / PEAK_INT8_OPS_PER_S, 1),
+                                   "rescale_bound_us": round(rescale_us, 1),
+                                   "rescale_bound_frac": round(rescale_us / us, 3),
                                    "weight_copies": copies}
             log(f"[bench] {name} M={m}: tile-layout prefill {us:.1f} us, {tops:.0f} TOPS "
-                f"({out[f'{name}_m{m}']['pct_int8_peak']:.1f}% of 5 POP/s)")
+                f"({out[f'{name}_m{m}']['pct_int8_peak']:.1f}% of 5 POP/s; rescale bound {rescale_us:.1f} us, "
+                f"{100 * rescale_us / us:.0f}% of the call)")
             for ag in ((64, 32) if agroups else ()):
                 qg = torch.empty((m, w.k), dtype=torch.int8, device=dev)
                 xsg = torch.empty((m, w.k // ag), dtype=torch.float32, device=dev)
