@@ -218,11 +218,13 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
     constexpr int XSL = (XSV + 63) / 64;    // their loads per lane
     static_assert(AG == 128 || AG == 64 || AG == 32, "activation group");
     static_assert(MC <= 4 || (MC == 8 && AG == 128), "eight-column passes take 128-element activation groups");
-    // COLK (2..4 columns from natural-order q): A rows 4c..4c+3 all carry
-    // column c, so the lanes of k block kb hold column kb in every D row and
-    // one output each: the epilogue takes 3 VALU per group whatever the
-    // column count, against 3 per group and column with rows = columns.
-    constexpr bool COLK = !FUSED && AG == 128 && MC >= 2 && MC <= 4;
+    // COLK (2..4 columns, natural-order q or quantised in the kernel): A rows
+    // 4c..4c+3 all carry column c, so the lanes of k block kb hold column kb
+    // in every D row and one output each: the epilogue takes 3 VALU per group
+    // whatever the column count, against 3 per group and column with rows =
+    // columns.  A lane takes its column's xs from memory, or from the LDS
+    // copy the in-kernel quantiser writes.
+    constexpr bool COLK = AG == 128 && MC >= 2 && MC <= 4;
     constexpr int R = COLK ? 1 : (MC < 4 ? MC : 4);  // outputs per lane and class (D rows 4*kb + r)
     constexpr int KBU = COLK ? MC : (MC > 4 ? 2 : 1);  // lane groups kb holding outputs
     constexpr bool XS_VEC = !src_fused(SRC) && (AG < 128 || MC > 4);  // xs through LDS from vector loads
@@ -244,7 +246,8 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
     const auto tile_rs = make_rsrc(tiles + (size_t)tile * s8 * kSegUnit, (uint32_t)(s8 * kSegUnit));
     const auto q_rs = make_rsrc(FUSED ? nullptr : q + (size_t)m0 * k, FUSED ? 0u : (uint32_t)(mcount * k));
     const i32x4_t xs_srs = make_srsrc(FUSED ? nullptr : xs + (size_t)m0 * groups, FUSED ? 0u : (uint32_t)(mcount * groups * 4));
-    const auto xsc_rs = make_rsrc(COLK ? xs + (size_t)m0 * groups : nullptr, COLK ? (uint32_t)(mcount * groups * 4) : 0u);
+    const auto xsc_rs = make_rsrc(COLK && !FUSED ? xs + (size_t)m0 * groups : nullptr,
+                                  COLK && !FUSED ? (uint32_t)(mcount * groups * 4) : 0u);
     const auto xsa_rs = make_rsrc(XS_VEC ? xs + (size_t)m0 * groups * S : nullptr,
                                   XS_VEC ? (uint32_t)(mcount * groups * S * 4) : 0u);
     const auto x_rs = make_rsrc(
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
         uint4 qv[QLOADS];
         uint4 xraw[QLOADS][FUSED ? XL : 1];
         float xss[FUSED || XS_VEC || COLK ? 1 : MC][CPW];  // xs of the wave's groups, scalar loads (uniform)
-        uint4 xlv[COLK ? 2 : 1];                     // COLK: xs of this lane's column, vector loads
+        uint4 xlv[COLK && !FUSED ? 2 : 1];           // COLK: xs of this lane's column, vector loads
         uint32_t xsa[XS_VEC ? XSL : 1];              // xs through LDS (AG < 128 or MC > 4), vector loads
         uint4 wsv;
         uint4 cw[CPW / 2];
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
                 const bool ok = i < XSV && col < mcount && a < groups * S;
                 g.xsa[t] = buf_load4(xsa_rs, ok ? (uint32_t)((col * groups * S + a) * 4) : kBufferOOB);
             }
-        } else if constexpr (COLK) {
+        } else if constexpr (COLK && !FUSED) {
             // The eight xs of this lane's column (lanes past the last column
             // read the last one; past the last group the values are never
             // used: those groups' dots are zero).
@@ -329,7 +332,8 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
         }
     };
     // Private region: the staged columns (CPW groups each), then per class c
-    // of the wave 8 floats xs[c][m] and 8 ints -sum(q)[c][m].
+    // of the wave 8 floats xs[c][m] (COLK: xs[m][c]) and 8 ints -sum(q)[c][m]
+    // (COLK: four copies of each).
     unsigned char* region = smem + (size_t)wave * tiles_region_bytes(MC, CPW, AG);
     float* red = reinterpret_cast<float*>(smem + (size_t)nwaves * tiles_region_bytes(MC, CPW, AG));
     constexpr int NCOLS = tiles_cols_staged(MC, CPW);
@@ -378,7 +382,10 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
                 x_to_float16<SRC>(g.xraw[t], xf);
                 float scale;
                 v = quantize_lane16<false, LPS>(xf, sq, scale);  // the LPS lanes of the group agree
-                if ((lane & (LPS - 1)) == 0 && m < MC) xs_lds[((c_lo + (ch >> 3)) * S + (ch & 7) / LPS) * 8 + m] = scale;
+                if ((lane & (LPS - 1)) == 0 && m < MC) {
+                    if constexpr (COLK) xs_lds[m * 8 + c_lo + (ch >> 3)] = scale;
+                    else xs_lds[((c_lo + (ch >> 3)) * S + (ch & 7) / LPS) * 8 + m] = scale;
+                }
             } else {
                 v = g.qv[t];
                 sq = dot4(v.x, 0x01010101u, 0);
@@ -411,13 +418,16 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // COLK: the activation scales of this lane's column (g.xss[r] holds
-        // column min(r, mcount - 1); lanes past the last column are never
-        // stored).
+        // COLK: the activation scales of this lane's column (loaded for
+        // column min(kb, mcount - 1), or read from the quantiser's LDS copy;
+        // lanes past the last column are never stored).
         float xl[COLK ? CPW : 1];
         if constexpr (COLK) {
 #pragma unroll
-            for (int c = 0; c < CPW; ++c) xl[c] = __uint_as_float(word_of(g.xlv[c >> 2], c & 3));
+            for (int c = 0; c < CPW; ++c) {
+                if constexpr (FUSED) xl[c] = xs_lds[small_mod(kb, mcount) * 8 + c_lo + c];
+                else xl[c] = __uint_as_float(word_of(g.xlv[c >> 2], c & 3));
+            }
         }
 
         // 3. Group dots on the matrix cores, two groups at a time: D starts
@@ -483,7 +493,7 @@ __global__ __launch_bounds__(1024) void small_m_tiles_kernel(
                 const int4 nsq = COLK ? *reinterpret_cast<const int4*>(nsq_colk + (c_lo + c) * 16)
                                       : *reinterpret_cast<const int4*>(nsq_lds + (c_lo + c) * 8 + col4);
                 D[p] = v4i{nsq.x, nsq.y, nsq.z, nsq.w};
-                if constexpr (FUSED || XS_VEC) xsg[p] = *reinterpret_cast<const float4*>(xs_lds + (c_lo + c) * 8 + col4);
+                if constexpr ((FUSED || XS_VEC) && !COLK) xsg[p] = *reinterpret_cast<const float4*>(xs_lds + (c_lo + c) * 8 + col4);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const uint32_t d = word_of(g.cw[c >> 1], 2 * (c & 1) + h);
